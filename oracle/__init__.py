@@ -1,0 +1,27 @@
+"""fp64 CPU oracle for PowerSGD bucket compression.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path. It shares no code with
+the HIP library and imports nothing from it.
+
+Parity status per function (what pins each one is listed in the tests):
+  rng.philox4x64_10, rng.mulhilo64 .... pinned (numpy.random.Philox, Python ints)
+  rng.box_muller ...................... pinned (closed-form points, distribution)
+  rng.standard_normal_q0 .............. pinned (layout/key invariants, distribution)
+  powersgd.should_compress ............ pinned (brute-force integer arithmetic)
+  powersgd.gram_schmidt ............... pinned (QR uniqueness, Householder QR,
+                                        closed forms for epsilon > 0)
+  OracleState.compress_bucket ......... pinned (rational projection, hand-worked
+                                        example, invariants, Eckart-Young limit)
+"""
+from .powersgd import (HParams, LayoutChanged, OracleState, StepResult, ViewResult,
+                       compress_matrix_step,
+                       effective_rank, gram_schmidt, matrix_view, should_compress)
+from .rng import box_muller, mulhilo64, philox4x64_10, standard_normal_q0
+
+__all__ = [
+    "HParams", "LayoutChanged", "OracleState", "StepResult", "ViewResult",
+    "compress_matrix_step",
+    "effective_rank", "gram_schmidt", "matrix_view", "should_compress",
+    "box_muller", "mulhilo64", "philox4x64_10", "standard_normal_q0",
+]
