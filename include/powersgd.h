@@ -1,0 +1,222 @@
+/*
+ * powersgd.h -- C ABI of the MI355X (gfx950) PowerSGD bucket-compression library.
+ *
+ * The library compresses one data-parallel rank's flat gradient bucket in place
+ * with PowerSGD, as described on "DDP Communication Hooks -- PyTorch 1.11.0",
+ * section "PowerSGD Hooks" (powerSGD_hook, steps 1 to 3.7), with the state and
+ * hyperparameters of section "PowerSGD State" and the same-shape batching switch
+ * of the translated page's "Состояние PowerSGD" item 5. A float16 variant fuses the
+ * loss-scale division and inf/NaN check of "torch.cuda.amp -- PyTorch 1.5.0",
+ * section "Gradient Scaling" (GradScaler.unscale_ and step).
+ *
+ * One rank: the allreduces of P, of Q and of the uncompressed tensors are the
+ * identity, so no collective is issued.
+ *
+ * All device work is enqueued on the caller's HIP stream and runs asynchronously;
+ * completion of that stream work plays the role of the hook's Future. Every
+ * function returns before the device work completes unless stated otherwise.
+ * A state is not thread-safe; distinct states are independent.
+ */
+#ifndef POWERSGD_H
+#define POWERSGD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct powersgd_state powersgd_state; /* opaque, owned by the library */
+
+typedef enum {
+  POWERSGD_OK = 0,
+  POWERSGD_ERR_INVALID_ARG = -1,     /* bad pointer, size, view or hyperparameter   */
+  POWERSGD_ERR_LAYOUT_CHANGED = -2,  /* memorized bucket called with new views      */
+  POWERSGD_ERR_OOM = -3,             /* device allocation failed                     */
+  POWERSGD_ERR_HIP = -4,             /* a HIP runtime call failed (detail: last_error) */
+  POWERSGD_ERR_UNSUPPORTED = -5,     /* e.g. a rank above POWERSGD_MAX_RANK          */
+  POWERSGD_ERR_NOT_FOUND = -6        /* introspection of a bucket/view never compressed */
+} powersgd_status;
+
+typedef enum { POWERSGD_F32 = 0, POWERSGD_F16 = 1 } powersgd_dtype;
+
+#define POWERSGD_MAX_NDIM 8
+#define POWERSGD_MAX_RANK 32
+
+/*
+ * Hyperparameters, named as PowerSGDState names them ("PowerSGD State" section;
+ * batch_tensors_with_same_shape from the translated page). process_group is
+ * absent: one rank. powersgd_hparams_init() fills the pages' defaults.
+ */
+typedef struct {
+  int32_t matrix_approximation_rank;            /* r; default 1; 1..POWERSGD_MAX_RANK  */
+  int32_t use_error_feedback;                   /* default 1                           */
+  int64_t start_powerSGD_iter;                  /* default 1000; >= 0                  */
+  double min_compression_rate;                  /* default 2; any finite value         */
+  int32_t warm_start;                           /* default 1                           */
+  int32_t batch_tensors_with_same_shape;        /* default 0                           */
+  double orthogonalization_epsilon;             /* default 0; >= 0, finite             */
+  uint64_t random_seed;                         /* default 0                           */
+  int64_t compression_stats_logging_frequency;  /* default 10000; <= 0 disables logs   */
+} powersgd_hparams;
+
+/*
+ * One per-parameter view of the flat bucket ("PowerSGD Hooks", powerSGD_hook step 1:
+ * the flat bucket seen as a list of per-parameter tensors). offset and shape are in
+ * elements; the view covers numel = prod(shape) contiguous elements from offset.
+ * ndim 0 or 1 views are never compressed; ndim >= 2 views are compressed as the
+ * row-major matrix shape[0] x prod(shape[1..ndim-1]) when they pass the rate test.
+ */
+typedef struct {
+  int64_t offset;
+  int64_t ndim;
+  int64_t shape[POWERSGD_MAX_NDIM];
+} powersgd_view;
+
+/* Fills hp with the defaults printed in the PowerSGDState signature. Never fails
+ * (a NULL hp is ignored). */
+void powersgd_hparams_init(powersgd_hparams* hp);
+
+/*
+ * Creates a state for device `device` ("PowerSGD State": the hyperparameters and the
+ * internal state "for all the gradients during the training"). hp is copied.
+ * Errors: INVALID_ARG for NULL pointers, r < 1, epsilon < 0 or not finite, a
+ * non-finite rate, start_powerSGD_iter < 0; UNSUPPORTED for r > POWERSGD_MAX_RANK;
+ * HIP if the device cannot be selected. Device memory is allocated lazily, per
+ * bucket_index, on the first compressing call.
+ */
+powersgd_status powersgd_state_create(const powersgd_hparams* hp, int32_t device,
+                                      powersgd_state** out);
+
+/* Waits for the state's outstanding device work, frees everything it owns. NULL is
+ * ignored. */
+void powersgd_state_destroy(powersgd_state* st);
+
+/*
+ * Compresses one bucket in place: powerSGD_hook steps 1 to 3.7 on one rank.
+ *
+ *   bucket        device pointer, numel elements of `dtype`, caller-owned; updated in
+ *                 place with P Q^T for compressed views (uncompressed views: F32 left
+ *                 untouched, F16 unscaled). Must stay valid until the stream work ends.
+ *   views         host array of nviews views, read during the call only; views must
+ *                 lie inside [0, numel) and must not overlap. Elements outside every
+ *                 view are neither read nor written.
+ *   bucket_index  key of the per-bucket memory (error feedback, warm-start Q);
+ *                 calling a memorized bucket_index with other views (or another
+ *                 numel) returns LAYOUT_CHANGED when error feedback or warm start is
+ *                 on, mirroring the "PowerSGD State" warning on rebuilt buckets;
+ *                 otherwise the new layout replaces the old.
+ *   is_last       non-zero on the last bucket of an iteration: advances the iteration
+ *                 counter (GradBucket.is_last) after this call.
+ *   dtype         F32: fp32 gradients. F16: fp16 loss-scaled gradients; the call is
+ *                 GradScaler.unscale_ for this bucket (values are multiplied by
+ *                 inv_loss_scale) fused with the inf/NaN check; output is unscaled
+ *                 fp16, rounded to nearest even.
+ *   inv_loss_scale  F16 only (ignored for F32): 1/scale; exact when a power of two.
+ *   found_inf_dev   F16 only (required, device int32, caller-owned): the call ORs 1
+ *                 into it when any view element is inf or NaN, and skips everything
+ *                 (bucket, error memory and Q left bit-identical) when the flag is
+ *                 non-zero after the check; the caller zeroes it before the first
+ *                 bucket of an iteration. Never read back on the host here.
+ *   stream        hipStream_t (NULL = the legacy default stream).
+ *
+ * While iteration < start_powerSGD_iter the call is the vanilla allreduce: F32 is a
+ * no-op, F16 does the unscale (and inf check) only; no state is created.
+ * Errors are returned before anything is enqueued: INVALID_ARG (NULL state/bucket
+ * or views with nviews > 0, numel < 0, view out of bounds, overlapping views,
+ * ndim out of range, negative dimension, F16 without found_inf_dev, unknown dtype),
+ * LAYOUT_CHANGED, OOM, HIP (launch failure; asynchronous faults surface at the
+ * caller's next synchronization).
+ */
+powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_index,
+                                         int32_t is_last, void* bucket,
+                                         powersgd_dtype dtype, int64_t numel,
+                                         const powersgd_view* views, int32_t nviews,
+                                         float inv_loss_scale, int32_t* found_inf_dev,
+                                         void* stream);
+
+/* Static text for a status code. */
+const char* powersgd_status_string(powersgd_status s);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* powersgd_last_error(void);
+
+/*
+ * Host-only classification of one view under hp, without a state or a device:
+ * *compress = 1 when the view would be compressed ("PowerSGD State",
+ * min_compression_rate: (n + m) * rank * rate < n * m, strict, evaluated exactly on the
+ * binary64 rate), *n and *m = the matrix shape (shape[0] x prod(rest); 0 for ndim < 2)
+ * and *rank = min(r, n, m) (0 when not compressed). Any output pointer may be NULL.
+ * INVALID_ARG for a NULL hp/view, ndim out of range or a negative dimension.
+ */
+powersgd_status powersgd_classify_view(const powersgd_hparams* hp, const powersgd_view* view,
+                                       int32_t* compress, int64_t* n, int64_t* m,
+                                       int32_t* rank);
+
+/* --- introspection (for parity checks and statistics) ------------------------ */
+
+/*
+ * Compression decisions of a memorized bucket ("PowerSGD State", min_compression_rate):
+ * out[v] = 1 when view v is compressed, else 0. nviews must equal the bucket's view
+ * count. Host memory; synchronous, no device work. NOT_FOUND if the bucket was never
+ * compressed.
+ */
+powersgd_status powersgd_get_decisions(powersgd_state* st, int64_t bucket_index,
+                                       uint8_t* out, int32_t nviews);
+
+/* Matrix shape and rank used for view v (rank = min(r, n, m)); rank 0 when the view
+ * is not compressed. Synchronous, host only. */
+powersgd_status powersgd_get_view_info(powersgd_state* st, int64_t bucket_index,
+                                       int32_t view, int64_t* n, int64_t* m,
+                                       int32_t* rank);
+
+/*
+ * Copies the latest orthogonalized P (n x rank, row-major) and Q = M'^T P (m x rank,
+ * row-major; the warm-start memory) of compressed view v into caller device buffers
+ * (either may be NULL), enqueued on `stream`.
+ */
+powersgd_status powersgd_copy_factors(powersgd_state* st, int64_t bucket_index,
+                                      int32_t view, float* p_dev, float* q_dev,
+                                      void* stream);
+
+/* Copies the error-feedback memory E (n x m, row-major, fp32) of compressed view v
+ * into a caller device buffer, enqueued on `stream`. NOT_FOUND without error
+ * feedback. */
+powersgd_status powersgd_copy_error(powersgd_state* st, int64_t bucket_index,
+                                    int32_t view, float* e_dev, void* stream);
+
+/*
+ * Iteration counter and compression statistics ("PowerSGD State",
+ * compression_stats_logging_frequency): numel_in = elements seen by compressing
+ * calls, numel_comm = elements an allreduce would carry ((n + m) * rank per compressed
+ * view, numel per other view). Host values; synchronous.
+ */
+powersgd_status powersgd_get_stats(powersgd_state* st, int64_t* iteration,
+                                   int64_t* numel_in, int64_t* numel_comm);
+
+/* --- kernel timing (HIP events on the caller's stream) ------------------------ */
+
+#define POWERSGD_NUM_KERNELS 6
+/* kernel kinds: 0 q_init, 1 pass1 (P = M'Q), 2 orthogonalize, 3 pass2 (Q = M'^T P),
+ * 4 pass3 (decompress + error), 5 unscale-only (F16 pass-through) */
+
+/* Turns per-kernel event timing on (non-zero) or off; clears accumulated times. */
+powersgd_status powersgd_set_timing(powersgd_state* st, int32_t enable);
+
+/*
+ * Waits for the recorded events and returns, per kernel kind, the summed duration in
+ * milliseconds, the number of launches and the algorithmic bytes those launches
+ * moved (minimum HBM traffic of each pass). Arrays of POWERSGD_NUM_KERNELS entries,
+ * any may be NULL.
+ */
+powersgd_status powersgd_get_kernel_times(powersgd_state* st, double* ms,
+                                          int64_t* launches, double* bytes);
+
+/* Name of a kernel kind ("" if out of range). */
+const char* powersgd_kernel_name(int32_t kind);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POWERSGD_H */

@@ -15,13 +15,13 @@ Parity status per function (what pins each one is listed in the tests):
                                         example, invariants, Eckart-Young limit)
 """
 from .powersgd import (HParams, LayoutChanged, OracleState, StepResult, ViewResult,
-                       compress_matrix_step,
+                       any_nonfinite, compress_matrix_step,
                        effective_rank, gram_schmidt, matrix_view, should_compress)
 from .rng import box_muller, mulhilo64, philox4x64_10, standard_normal_q0
 
 __all__ = [
     "HParams", "LayoutChanged", "OracleState", "StepResult", "ViewResult",
-    "compress_matrix_step",
+    "any_nonfinite", "compress_matrix_step",
     "effective_rank", "gram_schmidt", "matrix_view", "should_compress",
     "box_muller", "mulhilo64", "philox4x64_10", "standard_normal_q0",
 ]

@@ -146,6 +146,16 @@ class _BucketMemory:
     q: Dict[int, np.ndarray] = field(default_factory=dict)       # view -> warm Q
 
 
+def any_nonfinite(bucket: np.ndarray, views: Sequence[View]) -> bool:
+    """GradScaler's check ("Gradient Scaling", unscale_/step): is any gradient value
+    in any view inf or NaN?"""
+    for off, shp in views:
+        size = int(np.prod(shp, dtype=np.int64))
+        if not np.all(np.isfinite(bucket[off:off + size])):
+            return True
+    return False
+
+
 class LayoutChanged(Exception):
     """A bucket's views changed after its E or Q was memorized ("PowerSGD State"
     warning on rebuilt buckets)."""
@@ -184,12 +194,7 @@ class OracleState:
         x64 = bucket.astype(np.float64)
 
         # GradScaler.unscale_/step: look for inf/NaN, skip everything if found.
-        found_inf = False
-        if is_fp16:
-            for off, shp in views:
-                size = int(np.prod(shp, dtype=np.int64))
-                if not np.all(np.isfinite(x64[off:off + size])):
-                    found_inf = True
+        found_inf = is_fp16 and any_nonfinite(bucket, views)
         if found_inf:
             if is_last:
                 self.iteration += 1

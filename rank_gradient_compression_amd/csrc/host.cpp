@@ -1,0 +1,873 @@
+// Host runtime of the PowerSGD bucket-compression library: the C ABI of
+// include/powersgd.h, per-bucket plans (view classification, rate decisions,
+// work-item tables), device memory ownership and the launch sequence.
+//
+// Method: "DDP Communication Hooks -- PyTorch 1.11.0", section "PowerSGD State"
+// (hyperparameters, rate test, epsilon, the warning on rebuilt buckets) and section
+// "PowerSGD Hooks" (powerSGD_hook steps 1 to 3.7, error-feedback memory), on one
+// rank; fp16 unscale and inf skip from "torch.cuda.amp -- PyTorch 1.5.0", section
+// "Gradient Scaling".
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "powersgd.h"
+
+using namespace psgd;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+powersgd_status fail(powersgd_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+powersgd_status hip_fail(hipError_t e, const char* what) {
+  return fail(POWERSGD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Rate test of the "PowerSGD State" section, (n + m) * rank * rate < n * m, evaluated
+// exactly on the binary64 value of rate, written as mant * 2^e with an integer mant.
+bool should_compress(int64_t n, int64_t m, int64_t rank, double rate) {
+  if (n <= 0 || m <= 0) return false;
+  using i128 = __int128;
+  const i128 nm = static_cast<i128>(n) * m;              // < 2^63 (inside the bucket)
+  if (rate <= 0.0) return true;                          // left side <= 0 < n * m
+  int e = 0;
+  const double fr = std::frexp(rate, &e);                // rate = fr * 2^e, fr in [0.5, 1)
+  const int64_t mant = static_cast<int64_t>(std::ldexp(fr, 53));  // exact, < 2^53
+  e -= 53;                                               // rate = mant * 2^e
+  const i128 a = static_cast<i128>(n + m) * rank * mant;  // < 2^64 * 2^5 * 2^53
+  if (e >= 0) {
+    // a * 2^e < nm  <=>  a <= (nm - 1) >> e
+    if (e >= 126) return false;
+    return a <= ((nm - 1) >> e);
+  }
+  // a < nm * 2^-e; when the right side exceeds 2^125 it exceeds every a
+  const int sh = -e;
+  int bits = 0;
+  for (i128 t = nm; t > 0; t >>= 1) ++bits;
+  if (bits + sh >= 125) return true;
+  return a < (nm << sh);
+}
+
+struct HipDeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit HipDeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~HipDeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+template <typename T>
+powersgd_status upload(const std::vector<T>& v, T** dst, hipStream_t s) {
+  *dst = nullptr;
+  if (v.empty()) return POWERSGD_OK;
+  const size_t bytes = v.size() * sizeof(T);
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(dst), bytes);
+  if (e != hipSuccess) return fail(POWERSGD_ERR_OOM, "hipMalloc of a work table failed");
+  e = hipMemcpyAsync(*dst, v.data(), bytes, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync of a work table");
+  return POWERSGD_OK;
+}
+
+struct ViewKey {
+  int64_t offset;
+  std::vector<int64_t> shape;
+  bool operator==(const ViewKey& o) const { return offset == o.offset && shape == o.shape; }
+};
+
+// Everything derived from one bucket layout, plus the memory the method keeps for it.
+struct BucketPlan {
+  int64_t numel = 0;
+  std::vector<ViewKey> views;
+  std::vector<uint8_t> decision;        // per view: 1 = compressed
+  std::vector<int32_t> view_tensor;     // per view: tensor index or -1
+  std::vector<int64_t> view_n, view_m;  // matrix shape (0 for vectors)
+  std::vector<int32_t> view_rank;
+  int R = 1;
+  int rpl = 1;
+  int64_t compressed_elems = 0;
+  int64_t uncompressed_elems = 0;
+  int64_t comm_elems = 0;
+  int64_t all_elems = 0;
+  std::vector<TensorDesc> tensors;
+  std::vector<Tile> tiles1, tiles23;
+  std::vector<FlatTile> flat_unc, flat_all;
+  std::vector<OrthJob> pjobs, qjobs;
+  std::vector<QInitJob> qinit;
+  int64_t max_qcount = 0;
+  int64_t e_floats = 0, p_floats = 0, q_floats = 0, partial_floats = 0, ncounters = 0;
+
+  // device memory
+  float* E = nullptr;
+  float* P = nullptr;
+  float* Q = nullptr;
+  float* partial = nullptr;
+  int32_t* counters = nullptr;
+  TensorDesc* d_td = nullptr;         // rows vector-aligned where possible
+  TensorDesc* d_td_scalar = nullptr;  // same with every vec flag cleared
+  Tile* d_tiles1 = nullptr;
+  Tile* d_tiles23 = nullptr;
+  FlatTile* d_flat_unc = nullptr;
+  FlatTile* d_flat_all = nullptr;
+  OrthJob* d_pjobs = nullptr;
+  OrthJob* d_qjobs = nullptr;
+  QInitJob* d_qinit = nullptr;
+  bool allocated = false;
+  bool q_ready = false;
+
+  void release() {
+    void* ptrs[] = {E, P, Q, partial, counters, d_td, d_td_scalar, d_tiles1, d_tiles23,
+                    d_flat_unc, d_flat_all, d_pjobs, d_qjobs, d_qinit};
+    for (void* p : ptrs)
+      if (p) (void)hipFree(p);
+    E = P = Q = partial = nullptr;
+    counters = nullptr;
+    d_td = d_td_scalar = nullptr;
+    d_tiles1 = d_tiles23 = nullptr;
+    d_flat_unc = d_flat_all = nullptr;
+    d_pjobs = d_qjobs = nullptr;
+    d_qinit = nullptr;
+    allocated = false;
+  }
+  ~BucketPlan() { release(); }
+};
+
+constexpr int64_t kFlatChunk = 1 << 16;
+
+void add_flat(std::vector<FlatTile>& out, int64_t start, int64_t len) {
+  for (int64_t s = 0; s < len; s += kFlatChunk)
+    out.push_back(FlatTile{start + s, std::min(kFlatChunk, len - s)});
+}
+
+struct TimingRec {
+  int kind;
+  hipEvent_t start, stop;
+  double bytes;
+};
+
+}  // namespace
+
+struct powersgd_state {
+  powersgd_hparams hp;
+  int device = 0;
+  int64_t iteration = 0;
+  int64_t numel_in = 0;
+  int64_t numel_comm = 0;
+  int64_t next_log_iteration = 0;
+  std::map<int64_t, std::unique_ptr<BucketPlan>> buckets;
+  std::map<int64_t, std::unique_ptr<BucketPlan>> passthrough;  // fp16 unscale tables only
+  hipStream_t last_stream = nullptr;
+  // timing
+  bool timing = false;
+  std::vector<TimingRec> pending;
+  std::vector<hipEvent_t> free_events;
+  double t_ms[POWERSGD_NUM_KERNELS] = {};
+  int64_t t_count[POWERSGD_NUM_KERNELS] = {};
+  double t_bytes[POWERSGD_NUM_KERNELS] = {};
+};
+
+namespace {
+
+enum KernelKind { K_QINIT = 0, K_PASS1 = 1, K_ORTH = 2, K_PASS2 = 3, K_PASS3 = 4, K_UNSCALE = 5 };
+
+hipEvent_t take_event(powersgd_state* st) {
+  if (!st->free_events.empty()) {
+    hipEvent_t e = st->free_events.back();
+    st->free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Drains recorded events into the per-kernel totals (waits for them).
+void collect_timing(powersgd_state* st) {
+  for (TimingRec& r : st->pending) {
+    (void)hipEventSynchronize(r.stop);
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+      st->t_ms[r.kind] += ms;
+      st->t_count[r.kind] += 1;
+      st->t_bytes[r.kind] += r.bytes;
+    }
+    st->free_events.push_back(r.start);
+    st->free_events.push_back(r.stop);
+  }
+  st->pending.clear();
+}
+
+// Runs one launch, bracketed by events when timing is on.
+template <typename F>
+powersgd_status timed_launch(powersgd_state* st, hipStream_t s, int kind, double bytes,
+                             const char* what, F&& launch) {
+  TimingRec rec{kind, nullptr, nullptr, bytes};
+  if (st->timing) {
+    if (st->pending.size() > 4096) collect_timing(st);
+    rec.start = take_event(st);
+    rec.stop = take_event(st);
+    if (rec.start && rec.stop) (void)hipEventRecord(rec.start, s);
+  }
+  const hipError_t e = launch();
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (st->timing && rec.start && rec.stop) {
+    (void)hipEventRecord(rec.stop, s);
+    st->pending.push_back(rec);
+  }
+  return POWERSGD_OK;
+}
+
+powersgd_status validate_views(const powersgd_view* views, int32_t nviews, int64_t numel,
+                               std::vector<ViewKey>& out) {
+  out.clear();
+  out.reserve(nviews);
+  std::vector<std::pair<int64_t, int64_t>> ranges;
+  for (int32_t v = 0; v < nviews; ++v) {
+    const powersgd_view& pv = views[v];
+    if (pv.ndim < 0 || pv.ndim > POWERSGD_MAX_NDIM)
+      return fail(POWERSGD_ERR_INVALID_ARG, "view " + std::to_string(v) + ": ndim out of range");
+    ViewKey k;
+    k.offset = pv.offset;
+    int64_t size = 1;
+    for (int64_t d = 0; d < pv.ndim; ++d) {
+      const int64_t s = pv.shape[d];
+      if (s < 0) return fail(POWERSGD_ERR_INVALID_ARG, "view " + std::to_string(v) + ": negative dimension");
+      if (s > 0 && size > INT64_MAX / s)
+        return fail(POWERSGD_ERR_INVALID_ARG, "view " + std::to_string(v) + ": size overflows");
+      size *= s;
+      k.shape.push_back(s);
+    }
+    if (pv.offset < 0 || pv.offset > numel || size > numel - pv.offset)
+      return fail(POWERSGD_ERR_INVALID_ARG, "view " + std::to_string(v) + ": outside the bucket");
+    if (size > 0) ranges.emplace_back(pv.offset, pv.offset + size);
+    out.push_back(std::move(k));
+  }
+  std::sort(ranges.begin(), ranges.end());
+  for (size_t i = 1; i < ranges.size(); ++i)
+    if (ranges[i].first < ranges[i - 1].second)
+      return fail(POWERSGD_ERR_INVALID_ARG, "views overlap");
+  return POWERSGD_OK;
+}
+
+int64_t view_numel(const ViewKey& k) {
+  int64_t s = 1;
+  for (int64_t d : k.shape) s *= d;
+  return s;
+}
+
+// Classification, rate decisions and work tables for one layout (host only).
+powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
+                           std::vector<ViewKey>&& views, BucketPlan& pl) {
+  pl.numel = numel;
+  pl.views = std::move(views);
+  const size_t nv = pl.views.size();
+  pl.decision.assign(nv, 0);
+  pl.view_tensor.assign(nv, -1);
+  pl.view_n.assign(nv, 0);
+  pl.view_m.assign(nv, 0);
+  pl.view_rank.assign(nv, 0);
+  int max_rank = 1;
+  for (size_t v = 0; v < nv; ++v) {
+    const ViewKey& k = pl.views[v];
+    const int64_t size = view_numel(k);
+    pl.all_elems += size;
+    bool comp = false;
+    if (k.shape.size() >= 2) {
+      const int64_t n = k.shape[0];
+      const int64_t m = n > 0 ? size / n : 0;
+      const int64_t rank = std::min<int64_t>(hp.matrix_approximation_rank, std::min(n, m));
+      comp = should_compress(n, m, rank, hp.min_compression_rate);
+      if (comp) {
+        if (n > INT32_MAX || m > INT32_MAX)
+          return fail(POWERSGD_ERR_UNSUPPORTED, "matrix dimension above 2^31 - 1");
+        pl.view_n[v] = n;
+        pl.view_m[v] = m;
+        pl.view_rank[v] = static_cast<int32_t>(rank);
+        max_rank = std::max<int>(max_rank, static_cast<int>(rank));
+      }
+    }
+    pl.decision[v] = comp ? 1 : 0;
+    if (comp) {
+      pl.compressed_elems += size;
+      pl.comm_elems += (pl.view_n[v] + pl.view_m[v]) * pl.view_rank[v];
+    } else {
+      pl.uncompressed_elems += size;
+      pl.comm_elems += size;
+      add_flat(pl.flat_unc, k.offset, size);
+    }
+    add_flat(pl.flat_all, k.offset, size);
+  }
+  pl.R = pow2_ceil(max_rank);
+  pl.rpl = pass1_rows_per_lane(pl.R);
+  const int R = pl.R;
+
+  // Work-item size: enough workgroups to fill 256 CUs several times over, and no
+  // more than 64K elements (256 KB of fp32) each.
+  const int64_t target =
+      std::min<int64_t>(1 << 16, std::max<int64_t>(1 << 14, pl.compressed_elems / 2048));
+  int64_t eoff = 0, poff = 0, qoff = 0;
+  int32_t pslot = 0, cslot = 0;
+  for (size_t v = 0; v < nv; ++v) {
+    if (!pl.decision[v]) continue;
+    TensorDesc d{};
+    d.boff = pl.views[v].offset;
+    d.n = static_cast<int32_t>(pl.view_n[v]);
+    d.m = static_cast<int32_t>(pl.view_m[v]);
+    d.rank = pl.view_rank[v];
+    d.vec = (d.boff % 4 == 0 && d.m % 4 == 0) ? 1 : 0;
+    d.view = static_cast<int32_t>(v);
+    d.eoff = eoff;
+    d.poff = poff;
+    d.qoff = qoff;
+    eoff += round_up(static_cast<int64_t>(d.n) * d.m, 64);
+    poff += round_up(static_cast<int64_t>(d.n) * R, 64);
+    qoff += round_up(static_cast<int64_t>(d.m) * R, 64);
+    // pass 2 / pass 3 blocks
+    d.ncb = static_cast<int32_t>((d.m + kColBlock - 1) / kColBlock);
+    const int64_t width = std::min<int64_t>(d.m, kColBlock);
+    int64_t rpb = round_up(std::max<int64_t>(4, (target + width - 1) / width), 4);
+    rpb = std::min<int64_t>(rpb, round_up(d.n, 4));
+    d.rpb = static_cast<int32_t>(rpb);
+    d.nrb = static_cast<int32_t>((d.n + rpb - 1) / rpb);
+    if (d.nrb > 1) {
+      d.pslot = pslot;
+      d.cslot = cslot;
+      pslot += d.nrb * d.ncb;
+      cslot += d.ncb;
+    }
+    const int32_t ti = static_cast<int32_t>(pl.tensors.size());
+    pl.view_tensor[v] = ti;
+    // pass 1 row tiles
+    const int64_t group = 4 * static_cast<int64_t>(pl.rpl);
+    int64_t rpt = round_up(std::max<int64_t>(1, (target + d.m - 1) / d.m), group);
+    rpt = std::min<int64_t>(rpt, round_up(d.n, group));
+    for (int64_t r0 = 0; r0 < d.n; r0 += rpt)
+      pl.tiles1.push_back(Tile{ti, static_cast<int32_t>(r0),
+                               static_cast<int32_t>(std::min<int64_t>(rpt, d.n - r0)), 0});
+    for (int32_t cb = 0; cb < d.ncb; ++cb)
+      for (int32_t rb = 0; rb < d.nrb; ++rb) pl.tiles23.push_back(Tile{ti, rb, cb, 0});
+    pl.pjobs.push_back(OrthJob{d.poff, d.n, d.rank});
+    pl.qjobs.push_back(OrthJob{d.qoff, d.m, d.rank});
+    pl.qinit.push_back(QInitJob{d.qoff, d.m, d.rank, d.view, 0});
+    pl.max_qcount = std::max<int64_t>(pl.max_qcount, static_cast<int64_t>(d.m) * d.rank);
+    pl.tensors.push_back(d);
+  }
+  pl.e_floats = eoff;
+  pl.p_floats = poff;
+  pl.q_floats = qoff;
+  pl.partial_floats = static_cast<int64_t>(pslot) * kColBlock * R;
+  pl.ncounters = cslot;
+  return POWERSGD_OK;
+}
+
+powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
+  auto alloc = [&](void** p, size_t bytes) -> bool {
+    if (bytes == 0) {
+      *p = nullptr;
+      return true;
+    }
+    return hipMalloc(p, bytes) == hipSuccess;
+  };
+  bool ok = true;
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.E), need_e ? pl.e_floats * sizeof(float) : 0);
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.P), pl.p_floats * sizeof(float));
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.Q), pl.q_floats * sizeof(float));
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.partial), pl.partial_floats * sizeof(float));
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.counters), pl.ncounters * sizeof(int32_t));
+  if (!ok) {
+    pl.release();
+    return fail(POWERSGD_ERR_OOM, "device allocation of the bucket state failed");
+  }
+  hipError_t e = hipSuccess;
+  if (pl.E && e == hipSuccess) e = hipMemsetAsync(pl.E, 0, pl.e_floats * sizeof(float), s);
+  if (pl.P && e == hipSuccess) e = hipMemsetAsync(pl.P, 0, pl.p_floats * sizeof(float), s);
+  if (pl.Q && e == hipSuccess) e = hipMemsetAsync(pl.Q, 0, pl.q_floats * sizeof(float), s);
+  if (pl.counters && e == hipSuccess)
+    e = hipMemsetAsync(pl.counters, 0, pl.ncounters * sizeof(int32_t), s);
+  if (e != hipSuccess) {
+    pl.release();
+    return hip_fail(e, "hipMemsetAsync of the bucket state");
+  }
+  std::vector<TensorDesc> scalar = pl.tensors;
+  for (TensorDesc& d : scalar) d.vec = 0;
+  powersgd_status st = POWERSGD_OK;
+  if (st == POWERSGD_OK) st = upload(pl.tensors, &pl.d_td, s);
+  if (st == POWERSGD_OK) st = upload(scalar, &pl.d_td_scalar, s);
+  if (st == POWERSGD_OK) st = upload(pl.tiles1, &pl.d_tiles1, s);
+  if (st == POWERSGD_OK) st = upload(pl.tiles23, &pl.d_tiles23, s);
+  if (st == POWERSGD_OK) st = upload(pl.flat_unc, &pl.d_flat_unc, s);
+  if (st == POWERSGD_OK) st = upload(pl.flat_all, &pl.d_flat_all, s);
+  if (st == POWERSGD_OK) st = upload(pl.pjobs, &pl.d_pjobs, s);
+  if (st == POWERSGD_OK) st = upload(pl.qjobs, &pl.d_qjobs, s);
+  if (st == POWERSGD_OK) st = upload(pl.qinit, &pl.d_qinit, s);
+  if (st != POWERSGD_OK) {
+    pl.release();
+    return st;
+  }
+  // The host vectors above must outlive the asynchronous uploads.
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    pl.release();
+    return hip_fail(e, "hipStreamSynchronize after the state upload");
+  }
+  pl.allocated = true;
+  return POWERSGD_OK;
+}
+
+bool same_layout(const BucketPlan& pl, int64_t numel, const std::vector<ViewKey>& views) {
+  return pl.numel == numel && pl.views == views;
+}
+
+// Algorithmic bytes of each pass per compressed element (minimum traffic).
+double pass_bytes(int kind, bool f16, bool ef) {
+  const double g = f16 ? 2.0 : 4.0;
+  switch (kind) {
+    case K_PASS1: return f16 ? (g + (ef ? 4.0 : 0.0)) : (ef ? 12.0 : 4.0);
+    case K_PASS2: return f16 ? (g + (ef ? 4.0 : 0.0)) : 4.0;
+    case K_PASS3: return f16 ? (ef ? 12.0 : 4.0) : (ef ? 12.0 : 8.0);
+    default: return 0.0;
+  }
+}
+
+}  // namespace
+
+// ============================================================================ ABI
+
+extern "C" {
+
+void powersgd_hparams_init(powersgd_hparams* hp) {
+  if (!hp) return;
+  std::memset(hp, 0, sizeof(*hp));
+  hp->matrix_approximation_rank = 1;
+  hp->start_powerSGD_iter = 1000;
+  hp->min_compression_rate = 2.0;
+  hp->use_error_feedback = 1;
+  hp->warm_start = 1;
+  hp->orthogonalization_epsilon = 0.0;
+  hp->random_seed = 0;
+  hp->compression_stats_logging_frequency = 10000;
+  hp->batch_tensors_with_same_shape = 0;
+}
+
+const char* powersgd_status_string(powersgd_status s) {
+  switch (s) {
+    case POWERSGD_OK: return "ok";
+    case POWERSGD_ERR_INVALID_ARG: return "invalid argument";
+    case POWERSGD_ERR_LAYOUT_CHANGED: return "bucket layout changed after its state was memorized";
+    case POWERSGD_ERR_OOM: return "out of device memory";
+    case POWERSGD_ERR_HIP: return "HIP runtime error";
+    case POWERSGD_ERR_UNSUPPORTED: return "unsupported configuration";
+    case POWERSGD_ERR_NOT_FOUND: return "no such bucket or view";
+  }
+  return "unknown status";
+}
+
+const char* powersgd_last_error(void) { return g_last_error.c_str(); }
+
+const char* powersgd_kernel_name(int32_t kind) {
+  static const char* names[POWERSGD_NUM_KERNELS] = {"q_init", "pass1_mq", "orthogonalize",
+                                                    "pass2_mtp", "pass3_decompress_error",
+                                                    "unscale_only"};
+  if (kind < 0 || kind >= POWERSGD_NUM_KERNELS) return "";
+  return names[kind];
+}
+
+powersgd_status powersgd_state_create(const powersgd_hparams* hp, int32_t device,
+                                      powersgd_state** out) {
+  if (!out) return fail(POWERSGD_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!hp) return fail(POWERSGD_ERR_INVALID_ARG, "hp is NULL");
+  if (hp->matrix_approximation_rank < 1)
+    return fail(POWERSGD_ERR_INVALID_ARG, "matrix_approximation_rank must be >= 1");
+  if (hp->matrix_approximation_rank > POWERSGD_MAX_RANK)
+    return fail(POWERSGD_ERR_UNSUPPORTED, "matrix_approximation_rank above 32");
+  if (!std::isfinite(hp->orthogonalization_epsilon) || hp->orthogonalization_epsilon < 0.0)
+    return fail(POWERSGD_ERR_INVALID_ARG, "orthogonalization_epsilon must be finite and >= 0");
+  if (!std::isfinite(hp->min_compression_rate))
+    return fail(POWERSGD_ERR_INVALID_ARG, "min_compression_rate must be finite");
+  if (hp->start_powerSGD_iter < 0)
+    return fail(POWERSGD_ERR_INVALID_ARG, "start_powerSGD_iter must be >= 0");
+  if (device < 0) return fail(POWERSGD_ERR_INVALID_ARG, "device must be >= 0");
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (device >= count) return fail(POWERSGD_ERR_INVALID_ARG, "no such device");
+  auto* st = new (std::nothrow) powersgd_state();
+  if (!st) return fail(POWERSGD_ERR_OOM, "host allocation failed");
+  st->hp = *hp;
+  st->device = device;
+  st->next_log_iteration = hp->start_powerSGD_iter;
+  *out = st;
+  return POWERSGD_OK;
+}
+
+void powersgd_state_destroy(powersgd_state* st) {
+  if (!st) return;
+  HipDeviceGuard guard(st->device);
+  (void)hipDeviceSynchronize();
+  collect_timing(st);
+  for (hipEvent_t e : st->free_events) (void)hipEventDestroy(e);
+  st->buckets.clear();
+  st->passthrough.clear();
+  delete st;
+}
+
+powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_index,
+                                         int32_t is_last, void* bucket,
+                                         powersgd_dtype dtype, int64_t numel,
+                                         const powersgd_view* views, int32_t nviews,
+                                         float inv_loss_scale, int32_t* found_inf_dev,
+                                         void* stream) {
+  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
+  if (numel < 0) return fail(POWERSGD_ERR_INVALID_ARG, "numel < 0");
+  if (nviews < 0) return fail(POWERSGD_ERR_INVALID_ARG, "nviews < 0");
+  if (nviews > 0 && !views) return fail(POWERSGD_ERR_INVALID_ARG, "views is NULL");
+  if (numel > 0 && !bucket) return fail(POWERSGD_ERR_INVALID_ARG, "bucket is NULL");
+  if (dtype != POWERSGD_F32 && dtype != POWERSGD_F16)
+    return fail(POWERSGD_ERR_INVALID_ARG, "unknown dtype");
+  const bool f16 = dtype == POWERSGD_F16;
+  if (f16 && !found_inf_dev)
+    return fail(POWERSGD_ERR_INVALID_ARG, "fp16 buckets need found_inf_dev");
+  if (f16 && !std::isfinite(inv_loss_scale))
+    return fail(POWERSGD_ERR_INVALID_ARG, "inv_loss_scale must be finite");
+  std::vector<ViewKey> keys;
+  powersgd_status vs = validate_views(views, nviews, numel, keys);
+  if (vs != POWERSGD_OK) return vs;
+
+  HipDeviceGuard guard(st->device);
+  if (!guard.ok) return fail(POWERSGD_ERR_HIP, "hipSetDevice failed");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st->last_stream = s;
+  const powersgd_hparams& hp = st->hp;
+  const bool ef = hp.use_error_feedback != 0;
+  const uintptr_t base = reinterpret_cast<uintptr_t>(bucket);
+
+  // Vanilla allreduce phase (iteration < start_powerSGD_iter): identity on one rank;
+  // fp16 still does the unscale with its inf check.
+  if (st->iteration < hp.start_powerSGD_iter) {
+    if (f16) {
+      auto& slot = st->passthrough[bucket_index];
+      if (!slot || !same_layout(*slot, numel, keys)) {
+        auto pl = std::make_unique<BucketPlan>();
+        pl->numel = numel;
+        pl->views = keys;
+        for (const ViewKey& k : pl->views) add_flat(pl->flat_all, k.offset, view_numel(k));
+        powersgd_status u = upload(pl->flat_all, &pl->d_flat_all, s);
+        if (u != POWERSGD_OK) return u;
+        hipError_t e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+        slot = std::move(pl);
+      }
+      BucketPlan& pl = *slot;
+      const int nf = static_cast<int>(pl.flat_all.size());
+      double all = 0;
+      for (const FlatTile& f : pl.flat_all) all += static_cast<double>(f.len);
+      powersgd_status r = timed_launch(st, s, K_UNSCALE, all * 2.0, "fp16 check", [&] {
+        return launch_unscale_only(pl.d_flat_all, nf, bucket, inv_loss_scale, found_inf_dev,
+                                   true, s);
+      });
+      if (r != POWERSGD_OK) return r;
+      r = timed_launch(st, s, K_UNSCALE, all * 4.0, "fp16 unscale", [&] {
+        return launch_unscale_only(pl.d_flat_all, nf, bucket, inv_loss_scale, found_inf_dev,
+                                   false, s);
+      });
+      if (r != POWERSGD_OK) return r;
+    }
+    if (is_last) st->iteration += 1;
+    return POWERSGD_OK;
+  }
+
+  // Plan lookup; a memorized bucket must keep its layout.
+  auto it = st->buckets.find(bucket_index);
+  if (it != st->buckets.end() && !same_layout(*it->second, numel, keys)) {
+    if (ef || hp.warm_start)
+      return fail(POWERSGD_ERR_LAYOUT_CHANGED,
+                  "bucket " + std::to_string(bucket_index) + " was called with other views");
+    st->buckets.erase(it);
+    it = st->buckets.end();
+  }
+  if (it == st->buckets.end()) {
+    auto pl = std::make_unique<BucketPlan>();
+    powersgd_status b = build_plan(hp, numel, std::move(keys), *pl);
+    if (b != POWERSGD_OK) return b;
+    b = allocate_plan(*pl, ef, s);
+    if (b != POWERSGD_OK) return b;
+    it = st->buckets.emplace(bucket_index, std::move(pl)).first;
+  }
+  BucketPlan& pl = *it->second;
+  const int R = pl.R;
+  const int nt = static_cast<int>(pl.tensors.size());
+  const bool aligned = (base % 16) == 0;
+  const TensorDesc* td = aligned ? pl.d_td : pl.d_td_scalar;
+  const double ce = static_cast<double>(pl.compressed_elems);
+  const double ue = static_cast<double>(pl.uncompressed_elems);
+  const double eps = hp.orthogonalization_epsilon;
+  const uint64_t bucket_key = static_cast<uint64_t>(bucket_index);
+  powersgd_status r = POWERSGD_OK;
+
+  if (nt > 0) {
+    // Step 3.1: a fresh orthogonalized N(0, 1) draw when there is no warm Q.
+    if (!hp.warm_start || !pl.q_ready) {
+      const uint64_t epoch = hp.warm_start ? 0 : static_cast<uint64_t>(st->iteration);
+      r = timed_launch(st, s, K_QINIT, 0.0, "q_init", [&] {
+        return launch_qinit(R, pl.d_qinit, nt, pl.max_qcount, pl.Q, hp.random_seed,
+                            bucket_key, epoch, s);
+      });
+      if (r != POWERSGD_OK) return r;
+      r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize Q", [&] {
+        return launch_orth(R, pl.d_qjobs, nt, pl.Q, eps, nullptr, s);
+      });
+      if (r != POWERSGD_OK) return r;
+    }
+  }
+  // Pass 1 (+ fp16 inf check of every view).
+  {
+    Pass1Args a{};
+    a.tiles = pl.d_tiles1;
+    a.ntiles = static_cast<int32_t>(pl.tiles1.size());
+    a.ftiles = pl.d_flat_unc;
+    a.nftiles = static_cast<int32_t>(pl.flat_unc.size());
+    a.td = td;
+    a.bucket = bucket;
+    a.E = pl.E;
+    a.Q = pl.Q;
+    a.P = pl.P;
+    a.inv_scale = inv_loss_scale;
+    a.found_inf = found_inf_dev;
+    const double bytes = ce * pass_bytes(K_PASS1, f16, ef) + (f16 ? ue * 2.0 : 0.0);
+    r = timed_launch(st, s, K_PASS1, bytes, "pass 1",
+                     [&] { return launch_pass1(R, pl.rpl, f16, ef, a, s); });
+    if (r != POWERSGD_OK) return r;
+  }
+  if (nt > 0) {
+    // Step 3.4 (the allreduce of P, step 3.3, is the identity on one rank).
+    r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize P", [&] {
+      return launch_orth(R, pl.d_pjobs, nt, pl.P, eps, f16 ? found_inf_dev : nullptr, s);
+    });
+    if (r != POWERSGD_OK) return r;
+    // Step 3.5 (step 3.6 is the identity).
+    Pass2Args a{};
+    a.tiles = pl.d_tiles23;
+    a.ntiles = static_cast<int32_t>(pl.tiles23.size());
+    a.td = td;
+    a.bucket = bucket;
+    a.E = pl.E;
+    a.P = pl.P;
+    a.Q = pl.Q;
+    a.partial = pl.partial;
+    a.counters = pl.counters;
+    a.inv_scale = inv_loss_scale;
+    a.found_inf = found_inf_dev;
+    r = timed_launch(st, s, K_PASS2, ce * pass_bytes(K_PASS2, f16, ef), "pass 2",
+                     [&] { return launch_pass2(R, f16, ef, a, s); });
+    if (r != POWERSGD_OK) return r;
+  }
+  {
+    // Step 3.7 with the error update (+ fp16 unscale of the uncompressed views).
+    Pass3Args a{};
+    a.tiles = pl.d_tiles23;
+    a.ntiles = static_cast<int32_t>(pl.tiles23.size());
+    a.ftiles = pl.d_flat_unc;
+    a.nftiles = static_cast<int32_t>(pl.flat_unc.size());
+    a.td = td;
+    a.bucket = bucket;
+    a.E = pl.E;
+    a.P = pl.P;
+    a.Q = pl.Q;
+    a.inv_scale = inv_loss_scale;
+    a.found_inf = found_inf_dev;
+    const double bytes = ce * pass_bytes(K_PASS3, f16, ef) + (f16 ? ue * 4.0 : 0.0);
+    r = timed_launch(st, s, K_PASS3, bytes, "pass 3",
+                     [&] { return launch_pass3(R, f16, ef, a, s); });
+    if (r != POWERSGD_OK) return r;
+  }
+  pl.q_ready = hp.warm_start != 0;
+
+  st->numel_in += pl.all_elems;
+  st->numel_comm += pl.comm_elems;
+  if (is_last) {
+    if (hp.compression_stats_logging_frequency > 0 && st->iteration >= st->next_log_iteration) {
+      std::fprintf(stderr,
+                   "powersgd: iteration %lld, compression rate %.3f (%lld elements in, "
+                   "%lld communicated)\n",
+                   static_cast<long long>(st->iteration),
+                   st->numel_comm > 0 ? static_cast<double>(st->numel_in) / st->numel_comm : 0.0,
+                   static_cast<long long>(st->numel_in), static_cast<long long>(st->numel_comm));
+      st->next_log_iteration = st->iteration + hp.compression_stats_logging_frequency;
+    }
+    st->iteration += 1;
+  }
+  return POWERSGD_OK;
+}
+
+powersgd_status powersgd_classify_view(const powersgd_hparams* hp, const powersgd_view* view,
+                                       int32_t* compress, int64_t* n, int64_t* m,
+                                       int32_t* rank) {
+  if (!hp || !view) return fail(POWERSGD_ERR_INVALID_ARG, "NULL argument");
+  if (view->ndim < 0 || view->ndim > POWERSGD_MAX_NDIM)
+    return fail(POWERSGD_ERR_INVALID_ARG, "ndim out of range");
+  int64_t size = 1;
+  for (int64_t d = 0; d < view->ndim; ++d) {
+    if (view->shape[d] < 0) return fail(POWERSGD_ERR_INVALID_ARG, "negative dimension");
+    if (view->shape[d] > 0 && size > INT64_MAX / view->shape[d])
+      return fail(POWERSGD_ERR_INVALID_ARG, "size overflows");
+    size *= view->shape[d];
+  }
+  int64_t rows = 0, cols = 0, rk = 0;
+  bool comp = false;
+  if (view->ndim >= 2) {
+    rows = view->shape[0];
+    cols = 1;
+    for (int64_t d = 1; d < view->ndim; ++d) cols *= view->shape[d];
+    rk = std::min<int64_t>(hp->matrix_approximation_rank, std::min(rows, cols));
+    comp = rk >= 1 && should_compress(rows, cols, rk, hp->min_compression_rate);
+  }
+  if (compress) *compress = comp ? 1 : 0;
+  if (n) *n = view->ndim >= 2 ? rows : 0;
+  if (m) *m = view->ndim >= 2 ? cols : 0;
+  if (rank) *rank = comp ? static_cast<int32_t>(rk) : 0;
+  return POWERSGD_OK;
+}
+
+powersgd_status powersgd_get_decisions(powersgd_state* st, int64_t bucket_index, uint8_t* out,
+                                       int32_t nviews) {
+  if (!st || !out) return fail(POWERSGD_ERR_INVALID_ARG, "NULL argument");
+  auto it = st->buckets.find(bucket_index);
+  if (it == st->buckets.end()) return fail(POWERSGD_ERR_NOT_FOUND, "bucket never compressed");
+  const BucketPlan& pl = *it->second;
+  if (nviews != static_cast<int32_t>(pl.decision.size()))
+    return fail(POWERSGD_ERR_INVALID_ARG, "nviews does not match the bucket");
+  std::memcpy(out, pl.decision.data(), pl.decision.size());
+  return POWERSGD_OK;
+}
+
+powersgd_status powersgd_get_view_info(powersgd_state* st, int64_t bucket_index, int32_t view,
+                                       int64_t* n, int64_t* m, int32_t* rank) {
+  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
+  auto it = st->buckets.find(bucket_index);
+  if (it == st->buckets.end()) return fail(POWERSGD_ERR_NOT_FOUND, "bucket never compressed");
+  const BucketPlan& pl = *it->second;
+  if (view < 0 || view >= static_cast<int32_t>(pl.views.size()))
+    return fail(POWERSGD_ERR_INVALID_ARG, "view out of range");
+  if (n) *n = pl.view_n[view];
+  if (m) *m = pl.view_m[view];
+  if (rank) *rank = pl.view_rank[view];
+  return POWERSGD_OK;
+}
+
+static powersgd_status find_tensor(powersgd_state* st, int64_t bucket_index, int32_t view,
+                                   BucketPlan** plp, const TensorDesc** dp) {
+  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
+  auto it = st->buckets.find(bucket_index);
+  if (it == st->buckets.end()) return fail(POWERSGD_ERR_NOT_FOUND, "bucket never compressed");
+  BucketPlan& pl = *it->second;
+  if (view < 0 || view >= static_cast<int32_t>(pl.views.size()))
+    return fail(POWERSGD_ERR_INVALID_ARG, "view out of range");
+  const int32_t t = pl.view_tensor[view];
+  if (t < 0) return fail(POWERSGD_ERR_NOT_FOUND, "view is not compressed");
+  *plp = &pl;
+  *dp = &pl.tensors[t];
+  return POWERSGD_OK;
+}
+
+powersgd_status powersgd_copy_factors(powersgd_state* st, int64_t bucket_index, int32_t view,
+                                      float* p_dev, float* q_dev, void* stream) {
+  BucketPlan* pl = nullptr;
+  const TensorDesc* d = nullptr;
+  powersgd_status r = find_tensor(st, bucket_index, view, &pl, &d);
+  if (r != POWERSGD_OK) return r;
+  HipDeviceGuard guard(st->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t R = pl->R;
+  // P and Q are stored with row stride R; copy the first `rank` columns of each row.
+  if (p_dev) {
+    hipError_t e = hipMemcpy2DAsync(p_dev, d->rank * sizeof(float), pl->P + d->poff,
+                                    R * sizeof(float), d->rank * sizeof(float), d->n,
+                                    hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "copy of P");
+  }
+  if (q_dev) {
+    hipError_t e = hipMemcpy2DAsync(q_dev, d->rank * sizeof(float), pl->Q + d->qoff,
+                                    R * sizeof(float), d->rank * sizeof(float), d->m,
+                                    hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "copy of Q");
+  }
+  return POWERSGD_OK;
+}
+
+powersgd_status powersgd_copy_error(powersgd_state* st, int64_t bucket_index, int32_t view,
+                                    float* e_dev, void* stream) {
+  BucketPlan* pl = nullptr;
+  const TensorDesc* d = nullptr;
+  powersgd_status r = find_tensor(st, bucket_index, view, &pl, &d);
+  if (r != POWERSGD_OK) return r;
+  if (!pl->E) return fail(POWERSGD_ERR_NOT_FOUND, "error feedback is off");
+  if (!e_dev) return fail(POWERSGD_ERR_INVALID_ARG, "e_dev is NULL");
+  HipDeviceGuard guard(st->device);
+  hipError_t e = hipMemcpyAsync(e_dev, pl->E + d->eoff,
+                                static_cast<size_t>(d->n) * d->m * sizeof(float),
+                                hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "copy of E");
+  return POWERSGD_OK;
+}
+
+powersgd_status powersgd_get_stats(powersgd_state* st, int64_t* iteration, int64_t* numel_in,
+                                   int64_t* numel_comm) {
+  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
+  if (iteration) *iteration = st->iteration;
+  if (numel_in) *numel_in = st->numel_in;
+  if (numel_comm) *numel_comm = st->numel_comm;
+  return POWERSGD_OK;
+}
+
+powersgd_status powersgd_set_timing(powersgd_state* st, int32_t enable) {
+  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
+  HipDeviceGuard guard(st->device);
+  collect_timing(st);
+  st->timing = enable != 0;
+  for (int k = 0; k < POWERSGD_NUM_KERNELS; ++k) {
+    st->t_ms[k] = 0.0;
+    st->t_count[k] = 0;
+    st->t_bytes[k] = 0.0;
+  }
+  return POWERSGD_OK;
+}
+
+powersgd_status powersgd_get_kernel_times(powersgd_state* st, double* ms, int64_t* launches,
+                                          double* bytes) {
+  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
+  HipDeviceGuard guard(st->device);
+  collect_timing(st);
+  for (int k = 0; k < POWERSGD_NUM_KERNELS; ++k) {
+    if (ms) ms[k] = st->t_ms[k];
+    if (launches) launches[k] = st->t_count[k];
+    if (bytes) bytes[k] = st->t_bytes[k];
+  }
+  return POWERSGD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,700 @@
+// gfx950 kernels of the PowerSGD bucket-compression step.
+//
+// The step follows "DDP Communication Hooks -- PyTorch 1.11.0", section "PowerSGD
+// Hooks", powerSGD_hook steps 3.2 to 3.7 on one rank (both allreduces are the
+// identity), with error feedback (first warning of that section) and the fp16
+// unscale / inf-check of "torch.cuda.amp -- PyTorch 1.5.0", section "Gradient
+// Scaling". Every kernel covers all tensors of a bucket in one launch, driven by
+// a device table of work items, so a launch has thousands of workgroups.
+//
+//   pass 1  M' = G (+ E); fp32 writes M' back in place; P = M' Q.
+//           One wavefront owns a group of rows and sweeps all columns with 16-byte
+//           loads; per-lane partial dot products are reduced across the wavefront
+//           once per row group (halving butterfly: N values in N - 1 + 6 - log2 N
+//           shuffles). fp16: x * inv_scale and an OR of "not finite" into found_inf.
+//   orth    Modified Gram-Schmidt with epsilon on P (and on the initial Q draw).
+//           One workgroup per matrix; column norm and all dot products of a step
+//           come from one fp64 workgroup reduction.
+//   pass 2  Q = M'^T P. A workgroup owns a 256-column block of a row block; P rows
+//           are wave-uniform (scalar loads); the four wavefronts are combined in
+//           LDS in a fixed order, row blocks through a partial-sum buffer that the
+//           last-arriving workgroup sums in row-block order (deterministic, no
+//           floating-point atomics).
+//   pass 3  M_hat = P Q^T written into the bucket (fp16: round to nearest even),
+//           E = M' - M_hat.
+//   q_init  Philox4x64-10 + Box-Muller draw of the initial Q (counter layout in
+//           the public header's companion documentation).
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace psgd {
+namespace {
+
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n >> 1); }
+
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+// Reduces v[0..N) across the 64 lanes of a wavefront. On return, lane L holds the
+// wave-wide sum of v[L >> (6 - log2 N)]. N is a power of two <= 64.
+template <int N>
+__device__ __forceinline__ float wave_reduce_spread(float (&v)[N], int lane) {
+  constexpr int LOGN = ilog2(N);
+#pragma unroll
+  for (int s = 0; s < LOGN; ++s) {
+    const int mask = 32 >> s;
+    const int half = N >> (s + 1);
+    const bool upper = (lane & mask) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float send = upper ? v[i] : v[i + half];
+      const float keep = upper ? v[i + half] : v[i];
+      v[i] = keep + __shfl_xor(send, mask);
+    }
+  }
+  float x = v[0];
+#pragma unroll
+  for (int mask = (32 >> LOGN); mask >= 1; mask >>= 1) x += __shfl_xor(x, mask);
+  return x;
+}
+
+__device__ __forceinline__ bool half_bits_not_finite(uint16_t h) {
+  return (h & 0x7C00u) == 0x7C00u;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+  return __half2float(__ushort_as_half(h));
+}
+
+// Loads 4 gradient values starting at bucket element idx (valid = elements left in
+// the row); fp16 values are unscaled and checked.
+template <bool F16>
+__device__ __forceinline__ void load_grad4(const void* bucket, int64_t idx, bool vec,
+                                           int valid, float inv_scale, float (&x)[4],
+                                           int& bad) {
+  if constexpr (F16) {
+    const uint16_t* h = static_cast<const uint16_t*>(bucket) + idx;
+    uint16_t raw[4] = {0, 0, 0, 0};
+    if (vec) {
+      const uint2 w = *reinterpret_cast<const uint2*>(h);
+      raw[0] = w.x & 0xFFFFu;
+      raw[1] = w.x >> 16;
+      raw[2] = w.y & 0xFFFFu;
+      raw[3] = w.y >> 16;
+    } else {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (a < valid) raw[a] = h[a];
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      bad |= half_bits_not_finite(raw[a]) ? 1 : 0;
+      x[a] = half_bits_to_float(raw[a]) * inv_scale;
+    }
+  } else {
+    const float* f = static_cast<const float*>(bucket) + idx;
+    if (vec) {
+      const float4 w = *reinterpret_cast<const float4*>(f);
+      x[0] = w.x;
+      x[1] = w.y;
+      x[2] = w.z;
+      x[3] = w.w;
+    } else {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) x[a] = (a < valid) ? f[a] : 0.f;
+    }
+  }
+}
+
+__device__ __forceinline__ void load_f32x4(const float* p, bool vec, int valid,
+                                           float (&x)[4]) {
+  if (vec) {
+    const float4 w = *reinterpret_cast<const float4*>(p);
+    x[0] = w.x;
+    x[1] = w.y;
+    x[2] = w.z;
+    x[3] = w.w;
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) x[a] = (a < valid) ? p[a] : 0.f;
+  }
+}
+
+__device__ __forceinline__ void store_f32x4(float* p, bool vec, int valid,
+                                            const float (&x)[4]) {
+  if (vec) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      if (a < valid) p[a] = x[a];
+  }
+}
+
+__device__ __forceinline__ void store_f16x4(uint16_t* h, bool vec, int valid,
+                                            const float (&x)[4]) {
+  uint16_t o[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) o[a] = __half_as_ushort(__float2half_rn(x[a]));
+  if (vec) {
+    uint2 w;
+    w.x = static_cast<uint32_t>(o[0]) | (static_cast<uint32_t>(o[1]) << 16);
+    w.y = static_cast<uint32_t>(o[2]) | (static_cast<uint32_t>(o[3]) << 16);
+    *reinterpret_cast<uint2*>(h) = w;
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      if (a < valid) h[a] = o[a];
+  }
+}
+
+// q[a][k] = Q[(c + a) * R + k] for rows c..c+3 of a row-major (m x R) block; rows at
+// or beyond m read as zero.
+template <int R>
+__device__ __forceinline__ void load_q_rows(const float* __restrict__ Q, int c, int m,
+                                            float (&q)[4][R]) {
+  if (c + 3 < m) {
+    const float4* p = reinterpret_cast<const float4*>(Q + static_cast<int64_t>(c) * R);
+    if constexpr (R == 1) {
+      const float4 w = p[0];
+      q[0][0] = w.x;
+      q[1][0] = w.y;
+      q[2][0] = w.z;
+      q[3][0] = w.w;
+    } else if constexpr (R == 2) {
+      const float4 w0 = p[0], w1 = p[1];
+      q[0][0] = w0.x;
+      q[0][1] = w0.y;
+      q[1][0] = w0.z;
+      q[1][1] = w0.w;
+      q[2][0] = w1.x;
+      q[2][1] = w1.y;
+      q[3][0] = w1.z;
+      q[3][1] = w1.w;
+    } else {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int k4 = 0; k4 < R / 4; ++k4) {
+          const float4 w = p[a * (R / 4) + k4];
+          q[a][4 * k4 + 0] = w.x;
+          q[a][4 * k4 + 1] = w.y;
+          q[a][4 * k4 + 2] = w.z;
+          q[a][4 * k4 + 3] = w.w;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+      for (int k = 0; k < R; ++k)
+        q[a][k] = (c + a < m) ? Q[static_cast<int64_t>(c + a) * R + k] : 0.f;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------- pass 1
+
+__device__ void f16_check_range(const FlatTile ft, const void* bucket,
+                                int32_t* found_inf) {
+  const uint16_t* h = static_cast<const uint16_t*>(bucket) + ft.start;
+  int bad = 0;
+  for (int64_t i = threadIdx.x; i < ft.len; i += blockDim.x)
+    bad |= half_bits_not_finite(h[i]) ? 1 : 0;
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(found_inf, 1);
+}
+
+template <int R, int RPL, bool F16, bool EF>
+__global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
+  const int lane = threadIdx.x & 63;
+  if (static_cast<int>(blockIdx.x) >= args.ntiles) {
+    if constexpr (F16)
+      f16_check_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.found_inf);
+    return;
+  }
+  const int wave = wave_index();
+  const Tile t = args.tiles[blockIdx.x];
+  const TensorDesc d = args.td[t.tensor];
+  const int m = d.m;
+  const bool vec = d.vec != 0;
+  const int row_end = t.a + t.b;
+  const float* __restrict__ Qt = args.Q + d.qoff;
+  float* __restrict__ Et = args.E + d.eoff;
+  constexpr int N = RPL * R;
+  constexpr int LOGN = ilog2(N);
+  int bad = 0;
+  for (int rg = t.a + wave * RPL; rg < row_end; rg += 4 * RPL) {
+    float acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.f;
+    for (int c = lane * 4; c < m; c += kColBlock) {
+      float q[4][R];
+      load_q_rows<R>(Qt, c, m, q);
+      const int valid = m - c;
+#pragma unroll
+      for (int ri = 0; ri < RPL; ++ri) {
+        const int row = rg + ri;
+        if (row < row_end) {
+          const int64_t off = static_cast<int64_t>(row) * m + c;
+          float x[4];
+          load_grad4<F16>(args.bucket, d.boff + off, vec, valid, args.inv_scale, x, bad);
+          if constexpr (EF) {
+            float e[4];
+            load_f32x4(Et + off, vec, valid, e);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) x[a] += e[a];
+            if constexpr (!F16)
+              store_f32x4(static_cast<float*>(args.bucket) + d.boff + off, vec, valid, x);
+          }
+#pragma unroll
+          for (int k = 0; k < R; ++k)
+            acc[ri * R + k] += x[0] * q[0][k] + x[1] * q[1][k] + x[2] * q[2][k] +
+                               x[3] * q[3][k];
+        }
+      }
+    }
+    const float s = wave_reduce_spread<N>(acc, lane);
+    if ((lane & ((64 >> LOGN) - 1)) == 0) {
+      const int idx = lane >> (6 - LOGN);
+      const int ri = idx / R;
+      const int k = idx % R;
+      const int row = rg + ri;
+      if (row < row_end)
+        args.P[d.poff + static_cast<int64_t>(row) * R + k] = (k < d.rank) ? s : 0.f;
+    }
+  }
+  if constexpr (F16) {
+    if (__any(bad) && lane == 0) atomicOr(args.found_inf, 1);
+  }
+}
+
+// ----------------------------------------------------------------------- pass 2
+
+template <bool F16, bool EF>
+__device__ __forceinline__ void load_mprime4(const void* bucket, const float* Et,
+                                             const TensorDesc& d, int64_t off, bool vec,
+                                             int valid, float inv_scale, float (&x)[4]) {
+  int bad = 0;
+  load_grad4<F16>(bucket, d.boff + off, vec, valid, inv_scale, x, bad);
+  if constexpr (F16 && EF) {
+    float e[4];
+    load_f32x4(Et + off, vec, valid, e);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) x[a] += e[a];
+  }
+  // fp32 with error feedback: the bucket already holds M' (written by pass 1).
+}
+
+template <int R, bool F16, bool EF>
+__global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
+  if (F16 && *args.found_inf) return;
+  __shared__ float red[64 * 4 * R];
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_index();
+  const Tile t = args.tiles[blockIdx.x];
+  const TensorDesc d = args.td[t.tensor];
+  const int m = d.m;
+  const bool vec = d.vec != 0;
+  const int c = t.b * kColBlock + lane * 4;
+  const int r0 = t.a * d.rpb;
+  const int r1 = min(d.n, r0 + d.rpb);
+  const float* __restrict__ Pt = args.P + d.poff;
+  const float* __restrict__ Et = args.E + d.eoff;
+  float acc[4][R];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int k = 0; k < R; ++k) acc[a][k] = 0.f;
+  if (c < m) {
+    const int valid = m - c;
+    for (int row = r0 + wave; row < r1; row += 4) {
+      float x[4];
+      load_mprime4<F16, EF>(args.bucket, Et, d, static_cast<int64_t>(row) * m + c, vec,
+                            valid, args.inv_scale, x);
+      float p[R];
+#pragma unroll
+      for (int k = 0; k < R; ++k) p[k] = Pt[static_cast<int64_t>(row) * R + k];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int k = 0; k < R; ++k) acc[a][k] += x[a] * p[k];
+    }
+  }
+  // Combine the wavefronts in a fixed order: w0 + (w1 + (w2 + w3)).
+  float* mine = red + lane * 4 * R;
+  for (int w = 3; w >= 1; --w) {
+    if (wave == w) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+          mine[a * R + k] = (w == 3) ? acc[a][k] : acc[a][k] + mine[a * R + k];
+    }
+    __syncthreads();
+  }
+  float* Qt = args.Q + d.qoff;
+  if (d.nrb == 1) {
+    if (wave == 0 && c < m) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (c + a < m) {
+#pragma unroll
+          for (int k = 0; k < R; ++k)
+            Qt[static_cast<int64_t>(c + a) * R + k] =
+                (k < d.rank) ? acc[a][k] + mine[a * R + k] : 0.f;
+        }
+    }
+    return;
+  }
+  // Several row blocks: publish this block's partial, the last arrival sums them.
+  constexpr int SLOT = kColBlock * R;
+  float* part = args.partial;
+  if (wave == 0) {
+    float* dst = part + static_cast<int64_t>(d.pslot + t.b * d.nrb + t.a) * SLOT + lane * 4 * R;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int k = 0; k < R; ++k) dst[a * R + k] = acc[a][k] + mine[a * R + k];
+    __threadfence();
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = atomicAdd(args.counters + d.cslot + t.b, 1);
+    s_last = (prev == d.nrb - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const float* src = part + static_cast<int64_t>(d.pslot + t.b * d.nrb) * SLOT;
+  for (int f = threadIdx.x; f < SLOT; f += kThreads) {
+    const int col = t.b * kColBlock + f / R;
+    const int k = f % R;
+    if (col < m) {
+      float s = 0.f;
+      for (int rb = 0; rb < d.nrb; ++rb) s += src[static_cast<int64_t>(rb) * SLOT + f];
+      Qt[static_cast<int64_t>(col) * R + k] = (k < d.rank) ? s : 0.f;
+    }
+  }
+  if (threadIdx.x == 0) atomicExch(args.counters + d.cslot + t.b, 0);
+}
+
+// ----------------------------------------------------------------------- pass 3
+
+__device__ void f16_unscale_range(const FlatTile ft, void* bucket, float inv_scale) {
+  uint16_t* h = static_cast<uint16_t*>(bucket) + ft.start;
+  for (int64_t i = threadIdx.x; i < ft.len; i += blockDim.x)
+    h[i] = __half_as_ushort(__float2half_rn(half_bits_to_float(h[i]) * inv_scale));
+}
+
+template <int R, bool F16, bool EF>
+__global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
+  if (F16 && *args.found_inf) return;
+  if (static_cast<int>(blockIdx.x) >= args.ntiles) {
+    if constexpr (F16)
+      f16_unscale_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.inv_scale);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_index();
+  const Tile t = args.tiles[blockIdx.x];
+  const TensorDesc d = args.td[t.tensor];
+  const int m = d.m;
+  const bool vec = d.vec != 0;
+  const int c = t.b * kColBlock + lane * 4;
+  if (c >= m) return;
+  const int valid = m - c;
+  const int r0 = t.a * d.rpb;
+  const int r1 = min(d.n, r0 + d.rpb);
+  const float* __restrict__ Pt = args.P + d.poff;
+  float* __restrict__ Et = args.E + d.eoff;
+  float q[4][R];
+  load_q_rows<R>(args.Q + d.qoff, c, m, q);
+  for (int row = r0 + wave; row < r1; row += 4) {
+    const int64_t off = static_cast<int64_t>(row) * m + c;
+    float x[4];
+    load_mprime4<F16, EF>(args.bucket, Et, d, off, vec, valid, args.inv_scale, x);
+    float p[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) p[k] = Pt[static_cast<int64_t>(row) * R + k];
+    float mh[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < R; ++k) s += p[k] * q[a][k];
+      mh[a] = s;
+    }
+    if constexpr (F16)
+      store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, vec, valid, mh);
+    else
+      store_f32x4(static_cast<float*>(args.bucket) + d.boff + off, vec, valid, mh);
+    if constexpr (EF) {
+      float e[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) e[a] = x[a] - mh[a];
+      store_f32x4(Et + off, vec, valid, e);
+    }
+  }
+}
+
+// ------------------------------------------------------------ orthogonalization
+
+template <int R>
+__global__ void __launch_bounds__(kOrthThreads)
+    k_orth(const OrthJob* __restrict__ jobs, float* __restrict__ base, double eps,
+           const int32_t* __restrict__ found_inf) {
+  if (found_inf != nullptr && *found_inf) return;
+  constexpr int NW = kOrthThreads / 64;
+  __shared__ double red[NW][R];
+  __shared__ double tot[R];
+  const OrthJob j = jobs[blockIdx.x];
+  float* X = base + j.off;
+  const int rows = j.rows;
+  const int rank = j.rank;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int i = 0; i < rank; ++i) {
+    // s[k] = <x_i, x_k> for k >= i, in fp64 (the products of fp32 values are exact)
+    double s[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) s[k] = 0.0;
+    for (int row = threadIdx.x; row < rows; row += kOrthThreads) {
+      const float* xr = X + static_cast<int64_t>(row) * R;
+      const double xi = xr[i];
+#pragma unroll
+      for (int k = 0; k < R; ++k)
+        if (k >= i && k < rank) s[k] += xi * static_cast<double>(xr[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      if (k >= i && k < rank) {
+        double v = s[k];
+#pragma unroll
+        for (int mask = 32; mask >= 1; mask >>= 1) v += __shfl_xor(v, mask);
+        if (lane == 0) red[wave][k] = v;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {
+      const int k = threadIdx.x;
+      if (k >= i && k < rank) {
+        double v = 0.0;
+        for (int w = 0; w < NW; ++w) v += red[w][k];
+        tot[k] = v;
+      }
+    }
+    __syncthreads();
+    // q_i = x_i / (|x_i| + eps); x_k -= <q_i, x_k> q_i with <q_i, x_k> = s_k / (|x_i| + eps)
+    const double inv = 1.0 / (sqrt(tot[i]) + eps);
+    float coef[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+      coef[k] = (k > i && k < rank) ? static_cast<float>(tot[k] * inv) : 0.f;
+    for (int row = threadIdx.x; row < rows; row += kOrthThreads) {
+      float* xr = X + static_cast<int64_t>(row) * R;
+      const float qi = static_cast<float>(static_cast<double>(xr[i]) * inv);
+      xr[i] = qi;
+#pragma unroll
+      for (int k = 0; k < R; ++k)
+        if (k > i && k < rank) xr[k] -= coef[k] * qi;
+    }
+    __syncthreads();
+  }
+}
+
+// -------------------------------------------------------------------- q draw
+
+constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+
+// Philox4x64 with 10 rounds (Salmon et al., SC 2011).
+__device__ __forceinline__ void philox4x64_10(uint64_t (&x)[4], uint64_t k0, uint64_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += kPhiloxW0;
+      k1 += kPhiloxW1;
+    }
+    const uint64_t hi0 = __umul64hi(kPhiloxM0, x[0]);
+    const uint64_t lo0 = kPhiloxM0 * x[0];
+    const uint64_t hi1 = __umul64hi(kPhiloxM1, x[2]);
+    const uint64_t lo1 = kPhiloxM1 * x[2];
+    const uint64_t y0 = hi1 ^ x[1] ^ k0;
+    const uint64_t y2 = hi0 ^ x[3] ^ k1;
+    x[0] = y0;
+    x[1] = lo1;
+    x[2] = y2;
+    x[3] = lo0;
+  }
+}
+
+// Box-Muller in fp64: u in (0, 1] from the even word, v in [0, 1) from the odd word.
+__device__ __forceinline__ void box_muller(uint64_t we, uint64_t wo, double& z0,
+                                           double& z1) {
+  const double u = (static_cast<double>(we >> 11) + 1.0) * 0x1p-53;
+  const double v = static_cast<double>(wo >> 11) * 0x1p-53;
+  const double radius = sqrt(-2.0 * log(u));
+  const double angle = (2.0 * 3.141592653589793) * v;
+  z0 = radius * cos(angle);
+  z1 = radius * sin(angle);
+}
+
+__global__ void __launch_bounds__(256)
+    k_qinit(const QInitJob* __restrict__ jobs, float* __restrict__ Q, int R, uint64_t seed,
+            uint64_t bucket_key, uint64_t epoch) {
+  const QInitJob j = jobs[blockIdx.y];
+  const int64_t count = static_cast<int64_t>(j.m) * j.rank;
+  const int64_t nblocks = (count + 3) / 4;
+  for (int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; b < nblocks;
+       b += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    uint64_t w[4] = {static_cast<uint64_t>(b), static_cast<uint64_t>(j.view), epoch, 0};
+    philox4x64_10(w, seed, bucket_key);
+    double z[4];
+    box_muller(w[0], w[1], z[0], z[1]);
+    box_muller(w[2], w[3], z[2], z[3]);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int64_t e = 4 * b + a;
+      if (e < count) {
+        const int64_t row = e / j.rank;
+        const int k = static_cast<int>(e % j.rank);
+        Q[j.qoff + row * R + k] = static_cast<float>(z[a]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------- fp16 pass-through only
+
+__global__ void __launch_bounds__(256)
+    k_f16_check(const FlatTile* __restrict__ ft, const void* bucket, int32_t* found_inf) {
+  f16_check_range(ft[blockIdx.x], bucket, found_inf);
+}
+
+__global__ void __launch_bounds__(256)
+    k_f16_unscale(const FlatTile* __restrict__ ft, void* bucket, float inv_scale,
+                  const int32_t* __restrict__ found_inf) {
+  if (*found_inf) return;
+  f16_unscale_range(ft[blockIdx.x], bucket, inv_scale);
+}
+
+// ------------------------------------------------------------------ dispatch
+
+template <int R>
+hipError_t pass1_r(int rpl, bool f16, bool ef, const Pass1Args& a, hipStream_t s) {
+  const dim3 grid(a.ntiles + (f16 ? a.nftiles : 0));
+  if (grid.x == 0) return hipSuccess;
+#define PSGD_P1(RPL)                                                                      \
+  if (rpl == RPL) {                                                                       \
+    if (f16 && ef) k_pass1<R, RPL, true, true><<<grid, kThreads, 0, s>>>(a);              \
+    else if (f16) k_pass1<R, RPL, true, false><<<grid, kThreads, 0, s>>>(a);              \
+    else if (ef) k_pass1<R, RPL, false, true><<<grid, kThreads, 0, s>>>(a);               \
+    else k_pass1<R, RPL, false, false><<<grid, kThreads, 0, s>>>(a);                      \
+    return hipGetLastError();                                                             \
+  }
+  if constexpr (R * 8 <= 64) { PSGD_P1(8) }
+  if constexpr (R * 4 <= 64) { PSGD_P1(4) }
+  if constexpr (R * 2 <= 64) { PSGD_P1(2) }
+  PSGD_P1(1)
+#undef PSGD_P1
+  return hipErrorInvalidValue;
+}
+
+template <int R>
+hipError_t pass2_r(bool f16, bool ef, const Pass2Args& a, hipStream_t s) {
+  if (a.ntiles == 0) return hipSuccess;
+  const dim3 grid(a.ntiles);
+  if (f16 && ef) k_pass2<R, true, true><<<grid, kThreads, 0, s>>>(a);
+  else if (f16) k_pass2<R, true, false><<<grid, kThreads, 0, s>>>(a);
+  else if (ef) k_pass2<R, false, true><<<grid, kThreads, 0, s>>>(a);
+  else k_pass2<R, false, false><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int R>
+hipError_t pass3_r(bool f16, bool ef, const Pass3Args& a, hipStream_t s) {
+  const dim3 grid(a.ntiles + (f16 ? a.nftiles : 0));
+  if (grid.x == 0) return hipSuccess;
+  if (f16 && ef) k_pass3<R, true, true><<<grid, kThreads, 0, s>>>(a);
+  else if (f16) k_pass3<R, true, false><<<grid, kThreads, 0, s>>>(a);
+  else if (ef) k_pass3<R, false, true><<<grid, kThreads, 0, s>>>(a);
+  else k_pass3<R, false, false><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int pass1_rows_per_lane(int R) {
+  switch (R) {
+    case 1: return 8;
+    case 2: return 8;
+    case 4: return 4;
+    case 8: return 4;
+    case 16: return 2;
+    default: return 1;
+  }
+}
+
+#define PSGD_RANK_SWITCH(R, ...)                    \
+  switch (R) {                                      \
+    case 1: { constexpr int RR = 1; __VA_ARGS__; }   \
+    case 2: { constexpr int RR = 2; __VA_ARGS__; }   \
+    case 4: { constexpr int RR = 4; __VA_ARGS__; }   \
+    case 8: { constexpr int RR = 8; __VA_ARGS__; }   \
+    case 16: { constexpr int RR = 16; __VA_ARGS__; } \
+    case 32: { constexpr int RR = 32; __VA_ARGS__; } \
+    default: return hipErrorInvalidValue;           \
+  }
+
+hipError_t launch_pass1(int R, int rpl, bool f16, bool ef, const Pass1Args& a,
+                        hipStream_t s) {
+  PSGD_RANK_SWITCH(R, return pass1_r<RR>(rpl, f16, ef, a, s))
+}
+
+hipError_t launch_pass2(int R, bool f16, bool ef, const Pass2Args& a, hipStream_t s) {
+  PSGD_RANK_SWITCH(R, return pass2_r<RR>(f16, ef, a, s))
+}
+
+hipError_t launch_pass3(int R, bool f16, bool ef, const Pass3Args& a, hipStream_t s) {
+  PSGD_RANK_SWITCH(R, return pass3_r<RR>(f16, ef, a, s))
+}
+
+hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, float* base, double eps,
+                       const int32_t* found_inf, hipStream_t s) {
+  if (njobs == 0) return hipSuccess;
+  PSGD_RANK_SWITCH(R, {
+    k_orth<RR><<<dim3(njobs), kOrthThreads, 0, s>>>(jobs, base, eps, found_inf);
+    return hipGetLastError();
+  })
+}
+
+hipError_t launch_qinit(int R, const QInitJob* jobs, int njobs, int64_t max_count,
+                        float* Q, uint64_t seed, uint64_t bucket_key, uint64_t epoch,
+                        hipStream_t s) {
+  if (njobs == 0) return hipSuccess;
+  const int64_t blocks = ((max_count + 3) / 4 + 255) / 256;
+  const dim3 grid(static_cast<unsigned>(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks)),
+                  static_cast<unsigned>(njobs));
+  k_qinit<<<grid, 256, 0, s>>>(jobs, Q, R, seed, bucket_key, epoch);
+  return hipGetLastError();
+}
+
+hipError_t launch_unscale_only(const FlatTile* ftiles, int nftiles, void* bucket,
+                               float inv_scale, int32_t* found_inf, bool check,
+                               hipStream_t s) {
+  if (nftiles == 0) return hipSuccess;
+  if (check)
+    k_f16_check<<<dim3(nftiles), 256, 0, s>>>(ftiles, bucket, found_inf);
+  else
+    k_f16_unscale<<<dim3(nftiles), 256, 0, s>>>(ftiles, bucket, inv_scale, found_inf);
+  return hipGetLastError();
+}
+
+}  // namespace psgd
