@@ -1,0 +1,228 @@
+"""Benchmark of PowerSGD bucket compression on one MI355X.
+
+One step = one powersgd_compress_bucket call on a fresh synthetic gradient bucket
+(every pass of the method: error-feedback add, P = M'Q, Gram-Schmidt, Q = M'^T P,
+decompress + error update). Buckets are generated on the GPU before timing, one per
+step, so inputs are resident in HBM when the timed region starts.
+
+value = whole-job gradient throughput: bucket bytes per step / time per step.
+roofline = the dominant kernel's algorithmic bytes per launch / its mean launch
+duration (HIP events recorded by the library on the launch stream during the
+timed region), against the 8 TB/s HBM peak.
+cpu_baseline = the fp64 oracle timed on the host on a bounded sample of the same
+workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "gradient GB/s compressed per PowerSGD step + % of HBM roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_CONFIG = 1
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "internal.h", "host.cpp"):
+        with open(os.path.join(ROOT, "rank_gradient_compression_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/), if the
+    measurement was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, budget_s: float = 20.0):
+    """The oracle, as it stands, on whole steps of the same workload for ~budget_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from synthetic import BucketGenerator
+
+    gen = BucketGenerator(cfg, "cpu")
+    hp = oracle.HParams(**{k: v for k, v in cfg.hparams.items()
+                           if k in oracle.HParams.__dataclass_fields__})
+    st = oracle.OracleState(hp)
+    views = cfg.views()
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    times = []
+    t_start = time.perf_counter()
+    step = 0
+    while True:
+        bucket = gen.bucket(step)
+        arr = bucket.numpy()
+        scale = cfg.loss_scale if cfg.dtype == "f16" else 1.0
+        t0 = time.perf_counter()
+        st.compress_bucket(arr, views, inv_loss_scale=1.0 / scale)
+        times.append(time.perf_counter() - t0)
+        step += 1
+        if time.perf_counter() - t_start > budget_s or step >= cfg.steps:
+            break
+    per_step = float(np.median(times))
+    gbs = cfg.numel * cfg.element_bytes / per_step / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} whole steps of the {cfg.name} bucket "
+                      f"({cfg.numel} elements), median {per_step:.3f} s/step, fp64 numpy "
+                      f"with {threads} BLAS threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="skip the per-kernel event timing (no roofline object)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        eprint("bench.py measures one GPU only: the compression step runs on one rank and "
+               "this build issues no collectives; run with --gpus 1.")
+        return 2
+
+    import torch
+
+    from rank_gradient_compression_amd import PowerSGDState
+    from synthetic import CONFIGS, BucketGenerator
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    bucket_bytes = cfg.numel * cfg.element_bytes
+    total = args.steps + args.warmup
+    gen = BucketGenerator(cfg, "cuda")
+
+    # One distinct bucket per step while it fits in a third of free HBM; beyond that
+    # the pool is reused (the kernels' work does not depend on the values).
+    free, _ = torch.cuda.mem_get_info()
+    pool_n = max(1, min(total, int(free * 0.33) // bucket_bytes))
+    eprint(f"[bench] {cfg.name}: {cfg.numel} elements, {bucket_bytes / 1e6:.1f} MB per bucket, "
+           f"{pool_n} distinct buckets for {total} steps")
+    # Benchmark steps carry the workload's random inf draws only (the forced inf step
+    # belongs to the correctness runs).
+    pool = [gen.bucket(i, forced=False) for i in range(pool_n)]
+    views = cfg.views()
+    hp = dict(cfg.hparams)
+    hp["compression_stats_logging_frequency"] = 0
+    st = PowerSGDState(device=0, **hp)
+    stream = torch.cuda.current_stream()
+    found = torch.zeros(1, dtype=torch.int32, device=dev)
+    inv = 1.0 / cfg.loss_scale if cfg.dtype == "f16" else 1.0
+
+    def run(i):
+        if cfg.dtype == "f16":
+            found.zero_()      # a new iteration: GradScaler starts from "no inf found"
+        st.compress_bucket(pool[i % pool_n], views, inv_loss_scale=inv,
+                           found_inf=found if cfg.dtype == "f16" else None, stream=stream)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    eprint("[bench] warmup done")
+
+    st.set_timing(not args.no_kernel_timing)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = bucket_bytes / (ms_per_step * 1e-3) / 1e9
+
+    roofline = None
+    if not args.no_kernel_timing:
+        kt = st.kernel_times()
+        for name, ms, n, by in kt:
+            if n:
+                eprint(f"[bench] kernel {name:24s} launches {n:6d}  mean {ms / n * 1e3:9.2f} us"
+                       f"  algorithmic {by / n / 1e6:9.2f} MB/launch"
+                       + (f"  {by / (ms * 1e-3) / 1e9:8.1f} GB/s" if by > 0 else ""))
+        streaming = [(ms, name, n, by) for name, ms, n, by in kt if by > 0 and n > 0]
+        ms, name, n, by = max(streaming)
+        avg_s = ms * 1e-3 / n
+        achieved = by / n / avg_s / 1e9
+        sum_ms = sum(x[1] for x in kt)
+        eprint(f"[bench] kernels total {sum_ms / args.steps * 1e3:.1f} us/step of "
+               f"{ms_per_step * 1e3:.1f} us/step wall")
+        traffic = load_traffic(name, cfg.name)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "kernel": name,
+                    "mean_launch_us": round(avg_s * 1e6, 3),
+                    "algorithmic_bytes_per_launch": by / n}
+    st.close()
+    del pool
+    torch.cuda.empty_cache()
+
+    from rank_gradient_compression_amd import powersgd as api
+    hp_c = api.powersgd_hparams_init()
+    hp_c.matrix_approximation_rank = cfg.hparams["matrix_approximation_rank"]
+    hp_c.min_compression_rate = cfg.hparams["min_compression_rate"]
+    comp_elems = 0
+    for _, shp in views:
+        comp, n, m, _r = api.powersgd_classify_view(hp_c, shp)
+        comp_elems += n * m if comp else 0
+    per_elt = 28 if cfg.dtype == "f32" else 24
+    algo_bytes = comp_elems * per_elt + (0 if cfg.dtype == "f32" else
+                                         (cfg.numel - comp_elems) * 6)
+    step_frac = algo_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded low-rank + noise gradients, model-shaped views)",
+        "config": {"workload": cfg.name, "bucket_bytes": bucket_bytes,
+                   "views": len(views), "compressed_elements": comp_elems,
+                   "matrix_approximation_rank": cfg.hparams["matrix_approximation_rank"],
+                   "step_hbm_roofline_frac": round(step_frac, 4),
+                   "step_algorithmic_bytes": algo_bytes},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        eprint("[bench] timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -108,29 +108,28 @@ struct BucketPlan {
   std::vector<int64_t> view_n, view_m;  // matrix shape (0 for vectors)
   std::vector<int32_t> view_rank;
   int R = 1;
-  int rpl = 1;
   int64_t compressed_elems = 0;
   int64_t uncompressed_elems = 0;
   int64_t comm_elems = 0;
   int64_t all_elems = 0;
   std::vector<TensorDesc> tensors;
-  std::vector<Tile> tiles1, tiles23;
+  std::vector<Tile> tiles1, tiles23, tiles2r;
   std::vector<FlatTile> flat_unc, flat_all;
   std::vector<OrthJob> pjobs, qjobs;
   std::vector<QInitJob> qinit;
   int64_t max_qcount = 0;
-  int64_t e_floats = 0, p_floats = 0, q_floats = 0, partial_floats = 0, ncounters = 0;
+  int64_t e_floats = 0, p_floats = 0, q_floats = 0, partial_floats = 0;
 
   // device memory
   float* E = nullptr;
   float* P = nullptr;
   float* Q = nullptr;
   float* partial = nullptr;
-  int32_t* counters = nullptr;
   TensorDesc* d_td = nullptr;         // rows vector-aligned where possible
   TensorDesc* d_td_scalar = nullptr;  // same with every vec flag cleared
-  Tile* d_tiles1 = nullptr;
-  Tile* d_tiles23 = nullptr;
+  Tile* d_tiles1 = nullptr;   // pass 1 row blocks
+  Tile* d_tiles23 = nullptr;  // pass 2 / pass 3 (row block, column block)
+  Tile* d_tiles2r = nullptr;  // pass-2 partial sums (column blocks of split tensors)
   FlatTile* d_flat_unc = nullptr;
   FlatTile* d_flat_all = nullptr;
   OrthJob* d_pjobs = nullptr;
@@ -140,14 +139,13 @@ struct BucketPlan {
   bool q_ready = false;
 
   void release() {
-    void* ptrs[] = {E, P, Q, partial, counters, d_td, d_td_scalar, d_tiles1, d_tiles23,
+    void* ptrs[] = {E, P, Q, partial, d_td, d_td_scalar, d_tiles1, d_tiles23, d_tiles2r,
                     d_flat_unc, d_flat_all, d_pjobs, d_qjobs, d_qinit};
     for (void* p : ptrs)
       if (p) (void)hipFree(p);
     E = P = Q = partial = nullptr;
-    counters = nullptr;
     d_td = d_td_scalar = nullptr;
-    d_tiles1 = d_tiles23 = nullptr;
+    d_tiles1 = d_tiles23 = d_tiles2r = nullptr;
     d_flat_unc = d_flat_all = nullptr;
     d_pjobs = d_qjobs = nullptr;
     d_qinit = nullptr;
@@ -192,7 +190,9 @@ struct powersgd_state {
 
 namespace {
 
-enum KernelKind { K_QINIT = 0, K_PASS1 = 1, K_ORTH = 2, K_PASS2 = 3, K_PASS3 = 4, K_UNSCALE = 5 };
+enum KernelKind {
+  K_QINIT = 0, K_PASS1 = 1, K_ORTH = 2, K_PASS2 = 3, K_PASS3 = 4, K_UNSCALE = 5, K_PASS2R = 6
+};
 
 hipEvent_t take_event(powersgd_state* st) {
   if (!st->free_events.empty()) {
@@ -322,15 +322,15 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
     add_flat(pl.flat_all, k.offset, size);
   }
   pl.R = pow2_ceil(max_rank);
-  pl.rpl = pass1_rows_per_lane(pl.R);
   const int R = pl.R;
 
   // Work-item size: enough workgroups to fill 256 CUs several times over, and no
   // more than 64K elements (256 KB of fp32) each.
   const int64_t target =
-      std::min<int64_t>(1 << 16, std::max<int64_t>(1 << 14, pl.compressed_elems / 2048));
+      std::min<int64_t>(1 << 16, std::max<int64_t>(1 << 13, pl.compressed_elems / 2048));
+  const int64_t unroll1 = pass1_unroll(R);
   int64_t eoff = 0, poff = 0, qoff = 0;
-  int32_t pslot = 0, cslot = 0;
+  int32_t pslot = 0;
   for (size_t v = 0; v < nv; ++v) {
     if (!pl.decision[v]) continue;
     TensorDesc d{};
@@ -346,28 +346,32 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
     eoff += round_up(static_cast<int64_t>(d.n) * d.m, 64);
     poff += round_up(static_cast<int64_t>(d.n) * R, 64);
     qoff += round_up(static_cast<int64_t>(d.m) * R, 64);
-    // pass 2 / pass 3 blocks
-    d.ncb = static_cast<int32_t>((d.m + kColBlock - 1) / kColBlock);
+    const int32_t ti = static_cast<int32_t>(pl.tensors.size());
+    // pass 1: whole rows; slots of lprw threads sweep 4 * lprw columns at a time
+    d.lprw = pow2_ceil(static_cast<int>((std::min<int64_t>(d.m, 4 * kThreads) + 3) / 4));
+    {
+      const int64_t slots = kThreads / d.lprw;
+      int64_t rows = round_up(std::max<int64_t>(1, (target + d.m - 1) / d.m), slots * unroll1);
+      rows = std::min<int64_t>(rows, round_up(d.n, slots));
+      d.rpb1 = static_cast<int32_t>(rows);
+      for (int64_t r0 = 0, rb = 0; r0 < d.n; r0 += rows, ++rb)
+        pl.tiles1.push_back(Tile{ti, static_cast<int32_t>(rb), 0, 0});
+    }
+    // pass 2 / pass 3: (row block) x (256-column block)
     const int64_t width = std::min<int64_t>(d.m, kColBlock);
-    int64_t rpb = round_up(std::max<int64_t>(4, (target + width - 1) / width), 4);
-    rpb = std::min<int64_t>(rpb, round_up(d.n, 4));
+    d.lpr = pow2_ceil(static_cast<int>((width + 3) / 4));
+    const int64_t rpw = 64 / d.lpr;
+    int64_t rpb = round_up(std::max<int64_t>(1, (target + width - 1) / width), 16 * rpw);
+    rpb = std::min<int64_t>(rpb, round_up(d.n, 4 * rpw));
     d.rpb = static_cast<int32_t>(rpb);
     d.nrb = static_cast<int32_t>((d.n + rpb - 1) / rpb);
+    d.ncb = static_cast<int32_t>((d.m + kColBlock - 1) / kColBlock);
     if (d.nrb > 1) {
       d.pslot = pslot;
-      d.cslot = cslot;
       pslot += d.nrb * d.ncb;
-      cslot += d.ncb;
+      for (int32_t cb = 0; cb < d.ncb; ++cb) pl.tiles2r.push_back(Tile{ti, 0, cb, 0});
     }
-    const int32_t ti = static_cast<int32_t>(pl.tensors.size());
     pl.view_tensor[v] = ti;
-    // pass 1 row tiles
-    const int64_t group = 4 * static_cast<int64_t>(pl.rpl);
-    int64_t rpt = round_up(std::max<int64_t>(1, (target + d.m - 1) / d.m), group);
-    rpt = std::min<int64_t>(rpt, round_up(d.n, group));
-    for (int64_t r0 = 0; r0 < d.n; r0 += rpt)
-      pl.tiles1.push_back(Tile{ti, static_cast<int32_t>(r0),
-                               static_cast<int32_t>(std::min<int64_t>(rpt, d.n - r0)), 0});
     for (int32_t cb = 0; cb < d.ncb; ++cb)
       for (int32_t rb = 0; rb < d.nrb; ++rb) pl.tiles23.push_back(Tile{ti, rb, cb, 0});
     pl.pjobs.push_back(OrthJob{d.poff, d.n, d.rank});
@@ -380,7 +384,6 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
   pl.p_floats = poff;
   pl.q_floats = qoff;
   pl.partial_floats = static_cast<int64_t>(pslot) * kColBlock * R;
-  pl.ncounters = cslot;
   return POWERSGD_OK;
 }
 
@@ -397,7 +400,7 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   ok = ok && alloc(reinterpret_cast<void**>(&pl.P), pl.p_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.Q), pl.q_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.partial), pl.partial_floats * sizeof(float));
-  ok = ok && alloc(reinterpret_cast<void**>(&pl.counters), pl.ncounters * sizeof(int32_t));
+
   if (!ok) {
     pl.release();
     return fail(POWERSGD_ERR_OOM, "device allocation of the bucket state failed");
@@ -406,8 +409,7 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   if (pl.E && e == hipSuccess) e = hipMemsetAsync(pl.E, 0, pl.e_floats * sizeof(float), s);
   if (pl.P && e == hipSuccess) e = hipMemsetAsync(pl.P, 0, pl.p_floats * sizeof(float), s);
   if (pl.Q && e == hipSuccess) e = hipMemsetAsync(pl.Q, 0, pl.q_floats * sizeof(float), s);
-  if (pl.counters && e == hipSuccess)
-    e = hipMemsetAsync(pl.counters, 0, pl.ncounters * sizeof(int32_t), s);
+
   if (e != hipSuccess) {
     pl.release();
     return hip_fail(e, "hipMemsetAsync of the bucket state");
@@ -419,6 +421,7 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   if (st == POWERSGD_OK) st = upload(scalar, &pl.d_td_scalar, s);
   if (st == POWERSGD_OK) st = upload(pl.tiles1, &pl.d_tiles1, s);
   if (st == POWERSGD_OK) st = upload(pl.tiles23, &pl.d_tiles23, s);
+  if (st == POWERSGD_OK) st = upload(pl.tiles2r, &pl.d_tiles2r, s);
   if (st == POWERSGD_OK) st = upload(pl.flat_unc, &pl.d_flat_unc, s);
   if (st == POWERSGD_OK) st = upload(pl.flat_all, &pl.d_flat_all, s);
   if (st == POWERSGD_OK) st = upload(pl.pjobs, &pl.d_pjobs, s);
@@ -489,9 +492,9 @@ const char* powersgd_status_string(powersgd_status s) {
 const char* powersgd_last_error(void) { return g_last_error.c_str(); }
 
 const char* powersgd_kernel_name(int32_t kind) {
-  static const char* names[POWERSGD_NUM_KERNELS] = {"q_init", "pass1_mq", "orthogonalize",
-                                                    "pass2_mtp", "pass3_decompress_error",
-                                                    "unscale_only"};
+  static const char* names[POWERSGD_NUM_KERNELS] = {
+      "q_init", "pass1_mq", "orthogonalize", "pass2_mtp", "pass3_decompress_error",
+      "unscale_only", "pass2_reduce"};
   if (kind < 0 || kind >= POWERSGD_NUM_KERNELS) return "";
   return names[kind];
 }
@@ -660,7 +663,7 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
     a.found_inf = found_inf_dev;
     const double bytes = ce * pass_bytes(K_PASS1, f16, ef) + (f16 ? ue * 2.0 : 0.0);
     r = timed_launch(st, s, K_PASS1, bytes, "pass 1",
-                     [&] { return launch_pass1(R, pl.rpl, f16, ef, a, s); });
+                     [&] { return launch_pass1(R, f16, ef, a, s); });
     if (r != POWERSGD_OK) return r;
   }
   if (nt > 0) {
@@ -679,12 +682,23 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
     a.P = pl.P;
     a.Q = pl.Q;
     a.partial = pl.partial;
-    a.counters = pl.counters;
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
     r = timed_launch(st, s, K_PASS2, ce * pass_bytes(K_PASS2, f16, ef), "pass 2",
                      [&] { return launch_pass2(R, f16, ef, a, s); });
     if (r != POWERSGD_OK) return r;
+    if (!pl.tiles2r.empty()) {
+      Pass2ReduceArgs b{};
+      b.tiles = pl.d_tiles2r;
+      b.ntiles = static_cast<int32_t>(pl.tiles2r.size());
+      b.td = td;
+      b.partial = pl.partial;
+      b.Q = pl.Q;
+      b.found_inf = f16 ? found_inf_dev : nullptr;
+      r = timed_launch(st, s, K_PASS2R, 0.0, "pass 2 reduce",
+                       [&] { return launch_pass2_reduce(R, b, s); });
+      if (r != POWERSGD_OK) return r;
+    }
   }
   {
     // Step 3.7 with the error update (+ fp16 unscale of the uncompressed views).

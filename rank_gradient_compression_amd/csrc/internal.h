@@ -15,6 +15,14 @@ constexpr int kThreads = 256;
 constexpr int kOrthThreads = 512;
 
 // One compressed matrix of the bucket (n x m, row-major inside the flat bucket).
+//
+// Pass 1 work items are row blocks of rpb1 full rows: the 256 threads of a
+// workgroup form 256 / lprw row slots of lprw threads, a thread owning 4 consecutive
+// columns per sweep of 4 * lprw columns, so every dot product stays inside one
+// workgroup. Pass 2 and pass 3 work items are (row block of rpb rows) x (256-column
+// block): a wavefront's 64 lanes form 64 / lpr row slots of lpr lanes, a lane owning
+// 4 consecutive columns. Pass 2 writes one partial Q per row block when nrb > 1;
+// a separate reduction sums them in row-block order.
 struct TensorDesc {
   int64_t boff;   // first element of the view in the bucket
   int64_t eoff;   // first float of its error memory (multiple of 4)
@@ -24,15 +32,17 @@ struct TensorDesc {
   int32_t rank;   // columns of P and Q in use (<= R); the rest are kept at zero
   int32_t vec;    // 1: m % 4 == 0 and rows start 16-byte aligned in the bucket
   int32_t view;   // index of the view in the bucket (Q draw counter word)
-  int32_t rpb;    // rows per row block in pass 2 / pass 3
-  int32_t nrb;    // row blocks in pass 2 / pass 3
-  int32_t ncb;    // 256-column blocks in pass 2 / pass 3
-  int32_t pslot;  // first partial-sum slot of pass 2 (nrb * ncb slots when nrb > 1)
-  int32_t cslot;  // first arrival counter of pass 2 (ncb counters when nrb > 1)
+  int32_t lprw;   // pass 1: threads per row slot (power of two, <= 256)
+  int32_t rpb1;   // pass 1: rows per row block
+  int32_t lpr;    // pass 2/3: lanes per row slot (power of two, <= 64)
+  int32_t rpb;    // pass 2/3: rows per row block
+  int32_t nrb;    // pass 2/3: row blocks
+  int32_t ncb;    // pass 2/3: 256-column blocks
+  int32_t pslot;  // first pass-2 partial slot (nrb * ncb slots when nrb > 1)
 };
 
-// Pass 1 work item: rows [row0, row0 + nrows) of one tensor, all columns.
-// Pass 2 / pass 3 work item: row block `a`, column block `b` of one tensor.
+// Work item of the streaming passes: row block `a` (and column block `b` in
+// passes 2 and 3) of a tensor.
 struct Tile {
   int32_t tensor;
   int32_t a;
@@ -85,8 +95,17 @@ struct Pass2Args {
   const float* P;
   float* Q;
   float* partial;
-  int32_t* counters;
   float inv_scale;
+  const int32_t* found_inf;
+};
+
+// Sum of pass-2 partial slots: one work item per (tensor, column block).
+struct Pass2ReduceArgs {
+  const Tile* tiles;       // a = unused, b = column block
+  int32_t ntiles;
+  const TensorDesc* td;
+  const float* partial;
+  float* Q;
   const int32_t* found_inf;
 };
 
@@ -105,9 +124,9 @@ struct Pass3Args {
 };
 
 // Launchers (kernels.hip). R is the padded rank (1, 2, 4, 8, 16 or 32).
-hipError_t launch_pass1(int R, int rows_per_lane, bool f16, bool ef, const Pass1Args& a,
-                        hipStream_t s);
+hipError_t launch_pass1(int R, bool f16, bool ef, const Pass1Args& a, hipStream_t s);
 hipError_t launch_pass2(int R, bool f16, bool ef, const Pass2Args& a, hipStream_t s);
+hipError_t launch_pass2_reduce(int R, const Pass2ReduceArgs& a, hipStream_t s);
 hipError_t launch_pass3(int R, bool f16, bool ef, const Pass3Args& a, hipStream_t s);
 hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, float* base, double eps,
                        const int32_t* found_inf, hipStream_t s);
@@ -118,7 +137,7 @@ hipError_t launch_unscale_only(const FlatTile* ftiles, int nftiles, void* bucket
                                float inv_scale, int32_t* found_inf, bool check,
                                hipStream_t s);
 
-// Rows of one pass-1 row group per wavefront, as chosen for a padded rank R.
-int pass1_rows_per_lane(int R);
+// Rows loaded per thread before use in pass 1 (P = M' Q), by padded rank.
+constexpr int pass1_unroll(int R) { return R <= 4 ? 4 : (R <= 8 ? 2 : 1); }
 
 }  // namespace psgd

@@ -7,19 +7,21 @@
 // Scaling". Every kernel covers all tensors of a bucket in one launch, driven by
 // a device table of work items, so a launch has thousands of workgroups.
 //
-//   pass 1  M' = G (+ E); fp32 writes M' back in place; P = M' Q.
-//           One wavefront owns a group of rows and sweeps all columns with 16-byte
-//           loads; per-lane partial dot products are reduced across the wavefront
-//           once per row group (halving butterfly: N values in N - 1 + 6 - log2 N
-//           shuffles). fp16: x * inv_scale and an OR of "not finite" into found_inf.
+//   Streaming passes share one tiling: (row block x 256-column block) work items;
+//   a lane owns 4 consecutive columns (16-byte accesses) and keeps several rows of
+//   loads in flight; narrow matrices pack several rows into one wavefront.
+//   pass 1  M' = G (+ E); fp32 writes M' back in place; P = M' Q. A workgroup owns
+//           whole rows, so each dot product is finished inside it (shuffles, then
+//           LDS across wavefronts). fp16: x * inv_scale and an OR of "not finite"
+//           into found_inf.
 //   orth    Modified Gram-Schmidt with epsilon on P (and on the initial Q draw).
 //           One workgroup per matrix; column norm and all dot products of a step
 //           come from one fp64 workgroup reduction.
-//   pass 2  Q = M'^T P. A workgroup owns a 256-column block of a row block; P rows
-//           are wave-uniform (scalar loads); the four wavefronts are combined in
-//           LDS in a fixed order, row blocks through a partial-sum buffer that the
-//           last-arriving workgroup sums in row-block order (deterministic, no
-//           floating-point atomics).
+//   pass 2  Q = M'^T P. A workgroup owns a 256-column block of a row block; its row
+//           slots and wavefronts are combined in a fixed order; tensors with several
+//           row blocks write one partial per block, summed in row-block order by a
+//           small second kernel (deterministic, no atomics, no inter-workgroup
+//           fences: the kernel boundary publishes the partials).
 //   pass 3  M_hat = P Q^T written into the bucket (fp16: round to nearest even),
 //           E = M' - M_hat.
 //   q_init  Philox4x64-10 + Box-Muller draw of the initial Q (counter layout in
@@ -36,29 +38,6 @@ constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n >> 1); }
 
 __device__ __forceinline__ int wave_index() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-}
-
-// Reduces v[0..N) across the 64 lanes of a wavefront. On return, lane L holds the
-// wave-wide sum of v[L >> (6 - log2 N)]. N is a power of two <= 64.
-template <int N>
-__device__ __forceinline__ float wave_reduce_spread(float (&v)[N], int lane) {
-  constexpr int LOGN = ilog2(N);
-#pragma unroll
-  for (int s = 0; s < LOGN; ++s) {
-    const int mask = 32 >> s;
-    const int half = N >> (s + 1);
-    const bool upper = (lane & mask) != 0;
-#pragma unroll
-    for (int i = 0; i < half; ++i) {
-      const float send = upper ? v[i] : v[i + half];
-      const float keep = upper ? v[i + half] : v[i];
-      v[i] = keep + __shfl_xor(send, mask);
-    }
-  }
-  float x = v[0];
-#pragma unroll
-  for (int mask = (32 >> LOGN); mask >= 1; mask >>= 1) x += __shfl_xor(x, mask);
-  return x;
 }
 
 __device__ __forceinline__ bool half_bits_not_finite(uint16_t h) {
@@ -197,6 +176,49 @@ __device__ __forceinline__ void load_q_rows(const float* __restrict__ Q, int c, 
   }
 }
 
+// Lane geometry of a tile (see TensorDesc): row slot, column group and first column.
+struct LaneGeom {
+  int lpr;      // lanes per row slot
+  int rpw;      // row slots per wavefront
+  int slot;     // this lane's row slot
+  int g;        // this lane's column group inside the slot
+  int c;        // first of this lane's 4 columns
+  bool col_ok;  // the lane owns at least one column of the matrix
+  int valid;    // columns left in the row from c
+};
+
+__device__ __forceinline__ LaneGeom lane_geom(const TensorDesc& d, int cb, int lane) {
+  LaneGeom L;
+  L.lpr = d.lpr;
+  L.rpw = 64 / d.lpr;
+  L.slot = lane / d.lpr;
+  L.g = lane - L.slot * d.lpr;
+  L.c = cb * kColBlock + L.g * 4;
+  L.col_ok = L.c < d.m;
+  L.valid = d.m - L.c;
+  return L;
+}
+
+// P row `row` (R floats, 16-byte aligned when R >= 4).
+template <int R>
+__device__ __forceinline__ void load_p_row(const float* __restrict__ Pt, int row,
+                                           float (&p)[R]) {
+  const float* src = Pt + static_cast<int64_t>(row) * R;
+  if constexpr (R % 4 == 0) {
+#pragma unroll
+    for (int k4 = 0; k4 < R / 4; ++k4) {
+      const float4 w = reinterpret_cast<const float4*>(src)[k4];
+      p[4 * k4 + 0] = w.x;
+      p[4 * k4 + 1] = w.y;
+      p[4 * k4 + 2] = w.z;
+      p[4 * k4 + 3] = w.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < R; ++k) p[k] = src[k];
+  }
+}
+
 // ----------------------------------------------------------------------- pass 1
 
 __device__ void f16_check_range(const FlatTile ft, const void* bucket,
@@ -208,9 +230,14 @@ __device__ void f16_check_range(const FlatTile ft, const void* bucket,
   if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(found_inf, 1);
 }
 
-template <int R, int RPL, bool F16, bool EF>
+// P = M' Q over one row block. Threads of a row slot sweep the row's columns,
+// U rows per thread are loaded before any is used, and the slot's partial dot
+// products are summed with shuffles (and through LDS when a slot spans wavefronts).
+template <int R, int U, bool F16, bool EF>
 __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
-  const int lane = threadIdx.x & 63;
+  __shared__ float red[kThreads / 64][U * R];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
     if constexpr (F16)
       f16_check_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.found_inf);
@@ -220,51 +247,113 @@ __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   const int m = d.m;
+  const int lprw = d.lprw;
+  const int slots = kThreads / lprw;
+  const int slot = tid / lprw;
+  const int g = tid - slot * lprw;
+  const int sweep = 4 * lprw;
   const bool vec = d.vec != 0;
-  const int row_end = t.a + t.b;
+  const int r0 = t.a * d.rpb1;
+  const int r1 = min(d.n, r0 + d.rpb1);
   const float* __restrict__ Qt = args.Q + d.qoff;
   float* __restrict__ Et = args.E + d.eoff;
-  constexpr int N = RPL * R;
-  constexpr int LOGN = ilog2(N);
   int bad = 0;
-  for (int rg = t.a + wave * RPL; rg < row_end; rg += 4 * RPL) {
-    float acc[N];
+  for (int rw = r0; rw < r1; rw += slots * U) {
+    float acc[U][R];
 #pragma unroll
-    for (int i = 0; i < N; ++i) acc[i] = 0.f;
-    for (int c = lane * 4; c < m; c += kColBlock) {
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < R; ++k) acc[u][k] = 0.f;
+    for (int c = g * 4; c < m; c += sweep) {
+      const int valid = m - c;
       float q[4][R];
       load_q_rows<R>(Qt, c, m, q);
-      const int valid = m - c;
+      float x[U][4];
 #pragma unroll
-      for (int ri = 0; ri < RPL; ++ri) {
-        const int row = rg + ri;
-        if (row < row_end) {
-          const int64_t off = static_cast<int64_t>(row) * m + c;
-          float x[4];
-          load_grad4<F16>(args.bucket, d.boff + off, vec, valid, args.inv_scale, x, bad);
-          if constexpr (EF) {
-            float e[4];
-            load_f32x4(Et + off, vec, valid, e);
+      for (int u = 0; u < U; ++u) {
+        const int row = rw + u * slots + slot;
+        if (row < r1) {
+          load_grad4<F16>(args.bucket, d.boff + static_cast<int64_t>(row) * m + c, vec, valid,
+                          args.inv_scale, x[u], bad);
+        } else {
 #pragma unroll
-            for (int a = 0; a < 4; ++a) x[a] += e[a];
-            if constexpr (!F16)
-              store_f32x4(static_cast<float*>(args.bucket) + d.boff + off, vec, valid, x);
-          }
-#pragma unroll
-          for (int k = 0; k < R; ++k)
-            acc[ri * R + k] += x[0] * q[0][k] + x[1] * q[1][k] + x[2] * q[2][k] +
-                               x[3] * q[3][k];
+          for (int a = 0; a < 4; ++a) x[u][a] = 0.f;
         }
       }
+      if constexpr (EF) {
+        float e[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int row = rw + u * slots + slot;
+          if (row < r1) {
+            load_f32x4(Et + static_cast<int64_t>(row) * m + c, vec, valid, e[u]);
+          } else {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) e[u][a] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) x[u][a] += e[u][a];
+          if constexpr (!F16) {
+            const int row = rw + u * slots + slot;
+            if (row < r1)
+              store_f32x4(static_cast<float*>(args.bucket) + d.boff +
+                              static_cast<int64_t>(row) * m + c,
+                          vec, valid, x[u]);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+          acc[u][k] += x[u][0] * q[0][k] + x[u][1] * q[1][k] + x[u][2] * q[2][k] +
+                       x[u][3] * q[3][k];
     }
-    const float s = wave_reduce_spread<N>(acc, lane);
-    if ((lane & ((64 >> LOGN) - 1)) == 0) {
-      const int idx = lane >> (6 - LOGN);
-      const int ri = idx / R;
-      const int k = idx % R;
-      const int row = rg + ri;
-      if (row < row_end)
-        args.P[d.poff + static_cast<int64_t>(row) * R + k] = (k < d.rank) ? s : 0.f;
+    // sum over the slot's threads inside the wavefront
+    const int wmask = lprw < 64 ? lprw : 64;
+    for (int mask = wmask >> 1; mask > 0; mask >>= 1) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int k = 0; k < R; ++k) acc[u][k] += __shfl_xor(acc[u][k], mask);
+    }
+    if (lprw <= 64) {
+      if (g == 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int row = rw + u * slots + slot;
+          if (row < r1) {
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+              args.P[d.poff + static_cast<int64_t>(row) * R + k] = (k < d.rank) ? acc[u][k] : 0.f;
+          }
+        }
+      }
+    } else {
+      // a slot spans lprw / 64 wavefronts: add their sums in wavefront order
+      if (lane == 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int k = 0; k < R; ++k) red[wave][u * R + k] = acc[u][k];
+      }
+      __syncthreads();
+      const int wps = lprw / 64;
+      if (tid < slots * U * R) {
+        const int s2 = tid / (U * R);
+        const int uk = tid - s2 * (U * R);
+        const int u = uk / R;
+        const int k = uk - u * R;
+        float v = 0.f;
+        for (int w = 0; w < wps; ++w) v += red[s2 * wps + w][uk];
+        const int row = rw + u * slots + s2;
+        if (row < r1)
+          args.P[d.poff + static_cast<int64_t>(row) * R + k] = (k < d.rank) ? v : 0.f;
+      }
+      __syncthreads();
     }
   }
   if constexpr (F16) {
@@ -289,20 +378,21 @@ __device__ __forceinline__ void load_mprime4(const void* bucket, const float* Et
   // fp32 with error feedback: the bucket already holds M' (written by pass 1).
 }
 
-template <int R, bool F16, bool EF>
+// Q = M'^T P over one tile; row slots and wavefronts are combined in a fixed order;
+// with several row blocks each writes a partial slot (summed by k_pass2_reduce).
+template <int R, int U, bool F16, bool EF>
 __global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
   if (F16 && *args.found_inf) return;
   __shared__ float red[64 * 4 * R];
-  __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
-  const int m = d.m;
+  const LaneGeom L = lane_geom(d, t.b, lane);
   const bool vec = d.vec != 0;
-  const int c = t.b * kColBlock + lane * 4;
   const int r0 = t.a * d.rpb;
   const int r1 = min(d.n, r0 + d.rpb);
+  const int stride = 4 * L.rpw;
   const float* __restrict__ Pt = args.P + d.poff;
   const float* __restrict__ Et = args.E + d.eoff;
   float acc[4][R];
@@ -310,25 +400,44 @@ __global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int k = 0; k < R; ++k) acc[a][k] = 0.f;
-  if (c < m) {
-    const int valid = m - c;
-    for (int row = r0 + wave; row < r1; row += 4) {
-      float x[4];
-      load_mprime4<F16, EF>(args.bucket, Et, d, static_cast<int64_t>(row) * m + c, vec,
-                            valid, args.inv_scale, x);
-      float p[R];
+  if (L.col_ok) {
+    for (int rw = r0 + wave * L.rpw; rw < r1; rw += stride * U) {
+      float x[U][4];
+      float p[U][R];
 #pragma unroll
-      for (int k = 0; k < R; ++k) p[k] = Pt[static_cast<int64_t>(row) * R + k];
+      for (int u = 0; u < U; ++u) {
+        const int row = rw + u * stride + L.slot;
+        if (row < r1) {
+          load_mprime4<F16, EF>(args.bucket, Et, d, static_cast<int64_t>(row) * d.m + L.c,
+                                vec, L.valid, args.inv_scale, x[u]);
+          load_p_row<R>(Pt, row, p[u]);
+        } else {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+          for (int a = 0; a < 4; ++a) x[u][a] = 0.f;
 #pragma unroll
-        for (int k = 0; k < R; ++k) acc[a][k] += x[a] * p[k];
+          for (int k = 0; k < R; ++k) p[u][k] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int k = 0; k < R; ++k) acc[a][k] += x[u][a] * p[u][k];
     }
   }
-  // Combine the wavefronts in a fixed order: w0 + (w1 + (w2 + w3)).
-  float* mine = red + lane * 4 * R;
+  // sum over the row slots of the wavefront (lanes with the same column group)
+  for (int mask = L.lpr; mask < 64; mask <<= 1) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int k = 0; k < R; ++k) acc[a][k] += __shfl_xor(acc[a][k], mask);
+  }
+  // combine the wavefronts in a fixed order: w0 + (w1 + (w2 + w3))
+  const bool writer = L.slot == 0;
+  float* mine = red + L.g * 4 * R;
   for (int w = 3; w >= 1; --w) {
-    if (wave == w) {
+    if (wave == w && writer) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -339,48 +448,50 @@ __global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
   }
   float* Qt = args.Q + d.qoff;
   if (d.nrb == 1) {
-    if (wave == 0 && c < m) {
+    if (wave == 0 && writer && L.col_ok) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
-        if (c + a < m) {
+        if (a < L.valid) {
 #pragma unroll
           for (int k = 0; k < R; ++k)
-            Qt[static_cast<int64_t>(c + a) * R + k] =
+            Qt[static_cast<int64_t>(L.c + a) * R + k] =
                 (k < d.rank) ? acc[a][k] + mine[a * R + k] : 0.f;
         }
     }
     return;
   }
-  // Several row blocks: publish this block's partial, the last arrival sums them.
-  constexpr int SLOT = kColBlock * R;
-  float* part = args.partial;
-  if (wave == 0) {
-    float* dst = part + static_cast<int64_t>(d.pslot + t.b * d.nrb + t.a) * SLOT + lane * 4 * R;
+  if (wave == 0 && writer) {
+    float* dst = args.partial +
+                 static_cast<int64_t>(d.pslot + t.b * d.nrb + t.a) * (kColBlock * R) +
+                 L.g * 4 * R;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int k = 0; k < R; ++k) dst[a * R + k] = acc[a][k] + mine[a * R + k];
-    __threadfence();
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(args.counters + d.cslot + t.b, 1);
-    s_last = (prev == d.nrb - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const float* src = part + static_cast<int64_t>(d.pslot + t.b * d.nrb) * SLOT;
-  for (int f = threadIdx.x; f < SLOT; f += kThreads) {
+}
+
+// Q of the tensors with several row blocks: the partial slots of a column block
+// summed in row-block order.
+template <int R>
+__global__ void __launch_bounds__(kThreads) k_pass2_reduce(Pass2ReduceArgs args) {
+  if (args.found_inf != nullptr && *args.found_inf) return;
+  const Tile t = args.tiles[blockIdx.x];
+  const TensorDesc d = args.td[t.tensor];
+  constexpr int SLOT = kColBlock * R;
+  const float* src = args.partial + static_cast<int64_t>(d.pslot + t.b * d.nrb) * SLOT;
+  float* Qt = args.Q + d.qoff;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int f = threadIdx.x + i * kThreads;
     const int col = t.b * kColBlock + f / R;
     const int k = f % R;
-    if (col < m) {
+    if (col < d.m) {
       float s = 0.f;
       for (int rb = 0; rb < d.nrb; ++rb) s += src[static_cast<int64_t>(rb) * SLOT + f];
       Qt[static_cast<int64_t>(col) * R + k] = (k < d.rank) ? s : 0.f;
     }
   }
-  if (threadIdx.x == 0) atomicExch(args.counters + d.cslot + t.b, 0);
 }
 
 // ----------------------------------------------------------------------- pass 3
@@ -391,7 +502,8 @@ __device__ void f16_unscale_range(const FlatTile ft, void* bucket, float inv_sca
     h[i] = __half_as_ushort(__float2half_rn(half_bits_to_float(h[i]) * inv_scale));
 }
 
-template <int R, bool F16, bool EF>
+// M_hat = P Q^T into the bucket and E = M' - M_hat over one tile.
+template <int R, int U, bool F16, bool EF>
 __global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
   if (F16 && *args.found_inf) return;
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
@@ -403,41 +515,51 @@ __global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
   const int wave = wave_index();
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
-  const int m = d.m;
+  const LaneGeom L = lane_geom(d, t.b, lane);
+  if (!L.col_ok) return;
   const bool vec = d.vec != 0;
-  const int c = t.b * kColBlock + lane * 4;
-  if (c >= m) return;
-  const int valid = m - c;
   const int r0 = t.a * d.rpb;
   const int r1 = min(d.n, r0 + d.rpb);
+  const int stride = 4 * L.rpw;
   const float* __restrict__ Pt = args.P + d.poff;
   float* __restrict__ Et = args.E + d.eoff;
   float q[4][R];
-  load_q_rows<R>(args.Q + d.qoff, c, m, q);
-  for (int row = r0 + wave; row < r1; row += 4) {
-    const int64_t off = static_cast<int64_t>(row) * m + c;
-    float x[4];
-    load_mprime4<F16, EF>(args.bucket, Et, d, off, vec, valid, args.inv_scale, x);
-    float p[R];
+  load_q_rows<R>(args.Q + d.qoff, L.c, d.m, q);
+  for (int rw = r0 + wave * L.rpw; rw < r1; rw += stride * U) {
+    float x[U][4];
+    float p[U][R];
 #pragma unroll
-    for (int k = 0; k < R; ++k) p[k] = Pt[static_cast<int64_t>(row) * R + k];
-    float mh[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      float s = 0.f;
-#pragma unroll
-      for (int k = 0; k < R; ++k) s += p[k] * q[a][k];
-      mh[a] = s;
+    for (int u = 0; u < U; ++u) {
+      const int row = rw + u * stride + L.slot;
+      if (row < r1) {
+        load_mprime4<F16, EF>(args.bucket, Et, d, static_cast<int64_t>(row) * d.m + L.c, vec,
+                              L.valid, args.inv_scale, x[u]);
+        load_p_row<R>(Pt, row, p[u]);
+      }
     }
-    if constexpr (F16)
-      store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, vec, valid, mh);
-    else
-      store_f32x4(static_cast<float*>(args.bucket) + d.boff + off, vec, valid, mh);
-    if constexpr (EF) {
-      float e[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) e[a] = x[a] - mh[a];
-      store_f32x4(Et + off, vec, valid, e);
+    for (int u = 0; u < U; ++u) {
+      const int row = rw + u * stride + L.slot;
+      if (row >= r1) continue;
+      const int64_t off = static_cast<int64_t>(row) * d.m + L.c;
+      float mh[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < R; ++k) s += p[u][k] * q[a][k];
+        mh[a] = s;
+      }
+      if constexpr (F16)
+        store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, vec, L.valid, mh);
+      else
+        store_f32x4(static_cast<float*>(args.bucket) + d.boff + off, vec, L.valid, mh);
+      if constexpr (EF) {
+        float e[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) e[a] = x[u][a] - mh[a];
+        store_f32x4(Et + off, vec, L.valid, e);
+      }
     }
   }
 }
@@ -587,34 +709,32 @@ __global__ void __launch_bounds__(256)
 
 // ------------------------------------------------------------------ dispatch
 
+// Rows loaded per lane before use, by rank (register budget).
+template <int R> constexpr int unroll1() { return pass1_unroll(R); }
+template <int R> constexpr int unroll2() { return R <= 4 ? 8 : (R <= 8 ? 4 : (R <= 16 ? 2 : 1)); }
+template <int R> constexpr int unroll3() { return R <= 8 ? 4 : (R <= 16 ? 2 : 1); }
+
 template <int R>
-hipError_t pass1_r(int rpl, bool f16, bool ef, const Pass1Args& a, hipStream_t s) {
+hipError_t pass1_r(bool f16, bool ef, const Pass1Args& a, hipStream_t s) {
   const dim3 grid(a.ntiles + (f16 ? a.nftiles : 0));
   if (grid.x == 0) return hipSuccess;
-#define PSGD_P1(RPL)                                                                      \
-  if (rpl == RPL) {                                                                       \
-    if (f16 && ef) k_pass1<R, RPL, true, true><<<grid, kThreads, 0, s>>>(a);              \
-    else if (f16) k_pass1<R, RPL, true, false><<<grid, kThreads, 0, s>>>(a);              \
-    else if (ef) k_pass1<R, RPL, false, true><<<grid, kThreads, 0, s>>>(a);               \
-    else k_pass1<R, RPL, false, false><<<grid, kThreads, 0, s>>>(a);                      \
-    return hipGetLastError();                                                             \
-  }
-  if constexpr (R * 8 <= 64) { PSGD_P1(8) }
-  if constexpr (R * 4 <= 64) { PSGD_P1(4) }
-  if constexpr (R * 2 <= 64) { PSGD_P1(2) }
-  PSGD_P1(1)
-#undef PSGD_P1
-  return hipErrorInvalidValue;
+  constexpr int U = unroll1<R>();
+  if (f16 && ef) k_pass1<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
+  else if (f16) k_pass1<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
+  else if (ef) k_pass1<R, U, false, true><<<grid, kThreads, 0, s>>>(a);
+  else k_pass1<R, U, false, false><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <int R>
 hipError_t pass2_r(bool f16, bool ef, const Pass2Args& a, hipStream_t s) {
   if (a.ntiles == 0) return hipSuccess;
   const dim3 grid(a.ntiles);
-  if (f16 && ef) k_pass2<R, true, true><<<grid, kThreads, 0, s>>>(a);
-  else if (f16) k_pass2<R, true, false><<<grid, kThreads, 0, s>>>(a);
-  else if (ef) k_pass2<R, false, true><<<grid, kThreads, 0, s>>>(a);
-  else k_pass2<R, false, false><<<grid, kThreads, 0, s>>>(a);
+  constexpr int U = unroll2<R>();
+  if (f16 && ef) k_pass2<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
+  else if (f16) k_pass2<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
+  else if (ef) k_pass2<R, U, false, true><<<grid, kThreads, 0, s>>>(a);
+  else k_pass2<R, U, false, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -622,25 +742,15 @@ template <int R>
 hipError_t pass3_r(bool f16, bool ef, const Pass3Args& a, hipStream_t s) {
   const dim3 grid(a.ntiles + (f16 ? a.nftiles : 0));
   if (grid.x == 0) return hipSuccess;
-  if (f16 && ef) k_pass3<R, true, true><<<grid, kThreads, 0, s>>>(a);
-  else if (f16) k_pass3<R, true, false><<<grid, kThreads, 0, s>>>(a);
-  else if (ef) k_pass3<R, false, true><<<grid, kThreads, 0, s>>>(a);
-  else k_pass3<R, false, false><<<grid, kThreads, 0, s>>>(a);
+  constexpr int U = unroll3<R>();
+  if (f16 && ef) k_pass3<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
+  else if (f16) k_pass3<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
+  else if (ef) k_pass3<R, U, false, true><<<grid, kThreads, 0, s>>>(a);
+  else k_pass3<R, U, false, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
-
-int pass1_rows_per_lane(int R) {
-  switch (R) {
-    case 1: return 8;
-    case 2: return 8;
-    case 4: return 4;
-    case 8: return 4;
-    case 16: return 2;
-    default: return 1;
-  }
-}
 
 #define PSGD_RANK_SWITCH(R, ...)                    \
   switch (R) {                                      \
@@ -653,13 +763,20 @@ int pass1_rows_per_lane(int R) {
     default: return hipErrorInvalidValue;           \
   }
 
-hipError_t launch_pass1(int R, int rpl, bool f16, bool ef, const Pass1Args& a,
-                        hipStream_t s) {
-  PSGD_RANK_SWITCH(R, return pass1_r<RR>(rpl, f16, ef, a, s))
+hipError_t launch_pass1(int R, bool f16, bool ef, const Pass1Args& a, hipStream_t s) {
+  PSGD_RANK_SWITCH(R, return pass1_r<RR>(f16, ef, a, s))
 }
 
 hipError_t launch_pass2(int R, bool f16, bool ef, const Pass2Args& a, hipStream_t s) {
   PSGD_RANK_SWITCH(R, return pass2_r<RR>(f16, ef, a, s))
+}
+
+hipError_t launch_pass2_reduce(int R, const Pass2ReduceArgs& a, hipStream_t s) {
+  if (a.ntiles == 0) return hipSuccess;
+  PSGD_RANK_SWITCH(R, {
+    k_pass2_reduce<RR><<<dim3(a.ntiles), kThreads, 0, s>>>(a);
+    return hipGetLastError();
+  })
 }
 
 hipError_t launch_pass3(int R, bool f16, bool ef, const Pass3Args& a, hipStream_t s) {

@@ -75,11 +75,13 @@ class BucketGenerator:
                                       device=self.device))
         return out
 
-    def inf_injected(self, step: int) -> bool:
+    def inf_injected(self, step: int, forced: bool = True) -> bool:
+        """Whether `step` carries an injected inf: the workload's Bernoulli draw, plus
+        the forced steps of the correctness runs when `forced`."""
         cfg = self.cfg
         if cfg.dtype != "f16":
             return False
-        if step in cfg.forced_inf_steps:
+        if forced and step in cfg.forced_inf_steps:
             return True
         if cfg.inf_probability <= 0.0:
             return False
@@ -87,7 +89,7 @@ class BucketGenerator:
         return bool(torch.rand(1, generator=g).item() < cfg.inf_probability)
 
     def bucket(self, step: int, loss_scale: Optional[float] = None,
-               inject_inf: Optional[bool] = None) -> torch.Tensor:
+               inject_inf: Optional[bool] = None, forced: bool = True) -> torch.Tensor:
         """The stored bucket of `step`: fp32 gradients, or loss-scaled fp16 ones."""
         cfg = self.cfg
         g = self.gradient(step)
@@ -96,7 +98,7 @@ class BucketGenerator:
         scale = cfg.loss_scale if loss_scale is None else loss_scale
         h = (g * (cfg.amp_prescale * scale)).to(torch.float16)
         if inject_inf is None:
-            inject_inf = self.inf_injected(step)
+            inject_inf = self.inf_injected(step, forced)
         if inject_inf:
             gen = torch.Generator().manual_seed(_seed(cfg.seed, 1, _ROLE_INF, step))
             pos = int(torch.randint(0, cfg.numel, (1,), generator=gen).item())
