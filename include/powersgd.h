@@ -196,10 +196,12 @@ powersgd_status powersgd_get_stats(powersgd_state* st, int64_t* iteration,
 
 /* --- kernel timing (HIP events on the caller's stream) ------------------------ */
 
-#define POWERSGD_NUM_KERNELS 7
-/* kernel kinds: 0 q_init, 1 pass1 (P = M'Q), 2 orthogonalize, 3 pass2 (Q = M'^T P,
- * per row block), 4 pass3 (decompress + error), 5 unscale-only (F16 pass-through),
- * 6 pass2_reduce (sum of pass-2 row-block partials) */
+#define POWERSGD_NUM_KERNELS 8
+/* kernel kinds: 0 q_init, 1 pass1 (P = M'Q, plus the Gram partials of P for ranks
+ * <= 8), 2 orthogonalize (Gram-Schmidt from the Gram partials, P <- P T),
+ * 3 pass2 (Q = M'^T P, per row block), 4 pass3 (decompress + error), 5 unscale-only
+ * (F16 pass-through), 6 pass2_reduce (sum of pass-2 row-block partials), 7 gram
+ * (Gram partials read from P or Q, ranks > 8 and the initial Q) */
 
 /* Turns per-kernel event timing on (non-zero) or off; clears accumulated times. */
 powersgd_status powersgd_set_timing(powersgd_state* st, int32_t enable);

@@ -116,15 +116,19 @@ struct BucketPlan {
   std::vector<Tile> tiles1, tiles23, tiles2r;
   std::vector<FlatTile> flat_unc, flat_all;
   std::vector<OrthJob> pjobs, qjobs;
+  std::vector<Tile> pgram_tiles, qgram_tiles;  // (job, partial) for the Gram kernel
   std::vector<QInitJob> qinit;
   int64_t max_qcount = 0;
-  int64_t e_floats = 0, p_floats = 0, q_floats = 0, partial_floats = 0;
+  int64_t e_floats = 0, p_floats = 0, q_floats = 0, partial_floats = 0, gram_doubles = 0;
 
   // device memory
   float* E = nullptr;
   float* P = nullptr;
   float* Q = nullptr;
   float* partial = nullptr;
+  double* gram = nullptr;
+  Tile* d_pgram_tiles = nullptr;
+  Tile* d_qgram_tiles = nullptr;
   TensorDesc* d_td = nullptr;         // rows vector-aligned where possible
   TensorDesc* d_td_scalar = nullptr;  // same with every vec flag cleared
   Tile* d_tiles1 = nullptr;   // pass 1 row blocks
@@ -139,11 +143,14 @@ struct BucketPlan {
   bool q_ready = false;
 
   void release() {
-    void* ptrs[] = {E, P, Q, partial, d_td, d_td_scalar, d_tiles1, d_tiles23, d_tiles2r,
-                    d_flat_unc, d_flat_all, d_pjobs, d_qjobs, d_qinit};
+    void* ptrs[] = {E, P, Q, partial, gram, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
+                    d_tiles1, d_tiles23, d_tiles2r, d_flat_unc, d_flat_all, d_pjobs, d_qjobs,
+                    d_qinit};
     for (void* p : ptrs)
       if (p) (void)hipFree(p);
     E = P = Q = partial = nullptr;
+    gram = nullptr;
+    d_pgram_tiles = d_qgram_tiles = nullptr;
     d_td = d_td_scalar = nullptr;
     d_tiles1 = d_tiles23 = d_tiles2r = nullptr;
     d_flat_unc = d_flat_all = nullptr;
@@ -191,7 +198,8 @@ struct powersgd_state {
 namespace {
 
 enum KernelKind {
-  K_QINIT = 0, K_PASS1 = 1, K_ORTH = 2, K_PASS2 = 3, K_PASS3 = 4, K_UNSCALE = 5, K_PASS2R = 6
+  K_QINIT = 0, K_PASS1 = 1, K_ORTH = 2, K_PASS2 = 3, K_PASS3 = 4, K_UNSCALE = 5, K_PASS2R = 6,
+  K_GRAM = 7
 };
 
 hipEvent_t take_event(powersgd_state* st) {
@@ -329,6 +337,9 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
   const int64_t target =
       std::min<int64_t>(1 << 16, std::max<int64_t>(1 << 13, pl.compressed_elems / 2048));
   const int64_t unroll1 = pass1_unroll(R);
+  const int64_t ng = static_cast<int64_t>(R) * (R + 1) / 2;
+  const bool fused_gram = R <= kMaxFusedGramRank;
+  int64_t goff = 0;
   int64_t eoff = 0, poff = 0, qoff = 0;
   int32_t pslot = 0;
   for (size_t v = 0; v < nv; ++v) {
@@ -357,6 +368,17 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
       for (int64_t r0 = 0, rb = 0; r0 < d.n; r0 += rows, ++rb)
         pl.tiles1.push_back(Tile{ti, static_cast<int32_t>(rb), 0, 0});
     }
+    // Gram partials of P: one per pass-1 row block (fused) or per kGramRows rows
+    {
+      const int32_t rpp = fused_gram ? d.rpb1 : kGramRows;
+      const int32_t nparts = static_cast<int32_t>((d.n + rpp - 1) / rpp);
+      d.goff = goff;
+      pl.pjobs.push_back(OrthJob{d.poff, goff, d.n, d.rank, nparts, rpp});
+      if (!fused_gram)
+        for (int32_t pp = 0; pp < nparts; ++pp)
+          pl.pgram_tiles.push_back(Tile{static_cast<int32_t>(pl.pjobs.size() - 1), pp, 0, 0});
+      goff += nparts * ng;
+    }
     // pass 2 / pass 3: (row block) x (256-column block)
     const int64_t width = std::min<int64_t>(d.m, kColBlock);
     d.lpr = pow2_ceil(static_cast<int>((width + 3) / 4));
@@ -374,8 +396,13 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
     pl.view_tensor[v] = ti;
     for (int32_t cb = 0; cb < d.ncb; ++cb)
       for (int32_t rb = 0; rb < d.nrb; ++rb) pl.tiles23.push_back(Tile{ti, rb, cb, 0});
-    pl.pjobs.push_back(OrthJob{d.poff, d.n, d.rank});
-    pl.qjobs.push_back(OrthJob{d.qoff, d.m, d.rank});
+    {
+      const int32_t nparts = static_cast<int32_t>((d.m + kGramRows - 1) / kGramRows);
+      pl.qjobs.push_back(OrthJob{d.qoff, goff, d.m, d.rank, nparts, kGramRows});
+      for (int32_t pp = 0; pp < nparts; ++pp)
+        pl.qgram_tiles.push_back(Tile{static_cast<int32_t>(pl.qjobs.size() - 1), pp, 0, 0});
+      goff += nparts * ng;
+    }
     pl.qinit.push_back(QInitJob{d.qoff, d.m, d.rank, d.view, 0});
     pl.max_qcount = std::max<int64_t>(pl.max_qcount, static_cast<int64_t>(d.m) * d.rank);
     pl.tensors.push_back(d);
@@ -384,6 +411,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
   pl.p_floats = poff;
   pl.q_floats = qoff;
   pl.partial_floats = static_cast<int64_t>(pslot) * kColBlock * R;
+  pl.gram_doubles = goff;
   return POWERSGD_OK;
 }
 
@@ -400,6 +428,7 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   ok = ok && alloc(reinterpret_cast<void**>(&pl.P), pl.p_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.Q), pl.q_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.partial), pl.partial_floats * sizeof(float));
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.gram), pl.gram_doubles * sizeof(double));
 
   if (!ok) {
     pl.release();
@@ -427,6 +456,8 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   if (st == POWERSGD_OK) st = upload(pl.pjobs, &pl.d_pjobs, s);
   if (st == POWERSGD_OK) st = upload(pl.qjobs, &pl.d_qjobs, s);
   if (st == POWERSGD_OK) st = upload(pl.qinit, &pl.d_qinit, s);
+  if (st == POWERSGD_OK) st = upload(pl.pgram_tiles, &pl.d_pgram_tiles, s);
+  if (st == POWERSGD_OK) st = upload(pl.qgram_tiles, &pl.d_qgram_tiles, s);
   if (st != POWERSGD_OK) {
     pl.release();
     return st;
@@ -494,7 +525,7 @@ const char* powersgd_last_error(void) { return g_last_error.c_str(); }
 const char* powersgd_kernel_name(int32_t kind) {
   static const char* names[POWERSGD_NUM_KERNELS] = {
       "q_init", "pass1_mq", "orthogonalize", "pass2_mtp", "pass3_decompress_error",
-      "unscale_only", "pass2_reduce"};
+      "unscale_only", "pass2_reduce", "gram"};
   if (kind < 0 || kind >= POWERSGD_NUM_KERNELS) return "";
   return names[kind];
 }
@@ -641,8 +672,13 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
                             bucket_key, epoch, s);
       });
       if (r != POWERSGD_OK) return r;
+      r = timed_launch(st, s, K_GRAM, 0.0, "Gram of Q", [&] {
+        return launch_gram(R, pl.d_qgram_tiles, static_cast<int>(pl.qgram_tiles.size()),
+                           pl.d_qjobs, pl.Q, pl.gram, nullptr, s);
+      });
+      if (r != POWERSGD_OK) return r;
       r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize Q", [&] {
-        return launch_orth(R, pl.d_qjobs, nt, pl.Q, eps, nullptr, s);
+        return launch_orth(R, pl.d_qjobs, nt, pl.Q, pl.gram, eps, nullptr, s);
       });
       if (r != POWERSGD_OK) return r;
     }
@@ -659,6 +695,7 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
     a.E = pl.E;
     a.Q = pl.Q;
     a.P = pl.P;
+    a.gram = pl.gram;
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
     const double bytes = ce * pass_bytes(K_PASS1, f16, ef) + (f16 ? ue * 2.0 : 0.0);
@@ -668,8 +705,16 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
   }
   if (nt > 0) {
     // Step 3.4 (the allreduce of P, step 3.3, is the identity on one rank).
+    if (!pl.pgram_tiles.empty()) {
+      r = timed_launch(st, s, K_GRAM, 0.0, "Gram of P", [&] {
+        return launch_gram(R, pl.d_pgram_tiles, static_cast<int>(pl.pgram_tiles.size()),
+                           pl.d_pjobs, pl.P, pl.gram, f16 ? found_inf_dev : nullptr, s);
+      });
+      if (r != POWERSGD_OK) return r;
+    }
     r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize P", [&] {
-      return launch_orth(R, pl.d_pjobs, nt, pl.P, eps, f16 ? found_inf_dev : nullptr, s);
+      return launch_orth(R, pl.d_pjobs, nt, pl.P, pl.gram, eps, f16 ? found_inf_dev : nullptr,
+                         s);
     });
     if (r != POWERSGD_OK) return r;
     // Step 3.5 (step 3.6 is the identity).

@@ -11,8 +11,6 @@ namespace psgd {
 constexpr int kColBlock = 256;
 // Threads per workgroup of the streaming passes (4 wavefronts of 64).
 constexpr int kThreads = 256;
-// Threads per workgroup of the orthogonalization kernel.
-constexpr int kOrthThreads = 512;
 
 // One compressed matrix of the bucket (n x m, row-major inside the flat bucket).
 //
@@ -32,6 +30,7 @@ struct TensorDesc {
   int32_t rank;   // columns of P and Q in use (<= R); the rest are kept at zero
   int32_t vec;    // 1: m % 4 == 0 and rows start 16-byte aligned in the bucket
   int32_t view;   // index of the view in the bucket (Q draw counter word)
+  int64_t goff;   // first double of its P Gram partials (one per pass-1 row block)
   int32_t lprw;   // pass 1: threads per row slot (power of two, <= 256)
   int32_t rpb1;   // pass 1: rows per row block
   int32_t lpr;    // pass 2/3: lanes per row slot (power of two, <= 64)
@@ -56,12 +55,23 @@ struct FlatTile {
   int64_t len;
 };
 
-// Orthogonalization job: `rows` x R block at `off` (row stride R), `rank` columns.
+// Orthogonalization job: the `rows` x R block at `off` (row stride R, `rank` columns in
+// use). Its Gram matrix arrives as `nparts` partials of R(R+1)/2 doubles at `goff`
+// (packed upper triangle), partial p covering rows [p * rpp, (p + 1) * rpp).
 struct OrthJob {
   int64_t off;
+  int64_t goff;
   int32_t rows;
   int32_t rank;
+  int32_t nparts;
+  int32_t rpp;
 };
+
+// Packed upper-triangle index of Gram entry (i, j), i <= j < R.
+__host__ __device__ constexpr int tri_index(int i, int j, int R) {
+  return i * R - i * (i - 1) / 2 + (j - i);
+}
+template <int R> constexpr int gram_size() { return R * (R + 1) / 2; }
 
 // Initial-Q job: the m x rank draw of one view, stored with row stride R.
 struct QInitJob {
@@ -82,6 +92,7 @@ struct Pass1Args {
   float* E;
   const float* Q;
   float* P;
+  double* gram;            // P Gram partials (ranks <= 8: computed here)
   float inv_scale;
   int32_t* found_inf;
 };
@@ -128,8 +139,11 @@ hipError_t launch_pass1(int R, bool f16, bool ef, const Pass1Args& a, hipStream_
 hipError_t launch_pass2(int R, bool f16, bool ef, const Pass2Args& a, hipStream_t s);
 hipError_t launch_pass2_reduce(int R, const Pass2ReduceArgs& a, hipStream_t s);
 hipError_t launch_pass3(int R, bool f16, bool ef, const Pass3Args& a, hipStream_t s);
-hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, float* base, double eps,
-                       const int32_t* found_inf, hipStream_t s);
+hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs,
+                       const float* base, double* gram, const int32_t* found_inf,
+                       hipStream_t s);
+hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, float* base, const double* gram,
+                       double eps, const int32_t* found_inf, hipStream_t s);
 hipError_t launch_qinit(int R, const QInitJob* jobs, int njobs, int64_t max_count,
                         float* Q, uint64_t seed, uint64_t bucket_key, uint64_t epoch,
                         hipStream_t s);
@@ -138,6 +152,11 @@ hipError_t launch_unscale_only(const FlatTile* ftiles, int nftiles, void* bucket
                                hipStream_t s);
 
 // Rows loaded per thread before use in pass 1 (P = M' Q), by padded rank.
-constexpr int pass1_unroll(int R) { return R <= 4 ? 4 : (R <= 8 ? 2 : 1); }
+constexpr int pass1_unroll(int R) { return R <= 4 ? 4 : 1; }
+// Pass 1 also accumulates the Gram partials of P up to this padded rank; above it a
+// separate Gram kernel reads P.
+constexpr int kMaxFusedGramRank = 8;
+// Rows per Gram partial of the separate Gram kernel.
+constexpr int kGramRows = 256;
 
 }  // namespace psgd

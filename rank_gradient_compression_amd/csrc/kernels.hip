@@ -14,9 +14,11 @@
 //           whole rows, so each dot product is finished inside it (shuffles, then
 //           LDS across wavefronts). fp16: x * inv_scale and an OR of "not finite"
 //           into found_inf.
-//   orth    Modified Gram-Schmidt with epsilon on P (and on the initial Q draw).
-//           One workgroup per matrix; column norm and all dot products of a step
-//           come from one fp64 workgroup reduction.
+//   orth    Gram-Schmidt with epsilon on P (and on the initial Q draw) from fp64 Gram
+//           partials (pass 1 accumulates them for ranks <= 8, a small LDS-staged
+//           kernel otherwise): one workgroup per matrix sums them in fixed order,
+//           runs the recurrence on r x r coefficient vectors (lane j owns column j)
+//           and applies P <- P T in fp64.
 //   pass 2  Q = M'^T P. A workgroup owns a 256-column block of a row block; its row
 //           slots and wavefronts are combined in a fixed order; tensors with several
 //           row blocks write one partial per block, summed in row-block order by a
@@ -219,6 +221,21 @@ __device__ __forceinline__ void load_p_row(const float* __restrict__ Pt, int row
   }
 }
 
+template <int R>
+__device__ __forceinline__ void store_p_row(float* __restrict__ Pt, int row,
+                                            const float (&p)[R]) {
+  float* dst = Pt + static_cast<int64_t>(row) * R;
+  if constexpr (R % 4 == 0) {
+#pragma unroll
+    for (int k4 = 0; k4 < R / 4; ++k4)
+      reinterpret_cast<float4*>(dst)[k4] =
+          make_float4(p[4 * k4], p[4 * k4 + 1], p[4 * k4 + 2], p[4 * k4 + 3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < R; ++k) dst[k] = p[k];
+  }
+}
+
 // ----------------------------------------------------------------------- pass 1
 
 __device__ void f16_check_range(const FlatTile ft, const void* bucket,
@@ -233,9 +250,48 @@ __device__ void f16_check_range(const FlatTile ft, const void* bucket,
 // P = M' Q over one row block. Threads of a row slot sweep the row's columns,
 // U rows per thread are loaded before any is used, and the slot's partial dot
 // products are summed with shuffles (and through LDS when a slot spans wavefronts).
+// Adds the outer product of one P row (masked to the rank in use) to packed fp64
+// Gram accumulators.
+template <int R>
+__device__ __forceinline__ void gram_add(double (&gacc)[gram_size<R>()], const float (&p)[R]) {
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int j = i; j < R; ++j)
+      gacc[tri_index(i, j, R)] += static_cast<double>(p[i]) * static_cast<double>(p[j]);
+}
+
+// Sums NG doubles over the workgroup in a fixed order (wavefront shuffles, then the
+// four wavefronts in order) and writes them to dst (threads < NG).
+template <int NG>
+__device__ __forceinline__ void block_sum_to(double (&v)[NG], double* dst, double (*red)[NG]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int e = 0; e < NG; ++e) {
+    double x = v[e];
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) x += __shfl_xor(x, mask);
+    v[e] = x;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < NG; ++e) red[wave][e] = v[e];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < NG; e += kThreads)
+    dst[e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+}
+
 template <int R, int U, bool F16, bool EF>
 __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
+  constexpr bool GRAM = R <= kMaxFusedGramRank;
+  constexpr int NG = GRAM ? gram_size<R>() : 1;
   __shared__ float red[kThreads / 64][U * R];
+  __shared__ double gred[kThreads / 64][NG];
+  double gacc[NG];
+#pragma unroll
+  for (int e = 0; e < NG; ++e) gacc[e] = 0.0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
@@ -326,9 +382,11 @@ __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
         for (int u = 0; u < U; ++u) {
           const int row = rw + u * slots + slot;
           if (row < r1) {
+            float pr[R];
 #pragma unroll
-            for (int k = 0; k < R; ++k)
-              args.P[d.poff + static_cast<int64_t>(row) * R + k] = (k < d.rank) ? acc[u][k] : 0.f;
+            for (int k = 0; k < R; ++k) pr[k] = (k < d.rank) ? acc[u][k] : 0.f;
+            store_p_row<R>(args.P + d.poff, row, pr);
+            if constexpr (GRAM) gram_add<R>(gacc, pr);
           }
         }
       }
@@ -342,16 +400,21 @@ __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
       }
       __syncthreads();
       const int wps = lprw / 64;
-      if (tid < slots * U * R) {
-        const int s2 = tid / (U * R);
-        const int uk = tid - s2 * (U * R);
-        const int u = uk / R;
-        const int k = uk - u * R;
-        float v = 0.f;
-        for (int w = 0; w < wps; ++w) v += red[s2 * wps + w][uk];
+      if (tid < slots * U) {
+        const int s2 = tid / U;
+        const int u = tid - s2 * U;
         const int row = rw + u * slots + s2;
-        if (row < r1)
-          args.P[d.poff + static_cast<int64_t>(row) * R + k] = (k < d.rank) ? v : 0.f;
+        if (row < r1) {
+          float pr[R];
+#pragma unroll
+          for (int k = 0; k < R; ++k) {
+            float v = 0.f;
+            for (int w = 0; w < wps; ++w) v += red[s2 * wps + w][u * R + k];
+            pr[k] = (k < d.rank) ? v : 0.f;
+          }
+          store_p_row<R>(args.P + d.poff, row, pr);
+          if constexpr (GRAM) gram_add<R>(gacc, pr);
+        }
       }
       __syncthreads();
     }
@@ -359,6 +422,8 @@ __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
   if constexpr (F16) {
     if (__any(bad) && lane == 0) atomicOr(args.found_inf, 1);
   }
+  if constexpr (GRAM)
+    block_sum_to<NG>(gacc, args.gram + d.goff + static_cast<int64_t>(t.a) * NG, gred);
 }
 
 // ----------------------------------------------------------------------- pass 2
@@ -479,6 +544,7 @@ __global__ void __launch_bounds__(kThreads) k_pass2_reduce(Pass2ReduceArgs args)
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   constexpr int SLOT = kColBlock * R;
+  constexpr int B = 8;  // partial slots loaded before they are added (in order)
   const float* src = args.partial + static_cast<int64_t>(d.pslot + t.b * d.nrb) * SLOT;
   float* Qt = args.Q + d.qoff;
 #pragma unroll
@@ -488,7 +554,14 @@ __global__ void __launch_bounds__(kThreads) k_pass2_reduce(Pass2ReduceArgs args)
     const int k = f % R;
     if (col < d.m) {
       float s = 0.f;
-      for (int rb = 0; rb < d.nrb; ++rb) s += src[static_cast<int64_t>(rb) * SLOT + f];
+      for (int rb = 0; rb < d.nrb; rb += B) {
+        float v[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+          v[b] = (rb + b < d.nrb) ? src[static_cast<int64_t>(rb + b) * SLOT + f] : 0.f;
+#pragma unroll
+        for (int b = 0; b < B; ++b) s += v[b];
+      }
       Qt[static_cast<int64_t>(col) * R + k] = (k < d.rank) ? s : 0.f;
     }
   }
@@ -565,67 +638,176 @@ __global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
 }
 
 // ------------------------------------------------------------ orthogonalization
+//
+// Gram-Schmidt with epsilon (step 3.4) evaluated on the Gram matrix: every vector
+// the recurrence forms is a combination P c of the columns of P, so its norm and
+// its dot products are c^T G c' with G = P^T P. The recurrence runs on the r x r
+// coefficient vectors in fp64 and the result is applied once, P <- P T, in fp64.
 
+// Gram partials of one row chunk of a job, staged through LDS.
 template <int R>
-__global__ void __launch_bounds__(kOrthThreads)
-    k_orth(const OrthJob* __restrict__ jobs, float* __restrict__ base, double eps,
+__global__ void __launch_bounds__(kThreads)
+    k_gram(const Tile* __restrict__ tiles, const OrthJob* __restrict__ jobs,
+           const float* __restrict__ base, double* __restrict__ gram,
            const int32_t* __restrict__ found_inf) {
   if (found_inf != nullptr && *found_inf) return;
-  constexpr int NW = kOrthThreads / 64;
-  __shared__ double red[NW][R];
-  __shared__ double tot[R];
+  constexpr int NG = gram_size<R>();
+  __shared__ float xs[kGramRows * R];
+  const Tile t = tiles[blockIdx.x];
+  const OrthJob j = jobs[t.tensor];
+  const int r0 = t.a * j.rpp;
+  const int nr = min(j.rpp, j.rows - r0);
+  const float* X = base + j.off + static_cast<int64_t>(r0) * R;
+  for (int f = threadIdx.x; f < nr * R; f += kThreads) xs[f] = X[f];
+  __syncthreads();
+  double* out = gram + j.goff + static_cast<int64_t>(t.a) * NG;
+  for (int e = threadIdx.x; e < NG; e += kThreads) {
+    // entry e of the packed triangle -> (a, b)
+    int a = 0, rem = e;
+    while (rem >= R - a) {
+      rem -= R - a;
+      ++a;
+    }
+    const int b = a + rem;
+    double s = 0.0;
+    for (int r = 0; r < nr; ++r)
+      s += static_cast<double>(xs[r * R + a]) * static_cast<double>(xs[r * R + b]);
+    out[e] = s;
+  }
+}
+
+template <int R>
+__global__ void __launch_bounds__(kThreads)
+    k_orth(const OrthJob* __restrict__ jobs, float* __restrict__ base,
+           const double* __restrict__ gram, double eps, const int32_t* __restrict__ found_inf) {
+  if (found_inf != nullptr && *found_inf) return;
+  constexpr int NG = gram_size<R>();
+  __shared__ double sG[R][R];
+  __shared__ double sT[R][R];
+  __shared__ double sC[R];
+  __shared__ double sW[R];
+  __shared__ double sRed[4][NG];
   const OrthJob j = jobs[blockIdx.x];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  // 1. G = sum of the partials, in partial order per thread, then the fixed-order
+  //    combination of strided thread sums.
+  {
+    constexpr int PER = (NG + kThreads - 1) / kThreads;
+    // threads split the entries; with spare threads, also the partials
+    if constexpr (NG <= kThreads / 4) {
+      // 4 groups of threads each sum every 4th partial
+      const int grp = tid / NG;
+      const int e = tid - grp * NG;
+      if (grp < 4) {
+        double s = 0.0;
+        for (int p = grp; p < j.nparts; p += 32) {
+          double v[8];
+#pragma unroll
+          for (int b = 0; b < 8; ++b)
+            v[b] = (p + 4 * b < j.nparts) ? gram[j.goff + static_cast<int64_t>(p + 4 * b) * NG + e]
+                                          : 0.0;
+#pragma unroll
+          for (int b = 0; b < 8; ++b) s += v[b];
+        }
+        sRed[grp][e] = s;
+      }
+      __syncthreads();
+      if (tid < NG) {
+        const double g = ((sRed[0][tid] + sRed[1][tid]) + sRed[2][tid]) + sRed[3][tid];
+        int a = 0, rem = tid;
+        while (rem >= R - a) {
+          rem -= R - a;
+          ++a;
+        }
+        const int b = a + rem;
+        sG[a][b] = g;
+        sG[b][a] = g;
+      }
+    } else {
+      for (int i = 0; i < PER; ++i) {
+        const int e = tid + i * kThreads;
+        if (e < NG) {
+          // partials loaded eight at a time, added in partial order
+          double s = 0.0;
+          for (int p = 0; p < j.nparts; p += 8) {
+            double v[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+              v[b] = (p + b < j.nparts) ? gram[j.goff + static_cast<int64_t>(p + b) * NG + e]
+                                        : 0.0;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) s += v[b];
+          }
+          int a = 0, rem = e;
+          while (rem >= R - a) {
+            rem -= R - a;
+            ++a;
+          }
+          const int b = a + rem;
+          sG[a][b] = s;
+          sG[b][a] = s;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // 2. the recurrence on coefficient vectors: lane c of wavefront 0 owns column c
+  double cvec[R];
+#pragma unroll
+  for (int l = 0; l < R; ++l) cvec[l] = (l == lane) ? 1.0 : 0.0;
+  for (int i = 0; i < j.rank; ++i) {
+    if (wave == 0 && lane == i) {
+#pragma unroll
+      for (int l = 0; l < R; ++l) sC[l] = cvec[l];
+    }
+    __syncthreads();
+    double w = 0.0;  // (G c_i)_lane
+    if (wave == 0 && lane < R) {
+#pragma unroll
+      for (int l = 0; l < R; ++l) w += sG[lane][l] * sC[l];
+    }
+    double nn = (wave == 0 && lane < R) ? sC[lane] * w : 0.0;
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) nn += __shfl_xor(nn, mask);
+    // |v_i|^2 = c_i^T G c_i; q_i = v_i / (|v_i| + eps)
+    const double inv = 1.0 / (sqrt(nn > 0.0 ? nn : 0.0) + eps);
+    if (wave == 0 && lane < R) sW[lane] = w * inv;  // G q_i (in coefficients)
+    __syncthreads();
+    if (wave == 0 && lane < j.rank) {
+      if (lane == i) {
+#pragma unroll
+        for (int l = 0; l < R; ++l) cvec[l] *= inv;
+      } else if (lane > i) {
+        // <q_i, v_lane> = c_lane^T G c_i / (|v_i| + eps); v_lane -= <q_i, v_lane> q_i
+        double coef = 0.0;
+#pragma unroll
+        for (int l = 0; l < R; ++l) coef += cvec[l] * sW[l];
+#pragma unroll
+        for (int l = 0; l < R; ++l) cvec[l] -= coef * (sC[l] * inv);
+      }
+    }
+    __syncthreads();
+  }
+  if (wave == 0 && lane < R) {
+#pragma unroll
+    for (int l = 0; l < R; ++l) sT[l][lane] = cvec[l];
+  }
+  __syncthreads();
+  // 3. P <- P T in fp64, rounded once to fp32 (T is upper triangular)
   float* X = base + j.off;
-  const int rows = j.rows;
-  const int rank = j.rank;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  for (int i = 0; i < rank; ++i) {
-    // s[k] = <x_i, x_k> for k >= i, in fp64 (the products of fp32 values are exact)
-    double s[R];
-#pragma unroll
-    for (int k = 0; k < R; ++k) s[k] = 0.0;
-    for (int row = threadIdx.x; row < rows; row += kOrthThreads) {
-      const float* xr = X + static_cast<int64_t>(row) * R;
-      const double xi = xr[i];
-#pragma unroll
-      for (int k = 0; k < R; ++k)
-        if (k >= i && k < rank) s[k] += xi * static_cast<double>(xr[k]);
-    }
-#pragma unroll
+  for (int row = tid; row < j.rows; row += kThreads) {
+    float x[R];
+    load_p_row<R>(X, row, x);
+    float* dst = X + static_cast<int64_t>(row) * R;
+#pragma unroll 1
     for (int k = 0; k < R; ++k) {
-      if (k >= i && k < rank) {
-        double v = s[k];
+      double s = 0.0;
 #pragma unroll
-        for (int mask = 32; mask >= 1; mask >>= 1) v += __shfl_xor(v, mask);
-        if (lane == 0) red[wave][k] = v;
-      }
+      for (int l = 0; l < R; ++l) s += static_cast<double>(x[l]) * sT[l][k];
+      dst[k] = static_cast<float>(s);
     }
-    __syncthreads();
-    if (threadIdx.x < R) {
-      const int k = threadIdx.x;
-      if (k >= i && k < rank) {
-        double v = 0.0;
-        for (int w = 0; w < NW; ++w) v += red[w][k];
-        tot[k] = v;
-      }
-    }
-    __syncthreads();
-    // q_i = x_i / (|x_i| + eps); x_k -= <q_i, x_k> q_i with <q_i, x_k> = s_k / (|x_i| + eps)
-    const double inv = 1.0 / (sqrt(tot[i]) + eps);
-    float coef[R];
-#pragma unroll
-    for (int k = 0; k < R; ++k)
-      coef[k] = (k > i && k < rank) ? static_cast<float>(tot[k] * inv) : 0.f;
-    for (int row = threadIdx.x; row < rows; row += kOrthThreads) {
-      float* xr = X + static_cast<int64_t>(row) * R;
-      const float qi = static_cast<float>(static_cast<double>(xr[i]) * inv);
-      xr[i] = qi;
-#pragma unroll
-      for (int k = 0; k < R; ++k)
-        if (k > i && k < rank) xr[k] -= coef[k] * qi;
-    }
-    __syncthreads();
   }
 }
 
@@ -783,11 +965,21 @@ hipError_t launch_pass3(int R, bool f16, bool ef, const Pass3Args& a, hipStream_
   PSGD_RANK_SWITCH(R, return pass3_r<RR>(f16, ef, a, s))
 }
 
-hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, float* base, double eps,
-                       const int32_t* found_inf, hipStream_t s) {
+hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs,
+                       const float* base, double* gram, const int32_t* found_inf,
+                       hipStream_t s) {
+  if (ntiles == 0) return hipSuccess;
+  PSGD_RANK_SWITCH(R, {
+    k_gram<RR><<<dim3(ntiles), kThreads, 0, s>>>(tiles, jobs, base, gram, found_inf);
+    return hipGetLastError();
+  })
+}
+
+hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, float* base, const double* gram,
+                       double eps, const int32_t* found_inf, hipStream_t s) {
   if (njobs == 0) return hipSuccess;
   PSGD_RANK_SWITCH(R, {
-    k_orth<RR><<<dim3(njobs), kOrthThreads, 0, s>>>(jobs, base, eps, found_inf);
+    k_orth<RR><<<dim3(njobs), kThreads, 0, s>>>(jobs, base, gram, eps, found_inf);
     return hipGetLastError();
   })
 }

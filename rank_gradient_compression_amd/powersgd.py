@@ -24,7 +24,7 @@ POWERSGD_F32 = 0
 POWERSGD_F16 = 1
 POWERSGD_MAX_NDIM = 8
 POWERSGD_MAX_RANK = 32
-POWERSGD_NUM_KERNELS = 7
+POWERSGD_NUM_KERNELS = 8
 
 # Every function the header declares, for load checks.
 EXPORTED = (
