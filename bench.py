@@ -64,6 +64,25 @@ def load_traffic(kernel: str, workload: str):
         return None
 
 
+def copy_bandwidth(torch, nbytes: int = 1 << 31, reps: int = 10) -> float:
+    """GB/s of a plain device-to-device copy (bytes read + bytes written)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(cfg, budget_s: float = 20.0):
     """The oracle, as it stands, on whole steps of the same workload for ~budget_s."""
     import numpy as np
@@ -124,6 +143,8 @@ def main() -> int:
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    copy_gbs = copy_bandwidth(torch)
+    eprint(f"[bench] device-to-device copy: {copy_gbs:.0f} GB/s (read + write)")
     bucket_bytes = cfg.numel * cfg.element_bytes
     total = args.steps + args.warmup
     gen = BucketGenerator(cfg, "cuda")
@@ -214,6 +235,7 @@ def main() -> int:
                    "views": len(views), "compressed_elements": comp_elems,
                    "matrix_approximation_rank": cfg.hparams["matrix_approximation_rank"],
                    "step_hbm_roofline_frac": round(step_frac, 4),
+                   "measured_copy_GBps": round(copy_gbs, 1),
                    "step_algorithmic_bytes": algo_bytes},
         "roofline": roofline,
     }

@@ -22,6 +22,12 @@
 
 #include <stdint.h>
 
+#if defined(__GNUC__) || defined(__clang__)
+#define POWERSGD_API __attribute__((visibility("default")))
+#else
+#define POWERSGD_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -75,7 +81,7 @@ typedef struct {
 
 /* Fills hp with the defaults printed in the PowerSGDState signature. Never fails
  * (a NULL hp is ignored). */
-void powersgd_hparams_init(powersgd_hparams* hp);
+POWERSGD_API void powersgd_hparams_init(powersgd_hparams* hp);
 
 /*
  * Creates a state for device `device` ("PowerSGD State": the hyperparameters and the
@@ -85,12 +91,12 @@ void powersgd_hparams_init(powersgd_hparams* hp);
  * HIP if the device cannot be selected. Device memory is allocated lazily, per
  * bucket_index, on the first compressing call.
  */
-powersgd_status powersgd_state_create(const powersgd_hparams* hp, int32_t device,
+POWERSGD_API powersgd_status powersgd_state_create(const powersgd_hparams* hp, int32_t device,
                                       powersgd_state** out);
 
 /* Waits for the state's outstanding device work, frees everything it owns. NULL is
  * ignored. */
-void powersgd_state_destroy(powersgd_state* st);
+POWERSGD_API void powersgd_state_destroy(powersgd_state* st);
 
 /*
  * Compresses one bucket in place: powerSGD_hook steps 1 to 3.7 on one rank.
@@ -128,7 +134,7 @@ void powersgd_state_destroy(powersgd_state* st);
  * LAYOUT_CHANGED, OOM, HIP (launch failure; asynchronous faults surface at the
  * caller's next synchronization).
  */
-powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_index,
+POWERSGD_API powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_index,
                                          int32_t is_last, void* bucket,
                                          powersgd_dtype dtype, int64_t numel,
                                          const powersgd_view* views, int32_t nviews,
@@ -136,10 +142,10 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
                                          void* stream);
 
 /* Static text for a status code. */
-const char* powersgd_status_string(powersgd_status s);
+POWERSGD_API const char* powersgd_status_string(powersgd_status s);
 
 /* Detail of the calling thread's last failed call ("" if none). */
-const char* powersgd_last_error(void);
+POWERSGD_API const char* powersgd_last_error(void);
 
 /*
  * Host-only classification of one view under hp, without a state or a device:
@@ -149,7 +155,7 @@ const char* powersgd_last_error(void);
  * and *rank = min(r, n, m) (0 when not compressed). Any output pointer may be NULL.
  * INVALID_ARG for a NULL hp/view, ndim out of range or a negative dimension.
  */
-powersgd_status powersgd_classify_view(const powersgd_hparams* hp, const powersgd_view* view,
+POWERSGD_API powersgd_status powersgd_classify_view(const powersgd_hparams* hp, const powersgd_view* view,
                                        int32_t* compress, int64_t* n, int64_t* m,
                                        int32_t* rank);
 
@@ -161,12 +167,12 @@ powersgd_status powersgd_classify_view(const powersgd_hparams* hp, const powersg
  * count. Host memory; synchronous, no device work. NOT_FOUND if the bucket was never
  * compressed.
  */
-powersgd_status powersgd_get_decisions(powersgd_state* st, int64_t bucket_index,
+POWERSGD_API powersgd_status powersgd_get_decisions(powersgd_state* st, int64_t bucket_index,
                                        uint8_t* out, int32_t nviews);
 
 /* Matrix shape and rank used for view v (rank = min(r, n, m)); rank 0 when the view
  * is not compressed. Synchronous, host only. */
-powersgd_status powersgd_get_view_info(powersgd_state* st, int64_t bucket_index,
+POWERSGD_API powersgd_status powersgd_get_view_info(powersgd_state* st, int64_t bucket_index,
                                        int32_t view, int64_t* n, int64_t* m,
                                        int32_t* rank);
 
@@ -175,14 +181,14 @@ powersgd_status powersgd_get_view_info(powersgd_state* st, int64_t bucket_index,
  * row-major; the warm-start memory) of compressed view v into caller device buffers
  * (either may be NULL), enqueued on `stream`.
  */
-powersgd_status powersgd_copy_factors(powersgd_state* st, int64_t bucket_index,
+POWERSGD_API powersgd_status powersgd_copy_factors(powersgd_state* st, int64_t bucket_index,
                                       int32_t view, float* p_dev, float* q_dev,
                                       void* stream);
 
 /* Copies the error-feedback memory E (n x m, row-major, fp32) of compressed view v
  * into a caller device buffer, enqueued on `stream`. NOT_FOUND without error
  * feedback. */
-powersgd_status powersgd_copy_error(powersgd_state* st, int64_t bucket_index,
+POWERSGD_API powersgd_status powersgd_copy_error(powersgd_state* st, int64_t bucket_index,
                                     int32_t view, float* e_dev, void* stream);
 
 /*
@@ -191,7 +197,7 @@ powersgd_status powersgd_copy_error(powersgd_state* st, int64_t bucket_index,
  * calls, numel_comm = elements an allreduce would carry ((n + m) * rank per compressed
  * view, numel per other view). Host values; synchronous.
  */
-powersgd_status powersgd_get_stats(powersgd_state* st, int64_t* iteration,
+POWERSGD_API powersgd_status powersgd_get_stats(powersgd_state* st, int64_t* iteration,
                                    int64_t* numel_in, int64_t* numel_comm);
 
 /* --- kernel timing (HIP events on the caller's stream) ------------------------ */
@@ -204,7 +210,7 @@ powersgd_status powersgd_get_stats(powersgd_state* st, int64_t* iteration,
  * (Gram partials read from P or Q, ranks > 8 and the initial Q) */
 
 /* Turns per-kernel event timing on (non-zero) or off; clears accumulated times. */
-powersgd_status powersgd_set_timing(powersgd_state* st, int32_t enable);
+POWERSGD_API powersgd_status powersgd_set_timing(powersgd_state* st, int32_t enable);
 
 /*
  * Waits for the recorded events and returns, per kernel kind, the summed duration in
@@ -212,11 +218,11 @@ powersgd_status powersgd_set_timing(powersgd_state* st, int32_t enable);
  * moved (minimum HBM traffic of each pass). Arrays of POWERSGD_NUM_KERNELS entries,
  * any may be NULL.
  */
-powersgd_status powersgd_get_kernel_times(powersgd_state* st, double* ms,
+POWERSGD_API powersgd_status powersgd_get_kernel_times(powersgd_state* st, double* ms,
                                           int64_t* launches, double* bytes);
 
 /* Name of a kernel kind ("" if out of range). */
-const char* powersgd_kernel_name(int32_t kind);
+POWERSGD_API const char* powersgd_kernel_name(int32_t kind);
 
 #ifdef __cplusplus
 }

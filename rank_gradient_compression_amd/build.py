@@ -15,7 +15,7 @@ SOURCES = ["host.cpp", "kernels.hip"]
 
 # Packed fp32 instructions are switched off for every HIP translation unit.
 HIP_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
 ]

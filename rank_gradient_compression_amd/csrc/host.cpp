@@ -119,6 +119,7 @@ struct BucketPlan {
   std::vector<Tile> pgram_tiles, qgram_tiles;  // (job, partial) for the Gram kernel
   std::vector<QInitJob> qinit;
   int64_t max_qcount = 0;
+  int max_prows = 0, max_qrows = 0;
   int64_t e_floats = 0, p_floats = 0, q_floats = 0, partial_floats = 0, gram_doubles = 0;
 
   // device memory
@@ -405,6 +406,8 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
     }
     pl.qinit.push_back(QInitJob{d.qoff, d.m, d.rank, d.view, 0});
     pl.max_qcount = std::max<int64_t>(pl.max_qcount, static_cast<int64_t>(d.m) * d.rank);
+    pl.max_prows = std::max(pl.max_prows, d.n);
+    pl.max_qrows = std::max(pl.max_qrows, d.m);
     pl.tensors.push_back(d);
   }
   pl.e_floats = eoff;
@@ -678,7 +681,7 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
       });
       if (r != POWERSGD_OK) return r;
       r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize Q", [&] {
-        return launch_orth(R, pl.d_qjobs, nt, pl.Q, pl.gram, eps, nullptr, s);
+        return launch_orth(R, pl.d_qjobs, nt, pl.max_qrows, pl.Q, pl.gram, eps, nullptr, s);
       });
       if (r != POWERSGD_OK) return r;
     }
@@ -713,8 +716,8 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
       if (r != POWERSGD_OK) return r;
     }
     r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize P", [&] {
-      return launch_orth(R, pl.d_pjobs, nt, pl.P, pl.gram, eps, f16 ? found_inf_dev : nullptr,
-                         s);
+      return launch_orth(R, pl.d_pjobs, nt, pl.max_prows, pl.P, pl.gram, eps,
+                         f16 ? found_inf_dev : nullptr, s);
     });
     if (r != POWERSGD_OK) return r;
     // Step 3.5 (step 3.6 is the identity).

@@ -142,8 +142,9 @@ hipError_t launch_pass3(int R, bool f16, bool ef, const Pass3Args& a, hipStream_
 hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs,
                        const float* base, double* gram, const int32_t* found_inf,
                        hipStream_t s);
-hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, float* base, const double* gram,
-                       double eps, const int32_t* found_inf, hipStream_t s);
+hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, int max_rows, float* base,
+                       const double* gram, double eps, const int32_t* found_inf,
+                       hipStream_t s);
 hipError_t launch_qinit(int R, const QInitJob* jobs, int njobs, int64_t max_count,
                         float* Q, uint64_t seed, uint64_t bucket_key, uint64_t epoch,
                         hipStream_t s);
@@ -158,5 +159,8 @@ constexpr int pass1_unroll(int R) { return R <= 4 ? 4 : 1; }
 constexpr int kMaxFusedGramRank = 8;
 // Rows per Gram partial of the separate Gram kernel.
 constexpr int kGramRows = 256;
+// Rows transformed by one workgroup of the orthogonalization kernel (each workgroup
+// recomputes the small r x r transform from the Gram partials).
+constexpr int kOrthRows = 1024;
 
 }  // namespace psgd

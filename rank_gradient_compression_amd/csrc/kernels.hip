@@ -34,7 +34,9 @@
 #include "internal.h"
 
 namespace psgd {
-namespace {
+// Kernels and their device helpers live in a named namespace so that profiler
+// output shows readable names (psgd::kern::k_pass1<...>).
+namespace kern {
 
 constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n >> 1); }
 
@@ -544,7 +546,7 @@ __global__ void __launch_bounds__(kThreads) k_pass2_reduce(Pass2ReduceArgs args)
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   constexpr int SLOT = kColBlock * R;
-  constexpr int B = 8;  // partial slots loaded before they are added (in order)
+  constexpr int B = 16;  // partial slots loaded before they are added (in order)
   const float* src = args.partial + static_cast<int64_t>(d.pslot + t.b * d.nrb) * SLOT;
   float* Qt = args.Q + d.qoff;
 #pragma unroll
@@ -687,10 +689,12 @@ __global__ void __launch_bounds__(kThreads)
   __shared__ double sC[R];
   __shared__ double sW[R];
   __shared__ double sRed[4][NG];
-  const OrthJob j = jobs[blockIdx.x];
+  const OrthJob j = jobs[blockIdx.y];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int row_begin = blockIdx.x * kOrthRows;
+  if (row_begin >= j.rows) return;
   // 1. G = sum of the partials, in partial order per thread, then the fixed-order
   //    combination of strided thread sums.
   {
@@ -734,11 +738,11 @@ __global__ void __launch_bounds__(kThreads)
           for (int p = 0; p < j.nparts; p += 8) {
             double v[8];
 #pragma unroll
-            for (int b = 0; b < 8; ++b)
-              v[b] = (p + b < j.nparts) ? gram[j.goff + static_cast<int64_t>(p + b) * NG + e]
-                                        : 0.0;
+          for (int b = 0; b < 8; ++b)
+            v[b] = (p + b < j.nparts) ? gram[j.goff + static_cast<int64_t>(p + b) * NG + e]
+                                      : 0.0;
 #pragma unroll
-            for (int b = 0; b < 8; ++b) s += v[b];
+          for (int b = 0; b < 8; ++b) s += v[b];
           }
           int a = 0, rem = e;
           while (rem >= R - a) {
@@ -795,18 +799,35 @@ __global__ void __launch_bounds__(kThreads)
     for (int l = 0; l < R; ++l) sT[l][lane] = cvec[l];
   }
   __syncthreads();
-  // 3. P <- P T in fp64, rounded once to fp32 (T is upper triangular)
+  // 3. P <- P T in fp64, rounded once to fp32, for this workgroup's rows; several
+  //    rows are loaded before any is transformed.
   float* X = base + j.off;
-  for (int row = tid; row < j.rows; row += kThreads) {
-    float x[R];
-    load_p_row<R>(X, row, x);
-    float* dst = X + static_cast<int64_t>(row) * R;
-#pragma unroll 1
-    for (int k = 0; k < R; ++k) {
-      double s = 0.0;
+  const int row_end = min(j.rows, row_begin + kOrthRows);
+  constexpr int B = R <= 8 ? 4 : 1;
+  for (int row0 = row_begin + tid; row0 < row_end; row0 += kThreads * B) {
+    float x[B][R];
 #pragma unroll
-      for (int l = 0; l < R; ++l) s += static_cast<double>(x[l]) * sT[l][k];
-      dst[k] = static_cast<float>(s);
+    for (int b = 0; b < B; ++b) {
+      const int row = row0 + b * kThreads;
+      if (row < row_end) {
+        load_p_row<R>(X, row, x[b]);
+      } else {
+#pragma unroll
+        for (int l = 0; l < R; ++l) x[b][l] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int row = row0 + b * kThreads;
+      if (row >= row_end) continue;
+      float* dst = X + static_cast<int64_t>(row) * R;
+#pragma unroll 1
+      for (int k = 0; k < R; ++k) {
+        double s = 0.0;
+#pragma unroll
+        for (int l = 0; l < R; ++l) s += static_cast<double>(x[b][l]) * sT[l][k];
+        dst[k] = static_cast<float>(s);
+      }
     }
   }
 }
@@ -932,7 +953,9 @@ hipError_t pass3_r(bool f16, bool ef, const Pass3Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-}  // namespace
+}  // namespace kern
+
+using namespace kern;
 
 #define PSGD_RANK_SWITCH(R, ...)                    \
   switch (R) {                                      \
@@ -975,11 +998,13 @@ hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs
   })
 }
 
-hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, float* base, const double* gram,
-                       double eps, const int32_t* found_inf, hipStream_t s) {
+hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, int max_rows, float* base,
+                       const double* gram, double eps, const int32_t* found_inf,
+                       hipStream_t s) {
   if (njobs == 0) return hipSuccess;
+  const dim3 grid((max_rows + kOrthRows - 1) / kOrthRows, njobs);
   PSGD_RANK_SWITCH(R, {
-    k_orth<RR><<<dim3(njobs), kThreads, 0, s>>>(jobs, base, gram, eps, found_inf);
+    k_orth<RR><<<grid, kThreads, 0, s>>>(jobs, base, gram, eps, found_inf);
     return hipGetLastError();
   })
 }

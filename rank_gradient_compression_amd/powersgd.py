@@ -68,11 +68,12 @@ _lib: Optional[ctypes.CDLL] = None
 
 
 def load_library(path: Optional[str] = None) -> ctypes.CDLL:
-    """Loads the built library (raises if it has not been built)."""
+    """Loads the built library (raises if it has not been built). The environment
+    variable RGC_POWERSGD_LIBRARY may name another build of it."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    path = path or _build.library_path()
+    path = path or os.environ.get("RGC_POWERSGD_LIBRARY") or _build.library_path()
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it first (python -m rank_gradient_compression_amd.build)")
