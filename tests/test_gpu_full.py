@@ -1,0 +1,102 @@
+"""GPU parity at the benchmark workloads' full sizes, with the benchmark's own
+plans (same views, hyperparameters, launch configuration) and inputs generated on
+the GPU. The ResNet-50-shaped bucket is compared whole against the oracle; for the
+larger buckets the oracle follows a sample of views (one or two per shape) through
+every step with its own per-matrix functions, every other view is checked through
+properties that hold at any size (vectors untouched, M_hat + E = M' + E_prev)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import TOL, BucketParity, StepReport, TensorTrack, compare_sampled, log, numel
+from rank_gradient_compression_amd import PowerSGDState
+from synthetic import CONFIGS, BucketGenerator
+
+pytestmark = pytest.mark.gpu
+
+
+def test_resnet50_bucket_full_every_view_every_step():
+    cfg = CONFIGS[1]
+    log(f"case: {cfg.name} full size, {cfg.steps} steps, whole-bucket oracle")
+    gen = BucketGenerator(cfg, "cuda")
+    par = BucketParity(cfg.hparams, cfg.views(), "f32")
+    for step in range(cfg.steps):
+        rep = par.step(gen.bucket(step).cpu(), step)
+        log(f"  step {step}: " + ", ".join(f"{k}={v:.2e}" for k, v in rep.worst.items()))
+
+
+def _sampled(cfg, sample_views, steps=None):
+    views = cfg.views()
+    gen = BucketGenerator(cfg, "cuda")
+    hp = dict(cfg.hparams)
+    hp["compression_stats_logging_frequency"] = 0
+    gpu = PowerSGDState(**hp)
+    tracks = {}
+    tol = TOL[cfg.dtype]
+    scale = cfg.loss_scale
+    found = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e_prev_sum = None
+    for step in range(cfg.steps if steps is None else steps):
+        if cfg.dtype == "f16":
+            bucket = gen.bucket(step, loss_scale=scale)
+            inv = 1.0 / scale
+        else:
+            bucket = gen.bucket(step)
+            inv = 1.0
+        host_in = {vi: bucket[off:off + numel(shp)].cpu() for vi, (off, shp) in
+                   enumerate(views) if vi in sample_views}
+        vec_in = [(off, bucket[off:off + numel(shp)].clone()) for off, shp in views
+                  if len(shp) < 2]
+        inf = False
+        if cfg.dtype == "f16":
+            inf = oracle.any_nonfinite(bucket.cpu().numpy(), views)
+        found.zero_()
+        gpu.compress_bucket(bucket, views, inv_loss_scale=inv,
+                            found_inf=found if cfg.dtype == "f16" else None)
+        torch.cuda.synchronize()
+        rep = StepReport(step=step, found_inf=inf)
+        if cfg.dtype == "f16":
+            assert bool(found.item()) == inf, step
+        if inf:
+            log(f"  step {step}: inf found, skipped")
+            scale *= 0.5
+            continue
+        for vi in sample_views:
+            off, shp = views[vi]
+            n, m, r = gpu.view_info(0, vi)
+            if vi not in tracks:
+                tracks[vi] = TensorTrack(hp, vi, n, m, r)
+            g = host_in[vi].double().numpy()
+            if cfg.dtype == "f16":
+                g = g * inv
+            vr = tracks[vi].step(g, step)
+            compare_sampled(gpu, 0, vi, vr, bucket[off:off + numel(shp)], tol, rep)
+        for off, v in vec_in:
+            got = bucket[off:off + v.numel()]
+            if cfg.dtype == "f32":
+                assert torch.equal(got, v)
+            else:
+                exp = (v.float() * inv).half()
+                assert torch.equal(got.view(torch.int16), exp.view(torch.int16))
+        log(f"  step {step}: " + ", ".join(f"{k}={v:.2e}" for k, v in rep.worst.items()))
+    return gpu
+
+
+def test_bert_large_bucket_full_sampled_views():
+    cfg = CONFIGS[2]
+    # first layer's Q, FFN-in, FFN-out and the last layer's attention output
+    log(f"case: {cfg.name} full size, {cfg.steps} steps, sampled views")
+    _sampled(cfg, sample_views=[0, 4, 5, 369])
+
+
+def test_amp_bucket_full_sampled_views_with_inf_step():
+    cfg = CONFIGS[4]
+    log(f"case: {cfg.name} full size, {cfg.steps} steps (inf at step 10), sampled views")
+    _sampled(cfg, sample_views=[0, 4, 5])
+
+
+def test_gpt_bucket_full_sampled_views():
+    cfg = CONFIGS[3]
+    log(f"case: {cfg.name} full size, {cfg.steps} steps, sampled views")
+    _sampled(cfg, sample_views=[0, 3, 4, 39])
