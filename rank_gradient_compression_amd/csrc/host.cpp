@@ -121,11 +121,13 @@ struct BucketPlan {
   int64_t max_qcount = 0;
   int max_prows = 0, max_qrows = 0;
   int64_t e_floats = 0, p_floats = 0, q_floats = 0, partial_floats = 0, gram_doubles = 0;
+  int64_t qt_floats = 0;
 
   // device memory
   float* E = nullptr;
   float* P = nullptr;
   float* Q = nullptr;
+  float* QT = nullptr;  // matrix-core ranks: Q transposed
   float* partial = nullptr;
   double* gram = nullptr;
   Tile* d_pgram_tiles = nullptr;
@@ -144,12 +146,12 @@ struct BucketPlan {
   bool q_ready = false;
 
   void release() {
-    void* ptrs[] = {E, P, Q, partial, gram, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
+    void* ptrs[] = {E, P, Q, QT, partial, gram, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
                     d_tiles1, d_tiles23, d_tiles2r, d_flat_unc, d_flat_all, d_pjobs, d_qjobs,
                     d_qinit};
     for (void* p : ptrs)
       if (p) (void)hipFree(p);
-    E = P = Q = partial = nullptr;
+    E = P = Q = QT = partial = nullptr;
     gram = nullptr;
     d_pgram_tiles = d_qgram_tiles = nullptr;
     d_td = d_td_scalar = nullptr;
@@ -341,7 +343,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
   const int64_t ng = static_cast<int64_t>(R) * (R + 1) / 2;
   const bool fused_gram = R <= kMaxFusedGramRank;
   int64_t goff = 0;
-  int64_t eoff = 0, poff = 0, qoff = 0;
+  int64_t eoff = 0, poff = 0, qoff = 0, qtoff = 0;
   int32_t pslot = 0;
   for (size_t v = 0; v < nv; ++v) {
     if (!pl.decision[v]) continue;
@@ -358,13 +360,25 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
     eoff += round_up(static_cast<int64_t>(d.n) * d.m, 64);
     poff += round_up(static_cast<int64_t>(d.n) * R, 64);
     qoff += round_up(static_cast<int64_t>(d.m) * R, 64);
+    d.mstride = static_cast<int32_t>(round_up(d.m, 4));
+    d.qtoff = -1;
+    if (R >= kMfmaMinRank) {
+      d.qtoff = qtoff;
+      qtoff += round_up(static_cast<int64_t>(d.mstride) * R, 64);
+    }
     const int32_t ti = static_cast<int32_t>(pl.tensors.size());
     // pass 1: whole rows; slots of lprw threads sweep 4 * lprw columns at a time
+    // (matrix-core ranks: 16 rows per wavefront)
     d.lprw = pow2_ceil(static_cast<int>((std::min<int64_t>(d.m, 4 * kThreads) + 3) / 4));
     {
-      const int64_t slots = kThreads / d.lprw;
-      int64_t rows = round_up(std::max<int64_t>(1, (target + d.m - 1) / d.m), slots * unroll1);
-      rows = std::min<int64_t>(rows, round_up(d.n, slots));
+      int64_t rows;
+      if (R >= kMfmaMinRank) {
+        rows = kMfmaPass1Rows;
+      } else {
+        const int64_t slots = kThreads / d.lprw;
+        rows = round_up(std::max<int64_t>(1, (target + d.m - 1) / d.m), slots * unroll1);
+        rows = std::min<int64_t>(rows, round_up(d.n, slots));
+      }
       d.rpb1 = static_cast<int32_t>(rows);
       for (int64_t r0 = 0, rb = 0; r0 < d.n; r0 += rows, ++rb)
         pl.tiles1.push_back(Tile{ti, static_cast<int32_t>(rb), 0, 0});
@@ -374,7 +388,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
       const int32_t rpp = fused_gram ? d.rpb1 : kGramRows;
       const int32_t nparts = static_cast<int32_t>((d.n + rpp - 1) / rpp);
       d.goff = goff;
-      pl.pjobs.push_back(OrthJob{d.poff, goff, d.n, d.rank, nparts, rpp});
+      pl.pjobs.push_back(OrthJob{d.poff, goff, -1, d.n, d.rank, nparts, rpp, 0, 0});
       if (!fused_gram)
         for (int32_t pp = 0; pp < nparts; ++pp)
           pl.pgram_tiles.push_back(Tile{static_cast<int32_t>(pl.pjobs.size() - 1), pp, 0, 0});
@@ -386,6 +400,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
     const int64_t rpw = 64 / d.lpr;
     int64_t rpb = round_up(std::max<int64_t>(1, (target + width - 1) / width), 16 * rpw);
     rpb = std::min<int64_t>(rpb, round_up(d.n, 4 * rpw));
+    if (R >= kMfmaMinRank) rpb = std::min<int64_t>(kMfmaRowBlock, round_up(d.n, 16));
     d.rpb = static_cast<int32_t>(rpb);
     d.nrb = static_cast<int32_t>((d.n + rpb - 1) / rpb);
     d.ncb = static_cast<int32_t>((d.m + kColBlock - 1) / kColBlock);
@@ -399,7 +414,8 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
       for (int32_t rb = 0; rb < d.nrb; ++rb) pl.tiles23.push_back(Tile{ti, rb, cb, 0});
     {
       const int32_t nparts = static_cast<int32_t>((d.m + kGramRows - 1) / kGramRows);
-      pl.qjobs.push_back(OrthJob{d.qoff, goff, d.m, d.rank, nparts, kGramRows});
+      pl.qjobs.push_back(
+          OrthJob{d.qoff, goff, d.qtoff, d.m, d.rank, nparts, kGramRows, d.mstride, 0});
       for (int32_t pp = 0; pp < nparts; ++pp)
         pl.qgram_tiles.push_back(Tile{static_cast<int32_t>(pl.qjobs.size() - 1), pp, 0, 0});
       goff += nparts * ng;
@@ -415,6 +431,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
   pl.q_floats = qoff;
   pl.partial_floats = static_cast<int64_t>(pslot) * kColBlock * R;
   pl.gram_doubles = goff;
+  pl.qt_floats = qtoff;
   return POWERSGD_OK;
 }
 
@@ -430,6 +447,7 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   ok = ok && alloc(reinterpret_cast<void**>(&pl.E), need_e ? pl.e_floats * sizeof(float) : 0);
   ok = ok && alloc(reinterpret_cast<void**>(&pl.P), pl.p_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.Q), pl.q_floats * sizeof(float));
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.QT), pl.qt_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.partial), pl.partial_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.gram), pl.gram_doubles * sizeof(double));
 
@@ -441,6 +459,7 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   if (pl.E && e == hipSuccess) e = hipMemsetAsync(pl.E, 0, pl.e_floats * sizeof(float), s);
   if (pl.P && e == hipSuccess) e = hipMemsetAsync(pl.P, 0, pl.p_floats * sizeof(float), s);
   if (pl.Q && e == hipSuccess) e = hipMemsetAsync(pl.Q, 0, pl.q_floats * sizeof(float), s);
+  if (pl.QT && e == hipSuccess) e = hipMemsetAsync(pl.QT, 0, pl.qt_floats * sizeof(float), s);
 
   if (e != hipSuccess) {
     pl.release();
@@ -681,7 +700,8 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
       });
       if (r != POWERSGD_OK) return r;
       r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize Q", [&] {
-        return launch_orth(R, pl.d_qjobs, nt, pl.max_qrows, pl.Q, pl.gram, eps, nullptr, s);
+        return launch_orth(R, pl.d_qjobs, nt, pl.max_qrows, pl.Q, pl.QT, pl.gram, eps, nullptr,
+                           s);
       });
       if (r != POWERSGD_OK) return r;
     }
@@ -697,6 +717,7 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
     a.bucket = bucket;
     a.E = pl.E;
     a.Q = pl.Q;
+    a.QT = pl.QT;
     a.P = pl.P;
     a.gram = pl.gram;
     a.inv_scale = inv_loss_scale;
@@ -716,7 +737,7 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
       if (r != POWERSGD_OK) return r;
     }
     r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize P", [&] {
-      return launch_orth(R, pl.d_pjobs, nt, pl.max_prows, pl.P, pl.gram, eps,
+      return launch_orth(R, pl.d_pjobs, nt, pl.max_prows, pl.P, nullptr, pl.gram, eps,
                          f16 ? found_inf_dev : nullptr, s);
     });
     if (r != POWERSGD_OK) return r;
@@ -729,6 +750,7 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
     a.E = pl.E;
     a.P = pl.P;
     a.Q = pl.Q;
+    a.QT = pl.QT;
     a.partial = pl.partial;
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
@@ -742,6 +764,7 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
       b.td = td;
       b.partial = pl.partial;
       b.Q = pl.Q;
+      b.QT = pl.QT;
       b.found_inf = f16 ? found_inf_dev : nullptr;
       r = timed_launch(st, s, K_PASS2R, 0.0, "pass 2 reduce",
                        [&] { return launch_pass2_reduce(R, b, s); });

@@ -31,6 +31,9 @@ struct TensorDesc {
   int32_t vec;    // 1: m % 4 == 0 and rows start 16-byte aligned in the bucket
   int32_t view;   // index of the view in the bucket (Q draw counter word)
   int64_t goff;   // first double of its P Gram partials (one per pass-1 row block)
+  int64_t qtoff;  // matrix-core ranks: first float of Q^T (R rows of mstride floats)
+  int32_t mstride;  // row stride of Q^T: m rounded up to a multiple of 4 (padding zero)
+  int32_t pad0;
   int32_t lprw;   // pass 1: threads per row slot (power of two, <= 256)
   int32_t rpb1;   // pass 1: rows per row block
   int32_t lpr;    // pass 2/3: lanes per row slot (power of two, <= 64)
@@ -61,10 +64,13 @@ struct FlatTile {
 struct OrthJob {
   int64_t off;
   int64_t goff;
+  int64_t toff;     // >= 0: also write the result transposed (R rows of tstride floats)
   int32_t rows;
   int32_t rank;
   int32_t nparts;
   int32_t rpp;
+  int32_t tstride;
+  int32_t pad;
 };
 
 // Packed upper-triangle index of Gram entry (i, j), i <= j < R.
@@ -92,6 +98,7 @@ struct Pass1Args {
   float* E;
   const float* Q;
   float* P;
+  const float* QT;         // matrix-core ranks: Q^T (B fragments as 16-byte loads)
   double* gram;            // P Gram partials (ranks <= 8: computed here)
   float inv_scale;
   int32_t* found_inf;
@@ -105,6 +112,7 @@ struct Pass2Args {
   const float* E;
   const float* P;
   float* Q;
+  float* QT;               // matrix-core ranks: Q^T, written next to Q (else null)
   float* partial;
   float inv_scale;
   const int32_t* found_inf;
@@ -117,6 +125,7 @@ struct Pass2ReduceArgs {
   const TensorDesc* td;
   const float* partial;
   float* Q;
+  float* QT;               // matrix-core ranks: Q^T, written next to Q (else null)
   const int32_t* found_inf;
 };
 
@@ -143,8 +152,8 @@ hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs
                        const float* base, double* gram, const int32_t* found_inf,
                        hipStream_t s);
 hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, int max_rows, float* base,
-                       const double* gram, double eps, const int32_t* found_inf,
-                       hipStream_t s);
+                       float* tbase, const double* gram, double eps,
+                       const int32_t* found_inf, hipStream_t s);
 hipError_t launch_qinit(int R, const QInitJob* jobs, int njobs, int64_t max_count,
                         float* Q, uint64_t seed, uint64_t bucket_key, uint64_t epoch,
                         hipStream_t s);
@@ -157,6 +166,12 @@ constexpr int pass1_unroll(int R) { return R <= 4 ? 4 : 1; }
 // Pass 1 also accumulates the Gram partials of P up to this padded rank; above it a
 // separate Gram kernel reads P.
 constexpr int kMaxFusedGramRank = 8;
+// Padded ranks from this value up run the three passes on matrix cores
+// (v_mfma_f32_16x16x4f32): pass-1 row blocks are 64 rows (16 per wavefront), pass 2
+// and pass 3 tiles are kMfmaRowBlock rows x 256 columns (64 per wavefront).
+constexpr int kMfmaMinRank = 16;
+constexpr int kMfmaPass1Rows = 64;
+constexpr int kMfmaRowBlock = 1024;
 // Rows per Gram partial of the separate Gram kernel.
 constexpr int kGramRows = 256;
 // Rows transformed by one workgroup of the orthogonalization kernel (each workgroup

@@ -564,7 +564,9 @@ __global__ void __launch_bounds__(kThreads) k_pass2_reduce(Pass2ReduceArgs args)
 #pragma unroll
         for (int b = 0; b < B; ++b) s += v[b];
       }
-      Qt[static_cast<int64_t>(col) * R + k] = (k < d.rank) ? s : 0.f;
+      const float q = (k < d.rank) ? s : 0.f;
+      Qt[static_cast<int64_t>(col) * R + k] = q;
+      if (args.QT != nullptr) args.QT[d.qtoff + static_cast<int64_t>(k) * d.mstride + col] = q;
     }
   }
 }
@@ -639,6 +641,391 @@ __global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
   }
 }
 
+// ------------------------------------------------- matrix-core passes (R = 16, 32)
+//
+// For ranks 16 and 32 each element of M' meets R multiply-adds in every pass, so the
+// three passes run on v_mfma_f32_16x16x4f32 (lane l supplies A[l%16][l/16] and
+// B[l/16][l%16]; D register v of lane l is D[4*(l/16)+v][l%16]). A lane's 16-byte
+// load of 4 consecutive columns feeds 4 MFMA K-steps (or 4 output rows) directly.
+
+typedef float mfma_f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ mfma_f4 mfma16(float a, float b, mfma_f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Loads 4 gradient values of a 16-byte aligned group without a branch (address
+// already clamped into the matrix); fp16 values are unscaled, `raw_bad` tells whether
+// any of them is inf or NaN.
+template <bool F16>
+__device__ __forceinline__ void load_grad4_vec(const void* bucket, int64_t idx, float inv_scale,
+                                               float (&x)[4], bool& raw_bad) {
+  if constexpr (F16) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(bucket) + idx);
+    const uint16_t raw[4] = {static_cast<uint16_t>(w.x & 0xFFFFu), static_cast<uint16_t>(w.x >> 16),
+                             static_cast<uint16_t>(w.y & 0xFFFFu), static_cast<uint16_t>(w.y >> 16)};
+    raw_bad = false;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      raw_bad |= half_bits_not_finite(raw[a]);
+      x[a] = half_bits_to_float(raw[a]) * inv_scale;
+    }
+  } else {
+    const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(bucket) + idx);
+    x[0] = w.x;
+    x[1] = w.y;
+    x[2] = w.z;
+    x[3] = w.w;
+    raw_bad = false;
+  }
+}
+
+__device__ __forceinline__ void load_f4(const float* p, float (&x)[4]) {
+  const float4 w = *reinterpret_cast<const float4*>(p);
+  x[0] = w.x;
+  x[1] = w.y;
+  x[2] = w.z;
+  x[3] = w.w;
+}
+
+// Pass 1, P = M' Q: a wavefront owns 16 rows; K advances 16 columns per step (lane
+// group h loads columns 4h..4h+3, MFMA K-step s pairs them with Q row 4h+s, read as
+// 16 bytes of Q^T). VEC: rows are 16-byte aligned, so all loads of U steps are issued
+// from clamped addresses before any is used, and invalid lanes are masked after.
+template <int R, bool F16, bool EF, bool VEC>
+__device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const TensorDesc& d,
+                                                const Tile& t, int lane, int wave) {
+  constexpr int NT = R / 16;
+  constexpr int U = 4;
+  const int m = d.m;
+  const int r0 = t.a * d.rpb1;
+  const int r1 = min(d.n, r0 + d.rpb1);
+  const int h = lane >> 4;
+  const int cl = lane & 15;
+  const int rw = r0 + 16 * wave;
+  if (rw >= r1) return;
+  const int row = rw + cl;
+  const bool row_ok = row < r1;
+  const int rowc = min(row, r1 - 1);
+  float* __restrict__ Et = args.E + d.eoff;
+  const float* __restrict__ QTt = args.QT + d.qtoff;
+  mfma_f4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
+  int bad = 0;
+  for (int k0 = 0; k0 < m; k0 += 16 * U) {
+    float x[U][4];
+    float e[U][4];
+    float b[U][NT][4];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int col = k0 + 16 * u + 4 * h;
+      ok[u] = row_ok && col < m;
+      if constexpr (VEC) {
+        const int colc = min(col, m - 4);
+        const int64_t off = static_cast<int64_t>(rowc) * m + colc;
+        bool rb;
+        load_grad4_vec<F16>(args.bucket, d.boff + off, args.inv_scale, x[u], rb);
+        if (ok[u] && rb) bad = 1;
+        if constexpr (EF) load_f4(Et + off, e[u]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          load_f4(QTt + static_cast<int64_t>(16 * nt + cl) * d.mstride + colc, b[u][nt]);
+      } else {
+        if (ok[u]) {
+          const int64_t off = static_cast<int64_t>(row) * m + col;
+          load_grad4<F16>(args.bucket, d.boff + off, false, m - col, args.inv_scale, x[u], bad);
+          if constexpr (EF) load_f32x4(Et + off, false, m - col, e[u]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            b[u][nt][a] = (col + a < m) ? QTt[static_cast<int64_t>(16 * nt + cl) * d.mstride + col + a]
+                                        : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int col = k0 + 16 * u + 4 * h;
+      if constexpr (VEC) {
+        if (col >= m) {  // clamped duplicate columns: contribute nothing
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) b[u][nt][a] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float v = x[u][a];
+        if constexpr (EF) v += e[u][a];
+        x[u][a] = ok[u] ? v : 0.f;
+      }
+      if constexpr (EF && !F16) {
+        if (ok[u])
+          store_f32x4(static_cast<float*>(args.bucket) + d.boff + static_cast<int64_t>(row) * m + col,
+                      VEC, m - col, x[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(x[u][s4], b[u][nt][s4], acc[nt]);
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int prow = rw + 4 * h + v;
+      const int k = 16 * nt + cl;
+      if (prow < r1)
+        args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? acc[nt][v] : 0.f;
+    }
+  }
+  if constexpr (F16) {
+    if (__any(bad) && lane == 0) atomicOr(args.found_inf, 1);
+  }
+}
+
+template <int R, bool F16, bool EF>
+__global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
+  const int lane = threadIdx.x & 63;
+  if (static_cast<int>(blockIdx.x) >= args.ntiles) {
+    if constexpr (F16)
+      f16_check_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.found_inf);
+    return;
+  }
+  const int wave = wave_index();
+  const Tile t = args.tiles[blockIdx.x];
+  const TensorDesc d = args.td[t.tensor];
+  if (d.vec)
+    pass1_mfma_body<R, F16, EF, true>(args, d, t, lane, wave);
+  else
+    pass1_mfma_body<R, F16, EF, false>(args, d, t, lane, wave);
+}
+
+// Pass 2, Q = M'^T P: a wavefront owns 64 columns of the tile; lane group h takes row
+// 4 * step + h, lane cl the columns 4cl..4cl+3, so accumulator s holds the output
+// columns c0 + 4i + s (i = MFMA output row).
+template <int R, bool F16, bool EF, bool VEC>
+__device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const TensorDesc& d,
+                                                const Tile& t, int lane, int wave) {
+  constexpr int NT = R / 16;
+  constexpr int U = 4;
+  const int m = d.m;
+  const int r0 = t.a * d.rpb;
+  const int r1 = min(d.n, r0 + d.rpb);
+  const int h = lane >> 4;
+  const int cl = lane & 15;
+  const int c0 = t.b * kColBlock + 64 * wave;
+  if (c0 >= m) return;
+  const int col = c0 + 4 * cl;
+  const bool col_ok = col < m;
+  const int colc = VEC ? min(col, m - 4) : col;
+  const float* __restrict__ Pt = args.P + d.poff;
+  const float* __restrict__ Et = args.E + d.eoff;
+  mfma_f4 acc[4][NT];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[s4][nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
+  for (int rr = r0; rr < r1; rr += 4 * U) {
+    float x[U][4];
+    float p[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = rr + 4 * u + h;
+      const int rowc = min(row, r1 - 1);
+      if constexpr (VEC) {
+        const int64_t off = static_cast<int64_t>(rowc) * m + colc;
+        bool rb;
+        load_grad4_vec<F16>(args.bucket, d.boff + off, args.inv_scale, x[u], rb);
+        if constexpr (F16 && EF) {
+          float e[4];
+          load_f4(Et + off, e);
+#pragma unroll
+          for (int a = 0; a < 4; ++a) x[u][a] += e[a];
+        }
+      } else {
+        if (row < r1 && col_ok) {
+          load_mprime4<F16, EF>(args.bucket, Et, d, static_cast<int64_t>(row) * m + col, false,
+                                m - col, args.inv_scale, x[u]);
+        } else {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) x[u][a] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) p[u][nt] = Pt[static_cast<int64_t>(rowc) * R + 16 * nt + cl];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool rok = rr + 4 * u + h < r1;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) x[u][a] = (rok && col_ok) ? x[u][a] : 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) p[u][nt] = rok ? p[u][nt] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[s4][nt] = mfma16(x[u][s4], p[u][nt], acc[s4][nt]);
+  }
+  float* Qt = args.Q + d.qoff;
+  float* part = args.partial + static_cast<int64_t>(d.pslot + t.b * d.nrb + t.a) * (kColBlock * R);
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int qcol = c0 + 16 * h + 4 * v + s4;  // output row i = 4h + v -> column c0 + 4i + s
+        const int k = 16 * nt + cl;
+        if (qcol < m) {
+          const float val = acc[s4][nt][v];
+          if (d.nrb == 1) {
+            const float q = (k < d.rank) ? val : 0.f;
+            Qt[static_cast<int64_t>(qcol) * R + k] = q;
+            args.QT[d.qtoff + static_cast<int64_t>(k) * d.mstride + qcol] = q;
+          } else {
+            part[(qcol - t.b * kColBlock) * R + k] = val;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int R, bool F16, bool EF>
+__global__ void __launch_bounds__(kThreads) k_pass2_mfma(Pass2Args args) {
+  if (F16 && *args.found_inf) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_index();
+  const Tile t = args.tiles[blockIdx.x];
+  const TensorDesc d = args.td[t.tensor];
+  if (d.vec)
+    pass2_mfma_body<R, F16, EF, true>(args, d, t, lane, wave);
+  else
+    pass2_mfma_body<R, F16, EF, false>(args, d, t, lane, wave);
+}
+
+// Pass 3, M_hat = P Q^T and E = M' - M_hat, computed as (Q P^T)^T so that lane l
+// holds 4 consecutive columns (4h..4h+3) of row cl of each 16 x 16 output block.
+// MFMA K-step kq of lane group h uses rank index h * KQ + kq, so A and B fragments are
+// KQ consecutive floats of a Q row and of a P row.
+template <int R, bool F16, bool EF, bool VEC>
+__device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const TensorDesc& d,
+                                                const Tile& t, int lane, int wave) {
+  constexpr int KQ = R / 4;
+  constexpr int UR = 2;  // 16-row steps loaded before use
+  const int m = d.m;
+  const int r0 = t.a * d.rpb;
+  const int r1 = min(d.n, r0 + d.rpb);
+  const int h = lane >> 4;
+  const int cl = lane & 15;
+  const int c0 = t.b * kColBlock + 64 * wave;
+  if (c0 >= m) return;
+  const float* __restrict__ Pt = args.P + d.poff;
+  const float* __restrict__ Qt = args.Q + d.qoff;
+  float* __restrict__ Et = args.E + d.eoff;
+  float qa[4][KQ];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int qcol = min(c0 + 16 * g + cl, m - 1);
+#pragma unroll
+    for (int k4 = 0; k4 < KQ / 4; ++k4) {
+      float w[4];
+      load_f4(Qt + static_cast<int64_t>(qcol) * R + h * KQ + 4 * k4, w);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) qa[g][4 * k4 + a] = w[a];
+    }
+  }
+  for (int rr = r0; rr < r1; rr += 16 * UR) {
+    float pb[UR][KQ];
+    float x[UR][4][4];
+#pragma unroll
+    for (int ur = 0; ur < UR; ++ur) {
+      const int row = rr + 16 * ur + cl;
+      const int rowc = min(row, r1 - 1);
+#pragma unroll
+      for (int k4 = 0; k4 < KQ / 4; ++k4) {
+        float w[4];
+        load_f4(Pt + static_cast<int64_t>(rowc) * R + h * KQ + 4 * k4, w);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) pb[ur][4 * k4 + a] = w[a];
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = c0 + 16 * g + 4 * h;
+        if constexpr (VEC) {
+          const int64_t off = static_cast<int64_t>(rowc) * m + min(col, m - 4);
+          bool rb;
+          load_grad4_vec<F16>(args.bucket, d.boff + off, args.inv_scale, x[ur][g], rb);
+          if constexpr (F16 && EF) {
+            float e[4];
+            load_f4(Et + off, e);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) x[ur][g][a] += e[a];
+          }
+        } else {
+          if (row < r1 && col < m)
+            load_mprime4<F16, EF>(args.bucket, Et, d, static_cast<int64_t>(row) * m + col, false,
+                                  m - col, args.inv_scale, x[ur][g]);
+        }
+      }
+    }
+#pragma unroll
+    for (int ur = 0; ur < UR; ++ur) {
+      const int row = rr + 16 * ur + cl;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        mfma_f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) acc = mfma16(qa[g][kq], pb[ur][kq], acc);
+        const int col = c0 + 16 * g + 4 * h;
+        if (row < r1 && col < m) {
+          const int64_t off = static_cast<int64_t>(row) * m + col;
+          float mh[4] = {acc[0], acc[1], acc[2], acc[3]};
+          if constexpr (F16)
+            store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, VEC, m - col, mh);
+          else
+            store_f32x4(static_cast<float*>(args.bucket) + d.boff + off, VEC, m - col, mh);
+          if constexpr (EF) {
+            float e[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) e[a] = x[ur][g][a] - mh[a];
+            store_f32x4(Et + off, VEC, m - col, e);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int R, bool F16, bool EF>
+__global__ void __launch_bounds__(kThreads) k_pass3_mfma(Pass3Args args) {
+  if (F16 && *args.found_inf) return;
+  if (static_cast<int>(blockIdx.x) >= args.ntiles) {
+    if constexpr (F16)
+      f16_unscale_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.inv_scale);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_index();
+  const Tile t = args.tiles[blockIdx.x];
+  const TensorDesc d = args.td[t.tensor];
+  if (d.vec)
+    pass3_mfma_body<R, F16, EF, true>(args, d, t, lane, wave);
+  else
+    pass3_mfma_body<R, F16, EF, false>(args, d, t, lane, wave);
+}
+
 // ------------------------------------------------------------ orthogonalization
 //
 // Gram-Schmidt with epsilon (step 3.4) evaluated on the Gram matrix: every vector
@@ -680,7 +1067,7 @@ __global__ void __launch_bounds__(kThreads)
 
 template <int R>
 __global__ void __launch_bounds__(kThreads)
-    k_orth(const OrthJob* __restrict__ jobs, float* __restrict__ base,
+    k_orth(const OrthJob* __restrict__ jobs, float* __restrict__ base, float* __restrict__ tbase,
            const double* __restrict__ gram, double eps, const int32_t* __restrict__ found_inf) {
   if (found_inf != nullptr && *found_inf) return;
   constexpr int NG = gram_size<R>();
@@ -827,6 +1214,8 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int l = 0; l < R; ++l) s += static_cast<double>(x[b][l]) * sT[l][k];
         dst[k] = static_cast<float>(s);
+        if (j.toff >= 0)
+          tbase[j.toff + static_cast<int64_t>(k) * j.tstride + row] = static_cast<float>(s);
       }
     }
   }
@@ -921,6 +1310,13 @@ template <int R>
 hipError_t pass1_r(bool f16, bool ef, const Pass1Args& a, hipStream_t s) {
   const dim3 grid(a.ntiles + (f16 ? a.nftiles : 0));
   if (grid.x == 0) return hipSuccess;
+  if constexpr (R >= kMfmaMinRank) {
+    if (f16 && ef) k_pass1_mfma<R, true, true><<<grid, kThreads, 0, s>>>(a);
+    else if (f16) k_pass1_mfma<R, true, false><<<grid, kThreads, 0, s>>>(a);
+    else if (ef) k_pass1_mfma<R, false, true><<<grid, kThreads, 0, s>>>(a);
+    else k_pass1_mfma<R, false, false><<<grid, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
   constexpr int U = unroll1<R>();
   if (f16 && ef) k_pass1<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
   else if (f16) k_pass1<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
@@ -933,6 +1329,13 @@ template <int R>
 hipError_t pass2_r(bool f16, bool ef, const Pass2Args& a, hipStream_t s) {
   if (a.ntiles == 0) return hipSuccess;
   const dim3 grid(a.ntiles);
+  if constexpr (R >= kMfmaMinRank) {
+    if (f16 && ef) k_pass2_mfma<R, true, true><<<grid, kThreads, 0, s>>>(a);
+    else if (f16) k_pass2_mfma<R, true, false><<<grid, kThreads, 0, s>>>(a);
+    else if (ef) k_pass2_mfma<R, false, true><<<grid, kThreads, 0, s>>>(a);
+    else k_pass2_mfma<R, false, false><<<grid, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
   constexpr int U = unroll2<R>();
   if (f16 && ef) k_pass2<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
   else if (f16) k_pass2<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
@@ -945,6 +1348,13 @@ template <int R>
 hipError_t pass3_r(bool f16, bool ef, const Pass3Args& a, hipStream_t s) {
   const dim3 grid(a.ntiles + (f16 ? a.nftiles : 0));
   if (grid.x == 0) return hipSuccess;
+  if constexpr (R >= kMfmaMinRank) {
+    if (f16 && ef) k_pass3_mfma<R, true, true><<<grid, kThreads, 0, s>>>(a);
+    else if (f16) k_pass3_mfma<R, true, false><<<grid, kThreads, 0, s>>>(a);
+    else if (ef) k_pass3_mfma<R, false, true><<<grid, kThreads, 0, s>>>(a);
+    else k_pass3_mfma<R, false, false><<<grid, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
   constexpr int U = unroll3<R>();
   if (f16 && ef) k_pass3<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
   else if (f16) k_pass3<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
@@ -999,12 +1409,12 @@ hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs
 }
 
 hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, int max_rows, float* base,
-                       const double* gram, double eps, const int32_t* found_inf,
-                       hipStream_t s) {
+                       float* tbase, const double* gram, double eps,
+                       const int32_t* found_inf, hipStream_t s) {
   if (njobs == 0) return hipSuccess;
   const dim3 grid((max_rows + kOrthRows - 1) / kOrthRows, njobs);
   PSGD_RANK_SWITCH(R, {
-    k_orth<RR><<<grid, kThreads, 0, s>>>(jobs, base, gram, eps, found_inf);
+    k_orth<RR><<<grid, kThreads, 0, s>>>(jobs, base, tbase, gram, eps, found_inf);
     return hipGetLastError();
   })
 }

@@ -272,3 +272,18 @@ def test_full_rank_square_bucket_recovers_input():
     par = _run_parity(_hp(matrix_approximation_rank=8, min_compression_rate=0.1), shapes,
                       steps=2)
     assert par.gpu.decisions(0, 1) == [1]
+
+
+@pytest.mark.parametrize("rank", [16, 20, 32])
+def test_matrix_core_ranks_with_ragged_shapes(rank):
+    log(f"case: rank {rank} on matrix cores, ragged rows/columns, misaligned view")
+    shapes = [(300, 520), (77, 1030), (37,), (130, 129), (1029, 64)]
+    _run_parity(_hp(matrix_approximation_rank=rank, orthogonalization_epsilon=1e-8,
+                    min_compression_rate=1.0), shapes, steps=3)
+
+
+def test_matrix_core_rank32_fp16():
+    log("case: rank 32, fp16 bucket")
+    shapes = [(256, 320), (64,), (160, 512)]
+    _run_parity(_hp(matrix_approximation_rank=32), shapes, steps=3, dtype="f16",
+                inv_scale=2.0 ** -8, bucket_fn=lambda s: _rand_bucket(shapes, 110 + s, 20.0))
