@@ -17,7 +17,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -36,14 +35,6 @@ def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for name in ("kernels.hip", "internal.h", "host.cpp"):
-        with open(os.path.join(ROOT, "rank_gradient_compression_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 counters (profiles/), if the
     measurement was taken on the current kernel sources."""
@@ -56,7 +47,8 @@ def load_traffic(kernel: str, workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("source_hash") != kernel_source_hash():
+    from rank_gradient_compression_amd.rocprof_summary import source_hash
+    if vals.get("source_hash") != source_hash():
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -146,7 +138,7 @@ def main() -> int:
     copy_gbs = copy_bandwidth(torch)
     eprint(f"[bench] device-to-device copy: {copy_gbs:.0f} GB/s (read + write)")
     bucket_bytes = cfg.numel * cfg.element_bytes
-    total = args.steps + args.warmup
+    total = 2 * args.steps + args.warmup
     gen = BucketGenerator(cfg, "cuda")
 
     # One distinct bucket per step while it fits in a third of free HBM; beyond that
@@ -177,7 +169,7 @@ def main() -> int:
     torch.cuda.synchronize()
     eprint("[bench] warmup done")
 
-    st.set_timing(not args.no_kernel_timing)
+    # Timed region: K steps back to back, no per-kernel events.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -187,6 +179,19 @@ def main() -> int:
     ms_per_step = elapsed * 1e3 / args.steps
     value = bucket_bytes / (ms_per_step * 1e-3) / 1e9
 
+    # Second timed region over the same K steps with HIP events recorded by the
+    # library around every kernel on the launch stream (events between kernels add
+    # host and queue work, so they are kept out of the region `value` comes from).
+    if not args.no_kernel_timing:
+        st.set_timing(True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            run(args.warmup + args.steps + i)
+        torch.cuda.synchronize()
+        ev_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+        eprint(f"[bench] {ms_per_step * 1e3:.1f} us/step; with per-kernel events "
+               f"{ev_ms * 1e3:.1f} us/step")
     roofline = None
     if not args.no_kernel_timing:
         kt = st.kernel_times()
@@ -200,8 +205,7 @@ def main() -> int:
         avg_s = ms * 1e-3 / n
         achieved = by / n / avg_s / 1e9
         sum_ms = sum(x[1] for x in kt)
-        eprint(f"[bench] kernels total {sum_ms / args.steps * 1e3:.1f} us/step of "
-               f"{ms_per_step * 1e3:.1f} us/step wall")
+        eprint(f"[bench] kernels total {sum_ms / args.steps * 1e3:.1f} us/step")
         traffic = load_traffic(name, cfg.name)
         roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
