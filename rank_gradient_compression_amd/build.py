@@ -32,12 +32,16 @@ def library_path() -> str:
     return os.path.join(LIBDIR, LIBNAME)
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(LIBDIR, exist_ok=True)
-    out = library_path()
+def build(verbose: bool = False, defines: dict | None = None, out: str | None = None) -> str:
+    """Compiles the library. `defines` overrides the build-time tuning constants
+    (PSGD_PASS1_ROWS, PSGD_PASS2_ROWS, PSGD_PASS3_ROWS, PSGD_TILES_PER_BUCKET); `out`
+    writes the library elsewhere than the package's lib/ folder."""
+    out = out or library_path()
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    macros = [f"-D{k}={v}" for k, v in sorted((defines or {}).items())]
+    cmd = [hipcc(), *HIP_FLAGS, *macros, "-shared", "-I", os.path.join(ROOT, "include"), "-I",
+           CSRC, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)

@@ -113,7 +113,7 @@ struct BucketPlan {
   int64_t comm_elems = 0;
   int64_t all_elems = 0;
   std::vector<TensorDesc> tensors;
-  std::vector<Tile> tiles1, tiles23, tiles2r;
+  std::vector<Tile> tiles1, tiles2, tiles3, tiles2r;
   std::vector<FlatTile> flat_unc, flat_all;
   std::vector<OrthJob> pjobs, qjobs;
   std::vector<Tile> pgram_tiles, qgram_tiles;  // (job, partial) for the Gram kernel
@@ -126,6 +126,7 @@ struct BucketPlan {
   // device memory
   float* E = nullptr;
   float* P = nullptr;
+  float* Praw = nullptr;  // vector ranks: P as pass 1 writes it (pass 2 orthogonalizes)
   float* Q = nullptr;
   float* QT = nullptr;  // matrix-core ranks: Q transposed
   float* partial = nullptr;
@@ -135,7 +136,8 @@ struct BucketPlan {
   TensorDesc* d_td = nullptr;         // rows vector-aligned where possible
   TensorDesc* d_td_scalar = nullptr;  // same with every vec flag cleared
   Tile* d_tiles1 = nullptr;   // pass 1 row blocks
-  Tile* d_tiles23 = nullptr;  // pass 2 / pass 3 (row block, column block)
+  Tile* d_tiles2 = nullptr;   // pass 2 (row block, column block)
+  Tile* d_tiles3 = nullptr;   // pass 3 (row block, column block)
   Tile* d_tiles2r = nullptr;  // pass-2 partial sums (column blocks of split tensors)
   FlatTile* d_flat_unc = nullptr;
   FlatTile* d_flat_all = nullptr;
@@ -146,16 +148,16 @@ struct BucketPlan {
   bool q_ready = false;
 
   void release() {
-    void* ptrs[] = {E, P, Q, QT, partial, gram, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
-                    d_tiles1, d_tiles23, d_tiles2r, d_flat_unc, d_flat_all, d_pjobs, d_qjobs,
+    void* ptrs[] = {E, P, Praw, Q, QT, partial, gram, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
+                    d_tiles1, d_tiles2, d_tiles3, d_tiles2r, d_flat_unc, d_flat_all, d_pjobs, d_qjobs,
                     d_qinit};
     for (void* p : ptrs)
       if (p) (void)hipFree(p);
-    E = P = Q = QT = partial = nullptr;
+    E = P = Praw = Q = QT = partial = nullptr;
     gram = nullptr;
     d_pgram_tiles = d_qgram_tiles = nullptr;
     d_td = d_td_scalar = nullptr;
-    d_tiles1 = d_tiles23 = d_tiles2r = nullptr;
+    d_tiles1 = d_tiles2 = d_tiles3 = d_tiles2r = nullptr;
     d_flat_unc = d_flat_all = nullptr;
     d_pjobs = d_qjobs = nullptr;
     d_qinit = nullptr;
@@ -338,7 +340,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
   // Work-item size: enough workgroups to fill 256 CUs several times over, and no
   // more than 64K elements (256 KB of fp32) each.
   const int64_t target =
-      std::min<int64_t>(1 << 16, std::max<int64_t>(1 << 13, pl.compressed_elems / 2048));
+      std::min<int64_t>(1 << 16, std::max<int64_t>(1 << 13, pl.compressed_elems / PSGD_TILES_PER_BUCKET));
   const int64_t unroll1 = pass1_unroll(R);
   const int64_t ng = static_cast<int64_t>(R) * (R + 1) / 2;
   const bool fused_gram = R <= kMaxFusedGramRank;
@@ -378,6 +380,12 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
         const int64_t slots = kThreads / d.lprw;
         rows = round_up(std::max<int64_t>(1, (target + d.m - 1) / d.m), slots * unroll1);
         rows = std::min<int64_t>(rows, round_up(d.n, slots));
+        if (d.lprw > 64) {
+          // the wavefront sums of every row of the tile are parked in LDS
+          const int64_t wps = d.lprw / 64;
+          const int64_t step = slots * unroll1;
+          rows = std::min<int64_t>(rows, kPass1SlotSums / wps / step * step);
+        }
       }
       d.rpb1 = static_cast<int32_t>(rows);
       for (int64_t r0 = 0, rb = 0; r0 < d.n; r0 += rows, ++rb)
@@ -398,11 +406,21 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
     const int64_t width = std::min<int64_t>(d.m, kColBlock);
     d.lpr = pow2_ceil(static_cast<int>((width + 3) / 4));
     const int64_t rpw = 64 / d.lpr;
-    int64_t rpb = round_up(std::max<int64_t>(1, (target + width - 1) / width), 16 * rpw);
-    rpb = std::min<int64_t>(rpb, round_up(d.n, 4 * rpw));
-    if (R >= kMfmaMinRank) rpb = std::min<int64_t>(kMfmaRowBlock, round_up(d.n, 16));
+    auto row_block = [&](int64_t tgt) {
+      int64_t rb = round_up(std::max<int64_t>(1, (tgt + width - 1) / width), 16 * rpw);
+      rb = std::min<int64_t>(rb, round_up(d.n, 4 * rpw));
+      if (R >= kMfmaMinRank) rb = std::min<int64_t>(kMfmaRowBlock, round_up(d.n, 16));
+      return rb;
+    };
+    // vector ranks: every pass-2 workgroup orthogonalizes its P rows first, so its
+    // work items are larger (fewer of them pay that prologue) and its rows fit in LDS
+    int64_t rpb = row_block(fused_gram ? std::min<int64_t>(1 << 16, target * PSGD_PASS2_TILE_SCALE)
+                                       : target);
+    if (fused_gram) rpb = std::min<int64_t>(rpb, kPass2StageFloats / R);
     d.rpb = static_cast<int32_t>(rpb);
     d.nrb = static_cast<int32_t>((d.n + rpb - 1) / rpb);
+    d.rpb3 = static_cast<int32_t>(row_block(target));
+    const int32_t nrb3 = (d.n + d.rpb3 - 1) / d.rpb3;
     d.ncb = static_cast<int32_t>((d.m + kColBlock - 1) / kColBlock);
     if (d.nrb > 1) {
       d.pslot = pslot;
@@ -410,8 +428,10 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
       for (int32_t cb = 0; cb < d.ncb; ++cb) pl.tiles2r.push_back(Tile{ti, 0, cb, 0});
     }
     pl.view_tensor[v] = ti;
-    for (int32_t cb = 0; cb < d.ncb; ++cb)
-      for (int32_t rb = 0; rb < d.nrb; ++rb) pl.tiles23.push_back(Tile{ti, rb, cb, 0});
+    for (int32_t cb = 0; cb < d.ncb; ++cb) {
+      for (int32_t rb = 0; rb < d.nrb; ++rb) pl.tiles2.push_back(Tile{ti, rb, cb, 0});
+      for (int32_t rb = 0; rb < nrb3; ++rb) pl.tiles3.push_back(Tile{ti, rb, cb, 0});
+    }
     {
       const int32_t nparts = static_cast<int32_t>((d.m + kGramRows - 1) / kGramRows);
       pl.qjobs.push_back(
@@ -446,6 +466,8 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   bool ok = true;
   ok = ok && alloc(reinterpret_cast<void**>(&pl.E), need_e ? pl.e_floats * sizeof(float) : 0);
   ok = ok && alloc(reinterpret_cast<void**>(&pl.P), pl.p_floats * sizeof(float));
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.Praw),
+                   pl.R <= kMaxFusedGramRank ? pl.p_floats * sizeof(float) : 0);
   ok = ok && alloc(reinterpret_cast<void**>(&pl.Q), pl.q_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.QT), pl.qt_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.partial), pl.partial_floats * sizeof(float));
@@ -458,6 +480,8 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   hipError_t e = hipSuccess;
   if (pl.E && e == hipSuccess) e = hipMemsetAsync(pl.E, 0, pl.e_floats * sizeof(float), s);
   if (pl.P && e == hipSuccess) e = hipMemsetAsync(pl.P, 0, pl.p_floats * sizeof(float), s);
+  if (pl.Praw && e == hipSuccess)
+    e = hipMemsetAsync(pl.Praw, 0, pl.p_floats * sizeof(float), s);
   if (pl.Q && e == hipSuccess) e = hipMemsetAsync(pl.Q, 0, pl.q_floats * sizeof(float), s);
   if (pl.QT && e == hipSuccess) e = hipMemsetAsync(pl.QT, 0, pl.qt_floats * sizeof(float), s);
 
@@ -471,7 +495,8 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   if (st == POWERSGD_OK) st = upload(pl.tensors, &pl.d_td, s);
   if (st == POWERSGD_OK) st = upload(scalar, &pl.d_td_scalar, s);
   if (st == POWERSGD_OK) st = upload(pl.tiles1, &pl.d_tiles1, s);
-  if (st == POWERSGD_OK) st = upload(pl.tiles23, &pl.d_tiles23, s);
+  if (st == POWERSGD_OK) st = upload(pl.tiles2, &pl.d_tiles2, s);
+  if (st == POWERSGD_OK) st = upload(pl.tiles3, &pl.d_tiles3, s);
   if (st == POWERSGD_OK) st = upload(pl.tiles2r, &pl.d_tiles2r, s);
   if (st == POWERSGD_OK) st = upload(pl.flat_unc, &pl.d_flat_unc, s);
   if (st == POWERSGD_OK) st = upload(pl.flat_all, &pl.d_flat_all, s);
@@ -682,6 +707,8 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
   const double ce = static_cast<double>(pl.compressed_elems);
   const double ue = static_cast<double>(pl.uncompressed_elems);
   const double eps = hp.orthogonalization_epsilon;
+  // vector ranks: the Gram partials come from pass 1 and pass 2 orthogonalizes P itself
+  const bool fused = R <= kMaxFusedGramRank;
   const uint64_t bucket_key = static_cast<uint64_t>(bucket_index);
   powersgd_status r = POWERSGD_OK;
 
@@ -718,7 +745,7 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
     a.E = pl.E;
     a.Q = pl.Q;
     a.QT = pl.QT;
-    a.P = pl.P;
+    a.P = fused ? pl.Praw : pl.P;
     a.gram = pl.gram;
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
@@ -736,19 +763,24 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
       });
       if (r != POWERSGD_OK) return r;
     }
-    r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize P", [&] {
-      return launch_orth(R, pl.d_pjobs, nt, pl.max_prows, pl.P, nullptr, pl.gram, eps,
-                         f16 ? found_inf_dev : nullptr, s);
-    });
-    if (r != POWERSGD_OK) return r;
-    // Step 3.5 (step 3.6 is the identity).
+    if (!fused) {
+      r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize P", [&] {
+        return launch_orth(R, pl.d_pjobs, nt, pl.max_prows, pl.P, nullptr, pl.gram, eps,
+                           f16 ? found_inf_dev : nullptr, s);
+      });
+      if (r != POWERSGD_OK) return r;
+    }
+    // Step 3.5 (step 3.6 is the identity); vector ranks orthogonalize P on the way in.
     Pass2Args a{};
-    a.tiles = pl.d_tiles23;
-    a.ntiles = static_cast<int32_t>(pl.tiles23.size());
+    a.tiles = pl.d_tiles2;
+    a.ntiles = static_cast<int32_t>(pl.tiles2.size());
     a.td = td;
     a.bucket = bucket;
     a.E = pl.E;
-    a.P = pl.P;
+    a.P = fused ? pl.Praw : pl.P;
+    a.Pout = pl.P;
+    a.gram = pl.gram;
+    a.eps = eps;
     a.Q = pl.Q;
     a.QT = pl.QT;
     a.partial = pl.partial;
@@ -774,8 +806,8 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
   {
     // Step 3.7 with the error update (+ fp16 unscale of the uncompressed views).
     Pass3Args a{};
-    a.tiles = pl.d_tiles23;
-    a.ntiles = static_cast<int32_t>(pl.tiles23.size());
+    a.tiles = pl.d_tiles3;
+    a.ntiles = static_cast<int32_t>(pl.tiles3.size());
     a.ftiles = pl.d_flat_unc;
     a.nftiles = static_cast<int32_t>(pl.flat_unc.size());
     a.td = td;

@@ -17,10 +17,10 @@ constexpr int kThreads = 256;
 // Pass 1 work items are row blocks of rpb1 full rows: the 256 threads of a
 // workgroup form 256 / lprw row slots of lprw threads, a thread owning 4 consecutive
 // columns per sweep of 4 * lprw columns, so every dot product stays inside one
-// workgroup. Pass 2 and pass 3 work items are (row block of rpb rows) x (256-column
-// block): a wavefront's 64 lanes form 64 / lpr row slots of lpr lanes, a lane owning
-// 4 consecutive columns. Pass 2 writes one partial Q per row block when nrb > 1;
-// a separate reduction sums them in row-block order.
+// workgroup. Pass 2 work items are (row block of rpb rows) x (256-column block), pass
+// 3 ones (row block of rpb3 rows) x (256-column block): a wavefront's 64 lanes form
+// 64 / lpr row slots of lpr lanes, a lane owning 4 consecutive columns. Pass 2 writes
+// one partial Q per row block when nrb > 1; a separate reduction sums them.
 struct TensorDesc {
   int64_t boff;   // first element of the view in the bucket
   int64_t eoff;   // first float of its error memory (multiple of 4)
@@ -33,7 +33,7 @@ struct TensorDesc {
   int64_t goff;   // first double of its P Gram partials (one per pass-1 row block)
   int64_t qtoff;  // matrix-core ranks: first float of Q^T (R rows of mstride floats)
   int32_t mstride;  // row stride of Q^T: m rounded up to a multiple of 4 (padding zero)
-  int32_t pad0;
+  int32_t rpb3;     // pass 3: rows per row block (its own tiling, same lane geometry)
   int32_t lprw;   // pass 1: threads per row slot (power of two, <= 256)
   int32_t rpb1;   // pass 1: rows per row block
   int32_t lpr;    // pass 2/3: lanes per row slot (power of two, <= 64)
@@ -110,7 +110,10 @@ struct Pass2Args {
   const TensorDesc* td;
   const void* bucket;
   const float* E;
-  const float* P;
+  const float* P;          // vector ranks: P as pass 1 left it; matrix-core: orthogonalized
+  float* Pout;             // vector ranks: orthogonalized P (written by column block 0 tiles)
+  const double* gram;      // vector ranks: the Gram partials of P from pass 1
+  double eps;              // vector ranks: orthogonalization epsilon
   float* Q;
   float* QT;               // matrix-core ranks: Q^T, written next to Q (else null)
   float* partial;
@@ -161,8 +164,28 @@ hipError_t launch_unscale_only(const FlatTile* ftiles, int nftiles, void* bucket
                                float inv_scale, int32_t* found_inf, bool check,
                                hipStream_t s);
 
+// Tuning constants of the vector-rank streaming passes (overridable at build time).
+#ifndef PSGD_PASS1_ROWS
+#define PSGD_PASS1_ROWS 4  // pass 1 rows in flight per thread, padded ranks <= 4
+#endif
+#ifndef PSGD_PASS2_ROWS
+#define PSGD_PASS2_ROWS 8  // pass 2 rows in flight per lane, padded ranks <= 4
+#endif
+#ifndef PSGD_PASS3_ROWS
+#define PSGD_PASS3_ROWS 8  // pass 3 rows in flight per lane, padded ranks <= 8
+#endif
+#ifndef PSGD_TILES_PER_BUCKET
+#define PSGD_TILES_PER_BUCKET 4096  // work items aimed at per pass (before clamping)
+#endif
+#ifndef PSGD_PASS2_TILE_SCALE
+#define PSGD_PASS2_TILE_SCALE 4  // pass-2 work items this many times larger (vector ranks)
+#endif
+
 // Rows loaded per thread before use in pass 1 (P = M' Q), by padded rank.
-constexpr int pass1_unroll(int R) { return R <= 4 ? 4 : 1; }
+constexpr int pass1_unroll(int R) { return R <= 4 ? PSGD_PASS1_ROWS : 1; }
+// Pass 1 row sums parked in LDS per workgroup when a row slot spans several
+// wavefronts (rows of the tile x wavefronts per slot); the plan keeps tiles within it.
+constexpr int kPass1SlotSums = 544;
 // Pass 1 also accumulates the Gram partials of P up to this padded rank; above it a
 // separate Gram kernel reads P.
 constexpr int kMaxFusedGramRank = 8;
@@ -172,6 +195,11 @@ constexpr int kMaxFusedGramRank = 8;
 constexpr int kMfmaMinRank = 16;
 constexpr int kMfmaPass1Rows = 64;
 constexpr int kMfmaRowBlock = 1024;
+// Threads per workgroup of the pass-2 partial reduction.
+constexpr int kReduceThreads = 1024;
+// Vector ranks: floats of orthogonalized P rows a pass-2 workgroup keeps in LDS (the
+// plan keeps row blocks at or below kPass2StageFloats / R rows).
+constexpr int kPass2StageFloats = 4096;
 // Rows per Gram partial of the separate Gram kernel.
 constexpr int kGramRows = 256;
 // Rows transformed by one workgroup of the orthogonalization kernel (each workgroup

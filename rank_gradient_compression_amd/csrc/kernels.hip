@@ -16,12 +16,13 @@
 //           into found_inf.
 //   orth    Gram-Schmidt with epsilon on P (and on the initial Q draw) from fp64 Gram
 //           partials (pass 1 accumulates them for ranks <= 8, a small LDS-staged
-//           kernel otherwise): one workgroup per matrix sums them in fixed order,
-//           runs the recurrence on r x r coefficient vectors (lane j owns column j)
-//           and applies P <- P T in fp64.
+//           kernel otherwise): the partials are summed in a fixed order, the
+//           recurrence runs on r x r coefficient vectors (lane j owns column j) and
+//           P <- P T is applied in fp64. Ranks <= 8 do this in the prologue of every
+//           pass-2 workgroup for its own rows; larger ranks in a kernel of its own.
 //   pass 2  Q = M'^T P. A workgroup owns a 256-column block of a row block; its row
 //           slots and wavefronts are combined in a fixed order; tensors with several
-//           row blocks write one partial per block, summed in row-block order by a
+//           row blocks write one partial per block, summed in a fixed order by a
 //           small second kernel (deterministic, no atomics, no inter-workgroup
 //           fences: the kernel boundary publishes the partials).
 //   pass 3  M_hat = P Q^T written into the bucket (fp16: round to nearest even),
@@ -180,6 +181,113 @@ __device__ __forceinline__ void load_q_rows(const float* __restrict__ Q, int c, 
   }
 }
 
+// Loads 4 gradient values of a 16-byte aligned group without a branch (address
+// already clamped into the matrix); fp16 values are unscaled, `raw_bad` tells whether
+// any of them is inf or NaN.
+template <bool F16>
+__device__ __forceinline__ void load_grad4_vec(const void* bucket, int64_t idx, float inv_scale,
+                                               float (&x)[4], bool& raw_bad) {
+  if constexpr (F16) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(bucket) + idx);
+    const uint16_t raw[4] = {static_cast<uint16_t>(w.x & 0xFFFFu), static_cast<uint16_t>(w.x >> 16),
+                             static_cast<uint16_t>(w.y & 0xFFFFu), static_cast<uint16_t>(w.y >> 16)};
+    raw_bad = false;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      raw_bad |= half_bits_not_finite(raw[a]);
+      x[a] = half_bits_to_float(raw[a]) * inv_scale;
+    }
+  } else {
+    const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(bucket) + idx);
+    x[0] = w.x;
+    x[1] = w.y;
+    x[2] = w.z;
+    x[3] = w.w;
+    raw_bad = false;
+  }
+}
+
+__device__ __forceinline__ void load_f4(const float* p, float (&x)[4]) {
+  const float4 w = *reinterpret_cast<const float4*>(p);
+  x[0] = w.x;
+  x[1] = w.y;
+  x[2] = w.z;
+  x[3] = w.w;
+}
+
+// Branch-free loads of 4 consecutive values starting at element `idx` of a row that
+// has `valid` >= 1 elements left from there (the row index is clamped by the caller).
+// VEC: one aligned vector load. Otherwise four scalar loads at offsets clamped into
+// the row; the values past its end read as zero (and are never flagged as bad).
+template <bool VEC>
+__device__ __forceinline__ void ld_f32x4(const float* p, int valid, float (&x)[4]) {
+  if constexpr (VEC) {
+    load_f4(p, x);
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float v = p[min(a, valid - 1)];
+      x[a] = a < valid ? v : 0.f;
+    }
+  }
+}
+
+template <bool F16, bool VEC>
+__device__ __forceinline__ void ld_grad4(const void* bucket, int64_t idx, int valid,
+                                         float inv_scale, float (&x)[4], bool& raw_bad) {
+  if constexpr (VEC) {
+    load_grad4_vec<F16>(bucket, idx, inv_scale, x, raw_bad);
+  } else if constexpr (F16) {
+    const uint16_t* h = static_cast<const uint16_t*>(bucket) + idx;
+    raw_bad = false;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const uint16_t v = h[min(a, valid - 1)];
+      const bool in = a < valid;
+      raw_bad |= in && half_bits_not_finite(v);
+      x[a] = in ? half_bits_to_float(v) * inv_scale : 0.f;
+    }
+  } else {
+    ld_f32x4<false>(static_cast<const float*>(bucket) + idx, valid, x);
+    raw_bad = false;
+  }
+}
+
+template <bool VEC>
+__device__ __forceinline__ void st_f32x4(float* p, int valid, const float (&x)[4]) {
+  store_f32x4(p, VEC, valid, x);
+}
+
+// Q rows c..c+3 (R values each) of a row-major block; rows at or past m read as zero.
+template <int R, bool VEC>
+__device__ __forceinline__ void ld_q4(const float* __restrict__ Q, int c, int valid,
+                                      float (&q)[4][R]) {
+  if constexpr (VEC) {
+    const float4* p = reinterpret_cast<const float4*>(Q + static_cast<int64_t>(c) * R);
+    float f[4 * R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const float4 w = p[i];
+      f[4 * i + 0] = w.x;
+      f[4 * i + 1] = w.y;
+      f[4 * i + 2] = w.z;
+      f[4 * i + 3] = w.w;
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int k = 0; k < R; ++k) q[a][k] = f[a * R + k];
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const float v = Q[static_cast<int64_t>(c + min(a, valid - 1)) * R + k];
+        q[a][k] = a < valid ? v : 0.f;
+      }
+  }
+}
+
 // Lane geometry of a tile (see TensorDesc): row slot, column group and first column.
 struct LaneGeom {
   int lpr;      // lanes per row slot
@@ -203,6 +311,25 @@ __device__ __forceinline__ LaneGeom lane_geom(const TensorDesc& d, int cb, int l
   return L;
 }
 
+// Geometry of a tile of a matrix at least 256 columns wide: a row slot is a whole
+// wavefront, so the row a wavefront works on is uniform and P rows are scalar loads.
+template <bool WIDE>
+__device__ __forceinline__ LaneGeom tile_geom(const TensorDesc& d, int cb, int lane) {
+  if constexpr (WIDE) {
+    LaneGeom L;
+    L.lpr = 64;
+    L.rpw = 1;
+    L.slot = 0;
+    L.g = lane;
+    L.c = cb * kColBlock + lane * 4;
+    L.col_ok = L.c < d.m;
+    L.valid = d.m - L.c;
+    return L;
+  } else {
+    return lane_geom(d, cb, lane);
+  }
+}
+
 // P row `row` (R floats, 16-byte aligned when R >= 4).
 template <int R>
 __device__ __forceinline__ void load_p_row(const float* __restrict__ Pt, int row,
@@ -221,6 +348,18 @@ __device__ __forceinline__ void load_p_row(const float* __restrict__ Pt, int row
 #pragma unroll
     for (int k = 0; k < R; ++k) p[k] = src[k];
   }
+}
+
+// The same row when `row` is uniform across the wavefront: read through the constant
+// address space, so the compiler issues scalar loads (read-only; P was written by an
+// earlier kernel of the stream).
+template <int R>
+__device__ __forceinline__ void load_p_row_uniform(const float* __restrict__ Pt, int row,
+                                                   float (&p)[R]) {
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cfloat* src = (cfloat*)(Pt + static_cast<int64_t>(row) * R);
+#pragma unroll
+  for (int k = 0; k < R; ++k) p[k] = src[k];
 }
 
 template <int R>
@@ -249,9 +388,6 @@ __device__ void f16_check_range(const FlatTile ft, const void* bucket,
   if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(found_inf, 1);
 }
 
-// P = M' Q over one row block. Threads of a row slot sweep the row's columns,
-// U rows per thread are loaded before any is used, and the slot's partial dot
-// products are summed with shuffles (and through LDS when a slot spans wavefronts).
 // Adds the outer product of one P row (masked to the rank in use) to packed fp64
 // Gram accumulators.
 template <int R>
@@ -285,38 +421,48 @@ __device__ __forceinline__ void block_sum_to(double (&v)[NG], double* dst, doubl
     dst[e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
 }
 
-template <int R, int U, bool F16, bool EF>
-__global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
+template <int R>
+constexpr int pass1_ng() { return R <= kMaxFusedGramRank ? gram_size<R>() : 1; }
+
+// P = M' Q over one row block. Threads of a row slot sweep the row's columns,
+// U rows per thread are loaded before any is used, and the slot's partial dot
+// products are summed with shuffles (and through LDS when a slot spans wavefronts).
+// VEC: rows are 16-byte aligned and m % 4 == 0. The rows of a slot are clamped into
+// the row block, so every load of an iteration is issued before any is used; the
+// results of clamped duplicate rows are discarded.
+template <int R, int U, bool F16, bool EF, bool VEC>
+__device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDesc& d,
+                                           const Tile& t, float* red,
+                                           double (*gred)[pass1_ng<R>()]) {
   constexpr bool GRAM = R <= kMaxFusedGramRank;
-  constexpr int NG = GRAM ? gram_size<R>() : 1;
-  __shared__ float red[kThreads / 64][U * R];
-  __shared__ double gred[kThreads / 64][NG];
+  constexpr int NG = pass1_ng<R>();
   double gacc[NG];
 #pragma unroll
   for (int e = 0; e < NG; ++e) gacc[e] = 0.0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  if (static_cast<int>(blockIdx.x) >= args.ntiles) {
-    if constexpr (F16)
-      f16_check_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.found_inf);
-    return;
-  }
   const int wave = wave_index();
-  const Tile t = args.tiles[blockIdx.x];
-  const TensorDesc d = args.td[t.tensor];
   const int m = d.m;
   const int lprw = d.lprw;
   const int slots = kThreads / lprw;
   const int slot = tid / lprw;
   const int g = tid - slot * lprw;
   const int sweep = 4 * lprw;
-  const bool vec = d.vec != 0;
   const int r0 = t.a * d.rpb1;
   const int r1 = min(d.n, r0 + d.rpb1);
   const float* __restrict__ Qt = args.Q + d.qoff;
   float* __restrict__ Et = args.E + d.eoff;
+  float* __restrict__ Mt = static_cast<float*>(args.bucket) + d.boff;
   int bad = 0;
   for (int rw = r0; rw < r1; rw += slots * U) {
+    int64_t rbase[U];
+    bool rok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = rw + u * slots + slot;
+      rok[u] = row < r1;
+      rbase[u] = static_cast<int64_t>(min(row, r1 - 1)) * m;
+    }
     float acc[U][R];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -325,41 +471,24 @@ __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
     for (int c = g * 4; c < m; c += sweep) {
       const int valid = m - c;
       float q[4][R];
-      load_q_rows<R>(Qt, c, m, q);
+      ld_q4<R, VEC>(Qt, c, valid, q);
       float x[U][4];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int row = rw + u * slots + slot;
-        if (row < r1) {
-          load_grad4<F16>(args.bucket, d.boff + static_cast<int64_t>(row) * m + c, vec, valid,
-                          args.inv_scale, x[u], bad);
-        } else {
-#pragma unroll
-          for (int a = 0; a < 4; ++a) x[u][a] = 0.f;
-        }
+        bool rb;
+        ld_grad4<F16, VEC>(args.bucket, d.boff + rbase[u] + c, valid, args.inv_scale, x[u], rb);
+        if constexpr (F16) bad |= (rok[u] && rb) ? 1 : 0;
       }
       if constexpr (EF) {
         float e[U][4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int row = rw + u * slots + slot;
-          if (row < r1) {
-            load_f32x4(Et + static_cast<int64_t>(row) * m + c, vec, valid, e[u]);
-          } else {
-#pragma unroll
-            for (int a = 0; a < 4; ++a) e[u][a] = 0.f;
-          }
-        }
+        for (int u = 0; u < U; ++u) ld_f32x4<VEC>(Et + rbase[u] + c, valid, e[u]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
           for (int a = 0; a < 4; ++a) x[u][a] += e[u][a];
           if constexpr (!F16) {
-            const int row = rw + u * slots + slot;
-            if (row < r1)
-              store_f32x4(static_cast<float*>(args.bucket) + d.boff +
-                              static_cast<int64_t>(row) * m + c,
-                          vec, valid, x[u]);
+            if (rok[u]) st_f32x4<VEC>(Mt + rbase[u] + c, valid, x[u]);
           }
         }
       }
@@ -383,7 +512,7 @@ __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int row = rw + u * slots + slot;
-          if (row < r1) {
+          if (rok[u]) {
             float pr[R];
 #pragma unroll
             for (int k = 0; k < R; ++k) pr[k] = (k < d.rank) ? acc[u][k] : 0.f;
@@ -392,33 +521,33 @@ __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
           }
         }
       }
-    } else {
-      // a slot spans lprw / 64 wavefronts: add their sums in wavefront order
-      if (lane == 0) {
+    } else if (lane == 0) {
+      // a slot spans wps wavefronts: park this wavefront's sums until the tile ends
+      const int wps = lprw >> 6;
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        if (rok[u]) {
+          float* dst = red + ((rw + u * slots + slot - r0) * wps + (wave & (wps - 1))) * R;
 #pragma unroll
-          for (int k = 0; k < R; ++k) red[wave][u * R + k] = acc[u][k];
-      }
-      __syncthreads();
-      const int wps = lprw / 64;
-      if (tid < slots * U) {
-        const int s2 = tid / U;
-        const int u = tid - s2 * U;
-        const int row = rw + u * slots + s2;
-        if (row < r1) {
-          float pr[R];
-#pragma unroll
-          for (int k = 0; k < R; ++k) {
-            float v = 0.f;
-            for (int w = 0; w < wps; ++w) v += red[s2 * wps + w][u * R + k];
-            pr[k] = (k < d.rank) ? v : 0.f;
-          }
-          store_p_row<R>(args.P + d.poff, row, pr);
-          if constexpr (GRAM) gram_add<R>(gacc, pr);
+          for (int k = 0; k < R; ++k) dst[k] = acc[u][k];
         }
       }
-      __syncthreads();
+    }
+  }
+  if (lprw > 64) {
+    // add the wavefront sums of every row in wavefront order
+    __syncthreads();
+    const int wps = lprw >> 6;
+    for (int i = tid; i < r1 - r0; i += kThreads) {
+      float pr[R];
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        float v = 0.f;
+        for (int w = 0; w < wps; ++w) v += red[(i * wps + w) * R + k];
+        pr[k] = (k < d.rank) ? v : 0.f;
+      }
+      store_p_row<R>(args.P + d.poff, r0 + i, pr);
+      if constexpr (GRAM) gram_add<R>(gacc, pr);
     }
   }
   if constexpr (F16) {
@@ -428,62 +557,291 @@ __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
     block_sum_to<NG>(gacc, args.gram + d.goff + static_cast<int64_t>(t.a) * NG, gred);
 }
 
+template <int R, int U, bool F16, bool EF>
+__global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
+  __shared__ float red[kPass1SlotSums * R];
+  __shared__ double gred[kThreads / 64][pass1_ng<R>()];
+  if (static_cast<int>(blockIdx.x) >= args.ntiles) {
+    if constexpr (F16)
+      f16_check_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.found_inf);
+    return;
+  }
+  const Tile t = args.tiles[blockIdx.x];
+  const TensorDesc d = args.td[t.tensor];
+  if (d.vec)
+    pass1_body<R, U, F16, EF, true>(args, d, t, red, gred);
+  else
+    pass1_body<R, U, F16, EF, false>(args, d, t, red, gred);
+}
+
+// ------------------------------------------------------------ orthogonalization
+//
+// Gram-Schmidt with epsilon (step 3.4) evaluated on the Gram matrix: every vector
+// the recurrence forms is a combination P c of the columns of P, so its norm and
+// its dot products are c^T G c' with G = P^T P. The recurrence runs on the r x r
+// coefficient vectors in fp64 and the result is applied once, P <- P T, in fp64.
+
+// Lanes that share one Gram entry when the orthogonalization sums the partials: the
+// largest power of two with NG * GS <= 256 threads, at most a wavefront (1 = a thread
+// per entry).
+template <int R>
+constexpr int orth_group_size() {
+  int gs = 64;
+  while (gs > 1 && gs * gram_size<R>() > kThreads) gs /= 2;
+  return gs;
+}
+
+// Working set of the orthogonalization of one matrix (LDS).
+template <int R>
+struct OrthShared {
+  double G[R][R];  // Gram matrix
+  double T[R][R];  // P <- P T
+  double C[R];     // coefficients of the column being normalized
+  double W[R];     // G q_i in coefficients
+};
+
+// Sums the job's Gram partials into sh.G (every thread of the workgroup takes part;
+// ends with a barrier). `issued` runs once the first loads of partials are in flight
+// and before any is used, so a caller can queue loads of its own behind them.
+// Small ranks: a group of GS lanes of one wavefront per Gram entry, lane i adding
+// partials i, i + GS, ... (8 loads in flight), then a butterfly over the group.
+// Larger ranks: a thread per entry, the partials in order, 8 loads of each of its
+// entries in flight.
+template <int R, typename Issued>
+__device__ __forceinline__ void orth_gram_sum(const OrthJob& j, const double* __restrict__ gram,
+                                              OrthShared<R>& sh, Issued issued) {
+  constexpr int NG = gram_size<R>();
+  constexpr int GS = orth_group_size<R>();
+  const int tid = threadIdx.x;
+  auto store_entry = [&](int e, double v) {
+    int a = 0, rem = e;
+    while (rem >= R - a) {
+      rem -= R - a;
+      ++a;
+    }
+    const int b = a + rem;
+    sh.G[a][b] = v;
+    sh.G[b][a] = v;
+  };
+  if constexpr (GS > 1) {
+    const int e = min(tid / GS, NG - 1);  // threads past the last entry mirror it
+    const int gi = tid - (tid / GS) * GS;
+    auto load = [&](int p0, double (&v)[8]) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        v[b] = gram[j.goff + static_cast<int64_t>(min(p0 + b * GS, j.nparts - 1)) * NG + e];
+    };
+    auto add = [&](int p0, const double (&v)[8], double& s) {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) s += (p0 + b * GS < j.nparts) ? v[b] : 0.0;
+    };
+    double v[8];
+    load(gi, v);
+    // keep the issue order: the caller's loads go behind these
+    __builtin_amdgcn_sched_barrier(0);
+    issued();
+    __builtin_amdgcn_sched_barrier(0);
+    double s = 0.0;
+    add(gi, v, s);
+    for (int p0 = gi + 8 * GS; p0 < j.nparts; p0 += 8 * GS) {
+      load(p0, v);
+      add(p0, v, s);
+    }
+#pragma unroll
+    for (int mask = GS / 2; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask);
+    if (gi == 0 && tid / GS < NG) store_entry(e, s);
+  } else {
+    constexpr int PER = (NG + kThreads - 1) / kThreads;
+    double s[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) s[i] = 0.0;
+    issued();
+    for (int p0 = 0; p0 < j.nparts; p0 += 8) {
+      double v[PER][8];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = min(tid + i * kThreads, NG - 1);
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+          v[i][b] = gram[j.goff + static_cast<int64_t>(min(p0 + b, j.nparts - 1)) * NG + e];
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) s[i] += (p0 + b < j.nparts) ? v[i][b] : 0.0;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * kThreads;
+      if (e < NG) store_entry(e, s[i]);
+    }
+  }
+  __syncthreads();
+}
+
+// The recurrence on r x r coefficient vectors, from sh.G into sh.T. Wavefront 0 runs
+// it alone: LDS accesses of one wavefront take effect in program order, so its steps
+// need no workgroup barrier (wave barriers only keep the compiler from reordering);
+// one barrier at the end publishes sh.T to the workgroup.
+template <int R>
+__device__ __forceinline__ void orth_transform(int rank, double eps, OrthShared<R>& sh) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  if (tid < 64) {
+    // lane c owns column c
+    double cvec[R];
+#pragma unroll
+    for (int l = 0; l < R; ++l) cvec[l] = (l == lane) ? 1.0 : 0.0;
+    for (int i = 0; i < rank; ++i) {
+      if (lane == i) {
+#pragma unroll
+        for (int l = 0; l < R; ++l) sh.C[l] = cvec[l];
+      }
+      __builtin_amdgcn_wave_barrier();
+      double w = 0.0;  // (G c_i)_lane
+      if (lane < R) {
+#pragma unroll
+        for (int l = 0; l < R; ++l) w += sh.G[lane][l] * sh.C[l];
+      }
+      double nn = (lane < R) ? sh.C[lane] * w : 0.0;
+#pragma unroll
+      for (int mask = 32; mask >= 1; mask >>= 1) nn += __shfl_xor(nn, mask);
+      // |v_i|^2 = c_i^T G c_i; q_i = v_i / (|v_i| + eps)
+      const double inv = 1.0 / (sqrt(nn > 0.0 ? nn : 0.0) + eps);
+      if (lane < R) sh.W[lane] = w * inv;  // G q_i (in coefficients)
+      __builtin_amdgcn_wave_barrier();
+      if (lane < rank) {
+        if (lane == i) {
+#pragma unroll
+          for (int l = 0; l < R; ++l) cvec[l] *= inv;
+        } else if (lane > i) {
+          // <q_i, v_lane> = c_lane^T G c_i / (|v_i| + eps); v_lane -= <q_i, v_lane> q_i
+          double coef = 0.0;
+#pragma unroll
+          for (int l = 0; l < R; ++l) coef += cvec[l] * sh.W[l];
+#pragma unroll
+          for (int l = 0; l < R; ++l) cvec[l] -= coef * (sh.C[l] * inv);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    if (lane < R) {
+#pragma unroll
+      for (int l = 0; l < R; ++l) sh.T[l][lane] = cvec[l];
+    }
+  }
+  __syncthreads();
+}
+
 // ----------------------------------------------------------------------- pass 2
 
-template <bool F16, bool EF>
-__device__ __forceinline__ void load_mprime4(const void* bucket, const float* Et,
-                                             const TensorDesc& d, int64_t off, bool vec,
-                                             int valid, float inv_scale, float (&x)[4]) {
-  int bad = 0;
-  load_grad4<F16>(bucket, d.boff + off, vec, valid, inv_scale, x, bad);
+// M' at element `off` of a matrix (fp32 with error feedback: the bucket already holds
+// M', written by pass 1; fp16: unscaled gradient plus E).
+template <bool F16, bool EF, bool VEC>
+__device__ __forceinline__ void ld_mprime4(const void* bucket, const float* Et, int64_t boff,
+                                           int64_t off, int valid, float inv_scale,
+                                           float (&x)[4]) {
+  bool rb;
+  ld_grad4<F16, VEC>(bucket, boff + off, valid, inv_scale, x, rb);
   if constexpr (F16 && EF) {
     float e[4];
-    load_f32x4(Et + off, vec, valid, e);
+    ld_f32x4<VEC>(Et + off, valid, e);
 #pragma unroll
     for (int a = 0; a < 4; ++a) x[a] += e[a];
   }
-  // fp32 with error feedback: the bucket already holds M' (written by pass 1).
 }
 
-// Q = M'^T P over one tile; row slots and wavefronts are combined in a fixed order;
-// with several row blocks each writes a partial slot (summed by k_pass2_reduce).
-template <int R, int U, bool F16, bool EF>
-__global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
-  if (F16 && *args.found_inf) return;
-  __shared__ float red[64 * 4 * R];
+// Gram-Schmidt of P (step 3.4) for the rows of one pass-2 tile: the workgroup sums the
+// Gram partials pass 1 left, runs the recurrence and applies P <- P T (fp64, rounded
+// once) to its rows, which stay in LDS (sP, rows relative to r0). Tiles of column
+// block 0 also store them as the orthogonalized P. Every workgroup of a matrix takes
+// the same steps in the same order, so they all hold identical rows.
+template <int R, typename Issued>
+__device__ __forceinline__ void pass2_orth_rows(const Pass2Args& args, const TensorDesc& d,
+                                                const Tile& t, int r0, int r1,
+                                                OrthShared<R>& sh, float* sP, Issued issued) {
+  constexpr int PT = kPass2StageFloats / R / kThreads;  // rows per thread
+  static_assert(PT >= 1, "pass-2 row staging too small for this rank");
+  const int tid = threadIdx.x;
+  const float* __restrict__ Pt = args.P + d.poff;
+  float praw[PT][R];  // loaded before the Gram partials are summed
+#pragma unroll
+  for (int i = 0; i < PT; ++i) load_p_row<R>(Pt, min(r0 + tid + i * kThreads, r1 - 1), praw[i]);
+  __builtin_amdgcn_sched_barrier(0);
+  const OrthJob j{d.poff, d.goff, -1, d.n, d.rank, (d.n + d.rpb1 - 1) / d.rpb1, d.rpb1, 0, 0};
+  orth_gram_sum<R>(j, args.gram, sh, issued);
+  orth_transform<R>(d.rank, args.eps, sh);
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int row = r0 + tid + i * kThreads;
+    if (row < r1) {
+      float pr[R];
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        double acc = 0.0;
+#pragma unroll
+        for (int l = 0; l < R; ++l) acc += static_cast<double>(praw[i][l]) * sh.T[l][k];
+        pr[k] = static_cast<float>(acc);
+        sP[(row - r0) * R + k] = pr[k];
+      }
+      if (t.b == 0) store_p_row<R>(args.Pout + d.poff, row, pr);
+    }
+  }
+  __syncthreads();
+}
+
+// Q = M'^T P over one tile (P rows from LDS); row slots and wavefronts are combined in
+// a fixed order; with several row blocks each writes a partial slot (summed by
+// k_pass2_reduce). Rows are clamped into the tile so all loads of an iteration are
+// issued together; clamped duplicate rows are zeroed before they are accumulated. The
+// first rows of M' are requested during the orthogonalization prologue, after its own
+// loads (waits count loads in issue order) and before its barriers, which wait on
+// LDS only, so their latency overlaps it.
+template <int R, int U, bool F16, bool EF, bool VEC, bool WIDE>
+__device__ __forceinline__ void pass2_body(const Pass2Args& args, const TensorDesc& d,
+                                           const Tile& t, float* red, OrthShared<R>& sh,
+                                           float* sP) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
-  const Tile t = args.tiles[blockIdx.x];
-  const TensorDesc d = args.td[t.tensor];
-  const LaneGeom L = lane_geom(d, t.b, lane);
-  const bool vec = d.vec != 0;
+  const LaneGeom L = tile_geom<WIDE>(d, t.b, lane);
   const int r0 = t.a * d.rpb;
   const int r1 = min(d.n, r0 + d.rpb);
   const int stride = 4 * L.rpw;
-  const float* __restrict__ Pt = args.P + d.poff;
+  const int rw0 = r0 + wave * L.rpw;
   const float* __restrict__ Et = args.E + d.eoff;
+  // lanes past the last column load (and then ignore) an in-range group, so the first
+  // loads need no branch and the wait counts stay exact
+  const int cc = L.col_ok ? L.c : (VEC ? d.m - 4 : d.m - 1);
+  const int vv = L.col_ok ? L.valid : 1;
+  float x[U][4];
+  auto load_rows = [&](int rw) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int rowc = min(rw + u * stride + L.slot, r1 - 1);
+      ld_mprime4<F16, EF, VEC>(args.bucket, Et, d.boff, static_cast<int64_t>(rowc) * d.m + cc,
+                               vv, args.inv_scale, x[u]);
+    }
+  };
+  // the first rows of M' queue behind the loads of P rows and Gram partials
+  pass2_orth_rows<R>(args, d, t, r0, r1, sh, sP, [&] { load_rows(rw0); });
   float acc[4][R];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int k = 0; k < R; ++k) acc[a][k] = 0.f;
   if (L.col_ok) {
-    for (int rw = r0 + wave * L.rpw; rw < r1; rw += stride * U) {
-      float x[U][4];
+    for (int rw = rw0; rw < r1; rw += stride * U) {
+      if (rw != rw0) load_rows(rw);
       float p[U][R];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int row = rw + u * stride + L.slot;
-        if (row < r1) {
-          load_mprime4<F16, EF>(args.bucket, Et, d, static_cast<int64_t>(row) * d.m + L.c,
-                                vec, L.valid, args.inv_scale, x[u]);
-          load_p_row<R>(Pt, row, p[u]);
-        } else {
+        const bool ok = row < r1;
+        const int rowc = min(row, r1 - 1);
 #pragma unroll
-          for (int a = 0; a < 4; ++a) x[u][a] = 0.f;
+        for (int k = 0; k < R; ++k) p[u][k] = ok ? sP[(rowc - r0) * R + k] : 0.f;
 #pragma unroll
-          for (int k = 0; k < R; ++k) p[u][k] = 0.f;
-        }
+        for (int a = 0; a < 4; ++a) x[u][a] = ok ? x[u][a] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -538,35 +896,93 @@ __global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
   }
 }
 
-// Q of the tensors with several row blocks: the partial slots of a column block
-// summed in row-block order.
-template <int R>
-__global__ void __launch_bounds__(kThreads) k_pass2_reduce(Pass2ReduceArgs args) {
-  if (args.found_inf != nullptr && *args.found_inf) return;
+template <int R, int U, bool F16, bool EF>
+__global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
+  if (F16 && *args.found_inf) return;
+  __shared__ float red[64 * 4 * R];
+  __shared__ OrthShared<R> sh;
+  __shared__ float sP[kPass2StageFloats];
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
-  constexpr int SLOT = kColBlock * R;
-  constexpr int B = 16;  // partial slots loaded before they are added (in order)
-  const float* src = args.partial + static_cast<int64_t>(d.pslot + t.b * d.nrb) * SLOT;
+  if (d.vec && d.lpr == 64)
+    pass2_body<R, U, F16, EF, true, true>(args, d, t, red, sh, sP);
+  else if (d.vec)
+    pass2_body<R, U, F16, EF, true, false>(args, d, t, red, sh, sP);
+  else
+    pass2_body<R, U, F16, EF, false, false>(args, d, t, red, sh, sP);
+}
+
+// Q of the tensors with several row blocks: the partial slots of a column block summed
+// in a fixed order. A slot is 64R float4; the workgroup's threads split the float4 of
+// a slot and, when there are more threads than float4, the row blocks (subset s takes
+// row blocks s, s + NS, ...), so one round of loads covers many row blocks. The
+// subsets are then added in subset order through LDS.
+template <int R>
+__global__ void __launch_bounds__(kReduceThreads) k_pass2_reduce(Pass2ReduceArgs args) {
+  if (args.found_inf != nullptr && *args.found_inf) return;
+  constexpr int F4 = kColBlock * R / 4;
+  constexpr int W = F4 < kReduceThreads ? F4 : kReduceThreads;  // threads per subset
+  constexpr int PER = F4 / W;                                     // float4 per thread
+  constexpr int NS = kReduceThreads / W;                          // row-block subsets
+  constexpr int B = NS >= 8 ? 4 : 8;                              // loads in flight
+  __shared__ float4 part[NS > 1 ? NS - 1 : 1][NS > 1 ? W : 1];
+  const Tile t = args.tiles[blockIdx.x];
+  const TensorDesc d = args.td[t.tensor];
+  const int tid = threadIdx.x;
+  const int sub = tid / W;
+  const int j0 = tid - sub * W;
+  const float4* src = reinterpret_cast<const float4*>(
+      args.partial + static_cast<int64_t>(d.pslot + t.b * d.nrb) * (kColBlock * R));
+  float4 s[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int rb0 = sub; rb0 < d.nrb; rb0 += NS * B) {
+    float4 v[B][PER];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int rb = min(rb0 + b * NS, d.nrb - 1);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) v[b][i] = src[static_cast<int64_t>(rb) * F4 + j0 + i * W];
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const bool ok = rb0 + b * NS < d.nrb;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        s[i].x += ok ? v[b][i].x : 0.f;
+        s[i].y += ok ? v[b][i].y : 0.f;
+        s[i].z += ok ? v[b][i].z : 0.f;
+        s[i].w += ok ? v[b][i].w : 0.f;
+      }
+    }
+  }
+  if constexpr (NS > 1) {
+    if (sub > 0) part[sub - 1][j0] = s[0];
+    __syncthreads();
+    if (sub != 0) return;
+#pragma unroll 1
+    for (int q = 0; q < NS - 1; ++q) {
+      const float4 w = part[q][j0];
+      s[0].x += w.x;
+      s[0].y += w.y;
+      s[0].z += w.z;
+      s[0].w += w.w;
+    }
+  }
   float* Qt = args.Q + d.qoff;
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int f = threadIdx.x + i * kThreads;
-    const int col = t.b * kColBlock + f / R;
-    const int k = f % R;
-    if (col < d.m) {
-      float s = 0.f;
-      for (int rb = 0; rb < d.nrb; rb += B) {
-        float v[B];
+  for (int i = 0; i < PER; ++i) {
+    const float vals[4] = {s[i].x, s[i].y, s[i].z, s[i].w};
 #pragma unroll
-        for (int b = 0; b < B; ++b)
-          v[b] = (rb + b < d.nrb) ? src[static_cast<int64_t>(rb + b) * SLOT + f] : 0.f;
-#pragma unroll
-        for (int b = 0; b < B; ++b) s += v[b];
+    for (int a = 0; a < 4; ++a) {
+      const int f = 4 * (j0 + i * W) + a;  // float index inside the slot: column * R + k
+      const int col = t.b * kColBlock + f / R;
+      const int k = f % R;
+      if (col < d.m) {
+        const float q = (k < d.rank) ? vals[a] : 0.f;
+        Qt[static_cast<int64_t>(col) * R + k] = q;
+        if (args.QT != nullptr) args.QT[d.qtoff + static_cast<int64_t>(k) * d.mstride + col] = q;
       }
-      const float q = (k < d.rank) ? s : 0.f;
-      Qt[static_cast<int64_t>(col) * R + k] = q;
-      if (args.QT != nullptr) args.QT[d.qtoff + static_cast<int64_t>(k) * d.mstride + col] = q;
     }
   }
 }
@@ -579,24 +995,17 @@ __device__ void f16_unscale_range(const FlatTile ft, void* bucket, float inv_sca
     h[i] = __half_as_ushort(__float2half_rn(half_bits_to_float(h[i]) * inv_scale));
 }
 
-// M_hat = P Q^T into the bucket and E = M' - M_hat over one tile.
-template <int R, int U, bool F16, bool EF>
-__global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
-  if (F16 && *args.found_inf) return;
-  if (static_cast<int>(blockIdx.x) >= args.ntiles) {
-    if constexpr (F16)
-      f16_unscale_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.inv_scale);
-    return;
-  }
+// M_hat = P Q^T into the bucket and E = M' - M_hat over one tile. All loads of an
+// iteration come from rows clamped into the tile; stores are kept to real rows.
+template <int R, int U, bool F16, bool EF, bool VEC, bool WIDE>
+__device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDesc& d,
+                                           const Tile& t) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
-  const Tile t = args.tiles[blockIdx.x];
-  const TensorDesc d = args.td[t.tensor];
-  const LaneGeom L = lane_geom(d, t.b, lane);
+  const LaneGeom L = tile_geom<WIDE>(d, t.b, lane);
   if (!L.col_ok) return;
-  const bool vec = d.vec != 0;
-  const int r0 = t.a * d.rpb;
-  const int r1 = min(d.n, r0 + d.rpb);
+  const int r0 = t.a * d.rpb3;
+  const int r1 = min(d.n, r0 + d.rpb3);
   const int stride = 4 * L.rpw;
   const float* __restrict__ Pt = args.P + d.poff;
   float* __restrict__ Et = args.E + d.eoff;
@@ -607,12 +1016,13 @@ __global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
     float p[U][R];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int row = rw + u * stride + L.slot;
-      if (row < r1) {
-        load_mprime4<F16, EF>(args.bucket, Et, d, static_cast<int64_t>(row) * d.m + L.c, vec,
-                              L.valid, args.inv_scale, x[u]);
-        load_p_row<R>(Pt, row, p[u]);
-      }
+      const int rowc = min(rw + u * stride + L.slot, r1 - 1);
+      ld_mprime4<F16, EF, VEC>(args.bucket, Et, d.boff, static_cast<int64_t>(rowc) * d.m + L.c,
+                               L.valid, args.inv_scale, x[u]);
+      if constexpr (WIDE)
+        load_p_row_uniform<R>(Pt, __builtin_amdgcn_readfirstlane(rowc), p[u]);
+      else
+        load_p_row<R>(Pt, rowc, p[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -628,17 +1038,35 @@ __global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
         mh[a] = s;
       }
       if constexpr (F16)
-        store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, vec, L.valid, mh);
+        store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, VEC, L.valid, mh);
       else
-        store_f32x4(static_cast<float*>(args.bucket) + d.boff + off, vec, L.valid, mh);
+        st_f32x4<VEC>(static_cast<float*>(args.bucket) + d.boff + off, L.valid, mh);
       if constexpr (EF) {
         float e[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) e[a] = x[u][a] - mh[a];
-        store_f32x4(Et + off, vec, L.valid, e);
+        st_f32x4<VEC>(Et + off, L.valid, e);
       }
     }
   }
+}
+
+template <int R, int U, bool F16, bool EF>
+__global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
+  if (F16 && *args.found_inf) return;
+  if (static_cast<int>(blockIdx.x) >= args.ntiles) {
+    if constexpr (F16)
+      f16_unscale_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.inv_scale);
+    return;
+  }
+  const Tile t = args.tiles[blockIdx.x];
+  const TensorDesc d = args.td[t.tensor];
+  if (d.vec && d.lpr == 64)
+    pass3_body<R, U, F16, EF, true, true>(args, d, t);
+  else if (d.vec)
+    pass3_body<R, U, F16, EF, true, false>(args, d, t);
+  else
+    pass3_body<R, U, F16, EF, false, false>(args, d, t);
 }
 
 // ------------------------------------------------- matrix-core passes (R = 16, 32)
@@ -652,40 +1080,6 @@ typedef float mfma_f4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ mfma_f4 mfma16(float a, float b, mfma_f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Loads 4 gradient values of a 16-byte aligned group without a branch (address
-// already clamped into the matrix); fp16 values are unscaled, `raw_bad` tells whether
-// any of them is inf or NaN.
-template <bool F16>
-__device__ __forceinline__ void load_grad4_vec(const void* bucket, int64_t idx, float inv_scale,
-                                               float (&x)[4], bool& raw_bad) {
-  if constexpr (F16) {
-    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(bucket) + idx);
-    const uint16_t raw[4] = {static_cast<uint16_t>(w.x & 0xFFFFu), static_cast<uint16_t>(w.x >> 16),
-                             static_cast<uint16_t>(w.y & 0xFFFFu), static_cast<uint16_t>(w.y >> 16)};
-    raw_bad = false;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      raw_bad |= half_bits_not_finite(raw[a]);
-      x[a] = half_bits_to_float(raw[a]) * inv_scale;
-    }
-  } else {
-    const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(bucket) + idx);
-    x[0] = w.x;
-    x[1] = w.y;
-    x[2] = w.z;
-    x[3] = w.w;
-    raw_bad = false;
-  }
-}
-
-__device__ __forceinline__ void load_f4(const float* p, float (&x)[4]) {
-  const float4 w = *reinterpret_cast<const float4*>(p);
-  x[0] = w.x;
-  x[1] = w.y;
-  x[2] = w.z;
-  x[3] = w.w;
 }
 
 // Pass 1, P = M' Q: a wavefront owns 16 rows; K advances 16 columns per step (lane
@@ -852,8 +1246,8 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
         }
       } else {
         if (row < r1 && col_ok) {
-          load_mprime4<F16, EF>(args.bucket, Et, d, static_cast<int64_t>(row) * m + col, false,
-                                m - col, args.inv_scale, x[u]);
+          ld_mprime4<F16, EF, false>(args.bucket, Et, d.boff, static_cast<int64_t>(row) * m + col,
+                                     m - col, args.inv_scale, x[u]);
         } else {
 #pragma unroll
           for (int a = 0; a < 4; ++a) x[u][a] = 0.f;
@@ -925,8 +1319,8 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
   constexpr int KQ = R / 4;
   constexpr int UR = 2;  // 16-row steps loaded before use
   const int m = d.m;
-  const int r0 = t.a * d.rpb;
-  const int r1 = min(d.n, r0 + d.rpb);
+  const int r0 = t.a * d.rpb3;
+  const int r1 = min(d.n, r0 + d.rpb3);
   const int h = lane >> 4;
   const int cl = lane & 15;
   const int c0 = t.b * kColBlock + 64 * wave;
@@ -975,8 +1369,8 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
           }
         } else {
           if (row < r1 && col < m)
-            load_mprime4<F16, EF>(args.bucket, Et, d, static_cast<int64_t>(row) * m + col, false,
-                                  m - col, args.inv_scale, x[ur][g]);
+            ld_mprime4<F16, EF, false>(args.bucket, Et, d.boff, static_cast<int64_t>(row) * m + col,
+                                       m - col, args.inv_scale, x[ur][g]);
         }
       }
     }
@@ -1027,11 +1421,6 @@ __global__ void __launch_bounds__(kThreads) k_pass3_mfma(Pass3Args args) {
 }
 
 // ------------------------------------------------------------ orthogonalization
-//
-// Gram-Schmidt with epsilon (step 3.4) evaluated on the Gram matrix: every vector
-// the recurrence forms is a combination P c of the columns of P, so its norm and
-// its dot products are c^T G c' with G = P^T P. The recurrence runs on the r x r
-// coefficient vectors in fp64 and the result is applied once, P <- P T, in fp64.
 
 // Gram partials of one row chunk of a job, staged through LDS.
 template <int R>
@@ -1070,122 +1459,13 @@ __global__ void __launch_bounds__(kThreads)
     k_orth(const OrthJob* __restrict__ jobs, float* __restrict__ base, float* __restrict__ tbase,
            const double* __restrict__ gram, double eps, const int32_t* __restrict__ found_inf) {
   if (found_inf != nullptr && *found_inf) return;
-  constexpr int NG = gram_size<R>();
-  __shared__ double sG[R][R];
-  __shared__ double sT[R][R];
-  __shared__ double sC[R];
-  __shared__ double sW[R];
-  __shared__ double sRed[4][NG];
+  __shared__ OrthShared<R> sh;
   const OrthJob j = jobs[blockIdx.y];
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   const int row_begin = blockIdx.x * kOrthRows;
   if (row_begin >= j.rows) return;
-  // 1. G = sum of the partials, in partial order per thread, then the fixed-order
-  //    combination of strided thread sums.
-  {
-    constexpr int PER = (NG + kThreads - 1) / kThreads;
-    // threads split the entries; with spare threads, also the partials
-    if constexpr (NG <= kThreads / 4) {
-      // 4 groups of threads each sum every 4th partial
-      const int grp = tid / NG;
-      const int e = tid - grp * NG;
-      if (grp < 4) {
-        double s = 0.0;
-        for (int p = grp; p < j.nparts; p += 32) {
-          double v[8];
-#pragma unroll
-          for (int b = 0; b < 8; ++b)
-            v[b] = (p + 4 * b < j.nparts) ? gram[j.goff + static_cast<int64_t>(p + 4 * b) * NG + e]
-                                          : 0.0;
-#pragma unroll
-          for (int b = 0; b < 8; ++b) s += v[b];
-        }
-        sRed[grp][e] = s;
-      }
-      __syncthreads();
-      if (tid < NG) {
-        const double g = ((sRed[0][tid] + sRed[1][tid]) + sRed[2][tid]) + sRed[3][tid];
-        int a = 0, rem = tid;
-        while (rem >= R - a) {
-          rem -= R - a;
-          ++a;
-        }
-        const int b = a + rem;
-        sG[a][b] = g;
-        sG[b][a] = g;
-      }
-    } else {
-      for (int i = 0; i < PER; ++i) {
-        const int e = tid + i * kThreads;
-        if (e < NG) {
-          // partials loaded eight at a time, added in partial order
-          double s = 0.0;
-          for (int p = 0; p < j.nparts; p += 8) {
-            double v[8];
-#pragma unroll
-          for (int b = 0; b < 8; ++b)
-            v[b] = (p + b < j.nparts) ? gram[j.goff + static_cast<int64_t>(p + b) * NG + e]
-                                      : 0.0;
-#pragma unroll
-          for (int b = 0; b < 8; ++b) s += v[b];
-          }
-          int a = 0, rem = e;
-          while (rem >= R - a) {
-            rem -= R - a;
-            ++a;
-          }
-          const int b = a + rem;
-          sG[a][b] = s;
-          sG[b][a] = s;
-        }
-      }
-    }
-    __syncthreads();
-  }
-  // 2. the recurrence on coefficient vectors: lane c of wavefront 0 owns column c
-  double cvec[R];
-#pragma unroll
-  for (int l = 0; l < R; ++l) cvec[l] = (l == lane) ? 1.0 : 0.0;
-  for (int i = 0; i < j.rank; ++i) {
-    if (wave == 0 && lane == i) {
-#pragma unroll
-      for (int l = 0; l < R; ++l) sC[l] = cvec[l];
-    }
-    __syncthreads();
-    double w = 0.0;  // (G c_i)_lane
-    if (wave == 0 && lane < R) {
-#pragma unroll
-      for (int l = 0; l < R; ++l) w += sG[lane][l] * sC[l];
-    }
-    double nn = (wave == 0 && lane < R) ? sC[lane] * w : 0.0;
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) nn += __shfl_xor(nn, mask);
-    // |v_i|^2 = c_i^T G c_i; q_i = v_i / (|v_i| + eps)
-    const double inv = 1.0 / (sqrt(nn > 0.0 ? nn : 0.0) + eps);
-    if (wave == 0 && lane < R) sW[lane] = w * inv;  // G q_i (in coefficients)
-    __syncthreads();
-    if (wave == 0 && lane < j.rank) {
-      if (lane == i) {
-#pragma unroll
-        for (int l = 0; l < R; ++l) cvec[l] *= inv;
-      } else if (lane > i) {
-        // <q_i, v_lane> = c_lane^T G c_i / (|v_i| + eps); v_lane -= <q_i, v_lane> q_i
-        double coef = 0.0;
-#pragma unroll
-        for (int l = 0; l < R; ++l) coef += cvec[l] * sW[l];
-#pragma unroll
-        for (int l = 0; l < R; ++l) cvec[l] -= coef * (sC[l] * inv);
-      }
-    }
-    __syncthreads();
-  }
-  if (wave == 0 && lane < R) {
-#pragma unroll
-    for (int l = 0; l < R; ++l) sT[l][lane] = cvec[l];
-  }
-  __syncthreads();
+  orth_gram_sum<R>(j, gram, sh, [] {});
+  orth_transform<R>(j.rank, eps, sh);
   // 3. P <- P T in fp64, rounded once to fp32, for this workgroup's rows; several
   //    rows are loaded before any is transformed.
   float* X = base + j.off;
@@ -1212,7 +1492,7 @@ __global__ void __launch_bounds__(kThreads)
       for (int k = 0; k < R; ++k) {
         double s = 0.0;
 #pragma unroll
-        for (int l = 0; l < R; ++l) s += static_cast<double>(x[b][l]) * sT[l][k];
+        for (int l = 0; l < R; ++l) s += static_cast<double>(x[b][l]) * sh.T[l][k];
         dst[k] = static_cast<float>(s);
         if (j.toff >= 0)
           tbase[j.toff + static_cast<int64_t>(k) * j.tstride + row] = static_cast<float>(s);
@@ -1303,8 +1583,8 @@ __global__ void __launch_bounds__(256)
 
 // Rows loaded per lane before use, by rank (register budget).
 template <int R> constexpr int unroll1() { return pass1_unroll(R); }
-template <int R> constexpr int unroll2() { return R <= 4 ? 8 : (R <= 8 ? 4 : (R <= 16 ? 2 : 1)); }
-template <int R> constexpr int unroll3() { return R <= 8 ? 4 : (R <= 16 ? 2 : 1); }
+template <int R> constexpr int unroll2() { return R <= 4 ? PSGD_PASS2_ROWS : (R <= 8 ? 4 : 1); }
+template <int R> constexpr int unroll3() { return R <= 8 ? PSGD_PASS3_ROWS : 1; }
 
 template <int R>
 hipError_t pass1_r(bool f16, bool ef, const Pass1Args& a, hipStream_t s) {
@@ -1315,13 +1595,13 @@ hipError_t pass1_r(bool f16, bool ef, const Pass1Args& a, hipStream_t s) {
     else if (f16) k_pass1_mfma<R, true, false><<<grid, kThreads, 0, s>>>(a);
     else if (ef) k_pass1_mfma<R, false, true><<<grid, kThreads, 0, s>>>(a);
     else k_pass1_mfma<R, false, false><<<grid, kThreads, 0, s>>>(a);
-    return hipGetLastError();
+  } else {
+    constexpr int U = unroll1<R>();
+    if (f16 && ef) k_pass1<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
+    else if (f16) k_pass1<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
+    else if (ef) k_pass1<R, U, false, true><<<grid, kThreads, 0, s>>>(a);
+    else k_pass1<R, U, false, false><<<grid, kThreads, 0, s>>>(a);
   }
-  constexpr int U = unroll1<R>();
-  if (f16 && ef) k_pass1<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
-  else if (f16) k_pass1<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
-  else if (ef) k_pass1<R, U, false, true><<<grid, kThreads, 0, s>>>(a);
-  else k_pass1<R, U, false, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1334,13 +1614,13 @@ hipError_t pass2_r(bool f16, bool ef, const Pass2Args& a, hipStream_t s) {
     else if (f16) k_pass2_mfma<R, true, false><<<grid, kThreads, 0, s>>>(a);
     else if (ef) k_pass2_mfma<R, false, true><<<grid, kThreads, 0, s>>>(a);
     else k_pass2_mfma<R, false, false><<<grid, kThreads, 0, s>>>(a);
-    return hipGetLastError();
+  } else {
+    constexpr int U = unroll2<R>();
+    if (f16 && ef) k_pass2<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
+    else if (f16) k_pass2<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
+    else if (ef) k_pass2<R, U, false, true><<<grid, kThreads, 0, s>>>(a);
+    else k_pass2<R, U, false, false><<<grid, kThreads, 0, s>>>(a);
   }
-  constexpr int U = unroll2<R>();
-  if (f16 && ef) k_pass2<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
-  else if (f16) k_pass2<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
-  else if (ef) k_pass2<R, U, false, true><<<grid, kThreads, 0, s>>>(a);
-  else k_pass2<R, U, false, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1353,13 +1633,13 @@ hipError_t pass3_r(bool f16, bool ef, const Pass3Args& a, hipStream_t s) {
     else if (f16) k_pass3_mfma<R, true, false><<<grid, kThreads, 0, s>>>(a);
     else if (ef) k_pass3_mfma<R, false, true><<<grid, kThreads, 0, s>>>(a);
     else k_pass3_mfma<R, false, false><<<grid, kThreads, 0, s>>>(a);
-    return hipGetLastError();
+  } else {
+    constexpr int U = unroll3<R>();
+    if (f16 && ef) k_pass3<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
+    else if (f16) k_pass3<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
+    else if (ef) k_pass3<R, U, false, true><<<grid, kThreads, 0, s>>>(a);
+    else k_pass3<R, U, false, false><<<grid, kThreads, 0, s>>>(a);
   }
-  constexpr int U = unroll3<R>();
-  if (f16 && ef) k_pass3<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
-  else if (f16) k_pass3<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
-  else if (ef) k_pass3<R, U, false, true><<<grid, kThreads, 0, s>>>(a);
-  else k_pass3<R, U, false, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1389,7 +1669,7 @@ hipError_t launch_pass2(int R, bool f16, bool ef, const Pass2Args& a, hipStream_
 hipError_t launch_pass2_reduce(int R, const Pass2ReduceArgs& a, hipStream_t s) {
   if (a.ntiles == 0) return hipSuccess;
   PSGD_RANK_SWITCH(R, {
-    k_pass2_reduce<RR><<<dim3(a.ntiles), kThreads, 0, s>>>(a);
+    k_pass2_reduce<RR><<<dim3(a.ntiles), kReduceThreads, 0, s>>>(a);
     return hipGetLastError();
   })
 }

@@ -254,15 +254,20 @@ def test_empty_and_vector_only_buckets():
     assert torch.equal(d, ref)
 
 
-def test_kernel_timing_reports_every_pass():
-    st = PowerSGDState(**_hp())
+@pytest.mark.parametrize("rank,orth_launches", [(4, 1), (16, 4)])
+def test_kernel_timing_reports_every_pass(rank, orth_launches):
+    """Vector ranks orthogonalize P inside pass 2, so the orthogonalization kernel runs
+    once (the initial Q); matrix-core ranks run it for Q and then for P every step."""
+    log(f"case: kernel timing at rank {rank}")
+    st = PowerSGDState(**_hp(matrix_approximation_rank=rank))
     st.set_timing(True)
     d = torch.randn(512 * 300, device="cuda")
     for _ in range(3):
         st.compress_bucket(d, [(0, (512, 300))])
     times = {name: (ms, n, by) for name, ms, n, by in st.kernel_times()}
-    for k in ("pass1_mq", "orthogonalize", "pass2_mtp", "pass3_decompress_error"):
-        assert times[k][1] >= 3 and times[k][0] > 0, k
+    for k in ("pass1_mq", "pass2_mtp", "pass3_decompress_error"):
+        assert times[k][1] == 3 and times[k][0] > 0, k
+    assert times["orthogonalize"][1] == orth_launches
     assert times["pass1_mq"][2] == pytest.approx(3 * 512 * 300 * 12)
 
 
@@ -287,3 +292,12 @@ def test_matrix_core_rank32_fp16():
     shapes = [(256, 320), (64,), (160, 512)]
     _run_parity(_hp(matrix_approximation_rank=32), shapes, steps=3, dtype="f16",
                 inv_scale=2.0 ** -8, bucket_fn=lambda s: _rand_bucket(shapes, 110 + s, 20.0))
+
+
+def test_tall_narrow_matrices_keep_their_p_rows_in_lds():
+    """Row blocks of narrow matrices are capped so that a pass-2 workgroup holds its
+    orthogonalized P rows in LDS (ranks 4 and 8, several row blocks, ragged tails)."""
+    log("case: tall narrow matrices, r = 8, row blocks capped by the LDS staging")
+    hp = _hp(matrix_approximation_rank=8, min_compression_rate=0.5)
+    par = _run_parity(hp, [(5003, 4), (3001, 12), (2049, 9), (40,)], steps=3, seed=7)
+    assert par.gpu.decisions(0, 4) == [1, 1, 1, 0]
