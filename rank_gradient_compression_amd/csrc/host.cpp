@@ -707,7 +707,8 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
   const double ce = static_cast<double>(pl.compressed_elems);
   const double ue = static_cast<double>(pl.uncompressed_elems);
   const double eps = hp.orthogonalization_epsilon;
-  // vector ranks: the Gram partials come from pass 1 and pass 2 orthogonalizes P itself
+  // vector ranks: the Gram partials come from pass 1, pass 2 orthogonalizes P itself
+  // and pass 3 sums the pass-2 partials
   const bool fused = R <= kMaxFusedGramRank;
   const uint64_t bucket_key = static_cast<uint64_t>(bucket_index);
   powersgd_status r = POWERSGD_OK;
@@ -789,7 +790,7 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
     r = timed_launch(st, s, K_PASS2, ce * pass_bytes(K_PASS2, f16, ef), "pass 2",
                      [&] { return launch_pass2(R, f16, ef, a, s); });
     if (r != POWERSGD_OK) return r;
-    if (!pl.tiles2r.empty()) {
+    if (!fused && !pl.tiles2r.empty()) {
       Pass2ReduceArgs b{};
       b.tiles = pl.d_tiles2r;
       b.ntiles = static_cast<int32_t>(pl.tiles2r.size());
@@ -815,6 +816,7 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
     a.E = pl.E;
     a.P = pl.P;
     a.Q = pl.Q;
+    a.partial = pl.partial;  // vector ranks sum the pass-2 partials here
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
     const double bytes = ce * pass_bytes(K_PASS3, f16, ef) + (f16 ? ue * 4.0 : 0.0);

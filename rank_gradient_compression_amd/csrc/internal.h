@@ -141,7 +141,8 @@ struct Pass3Args {
   void* bucket;
   float* E;
   const float* P;
-  const float* Q;
+  float* Q;                // vector ranks: written here for tensors split into row blocks
+  const float* partial;    // vector ranks: pass-2 partial slots (summed here)
   float inv_scale;
   const int32_t* found_inf;
 };

@@ -22,9 +22,10 @@
 //           pass-2 workgroup for its own rows; larger ranks in a kernel of its own.
 //   pass 2  Q = M'^T P. A workgroup owns a 256-column block of a row block; its row
 //           slots and wavefronts are combined in a fixed order; tensors with several
-//           row blocks write one partial per block, summed in a fixed order by a
-//           small second kernel (deterministic, no atomics, no inter-workgroup
-//           fences: the kernel boundary publishes the partials).
+//           row blocks write one partial per block, summed in a fixed order by the
+//           pass-3 workgroups of that column block (vector ranks) or by a small
+//           kernel of its own (matrix-core ranks): deterministic, no atomics, no
+//           inter-workgroup fences (the kernel boundary publishes the partials).
 //   pass 3  M_hat = P Q^T written into the bucket (fp16: round to nearest even),
 //           E = M' - M_hat.
 //   q_init  Philox4x64-10 + Box-Muller draw of the initial Q (counter layout in
@@ -791,8 +792,8 @@ __device__ __forceinline__ void pass2_orth_rows(const Pass2Args& args, const Ten
 }
 
 // Q = M'^T P over one tile (P rows from LDS); row slots and wavefronts are combined in
-// a fixed order; with several row blocks each writes a partial slot (summed by
-// k_pass2_reduce). Rows are clamped into the tile so all loads of an iteration are
+// a fixed order; with several row blocks each writes a partial slot (summed at the
+// start of pass 3). Rows are clamped into the tile so all loads of an iteration are
 // issued together; clamped duplicate rows are zeroed before they are accumulated. The
 // first rows of M' are requested during the orthogonalization prologue, after its own
 // loads (waits count loads in issue order) and before its barriers, which wait on
@@ -995,22 +996,88 @@ __device__ void f16_unscale_range(const FlatTile ft, void* bucket, float inv_sca
     h[i] = __half_as_ushort(__float2half_rn(half_bits_to_float(h[i]) * inv_scale));
 }
 
+// Q for the lane's 4 columns when pass 2 split the matrix into several row blocks
+// (vector ranks): the partial slots of the column block are summed here instead of in
+// a kernel of their own. Wavefront w adds slots w, w + 4, ... in order; the four
+// sums are added in wavefront order through LDS (qred: 4 x 4R x 64 floats), so
+// every workgroup of the column block gets the same Q. Row block 0 stores it as the
+// warm-start Q.
+template <int R>
+__device__ __forceinline__ void pass3_q_from_partials(const Pass3Args& args, const TensorDesc& d,
+                                                      const Tile& t, const LaneGeom& L,
+                                                      int lane, int wave, float* qred,
+                                                      float (&q)[4][R]) {
+  constexpr int F = 4 * R;  // floats per lane: 4 columns x R
+  constexpr int NB = 4;     // slots in flight per lane
+  const float* base = args.partial + static_cast<int64_t>(d.pslot + t.b * d.nrb) * (kColBlock * R) +
+                      L.g * F;
+  float s[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) s[f] = 0.f;
+  for (int rb0 = wave; rb0 < d.nrb; rb0 += 4 * NB) {
+    float v[NB][F];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float4* src = reinterpret_cast<const float4*>(
+          base + static_cast<int64_t>(min(rb0 + 4 * b, d.nrb - 1)) * (kColBlock * R));
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const float4 w = src[i];
+        v[b][4 * i + 0] = w.x;
+        v[b][4 * i + 1] = w.y;
+        v[b][4 * i + 2] = w.z;
+        v[b][4 * i + 3] = w.w;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const bool ok = rb0 + 4 * b < d.nrb;
+#pragma unroll
+      for (int f = 0; f < F; ++f) s[f] += ok ? v[b][f] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < F; ++f) qred[(wave * F + f) * 64 + lane] = s[f];
+  __syncthreads();
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    float v = qred[f * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += qred[(w * F + f) * 64 + lane];
+    q[f / R][f % R] = v;
+  }
+  if (t.a == 0 && wave == 0 && L.slot == 0 && L.col_ok) {
+    float* Qt = args.Q + d.qoff;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      if (a < L.valid) {
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+          Qt[static_cast<int64_t>(L.c + a) * R + k] = (k < d.rank) ? q[a][k] : 0.f;
+      }
+  }
+}
+
 // M_hat = P Q^T into the bucket and E = M' - M_hat over one tile. All loads of an
 // iteration come from rows clamped into the tile; stores are kept to real rows.
 template <int R, int U, bool F16, bool EF, bool VEC, bool WIDE>
 __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDesc& d,
-                                           const Tile& t) {
+                                           const Tile& t, float* qred) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
   const LaneGeom L = tile_geom<WIDE>(d, t.b, lane);
+  float q[4][R];
+  if (d.nrb > 1) {
+    pass3_q_from_partials<R>(args, d, t, L, lane, wave, qred, q);
+  } else {
+    load_q_rows<R>(args.Q + d.qoff, L.c, d.m, q);
+  }
   if (!L.col_ok) return;
   const int r0 = t.a * d.rpb3;
   const int r1 = min(d.n, r0 + d.rpb3);
   const int stride = 4 * L.rpw;
   const float* __restrict__ Pt = args.P + d.poff;
   float* __restrict__ Et = args.E + d.eoff;
-  float q[4][R];
-  load_q_rows<R>(args.Q + d.qoff, L.c, d.m, q);
   for (int rw = r0 + wave * L.rpw; rw < r1; rw += stride * U) {
     float x[U][4];
     float p[U][R];
@@ -1054,6 +1121,7 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
 template <int R, int U, bool F16, bool EF>
 __global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
   if (F16 && *args.found_inf) return;
+  __shared__ float qred[4 * 4 * R * 64];
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
     if constexpr (F16)
       f16_unscale_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.inv_scale);
@@ -1062,11 +1130,11 @@ __global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec && d.lpr == 64)
-    pass3_body<R, U, F16, EF, true, true>(args, d, t);
+    pass3_body<R, U, F16, EF, true, true>(args, d, t, qred);
   else if (d.vec)
-    pass3_body<R, U, F16, EF, true, false>(args, d, t);
+    pass3_body<R, U, F16, EF, true, false>(args, d, t, qred);
   else
-    pass3_body<R, U, F16, EF, false, false>(args, d, t);
+    pass3_body<R, U, F16, EF, false, false>(args, d, t, qred);
 }
 
 // ------------------------------------------------- matrix-core passes (R = 16, 32)
