@@ -1150,13 +1150,17 @@ __device__ __forceinline__ mfma_f4 mfma16(float a, float b, mfma_f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Pass 1, P = M' Q: a wavefront owns 16 rows; K advances 16 columns per step (lane
-// group h loads columns 4h..4h+3, MFMA K-step s pairs them with Q row 4h+s, read as
-// 16 bytes of Q^T). VEC: rows are 16-byte aligned, so all loads of U steps are issued
-// from clamped addresses before any is used, and invalid lanes are masked after.
+// Pass 1, P = M' Q: a workgroup owns 16 rows. Wavefront w takes the 64-column chunks
+// w, w + 4, w + 8, ... (U = 4 K-steps of 16 columns each), so in every round the
+// workgroup reads a contiguous 1 KB of each of its rows; lane group h loads columns
+// 4h..4h+3 of a K-step (one 16-byte load per four MFMA K-steps) and the matching 16
+// bytes of Q^T rows 16nt + cl. The wavefronts' partial P are added in wavefront
+// order through LDS at the end (red: 4 x NT x 4 x 64 floats). VEC: rows are 16-byte
+// aligned, so all loads of a chunk are issued from clamped addresses before any is
+// used, and invalid lanes are masked after.
 template <int R, bool F16, bool EF, bool VEC>
 __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const TensorDesc& d,
-                                                const Tile& t, int lane, int wave) {
+                                                const Tile& t, int lane, int wave, float* red) {
   constexpr int NT = R / 16;
   constexpr int U = 4;
   const int m = d.m;
@@ -1164,18 +1168,17 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
   const int r1 = min(d.n, r0 + d.rpb1);
   const int h = lane >> 4;
   const int cl = lane & 15;
-  const int rw = r0 + 16 * wave;
-  if (rw >= r1) return;
-  const int row = rw + cl;
+  const int row = r0 + cl;
   const bool row_ok = row < r1;
   const int rowc = min(row, r1 - 1);
   float* __restrict__ Et = args.E + d.eoff;
+  float* __restrict__ Mt = static_cast<float*>(args.bucket) + d.boff;
   const float* __restrict__ QTt = args.QT + d.qtoff;
   mfma_f4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
   int bad = 0;
-  for (int k0 = 0; k0 < m; k0 += 16 * U) {
+  for (int k0 = 64 * wave; k0 < m; k0 += 256) {
     float x[U][4];
     float e[U][4];
     float b[U][NT][4];
@@ -1195,6 +1198,11 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
         for (int nt = 0; nt < NT; ++nt)
           load_f4(QTt + static_cast<int64_t>(16 * nt + cl) * d.mstride + colc, b[u][nt]);
       } else {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          x[u][a] = 0.f;
+          e[u][a] = 0.f;
+        }
         if (ok[u]) {
           const int64_t off = static_cast<int64_t>(row) * m + col;
           load_grad4<F16>(args.bucket, d.boff + off, false, m - col, args.inv_scale, x[u], bad);
@@ -1226,9 +1234,7 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
         x[u][a] = ok[u] ? v : 0.f;
       }
       if constexpr (EF && !F16) {
-        if (ok[u])
-          store_f32x4(static_cast<float*>(args.bucket) + d.boff + static_cast<int64_t>(row) * m + col,
-                      VEC, m - col, x[u]);
+        if (ok[u]) store_f32x4(Mt + static_cast<int64_t>(row) * m + col, VEC, m - col, x[u]);
       }
     }
 #pragma unroll
@@ -1238,23 +1244,34 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(x[u][s4], b[u][nt][s4], acc[nt]);
   }
+  if constexpr (F16) {
+    if (__any(bad) && lane == 0) atomicOr(args.found_inf, 1);
+  }
+  // partial P of every wavefront to LDS; wavefront 0 adds them in order
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[((wave * NT + nt) * 4 + v) * 64 + lane] = acc[nt][v];
+  __syncthreads();
+  if (wave != 0) return;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int prow = rw + 4 * h + v;
+      float sum = red[(nt * 4 + v) * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) sum += red[((w * NT + nt) * 4 + v) * 64 + lane];
+      const int prow = r0 + 4 * h + v;
       const int k = 16 * nt + cl;
-      if (prow < r1)
-        args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? acc[nt][v] : 0.f;
+      if (prow < r1) args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? sum : 0.f;
     }
-  }
-  if constexpr (F16) {
-    if (__any(bad) && lane == 0) atomicOr(args.found_inf, 1);
   }
 }
 
 template <int R, bool F16, bool EF>
 __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
+  static_assert(kMfmaPass1Rows == 16, "a workgroup owns one 16-row MFMA group");
+  __shared__ float red[4 * (R / 16) * 4 * 64];
   const int lane = threadIdx.x & 63;
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
     if constexpr (F16)
@@ -1265,9 +1282,9 @@ __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec)
-    pass1_mfma_body<R, F16, EF, true>(args, d, t, lane, wave);
+    pass1_mfma_body<R, F16, EF, true>(args, d, t, lane, wave, red);
   else
-    pass1_mfma_body<R, F16, EF, false>(args, d, t, lane, wave);
+    pass1_mfma_body<R, F16, EF, false>(args, d, t, lane, wave, red);
 }
 
 // Pass 2, Q = M'^T P: a wavefront owns 64 columns of the tile; lane group h takes row
