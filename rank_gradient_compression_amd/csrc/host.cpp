@@ -213,8 +213,10 @@ hipEvent_t take_event(powersgd_state* st) {
     st->free_events.pop_back();
     return e;
   }
+  // timing only: no system-scope fence (cache writeback) when the event is recorded,
+  // so the events disturb the kernels they bracket as little as possible
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
