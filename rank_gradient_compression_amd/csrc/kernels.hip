@@ -1487,6 +1487,105 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
   }
 }
 
+// Pass 3 on matrix cores with row-contiguous memory traffic (rows 16-byte aligned):
+// each 32-row step the wavefronts compute their 16 x 16 blocks of M_hat = (Q P^T)^T as
+// above (wavefront w: columns 64w..64w+63 of the 256-column block) into an LDS tile of
+// 32 rows x 256 columns; after a barrier wavefront w takes rows 8w..8w+7 of the tile,
+// lane l columns 4l..4l+3, so M' loads and the M_hat and E stores cover 1 KB of one
+// row per instruction instead of 64 bytes of 16 rows. The step's M' rows are
+// requested before its MFMAs.
+constexpr int kPass3TileStride = kColBlock + 4;  // LDS row stride (floats), padded
+
+template <int R, bool F16, bool EF>
+__device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const TensorDesc& d,
+                                                const Tile& t, int lane, int wave,
+                                                float* tile) {
+  constexpr int KQ = R / 4;
+  constexpr int UR = 2;         // 16-row MFMA groups per step
+  constexpr int SR = 16 * UR;   // rows per step
+  constexpr int RW = SR / 4;    // rows per wavefront in the row phase
+  constexpr int LS = kPass3TileStride;
+  const int m = d.m;
+  const int r0 = t.a * d.rpb3;
+  const int r1 = min(d.n, r0 + d.rpb3);
+  const int h = lane >> 4;
+  const int cl = lane & 15;
+  const int cw = t.b * kColBlock + 64 * wave;  // MFMA phase: this wavefront's columns
+  const int cr = t.b * kColBlock + 4 * lane;   // row phase: this lane's 4 columns
+  const bool cr_ok = cr < m;
+  const int crc = min(cr, m - 4);
+  const float* __restrict__ Pt = args.P + d.poff;
+  const float* __restrict__ Qt = args.Q + d.qoff;
+  float* __restrict__ Et = args.E + d.eoff;
+  float qa[4][KQ];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int qcol = min(cw + 16 * g + cl, m - 1);
+#pragma unroll
+    for (int k4 = 0; k4 < KQ / 4; ++k4) {
+      float w[4];
+      load_f4(Qt + static_cast<int64_t>(qcol) * R + h * KQ + 4 * k4, w);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) qa[g][4 * k4 + a] = w[a];
+    }
+  }
+  for (int rr = r0; rr < r1; rr += SR) {
+    float x[RW][4];
+    if constexpr (EF) {
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        const int row = min(rr + RW * wave + i, r1 - 1);
+        ld_mprime4<F16, EF, true>(args.bucket, Et, d.boff, static_cast<int64_t>(row) * m + crc, 4,
+                                  args.inv_scale, x[i]);
+      }
+    }
+    float pb[UR][KQ];
+#pragma unroll
+    for (int ur = 0; ur < UR; ++ur) {
+      const int rowc = min(rr + 16 * ur + cl, r1 - 1);
+#pragma unroll
+      for (int k4 = 0; k4 < KQ / 4; ++k4) {
+        float w[4];
+        load_f4(Pt + static_cast<int64_t>(rowc) * R + h * KQ + 4 * k4, w);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) pb[ur][4 * k4 + a] = w[a];
+      }
+    }
+#pragma unroll
+    for (int ur = 0; ur < UR; ++ur) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        mfma_f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) acc = mfma16(qa[g][kq], pb[ur][kq], acc);
+        *reinterpret_cast<float4*>(tile + (16 * ur + cl) * LS + 64 * wave + 16 * g + 4 * h) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int row = rr + RW * wave + i;
+      if (row < r1 && cr_ok) {
+        const float4 v = *reinterpret_cast<const float4*>(tile + (RW * wave + i) * LS + 4 * lane);
+        const float mh[4] = {v.x, v.y, v.z, v.w};
+        const int64_t off = static_cast<int64_t>(row) * m + cr;
+        if constexpr (F16)
+          store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, true, 4, mh);
+        else
+          store_f32x4(static_cast<float*>(args.bucket) + d.boff + off, true, 4, mh);
+        if constexpr (EF) {
+          float e[4];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) e[a] = x[i][a] - mh[a];
+          store_f32x4(Et + off, true, 4, e);
+        }
+      }
+    }
+    __syncthreads();  // the tile is rewritten by the next step
+  }
+}
+
 template <int R, bool F16, bool EF>
 __global__ void __launch_bounds__(kThreads) k_pass3_mfma(Pass3Args args) {
   if (F16 && *args.found_inf) return;
@@ -1495,12 +1594,13 @@ __global__ void __launch_bounds__(kThreads) k_pass3_mfma(Pass3Args args) {
       f16_unscale_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.inv_scale);
     return;
   }
+  __shared__ float tile[32 * kPass3TileStride];
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec)
-    pass3_mfma_body<R, F16, EF, true>(args, d, t, lane, wave);
+    pass3_mfma_rows<R, F16, EF>(args, d, t, lane, wave, tile);
   else
     pass3_mfma_body<R, F16, EF, false>(args, d, t, lane, wave);
 }
