@@ -1268,10 +1268,125 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
   }
 }
 
+// Pass 1 on matrix cores with row-contiguous memory traffic (rows 16-byte aligned): the
+// workgroup's 16 rows are processed in 256-column chunks. Row phase: wavefront w loads
+// rows 4w..4w+3 of the chunk (lane l: columns 4l..4l+3, 1 KB of a row per load), forms
+// M' (fp32 with error feedback: stored back the same way) and writes it to an LDS
+// tile. MFMA phase: wavefront w takes the chunk's columns 64w..64w+63 (four K-steps of
+// 16) from the tile, with the matching 16 bytes of Q^T rows 16nt + cl per K-step. The
+// next chunk's rows are requested before the MFMA phase of this one.
+constexpr int kPass1TileStride = kColBlock + 4;  // LDS row stride (floats), padded
+
+template <int R, bool F16, bool EF>
+__device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const TensorDesc& d,
+                                                const Tile& t, int lane, int wave, float* red,
+                                                float* tile) {
+  constexpr int NT = R / 16;
+  constexpr int LS = kPass1TileStride;
+  const int m = d.m;
+  const int r0 = t.a * d.rpb1;
+  const int r1 = min(d.n, r0 + d.rpb1);
+  const int h = lane >> 4;
+  const int cl = lane & 15;
+  float* __restrict__ Et = args.E + d.eoff;
+  float* __restrict__ Mt = static_cast<float*>(args.bucket) + d.boff;
+  const float* __restrict__ QTt = args.QT + d.qtoff;
+  mfma_f4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
+  int bad = 0;
+  // row phase geometry: rows 4w..4w+3 of the group, columns 4l..4l+3 of the chunk
+  int64_t rbase[4];
+  bool rok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = r0 + 4 * wave + i;
+    rok[i] = row < r1;
+    rbase[i] = static_cast<int64_t>(min(row, r1 - 1)) * m;
+  }
+  float xg[4][4], xe[4][4];
+  auto load_rows = [&](int k0) {
+    const int colc = min(k0 + 4 * lane, m - 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bool rb;
+      load_grad4_vec<F16>(args.bucket, d.boff + rbase[i] + colc, args.inv_scale, xg[i], rb);
+      if (rok[i] && k0 + 4 * lane < m && rb) bad = 1;
+      if constexpr (EF) load_f4(Et + rbase[i] + colc, xe[i]);
+    }
+  };
+  load_rows(0);
+  for (int k0 = 0; k0 < m; k0 += kColBlock) {
+    const int col = k0 + 4 * lane;
+    const bool cok = col < m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float x = xg[i][a];
+        if constexpr (EF) x += xe[i][a];
+        v[a] = (rok[i] && cok) ? x : 0.f;
+      }
+      if constexpr (EF && !F16) {
+        if (rok[i] && cok) store_f32x4(Mt + rbase[i] + col, true, 4, v);
+      }
+      *reinterpret_cast<float4*>(tile + (4 * wave + i) * LS + 4 * lane) =
+          make_float4(v[0], v[1], v[2], v[3]);
+    }
+    if (k0 + kColBlock < m) load_rows(k0 + kColBlock);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kc = 64 * wave + 16 * u + 4 * h;  // column inside the chunk
+      const int colc = min(k0 + kc, m - 4);
+      const float4 av = *reinterpret_cast<const float4*>(tile + cl * LS + kc);
+      const float a4[4] = {av.x, av.y, av.z, av.w};
+      float b[NT][4];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        load_f4(QTt + static_cast<int64_t>(16 * nt + cl) * d.mstride + colc, b[nt]);
+        if (k0 + kc >= m) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) b[nt][a] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(a4[s4], b[nt][s4], acc[nt]);
+    }
+    __syncthreads();  // the tile is rewritten by the next chunk
+  }
+  if constexpr (F16) {
+    if (__any(bad) && lane == 0) atomicOr(args.found_inf, 1);
+  }
+  // partial P of every wavefront to LDS; wavefront 0 adds them in order
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[((wave * NT + nt) * 4 + v) * 64 + lane] = acc[nt][v];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float sum = red[(nt * 4 + v) * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) sum += red[((w * NT + nt) * 4 + v) * 64 + lane];
+      const int prow = r0 + 4 * h + v;
+      const int k = 16 * nt + cl;
+      if (prow < r1) args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? sum : 0.f;
+    }
+  }
+}
+
 template <int R, bool F16, bool EF>
 __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
   static_assert(kMfmaPass1Rows == 16, "a workgroup owns one 16-row MFMA group");
   __shared__ float red[4 * (R / 16) * 4 * 64];
+  __shared__ float tile[16 * kPass1TileStride];
   const int lane = threadIdx.x & 63;
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
     if constexpr (F16)
@@ -1282,7 +1397,7 @@ __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec)
-    pass1_mfma_body<R, F16, EF, true>(args, d, t, lane, wave, red);
+    pass1_mfma_rows<R, F16, EF>(args, d, t, lane, wave, red, tile);
   else
     pass1_mfma_body<R, F16, EF, false>(args, d, t, lane, wave, red);
 }
