@@ -13,15 +13,19 @@ Parity status per function (what pins each one is listed in the tests):
                                         closed forms for epsilon > 0)
   OracleState.compress_bucket ......... pinned (rational projection, hand-worked
                                         example, invariants, Eckart-Young limit)
+  powersgd.batched_side ............... pinned (brute force over integers)
+  OracleState.compress_bucket_batched . pinned (hand-worked two-step example,
+                                        exact rank-1 recovery, error-feedback
+                                        identity over the padding, fp16 cases)
 """
 from .powersgd import (HParams, LayoutChanged, OracleState, StepResult, ViewResult,
-                       any_nonfinite, compress_matrix_step,
+                       any_nonfinite, batched_side, compress_matrix_step,
                        effective_rank, gram_schmidt, matrix_view, should_compress)
 from .rng import box_muller, mulhilo64, philox4x64_10, standard_normal_q0
 
 __all__ = [
     "HParams", "LayoutChanged", "OracleState", "StepResult", "ViewResult",
-    "any_nonfinite", "compress_matrix_step",
+    "any_nonfinite", "batched_side", "compress_matrix_step",
     "effective_rank", "gram_schmidt", "matrix_view", "should_compress",
     "box_muller", "mulhilo64", "philox4x64_10", "standard_normal_q0",
 ]

@@ -92,6 +92,15 @@ def should_compress(n: int, m: int, rank: int, min_compression_rate: float) -> b
     return (n + m) * rank * Fraction(min_compression_rate) < n * m
 
 
+def batched_side(numel: int) -> int:
+    """batched_powerSGD_hook step 1 ("PowerSGD Hooks"): the flat bucket is viewed as a
+    square matrix with zero padding; its side is the smallest s with s * s >= numel."""
+    if numel <= 0:
+        return 0
+    s = math.isqrt(numel)
+    return s if s * s == numel else s + 1
+
+
 def effective_rank(n: int, m: int, rank: int) -> int:
     """READING: a factor cannot have more columns than the matrix has rows or columns."""
     return min(rank, n, m)
@@ -259,6 +268,69 @@ class OracleState:
             result.output = out64.astype(np.float16)
         else:
             result.output = out64.astype(np.float32)
+        if is_last:
+            self.iteration += 1
+        return result
+
+    def compress_bucket_batched(self, bucket: np.ndarray, bucket_index: int = 0,
+                                is_last: bool = True,
+                                inv_loss_scale: float = 1.0) -> StepResult:
+        """One batched_powerSGD_hook call ("PowerSGD Hooks", batched_powerSGD_hook,
+        steps 1 to 9) on a single rank's flat bucket of numel elements.
+
+        The bucket, followed by s * s - numel zeros, is the s x s row-major matrix M
+        (step 1); then P = M Q, Gram-Schmidt, Q = M^T P, M_hat = P Q^T as in
+        powerSGD_hook (steps 2 to 8, both allreduces the identity), and the result is
+        M_hat's first numel elements (step 9).
+        READING: the state's error feedback and warm start apply as for powerSGD_hook,
+        with E covering all s * s entries (the padding of G is zero at every call, so
+        E's padded entries carry over); there is no rate test; the rank is
+        min(r, s); the Q draw uses view index 0; the memorized layout of the bucket is
+        ("batched", numel). The returned views list holds the one matrix; stats count
+        numel in and 2 s r communicated.
+        """
+        hp = self.hp
+        bucket = np.asarray(bucket)
+        if bucket.dtype not in (np.float32, np.float16):
+            raise TypeError("bucket must be float32 or float16")
+        is_fp16 = bucket.dtype == np.float16
+        numel = int(bucket.size)
+        x64 = bucket.astype(np.float64)
+        found_inf = is_fp16 and not bool(np.all(np.isfinite(bucket)))
+        if found_inf:
+            if is_last:
+                self.iteration += 1
+            return StepResult(output=bucket.copy(), output64=x64, found_inf=True,
+                              skipped=True, passthrough=False)
+        g_all = x64 * float(inv_loss_scale) if is_fp16 else x64
+        result = StepResult(output=bucket, output64=g_all.copy(), found_inf=False,
+                            skipped=False, passthrough=False)
+        if self.iteration < hp.start_powerSGD_iter:
+            result.passthrough = True
+            result.output = g_all.astype(bucket.dtype) if is_fp16 else bucket.copy()
+            if is_last:
+                self.iteration += 1
+            return result
+        layout = ("batched", numel)
+        mem = self.buckets.get(bucket_index)
+        if mem is not None and mem.layout != layout:
+            if hp.use_error_feedback or hp.warm_start:
+                raise LayoutChanged(f"bucket {bucket_index} changed its layout")
+            mem = None
+        if mem is None:
+            mem = _BucketMemory(layout=layout)
+            self.buckets[bucket_index] = mem
+        s = batched_side(numel)
+        if s > 0:
+            padded = np.zeros(s * s, dtype=np.float64)
+            padded[:numel] = g_all
+            rank = effective_rank(s, s, hp.matrix_approximation_rank)
+            vr = self._compress_matrix(padded.reshape(s, s), mem, 0, bucket_index, rank)
+            result.output64 = vr.m_hat.reshape(-1)[:numel].copy()
+            result.views.append(vr)
+            self.numel_comm += 2 * s * rank
+        self.numel_in += numel
+        result.output = result.output64.astype(bucket.dtype)
         if is_last:
             self.iteration += 1
         return result
