@@ -97,7 +97,10 @@ def cpu_baseline(cfg, budget_s: float = 20.0):
         arr = bucket.numpy()
         scale = cfg.loss_scale if cfg.dtype == "f16" else 1.0
         t0 = time.perf_counter()
-        st.compress_bucket(arr, views, inv_loss_scale=1.0 / scale)
+        if cfg.batched:
+            st.compress_bucket_batched(arr, inv_loss_scale=1.0 / scale)
+        else:
+            st.compress_bucket(arr, views, inv_loss_scale=1.0 / scale)
         times.append(time.perf_counter() - t0)
         step += 1
         if time.perf_counter() - t_start > budget_s or step >= cfg.steps:
@@ -129,7 +132,7 @@ def main() -> int:
 
     import torch
 
-    from rank_gradient_compression_amd import PowerSGDState
+    from rank_gradient_compression_amd import PowerSGDState, powersgd_batched_side
     from synthetic import CONFIGS, BucketGenerator
 
     cfg = CONFIGS[args.config]
@@ -150,6 +153,15 @@ def main() -> int:
     # Benchmark steps carry the workload's random inf draws only (the forced inf step
     # belongs to the correctness runs).
     pool = [gen.bucket(i, forced=False) for i in range(pool_n)]
+    side = powersgd_batched_side(cfg.numel) if cfg.batched else 0
+    if cfg.batched:
+        # the batched variant works in a buffer that holds the padded square matrix
+        padded = []
+        for b in pool:
+            buf = torch.zeros(side * side, dtype=b.dtype, device=dev)
+            buf[:cfg.numel].copy_(b)
+            padded.append(buf)
+        pool = padded
     views = cfg.views()
     hp = dict(cfg.hparams)
     hp["compression_stats_logging_frequency"] = 0
@@ -161,8 +173,13 @@ def main() -> int:
     def run(i):
         if cfg.dtype == "f16":
             found.zero_()      # a new iteration: GradScaler starts from "no inf found"
-        st.compress_bucket(pool[i % pool_n], views, inv_loss_scale=inv,
-                           found_inf=found if cfg.dtype == "f16" else None, stream=stream)
+        if cfg.batched:
+            st.compress_bucket_batched(pool[i % pool_n], numel=cfg.numel, inv_loss_scale=inv,
+                                       found_inf=found if cfg.dtype == "f16" else None,
+                                       stream=stream)
+        else:
+            st.compress_bucket(pool[i % pool_n], views, inv_loss_scale=inv,
+                               found_inf=found if cfg.dtype == "f16" else None, stream=stream)
 
     for i in range(args.warmup):
         run(i)
@@ -221,11 +238,14 @@ def main() -> int:
     hp_c.matrix_approximation_rank = cfg.hparams["matrix_approximation_rank"]
     hp_c.min_compression_rate = cfg.hparams["min_compression_rate"]
     comp_elems = 0
-    for _, shp in views:
-        comp, n, m, _r = api.powersgd_classify_view(hp_c, shp)
-        comp_elems += n * m if comp else 0
+    if cfg.batched:
+        comp_elems = side * side  # one padded square matrix
+    else:
+        for _, shp in views:
+            comp, n, m, _r = api.powersgd_classify_view(hp_c, shp)
+            comp_elems += n * m if comp else 0
     per_elt = 28 if cfg.dtype == "f32" else 24
-    algo_bytes = comp_elems * per_elt + (0 if cfg.dtype == "f32" else
+    algo_bytes = comp_elems * per_elt + (0 if cfg.dtype == "f32" or cfg.batched else
                                          (cfg.numel - comp_elems) * 6)
     step_frac = algo_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
 
@@ -237,6 +257,8 @@ def main() -> int:
         "data": "synthetic (seeded low-rank + noise gradients, model-shaped views)",
         "config": {"workload": cfg.name, "bucket_bytes": bucket_bytes,
                    "views": len(views), "compressed_elements": comp_elems,
+                   "variant": ("batched: one %d x %d padded matrix" % (side, side)
+                               if cfg.batched else "per-layer"),
                    "matrix_approximation_rank": cfg.hparams["matrix_approximation_rank"],
                    "step_hbm_roofline_frac": round(step_frac, 4),
                    "measured_copy_GBps": round(copy_gbs, 1),

@@ -141,6 +141,44 @@ POWERSGD_API powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_
                                          float inv_loss_scale, int32_t* found_inf_dev,
                                          void* stream);
 
+/*
+ * Side of the square matrix the batched variant views a bucket of `numel` elements
+ * as: the smallest s with s * s >= numel (0 for numel <= 0). Pure host function.
+ */
+POWERSGD_API int64_t powersgd_batched_side(int64_t numel);
+
+/*
+ * batched_powerSGD_hook on one rank ("DDP Communication Hooks -- PyTorch 1.11.0",
+ * section "PowerSGD Hooks", batched_powerSGD_hook steps 1 to 9): the whole bucket,
+ * zero-padded, is viewed as one s x s row-major matrix M (s = powersgd_batched_side);
+ * P = M Q, Gram-Schmidt with epsilon on P, Q = M^T P, M_hat = P Q^T, and the first
+ * numel elements of M_hat are the new bucket. Error feedback and warm start follow
+ * the state's hyperparameters as in powersgd_compress_bucket, with the error memory
+ * covering all s * s entries (the padding of the gradient is zero at every call).
+ * There is no rate test; the rank used is min(matrix_approximation_rank, s).
+ *
+ *   bucket        device pointer to `capacity` elements of `dtype`, caller-owned; the
+ *                 first numel are the gradients. The call writes zeros to elements
+ *                 [numel, s * s) before use and leaves M_hat's padding there, so the
+ *                 buffer doubles as the padded matrix (no copy); callers keep only the
+ *                 first numel elements (step 9, truncation).
+ *   capacity      elements available at `bucket`; must be >= s * s.
+ *   bucket_index, is_last, dtype, inv_loss_scale, found_inf_dev, stream: as for
+ *                 powersgd_compress_bucket. A bucket_index memorized by the per-layer
+ *                 call (or with another numel) is a layout change.
+ *
+ * Statistics count numel elements in and 2 * s * rank communicated per call.
+ * Errors: INVALID_ARG (NULL state, NULL bucket with numel > 0, numel < 0, capacity
+ * below s * s, F16 without found_inf_dev, unknown dtype), UNSUPPORTED (s above
+ * 2^31 - 1), LAYOUT_CHANGED, OOM, HIP; all returned before anything is enqueued.
+ */
+POWERSGD_API powersgd_status powersgd_compress_bucket_batched(powersgd_state* st,
+                                                 int64_t bucket_index, int32_t is_last,
+                                                 void* bucket, powersgd_dtype dtype,
+                                                 int64_t numel, int64_t capacity,
+                                                 float inv_loss_scale, int32_t* found_inf_dev,
+                                                 void* stream);
+
 /* Static text for a status code. */
 POWERSGD_API const char* powersgd_status_string(powersgd_status s);
 

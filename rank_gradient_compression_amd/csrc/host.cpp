@@ -101,7 +101,8 @@ struct ViewKey {
 
 // Everything derived from one bucket layout, plus the memory the method keeps for it.
 struct BucketPlan {
-  int64_t numel = 0;
+  int64_t numel = 0;      // bucket length (batched: the logical length, before padding)
+  bool batched = false;   // the whole bucket viewed as one padded square matrix
   std::vector<ViewKey> views;
   std::vector<uint8_t> decision;        // per view: 1 = compressed
   std::vector<int32_t> view_tensor;     // per view: tensor index or -1
@@ -295,9 +296,10 @@ int64_t view_numel(const ViewKey& k) {
 }
 
 // Classification, rate decisions and work tables for one layout (host only).
-powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
+powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batched,
                            std::vector<ViewKey>&& views, BucketPlan& pl) {
   pl.numel = numel;
+  pl.batched = batched;
   pl.views = std::move(views);
   const size_t nv = pl.views.size();
   pl.decision.assign(nv, 0);
@@ -315,7 +317,8 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
       const int64_t n = k.shape[0];
       const int64_t m = n > 0 ? size / n : 0;
       const int64_t rank = std::min<int64_t>(hp.matrix_approximation_rank, std::min(n, m));
-      comp = should_compress(n, m, rank, hp.min_compression_rate);
+      // the batched variant compresses its one square matrix without a rate test
+      comp = batched ? (n > 0 && m > 0) : should_compress(n, m, rank, hp.min_compression_rate);
       if (comp) {
         if (n > INT32_MAX || m > INT32_MAX)
           return fail(POWERSGD_ERR_UNSUPPORTED, "matrix dimension above 2^31 - 1");
@@ -336,6 +339,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel,
     }
     add_flat(pl.flat_all, k.offset, size);
   }
+  if (batched) pl.all_elems = numel;  // statistics count the bucket, not its padding
   pl.R = pow2_ceil(max_rank);
   const int R = pl.R;
 
@@ -521,8 +525,21 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   return POWERSGD_OK;
 }
 
-bool same_layout(const BucketPlan& pl, int64_t numel, const std::vector<ViewKey>& views) {
-  return pl.numel == numel && pl.views == views;
+bool same_layout(const BucketPlan& pl, int64_t numel, bool batched,
+                 const std::vector<ViewKey>& views) {
+  return pl.numel == numel && pl.batched == batched && pl.views == views;
+}
+
+// Side of the square matrix the batched variant views a bucket of `numel` elements as:
+// the smallest s with s * s >= numel.
+int64_t batched_side(int64_t numel) {
+  if (numel <= 0) return 0;
+  using u128 = unsigned __int128;
+  const u128 n = static_cast<u128>(numel);
+  int64_t s = static_cast<int64_t>(std::sqrt(static_cast<double>(numel)));
+  while (s > 0 && static_cast<u128>(s) * static_cast<u128>(s) >= n) --s;
+  while (static_cast<u128>(s) * static_cast<u128>(s) < n) ++s;
+  return s;
 }
 
 // Algorithmic bytes of each pass per compressed element (minimum traffic).
@@ -619,28 +636,15 @@ void powersgd_state_destroy(powersgd_state* st) {
   delete st;
 }
 
-powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_index,
-                                         int32_t is_last, void* bucket,
-                                         powersgd_dtype dtype, int64_t numel,
-                                         const powersgd_view* views, int32_t nviews,
-                                         float inv_loss_scale, int32_t* found_inf_dev,
-                                         void* stream) {
-  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
-  if (numel < 0) return fail(POWERSGD_ERR_INVALID_ARG, "numel < 0");
-  if (nviews < 0) return fail(POWERSGD_ERR_INVALID_ARG, "nviews < 0");
-  if (nviews > 0 && !views) return fail(POWERSGD_ERR_INVALID_ARG, "views is NULL");
-  if (numel > 0 && !bucket) return fail(POWERSGD_ERR_INVALID_ARG, "bucket is NULL");
-  if (dtype != POWERSGD_F32 && dtype != POWERSGD_F16)
-    return fail(POWERSGD_ERR_INVALID_ARG, "unknown dtype");
-  const bool f16 = dtype == POWERSGD_F16;
-  if (f16 && !found_inf_dev)
-    return fail(POWERSGD_ERR_INVALID_ARG, "fp16 buckets need found_inf_dev");
-  if (f16 && !std::isfinite(inv_loss_scale))
-    return fail(POWERSGD_ERR_INVALID_ARG, "inv_loss_scale must be finite");
-  std::vector<ViewKey> keys;
-  powersgd_status vs = validate_views(views, nviews, numel, keys);
-  if (vs != POWERSGD_OK) return vs;
+namespace {
 
+// One hook call on a validated bucket layout: the per-layer variant (`keys` = the
+// views) or the batched one (`keys` = the one padded square view, `numel` = the
+// bucket's own length).
+powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_last,
+                         void* bucket, bool f16, int64_t numel, bool batched,
+                         std::vector<ViewKey>& keys, float inv_loss_scale,
+                         int32_t* found_inf_dev, void* stream) {
   HipDeviceGuard guard(st->device);
   if (!guard.ok) return fail(POWERSGD_ERR_HIP, "hipSetDevice failed");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -654,11 +658,15 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
   if (st->iteration < hp.start_powerSGD_iter) {
     if (f16) {
       auto& slot = st->passthrough[bucket_index];
-      if (!slot || !same_layout(*slot, numel, keys)) {
+      if (!slot || !same_layout(*slot, numel, batched, keys)) {
         auto pl = std::make_unique<BucketPlan>();
         pl->numel = numel;
+        pl->batched = batched;
         pl->views = keys;
-        for (const ViewKey& k : pl->views) add_flat(pl->flat_all, k.offset, view_numel(k));
+        if (batched)
+          add_flat(pl->flat_all, 0, numel);
+        else
+          for (const ViewKey& k : pl->views) add_flat(pl->flat_all, k.offset, view_numel(k));
         powersgd_status u = upload(pl->flat_all, &pl->d_flat_all, s);
         if (u != POWERSGD_OK) return u;
         hipError_t e = hipStreamSynchronize(s);
@@ -686,7 +694,7 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
 
   // Plan lookup; a memorized bucket must keep its layout.
   auto it = st->buckets.find(bucket_index);
-  if (it != st->buckets.end() && !same_layout(*it->second, numel, keys)) {
+  if (it != st->buckets.end() && !same_layout(*it->second, numel, batched, keys)) {
     if (ef || hp.warm_start)
       return fail(POWERSGD_ERR_LAYOUT_CHANGED,
                   "bucket " + std::to_string(bucket_index) + " was called with other views");
@@ -695,7 +703,7 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
   }
   if (it == st->buckets.end()) {
     auto pl = std::make_unique<BucketPlan>();
-    powersgd_status b = build_plan(hp, numel, std::move(keys), *pl);
+    powersgd_status b = build_plan(hp, numel, batched, std::move(keys), *pl);
     if (b != POWERSGD_OK) return b;
     b = allocate_plan(*pl, ef, s);
     if (b != POWERSGD_OK) return b;
@@ -734,6 +742,15 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
                            s);
       });
       if (r != POWERSGD_OK) return r;
+    }
+  }
+  // Batched variant, step 1: the square matrix's padding past the bucket is zero.
+  if (batched && nt > 0) {
+    const int64_t side = pl.view_n[0];
+    const int64_t pad = side * side - numel;
+    if (pad > 0) {
+      hipError_t e = launch_fill_zero(bucket, f16, numel, pad, s);
+      if (e != hipSuccess) return hip_fail(e, "padding fill");
     }
   }
   // Pass 1 (+ fp16 inf check of every view).
@@ -843,6 +860,63 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
     st->iteration += 1;
   }
   return POWERSGD_OK;
+}
+
+
+}  // namespace
+
+powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_index,
+                                         int32_t is_last, void* bucket,
+                                         powersgd_dtype dtype, int64_t numel,
+                                         const powersgd_view* views, int32_t nviews,
+                                         float inv_loss_scale, int32_t* found_inf_dev,
+                                         void* stream) {
+  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
+  if (numel < 0) return fail(POWERSGD_ERR_INVALID_ARG, "numel < 0");
+  if (nviews < 0) return fail(POWERSGD_ERR_INVALID_ARG, "nviews < 0");
+  if (nviews > 0 && !views) return fail(POWERSGD_ERR_INVALID_ARG, "views is NULL");
+  if (numel > 0 && !bucket) return fail(POWERSGD_ERR_INVALID_ARG, "bucket is NULL");
+  if (dtype != POWERSGD_F32 && dtype != POWERSGD_F16)
+    return fail(POWERSGD_ERR_INVALID_ARG, "unknown dtype");
+  const bool f16 = dtype == POWERSGD_F16;
+  if (f16 && !found_inf_dev)
+    return fail(POWERSGD_ERR_INVALID_ARG, "fp16 buckets need found_inf_dev");
+  if (f16 && !std::isfinite(inv_loss_scale))
+    return fail(POWERSGD_ERR_INVALID_ARG, "inv_loss_scale must be finite");
+  std::vector<ViewKey> keys;
+  powersgd_status vs = validate_views(views, nviews, numel, keys);
+  if (vs != POWERSGD_OK) return vs;
+  return run_call(st, bucket_index, is_last, bucket, f16, numel, false, keys, inv_loss_scale,
+                  found_inf_dev, stream);
+}
+
+int64_t powersgd_batched_side(int64_t numel) { return batched_side(numel); }
+
+powersgd_status powersgd_compress_bucket_batched(powersgd_state* st, int64_t bucket_index,
+                                                 int32_t is_last, void* bucket,
+                                                 powersgd_dtype dtype, int64_t numel,
+                                                 int64_t capacity, float inv_loss_scale,
+                                                 int32_t* found_inf_dev, void* stream) {
+  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
+  if (numel < 0) return fail(POWERSGD_ERR_INVALID_ARG, "numel < 0");
+  if (numel > 0 && !bucket) return fail(POWERSGD_ERR_INVALID_ARG, "bucket is NULL");
+  if (dtype != POWERSGD_F32 && dtype != POWERSGD_F16)
+    return fail(POWERSGD_ERR_INVALID_ARG, "unknown dtype");
+  const bool f16 = dtype == POWERSGD_F16;
+  if (f16 && !found_inf_dev)
+    return fail(POWERSGD_ERR_INVALID_ARG, "fp16 buckets need found_inf_dev");
+  if (f16 && !std::isfinite(inv_loss_scale))
+    return fail(POWERSGD_ERR_INVALID_ARG, "inv_loss_scale must be finite");
+  const int64_t side = batched_side(numel);
+  if (side > INT32_MAX) return fail(POWERSGD_ERR_UNSUPPORTED, "bucket too large for the batched view");
+  if (capacity < side * side)
+    return fail(POWERSGD_ERR_INVALID_ARG,
+                "capacity " + std::to_string(capacity) + " is below the padded square of " +
+                    std::to_string(side * side) + " elements");
+  std::vector<ViewKey> keys;
+  if (numel > 0) keys.push_back(ViewKey{0, {side, side}});
+  return run_call(st, bucket_index, is_last, bucket, f16, numel, true, keys, inv_loss_scale,
+                  found_inf_dev, stream);
 }
 
 powersgd_status powersgd_classify_view(const powersgd_hparams* hp, const powersgd_view* view,

@@ -161,6 +161,9 @@ hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, int max_rows, floa
 hipError_t launch_qinit(int R, const QInitJob* jobs, int njobs, int64_t max_count,
                         float* Q, uint64_t seed, uint64_t bucket_key, uint64_t epoch,
                         hipStream_t s);
+// Zeroes elements [start, start + count) of a fp32 or fp16 buffer (a fill kernel, so
+// the call can be captured in a graph).
+hipError_t launch_fill_zero(void* base, bool f16, int64_t start, int64_t count, hipStream_t s);
 hipError_t launch_unscale_only(const FlatTile* ftiles, int nftiles, void* bucket,
                                float inv_scale, int32_t* found_inf, bool check,
                                hipStream_t s);

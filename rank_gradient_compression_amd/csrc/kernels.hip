@@ -216,14 +216,47 @@ __device__ __forceinline__ void load_f4(const float* p, float (&x)[4]) {
   x[3] = w.w;
 }
 
-// Branch-free loads of 4 consecutive values starting at element `idx` of a row that
-// has `valid` >= 1 elements left from there (the row index is clamped by the caller).
-// VEC: one aligned vector load. Otherwise four scalar loads at offsets clamped into
-// the row; the values past its end read as zero (and are never flagged as bad).
-template <bool VEC>
+// How the vector-rank passes access a matrix's rows (chosen per matrix):
+//   kLdAligned    rows 16-byte aligned (m % 4 == 0): one aligned 16-byte load per lane.
+//   kLdUnaligned  rows only 4-byte aligned (2-byte for fp16), m >= 4: one unaligned
+//                 16-byte (fp16: 8-byte) load per lane, which gfx950 performs in one
+//                 instruction; a row's last, partial group is loaded ending at column
+//                 m - 1 and moved into place with selects, so no load needs a branch.
+//   kLdScalar     m < 4: four scalar loads at offsets clamped into the row.
+constexpr int kLdScalar = 0;
+constexpr int kLdUnaligned = 1;
+constexpr int kLdAligned = 2;
+
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+typedef unsigned int u32x2u __attribute__((ext_vector_type(2), aligned(2)));
+
+// w[shift + a] for a = 0..3, zero past w[3]: the group loaded `shift` (0..3) elements
+// early. Two conditional shifts (by 1, then by 2) of plain two-way selects.
+__device__ __forceinline__ void shift_down4(const float (&w)[4], int shift, float (&x)[4]) {
+  const bool s1 = (shift & 1) != 0;
+  const bool s2 = (shift & 2) != 0;
+  const float a0 = s1 ? w[1] : w[0];
+  const float a1 = s1 ? w[2] : w[1];
+  const float a2 = s1 ? w[3] : w[2];
+  const float a3 = s1 ? 0.f : w[3];
+  x[0] = s2 ? a2 : a0;
+  x[1] = s2 ? a3 : a1;
+  x[2] = s2 ? 0.f : a2;
+  x[3] = s2 ? 0.f : a3;
+}
+
+// Branch-free loads of 4 consecutive values starting at element `p` of a row that has
+// `valid` >= 1 elements left from there (the row index is clamped by the caller); the
+// values past the row's end read as zero.
+template <int LD>
 __device__ __forceinline__ void ld_f32x4(const float* p, int valid, float (&x)[4]) {
-  if constexpr (VEC) {
+  if constexpr (LD == kLdAligned) {
     load_f4(p, x);
+  } else if constexpr (LD == kLdUnaligned) {
+    const int shift = valid >= 4 ? 0 : 4 - valid;
+    const f32x4u v = *reinterpret_cast<const f32x4u*>(p - shift);
+    const float w[4] = {v[0], v[1], v[2], v[3]};
+    shift_down4(w, shift, x);
   } else {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -233,11 +266,26 @@ __device__ __forceinline__ void ld_f32x4(const float* p, int valid, float (&x)[4
   }
 }
 
-template <bool F16, bool VEC>
+// Gradient values (fp16: unscaled; `raw_bad` = one of the values in the row is inf/NaN).
+template <bool F16, int LD>
 __device__ __forceinline__ void ld_grad4(const void* bucket, int64_t idx, int valid,
                                          float inv_scale, float (&x)[4], bool& raw_bad) {
-  if constexpr (VEC) {
+  if constexpr (LD == kLdAligned) {
     load_grad4_vec<F16>(bucket, idx, inv_scale, x, raw_bad);
+  } else if constexpr (F16 && LD == kLdUnaligned) {
+    const int shift = valid >= 4 ? 0 : 4 - valid;
+    const u32x2u v =
+        *reinterpret_cast<const u32x2u*>(static_cast<const uint16_t*>(bucket) + idx - shift);
+    const uint16_t raw[4] = {static_cast<uint16_t>(v[0] & 0xFFFFu), static_cast<uint16_t>(v[0] >> 16),
+                             static_cast<uint16_t>(v[1] & 0xFFFFu), static_cast<uint16_t>(v[1] >> 16)};
+    float w[4];
+    raw_bad = false;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      raw_bad |= (a >= shift) && half_bits_not_finite(raw[a]);  // the row's own values
+      w[a] = half_bits_to_float(raw[a]) * inv_scale;
+    }
+    shift_down4(w, shift, x);
   } else if constexpr (F16) {
     const uint16_t* h = static_cast<const uint16_t*>(bucket) + idx;
     raw_bad = false;
@@ -249,35 +297,76 @@ __device__ __forceinline__ void ld_grad4(const void* bucket, int64_t idx, int va
       x[a] = in ? half_bits_to_float(v) * inv_scale : 0.f;
     }
   } else {
-    ld_f32x4<false>(static_cast<const float*>(bucket) + idx, valid, x);
+    ld_f32x4<LD>(static_cast<const float*>(bucket) + idx, valid, x);
     raw_bad = false;
   }
 }
 
-template <bool VEC>
+template <int LD>
 __device__ __forceinline__ void st_f32x4(float* p, int valid, const float (&x)[4]) {
-  store_f32x4(p, VEC, valid, x);
+  if constexpr (LD == kLdAligned) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  } else if constexpr (LD == kLdUnaligned) {
+    if (valid >= 4) {
+      *reinterpret_cast<f32x4u*>(p) = f32x4u{x[0], x[1], x[2], x[3]};
+    } else {
+#pragma unroll
+      for (int a = 0; a < 3; ++a)
+        if (a < valid) p[a] = x[a];
+    }
+  } else {
+    store_f32x4(p, false, valid, x);
+  }
+}
+
+template <int LD>
+__device__ __forceinline__ void st_f16x4(uint16_t* h, int valid, const float (&x)[4]) {
+  if constexpr (LD == kLdUnaligned) {
+    if (valid >= 4) {
+      uint16_t o[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) o[a] = __half_as_ushort(__float2half_rn(x[a]));
+      *reinterpret_cast<u32x2u*>(h) =
+          u32x2u{static_cast<uint32_t>(o[0]) | (static_cast<uint32_t>(o[1]) << 16),
+                 static_cast<uint32_t>(o[2]) | (static_cast<uint32_t>(o[3]) << 16)};
+      return;
+    }
+  }
+  store_f16x4(h, LD == kLdAligned, valid, x);
 }
 
 // Q rows c..c+3 (R values each) of a row-major block; rows at or past m read as zero.
-template <int R, bool VEC>
+template <int R, int LD>
 __device__ __forceinline__ void ld_q4(const float* __restrict__ Q, int c, int valid,
                                       float (&q)[4][R]) {
-  if constexpr (VEC) {
-    const float4* p = reinterpret_cast<const float4*>(Q + static_cast<int64_t>(c) * R);
+  if constexpr (LD != kLdScalar) {
+    // kLdUnaligned: the four rows ending at row m - 1 when fewer than four are left
+    const int shift = (LD == kLdAligned || valid >= 4) ? 0 : 4 - valid;
+    const float* src = Q + static_cast<int64_t>(c - shift) * R;
     float f[4 * R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const float4 w = p[i];
-      f[4 * i + 0] = w.x;
-      f[4 * i + 1] = w.y;
-      f[4 * i + 2] = w.z;
-      f[4 * i + 3] = w.w;
+      float w[4];
+      if constexpr (LD == kLdAligned || R % 4 == 0) {
+        load_f4(src + 4 * i, w);
+      } else {
+        const f32x4u v = *reinterpret_cast<const f32x4u*>(src + 4 * i);
+        w[0] = v[0];
+        w[1] = v[1];
+        w[2] = v[2];
+        w[3] = v[3];
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) f[4 * i + a] = w[a];
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int k = 0; k < R; ++k) {
+      const float w[4] = {f[k], f[R + k], f[2 * R + k], f[3 * R + k]};
+      float x[4];
+      shift_down4(w, shift, x);
 #pragma unroll
-      for (int k = 0; k < R; ++k) q[a][k] = f[a * R + k];
+      for (int a = 0; a < 4; ++a) q[a][k] = x[a];
+    }
   } else {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -428,10 +517,10 @@ constexpr int pass1_ng() { return R <= kMaxFusedGramRank ? gram_size<R>() : 1; }
 // P = M' Q over one row block. Threads of a row slot sweep the row's columns,
 // U rows per thread are loaded before any is used, and the slot's partial dot
 // products are summed with shuffles (and through LDS when a slot spans wavefronts).
-// VEC: rows are 16-byte aligned and m % 4 == 0. The rows of a slot are clamped into
-// the row block, so every load of an iteration is issued before any is used; the
-// results of clamped duplicate rows are discarded.
-template <int R, int U, bool F16, bool EF, bool VEC>
+// LD: how the matrix's rows are loaded (kLdAligned, kLdUnaligned, kLdScalar). The rows
+// of a slot are clamped into the row block, so every load of an iteration is issued
+// before any is used; the results of clamped duplicate rows are discarded.
+template <int R, int U, bool F16, bool EF, int LD>
 __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDesc& d,
                                            const Tile& t, float* red,
                                            double (*gred)[pass1_ng<R>()]) {
@@ -472,24 +561,24 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
     for (int c = g * 4; c < m; c += sweep) {
       const int valid = m - c;
       float q[4][R];
-      ld_q4<R, VEC>(Qt, c, valid, q);
+      ld_q4<R, LD>(Qt, c, valid, q);
       float x[U][4];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         bool rb;
-        ld_grad4<F16, VEC>(args.bucket, d.boff + rbase[u] + c, valid, args.inv_scale, x[u], rb);
+        ld_grad4<F16, LD>(args.bucket, d.boff + rbase[u] + c, valid, args.inv_scale, x[u], rb);
         if constexpr (F16) bad |= (rok[u] && rb) ? 1 : 0;
       }
       if constexpr (EF) {
         float e[U][4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) ld_f32x4<VEC>(Et + rbase[u] + c, valid, e[u]);
+        for (int u = 0; u < U; ++u) ld_f32x4<LD>(Et + rbase[u] + c, valid, e[u]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
           for (int a = 0; a < 4; ++a) x[u][a] += e[u][a];
           if constexpr (!F16) {
-            if (rok[u]) st_f32x4<VEC>(Mt + rbase[u] + c, valid, x[u]);
+            if (rok[u]) st_f32x4<LD>(Mt + rbase[u] + c, valid, x[u]);
           }
         }
       }
@@ -570,9 +659,11 @@ __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec)
-    pass1_body<R, U, F16, EF, true>(args, d, t, red, gred);
+    pass1_body<R, U, F16, EF, kLdAligned>(args, d, t, red, gred);
+  else if (d.m >= 4)
+    pass1_body<R, U, F16, EF, kLdUnaligned>(args, d, t, red, gred);
   else
-    pass1_body<R, U, F16, EF, false>(args, d, t, red, gred);
+    pass1_body<R, U, F16, EF, kLdScalar>(args, d, t, red, gred);
 }
 
 // ------------------------------------------------------------ orthogonalization
@@ -595,8 +686,8 @@ constexpr int orth_group_size() {
 // Working set of the orthogonalization of one matrix (LDS).
 template <int R>
 struct OrthShared {
-  double G[R][R];  // Gram matrix
-  double T[R][R];  // P <- P T
+  double G[R][R + 1];  // Gram matrix (rows padded: lane j reads row j without bank conflicts)
+  double T[R][R];      // P <- P T
   double C[R];     // coefficients of the column being normalized
   double W[R];     // G q_i in coefficients
 };
@@ -738,15 +829,15 @@ __device__ __forceinline__ void orth_transform(int rank, double eps, OrthShared<
 
 // M' at element `off` of a matrix (fp32 with error feedback: the bucket already holds
 // M', written by pass 1; fp16: unscaled gradient plus E).
-template <bool F16, bool EF, bool VEC>
+template <bool F16, bool EF, int LD>
 __device__ __forceinline__ void ld_mprime4(const void* bucket, const float* Et, int64_t boff,
                                            int64_t off, int valid, float inv_scale,
                                            float (&x)[4]) {
   bool rb;
-  ld_grad4<F16, VEC>(bucket, boff + off, valid, inv_scale, x, rb);
+  ld_grad4<F16, LD>(bucket, boff + off, valid, inv_scale, x, rb);
   if constexpr (F16 && EF) {
     float e[4];
-    ld_f32x4<VEC>(Et + off, valid, e);
+    ld_f32x4<LD>(Et + off, valid, e);
 #pragma unroll
     for (int a = 0; a < 4; ++a) x[a] += e[a];
   }
@@ -798,7 +889,7 @@ __device__ __forceinline__ void pass2_orth_rows(const Pass2Args& args, const Ten
 // first rows of M' are requested during the orthogonalization prologue, after its own
 // loads (waits count loads in issue order) and before its barriers, which wait on
 // LDS only, so their latency overlaps it.
-template <int R, int U, bool F16, bool EF, bool VEC, bool WIDE>
+template <int R, int U, bool F16, bool EF, int LD, bool WIDE>
 __device__ __forceinline__ void pass2_body(const Pass2Args& args, const TensorDesc& d,
                                            const Tile& t, float* red, OrthShared<R>& sh,
                                            float* sP) {
@@ -812,14 +903,14 @@ __device__ __forceinline__ void pass2_body(const Pass2Args& args, const TensorDe
   const float* __restrict__ Et = args.E + d.eoff;
   // lanes past the last column load (and then ignore) an in-range group, so the first
   // loads need no branch and the wait counts stay exact
-  const int cc = L.col_ok ? L.c : (VEC ? d.m - 4 : d.m - 1);
+  const int cc = L.col_ok ? L.c : (LD == kLdScalar ? d.m - 1 : d.m - 4);
   const int vv = L.col_ok ? L.valid : 1;
   float x[U][4];
   auto load_rows = [&](int rw) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int rowc = min(rw + u * stride + L.slot, r1 - 1);
-      ld_mprime4<F16, EF, VEC>(args.bucket, Et, d.boff, static_cast<int64_t>(rowc) * d.m + cc,
+      ld_mprime4<F16, EF, LD>(args.bucket, Et, d.boff, static_cast<int64_t>(rowc) * d.m + cc,
                                vv, args.inv_scale, x[u]);
     }
   };
@@ -906,11 +997,13 @@ __global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec && d.lpr == 64)
-    pass2_body<R, U, F16, EF, true, true>(args, d, t, red, sh, sP);
+    pass2_body<R, U, F16, EF, kLdAligned, true>(args, d, t, red, sh, sP);
   else if (d.vec)
-    pass2_body<R, U, F16, EF, true, false>(args, d, t, red, sh, sP);
+    pass2_body<R, U, F16, EF, kLdAligned, false>(args, d, t, red, sh, sP);
+  else if (d.m >= 4)
+    pass2_body<R, U, F16, EF, kLdUnaligned, false>(args, d, t, red, sh, sP);
   else
-    pass2_body<R, U, F16, EF, false, false>(args, d, t, red, sh, sP);
+    pass2_body<R, U, F16, EF, kLdScalar, false>(args, d, t, red, sh, sP);
 }
 
 // Q of the tensors with several row blocks: the partial slots of a column block summed
@@ -1060,7 +1153,7 @@ __device__ __forceinline__ void pass3_q_from_partials(const Pass3Args& args, con
 
 // M_hat = P Q^T into the bucket and E = M' - M_hat over one tile. All loads of an
 // iteration come from rows clamped into the tile; stores are kept to real rows.
-template <int R, int U, bool F16, bool EF, bool VEC, bool WIDE>
+template <int R, int U, bool F16, bool EF, int LD, bool WIDE>
 __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDesc& d,
                                            const Tile& t, float* qred) {
   const int lane = threadIdx.x & 63;
@@ -1084,7 +1177,7 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int rowc = min(rw + u * stride + L.slot, r1 - 1);
-      ld_mprime4<F16, EF, VEC>(args.bucket, Et, d.boff, static_cast<int64_t>(rowc) * d.m + L.c,
+      ld_mprime4<F16, EF, LD>(args.bucket, Et, d.boff, static_cast<int64_t>(rowc) * d.m + L.c,
                                L.valid, args.inv_scale, x[u]);
       if constexpr (WIDE)
         load_p_row_uniform<R>(Pt, __builtin_amdgcn_readfirstlane(rowc), p[u]);
@@ -1105,14 +1198,14 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
         mh[a] = s;
       }
       if constexpr (F16)
-        store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, VEC, L.valid, mh);
+        st_f16x4<LD>(static_cast<uint16_t*>(args.bucket) + d.boff + off, L.valid, mh);
       else
-        st_f32x4<VEC>(static_cast<float*>(args.bucket) + d.boff + off, L.valid, mh);
+        st_f32x4<LD>(static_cast<float*>(args.bucket) + d.boff + off, L.valid, mh);
       if constexpr (EF) {
         float e[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) e[a] = x[u][a] - mh[a];
-        st_f32x4<VEC>(Et + off, L.valid, e);
+        st_f32x4<LD>(Et + off, L.valid, e);
       }
     }
   }
@@ -1130,11 +1223,13 @@ __global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec && d.lpr == 64)
-    pass3_body<R, U, F16, EF, true, true>(args, d, t, qred);
+    pass3_body<R, U, F16, EF, kLdAligned, true>(args, d, t, qred);
   else if (d.vec)
-    pass3_body<R, U, F16, EF, true, false>(args, d, t, qred);
+    pass3_body<R, U, F16, EF, kLdAligned, false>(args, d, t, qred);
+  else if (d.m >= 4)
+    pass3_body<R, U, F16, EF, kLdUnaligned, false>(args, d, t, qred);
   else
-    pass3_body<R, U, F16, EF, false, false>(args, d, t, qred);
+    pass3_body<R, U, F16, EF, kLdScalar, false>(args, d, t, qred);
 }
 
 // ------------------------------------------------- matrix-core passes (R = 16, 32)
@@ -1446,7 +1541,7 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
         }
       } else {
         if (row < r1 && col_ok) {
-          ld_mprime4<F16, EF, false>(args.bucket, Et, d.boff, static_cast<int64_t>(row) * m + col,
+          ld_mprime4<F16, EF, kLdScalar>(args.bucket, Et, d.boff, static_cast<int64_t>(row) * m + col,
                                      m - col, args.inv_scale, x[u]);
         } else {
 #pragma unroll
@@ -1569,7 +1664,7 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
           }
         } else {
           if (row < r1 && col < m)
-            ld_mprime4<F16, EF, false>(args.bucket, Et, d.boff, static_cast<int64_t>(row) * m + col,
+            ld_mprime4<F16, EF, kLdScalar>(args.bucket, Et, d.boff, static_cast<int64_t>(row) * m + col,
                                        m - col, args.inv_scale, x[ur][g]);
         }
       }
@@ -1650,7 +1745,7 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
         const int row = min(rr + RW * wave + i, r1 - 1);
-        ld_mprime4<F16, EF, true>(args.bucket, Et, d.boff, static_cast<int64_t>(row) * m + crc, 4,
+        ld_mprime4<F16, EF, kLdAligned>(args.bucket, Et, d.boff, static_cast<int64_t>(row) * m + crc, 4,
                                   args.inv_scale, x[i]);
       }
     }
@@ -1879,6 +1974,16 @@ __global__ void __launch_bounds__(256)
   f16_unscale_range(ft[blockIdx.x], bucket, inv_scale);
 }
 
+__global__ void __launch_bounds__(256)
+    k_fill_zero(void* base, int elem_bytes, int64_t start, int64_t count) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < count; i += gridDim.x * 256ll) {
+    if (elem_bytes == 2)
+      static_cast<uint16_t*>(base)[start + i] = 0;
+    else
+      static_cast<float*>(base)[start + i] = 0.f;
+  }
+}
+
 // ------------------------------------------------------------------ dispatch
 
 // Rows loaded per lane before use, by rank (register budget).
@@ -2007,6 +2112,14 @@ hipError_t launch_qinit(int R, const QInitJob* jobs, int njobs, int64_t max_coun
   const dim3 grid(static_cast<unsigned>(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks)),
                   static_cast<unsigned>(njobs));
   k_qinit<<<grid, 256, 0, s>>>(jobs, Q, R, seed, bucket_key, epoch);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* base, bool f16, int64_t start, int64_t count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  const int64_t blocks = (count + 255) / 256;
+  k_fill_zero<<<dim3(static_cast<unsigned>(blocks < 1024 ? blocks : 1024)), 256, 0, s>>>(
+      base, f16 ? 2 : 4, start, count);
   return hipGetLastError();
 }
 

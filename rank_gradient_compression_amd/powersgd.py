@@ -33,6 +33,7 @@ EXPORTED = (
     "powersgd_get_decisions", "powersgd_get_view_info", "powersgd_copy_factors",
     "powersgd_copy_error", "powersgd_get_stats", "powersgd_set_timing",
     "powersgd_get_kernel_times", "powersgd_kernel_name", "powersgd_classify_view",
+    "powersgd_batched_side", "powersgd_compress_bucket_batched",
 )
 
 
@@ -87,6 +88,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "powersgd_state_destroy": (None, [P]),
         "powersgd_compress_bucket": (i32, [P, i64, i32, P, i32, i64,
                                            ctypes.POINTER(powersgd_view), i32, f32, P, P]),
+        "powersgd_batched_side": (i64, [i64]),
+        "powersgd_compress_bucket_batched": (i32, [P, i64, i32, P, i32, i64, i64, f32, P, P]),
         "powersgd_status_string": (ctypes.c_char_p, [i32]),
         "powersgd_last_error": (ctypes.c_char_p, []),
         "powersgd_get_decisions": (i32, [P, i64, ctypes.POINTER(ctypes.c_uint8), i32]),
@@ -166,6 +169,21 @@ def powersgd_compress_bucket(state, bucket_index: int, is_last: bool, bucket_ptr
     _check(load_library().powersgd_compress_bucket(
         state, int(bucket_index), int(bool(is_last)), ctypes.c_void_p(bucket_ptr), int(dtype),
         int(numel), arr, len(views), float(inv_loss_scale),
+        ctypes.c_void_p(found_inf_ptr) if found_inf_ptr else None,
+        ctypes.c_void_p(stream) if stream else None))
+
+
+def powersgd_batched_side(numel: int) -> int:
+    return int(load_library().powersgd_batched_side(int(numel)))
+
+
+def powersgd_compress_bucket_batched(state, bucket_index: int, is_last: bool, bucket_ptr: int,
+                                     dtype: int, numel: int, capacity: int,
+                                     inv_loss_scale: float, found_inf_ptr: Optional[int],
+                                     stream: Optional[int]) -> None:
+    _check(load_library().powersgd_compress_bucket_batched(
+        state, int(bucket_index), int(bool(is_last)), ctypes.c_void_p(bucket_ptr), int(dtype),
+        int(numel), int(capacity), float(inv_loss_scale),
         ctypes.c_void_p(found_inf_ptr) if found_inf_ptr else None,
         ctypes.c_void_p(stream) if stream else None))
 
@@ -267,9 +285,8 @@ class PowerSGDState:
             stream = torch.cuda.current_stream()
         return int(stream.cuda_stream)
 
-    def compress_bucket(self, bucket, views: Sequence[Tuple[int, Sequence[int]]],
-                        bucket_index: int = 0, is_last: bool = True,
-                        inv_loss_scale: float = 1.0, found_inf=None, stream=None) -> None:
+    @staticmethod
+    def _bucket_args(bucket, found_inf):
         import torch
         if not bucket.is_cuda or not bucket.is_contiguous() or bucket.dim() != 1:
             raise ValueError("bucket must be a contiguous 1-D device tensor")
@@ -284,9 +301,29 @@ class PowerSGDState:
             if found_inf.dtype != torch.int32 or not found_inf.is_cuda:
                 raise TypeError("found_inf must be a device int32 tensor")
             fi = found_inf.data_ptr()
+        return dtype, fi
+
+    def compress_bucket(self, bucket, views: Sequence[Tuple[int, Sequence[int]]],
+                        bucket_index: int = 0, is_last: bool = True,
+                        inv_loss_scale: float = 1.0, found_inf=None, stream=None) -> None:
+        dtype, fi = self._bucket_args(bucket, found_inf)
         powersgd_compress_bucket(self._state, bucket_index, is_last, bucket.data_ptr(), dtype,
                                  bucket.numel(), list(views), inv_loss_scale, fi,
                                  self._stream_handle(stream))
+
+    def compress_bucket_batched(self, buffer, numel: Optional[int] = None,
+                                bucket_index: int = 0, is_last: bool = True,
+                                inv_loss_scale: float = 1.0, found_inf=None,
+                                stream=None) -> None:
+        """batched_powerSGD_hook on the first `numel` elements of `buffer` (default: all
+        of it), which must hold at least powersgd_batched_side(numel) ** 2 elements:
+        the buffer is the zero-padded square matrix, and its first numel elements are
+        the result."""
+        dtype, fi = self._bucket_args(buffer, found_inf)
+        n = buffer.numel() if numel is None else int(numel)
+        powersgd_compress_bucket_batched(self._state, bucket_index, is_last, buffer.data_ptr(),
+                                         dtype, n, buffer.numel(), inv_loss_scale, fi,
+                                         self._stream_handle(stream))
 
     def decisions(self, bucket_index: int, nviews: int) -> List[int]:
         return powersgd_get_decisions(self._state, bucket_index, nviews)

@@ -1,4 +1,4 @@
-"""The five benchmark workloads as bucket layouts plus generator parameters.
+"""The benchmark workloads as bucket layouts plus generator parameters.
 
 Each workload is a flat gradient bucket of parameter-shaped views packed
 back to back with no padding, in the order listed, the way a data-parallel
@@ -31,6 +31,7 @@ class WorkloadConfig:
     forced_inf_steps: Tuple[int, ...] = ()
     seed: int = 0
     notes: str = ""
+    batched: bool = False         # the whole bucket as one zero-padded square matrix
 
     def views(self):
         return packed_views(self.shapes)
@@ -118,6 +119,13 @@ CONFIGS: Dict[int, WorkloadConfig] = {
         forced_inf_steps=(10,), seed=1004,
         notes="fp16 value = RNE(G * 2^-10 * S); the 2^-10 keeps |value| below the fp16 "
               "maximum at S = 65536"),
+    5: WorkloadConfig(
+        name="resnet50-bucket-batched-r1", shapes=_resnet50_shapes(),
+        hparams=_hp(matrix_approximation_rank=1), steps=10,
+        spectrum_rank=8, spectrum_power=1.0, seed=1001, batched=True,
+        notes="the ResNet-50 bucket (same values as the per-layer workload) viewed as one "
+              "4315 x 4315 matrix, 4313 padded zeros; rank 1 as the pages recommend for "
+              "this variant"),
 }
 
 
@@ -130,4 +138,4 @@ def shrink_config(cfg: WorkloadConfig, shapes: List[Shape], steps: int = None,
         spectrum_power=cfg.spectrum_power, noise_std=cfg.noise_std, dtype=cfg.dtype,
         amp_prescale=cfg.amp_prescale, loss_scale=cfg.loss_scale,
         inf_probability=cfg.inf_probability, forced_inf_steps=cfg.forced_inf_steps,
-        seed=cfg.seed, notes=cfg.notes)
+        seed=cfg.seed, notes=cfg.notes, batched=cfg.batched)

@@ -9,7 +9,7 @@ import re
 import numpy as np
 import pytest
 
-from oracle import effective_rank, matrix_view, should_compress
+from oracle import batched_side, effective_rank, matrix_view, should_compress
 from rank_gradient_compression_amd import powersgd as api
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -153,6 +153,8 @@ def test_invalid_arguments_are_rejected_before_device_work(lib):
     views = api.make_views([(0, (4, 4))])
     assert lib.powersgd_compress_bucket(None, 0, 1, ctypes.c_void_p(16), 0, 16, views, 1, 1.0,
                                         None, None) == api.POWERSGD_ERR_INVALID_ARG
+    assert lib.powersgd_compress_bucket_batched(None, 0, 1, ctypes.c_void_p(16), 0, 16, 16, 1.0,
+                                                None, None) == api.POWERSGD_ERR_INVALID_ARG
     assert lib.powersgd_get_stats(None, None, None, None) == api.POWERSGD_ERR_INVALID_ARG
     assert lib.powersgd_set_timing(None, 1) == api.POWERSGD_ERR_INVALID_ARG
     assert "NULL" in api.powersgd_last_error()
@@ -170,3 +172,12 @@ def test_classify_rejects_bad_views(lib):
     v = api.make_views([(0, (3, -4))])
     assert lib.powersgd_classify_view(ctypes.byref(hp), v, ctypes.byref(c), None, None,
                                       None) == api.POWERSGD_ERR_INVALID_ARG
+
+
+def test_batched_side_is_bit_exact_with_oracle(lib):
+    """powersgd_batched_side against the oracle's definition (smallest s, s*s >= n)."""
+    ns = list(range(0, 5000)) + [s * s + d for s in (4314, 4315, 46340, 46341, 3037000499)
+                                 for d in (-1, 0, 1)]
+    for n in ns:
+        assert api.powersgd_batched_side(n) == batched_side(n), n
+    assert api.powersgd_batched_side(-5) == 0
