@@ -159,7 +159,8 @@ POWERSGD_API int64_t powersgd_batched_side(int64_t numel);
  *
  *   bucket        device pointer to `capacity` elements of `dtype`, caller-owned; the
  *                 first numel are the gradients. The call writes zeros to elements
- *                 [numel, s * s) before use and leaves M_hat's padding there, so the
+ *                 [numel, s * s) before use (also when an fp16 call is skipped) and
+ *                 leaves M_hat's padding there, so the
  *                 buffer doubles as the padded matrix (no copy); callers keep only the
  *                 first numel elements (step 9, truncation).
  *   capacity      elements available at `bucket`; must be >= s * s.
