@@ -35,6 +35,7 @@ matrix product (numpy's `@`).
 from __future__ import annotations
 
 import math
+import struct
 from dataclasses import dataclass, field
 from fractions import Fraction
 from typing import Dict, List, Optional, Sequence, Tuple
@@ -151,6 +152,7 @@ class StepResult:
 @dataclass
 class _BucketMemory:
     layout: Tuple
+    numel: int = 0                                               # bucket length
     error: Dict[int, np.ndarray] = field(default_factory=dict)   # view -> E (fp64)
     q: Dict[int, np.ndarray] = field(default_factory=dict)       # view -> warm Q
 
@@ -184,7 +186,39 @@ class OracleState:
         self.iteration = 0
         self.numel_in = 0
         self.numel_comm = 0
+        # iteration at or after which the next statistics line is due
+        self.next_log_iteration = hp.start_powerSGD_iter
         self.buckets: Dict[int, _BucketMemory] = {}
+
+    def _end_call(self, is_last: bool, compressing: bool) -> None:
+        """Iteration bookkeeping at the end of a call: the last bucket of an iteration
+        advances the counter; past start_powerSGD_iter it also moves the statistics
+        schedule on by compression_stats_logging_frequency when a line was due
+        ("PowerSGD State", compression_stats_logging_frequency)."""
+        if not is_last:
+            return
+        freq = self.hp.compression_stats_logging_frequency
+        if compressing and freq > 0 and self.iteration >= self.next_log_iteration:
+            self.next_log_iteration = self.iteration + freq
+        self.iteration += 1
+
+    def _view_counts(self, views: Sequence[View]) -> Tuple[int, int]:
+        """Elements in, and elements an allreduce would carry, for one per-layer call:
+        (n + m) * rank per compressed view, numel per other view."""
+        hp = self.hp
+        numel_in = comm = 0
+        for _, shp in views:
+            size = int(np.prod(shp, dtype=np.int64))
+            numel_in += size
+            nm = matrix_view(shp)
+            if nm is not None:
+                n, m = nm
+                rank = effective_rank(n, m, hp.matrix_approximation_rank)
+                if should_compress(n, m, rank, hp.min_compression_rate):
+                    comm += (n + m) * rank
+                    continue
+            comm += size
+        return numel_in, comm
 
     def compress_bucket(self, bucket: np.ndarray, views: Sequence[View],
                         bucket_index: int = 0, is_last: bool = True,
@@ -203,10 +237,17 @@ class OracleState:
         x64 = bucket.astype(np.float64)
 
         # GradScaler.unscale_/step: look for inf/NaN, skip everything if found.
+        # READING: past start_powerSGD_iter the call still counts in the compression
+        # statistics: the hook compresses and communicates before GradScaler.step
+        # decides to skip the update, and the statistics describe that communication.
         found_inf = is_fp16 and any_nonfinite(bucket, views)
         if found_inf:
-            if is_last:
-                self.iteration += 1
+            compressing = self.iteration >= hp.start_powerSGD_iter
+            if compressing:
+                n_in, n_comm = self._view_counts(views)
+                self.numel_in += n_in
+                self.numel_comm += n_comm
+            self._end_call(is_last, compressing)
             return StepResult(output=bucket.copy(), output64=x64, found_inf=True,
                               skipped=True, passthrough=False)
 
@@ -224,8 +265,7 @@ class OracleState:
                 out64[off:off + size] = g_all[off:off + size]
                 result.views.append(ViewResult(compressed=False))
             result.output = out64.astype(bucket.dtype) if is_fp16 else bucket.copy()
-            if is_last:
-                self.iteration += 1
+            self._end_call(is_last, False)
             return result
 
         layout = tuple(views)
@@ -235,7 +275,7 @@ class OracleState:
                 raise LayoutChanged(f"bucket {bucket_index} changed its layout")
             mem = None
         if mem is None:
-            mem = _BucketMemory(layout=layout)
+            mem = _BucketMemory(layout=layout, numel=int(bucket.size))
             self.buckets[bucket_index] = mem
 
         comm = 0
@@ -268,8 +308,7 @@ class OracleState:
             result.output = out64.astype(np.float16)
         else:
             result.output = out64.astype(np.float32)
-        if is_last:
-            self.iteration += 1
+        self._end_call(is_last, True)
         return result
 
     def compress_bucket_batched(self, bucket: np.ndarray, bucket_index: int = 0,
@@ -297,9 +336,15 @@ class OracleState:
         numel = int(bucket.size)
         x64 = bucket.astype(np.float64)
         found_inf = is_fp16 and not bool(np.all(np.isfinite(bucket)))
+        s = batched_side(numel)
         if found_inf:
-            if is_last:
-                self.iteration += 1
+            # statistics count the skipped call, as in compress_bucket
+            compressing = self.iteration >= hp.start_powerSGD_iter
+            if compressing:
+                self.numel_in += numel
+                if s > 0:
+                    self.numel_comm += 2 * s * effective_rank(s, s, hp.matrix_approximation_rank)
+            self._end_call(is_last, compressing)
             return StepResult(output=bucket.copy(), output64=x64, found_inf=True,
                               skipped=True, passthrough=False)
         g_all = x64 * float(inv_loss_scale) if is_fp16 else x64
@@ -308,8 +353,7 @@ class OracleState:
         if self.iteration < hp.start_powerSGD_iter:
             result.passthrough = True
             result.output = g_all.astype(bucket.dtype) if is_fp16 else bucket.copy()
-            if is_last:
-                self.iteration += 1
+            self._end_call(is_last, False)
             return result
         layout = ("batched", numel)
         mem = self.buckets.get(bucket_index)
@@ -318,9 +362,8 @@ class OracleState:
                 raise LayoutChanged(f"bucket {bucket_index} changed its layout")
             mem = None
         if mem is None:
-            mem = _BucketMemory(layout=layout)
+            mem = _BucketMemory(layout=layout, numel=numel)
             self.buckets[bucket_index] = mem
-        s = batched_side(numel)
         if s > 0:
             padded = np.zeros(s * s, dtype=np.float64)
             padded[:numel] = g_all
@@ -331,9 +374,158 @@ class OracleState:
             self.numel_comm += 2 * s * rank
         self.numel_in += numel
         result.output = result.output64.astype(bucket.dtype)
-        if is_last:
-            self.iteration += 1
+        self._end_call(is_last, True)
         return result
+
+    # ---- snapshot (checkpoint / resume) -------------------------------------------
+    # The pages describe no PowerSGDState checkpoint (GradScaler.state_dict in
+    # "Gradient Scaling" is the analogue). The byte format is the library's documented
+    # version-1 snapshot, written here independently: a little-endian 80-byte header,
+    # then per bucket (ascending index) its record, its views, and per compressed view
+    # E (n*m binary32, with error feedback) and the warm-start Q (m*k binary32).
+
+    _SNAP_MAGIC = b"PSGDSNAP"
+    _SNAP_HEADER = struct.Struct("<8sIIiIdQqqqqq")   # 80 bytes
+    _SNAP_BUCKET = struct.Struct("<qqIIq")           # 32 bytes
+
+    def _snapshot_views(self, mem: _BucketMemory):
+        """(batched, views, compressed view indices with their (n, m, rank))."""
+        hp = self.hp
+        if mem.layout[:1] == ("batched",):
+            s = batched_side(mem.numel)
+            if s == 0:
+                return True, [], []
+            return True, [(0, (s, s))], [(0, s, s, effective_rank(s, s,
+                                                                   hp.matrix_approximation_rank))]
+        views = list(mem.layout)
+        comp = []
+        for vi, (_, shp) in enumerate(views):
+            nm = matrix_view(shp)
+            if nm is None:
+                continue
+            n, m = nm
+            rank = effective_rank(n, m, hp.matrix_approximation_rank)
+            if should_compress(n, m, rank, hp.min_compression_rate):
+                comp.append((vi, n, m, rank))
+        return False, views, comp
+
+    def export_state(self) -> bytes:
+        """The state as a version-1 snapshot. E and Q are rounded to binary32, the
+        precision the snapshot stores."""
+        hp = self.hp
+        flags = (1 if hp.use_error_feedback else 0) | (2 if hp.warm_start else 0)
+        parts = [self._SNAP_HEADER.pack(
+            self._SNAP_MAGIC, 1, flags, hp.matrix_approximation_rank, 0,
+            float(hp.min_compression_rate), hp.random_seed, self.iteration, self.numel_in,
+            self.numel_comm, self.next_log_iteration, len(self.buckets))]
+        for idx in sorted(self.buckets):
+            mem = self.buckets[idx]
+            batched, views, comp = self._snapshot_views(mem)
+            has_q = bool(hp.warm_start and comp and all(vi in mem.q for vi, *_ in comp))
+            parts.append(self._SNAP_BUCKET.pack(idx, mem.numel, int(batched), int(has_q),
+                                                len(views)))
+            for off, shp in views:
+                parts.append(struct.pack(f"<qq{len(shp)}q", off, len(shp), *shp))
+            for vi, n, m, rank in comp:
+                if hp.use_error_feedback:
+                    e = mem.error.get(vi)
+                    if e is None:
+                        e = np.zeros((n, m))
+                    parts.append(np.ascontiguousarray(e, dtype="<f4").tobytes())
+                if has_q:
+                    parts.append(np.ascontiguousarray(mem.q[vi], dtype="<f4").tobytes())
+        return b"".join(parts)
+
+    def import_state(self, data: bytes) -> None:
+        """Replaces the state with a version-1 snapshot taken under the same error
+        feedback, warm start, rank, min_compression_rate and random_seed. Raises
+        ValueError (state unchanged) on anything malformed."""
+        hp = self.hp
+        data = bytes(data)
+        pos = 0
+
+        def take(fmt_or_len):
+            nonlocal pos
+            if isinstance(fmt_or_len, int):
+                if fmt_or_len < 0 or pos + fmt_or_len > len(data):
+                    raise ValueError("snapshot truncated")
+                out = data[pos:pos + fmt_or_len]
+                pos += fmt_or_len
+                return out
+            st = fmt_or_len if isinstance(fmt_or_len, struct.Struct) else struct.Struct(fmt_or_len)
+            if pos + st.size > len(data):
+                raise ValueError("snapshot truncated")
+            out = st.unpack_from(data, pos)
+            pos += st.size
+            return out
+
+        (magic, version, flags, rank, reserved, rate, seed, iteration, numel_in, numel_comm,
+         next_log, nbuckets) = take(self._SNAP_HEADER)
+        if magic != self._SNAP_MAGIC:
+            raise ValueError("bad magic")
+        if version != 1:
+            raise ValueError(f"unknown version {version}")
+        if reserved != 0 or flags & ~3:
+            raise ValueError("bad flags")
+        want = (1 if hp.use_error_feedback else 0) | (2 if hp.warm_start else 0)
+        if (flags != want or rank != hp.matrix_approximation_rank or seed != hp.random_seed
+                or struct.pack("<d", rate) != struct.pack("<d", float(hp.min_compression_rate))):
+            raise ValueError("snapshot taken under other hyperparameters")
+        if min(iteration, numel_in, numel_comm, next_log, nbuckets) < 0:
+            raise ValueError("negative counter")
+        buckets: Dict[int, _BucketMemory] = {}
+        prev = None
+        for _ in range(nbuckets):
+            idx, numel, batched, has_q, nviews = take(self._SNAP_BUCKET)
+            if prev is not None and idx <= prev:
+                raise ValueError("bucket indices not strictly ascending")
+            prev = idx
+            if numel < 0 or nviews < 0 or batched > 1 or has_q > 1:
+                raise ValueError("bad bucket record")
+            if has_q and not hp.warm_start:
+                raise ValueError("warm-start Q without warm start")
+            views = []
+            for _ in range(nviews):
+                off, ndim = take("<qq")
+                if not 0 <= ndim <= 8:
+                    raise ValueError("view ndim out of range")
+                shp = take(f"<{ndim}q") if ndim else ()
+                views.append((off, tuple(shp)))
+            if batched:
+                s = batched_side(numel)
+                if views != ([(0, (s, s))] if numel > 0 else []):
+                    raise ValueError("batched bucket is not one s x s view")
+                mem = _BucketMemory(layout=("batched", numel), numel=numel)
+            else:
+                spans = []
+                for off, shp in views:
+                    size = int(np.prod(shp, dtype=np.int64)) if shp else 1
+                    if min(shp, default=0) < 0 or off < 0 or off + size > numel:
+                        raise ValueError("view outside the bucket")
+                    if size > 0:
+                        spans.append((off, off + size))
+                spans.sort()
+                if any(b[0] < a[1] for a, b in zip(spans, spans[1:])):
+                    raise ValueError("views overlap")
+                mem = _BucketMemory(layout=tuple(views), numel=numel)
+            _, _, comp = self._snapshot_views(mem)
+            if has_q and not comp:
+                raise ValueError("warm-start Q on a bucket with no compressed view")
+            for vi, n, m, k in comp:
+                if hp.use_error_feedback:
+                    raw = take(4 * n * m)
+                    mem.error[vi] = np.frombuffer(raw, dtype="<f4").astype(np.float64).reshape(n, m)
+                if has_q:
+                    raw = take(4 * m * k)
+                    mem.q[vi] = np.frombuffer(raw, dtype="<f4").astype(np.float64).reshape(m, k)
+            buckets[idx] = mem
+        if pos != len(data):
+            raise ValueError(f"{len(data) - pos} trailing bytes")
+        self.buckets = buckets
+        self.iteration = iteration
+        self.numel_in = numel_in
+        self.numel_comm = numel_comm
+        self.next_log_iteration = next_log
 
     def _compress_matrix(self, g: np.ndarray, mem: _BucketMemory, view: int,
                          bucket_index: int, rank: int) -> ViewResult:
