@@ -239,6 +239,64 @@ POWERSGD_API powersgd_status powersgd_copy_error(powersgd_state* st, int64_t buc
 POWERSGD_API powersgd_status powersgd_get_stats(powersgd_state* st, int64_t* iteration,
                                    int64_t* numel_in, int64_t* numel_comm);
 
+/* --- state snapshot (checkpoint / resume) ------------------------------------- */
+
+/*
+ * The state PowerSGDState keeps between calls ("PowerSGD State": error memory and
+ * warm-start Q per bucket, the iteration counter and the compression statistics) as
+ * one host byte string, so a job can checkpoint it and resume with the same
+ * trajectory. The pages give no format (GradScaler's state_dict in the AMP page,
+ * "Gradient Scaling", is the analogue); this one is defined here.
+ *
+ * Format, version 1. Little-endian, no padding; i64/u64/u32/i32 integers, f64 and f32
+ * IEEE binary64/binary32.
+ *   header, 80 bytes:
+ *     char[8] "PSGDSNAP"; u32 version = 1; u32 flags (bit 0 use_error_feedback,
+ *     bit 1 warm_start); i32 matrix_approximation_rank; u32 reserved = 0;
+ *     f64 min_compression_rate; u64 random_seed; i64 iteration; i64 numel_in;
+ *     i64 numel_comm; i64 next_log_iteration (first iteration at which the next
+ *     statistics line is logged); i64 B = number of bucket records.
+ *   B bucket records, in ascending bucket_index:
+ *     i64 bucket_index; i64 numel (the batched variant: the length before padding);
+ *     u32 batched (1: the batched variant); u32 has_q (1: a warm-start Q follows for
+ *     every compressed view); i64 V = number of views;
+ *     V view records: i64 offset; i64 ndim; ndim x i64 shape (the batched variant: one
+ *     view, offset 0, shape (s, s), s = powersgd_batched_side(numel));
+ *     then for each compressed view in view order, n x m its matrix and k = min(r, n,
+ *     m) its rank: n*m f32, E row-major (only when flags bit 0 is set), then m*k f32,
+ *     Q row-major (only when has_q).
+ * A bucket is recorded once it has been called past start_powerSGD_iter (fp16
+ * pass-through tables hold no state and are not recorded).
+ */
+
+/*
+ * Writes the snapshot of `st` into `host_buf` (host memory, `capacity` bytes) and
+ * stores its length in *size. With host_buf NULL only *size is set (a size query).
+ * The device-to-host copies are enqueued on `stream` after the work already there and
+ * waited for, so the snapshot reflects every call enqueued on that stream before it;
+ * calls on other streams must have completed.
+ * Errors: INVALID_ARG (NULL state or size, capacity below the length), HIP.
+ */
+POWERSGD_API powersgd_status powersgd_state_export(powersgd_state* st, void* host_buf,
+                                                   int64_t capacity, int64_t* size,
+                                                   void* stream);
+
+/*
+ * Replaces the state of `st` with a snapshot from powersgd_state_export (host memory,
+ * `size` bytes). The snapshot's flags, matrix_approximation_rank, min_compression_rate
+ * and random_seed must equal the state's hyperparameters (they decide which memory
+ * exists and which random numbers a later call draws); the other hyperparameters are
+ * the state's own. Uploads are enqueued on `stream` and waited for; no call on the
+ * state may be in flight. The whole snapshot is checked and the new device memory
+ * filled before anything of the old state is released: on any error the state is
+ * unchanged.
+ * Errors: INVALID_ARG (NULL pointers, bad magic or version, mismatched
+ * hyperparameters, a record that is inconsistent or runs past `size`, trailing bytes),
+ * UNSUPPORTED (a view the library cannot hold), OOM, HIP.
+ */
+POWERSGD_API powersgd_status powersgd_state_import(powersgd_state* st, const void* host_buf,
+                                                   int64_t size, void* stream);
+
 /* --- kernel timing (HIP events on the caller's stream) ------------------------ */
 
 #define POWERSGD_NUM_KERNELS 8

@@ -1039,6 +1039,322 @@ powersgd_status powersgd_get_stats(powersgd_state* st, int64_t* iteration, int64
   return POWERSGD_OK;
 }
 
+// --- state snapshot --------------------------------------------------------------
+// The byte format is the one include/powersgd.h defines (version 1).
+
+extern "C++" {
+namespace {
+
+static_assert(__BYTE_ORDER__ == __ORDER_LITTLE_ENDIAN__, "the snapshot format is little-endian");
+
+constexpr char kSnapMagic[8] = {'P', 'S', 'G', 'D', 'S', 'N', 'A', 'P'};
+constexpr uint32_t kSnapVersion = 1;
+
+// Appends fields at `pos`; with a NULL base it only measures.
+struct SnapWriter {
+  uint8_t* base = nullptr;
+  int64_t pos = 0;
+  template <class T>
+  void put(T v) {
+    if (base) std::memcpy(base + pos, &v, sizeof(T));
+    pos += static_cast<int64_t>(sizeof(T));
+  }
+  uint8_t* take(int64_t bytes) {
+    uint8_t* at = base ? base + pos : nullptr;
+    pos += bytes;
+    return at;
+  }
+};
+
+// Reads fields from [base, base + size); every read is checked against the end.
+struct SnapReader {
+  const uint8_t* base;
+  int64_t size;
+  int64_t pos = 0;
+  template <class T>
+  bool get(T& v) {
+    if (size - pos < static_cast<int64_t>(sizeof(T))) return false;
+    std::memcpy(&v, base + pos, sizeof(T));
+    pos += static_cast<int64_t>(sizeof(T));
+    return true;
+  }
+  const uint8_t* take(int64_t bytes) {
+    if (bytes < 0 || size - pos < bytes) return nullptr;
+    const uint8_t* at = base + pos;
+    pos += bytes;
+    return at;
+  }
+};
+
+uint32_t snap_flags(const powersgd_hparams& hp) {
+  return (hp.use_error_feedback ? 1u : 0u) | (hp.warm_start ? 2u : 0u);
+}
+
+bool snap_has_q(const powersgd_hparams& hp, const BucketPlan& pl) {
+  return hp.warm_start && pl.q_ready && !pl.tensors.empty();
+}
+
+// Writes (or measures, with w.base NULL) the snapshot; with `copy` the E and Q blocks
+// are enqueued as device-to-host copies on s.
+powersgd_status write_snapshot(const powersgd_state* st, SnapWriter& w, bool copy,
+                               hipStream_t s) {
+  const powersgd_hparams& hp = st->hp;
+  const bool ef = hp.use_error_feedback != 0;
+  for (char c : kSnapMagic) w.put(c);
+  w.put<uint32_t>(kSnapVersion);
+  w.put<uint32_t>(snap_flags(hp));
+  w.put<int32_t>(hp.matrix_approximation_rank);
+  w.put<uint32_t>(0);
+  w.put<double>(hp.min_compression_rate);
+  w.put<uint64_t>(hp.random_seed);
+  w.put<int64_t>(st->iteration);
+  w.put<int64_t>(st->numel_in);
+  w.put<int64_t>(st->numel_comm);
+  w.put<int64_t>(st->next_log_iteration);
+  w.put<int64_t>(static_cast<int64_t>(st->buckets.size()));
+  for (const auto& kv : st->buckets) {  // std::map: ascending bucket index
+    const BucketPlan& pl = *kv.second;
+    const bool has_q = snap_has_q(hp, pl);
+    w.put<int64_t>(kv.first);
+    w.put<int64_t>(pl.numel);
+    w.put<uint32_t>(pl.batched ? 1u : 0u);
+    w.put<uint32_t>(has_q ? 1u : 0u);
+    w.put<int64_t>(static_cast<int64_t>(pl.views.size()));
+    for (const ViewKey& k : pl.views) {
+      w.put<int64_t>(k.offset);
+      w.put<int64_t>(static_cast<int64_t>(k.shape.size()));
+      for (int64_t d : k.shape) w.put<int64_t>(d);
+    }
+    for (size_t v = 0; v < pl.views.size(); ++v) {
+      const int32_t t = pl.view_tensor[v];
+      if (t < 0) continue;
+      const TensorDesc& d = pl.tensors[t];
+      if (ef) {
+        const int64_t bytes = static_cast<int64_t>(d.n) * d.m * 4;
+        uint8_t* dst = w.take(bytes);
+        if (copy && bytes > 0) {
+          hipError_t e = hipMemcpyAsync(dst, pl.E + d.eoff, bytes, hipMemcpyDeviceToHost, s);
+          if (e != hipSuccess) return hip_fail(e, "snapshot copy of E");
+        }
+      }
+      if (has_q) {
+        const int64_t bytes = static_cast<int64_t>(d.m) * d.rank * 4;
+        uint8_t* dst = w.take(bytes);
+        if (copy && bytes > 0) {
+          // Q is stored with row stride R; the snapshot keeps the rank in use
+          hipError_t e = hipMemcpy2DAsync(dst, d.rank * sizeof(float), pl.Q + d.qoff,
+                                          pl.R * sizeof(float), d.rank * sizeof(float), d.m,
+                                          hipMemcpyDeviceToHost, s);
+          if (e != hipSuccess) return hip_fail(e, "snapshot copy of Q");
+        }
+      }
+    }
+  }
+  return POWERSGD_OK;
+}
+
+// One bucket record of a snapshot being imported: its new plan and where its E and Q
+// blocks sit in the snapshot, per tensor.
+struct SnapBucket {
+  int64_t index = 0;
+  bool has_q = false;
+  std::unique_ptr<BucketPlan> plan;
+  std::vector<const uint8_t*> e_src, q_src;
+};
+
+powersgd_status snap_bad(const std::string& what) {
+  return fail(POWERSGD_ERR_INVALID_ARG, "snapshot: " + what);
+}
+
+powersgd_status read_bucket(const powersgd_hparams& hp, SnapReader& rd, int64_t prev_index,
+                            SnapBucket& out) {
+  int64_t numel = 0, nviews = 0;
+  uint32_t batched = 0, has_q = 0;
+  if (!rd.get(out.index) || !rd.get(numel) || !rd.get(batched) || !rd.get(has_q) ||
+      !rd.get(nviews))
+    return snap_bad("truncated bucket record");
+  if (out.index <= prev_index) return snap_bad("bucket indices not strictly ascending");
+  if (numel < 0 || nviews < 0 || batched > 1 || has_q > 1)
+    return snap_bad("bad field in the record of bucket " + std::to_string(out.index));
+  if (has_q && !hp.warm_start) return snap_bad("warm-start Q without warm start");
+  // every view record takes at least 16 bytes
+  if (nviews > (rd.size - rd.pos) / 16) return snap_bad("truncated view records");
+  std::vector<powersgd_view> views(static_cast<size_t>(nviews));
+  for (powersgd_view& pv : views) {
+    std::memset(&pv, 0, sizeof(pv));
+    if (!rd.get(pv.offset) || !rd.get(pv.ndim)) return snap_bad("truncated view record");
+    if (pv.ndim < 0 || pv.ndim > POWERSGD_MAX_NDIM) return snap_bad("view ndim out of range");
+    for (int64_t d = 0; d < pv.ndim; ++d)
+      if (!rd.get(pv.shape[d])) return snap_bad("truncated view shape");
+  }
+  std::vector<ViewKey> keys;
+  if (batched) {
+    const int64_t side = batched_side(numel);
+    if (side > INT32_MAX) return fail(POWERSGD_ERR_UNSUPPORTED, "snapshot: batched bucket too large");
+    const bool ok = numel == 0 ? nviews == 0
+                               : nviews == 1 && views[0].offset == 0 && views[0].ndim == 2 &&
+                                     views[0].shape[0] == side && views[0].shape[1] == side;
+    if (!ok) return snap_bad("batched bucket " + std::to_string(out.index) + " is not one s x s view");
+    if (numel > 0) keys.push_back(ViewKey{0, {side, side}});
+  } else {
+    powersgd_status vs = validate_views(views.data(), static_cast<int32_t>(nviews), numel, keys);
+    if (vs != POWERSGD_OK) return vs;
+    if (nviews > INT32_MAX) return snap_bad("too many views");
+  }
+  out.plan = std::make_unique<BucketPlan>();
+  powersgd_status b = build_plan(hp, numel, batched != 0, std::move(keys), *out.plan);
+  if (b != POWERSGD_OK) return b;
+  BucketPlan& pl = *out.plan;
+  if (has_q && pl.tensors.empty()) return snap_bad("warm-start Q on a bucket with no compressed view");
+  out.has_q = has_q != 0;
+  out.e_src.assign(pl.tensors.size(), nullptr);
+  out.q_src.assign(pl.tensors.size(), nullptr);
+  for (size_t v = 0; v < pl.views.size(); ++v) {
+    const int32_t t = pl.view_tensor[v];
+    if (t < 0) continue;
+    const TensorDesc& d = pl.tensors[t];
+    if (hp.use_error_feedback) {
+      out.e_src[t] = rd.take(static_cast<int64_t>(d.n) * d.m * 4);
+      if (!out.e_src[t]) return snap_bad("truncated error memory");
+    }
+    if (has_q) {
+      out.q_src[t] = rd.take(static_cast<int64_t>(d.m) * d.rank * 4);
+      if (!out.q_src[t]) return snap_bad("truncated warm-start Q");
+    }
+  }
+  return POWERSGD_OK;
+}
+
+// Allocates a parsed bucket's device memory and enqueues the uploads of its E, Q and
+// (matrix-core ranks) Q transposed. Host staging of Q^T goes to `keep`, which must
+// outlive the copies.
+powersgd_status upload_bucket(const powersgd_hparams& hp, SnapBucket& sb, hipStream_t s,
+                              std::vector<std::vector<float>>& keep) {
+  BucketPlan& pl = *sb.plan;
+  powersgd_status r = allocate_plan(pl, hp.use_error_feedback != 0, s);
+  if (r != POWERSGD_OK) return r;
+  for (size_t t = 0; t < pl.tensors.size(); ++t) {
+    const TensorDesc& d = pl.tensors[t];
+    if (sb.e_src[t] && static_cast<int64_t>(d.n) * d.m > 0) {
+      hipError_t e = hipMemcpyAsync(pl.E + d.eoff, sb.e_src[t],
+                                    static_cast<size_t>(d.n) * d.m * sizeof(float),
+                                    hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "snapshot upload of E");
+    }
+    if (sb.q_src[t]) {
+      hipError_t e = hipMemcpy2DAsync(pl.Q + d.qoff, pl.R * sizeof(float), sb.q_src[t],
+                                      d.rank * sizeof(float), d.rank * sizeof(float), d.m,
+                                      hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "snapshot upload of Q");
+      if (pl.QT && d.qtoff >= 0) {
+        // rows k < rank of Q^T; rows up to R and the columns past m stay zero
+        std::vector<float> qt(static_cast<size_t>(d.rank) * d.mstride, 0.f);
+        for (int32_t j = 0; j < d.m; ++j)
+          for (int32_t k = 0; k < d.rank; ++k)
+            std::memcpy(&qt[static_cast<size_t>(k) * d.mstride + j],
+                        sb.q_src[t] + (static_cast<size_t>(j) * d.rank + k) * 4, 4);
+        keep.push_back(std::move(qt));
+        e = hipMemcpyAsync(pl.QT + d.qtoff, keep.back().data(), keep.back().size() * sizeof(float),
+                           hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "snapshot upload of Q transposed");
+      }
+    }
+  }
+  pl.q_ready = sb.has_q;
+  return POWERSGD_OK;
+}
+
+}  // namespace
+}  // extern "C++"
+
+powersgd_status powersgd_state_export(powersgd_state* st, void* host_buf, int64_t capacity,
+                                      int64_t* size, void* stream) {
+  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
+  if (!size) return fail(POWERSGD_ERR_INVALID_ARG, "size is NULL");
+  SnapWriter measure;
+  powersgd_status r = write_snapshot(st, measure, false, nullptr);
+  if (r != POWERSGD_OK) return r;
+  *size = measure.pos;
+  if (!host_buf) return POWERSGD_OK;
+  if (capacity < measure.pos)
+    return fail(POWERSGD_ERR_INVALID_ARG, "capacity " + std::to_string(capacity) +
+                                              " is below the snapshot's " +
+                                              std::to_string(measure.pos) + " bytes");
+  HipDeviceGuard guard(st->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SnapWriter w;
+  w.base = static_cast<uint8_t*>(host_buf);
+  r = write_snapshot(st, w, true, s);
+  hipError_t e = hipStreamSynchronize(s);
+  if (r != POWERSGD_OK) return r;
+  if (e != hipSuccess) return hip_fail(e, "snapshot copies");
+  return POWERSGD_OK;
+}
+
+powersgd_status powersgd_state_import(powersgd_state* st, const void* host_buf, int64_t size,
+                                      void* stream) {
+  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
+  if (!host_buf || size < 0) return fail(POWERSGD_ERR_INVALID_ARG, "snapshot buffer is NULL or size < 0");
+  const powersgd_hparams& hp = st->hp;
+  SnapReader rd{static_cast<const uint8_t*>(host_buf), size};
+  char magic[8];
+  for (char& c : magic)
+    if (!rd.get(c)) return snap_bad("truncated header");
+  if (std::memcmp(magic, kSnapMagic, 8) != 0) return snap_bad("bad magic");
+  uint32_t version = 0, flags = 0, reserved = 0;
+  int32_t rank = 0;
+  double rate = 0.0;
+  uint64_t seed = 0;
+  int64_t iteration = 0, numel_in = 0, numel_comm = 0, next_log = 0, nbuckets = 0;
+  if (!rd.get(version)) return snap_bad("truncated header");
+  if (version != kSnapVersion) return snap_bad("unknown version " + std::to_string(version));
+  if (!rd.get(flags) || !rd.get(rank) || !rd.get(reserved) || !rd.get(rate) || !rd.get(seed) ||
+      !rd.get(iteration) || !rd.get(numel_in) || !rd.get(numel_comm) || !rd.get(next_log) ||
+      !rd.get(nbuckets))
+    return snap_bad("truncated header");
+  if (reserved != 0 || (flags & ~3u) != 0) return snap_bad("bad flags");
+  if (flags != snap_flags(hp) || rank != hp.matrix_approximation_rank ||
+      std::memcmp(&rate, &hp.min_compression_rate, sizeof(double)) != 0 || seed != hp.random_seed)
+    return snap_bad("taken under other hyperparameters (error feedback, warm start, rank, "
+                    "min_compression_rate or random_seed differ)");
+  if (iteration < 0 || numel_in < 0 || numel_comm < 0 || next_log < 0 || nbuckets < 0)
+    return snap_bad("negative counter");
+  if (nbuckets > (rd.size - rd.pos) / 32) return snap_bad("truncated bucket records");
+
+  std::vector<SnapBucket> parsed(static_cast<size_t>(nbuckets));
+  int64_t prev = INT64_MIN;
+  for (SnapBucket& sb : parsed) {
+    if (prev == INT64_MAX) return snap_bad("bucket indices not strictly ascending");
+    powersgd_status r = read_bucket(hp, rd, prev, sb);
+    if (r != POWERSGD_OK) return r;
+    prev = sb.index;
+  }
+  if (rd.pos != rd.size) return snap_bad(std::to_string(rd.size - rd.pos) + " trailing bytes");
+
+  HipDeviceGuard guard(st->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<std::vector<float>> keep;
+  powersgd_status r = POWERSGD_OK;
+  for (SnapBucket& sb : parsed) {
+    r = upload_bucket(hp, sb, s, keep);
+    if (r != POWERSGD_OK) break;
+  }
+  // wait for the uploads (also on failure: the host sources must outlive them)
+  hipError_t e = hipStreamSynchronize(s);
+  if (r != POWERSGD_OK) return r;
+  if (e != hipSuccess) return hip_fail(e, "snapshot uploads");
+
+  std::map<int64_t, std::unique_ptr<BucketPlan>> fresh;
+  for (SnapBucket& sb : parsed) fresh.emplace(sb.index, std::move(sb.plan));
+  st->buckets.swap(fresh);  // the old plans are released with `fresh`
+  st->passthrough.clear();
+  st->iteration = iteration;
+  st->numel_in = numel_in;
+  st->numel_comm = numel_comm;
+  st->next_log_iteration = next_log;
+  return POWERSGD_OK;
+}
+
 powersgd_status powersgd_set_timing(powersgd_state* st, int32_t enable) {
   if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
   HipDeviceGuard guard(st->device);

@@ -34,6 +34,7 @@ EXPORTED = (
     "powersgd_copy_error", "powersgd_get_stats", "powersgd_set_timing",
     "powersgd_get_kernel_times", "powersgd_kernel_name", "powersgd_classify_view",
     "powersgd_batched_side", "powersgd_compress_bucket_batched",
+    "powersgd_state_export", "powersgd_state_import",
 )
 
 
@@ -103,6 +104,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "powersgd_get_kernel_times": (i32, [P, ctypes.POINTER(f64), ctypes.POINTER(i64),
                                             ctypes.POINTER(f64)]),
         "powersgd_kernel_name": (ctypes.c_char_p, [i32]),
+        "powersgd_state_export": (i32, [P, P, i64, ctypes.POINTER(i64), P]),
+        "powersgd_state_import": (i32, [P, P, i64, P]),
         "powersgd_classify_view": (i32, [ctypes.POINTER(powersgd_hparams),
                                          ctypes.POINTER(powersgd_view), ctypes.POINTER(i32),
                                          ctypes.POINTER(i64), ctypes.POINTER(i64),
@@ -220,6 +223,28 @@ def powersgd_get_stats(state) -> Tuple[int, int, int]:
     _check(load_library().powersgd_get_stats(state, ctypes.byref(it), ctypes.byref(a),
                                              ctypes.byref(b)))
     return it.value, a.value, b.value
+
+
+def powersgd_state_export(state, stream: Optional[int]) -> bytearray:
+    lib = load_library()
+    size = ctypes.c_int64()
+    _check(lib.powersgd_state_export(state, None, 0, ctypes.byref(size), None))
+    out = bytearray(size.value)
+    view = (ctypes.c_char * max(size.value, 1)).from_buffer(out if size.value else bytearray(1))
+    _check(lib.powersgd_state_export(state, view, size.value, ctypes.byref(size),
+                                     ctypes.c_void_p(stream) if stream else None))
+    return out
+
+
+def powersgd_state_import(state, snapshot, stream: Optional[int]) -> None:
+    if isinstance(snapshot, bytes):
+        data, n = snapshot, len(snapshot)
+    else:
+        buf = bytearray(snapshot) if not isinstance(snapshot, bytearray) else snapshot
+        n = len(buf)
+        data = (ctypes.c_char * max(n, 1)).from_buffer(buf if n else bytearray(1))
+    _check(load_library().powersgd_state_import(state, data, n,
+                                                ctypes.c_void_p(stream) if stream else None))
 
 
 def powersgd_set_timing(state, enable: bool) -> None:
@@ -351,6 +376,15 @@ class PowerSGDState:
 
     def stats(self) -> Tuple[int, int, int]:
         return powersgd_get_stats(self._state)
+
+    def export_state(self, stream=None) -> bytearray:
+        """The state's snapshot (format in include/powersgd.h), after the work already
+        enqueued on `stream`."""
+        return powersgd_state_export(self._state, self._stream_handle(stream))
+
+    def import_state(self, snapshot, stream=None) -> None:
+        """Replaces the state with a snapshot taken under the same hyperparameters."""
+        powersgd_state_import(self._state, snapshot, self._stream_handle(stream))
 
     def set_timing(self, enable: bool) -> None:
         powersgd_set_timing(self._state, enable)
