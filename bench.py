@@ -122,6 +122,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="skip the per-kernel event timing (no roofline object)")
+    ap.add_argument("--snapshot", action="store_true",
+                    help="also time one state export and import after the run (stderr)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -229,6 +231,18 @@ def main() -> int:
                     "traffic": traffic, "kernel": name,
                     "mean_launch_us": round(avg_s * 1e6, 3),
                     "algorithmic_bytes_per_launch": by / n}
+    if args.snapshot:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        blob = st.export_state()
+        t_exp = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        st.import_state(blob)
+        t_imp = time.perf_counter() - t0
+        eprint(f"[bench] snapshot {len(blob) / 1e6:.1f} MB: export {t_exp * 1e3:.1f} ms "
+               f"({len(blob) / t_exp / 1e9:.2f} GB/s), import {t_imp * 1e3:.1f} ms "
+               f"({len(blob) / t_imp / 1e9:.2f} GB/s), host side a Python bytearray")
+        del blob
     st.close()
     del pool
     torch.cuda.empty_cache()

@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <list>
 #include <map>
 #include <memory>
 #include <string>
@@ -1094,10 +1095,104 @@ bool snap_has_q(const powersgd_hparams& hp, const BucketPlan& pl) {
   return hp.warm_start && pl.q_ready && !pl.tensors.empty();
 }
 
-// Writes (or measures, with w.base NULL) the snapshot; with `copy` the E and Q blocks
-// are enqueued as device-to-host copies on s.
-powersgd_status write_snapshot(const powersgd_state* st, SnapWriter& w, bool copy,
-                               hipStream_t s) {
+// One contiguous transfer between device memory and (pageable) host memory.
+struct CopySeg {
+  void* dev;
+  uint8_t* host;
+  int64_t bytes;
+};
+
+// Runs the transfers through two pinned staging buffers on stream s: the DMA of one
+// buffer overlaps the host memcpy of the other (pageable transfers run at a fraction
+// of the link rate). Returns after every transfer has completed.
+powersgd_status staged_copy(const std::vector<CopySeg>& segs, bool to_host, hipStream_t s) {
+  constexpr int64_t kStageBytes = int64_t{16} << 20;
+  int64_t total = 0;
+  for (const CopySeg& c : segs) total += c.bytes;
+  if (total == 0) return POWERSGD_OK;
+  const int64_t cap = std::min(total, kStageBytes);
+  uint8_t* pin[2] = {nullptr, nullptr};
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  struct Piece {
+    uint8_t* host;
+    int64_t at, bytes;
+  };
+  std::vector<Piece> pending[2];
+  bool busy[2] = {false, false};
+  powersgd_status r = POWERSGD_OK;
+  auto check = [&](hipError_t e, const char* what) {
+    if (e != hipSuccess && r == POWERSGD_OK) r = hip_fail(e, what);
+    return r == POWERSGD_OK;
+  };
+  // waits for buffer b's transfers; device-to-host pieces are then copied out
+  auto drain = [&](int b) {
+    if (!busy[b]) return;
+    busy[b] = false;
+    if (!check(hipEventSynchronize(ev[b]), "staged copy")) return;
+    for (const Piece& pc : pending[b]) std::memcpy(pc.host, pin[b] + pc.at, pc.bytes);
+    pending[b].clear();
+  };
+  for (int b = 0; b < 2 && r == POWERSGD_OK; ++b) {
+    check(hipHostMalloc(reinterpret_cast<void**>(&pin[b]), cap, hipHostMallocDefault),
+          "hipHostMalloc of the staging buffer");
+    if (r == POWERSGD_OK) check(hipEventCreateWithFlags(&ev[b], hipEventDisableTiming), "hipEventCreate");
+  }
+  int b = 0;
+  int64_t fill = 0;
+  for (const CopySeg& c : segs) {
+    int64_t done = 0;
+    while (done < c.bytes && r == POWERSGD_OK) {
+      const int64_t n = std::min(c.bytes - done, cap - fill);
+      uint8_t* dev = static_cast<uint8_t*>(c.dev) + done;
+      if (to_host) {
+        check(hipMemcpyAsync(pin[b] + fill, dev, n, hipMemcpyDeviceToHost, s), "staged copy");
+        pending[b].push_back(Piece{c.host + done, fill, n});
+      } else {
+        std::memcpy(pin[b] + fill, c.host + done, n);
+        check(hipMemcpyAsync(dev, pin[b] + fill, n, hipMemcpyHostToDevice, s), "staged copy");
+      }
+      done += n;
+      fill += n;
+      if (fill == cap) {
+        check(hipEventRecord(ev[b], s), "hipEventRecord");
+        busy[b] = true;
+        b ^= 1;
+        drain(b);
+        fill = 0;
+      }
+    }
+  }
+  if (fill > 0 && r == POWERSGD_OK) {
+    check(hipEventRecord(ev[b], s), "hipEventRecord");
+    busy[b] = true;
+  }
+  // every enqueued transfer ends before the staging buffers are freed, also on error
+  (void)hipStreamSynchronize(s);
+  for (int k = 0; k < 2; ++k) {
+    if (r == POWERSGD_OK) drain(k);
+    if (ev[k]) (void)hipEventDestroy(ev[k]);
+    if (pin[k]) (void)hipHostFree(pin[k]);
+  }
+  return r;
+}
+
+// Device-to-host work of an export: the transfers, and for every warm-start Q the
+// whole strided Q buffer of its bucket, compacted into the snapshot afterwards.
+struct ExportCopies {
+  std::vector<CopySeg> segs;
+  std::vector<std::vector<float>> qbufs;  // per bucket with a Q: its Q buffer (row stride R)
+  struct QPiece {
+    size_t qbuf;
+    int64_t qoff;
+    int32_t m, rank, R;
+    uint8_t* dst;
+  };
+  std::vector<QPiece> qpieces;
+};
+
+// Writes (or measures, with w.base NULL) the snapshot; with `copies` it lists the
+// E and Q transfers instead of writing their bytes.
+void write_snapshot(const powersgd_state* st, SnapWriter& w, ExportCopies* copies) {
   const powersgd_hparams& hp = st->hp;
   const bool ef = hp.use_error_feedback != 0;
   for (char c : kSnapMagic) w.put(c);
@@ -1125,6 +1220,13 @@ powersgd_status write_snapshot(const powersgd_state* st, SnapWriter& w, bool cop
       w.put<int64_t>(static_cast<int64_t>(k.shape.size()));
       for (int64_t d : k.shape) w.put<int64_t>(d);
     }
+    size_t qbuf = 0;
+    if (copies && has_q) {
+      copies->qbufs.emplace_back(static_cast<size_t>(pl.q_floats));
+      qbuf = copies->qbufs.size() - 1;
+      copies->segs.push_back(CopySeg{pl.Q, reinterpret_cast<uint8_t*>(copies->qbufs[qbuf].data()),
+                                     pl.q_floats * 4});
+    }
     for (size_t v = 0; v < pl.views.size(); ++v) {
       const int32_t t = pl.view_tensor[v];
       if (t < 0) continue;
@@ -1132,25 +1234,15 @@ powersgd_status write_snapshot(const powersgd_state* st, SnapWriter& w, bool cop
       if (ef) {
         const int64_t bytes = static_cast<int64_t>(d.n) * d.m * 4;
         uint8_t* dst = w.take(bytes);
-        if (copy && bytes > 0) {
-          hipError_t e = hipMemcpyAsync(dst, pl.E + d.eoff, bytes, hipMemcpyDeviceToHost, s);
-          if (e != hipSuccess) return hip_fail(e, "snapshot copy of E");
-        }
+        if (copies && bytes > 0) copies->segs.push_back(CopySeg{pl.E + d.eoff, dst, bytes});
       }
       if (has_q) {
-        const int64_t bytes = static_cast<int64_t>(d.m) * d.rank * 4;
-        uint8_t* dst = w.take(bytes);
-        if (copy && bytes > 0) {
-          // Q is stored with row stride R; the snapshot keeps the rank in use
-          hipError_t e = hipMemcpy2DAsync(dst, d.rank * sizeof(float), pl.Q + d.qoff,
-                                          pl.R * sizeof(float), d.rank * sizeof(float), d.m,
-                                          hipMemcpyDeviceToHost, s);
-          if (e != hipSuccess) return hip_fail(e, "snapshot copy of Q");
-        }
+        uint8_t* dst = w.take(static_cast<int64_t>(d.m) * d.rank * 4);
+        if (copies)
+          copies->qpieces.push_back(ExportCopies::QPiece{qbuf, d.qoff, d.m, d.rank, pl.R, dst});
       }
     }
   }
-  return POWERSGD_OK;
 }
 
 // One bucket record of a snapshot being imported: its new plan and where its E and Q
@@ -1225,41 +1317,43 @@ powersgd_status read_bucket(const powersgd_hparams& hp, SnapReader& rd, int64_t 
   return POWERSGD_OK;
 }
 
-// Allocates a parsed bucket's device memory and enqueues the uploads of its E, Q and
-// (matrix-core ranks) Q transposed. Host staging of Q^T goes to `keep`, which must
-// outlive the copies.
+// Allocates a parsed bucket's device memory and lists the uploads of its E, its Q
+// buffer (row stride R) and, for matrix-core ranks, Q transposed; the Q buffers are
+// assembled on the host in `keep`, which must outlive the transfers.
 powersgd_status upload_bucket(const powersgd_hparams& hp, SnapBucket& sb, hipStream_t s,
-                              std::vector<std::vector<float>>& keep) {
+                              std::vector<CopySeg>& segs,
+                              std::list<std::vector<float>>& keep) {
   BucketPlan& pl = *sb.plan;
   powersgd_status r = allocate_plan(pl, hp.use_error_feedback != 0, s);
   if (r != POWERSGD_OK) return r;
-  for (size_t t = 0; t < pl.tensors.size(); ++t) {
-    const TensorDesc& d = pl.tensors[t];
-    if (sb.e_src[t] && static_cast<int64_t>(d.n) * d.m > 0) {
-      hipError_t e = hipMemcpyAsync(pl.E + d.eoff, sb.e_src[t],
-                                    static_cast<size_t>(d.n) * d.m * sizeof(float),
-                                    hipMemcpyHostToDevice, s);
-      if (e != hipSuccess) return hip_fail(e, "snapshot upload of E");
-    }
-    if (sb.q_src[t]) {
-      hipError_t e = hipMemcpy2DAsync(pl.Q + d.qoff, pl.R * sizeof(float), sb.q_src[t],
-                                      d.rank * sizeof(float), d.rank * sizeof(float), d.m,
-                                      hipMemcpyHostToDevice, s);
-      if (e != hipSuccess) return hip_fail(e, "snapshot upload of Q");
-      if (pl.QT && d.qtoff >= 0) {
-        // rows k < rank of Q^T; rows up to R and the columns past m stay zero
-        std::vector<float> qt(static_cast<size_t>(d.rank) * d.mstride, 0.f);
-        for (int32_t j = 0; j < d.m; ++j)
-          for (int32_t k = 0; k < d.rank; ++k)
-            std::memcpy(&qt[static_cast<size_t>(k) * d.mstride + j],
-                        sb.q_src[t] + (static_cast<size_t>(j) * d.rank + k) * 4, 4);
-        keep.push_back(std::move(qt));
-        e = hipMemcpyAsync(pl.QT + d.qtoff, keep.back().data(), keep.back().size() * sizeof(float),
-                           hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) return hip_fail(e, "snapshot upload of Q transposed");
-      }
+  std::vector<float>* q = nullptr;
+  std::vector<float>* qt = nullptr;
+  if (sb.has_q) {
+    // columns past each tensor's rank, and Q^T's rows past it and columns past m, stay zero
+    keep.emplace_back(static_cast<size_t>(pl.q_floats), 0.f);
+    q = &keep.back();
+    if (pl.QT) {
+      keep.emplace_back(static_cast<size_t>(pl.qt_floats), 0.f);
+      qt = &keep.back();
     }
   }
+  for (size_t t = 0; t < pl.tensors.size(); ++t) {
+    const TensorDesc& d = pl.tensors[t];
+    if (sb.e_src[t] && static_cast<int64_t>(d.n) * d.m > 0)
+      segs.push_back(CopySeg{pl.E + d.eoff, const_cast<uint8_t*>(sb.e_src[t]),
+                             static_cast<int64_t>(d.n) * d.m * 4});
+    if (!q || !sb.q_src[t]) continue;
+    for (int32_t j = 0; j < d.m; ++j)
+      for (int32_t k = 0; k < d.rank; ++k) {
+        float v;
+        std::memcpy(&v, sb.q_src[t] + (static_cast<size_t>(j) * d.rank + k) * 4, 4);
+        (*q)[static_cast<size_t>(d.qoff) + static_cast<size_t>(j) * pl.R + k] = v;
+        if (qt && d.qtoff >= 0)
+          (*qt)[static_cast<size_t>(d.qtoff) + static_cast<size_t>(k) * d.mstride + j] = v;
+      }
+  }
+  if (q) segs.push_back(CopySeg{pl.Q, reinterpret_cast<uint8_t*>(q->data()), pl.q_floats * 4});
+  if (qt) segs.push_back(CopySeg{pl.QT, reinterpret_cast<uint8_t*>(qt->data()), pl.qt_floats * 4});
   pl.q_ready = sb.has_q;
   return POWERSGD_OK;
 }
@@ -1272,8 +1366,7 @@ powersgd_status powersgd_state_export(powersgd_state* st, void* host_buf, int64_
   if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
   if (!size) return fail(POWERSGD_ERR_INVALID_ARG, "size is NULL");
   SnapWriter measure;
-  powersgd_status r = write_snapshot(st, measure, false, nullptr);
-  if (r != POWERSGD_OK) return r;
+  write_snapshot(st, measure, nullptr);
   *size = measure.pos;
   if (!host_buf) return POWERSGD_OK;
   if (capacity < measure.pos)
@@ -1284,10 +1377,16 @@ powersgd_status powersgd_state_export(powersgd_state* st, void* host_buf, int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   SnapWriter w;
   w.base = static_cast<uint8_t*>(host_buf);
-  r = write_snapshot(st, w, true, s);
-  hipError_t e = hipStreamSynchronize(s);
+  ExportCopies copies;
+  write_snapshot(st, w, &copies);
+  powersgd_status r = staged_copy(copies.segs, true, s);
   if (r != POWERSGD_OK) return r;
-  if (e != hipSuccess) return hip_fail(e, "snapshot copies");
+  for (const ExportCopies::QPiece& qp : copies.qpieces) {
+    const float* src = copies.qbufs[qp.qbuf].data() + qp.qoff;
+    for (int32_t j = 0; j < qp.m; ++j)
+      std::memcpy(qp.dst + static_cast<size_t>(j) * qp.rank * 4,
+                  src + static_cast<size_t>(j) * qp.R, static_cast<size_t>(qp.rank) * 4);
+  }
   return POWERSGD_OK;
 }
 
@@ -1333,16 +1432,18 @@ powersgd_status powersgd_state_import(powersgd_state* st, const void* host_buf, 
 
   HipDeviceGuard guard(st->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  std::vector<std::vector<float>> keep;
+  std::list<std::vector<float>> keep;  // stable addresses while the list grows
+  std::vector<CopySeg> segs;
   powersgd_status r = POWERSGD_OK;
   for (SnapBucket& sb : parsed) {
-    r = upload_bucket(hp, sb, s, keep);
+    r = upload_bucket(hp, sb, s, segs, keep);
     if (r != POWERSGD_OK) break;
   }
-  // wait for the uploads (also on failure: the host sources must outlive them)
-  hipError_t e = hipStreamSynchronize(s);
-  if (r != POWERSGD_OK) return r;
-  if (e != hipSuccess) return hip_fail(e, "snapshot uploads");
+  if (r == POWERSGD_OK) r = staged_copy(segs, false, s);
+  if (r != POWERSGD_OK) {
+    (void)hipStreamSynchronize(s);  // allocation work of the new plans, before they are freed
+    return r;
+  }
 
   std::map<int64_t, std::unique_ptr<BucketPlan>> fresh;
   for (SnapBucket& sb : parsed) fresh.emplace(sb.index, std::move(sb.plan));
