@@ -377,27 +377,127 @@ class OracleState:
         self._end_call(is_last, True)
         return result
 
+    def compress_bucket_wrapped(self, bucket: np.ndarray, views: Sequence[View],
+                                compute_dtype: str = "f16", bucket_index: int = 0,
+                                is_last: bool = True) -> StepResult:
+        """fp16_compress_wrapper(powerSGD_hook) or bf16_compress_wrapper(powerSGD_hook)
+        ("Default Communication Hooks") on one rank's fp32 bucket: the bucket is cast
+        to 16 bits, the hook runs on that tensor with every tensor it materializes held
+        in 16 bits (oracle.lowp), and the result is cast back to fp32.
+
+        READING: elements outside every view are left as they are (a DDP bucket has
+        none); the Q draw is the binary32 draw of powerSGD_hook cast to 16 bits, then
+        orthogonalized and rounded; the memorized layout is ("wrapped", dtype, views),
+        so E and Q of another variant are never reused. No loss scaling is involved:
+        values beyond the 16-bit range become inf and propagate.
+        """
+        from .lowp import ROUNDERS, compress_matrix_step_lowp
+
+        hp = self.hp
+        rnd = ROUNDERS[compute_dtype]
+        bucket = np.asarray(bucket)
+        if bucket.dtype != np.float32:
+            raise TypeError("the wrapped hook takes a float32 bucket")
+        views = [(int(off), tuple(int(d) for d in shp)) for off, shp in views]
+        x64 = bucket.astype(np.float64)
+        out64 = x64.copy()
+        result = StepResult(output=bucket, output64=out64, found_inf=False, skipped=False,
+                            passthrough=False)
+        # the wrapper's cast of the gradients
+        b16 = x64.copy()
+        for off, shp in views:
+            size = int(np.prod(shp, dtype=np.int64))
+            b16[off:off + size] = rnd(x64[off:off + size])
+        if self.iteration < hp.start_powerSGD_iter:
+            result.passthrough = True
+            for off, shp in views:
+                size = int(np.prod(shp, dtype=np.int64))
+                out64[off:off + size] = b16[off:off + size]
+                result.views.append(ViewResult(compressed=False))
+            result.output = out64.astype(np.float32)
+            self._end_call(is_last, False)
+            return result
+
+        layout = ("wrapped", compute_dtype, tuple(views))
+        mem = self.buckets.get(bucket_index)
+        if mem is not None and mem.layout != layout:
+            if hp.use_error_feedback or hp.warm_start:
+                raise LayoutChanged(f"bucket {bucket_index} changed its layout")
+            mem = None
+        if mem is None:
+            mem = _BucketMemory(layout=layout, numel=int(bucket.size))
+            self.buckets[bucket_index] = mem
+
+        eps = float(hp.orthogonalization_epsilon)
+        comm = numel_in = 0
+        for vi, (off, shp) in enumerate(views):
+            size = int(np.prod(shp, dtype=np.int64))
+            numel_in += size
+            g16 = b16[off:off + size]
+            nm = matrix_view(shp)
+            compress = False
+            if nm is not None:
+                n, m = nm
+                rank = effective_rank(n, m, hp.matrix_approximation_rank)
+                compress = should_compress(n, m, rank, hp.min_compression_rate)
+            if not compress:
+                out64[off:off + size] = g16
+                comm += size
+                result.views.append(ViewResult(compressed=False))
+                continue
+            if hp.warm_start and vi in mem.q:
+                q = mem.q[vi]
+            else:
+                epoch = 0 if hp.warm_start else self.iteration
+                draw = standard_normal_q0(m, rank, hp.random_seed, bucket_index, vi, epoch)
+                q = rnd(gram_schmidt(rnd(draw), eps))
+            e_prev = mem.error.get(vi) if hp.use_error_feedback else None
+            m_prime, p, q_new, m_hat, err = compress_matrix_step_lowp(
+                g16.reshape(n, m), e_prev, q, eps, hp.use_error_feedback, rnd)
+            if hp.use_error_feedback:
+                mem.error[vi] = err
+            if hp.warm_start:
+                mem.q[vi] = q_new
+            out64[off:off + size] = m_hat.reshape(-1)
+            comm += (n + m) * rank
+            result.views.append(ViewResult(compressed=True, n=n, m=m, rank=rank,
+                                           m_prime=m_prime, p=p, q=q_new, m_hat=m_hat,
+                                           error=err))
+        self.numel_in += numel_in
+        self.numel_comm += comm
+        result.output = out64.astype(np.float32)
+        self._end_call(is_last, True)
+        return result
+
     # ---- snapshot (checkpoint / resume) -------------------------------------------
     # The pages describe no PowerSGDState checkpoint (GradScaler.state_dict in
     # "Gradient Scaling" is the analogue). The byte format is the library's documented
     # version-1 snapshot, written here independently: a little-endian 80-byte header,
-    # then per bucket (ascending index) its record, its views, and per compressed view
-    # E (n*m binary32, with error feedback) and the warm-start Q (m*k binary32).
+    # then per bucket (ascending index) its record (the variant word: bit 0 batched,
+    # bits 8-9 the precision of a wrapped bucket's state, 1 binary16, 2 bfloat16), its
+    # views, and per compressed view E (n*m binary32, with error feedback) and the
+    # warm-start Q (m*k binary32).
 
     _SNAP_MAGIC = b"PSGDSNAP"
     _SNAP_HEADER = struct.Struct("<8sIIiIdQqqqqq")   # 80 bytes
     _SNAP_BUCKET = struct.Struct("<qqIIq")           # 32 bytes
 
+    _SNAP_PRECISION = {None: 0, "f16": 1, "bf16": 2}
+
     def _snapshot_views(self, mem: _BucketMemory):
-        """(batched, views, compressed view indices with their (n, m, rank))."""
+        """(batched, 16-bit precision or None, views, compressed view indices with their
+        (n, m, rank))."""
         hp = self.hp
         if mem.layout[:1] == ("batched",):
             s = batched_side(mem.numel)
             if s == 0:
-                return True, [], []
-            return True, [(0, (s, s))], [(0, s, s, effective_rank(s, s,
-                                                                   hp.matrix_approximation_rank))]
+                return True, None, [], []
+            return True, None, [(0, (s, s))], [(0, s, s, effective_rank(
+                s, s, hp.matrix_approximation_rank))]
+        prec = None
         views = list(mem.layout)
+        if mem.layout[:1] == ("wrapped",):
+            prec, views = mem.layout[1], list(mem.layout[2])
         comp = []
         for vi, (_, shp) in enumerate(views):
             nm = matrix_view(shp)
@@ -407,7 +507,7 @@ class OracleState:
             rank = effective_rank(n, m, hp.matrix_approximation_rank)
             if should_compress(n, m, rank, hp.min_compression_rate):
                 comp.append((vi, n, m, rank))
-        return False, views, comp
+        return False, prec, views, comp
 
     def export_state(self) -> bytes:
         """The state as a version-1 snapshot. E and Q are rounded to binary32, the
@@ -420,9 +520,10 @@ class OracleState:
             self.numel_comm, self.next_log_iteration, len(self.buckets))]
         for idx in sorted(self.buckets):
             mem = self.buckets[idx]
-            batched, views, comp = self._snapshot_views(mem)
+            batched, prec, views, comp = self._snapshot_views(mem)
             has_q = bool(hp.warm_start and comp and all(vi in mem.q for vi, *_ in comp))
-            parts.append(self._SNAP_BUCKET.pack(idx, mem.numel, int(batched), int(has_q),
+            variant = int(batched) | (self._SNAP_PRECISION[prec] << 8)
+            parts.append(self._SNAP_BUCKET.pack(idx, mem.numel, variant, int(has_q),
                                                 len(views)))
             for off, shp in views:
                 parts.append(struct.pack(f"<qq{len(shp)}q", off, len(shp), *shp))
@@ -476,12 +577,15 @@ class OracleState:
         buckets: Dict[int, _BucketMemory] = {}
         prev = None
         for _ in range(nbuckets):
-            idx, numel, batched, has_q, nviews = take(self._SNAP_BUCKET)
+            idx, numel, variant, has_q, nviews = take(self._SNAP_BUCKET)
             if prev is not None and idx <= prev:
                 raise ValueError("bucket indices not strictly ascending")
             prev = idx
-            if numel < 0 or nviews < 0 or batched > 1 or has_q > 1:
+            batched, pcode = variant & 1, (variant >> 8) & 3
+            if (numel < 0 or nviews < 0 or variant & ~0x301 or pcode == 3 or has_q > 1
+                    or (batched and pcode)):
                 raise ValueError("bad bucket record")
+            prec = {0: None, 1: "f16", 2: "bf16"}[pcode]
             if has_q and not hp.warm_start:
                 raise ValueError("warm-start Q without warm start")
             views = []
@@ -507,17 +611,23 @@ class OracleState:
                 spans.sort()
                 if any(b[0] < a[1] for a, b in zip(spans, spans[1:])):
                     raise ValueError("views overlap")
-                mem = _BucketMemory(layout=tuple(views), numel=numel)
-            _, _, comp = self._snapshot_views(mem)
+                layout = tuple(views) if prec is None else ("wrapped", prec, tuple(views))
+                mem = _BucketMemory(layout=layout, numel=numel)
+            _, _, _, comp = self._snapshot_views(mem)
+            # a 16-bit state holds 16-bit values: what the snapshot gives is rounded
+            from .lowp import ROUNDERS
+            fix = (lambda a: a) if prec is None else ROUNDERS[prec]
             if has_q and not comp:
                 raise ValueError("warm-start Q on a bucket with no compressed view")
             for vi, n, m, k in comp:
                 if hp.use_error_feedback:
                     raw = take(4 * n * m)
-                    mem.error[vi] = np.frombuffer(raw, dtype="<f4").astype(np.float64).reshape(n, m)
+                    mem.error[vi] = fix(np.frombuffer(raw, dtype="<f4").astype(np.float64)
+                                        ).reshape(n, m)
                 if has_q:
                     raw = take(4 * m * k)
-                    mem.q[vi] = np.frombuffer(raw, dtype="<f4").astype(np.float64).reshape(m, k)
+                    mem.q[vi] = fix(np.frombuffer(raw, dtype="<f4").astype(np.float64)
+                                    ).reshape(m, k)
             buckets[idx] = mem
         if pos != len(data):
             raise ValueError(f"{len(data) - pos} trailing bytes")

@@ -212,3 +212,32 @@ def test_logging_schedule():
     # a bucket that is not the last of its iteration moves nothing
     st.compress_bucket(_bucket(9), _views(), bucket_index=3, is_last=False)
     assert (st.iteration, st.next_log_iteration) == (9, 11)
+
+
+@pytest.mark.parametrize("dt,code", [("f16", 1), ("bf16", 2)])
+def test_wrapped_buckets_record_their_precision(dt, code):
+    hp = _hp()
+    a = oracle.OracleState(hp)
+    for t in range(2):
+        a.compress_bucket_wrapped(_bucket(t), _views(), dt, bucket_index=6)
+    blob = a.export_state()
+    # the one bucket record follows the header: index, numel, then the variant word
+    idx, numel, variant = struct.unpack_from("<qqI", blob, 80)
+    assert (idx, numel, variant) == (6, 944, code << 8)
+    b = oracle.OracleState(hp)
+    b.import_state(blob)
+    assert b.export_state() == blob
+    assert b.buckets[6].layout == ("wrapped", dt, tuple(_views()))
+    ra = a.compress_bucket_wrapped(_bucket(2), _views(), dt, bucket_index=6)
+    rb = b.compress_bucket_wrapped(_bucket(2), _views(), dt, bucket_index=6)
+    np.testing.assert_array_equal(ra.output, rb.output)   # 16-bit state: nothing lost
+    # a value that is not 16-bit is rounded into the 16-bit state on import
+    first_e = 80 + 32 + sum(16 + 8 * len(shp) for _, shp in _views())
+    x = bytearray(blob)
+    struct.pack_into("<f", x, first_e, 1.0 + 2.0 ** -20)
+    b.import_state(bytes(x))
+    assert b.buckets[6].error[0][0, 0] == 1.0
+    # precision code 3 and a batched 16-bit bucket do not exist
+    for bad in (3 << 8, (code << 8) | 1, code << 10):
+        with pytest.raises(ValueError):
+            b.import_state(_corrupt(blob, 96, "<I", bad))
