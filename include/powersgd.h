@@ -44,7 +44,7 @@ typedef enum {
   POWERSGD_ERR_NOT_FOUND = -6        /* introspection of a bucket/view never compressed */
 } powersgd_status;
 
-typedef enum { POWERSGD_F32 = 0, POWERSGD_F16 = 1 } powersgd_dtype;
+typedef enum { POWERSGD_F32 = 0, POWERSGD_F16 = 1, POWERSGD_BF16 = 2 } powersgd_dtype;
 
 #define POWERSGD_MAX_NDIM 8
 #define POWERSGD_MAX_RANK 32
@@ -142,6 +142,39 @@ POWERSGD_API powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_
                                          void* stream);
 
 /*
+ * powerSGD_hook wrapped by fp16_compress_wrapper or bf16_compress_wrapper ("DDP
+ * Communication Hooks -- PyTorch 1.11.0", section "Default Communication Hooks"): the
+ * fp32 bucket is cast to 16 bits, the hook runs on the 16-bit tensor and the result is
+ * cast back to fp32, in place. Every tensor the hook forms is a 16-bit value rounded to
+ * nearest even where it is formed: the cast gradient, M' = G + E, P = M'Q, P after
+ * Gram-Schmidt, Q = M'^T P, M_hat = P Q^T and E = M' - M_hat (also the initial draw of
+ * Q, cast from its binary32 value); sums and products accumulate in fp32 (the
+ * Gram-Schmidt recurrence in fp64). The bucket's error memory E and the M' of a call
+ * are 16-bit arrays; the warm-start Q holds 16-bit values.
+ *
+ *   bucket         device pointer to numel fp32 gradients, caller-owned; compressed
+ *                  views receive M_hat, uncompressed views their 16-bit cast (both as
+ *                  fp32). Elements outside every view are neither read nor written.
+ *   compute_dtype  POWERSGD_F16 (fp16_compress_wrapper) or POWERSGD_BF16
+ *                  (bf16_compress_wrapper).
+ *   bucket_index, is_last, views, nviews, stream: as for powersgd_compress_bucket; a
+ *                  bucket_index memorized by another variant (or precision) is a
+ *                  layout change. No loss scaling: values beyond the 16-bit range
+ *                  become inf and propagate.
+ *
+ * Before start_powerSGD_iter the call is the cast to 16 bits and back. The matrix-core
+ * ranks are not supported here: matrix_approximation_rank must be <= 8.
+ * Errors: INVALID_ARG (as for powersgd_compress_bucket; compute_dtype not F16/BF16),
+ * UNSUPPORTED (rank above 8), LAYOUT_CHANGED, OOM, HIP; returned before anything is
+ * enqueued.
+ */
+POWERSGD_API powersgd_status powersgd_compress_bucket_wrapped(powersgd_state* st,
+                                                 int64_t bucket_index, int32_t is_last,
+                                                 float* bucket, powersgd_dtype compute_dtype,
+                                                 int64_t numel, const powersgd_view* views,
+                                                 int32_t nviews, void* stream);
+
+/*
  * Side of the square matrix the batched variant views a bucket of `numel` elements
  * as: the smallest s with s * s >= numel (0 for numel <= 0). Pure host function.
  */
@@ -224,9 +257,9 @@ POWERSGD_API powersgd_status powersgd_copy_factors(powersgd_state* st, int64_t b
                                       int32_t view, float* p_dev, float* q_dev,
                                       void* stream);
 
-/* Copies the error-feedback memory E (n x m, row-major, fp32) of compressed view v
- * into a caller device buffer, enqueued on `stream`. NOT_FOUND without error
- * feedback. */
+/* Copies the error-feedback memory E (n x m, row-major, fp32; a 16-bit state's values
+ * widened exactly) of compressed view v into a caller device buffer, enqueued on
+ * `stream`. NOT_FOUND without error feedback. */
 POWERSGD_API powersgd_status powersgd_copy_error(powersgd_state* st, int64_t bucket_index,
                                     int32_t view, float* e_dev, void* stream);
 
@@ -258,15 +291,18 @@ POWERSGD_API powersgd_status powersgd_get_stats(powersgd_state* st, int64_t* ite
  *     statistics line is logged); i64 B = number of bucket records.
  *   B bucket records, in ascending bucket_index:
  *     i64 bucket_index; i64 numel (the batched variant: the length before padding);
- *     u32 batched (1: the batched variant); u32 has_q (1: a warm-start Q follows for
- *     every compressed view); i64 V = number of views;
+ *     u32 variant (bit 0: the batched variant; bits 8-9: the precision of a bucket
+ *     compressed through powersgd_compress_bucket_wrapped, 1 binary16, 2 bfloat16, 0
+ *     otherwise; other bits zero); u32 has_q (1: a warm-start Q follows for every
+ *     compressed view); i64 V = number of views;
  *     V view records: i64 offset; i64 ndim; ndim x i64 shape (the batched variant: one
  *     view, offset 0, shape (s, s), s = powersgd_batched_side(numel));
  *     then for each compressed view in view order, n x m its matrix and k = min(r, n,
  *     m) its rank: n*m f32, E row-major (only when flags bit 0 is set), then m*k f32,
  *     Q row-major (only when has_q).
- * A bucket is recorded once it has been called past start_powerSGD_iter (fp16
- * pass-through tables hold no state and are not recorded).
+ * E and Q are written as binary32 also for a 16-bit state (exactly); import rounds
+ * them to the bucket's precision. A bucket is recorded once it has been called past
+ * start_powerSGD_iter (fp16 pass-through tables hold no state and are not recorded).
  */
 
 /*

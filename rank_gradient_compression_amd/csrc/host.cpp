@@ -104,6 +104,7 @@ struct ViewKey {
 struct BucketPlan {
   int64_t numel = 0;      // bucket length (batched: the logical length, before padding)
   bool batched = false;   // the whole bucket viewed as one padded square matrix
+  int st = kStF32;        // state precision (16-bit for the wrapped hook)
   std::vector<ViewKey> views;
   std::vector<uint8_t> decision;        // per view: 1 = compressed
   std::vector<int32_t> view_tensor;     // per view: tensor index or -1
@@ -127,6 +128,8 @@ struct BucketPlan {
 
   // device memory
   float* E = nullptr;
+  uint16_t* Eh = nullptr;  // 16-bit state: E
+  uint16_t* Mh = nullptr;  // 16-bit state: M' of the current call
   float* P = nullptr;
   float* Praw = nullptr;  // vector ranks: P as pass 1 writes it (pass 2 orthogonalizes)
   float* Q = nullptr;
@@ -150,12 +153,13 @@ struct BucketPlan {
   bool q_ready = false;
 
   void release() {
-    void* ptrs[] = {E, P, Praw, Q, QT, partial, gram, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
+    void* ptrs[] = {E, Eh, Mh, P, Praw, Q, QT, partial, gram, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
                     d_tiles1, d_tiles2, d_tiles3, d_tiles2r, d_flat_unc, d_flat_all, d_pjobs, d_qjobs,
                     d_qinit};
     for (void* p : ptrs)
       if (p) (void)hipFree(p);
     E = P = Praw = Q = QT = partial = nullptr;
+    Eh = Mh = nullptr;
     gram = nullptr;
     d_pgram_tiles = d_qgram_tiles = nullptr;
     d_td = d_td_scalar = nullptr;
@@ -471,7 +475,12 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
     return hipMalloc(p, bytes) == hipSuccess;
   };
   bool ok = true;
-  ok = ok && alloc(reinterpret_cast<void**>(&pl.E), need_e ? pl.e_floats * sizeof(float) : 0);
+  const bool h16 = pl.st != kStF32;
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.E),
+                   (need_e && !h16) ? pl.e_floats * sizeof(float) : 0);
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.Eh),
+                   (need_e && h16) ? pl.e_floats * sizeof(uint16_t) : 0);
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.Mh), h16 ? pl.e_floats * sizeof(uint16_t) : 0);
   ok = ok && alloc(reinterpret_cast<void**>(&pl.P), pl.p_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.Praw),
                    pl.R <= kMaxFusedGramRank ? pl.p_floats * sizeof(float) : 0);
@@ -486,6 +495,8 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   }
   hipError_t e = hipSuccess;
   if (pl.E && e == hipSuccess) e = hipMemsetAsync(pl.E, 0, pl.e_floats * sizeof(float), s);
+  if (pl.Eh && e == hipSuccess) e = hipMemsetAsync(pl.Eh, 0, pl.e_floats * sizeof(uint16_t), s);
+  if (pl.Mh && e == hipSuccess) e = hipMemsetAsync(pl.Mh, 0, pl.e_floats * sizeof(uint16_t), s);
   if (pl.P && e == hipSuccess) e = hipMemsetAsync(pl.P, 0, pl.p_floats * sizeof(float), s);
   if (pl.Praw && e == hipSuccess)
     e = hipMemsetAsync(pl.Praw, 0, pl.p_floats * sizeof(float), s);
@@ -526,9 +537,9 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   return POWERSGD_OK;
 }
 
-bool same_layout(const BucketPlan& pl, int64_t numel, bool batched,
+bool same_layout(const BucketPlan& pl, int64_t numel, bool batched, int prec,
                  const std::vector<ViewKey>& views) {
-  return pl.numel == numel && pl.batched == batched && pl.views == views;
+  return pl.numel == numel && pl.batched == batched && pl.st == prec && pl.views == views;
 }
 
 // Side of the square matrix the batched variant views a bucket of `numel` elements as:
@@ -544,7 +555,16 @@ int64_t batched_side(int64_t numel) {
 }
 
 // Algorithmic bytes of each pass per compressed element (minimum traffic).
-double pass_bytes(int kind, bool f16, bool ef) {
+double pass_bytes(int kind, bool f16, bool ef, int prec = kStF32) {
+  if (prec != kStF32) {
+    // fp32 bucket, 16-bit M' and E
+    switch (kind) {
+      case K_PASS1: return 4.0 + (ef ? 2.0 : 0.0) + 2.0;
+      case K_PASS2: return 2.0;
+      case K_PASS3: return 2.0 + 4.0 + (ef ? 2.0 : 0.0);
+      default: return 0.0;
+    }
+  }
   const double g = f16 ? 2.0 : 4.0;
   switch (kind) {
     case K_PASS1: return f16 ? (g + (ef ? 4.0 : 0.0)) : (ef ? 12.0 : 4.0);
@@ -643,7 +663,7 @@ namespace {
 // views) or the batched one (`keys` = the one padded square view, `numel` = the
 // bucket's own length).
 powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_last,
-                         void* bucket, bool f16, int64_t numel, bool batched,
+                         void* bucket, bool f16, int64_t numel, bool batched, int prec,
                          std::vector<ViewKey>& keys, float inv_loss_scale,
                          int32_t* found_inf_dev, void* stream) {
   HipDeviceGuard guard(st->device);
@@ -655,14 +675,15 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
   const uintptr_t base = reinterpret_cast<uintptr_t>(bucket);
 
   // Vanilla allreduce phase (iteration < start_powerSGD_iter): identity on one rank;
-  // fp16 still does the unscale with its inf check.
+  // fp16 still does the unscale with its inf check, the wrapped hook the 16-bit cast.
   if (st->iteration < hp.start_powerSGD_iter) {
-    if (f16) {
+    if (f16 || prec != kStF32) {
       auto& slot = st->passthrough[bucket_index];
-      if (!slot || !same_layout(*slot, numel, batched, keys)) {
+      if (!slot || !same_layout(*slot, numel, batched, prec, keys)) {
         auto pl = std::make_unique<BucketPlan>();
         pl->numel = numel;
         pl->batched = batched;
+        pl->st = prec;
         pl->views = keys;
         if (batched)
           add_flat(pl->flat_all, 0, numel);
@@ -678,6 +699,14 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
       const int nf = static_cast<int>(pl.flat_all.size());
       double all = 0;
       for (const FlatTile& f : pl.flat_all) all += static_cast<double>(f.len);
+      if (prec != kStF32) {
+        powersgd_status r = timed_launch(st, s, K_UNSCALE, all * 8.0, "16-bit cast", [&] {
+          return launch_round_only(pl.d_flat_all, nf, bucket, prec, s);
+        });
+        if (r != POWERSGD_OK) return r;
+        if (is_last) st->iteration += 1;
+        return POWERSGD_OK;
+      }
       powersgd_status r = timed_launch(st, s, K_UNSCALE, all * 2.0, "fp16 check", [&] {
         return launch_unscale_only(pl.d_flat_all, nf, bucket, inv_loss_scale, found_inf_dev,
                                    true, s);
@@ -695,7 +724,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
 
   // Plan lookup; a memorized bucket must keep its layout.
   auto it = st->buckets.find(bucket_index);
-  if (it != st->buckets.end() && !same_layout(*it->second, numel, batched, keys)) {
+  if (it != st->buckets.end() && !same_layout(*it->second, numel, batched, prec, keys)) {
     if (ef || hp.warm_start)
       return fail(POWERSGD_ERR_LAYOUT_CHANGED,
                   "bucket " + std::to_string(bucket_index) + " was called with other views");
@@ -706,6 +735,10 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     auto pl = std::make_unique<BucketPlan>();
     powersgd_status b = build_plan(hp, numel, batched, std::move(keys), *pl);
     if (b != POWERSGD_OK) return b;
+    if (prec != kStF32 && pl->R > kMaxFusedGramRank)
+      return fail(POWERSGD_ERR_UNSUPPORTED,
+                  "the 16-bit wrapped hook supports matrix_approximation_rank <= 8");
+    pl->st = prec;
     b = allocate_plan(*pl, ef, s);
     if (b != POWERSGD_OK) return b;
     it = st->buckets.emplace(bucket_index, std::move(pl)).first;
@@ -730,7 +763,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
       const uint64_t epoch = hp.warm_start ? 0 : static_cast<uint64_t>(st->iteration);
       r = timed_launch(st, s, K_QINIT, 0.0, "q_init", [&] {
         return launch_qinit(R, pl.d_qinit, nt, pl.max_qcount, pl.Q, hp.random_seed,
-                            bucket_key, epoch, s);
+                            bucket_key, epoch, prec, s);
       });
       if (r != POWERSGD_OK) return r;
       r = timed_launch(st, s, K_GRAM, 0.0, "Gram of Q", [&] {
@@ -740,7 +773,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
       if (r != POWERSGD_OK) return r;
       r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize Q", [&] {
         return launch_orth(R, pl.d_qjobs, nt, pl.max_qrows, pl.Q, pl.QT, pl.gram, eps, nullptr,
-                           s);
+                           prec, s);
       });
       if (r != POWERSGD_OK) return r;
     }
@@ -768,11 +801,13 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.QT = pl.QT;
     a.P = fused ? pl.Praw : pl.P;
     a.gram = pl.gram;
+    a.Eh = pl.Eh;
+    a.Mh = pl.Mh;
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
-    const double bytes = ce * pass_bytes(K_PASS1, f16, ef) + (f16 ? ue * 2.0 : 0.0);
+    const double bytes = ce * pass_bytes(K_PASS1, f16, ef, prec) + (f16 ? ue * 2.0 : 0.0);
     r = timed_launch(st, s, K_PASS1, bytes, "pass 1",
-                     [&] { return launch_pass1(R, f16, ef, a, s); });
+                     [&] { return launch_pass1(R, f16, ef, prec, a, s); });
     if (r != POWERSGD_OK) return r;
   }
   if (nt > 0) {
@@ -787,7 +822,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     if (!fused) {
       r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize P", [&] {
         return launch_orth(R, pl.d_pjobs, nt, pl.max_prows, pl.P, nullptr, pl.gram, eps,
-                           f16 ? found_inf_dev : nullptr, s);
+                           f16 ? found_inf_dev : nullptr, prec, s);
       });
       if (r != POWERSGD_OK) return r;
     }
@@ -805,10 +840,11 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.Q = pl.Q;
     a.QT = pl.QT;
     a.partial = pl.partial;
+    a.Mh = pl.Mh;
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
-    r = timed_launch(st, s, K_PASS2, ce * pass_bytes(K_PASS2, f16, ef), "pass 2",
-                     [&] { return launch_pass2(R, f16, ef, a, s); });
+    r = timed_launch(st, s, K_PASS2, ce * pass_bytes(K_PASS2, f16, ef, prec), "pass 2",
+                     [&] { return launch_pass2(R, f16, ef, prec, a, s); });
     if (r != POWERSGD_OK) return r;
     if (!fused && !pl.tiles2r.empty()) {
       Pass2ReduceArgs b{};
@@ -837,11 +873,14 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.P = pl.P;
     a.Q = pl.Q;
     a.partial = pl.partial;  // vector ranks sum the pass-2 partials here
+    a.Eh = pl.Eh;
+    a.Mh = pl.Mh;
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
-    const double bytes = ce * pass_bytes(K_PASS3, f16, ef) + (f16 ? ue * 4.0 : 0.0);
+    const double bytes = ce * pass_bytes(K_PASS3, f16, ef, prec) +
+                         (f16 ? ue * 4.0 : (prec != kStF32 ? ue * 8.0 : 0.0));
     r = timed_launch(st, s, K_PASS3, bytes, "pass 3",
-                     [&] { return launch_pass3(R, f16, ef, a, s); });
+                     [&] { return launch_pass3(R, f16, ef, prec, a, s); });
     if (r != POWERSGD_OK) return r;
   }
   pl.q_ready = hp.warm_start != 0;
@@ -887,8 +926,35 @@ powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_t bucket_inde
   std::vector<ViewKey> keys;
   powersgd_status vs = validate_views(views, nviews, numel, keys);
   if (vs != POWERSGD_OK) return vs;
-  return run_call(st, bucket_index, is_last, bucket, f16, numel, false, keys, inv_loss_scale,
-                  found_inf_dev, stream);
+  return run_call(st, bucket_index, is_last, bucket, f16, numel, false, kStF32, keys,
+                  inv_loss_scale, found_inf_dev, stream);
+}
+
+powersgd_status powersgd_compress_bucket_wrapped(powersgd_state* st, int64_t bucket_index,
+                                                 int32_t is_last, float* bucket,
+                                                 powersgd_dtype compute_dtype, int64_t numel,
+                                                 const powersgd_view* views, int32_t nviews,
+                                                 void* stream) {
+  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
+  if (numel < 0) return fail(POWERSGD_ERR_INVALID_ARG, "numel < 0");
+  if (nviews < 0) return fail(POWERSGD_ERR_INVALID_ARG, "nviews < 0");
+  if (nviews > 0 && !views) return fail(POWERSGD_ERR_INVALID_ARG, "views is NULL");
+  if (numel > 0 && !bucket) return fail(POWERSGD_ERR_INVALID_ARG, "bucket is NULL");
+  int prec = kStF32;
+  if (compute_dtype == POWERSGD_F16)
+    prec = kStF16;
+  else if (compute_dtype == POWERSGD_BF16)
+    prec = kStBF16;
+  else
+    return fail(POWERSGD_ERR_INVALID_ARG, "compute_dtype must be F16 or BF16");
+  if (st->hp.matrix_approximation_rank > kMaxFusedGramRank)
+    return fail(POWERSGD_ERR_UNSUPPORTED,
+                "the 16-bit wrapped hook supports matrix_approximation_rank <= 8");
+  std::vector<ViewKey> keys;
+  powersgd_status vs = validate_views(views, nviews, numel, keys);
+  if (vs != POWERSGD_OK) return vs;
+  return run_call(st, bucket_index, is_last, bucket, false, numel, false, prec, keys, 1.0f,
+                  nullptr, stream);
 }
 
 int64_t powersgd_batched_side(int64_t numel) { return batched_side(numel); }
@@ -916,8 +982,8 @@ powersgd_status powersgd_compress_bucket_batched(powersgd_state* st, int64_t buc
                     std::to_string(side * side) + " elements");
   std::vector<ViewKey> keys;
   if (numel > 0) keys.push_back(ViewKey{0, {side, side}});
-  return run_call(st, bucket_index, is_last, bucket, f16, numel, true, keys, inv_loss_scale,
-                  found_inf_dev, stream);
+  return run_call(st, bucket_index, is_last, bucket, f16, numel, true, kStF32, keys,
+                  inv_loss_scale, found_inf_dev, stream);
 }
 
 powersgd_status powersgd_classify_view(const powersgd_hparams* hp, const powersgd_view* view,
@@ -1021,9 +1087,16 @@ powersgd_status powersgd_copy_error(powersgd_state* st, int64_t bucket_index, in
   const TensorDesc* d = nullptr;
   powersgd_status r = find_tensor(st, bucket_index, view, &pl, &d);
   if (r != POWERSGD_OK) return r;
-  if (!pl->E) return fail(POWERSGD_ERR_NOT_FOUND, "error feedback is off");
+  if (!pl->E && !pl->Eh) return fail(POWERSGD_ERR_NOT_FOUND, "error feedback is off");
   if (!e_dev) return fail(POWERSGD_ERR_INVALID_ARG, "e_dev is NULL");
   HipDeviceGuard guard(st->device);
+  if (pl->Eh) {
+    // a 16-bit state: its values widened to fp32
+    hipError_t e = launch_widen16(pl->Eh + d->eoff, e_dev, static_cast<int64_t>(d->n) * d->m,
+                                  pl->st, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "copy of E");
+    return POWERSGD_OK;
+  }
   hipError_t e = hipMemcpyAsync(e_dev, pl->E + d->eoff,
                                 static_cast<size_t>(d->n) * d->m * sizeof(float),
                                 hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
@@ -1086,6 +1159,34 @@ struct SnapReader {
     return at;
   }
 };
+
+// 16-bit state values on the host (snapshots): bfloat16 rounded to nearest even from
+// the binary32 pattern (as the kernels do), binary16 through the compiler's _Float16.
+uint16_t host_to_h16(float x, int prec) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  if (prec == kStBF16) {
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+  }
+  const _Float16 h = static_cast<_Float16>(x);
+  uint16_t b;
+  std::memcpy(&b, &h, 2);
+  return b;
+}
+
+float host_from_h16(uint16_t h, int prec) {
+  float f;
+  if (prec == kStBF16) {
+    const uint32_t u = static_cast<uint32_t>(h) << 16;
+    std::memcpy(&f, &u, 4);
+    return f;
+  }
+  _Float16 v;
+  std::memcpy(&v, &h, 2);
+  return static_cast<float>(v);
+}
 
 uint32_t snap_flags(const powersgd_hparams& hp) {
   return (hp.use_error_feedback ? 1u : 0u) | (hp.warm_start ? 2u : 0u);
@@ -1188,6 +1289,14 @@ struct ExportCopies {
     uint8_t* dst;
   };
   std::vector<QPiece> qpieces;
+  std::vector<std::vector<uint16_t>> ebufs;  // per 16-bit bucket: its E buffer
+  struct EPiece {
+    size_t ebuf;
+    int64_t eoff, count;
+    int prec;
+    uint8_t* dst;
+  };
+  std::vector<EPiece> epieces;
 };
 
 // Writes (or measures, with w.base NULL) the snapshot; with `copies` it lists the
@@ -1212,7 +1321,7 @@ void write_snapshot(const powersgd_state* st, SnapWriter& w, ExportCopies* copie
     const bool has_q = snap_has_q(hp, pl);
     w.put<int64_t>(kv.first);
     w.put<int64_t>(pl.numel);
-    w.put<uint32_t>(pl.batched ? 1u : 0u);
+    w.put<uint32_t>((pl.batched ? 1u : 0u) | (static_cast<uint32_t>(pl.st) << 8));
     w.put<uint32_t>(has_q ? 1u : 0u);
     w.put<int64_t>(static_cast<int64_t>(pl.views.size()));
     for (const ViewKey& k : pl.views) {
@@ -1220,7 +1329,13 @@ void write_snapshot(const powersgd_state* st, SnapWriter& w, ExportCopies* copie
       w.put<int64_t>(static_cast<int64_t>(k.shape.size()));
       for (int64_t d : k.shape) w.put<int64_t>(d);
     }
-    size_t qbuf = 0;
+    size_t qbuf = 0, ebuf = 0;
+    if (copies && ef && pl.st != kStF32 && pl.e_floats > 0) {
+      copies->ebufs.emplace_back(static_cast<size_t>(pl.e_floats));
+      ebuf = copies->ebufs.size() - 1;
+      copies->segs.push_back(CopySeg{pl.Eh, reinterpret_cast<uint8_t*>(copies->ebufs[ebuf].data()),
+                                     pl.e_floats * 2});
+    }
     if (copies && has_q) {
       copies->qbufs.emplace_back(static_cast<size_t>(pl.q_floats));
       qbuf = copies->qbufs.size() - 1;
@@ -1234,7 +1349,13 @@ void write_snapshot(const powersgd_state* st, SnapWriter& w, ExportCopies* copie
       if (ef) {
         const int64_t bytes = static_cast<int64_t>(d.n) * d.m * 4;
         uint8_t* dst = w.take(bytes);
-        if (copies && bytes > 0) copies->segs.push_back(CopySeg{pl.E + d.eoff, dst, bytes});
+        if (copies && bytes > 0) {
+          if (pl.st != kStF32)  // widened to binary32 after the transfer
+            copies->epieces.push_back(
+                ExportCopies::EPiece{ebuf, d.eoff, static_cast<int64_t>(d.n) * d.m, pl.st, dst});
+          else
+            copies->segs.push_back(CopySeg{pl.E + d.eoff, dst, bytes});
+        }
       }
       if (has_q) {
         uint8_t* dst = w.take(static_cast<int64_t>(d.m) * d.rank * 4);
@@ -1261,12 +1382,15 @@ powersgd_status snap_bad(const std::string& what) {
 powersgd_status read_bucket(const powersgd_hparams& hp, SnapReader& rd, int64_t prev_index,
                             SnapBucket& out) {
   int64_t numel = 0, nviews = 0;
-  uint32_t batched = 0, has_q = 0;
-  if (!rd.get(out.index) || !rd.get(numel) || !rd.get(batched) || !rd.get(has_q) ||
+  uint32_t variant = 0, has_q = 0;
+  if (!rd.get(out.index) || !rd.get(numel) || !rd.get(variant) || !rd.get(has_q) ||
       !rd.get(nviews))
     return snap_bad("truncated bucket record");
   if (out.index <= prev_index) return snap_bad("bucket indices not strictly ascending");
-  if (numel < 0 || nviews < 0 || batched > 1 || has_q > 1)
+  const uint32_t batched = variant & 1u;
+  const int prec = static_cast<int>((variant >> 8) & 3u);
+  if (numel < 0 || nviews < 0 || (variant & ~0x301u) != 0 || prec == 3 || (batched && prec) ||
+      has_q > 1)
     return snap_bad("bad field in the record of bucket " + std::to_string(out.index));
   if (has_q && !hp.warm_start) return snap_bad("warm-start Q without warm start");
   // every view record takes at least 16 bytes
@@ -1297,6 +1421,9 @@ powersgd_status read_bucket(const powersgd_hparams& hp, SnapReader& rd, int64_t 
   powersgd_status b = build_plan(hp, numel, batched != 0, std::move(keys), *out.plan);
   if (b != POWERSGD_OK) return b;
   BucketPlan& pl = *out.plan;
+  if (prec != kStF32 && pl.R > kMaxFusedGramRank)
+    return fail(POWERSGD_ERR_UNSUPPORTED, "snapshot: 16-bit state above rank 8");
+  pl.st = prec;
   if (has_q && pl.tensors.empty()) return snap_bad("warm-start Q on a bucket with no compressed view");
   out.has_q = has_q != 0;
   out.e_src.assign(pl.tensors.size(), nullptr);
@@ -1322,10 +1449,17 @@ powersgd_status read_bucket(const powersgd_hparams& hp, SnapReader& rd, int64_t 
 // assembled on the host in `keep`, which must outlive the transfers.
 powersgd_status upload_bucket(const powersgd_hparams& hp, SnapBucket& sb, hipStream_t s,
                               std::vector<CopySeg>& segs,
-                              std::list<std::vector<float>>& keep) {
+                              std::list<std::vector<float>>& keep,
+                              std::list<std::vector<uint16_t>>& keep16) {
   BucketPlan& pl = *sb.plan;
   powersgd_status r = allocate_plan(pl, hp.use_error_feedback != 0, s);
   if (r != POWERSGD_OK) return r;
+  const int prec = pl.st;
+  std::vector<uint16_t>* eh = nullptr;  // a 16-bit E, rounded from the snapshot's binary32
+  if (prec != kStF32 && pl.Eh) {
+    keep16.emplace_back(static_cast<size_t>(pl.e_floats), uint16_t{0});
+    eh = &keep16.back();
+  }
   std::vector<float>* q = nullptr;
   std::vector<float>* qt = nullptr;
   if (sb.has_q) {
@@ -1339,19 +1473,30 @@ powersgd_status upload_bucket(const powersgd_hparams& hp, SnapBucket& sb, hipStr
   }
   for (size_t t = 0; t < pl.tensors.size(); ++t) {
     const TensorDesc& d = pl.tensors[t];
-    if (sb.e_src[t] && static_cast<int64_t>(d.n) * d.m > 0)
-      segs.push_back(CopySeg{pl.E + d.eoff, const_cast<uint8_t*>(sb.e_src[t]),
-                             static_cast<int64_t>(d.n) * d.m * 4});
+    const int64_t ne = static_cast<int64_t>(d.n) * d.m;
+    if (sb.e_src[t] && ne > 0) {
+      if (eh) {
+        for (int64_t i = 0; i < ne; ++i) {
+          float v;
+          std::memcpy(&v, sb.e_src[t] + i * 4, 4);
+          (*eh)[static_cast<size_t>(d.eoff + i)] = host_to_h16(v, prec);
+        }
+      } else {
+        segs.push_back(CopySeg{pl.E + d.eoff, const_cast<uint8_t*>(sb.e_src[t]), ne * 4});
+      }
+    }
     if (!q || !sb.q_src[t]) continue;
     for (int32_t j = 0; j < d.m; ++j)
       for (int32_t k = 0; k < d.rank; ++k) {
         float v;
         std::memcpy(&v, sb.q_src[t] + (static_cast<size_t>(j) * d.rank + k) * 4, 4);
+        if (prec != kStF32) v = host_from_h16(host_to_h16(v, prec), prec);
         (*q)[static_cast<size_t>(d.qoff) + static_cast<size_t>(j) * pl.R + k] = v;
         if (qt && d.qtoff >= 0)
           (*qt)[static_cast<size_t>(d.qtoff) + static_cast<size_t>(k) * d.mstride + j] = v;
       }
   }
+  if (eh) segs.push_back(CopySeg{pl.Eh, reinterpret_cast<uint8_t*>(eh->data()), pl.e_floats * 2});
   if (q) segs.push_back(CopySeg{pl.Q, reinterpret_cast<uint8_t*>(q->data()), pl.q_floats * 4});
   if (qt) segs.push_back(CopySeg{pl.QT, reinterpret_cast<uint8_t*>(qt->data()), pl.qt_floats * 4});
   pl.q_ready = sb.has_q;
@@ -1381,6 +1526,13 @@ powersgd_status powersgd_state_export(powersgd_state* st, void* host_buf, int64_
   write_snapshot(st, w, &copies);
   powersgd_status r = staged_copy(copies.segs, true, s);
   if (r != POWERSGD_OK) return r;
+  for (const ExportCopies::EPiece& ep : copies.epieces) {
+    const uint16_t* src = copies.ebufs[ep.ebuf].data() + ep.eoff;
+    for (int64_t i = 0; i < ep.count; ++i) {
+      const float v = host_from_h16(src[i], ep.prec);
+      std::memcpy(ep.dst + i * 4, &v, 4);
+    }
+  }
   for (const ExportCopies::QPiece& qp : copies.qpieces) {
     const float* src = copies.qbufs[qp.qbuf].data() + qp.qoff;
     for (int32_t j = 0; j < qp.m; ++j)
@@ -1432,11 +1584,12 @@ powersgd_status powersgd_state_import(powersgd_state* st, const void* host_buf, 
 
   HipDeviceGuard guard(st->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  std::list<std::vector<float>> keep;  // stable addresses while the list grows
+  std::list<std::vector<float>> keep;  // stable addresses while the lists grow
+  std::list<std::vector<uint16_t>> keep16;
   std::vector<CopySeg> segs;
   powersgd_status r = POWERSGD_OK;
   for (SnapBucket& sb : parsed) {
-    r = upload_bucket(hp, sb, s, segs, keep);
+    r = upload_bucket(hp, sb, s, segs, keep, keep16);
     if (r != POWERSGD_OK) break;
   }
   if (r == POWERSGD_OK) r = staged_copy(segs, false, s);

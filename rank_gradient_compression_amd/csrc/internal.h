@@ -100,6 +100,8 @@ struct Pass1Args {
   float* P;
   const float* QT;         // matrix-core ranks: Q^T (B fragments as 16-byte loads)
   double* gram;            // P Gram partials (ranks <= 8: computed here)
+  uint16_t* Eh;            // 16-bit state: E (E's offsets)
+  uint16_t* Mh;            // 16-bit state: M' written here (E's offsets)
   float inv_scale;
   int32_t* found_inf;
 };
@@ -117,6 +119,7 @@ struct Pass2Args {
   float* Q;
   float* QT;               // matrix-core ranks: Q^T, written next to Q (else null)
   float* partial;
+  const uint16_t* Mh;      // 16-bit state: M' (E's offsets)
   float inv_scale;
   const int32_t* found_inf;
 };
@@ -143,24 +146,41 @@ struct Pass3Args {
   const float* P;
   float* Q;                // vector ranks: written here for tensors split into row blocks
   const float* partial;    // vector ranks: pass-2 partial slots (summed here)
+  uint16_t* Eh;            // 16-bit state: E (E's offsets)
+  const uint16_t* Mh;      // 16-bit state: M' (E's offsets)
   float inv_scale;
   const int32_t* found_inf;
 };
 
-// Launchers (kernels.hip). R is the padded rank (1, 2, 4, 8, 16 or 32).
-hipError_t launch_pass1(int R, bool f16, bool ef, const Pass1Args& a, hipStream_t s);
-hipError_t launch_pass2(int R, bool f16, bool ef, const Pass2Args& a, hipStream_t s);
+// Precision of the state a bucket keeps: kStF32 for the hook on fp32 or fp16 buckets;
+// kStF16 / kStBF16 for the hook wrapped by fp16_compress_wrapper / bf16_compress_wrapper
+// (the bucket stays fp32; M', E, P, Q and M_hat hold 16-bit values, rounded to nearest
+// even where each is formed; P and Q keep fp32 containers).
+constexpr int kStF32 = 0;
+constexpr int kStF16 = 1;
+constexpr int kStBF16 = 2;
+
+// Launchers (kernels.hip). R is the padded rank (1, 2, 4, 8, 16 or 32); st the state
+// precision (a 16-bit state needs R <= 8 and an fp32 bucket).
+hipError_t launch_pass1(int R, bool f16, bool ef, int st, const Pass1Args& a, hipStream_t s);
+hipError_t launch_pass2(int R, bool f16, bool ef, int st, const Pass2Args& a, hipStream_t s);
 hipError_t launch_pass2_reduce(int R, const Pass2ReduceArgs& a, hipStream_t s);
-hipError_t launch_pass3(int R, bool f16, bool ef, const Pass3Args& a, hipStream_t s);
+hipError_t launch_pass3(int R, bool f16, bool ef, int st, const Pass3Args& a, hipStream_t s);
 hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs,
                        const float* base, double* gram, const int32_t* found_inf,
                        hipStream_t s);
 hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, int max_rows, float* base,
                        float* tbase, const double* gram, double eps,
-                       const int32_t* found_inf, hipStream_t s);
+                       const int32_t* found_inf, int st, hipStream_t s);
 hipError_t launch_qinit(int R, const QInitJob* jobs, int njobs, int64_t max_count,
-                        float* Q, uint64_t seed, uint64_t bucket_key, uint64_t epoch,
+                        float* Q, uint64_t seed, uint64_t bucket_key, uint64_t epoch, int st,
                         hipStream_t s);
+// 16-bit state outside the compressed views: x <- x rounded to st's precision, in place
+// over fp32 ranges (the wrapper's cast and cast back).
+hipError_t launch_round_only(const FlatTile* ftiles, int nftiles, void* bucket, int st,
+                             hipStream_t s);
+// dst[i] = the 16-bit state value src[i] as fp32, i < count (introspection of E).
+hipError_t launch_widen16(const uint16_t* src, float* dst, int64_t count, int st, hipStream_t s);
 // Zeroes elements [start, start + count) of a fp32 or fp16 buffer (a fill kernel, so
 // the call can be captured in a graph).
 hipError_t launch_fill_zero(void* base, bool f16, int64_t start, int64_t count, hipStream_t s);

@@ -379,6 +379,90 @@ __device__ __forceinline__ void ld_q4(const float* __restrict__ Q, int c, int va
 }
 
 // Lane geometry of a tile (see TensorDesc): row slot, column group and first column.
+// ------------------------------------------------------- 16-bit state values
+//
+// The wrapped hook keeps M' and E as 16-bit values (binary16 or bfloat16), rounded to
+// nearest even wherever a value is formed; arithmetic stays in fp32.
+
+// bfloat16 bits of x rounded to nearest even: add half an ulp of the result (less one,
+// plus the kept part's lowest bit, which breaks ties toward even) and keep the upper
+// half of the binary32 pattern; overflow carries into the exponent and gives inf. NaN
+// stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <int ST>
+__device__ __forceinline__ uint16_t to_h16(float x) {
+  if constexpr (ST == kStBF16)
+    return f32_to_bf16_bits(x);
+  else
+    return __half_as_ushort(__float2half_rn(x));
+}
+
+template <int ST>
+__device__ __forceinline__ float from_h16(uint32_t h) {
+  if constexpr (ST == kStBF16)
+    return __uint_as_float((h & 0xFFFFu) << 16);
+  else
+    return half_bits_to_float(static_cast<uint16_t>(h & 0xFFFFu));
+}
+
+// x rounded to the state's precision (the identity for an fp32 state).
+template <int ST>
+__device__ __forceinline__ float rnd16(float x) {
+  if constexpr (ST == kStF32)
+    return x;
+  else
+    return from_h16<ST>(to_h16<ST>(x));
+}
+
+// 4 consecutive 16-bit state values of a row (the same access modes as ld_f32x4).
+template <int ST, int LD>
+__device__ __forceinline__ void ld_h4(const uint16_t* p, int valid, float (&x)[4]) {
+  if constexpr (LD == kLdAligned) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    x[0] = from_h16<ST>(v.x);
+    x[1] = from_h16<ST>(v.x >> 16);
+    x[2] = from_h16<ST>(v.y);
+    x[3] = from_h16<ST>(v.y >> 16);
+  } else if constexpr (LD == kLdUnaligned) {
+    const int shift = valid >= 4 ? 0 : 4 - valid;
+    const u32x2u v = *reinterpret_cast<const u32x2u*>(p - shift);
+    const float w[4] = {from_h16<ST>(v[0]), from_h16<ST>(v[0] >> 16), from_h16<ST>(v[1]),
+                        from_h16<ST>(v[1] >> 16)};
+    shift_down4(w, shift, x);
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const uint16_t v = p[min(a, valid - 1)];
+      x[a] = a < valid ? from_h16<ST>(v) : 0.f;
+    }
+  }
+}
+
+// Rounds 4 values to the state's precision and stores the first `valid` of them.
+template <int ST, int LD>
+__device__ __forceinline__ void st_h4(uint16_t* p, int valid, const float (&x)[4]) {
+  uint32_t o[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) o[a] = to_h16<ST>(x[a]);
+  if constexpr (LD == kLdAligned) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+  } else {
+    if (LD == kLdUnaligned && valid >= 4) {
+      *reinterpret_cast<u32x2u*>(p) = u32x2u{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+      return;
+    }
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+      if (a < valid) p[a] = static_cast<uint16_t>(o[a]);
+  }
+}
+
 struct LaneGeom {
   int lpr;      // lanes per row slot
   int rpw;      // row slots per wavefront
@@ -520,7 +604,7 @@ constexpr int pass1_ng() { return R <= kMaxFusedGramRank ? gram_size<R>() : 1; }
 // LD: how the matrix's rows are loaded (kLdAligned, kLdUnaligned, kLdScalar). The rows
 // of a slot are clamped into the row block, so every load of an iteration is issued
 // before any is used; the results of clamped duplicate rows are discarded.
-template <int R, int U, bool F16, bool EF, int LD>
+template <int R, int U, bool F16, bool EF, int LD, int ST>
 __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDesc& d,
                                            const Tile& t, float* red,
                                            double (*gred)[pass1_ng<R>()]) {
@@ -569,7 +653,26 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
         ld_grad4<F16, LD>(args.bucket, d.boff + rbase[u] + c, valid, args.inv_scale, x[u], rb);
         if constexpr (F16) bad |= (rok[u] && rb) ? 1 : 0;
       }
-      if constexpr (EF) {
+      if constexpr (ST != kStF32) {
+        // the wrapper's cast, then M' = G + E formed in 16 bits and kept for passes 2, 3
+        if constexpr (EF) {
+          float e[U][4];
+#pragma unroll
+          for (int u = 0; u < U; ++u) ld_h4<ST, LD>(args.Eh + d.eoff + rbase[u] + c, valid, e[u]);
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) x[u][a] = rnd16<ST>(rnd16<ST>(x[u][a]) + e[u][a]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) x[u][a] = rnd16<ST>(x[u][a]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (rok[u]) st_h4<ST, LD>(args.Mh + d.eoff + rbase[u] + c, valid, x[u]);
+      } else if constexpr (EF) {
         float e[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) ld_f32x4<LD>(Et + rbase[u] + c, valid, e[u]);
@@ -605,7 +708,7 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
           if (rok[u]) {
             float pr[R];
 #pragma unroll
-            for (int k = 0; k < R; ++k) pr[k] = (k < d.rank) ? acc[u][k] : 0.f;
+            for (int k = 0; k < R; ++k) pr[k] = (k < d.rank) ? rnd16<ST>(acc[u][k]) : 0.f;
             store_p_row<R>(args.P + d.poff, row, pr);
             if constexpr (GRAM) gram_add<R>(gacc, pr);
           }
@@ -634,7 +737,7 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
       for (int k = 0; k < R; ++k) {
         float v = 0.f;
         for (int w = 0; w < wps; ++w) v += red[(i * wps + w) * R + k];
-        pr[k] = (k < d.rank) ? v : 0.f;
+        pr[k] = (k < d.rank) ? rnd16<ST>(v) : 0.f;
       }
       store_p_row<R>(args.P + d.poff, r0 + i, pr);
       if constexpr (GRAM) gram_add<R>(gacc, pr);
@@ -647,7 +750,7 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
     block_sum_to<NG>(gacc, args.gram + d.goff + static_cast<int64_t>(t.a) * NG, gred);
 }
 
-template <int R, int U, bool F16, bool EF>
+template <int R, int U, bool F16, bool EF, int ST>
 __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
   __shared__ float red[kPass1SlotSums * R];
   __shared__ double gred[kThreads / 64][pass1_ng<R>()];
@@ -659,11 +762,11 @@ __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec)
-    pass1_body<R, U, F16, EF, kLdAligned>(args, d, t, red, gred);
+    pass1_body<R, U, F16, EF, kLdAligned, ST>(args, d, t, red, gred);
   else if (d.m >= 4)
-    pass1_body<R, U, F16, EF, kLdUnaligned>(args, d, t, red, gred);
+    pass1_body<R, U, F16, EF, kLdUnaligned, ST>(args, d, t, red, gred);
   else
-    pass1_body<R, U, F16, EF, kLdScalar>(args, d, t, red, gred);
+    pass1_body<R, U, F16, EF, kLdScalar, ST>(args, d, t, red, gred);
 }
 
 // ------------------------------------------------------------ orthogonalization
@@ -828,11 +931,15 @@ __device__ __forceinline__ void orth_transform(int rank, double eps, OrthShared<
 // ----------------------------------------------------------------------- pass 2
 
 // M' at element `off` of a matrix (fp32 with error feedback: the bucket already holds
-// M', written by pass 1; fp16: unscaled gradient plus E).
-template <bool F16, bool EF, int LD>
+// M', written by pass 1; fp16: unscaled gradient plus E; 16-bit state: M' from Mt).
+template <bool F16, bool EF, int LD, int ST = kStF32>
 __device__ __forceinline__ void ld_mprime4(const void* bucket, const float* Et, int64_t boff,
                                            int64_t off, int valid, float inv_scale,
-                                           float (&x)[4]) {
+                                           float (&x)[4], const uint16_t* Mt = nullptr) {
+  if constexpr (ST != kStF32) {
+    ld_h4<ST, LD>(Mt + off, valid, x);  // a 16-bit state keeps M' of pass 1
+    return;
+  }
   bool rb;
   ld_grad4<F16, LD>(bucket, boff + off, valid, inv_scale, x, rb);
   if constexpr (F16 && EF) {
@@ -848,7 +955,7 @@ __device__ __forceinline__ void ld_mprime4(const void* bucket, const float* Et, 
 // once) to its rows, which stay in LDS (sP, rows relative to r0). Tiles of column
 // block 0 also store them as the orthogonalized P. Every workgroup of a matrix takes
 // the same steps in the same order, so they all hold identical rows.
-template <int R, typename Issued>
+template <int R, int ST, typename Issued>
 __device__ __forceinline__ void pass2_orth_rows(const Pass2Args& args, const TensorDesc& d,
                                                 const Tile& t, int r0, int r1,
                                                 OrthShared<R>& sh, float* sP, Issued issued) {
@@ -873,7 +980,7 @@ __device__ __forceinline__ void pass2_orth_rows(const Pass2Args& args, const Ten
         double acc = 0.0;
 #pragma unroll
         for (int l = 0; l < R; ++l) acc += static_cast<double>(praw[i][l]) * sh.T[l][k];
-        pr[k] = static_cast<float>(acc);
+        pr[k] = rnd16<ST>(static_cast<float>(acc));
         sP[(row - r0) * R + k] = pr[k];
       }
       if (t.b == 0) store_p_row<R>(args.Pout + d.poff, row, pr);
@@ -889,7 +996,7 @@ __device__ __forceinline__ void pass2_orth_rows(const Pass2Args& args, const Ten
 // first rows of M' are requested during the orthogonalization prologue, after its own
 // loads (waits count loads in issue order) and before its barriers, which wait on
 // LDS only, so their latency overlaps it.
-template <int R, int U, bool F16, bool EF, int LD, bool WIDE>
+template <int R, int U, bool F16, bool EF, int LD, bool WIDE, int ST>
 __device__ __forceinline__ void pass2_body(const Pass2Args& args, const TensorDesc& d,
                                            const Tile& t, float* red, OrthShared<R>& sh,
                                            float* sP) {
@@ -902,20 +1009,23 @@ __device__ __forceinline__ void pass2_body(const Pass2Args& args, const TensorDe
   const int rw0 = r0 + wave * L.rpw;
   const float* __restrict__ Et = args.E + d.eoff;
   // lanes past the last column load (and then ignore) an in-range group, so the first
-  // loads need no branch and the wait counts stay exact
+  // loads need no branch and the wait counts stay exact: the row's last 4 elements
+  // (m >= 4; valid = 4 keeps the unaligned access from shifting further back) or its
+  // last element (m < 4)
   const int cc = L.col_ok ? L.c : (LD == kLdScalar ? d.m - 1 : d.m - 4);
-  const int vv = L.col_ok ? L.valid : 1;
+  const int vv = L.col_ok ? L.valid : (LD == kLdScalar ? 1 : 4);
   float x[U][4];
   auto load_rows = [&](int rw) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int rowc = min(rw + u * stride + L.slot, r1 - 1);
-      ld_mprime4<F16, EF, LD>(args.bucket, Et, d.boff, static_cast<int64_t>(rowc) * d.m + cc,
-                               vv, args.inv_scale, x[u]);
+      ld_mprime4<F16, EF, LD, ST>(args.bucket, Et, d.boff,
+                                   static_cast<int64_t>(rowc) * d.m + cc, vv, args.inv_scale,
+                                   x[u], ST != kStF32 ? args.Mh + d.eoff : nullptr);
     }
   };
   // the first rows of M' queue behind the loads of P rows and Gram partials
-  pass2_orth_rows<R>(args, d, t, r0, r1, sh, sP, [&] { load_rows(rw0); });
+  pass2_orth_rows<R, ST>(args, d, t, r0, r1, sh, sP, [&] { load_rows(rw0); });
   float acc[4][R];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -972,7 +1082,7 @@ __device__ __forceinline__ void pass2_body(const Pass2Args& args, const TensorDe
 #pragma unroll
           for (int k = 0; k < R; ++k)
             Qt[static_cast<int64_t>(L.c + a) * R + k] =
-                (k < d.rank) ? acc[a][k] + mine[a * R + k] : 0.f;
+                (k < d.rank) ? rnd16<ST>(acc[a][k] + mine[a * R + k]) : 0.f;
         }
     }
     return;
@@ -988,7 +1098,7 @@ __device__ __forceinline__ void pass2_body(const Pass2Args& args, const TensorDe
   }
 }
 
-template <int R, int U, bool F16, bool EF>
+template <int R, int U, bool F16, bool EF, int ST>
 __global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
   if (F16 && *args.found_inf) return;
   __shared__ float red[64 * 4 * R];
@@ -997,13 +1107,13 @@ __global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec && d.lpr == 64)
-    pass2_body<R, U, F16, EF, kLdAligned, true>(args, d, t, red, sh, sP);
+    pass2_body<R, U, F16, EF, kLdAligned, true, ST>(args, d, t, red, sh, sP);
   else if (d.vec)
-    pass2_body<R, U, F16, EF, kLdAligned, false>(args, d, t, red, sh, sP);
+    pass2_body<R, U, F16, EF, kLdAligned, false, ST>(args, d, t, red, sh, sP);
   else if (d.m >= 4)
-    pass2_body<R, U, F16, EF, kLdUnaligned, false>(args, d, t, red, sh, sP);
+    pass2_body<R, U, F16, EF, kLdUnaligned, false, ST>(args, d, t, red, sh, sP);
   else
-    pass2_body<R, U, F16, EF, kLdScalar, false>(args, d, t, red, sh, sP);
+    pass2_body<R, U, F16, EF, kLdScalar, false, ST>(args, d, t, red, sh, sP);
 }
 
 // Q of the tensors with several row blocks: the partial slots of a column block summed
@@ -1089,13 +1199,20 @@ __device__ void f16_unscale_range(const FlatTile ft, void* bucket, float inv_sca
     h[i] = __half_as_ushort(__float2half_rn(half_bits_to_float(h[i]) * inv_scale));
 }
 
+// The wrapper's cast to 16 bits and back, in place over an fp32 range.
+template <int ST>
+__device__ void round_range(const FlatTile ft, void* bucket) {
+  float* x = static_cast<float*>(bucket) + ft.start;
+  for (int64_t i = threadIdx.x; i < ft.len; i += blockDim.x) x[i] = rnd16<ST>(x[i]);
+}
+
 // Q for the lane's 4 columns when pass 2 split the matrix into several row blocks
 // (vector ranks): the partial slots of the column block are summed here instead of in
 // a kernel of their own. Wavefront w adds slots w, w + 4, ... in order; the four
 // sums are added in wavefront order through LDS (qred: 4 x 4R x 64 floats), so
 // every workgroup of the column block gets the same Q. Row block 0 stores it as the
 // warm-start Q.
-template <int R>
+template <int R, int ST>
 __device__ __forceinline__ void pass3_q_from_partials(const Pass3Args& args, const TensorDesc& d,
                                                       const Tile& t, const LaneGeom& L,
                                                       int lane, int wave, float* qred,
@@ -1137,7 +1254,7 @@ __device__ __forceinline__ void pass3_q_from_partials(const Pass3Args& args, con
     float v = qred[f * 64 + lane];
 #pragma unroll
     for (int w = 1; w < 4; ++w) v += qred[(w * F + f) * 64 + lane];
-    q[f / R][f % R] = v;
+    q[f / R][f % R] = rnd16<ST>(v);
   }
   if (t.a == 0 && wave == 0 && L.slot == 0 && L.col_ok) {
     float* Qt = args.Q + d.qoff;
@@ -1153,7 +1270,7 @@ __device__ __forceinline__ void pass3_q_from_partials(const Pass3Args& args, con
 
 // M_hat = P Q^T into the bucket and E = M' - M_hat over one tile. All loads of an
 // iteration come from rows clamped into the tile; stores are kept to real rows.
-template <int R, int U, bool F16, bool EF, int LD, bool WIDE>
+template <int R, int U, bool F16, bool EF, int LD, bool WIDE, int ST>
 __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDesc& d,
                                            const Tile& t, float* qred) {
   const int lane = threadIdx.x & 63;
@@ -1161,7 +1278,7 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
   const LaneGeom L = tile_geom<WIDE>(d, t.b, lane);
   float q[4][R];
   if (d.nrb > 1) {
-    pass3_q_from_partials<R>(args, d, t, L, lane, wave, qred, q);
+    pass3_q_from_partials<R, ST>(args, d, t, L, lane, wave, qred, q);
   } else {
     load_q_rows<R>(args.Q + d.qoff, L.c, d.m, q);
   }
@@ -1177,8 +1294,10 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int rowc = min(rw + u * stride + L.slot, r1 - 1);
-      ld_mprime4<F16, EF, LD>(args.bucket, Et, d.boff, static_cast<int64_t>(rowc) * d.m + L.c,
-                               L.valid, args.inv_scale, x[u]);
+      ld_mprime4<F16, EF, LD, ST>(args.bucket, Et, d.boff,
+                                   static_cast<int64_t>(rowc) * d.m + L.c, L.valid,
+                                   args.inv_scale, x[u],
+                                   ST != kStF32 ? args.Mh + d.eoff : nullptr);
       if constexpr (WIDE)
         load_p_row_uniform<R>(Pt, __builtin_amdgcn_readfirstlane(rowc), p[u]);
       else
@@ -1195,7 +1314,7 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
         float s = 0.f;
 #pragma unroll
         for (int k = 0; k < R; ++k) s += p[u][k] * q[a][k];
-        mh[a] = s;
+        mh[a] = rnd16<ST>(s);
       }
       if constexpr (F16)
         st_f16x4<LD>(static_cast<uint16_t*>(args.bucket) + d.boff + off, L.valid, mh);
@@ -1205,31 +1324,36 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
         float e[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) e[a] = x[u][a] - mh[a];
-        st_f32x4<LD>(Et + off, L.valid, e);
+        if constexpr (ST != kStF32)
+          st_h4<ST, LD>(args.Eh + d.eoff + off, L.valid, e);  // rounds E to 16 bits
+        else
+          st_f32x4<LD>(Et + off, L.valid, e);
       }
     }
   }
 }
 
-template <int R, int U, bool F16, bool EF>
+template <int R, int U, bool F16, bool EF, int ST>
 __global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
   if (F16 && *args.found_inf) return;
   __shared__ float qred[4 * 4 * R * 64];
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
     if constexpr (F16)
       f16_unscale_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.inv_scale);
+    else if constexpr (ST != kStF32)
+      round_range<ST>(args.ftiles[blockIdx.x - args.ntiles], args.bucket);
     return;
   }
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec && d.lpr == 64)
-    pass3_body<R, U, F16, EF, kLdAligned, true>(args, d, t, qred);
+    pass3_body<R, U, F16, EF, kLdAligned, true, ST>(args, d, t, qred);
   else if (d.vec)
-    pass3_body<R, U, F16, EF, kLdAligned, false>(args, d, t, qred);
+    pass3_body<R, U, F16, EF, kLdAligned, false, ST>(args, d, t, qred);
   else if (d.m >= 4)
-    pass3_body<R, U, F16, EF, kLdUnaligned, false>(args, d, t, qred);
+    pass3_body<R, U, F16, EF, kLdUnaligned, false, ST>(args, d, t, qred);
   else
-    pass3_body<R, U, F16, EF, kLdScalar, false>(args, d, t, qred);
+    pass3_body<R, U, F16, EF, kLdScalar, false, ST>(args, d, t, qred);
 }
 
 // ------------------------------------------------- matrix-core passes (R = 16, 32)
@@ -1849,7 +1973,7 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-template <int R>
+template <int R, int ST>
 __global__ void __launch_bounds__(kThreads)
     k_orth(const OrthJob* __restrict__ jobs, float* __restrict__ base, float* __restrict__ tbase,
            const double* __restrict__ gram, double eps, const int32_t* __restrict__ found_inf) {
@@ -1861,8 +1985,8 @@ __global__ void __launch_bounds__(kThreads)
   if (row_begin >= j.rows) return;
   orth_gram_sum<R>(j, gram, sh, [] {});
   orth_transform<R>(j.rank, eps, sh);
-  // 3. P <- P T in fp64, rounded once to fp32, for this workgroup's rows; several
-  //    rows are loaded before any is transformed.
+  // 3. P <- P T in fp64, rounded to fp32 (and to the state's 16 bits), for this
+  //    workgroup's rows; several rows are loaded before any is transformed.
   float* X = base + j.off;
   const int row_end = min(j.rows, row_begin + kOrthRows);
   constexpr int B = R <= 8 ? 4 : 1;
@@ -1888,9 +2012,9 @@ __global__ void __launch_bounds__(kThreads)
         double s = 0.0;
 #pragma unroll
         for (int l = 0; l < R; ++l) s += static_cast<double>(x[b][l]) * sh.T[l][k];
-        dst[k] = static_cast<float>(s);
-        if (j.toff >= 0)
-          tbase[j.toff + static_cast<int64_t>(k) * j.tstride + row] = static_cast<float>(s);
+        const float v = rnd16<ST>(static_cast<float>(s));
+        dst[k] = v;
+        if (j.toff >= 0) tbase[j.toff + static_cast<int64_t>(k) * j.tstride + row] = v;
       }
     }
   }
@@ -1935,6 +2059,7 @@ __device__ __forceinline__ void box_muller(uint64_t we, uint64_t wo, double& z0,
   z1 = radius * sin(angle);
 }
 
+template <int ST>
 __global__ void __launch_bounds__(256)
     k_qinit(const QInitJob* __restrict__ jobs, float* __restrict__ Q, int R, uint64_t seed,
             uint64_t bucket_key, uint64_t epoch) {
@@ -1954,7 +2079,7 @@ __global__ void __launch_bounds__(256)
       if (e < count) {
         const int64_t row = e / j.rank;
         const int k = static_cast<int>(e % j.rank);
-        Q[j.qoff + row * R + k] = static_cast<float>(z[a]);
+        Q[j.qoff + row * R + k] = rnd16<ST>(static_cast<float>(z[a]));  // binary32 draw
       }
     }
   }
@@ -1984,6 +2109,18 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+template <int ST>
+__global__ void __launch_bounds__(256) k_round16(const FlatTile* __restrict__ ft, void* bucket) {
+  round_range<ST>(ft[blockIdx.x], bucket);
+}
+
+template <int ST>
+__global__ void __launch_bounds__(256)
+    k_widen16(const uint16_t* __restrict__ src, float* __restrict__ dst, int64_t count) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < count; i += gridDim.x * 256ll)
+    dst[i] = from_h16<ST>(src[i]);
+}
+
 // ------------------------------------------------------------------ dispatch
 
 // Rows loaded per lane before use, by rank (register budget).
@@ -1991,59 +2128,94 @@ template <int R> constexpr int unroll1() { return pass1_unroll(R); }
 template <int R> constexpr int unroll2() { return R <= 4 ? PSGD_PASS2_ROWS : (R <= 8 ? 4 : 1); }
 template <int R> constexpr int unroll3() { return R <= 8 ? PSGD_PASS3_ROWS : 1; }
 
+// Kernel K<..., F16, EF, ST> for the run-time (f16, ef, st); a 16-bit state has an fp32
+// bucket. Returns false for a combination that does not exist.
+#define PSGD_VARIANTS(LAUNCH)                                   \
+  if (st == kStF16) {                                           \
+    if (f16) return false;                                      \
+    if (ef) LAUNCH(false, true, kStF16);                        \
+    else LAUNCH(false, false, kStF16);                          \
+  } else if (st == kStBF16) {                                   \
+    if (f16) return false;                                      \
+    if (ef) LAUNCH(false, true, kStBF16);                       \
+    else LAUNCH(false, false, kStBF16);                         \
+  } else {                                                      \
+    if (f16 && ef) LAUNCH(true, true, kStF32);                  \
+    else if (f16) LAUNCH(true, false, kStF32);                  \
+    else if (ef) LAUNCH(false, true, kStF32);                   \
+    else LAUNCH(false, false, kStF32);                          \
+  }                                                             \
+  return true;
+
 template <int R>
-hipError_t pass1_r(bool f16, bool ef, const Pass1Args& a, hipStream_t s) {
+bool pass1_vec(bool f16, bool ef, int st, const Pass1Args& a, dim3 grid, hipStream_t s) {
+  constexpr int U = unroll1<R>();
+#define PSGD_L1(F, E, S) k_pass1<R, U, F, E, S><<<grid, kThreads, 0, s>>>(a)
+  PSGD_VARIANTS(PSGD_L1)
+#undef PSGD_L1
+}
+
+template <int R>
+bool pass2_vec(bool f16, bool ef, int st, const Pass2Args& a, dim3 grid, hipStream_t s) {
+  constexpr int U = unroll2<R>();
+#define PSGD_L2(F, E, S) k_pass2<R, U, F, E, S><<<grid, kThreads, 0, s>>>(a)
+  PSGD_VARIANTS(PSGD_L2)
+#undef PSGD_L2
+}
+
+template <int R>
+bool pass3_vec(bool f16, bool ef, int st, const Pass3Args& a, dim3 grid, hipStream_t s) {
+  constexpr int U = unroll3<R>();
+#define PSGD_L3(F, E, S) k_pass3<R, U, F, E, S><<<grid, kThreads, 0, s>>>(a)
+  PSGD_VARIANTS(PSGD_L3)
+#undef PSGD_L3
+}
+
+template <int R>
+hipError_t pass1_r(bool f16, bool ef, int st, const Pass1Args& a, hipStream_t s) {
   const dim3 grid(a.ntiles + (f16 ? a.nftiles : 0));
   if (grid.x == 0) return hipSuccess;
   if constexpr (R >= kMfmaMinRank) {
+    if (st != kStF32) return hipErrorInvalidValue;  // 16-bit states: vector ranks only
     if (f16 && ef) k_pass1_mfma<R, true, true><<<grid, kThreads, 0, s>>>(a);
     else if (f16) k_pass1_mfma<R, true, false><<<grid, kThreads, 0, s>>>(a);
     else if (ef) k_pass1_mfma<R, false, true><<<grid, kThreads, 0, s>>>(a);
     else k_pass1_mfma<R, false, false><<<grid, kThreads, 0, s>>>(a);
   } else {
-    constexpr int U = unroll1<R>();
-    if (f16 && ef) k_pass1<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
-    else if (f16) k_pass1<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
-    else if (ef) k_pass1<R, U, false, true><<<grid, kThreads, 0, s>>>(a);
-    else k_pass1<R, U, false, false><<<grid, kThreads, 0, s>>>(a);
+    if (!pass1_vec<R>(f16, ef, st, a, grid, s)) return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int R>
-hipError_t pass2_r(bool f16, bool ef, const Pass2Args& a, hipStream_t s) {
+hipError_t pass2_r(bool f16, bool ef, int st, const Pass2Args& a, hipStream_t s) {
   if (a.ntiles == 0) return hipSuccess;
   const dim3 grid(a.ntiles);
   if constexpr (R >= kMfmaMinRank) {
+    if (st != kStF32) return hipErrorInvalidValue;
     if (f16 && ef) k_pass2_mfma<R, true, true><<<grid, kThreads, 0, s>>>(a);
     else if (f16) k_pass2_mfma<R, true, false><<<grid, kThreads, 0, s>>>(a);
     else if (ef) k_pass2_mfma<R, false, true><<<grid, kThreads, 0, s>>>(a);
     else k_pass2_mfma<R, false, false><<<grid, kThreads, 0, s>>>(a);
   } else {
-    constexpr int U = unroll2<R>();
-    if (f16 && ef) k_pass2<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
-    else if (f16) k_pass2<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
-    else if (ef) k_pass2<R, U, false, true><<<grid, kThreads, 0, s>>>(a);
-    else k_pass2<R, U, false, false><<<grid, kThreads, 0, s>>>(a);
+    if (!pass2_vec<R>(f16, ef, st, a, grid, s)) return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int R>
-hipError_t pass3_r(bool f16, bool ef, const Pass3Args& a, hipStream_t s) {
-  const dim3 grid(a.ntiles + (f16 ? a.nftiles : 0));
+hipError_t pass3_r(bool f16, bool ef, int st, const Pass3Args& a, hipStream_t s) {
+  // extra workgroups: fp16 unscale, or the 16-bit state's cast, of uncompressed views
+  const dim3 grid(a.ntiles + ((f16 || st != kStF32) ? a.nftiles : 0));
   if (grid.x == 0) return hipSuccess;
   if constexpr (R >= kMfmaMinRank) {
+    if (st != kStF32) return hipErrorInvalidValue;
     if (f16 && ef) k_pass3_mfma<R, true, true><<<grid, kThreads, 0, s>>>(a);
     else if (f16) k_pass3_mfma<R, true, false><<<grid, kThreads, 0, s>>>(a);
     else if (ef) k_pass3_mfma<R, false, true><<<grid, kThreads, 0, s>>>(a);
     else k_pass3_mfma<R, false, false><<<grid, kThreads, 0, s>>>(a);
   } else {
-    constexpr int U = unroll3<R>();
-    if (f16 && ef) k_pass3<R, U, true, true><<<grid, kThreads, 0, s>>>(a);
-    else if (f16) k_pass3<R, U, true, false><<<grid, kThreads, 0, s>>>(a);
-    else if (ef) k_pass3<R, U, false, true><<<grid, kThreads, 0, s>>>(a);
-    else k_pass3<R, U, false, false><<<grid, kThreads, 0, s>>>(a);
+    if (!pass3_vec<R>(f16, ef, st, a, grid, s)) return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -2063,12 +2235,12 @@ using namespace kern;
     default: return hipErrorInvalidValue;           \
   }
 
-hipError_t launch_pass1(int R, bool f16, bool ef, const Pass1Args& a, hipStream_t s) {
-  PSGD_RANK_SWITCH(R, return pass1_r<RR>(f16, ef, a, s))
+hipError_t launch_pass1(int R, bool f16, bool ef, int st, const Pass1Args& a, hipStream_t s) {
+  PSGD_RANK_SWITCH(R, return pass1_r<RR>(f16, ef, st, a, s))
 }
 
-hipError_t launch_pass2(int R, bool f16, bool ef, const Pass2Args& a, hipStream_t s) {
-  PSGD_RANK_SWITCH(R, return pass2_r<RR>(f16, ef, a, s))
+hipError_t launch_pass2(int R, bool f16, bool ef, int st, const Pass2Args& a, hipStream_t s) {
+  PSGD_RANK_SWITCH(R, return pass2_r<RR>(f16, ef, st, a, s))
 }
 
 hipError_t launch_pass2_reduce(int R, const Pass2ReduceArgs& a, hipStream_t s) {
@@ -2079,8 +2251,8 @@ hipError_t launch_pass2_reduce(int R, const Pass2ReduceArgs& a, hipStream_t s) {
   })
 }
 
-hipError_t launch_pass3(int R, bool f16, bool ef, const Pass3Args& a, hipStream_t s) {
-  PSGD_RANK_SWITCH(R, return pass3_r<RR>(f16, ef, a, s))
+hipError_t launch_pass3(int R, bool f16, bool ef, int st, const Pass3Args& a, hipStream_t s) {
+  PSGD_RANK_SWITCH(R, return pass3_r<RR>(f16, ef, st, a, s))
 }
 
 hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs,
@@ -2095,23 +2267,58 @@ hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs
 
 hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, int max_rows, float* base,
                        float* tbase, const double* gram, double eps,
-                       const int32_t* found_inf, hipStream_t s) {
+                       const int32_t* found_inf, int st, hipStream_t s) {
   if (njobs == 0) return hipSuccess;
   const dim3 grid((max_rows + kOrthRows - 1) / kOrthRows, njobs);
   PSGD_RANK_SWITCH(R, {
-    k_orth<RR><<<grid, kThreads, 0, s>>>(jobs, base, tbase, gram, eps, found_inf);
+    if (st == kStF16)
+      k_orth<RR, kStF16><<<grid, kThreads, 0, s>>>(jobs, base, tbase, gram, eps, found_inf);
+    else if (st == kStBF16)
+      k_orth<RR, kStBF16><<<grid, kThreads, 0, s>>>(jobs, base, tbase, gram, eps, found_inf);
+    else
+      k_orth<RR, kStF32><<<grid, kThreads, 0, s>>>(jobs, base, tbase, gram, eps, found_inf);
     return hipGetLastError();
   })
 }
 
 hipError_t launch_qinit(int R, const QInitJob* jobs, int njobs, int64_t max_count,
-                        float* Q, uint64_t seed, uint64_t bucket_key, uint64_t epoch,
+                        float* Q, uint64_t seed, uint64_t bucket_key, uint64_t epoch, int st,
                         hipStream_t s) {
   if (njobs == 0) return hipSuccess;
   const int64_t blocks = ((max_count + 3) / 4 + 255) / 256;
   const dim3 grid(static_cast<unsigned>(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks)),
                   static_cast<unsigned>(njobs));
-  k_qinit<<<grid, 256, 0, s>>>(jobs, Q, R, seed, bucket_key, epoch);
+  if (st == kStF16)
+    k_qinit<kStF16><<<grid, 256, 0, s>>>(jobs, Q, R, seed, bucket_key, epoch);
+  else if (st == kStBF16)
+    k_qinit<kStBF16><<<grid, 256, 0, s>>>(jobs, Q, R, seed, bucket_key, epoch);
+  else
+    k_qinit<kStF32><<<grid, 256, 0, s>>>(jobs, Q, R, seed, bucket_key, epoch);
+  return hipGetLastError();
+}
+
+hipError_t launch_widen16(const uint16_t* src, float* dst, int64_t count, int st, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  const int64_t blocks = (count + 255) / 256;
+  const dim3 grid(static_cast<unsigned>(blocks < 1024 ? blocks : 1024));
+  if (st == kStF16)
+    k_widen16<kStF16><<<grid, 256, 0, s>>>(src, dst, count);
+  else if (st == kStBF16)
+    k_widen16<kStBF16><<<grid, 256, 0, s>>>(src, dst, count);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_round_only(const FlatTile* ftiles, int nftiles, void* bucket, int st,
+                             hipStream_t s) {
+  if (nftiles == 0) return hipSuccess;
+  if (st == kStF16)
+    k_round16<kStF16><<<dim3(nftiles), 256, 0, s>>>(ftiles, bucket);
+  else if (st == kStBF16)
+    k_round16<kStBF16><<<dim3(nftiles), 256, 0, s>>>(ftiles, bucket);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

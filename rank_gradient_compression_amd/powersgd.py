@@ -22,6 +22,7 @@ POWERSGD_ERR_UNSUPPORTED = -5
 POWERSGD_ERR_NOT_FOUND = -6
 POWERSGD_F32 = 0
 POWERSGD_F16 = 1
+POWERSGD_BF16 = 2
 POWERSGD_MAX_NDIM = 8
 POWERSGD_MAX_RANK = 32
 POWERSGD_NUM_KERNELS = 8
@@ -34,7 +35,7 @@ EXPORTED = (
     "powersgd_copy_error", "powersgd_get_stats", "powersgd_set_timing",
     "powersgd_get_kernel_times", "powersgd_kernel_name", "powersgd_classify_view",
     "powersgd_batched_side", "powersgd_compress_bucket_batched",
-    "powersgd_state_export", "powersgd_state_import",
+    "powersgd_state_export", "powersgd_state_import", "powersgd_compress_bucket_wrapped",
 )
 
 
@@ -90,6 +91,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "powersgd_compress_bucket": (i32, [P, i64, i32, P, i32, i64,
                                            ctypes.POINTER(powersgd_view), i32, f32, P, P]),
         "powersgd_batched_side": (i64, [i64]),
+        "powersgd_compress_bucket_wrapped": (i32, [P, i64, i32, P, i32, i64,
+                                                   ctypes.POINTER(powersgd_view), i32, P]),
         "powersgd_compress_bucket_batched": (i32, [P, i64, i32, P, i32, i64, i64, f32, P, P]),
         "powersgd_status_string": (ctypes.c_char_p, [i32]),
         "powersgd_last_error": (ctypes.c_char_p, []),
@@ -173,6 +176,16 @@ def powersgd_compress_bucket(state, bucket_index: int, is_last: bool, bucket_ptr
         state, int(bucket_index), int(bool(is_last)), ctypes.c_void_p(bucket_ptr), int(dtype),
         int(numel), arr, len(views), float(inv_loss_scale),
         ctypes.c_void_p(found_inf_ptr) if found_inf_ptr else None,
+        ctypes.c_void_p(stream) if stream else None))
+
+
+def powersgd_compress_bucket_wrapped(state, bucket_index: int, is_last: bool,
+                                     bucket_ptr: int, compute_dtype: int, numel: int, views,
+                                     stream: Optional[int]) -> None:
+    arr = make_views(views)
+    _check(load_library().powersgd_compress_bucket_wrapped(
+        state, int(bucket_index), int(bool(is_last)), ctypes.c_void_p(bucket_ptr),
+        int(compute_dtype), int(numel), arr, len(views),
         ctypes.c_void_p(stream) if stream else None))
 
 
@@ -335,6 +348,21 @@ class PowerSGDState:
         powersgd_compress_bucket(self._state, bucket_index, is_last, bucket.data_ptr(), dtype,
                                  bucket.numel(), list(views), inv_loss_scale, fi,
                                  self._stream_handle(stream))
+
+    def compress_bucket_wrapped(self, bucket, views: Sequence[Tuple[int, Sequence[int]]],
+                                compute_dtype: str = "f16", bucket_index: int = 0,
+                                is_last: bool = True, stream=None) -> None:
+        """powerSGD_hook under fp16_compress_wrapper ("f16") or bf16_compress_wrapper
+        ("bf16") on a float32 bucket, in place."""
+        import torch
+        if not bucket.is_cuda or not bucket.is_contiguous() or bucket.dim() != 1:
+            raise ValueError("bucket must be a contiguous 1-D device tensor")
+        if bucket.dtype != torch.float32:
+            raise TypeError("the wrapped hook takes a float32 bucket")
+        dt = {"f16": POWERSGD_F16, "bf16": POWERSGD_BF16}[compute_dtype]
+        powersgd_compress_bucket_wrapped(self._state, bucket_index, is_last, bucket.data_ptr(),
+                                         dt, bucket.numel(), list(views),
+                                         self._stream_handle(stream))
 
     def compress_bucket_batched(self, buffer, numel: Optional[int] = None,
                                 bucket_index: int = 0, is_last: bool = True,

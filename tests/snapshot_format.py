@@ -2,7 +2,8 @@
 and the oracle's own readers): header fields, bucket records with their views, and the
 E and Q arrays of every compressed view. The compressed views and their ranks are
 decided by `classify(shape) -> None | (n, m, k)` for per-layer buckets; a batched
-bucket's one s x s view has rank min(r, s)."""
+bucket's one s x s view has rank min(r, s). The record's variant word keeps the
+batched flag in bit 0 and a 16-bit state's precision in bits 8-9."""
 from __future__ import annotations
 
 import struct
@@ -24,7 +25,8 @@ def parse(blob: bytes, classify: Callable[[Tuple[int, ...]], Optional[Tuple[int,
     ef = bool(head["flags"] & 1)
     buckets = []
     for _ in range(head["nbuckets"]):
-        idx, numel, batched, has_q, nviews = BUCKET.unpack_from(blob, pos)
+        idx, numel, variant, has_q, nviews = BUCKET.unpack_from(blob, pos)
+        batched = variant & 1
         pos += BUCKET.size
         views = []
         for _ in range(nviews):
@@ -33,7 +35,7 @@ def parse(blob: bytes, classify: Callable[[Tuple[int, ...]], Optional[Tuple[int,
             shp = struct.unpack_from(f"<{ndim}q", blob, pos)
             pos += 8 * ndim
             views.append((off, tuple(shp)))
-        rec = {"index": idx, "numel": numel, "batched": batched, "has_q": has_q,
+        rec = {"index": idx, "numel": numel, "variant": variant, "has_q": has_q,
                "views": views, "E": {}, "Q": {}}
         for vi, (_, shp) in enumerate(views):
             if batched:

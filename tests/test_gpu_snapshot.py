@@ -120,7 +120,7 @@ def test_export_matches_the_oracle(name, views, kw):
     assert head_g == head_o
     assert len(bk_g) == len(bk_o) == 2
     for bg, bo in zip(bk_g, bk_o):
-        for key in ("index", "numel", "batched", "has_q", "views"):
+        for key in ("index", "numel", "variant", "has_q", "views"):
             assert bg[key] == bo[key], key
         assert sorted(bg["E"]) == sorted(bo["E"]) and sorted(bg["Q"]) == sorted(bo["Q"])
         res = last[bg["index"]]

@@ -1,0 +1,206 @@
+"""GPU parity of the wrapped hook (fp16_compress_wrapper / bf16_compress_wrapper around
+powerSGD_hook) against the oracle, through the C ABI, element by element.
+
+Tolerance: both sides round every materialized tensor to 16 bits; they differ only in
+how the value before each rounding was accumulated (fp32 in the kernels, fp64 in the
+oracle), which moves a small fraction of results by one 16-bit ulp. The relative
+Frobenius difference of each quantity is held to 4u (u = 2^-11 for binary16, 2^-8 for
+bfloat16); the cast of uncompressed views is bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import log, oracle_hparams, rel_fro
+from rank_gradient_compression_amd import PowerSGDError, PowerSGDState
+from rank_gradient_compression_amd import powersgd as api
+from snapshot_format import parse
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f16": 4 * 2.0 ** -11, "bf16": 4 * 2.0 ** -8}
+
+# aligned rows (300 x 260), a conv view, rows of 77 floats (unaligned access), rows of
+# 3 floats (scalar access), vectors and a matrix the rate test keeps whole
+VIEWS = [(0, (64, 3, 3, 3)), (1728, (64,)), (1792, (4, 4)), (1808, (300, 260)),
+         (79808, (130, 77)), (89818, (400, 3)), (91018, (7,))]
+
+
+def _numel(views):
+    return max(off + int(np.prod(shp)) for off, shp in views)
+
+
+def _hp(**kw):
+    base = dict(matrix_approximation_rank=2, start_powerSGD_iter=0, min_compression_rate=2.0,
+                use_error_feedback=True, warm_start=True, orthogonalization_epsilon=0.0,
+                random_seed=3, compression_stats_logging_frequency=0)
+    base.update(kw)
+    return base
+
+
+def _bucket(views, step, seed, rank, scale=1.0):
+    out = torch.zeros(_numel(views), dtype=torch.float64)
+    k = max(16, 2 * rank)
+    for vi, (off, shp) in enumerate(views):
+        size = int(np.prod(shp))
+        gs = torch.Generator().manual_seed(seed * 7919 + step * 131 + vi)
+        if len(shp) < 2:
+            out[off:off + size] = torch.randn(size, generator=gs, dtype=torch.float64)
+            continue
+        n, m = shp[0], size // shp[0]
+        g = torch.Generator().manual_seed(seed * 104729 + vi)
+        u = torch.randn(n, k, generator=g, dtype=torch.float64)
+        v = torch.randn(m, k, generator=g, dtype=torch.float64)
+        w = torch.tensor([1.0 / (j + 1) for j in range(k)], dtype=torch.float64)
+        out[off:off + size] = ((u * w) @ v.T + 0.01 * torch.randn(
+            n, m, generator=gs, dtype=torch.float64)).reshape(-1)
+    return (out * scale).float()
+
+
+def _run(hp, dt, views, steps, seed=0, bucket_index=0, check_factors=True):
+    st = PowerSGDState(**hp)
+    orc = oracle.OracleState(oracle_hparams(hp))
+    tol = TOL[dt]
+    r = hp["matrix_approximation_rank"]
+    for t in range(steps):
+        x = _bucket(views, t, seed, r)
+        dev = x.cuda()
+        st.compress_bucket_wrapped(dev, views, dt, bucket_index=bucket_index)
+        res = orc.compress_bucket_wrapped(x.numpy(), views, dt, bucket_index=bucket_index)
+        torch.cuda.synchronize()
+        out = dev.cpu().numpy()
+        worst = {}
+        if res.passthrough:
+            np.testing.assert_array_equal(out, res.output)
+            log(f"  step {t}: pass-through cast, bit-exact")
+            continue
+        dec = st.decisions(bucket_index, len(views))
+        assert dec == [int(v.compressed) for v in res.views]
+        for vi, ((off, shp), vr) in enumerate(zip(views, res.views)):
+            size = int(np.prod(shp))
+            if not vr.compressed:
+                np.testing.assert_array_equal(out[off:off + size], res.output[off:off + size])
+                continue
+            n, m, k = st.view_info(bucket_index, vi)
+            assert (n, m, k) == (vr.n, vr.m, vr.rank)
+            errs = {"Mhat": rel_fro(out[off:off + size].reshape(n, m), vr.m_hat)}
+            if check_factors:
+                p, q = st.factors(bucket_index, vi)
+                p, q = p.double().cpu().numpy(), q.double().cpu().numpy()
+                errs["P"] = rel_fro(p, vr.p)
+                errs["Q"] = rel_fro(q, vr.q)
+                # the factors the library keeps are 16-bit values
+                rnd = oracle.round_f16 if dt == "f16" else oracle.round_bf16
+                assert np.all(rnd(p) == p) and np.all(rnd(q) == q)
+            if vr.error is not None:
+                e = st.error(bucket_index, vi).double().cpu().numpy()
+                ne, nm = np.linalg.norm(vr.error), np.linalg.norm(vr.m_prime)
+                errs["E"] = rel_fro(e, vr.error, nm if ne < 1e-3 * nm else None)
+            for key, v in errs.items():
+                worst[key] = max(worst.get(key, 0.0), v)
+                assert v <= tol, (t, vi, key, v, (n, m, k))
+        log(f"  step {t}: " + ", ".join(f"{k}={v:.2e}" for k, v in worst.items())
+            + f" (tol {tol:.1e})")
+    return st, orc
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("rank", [1, 2, 4, 8])
+def test_wrapped_parity(dt, rank):
+    log(f"case: wrapped hook {dt}, rank {rank}")
+    _run(_hp(matrix_approximation_rank=rank), dt, VIEWS, steps=4, seed=rank)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("ef,warm", [(False, True), (True, False), (False, False)])
+def test_wrapped_parity_without_feedback_or_warm_start(dt, ef, warm):
+    log(f"case: wrapped hook {dt}, error feedback {ef}, warm start {warm}")
+    _run(_hp(use_error_feedback=ef, warm_start=warm), dt, VIEWS, steps=3, seed=7)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_wrapped_pass_through_and_statistics(dt):
+    log(f"case: wrapped hook {dt}, start_powerSGD_iter 2")
+    hp = _hp(start_powerSGD_iter=2)
+    st, orc = _run(hp, dt, VIEWS, steps=4, seed=11)
+    assert st.stats() == (orc.iteration, orc.numel_in, orc.numel_comm)
+
+
+def test_wrapped_layout_and_argument_errors():
+    log("case: wrapped hook errors")
+    views = VIEWS
+    x = _bucket(views, 0, 1, 2).cuda()
+    st = PowerSGDState(**_hp())
+    st.compress_bucket_wrapped(x.clone(), views, "f16", bucket_index=0)
+    with pytest.raises(PowerSGDError) as ei:
+        st.compress_bucket_wrapped(x.clone(), views, "bf16", bucket_index=0)
+    assert ei.value.status == api.POWERSGD_ERR_LAYOUT_CHANGED
+    with pytest.raises(PowerSGDError) as ei:
+        st.compress_bucket(x.clone(), views, bucket_index=0)
+    assert ei.value.status == api.POWERSGD_ERR_LAYOUT_CHANGED
+    hi = PowerSGDState(**_hp(matrix_approximation_rank=16))
+    with pytest.raises(PowerSGDError) as ei:
+        hi.compress_bucket_wrapped(x.clone(), views, "f16")
+    assert ei.value.status == api.POWERSGD_ERR_UNSUPPORTED
+    lib = api.load_library()
+    arr = api.make_views(views)
+    assert lib.powersgd_compress_bucket_wrapped(st._state, 5, 1, x.data_ptr(), 0, x.numel(), arr,
+                                                len(views), None) == api.POWERSGD_ERR_INVALID_ARG
+    with pytest.raises(TypeError):
+        st.compress_bucket_wrapped(x.double(), views, "f16")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_wrapped_overflow_propagates_like_the_oracle(dt):
+    """Values beyond the 16-bit range become inf in the cast; the compressed view then
+    holds non-finite values exactly where the oracle's does."""
+    log(f"case: wrapped hook {dt}, overflow in the cast")
+    views = [(0, (64, 48)), (3072, (9,))]
+    hp = _hp(matrix_approximation_rank=1)
+    st = PowerSGDState(**hp)
+    orc = oracle.OracleState(oracle_hparams(hp))
+    x = _bucket(views, 0, 5, 1)
+    big = 1e5 if dt == "f16" else 3.4e38  # finite in fp32, beyond the 16-bit range
+    x[100] = big
+    x[3075] = -big
+    dev = x.cuda()
+    st.compress_bucket_wrapped(dev, views, dt)
+    res = orc.compress_bucket_wrapped(x.numpy(), views, dt)
+    out = dev.cpu().numpy()
+    np.testing.assert_array_equal(np.isfinite(out), np.isfinite(res.output))
+    assert not np.isfinite(out[3075]) and not np.all(np.isfinite(out[:3072]))
+
+
+@pytest.mark.parametrize("dt,code", [("f16", 1), ("bf16", 2)])
+def test_wrapped_snapshot_matches_the_oracle_and_resumes(dt, code):
+    log(f"case: snapshot of a wrapped {dt} bucket")
+    hp = _hp()
+    st, orc = _run(hp, dt, VIEWS, steps=2, seed=13, bucket_index=3, check_factors=False)
+    cls_hp = oracle_hparams(hp)
+
+    def cls(shp):
+        nm = oracle.matrix_view(shp)
+        if nm is None:
+            return None
+        n, m = nm
+        k = oracle.effective_rank(n, m, cls_hp.matrix_approximation_rank)
+        return (n, m, k) if oracle.should_compress(n, m, k, cls_hp.min_compression_rate) else None
+
+    blob = bytes(st.export_state())
+    head_g, bg = parse(blob, cls)
+    head_o, bo = parse(orc.export_state(), cls)
+    assert head_g == head_o
+    assert bg[0]["variant"] == bo[0]["variant"] == code << 8
+    for vi in bg[0]["E"]:
+        assert rel_fro(bg[0]["E"][vi], bo[0]["E"][vi]) <= TOL[dt] * 10
+        assert rel_fro(bg[0]["Q"][vi], bo[0]["Q"][vi]) <= TOL[dt]
+    # resuming from the library's own snapshot is bitwise identical
+    b = PowerSGDState(**hp)
+    b.import_state(blob)
+    assert bytes(b.export_state()) == blob
+    x = _bucket(VIEWS, 2, 13, 2).cuda()
+    xa, xb = x.clone(), x.clone()
+    st.compress_bucket_wrapped(xa, VIEWS, dt, bucket_index=3)
+    b.compress_bucket_wrapped(xb, VIEWS, dt, bucket_index=3)
+    torch.cuda.synchronize()
+    assert torch.equal(xa.view(torch.int32), xb.view(torch.int32))
