@@ -99,6 +99,8 @@ def cpu_baseline(cfg, budget_s: float = 20.0):
         t0 = time.perf_counter()
         if cfg.batched:
             st.compress_bucket_batched(arr, inv_loss_scale=1.0 / scale)
+        elif cfg.wrap:
+            st.compress_bucket_wrapped(arr, views, cfg.wrap)
         else:
             st.compress_bucket(arr, views, inv_loss_scale=1.0 / scale)
         times.append(time.perf_counter() - t0)
@@ -179,6 +181,8 @@ def main() -> int:
             st.compress_bucket_batched(pool[i % pool_n], numel=cfg.numel, inv_loss_scale=inv,
                                        found_inf=found if cfg.dtype == "f16" else None,
                                        stream=stream)
+        elif cfg.wrap:
+            st.compress_bucket_wrapped(pool[i % pool_n], views, cfg.wrap, stream=stream)
         else:
             st.compress_bucket(pool[i % pool_n], views, inv_loss_scale=inv,
                                found_inf=found if cfg.dtype == "f16" else None, stream=stream)
@@ -258,21 +262,28 @@ def main() -> int:
         for _, shp in views:
             comp, n, m, _r = api.powersgd_classify_view(hp_c, shp)
             comp_elems += n * m if comp else 0
-    per_elt = 28 if cfg.dtype == "f32" else 24
-    algo_bytes = comp_elems * per_elt + (0 if cfg.dtype == "f32" or cfg.batched else
-                                         (cfg.numel - comp_elems) * 6)
+    if cfg.wrap:
+        # fp32 bucket, 16-bit M' and E: 8 + 2 + 8 per compressed element; the cast of
+        # the other views reads and writes fp32
+        algo_bytes = comp_elems * 18 + (cfg.numel - comp_elems) * 8
+    else:
+        per_elt = 28 if cfg.dtype == "f32" else 24
+        algo_bytes = comp_elems * per_elt + (0 if cfg.dtype == "f32" or cfg.batched else
+                                             (cfg.numel - comp_elems) * 6)
     step_frac = algo_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": cfg.wrap or "f32",
         "data": "synthetic (seeded low-rank + noise gradients, model-shaped views)",
         "config": {"workload": cfg.name, "bucket_bytes": bucket_bytes,
                    "views": len(views), "compressed_elements": comp_elems,
                    "variant": ("batched: one %d x %d padded matrix" % (side, side)
-                               if cfg.batched else "per-layer"),
+                               if cfg.batched else
+                               "%s_compress_wrapper(powerSGD_hook), fp32 bucket" % cfg.wrap
+                               if cfg.wrap else "per-layer"),
                    "matrix_approximation_rank": cfg.hparams["matrix_approximation_rank"],
                    "step_hbm_roofline_frac": round(step_frac, 4),
                    "measured_copy_GBps": round(copy_gbs, 1),

@@ -32,6 +32,7 @@ class WorkloadConfig:
     seed: int = 0
     notes: str = ""
     batched: bool = False         # the whole bucket as one zero-padded square matrix
+    wrap: str = ""                # "f16" / "bf16": the hook under fp16/bf16_compress_wrapper
 
     def views(self):
         return packed_views(self.shapes)
@@ -126,6 +127,16 @@ CONFIGS: Dict[int, WorkloadConfig] = {
         notes="the ResNet-50 bucket (same values as the per-layer workload) viewed as one "
               "4315 x 4315 matrix, 4313 padded zeros; rank 1 as the pages recommend for "
               "this variant"),
+    6: WorkloadConfig(
+        name="resnet50-bucket-r2-bf16-wrapper", shapes=_resnet50_shapes(),
+        hparams=_hp(matrix_approximation_rank=2), steps=10,
+        spectrum_rank=8, spectrum_power=1.0, seed=1001, wrap="bf16",
+        notes="the ResNet-50 fp32 bucket under bf16_compress_wrapper(powerSGD_hook)"),
+    7: WorkloadConfig(
+        name="bert-large-bucket-r4-fp16-wrapper", shapes=_bert_large_shapes(),
+        hparams=_hp(matrix_approximation_rank=4, batch_tensors_with_same_shape=True),
+        steps=20, spectrum_rank=64, spectrum_power=1.0, seed=1002, wrap="f16",
+        notes="the BERT-large fp32 bucket under fp16_compress_wrapper(powerSGD_hook)"),
 }
 
 
@@ -138,4 +149,4 @@ def shrink_config(cfg: WorkloadConfig, shapes: List[Shape], steps: int = None,
         spectrum_power=cfg.spectrum_power, noise_std=cfg.noise_std, dtype=cfg.dtype,
         amp_prescale=cfg.amp_prescale, loss_scale=cfg.loss_scale,
         inf_probability=cfg.inf_probability, forced_inf_steps=cfg.forced_inf_steps,
-        seed=cfg.seed, notes=cfg.notes, batched=cfg.batched)
+        seed=cfg.seed, notes=cfg.notes, batched=cfg.batched, wrap=cfg.wrap)
