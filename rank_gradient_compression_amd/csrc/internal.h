@@ -198,6 +198,16 @@ hipError_t launch_unscale_only(const FlatTile* ftiles, int nftiles, void* bucket
 #ifndef PSGD_PASS3_ROWS
 #define PSGD_PASS3_ROWS 8  // pass 3 rows in flight per lane, padded ranks <= 8
 #endif
+// Rows in flight for a 16-bit state (its M' and E accesses are 8 bytes per lane).
+#ifndef PSGD_PASS1_ROWS_H
+#define PSGD_PASS1_ROWS_H PSGD_PASS1_ROWS
+#endif
+#ifndef PSGD_PASS2_ROWS_H
+#define PSGD_PASS2_ROWS_H PSGD_PASS2_ROWS
+#endif
+#ifndef PSGD_PASS3_ROWS_H
+#define PSGD_PASS3_ROWS_H PSGD_PASS3_ROWS
+#endif
 #ifndef PSGD_TILES_PER_BUCKET
 #define PSGD_TILES_PER_BUCKET 4096  // work items aimed at per pass (before clamping)
 #endif

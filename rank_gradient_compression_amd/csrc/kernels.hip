@@ -2124,9 +2124,18 @@ __global__ void __launch_bounds__(256)
 // ------------------------------------------------------------------ dispatch
 
 // Rows loaded per lane before use, by rank (register budget).
-template <int R> constexpr int unroll1() { return pass1_unroll(R); }
-template <int R> constexpr int unroll2() { return R <= 4 ? PSGD_PASS2_ROWS : (R <= 8 ? 4 : 1); }
-template <int R> constexpr int unroll3() { return R <= 8 ? PSGD_PASS3_ROWS : 1; }
+template <int R, int ST = kStF32>
+constexpr int unroll1() {
+  return ST == kStF32 ? pass1_unroll(R) : (R <= 4 ? PSGD_PASS1_ROWS_H : 1);
+}
+template <int R, int ST = kStF32>
+constexpr int unroll2() {
+  return R <= 4 ? (ST == kStF32 ? PSGD_PASS2_ROWS : PSGD_PASS2_ROWS_H) : (R <= 8 ? 4 : 1);
+}
+template <int R, int ST = kStF32>
+constexpr int unroll3() {
+  return R <= 8 ? (ST == kStF32 ? PSGD_PASS3_ROWS : PSGD_PASS3_ROWS_H) : 1;
+}
 
 // Kernel K<..., F16, EF, ST> for the run-time (f16, ef, st); a 16-bit state has an fp32
 // bucket. Returns false for a combination that does not exist.
@@ -2149,24 +2158,21 @@ template <int R> constexpr int unroll3() { return R <= 8 ? PSGD_PASS3_ROWS : 1; 
 
 template <int R>
 bool pass1_vec(bool f16, bool ef, int st, const Pass1Args& a, dim3 grid, hipStream_t s) {
-  constexpr int U = unroll1<R>();
-#define PSGD_L1(F, E, S) k_pass1<R, U, F, E, S><<<grid, kThreads, 0, s>>>(a)
+#define PSGD_L1(F, E, S) k_pass1<R, unroll1<R, S>(), F, E, S><<<grid, kThreads, 0, s>>>(a)
   PSGD_VARIANTS(PSGD_L1)
 #undef PSGD_L1
 }
 
 template <int R>
 bool pass2_vec(bool f16, bool ef, int st, const Pass2Args& a, dim3 grid, hipStream_t s) {
-  constexpr int U = unroll2<R>();
-#define PSGD_L2(F, E, S) k_pass2<R, U, F, E, S><<<grid, kThreads, 0, s>>>(a)
+#define PSGD_L2(F, E, S) k_pass2<R, unroll2<R, S>(), F, E, S><<<grid, kThreads, 0, s>>>(a)
   PSGD_VARIANTS(PSGD_L2)
 #undef PSGD_L2
 }
 
 template <int R>
 bool pass3_vec(bool f16, bool ef, int st, const Pass3Args& a, dim3 grid, hipStream_t s) {
-  constexpr int U = unroll3<R>();
-#define PSGD_L3(F, E, S) k_pass3<R, U, F, E, S><<<grid, kThreads, 0, s>>>(a)
+#define PSGD_L3(F, E, S) k_pass3<R, unroll3<R, S>(), F, E, S><<<grid, kThreads, 0, s>>>(a)
   PSGD_VARIANTS(PSGD_L3)
 #undef PSGD_L3
 }

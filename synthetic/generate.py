@@ -8,7 +8,8 @@ feedback and warm start see a persistent gradient direction) and the noise is
 new. A vector view holds N(0, 1) values drawn afresh every step.
 
 fp16 workloads store RNE(G * amp_prescale * loss_scale) and may receive one
-injected +inf at a seeded position on selected steps.
+injected +inf at a seeded position on selected steps; fp32 workloads store
+G * grad_scale (1 unless a workload sets it).
 
 Values depend on (workload seed, view, role, step) and on the device type
 (torch's CPU and GPU generators produce different streams); a given test or
@@ -94,7 +95,7 @@ class BucketGenerator:
         cfg = self.cfg
         g = self.gradient(step)
         if cfg.dtype == "f32":
-            return g
+            return g * cfg.grad_scale if cfg.grad_scale != 1.0 else g
         scale = cfg.loss_scale if loss_scale is None else loss_scale
         h = (g * (cfg.amp_prescale * scale)).to(torch.float16)
         if inject_inf is None:

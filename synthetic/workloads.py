@@ -33,6 +33,7 @@ class WorkloadConfig:
     notes: str = ""
     batched: bool = False         # the whole bucket as one zero-padded square matrix
     wrap: str = ""                # "f16" / "bf16": the hook under fp16/bf16_compress_wrapper
+    grad_scale: float = 1.0       # f32 only: gradient multiplier (a power of two: exact)
 
     def views(self):
         return packed_views(self.shapes)
@@ -136,7 +137,10 @@ CONFIGS: Dict[int, WorkloadConfig] = {
         name="bert-large-bucket-r4-fp16-wrapper", shapes=_bert_large_shapes(),
         hparams=_hp(matrix_approximation_rank=4, batch_tensors_with_same_shape=True),
         steps=20, spectrum_rank=64, spectrum_power=1.0, seed=1002, wrap="f16",
-        notes="the BERT-large fp32 bucket under fp16_compress_wrapper(powerSGD_hook)"),
+        grad_scale=2.0 ** -10,
+        notes="the BERT-large fp32 bucket, gradients x 2^-10, under "
+              "fp16_compress_wrapper(powerSGD_hook); unscaled, the warm-started P = M'Q "
+              "(about sigma^2, 1e6 here) would overflow binary16"),
 }
 
 
@@ -149,4 +153,5 @@ def shrink_config(cfg: WorkloadConfig, shapes: List[Shape], steps: int = None,
         spectrum_power=cfg.spectrum_power, noise_std=cfg.noise_std, dtype=cfg.dtype,
         amp_prescale=cfg.amp_prescale, loss_scale=cfg.loss_scale,
         inf_probability=cfg.inf_probability, forced_inf_steps=cfg.forced_inf_steps,
-        seed=cfg.seed, notes=cfg.notes, batched=cfg.batched, wrap=cfg.wrap)
+        seed=cfg.seed, notes=cfg.notes, batched=cfg.batched, wrap=cfg.wrap,
+        grad_scale=cfg.grad_scale)

@@ -9,7 +9,9 @@ import pytest
 import torch
 
 import oracle
-from parity import TOL, BucketParity, StepReport, TensorTrack, compare_sampled, log, numel
+from parity import (TOL, TOL_WRAPPED, WRAPPED_ORACLE_STEPS, BucketParity, StepReport,
+                    TensorTrack, TensorTrackWrapped, check_wrapped_properties, compare_sampled,
+                    log, numel, oracle_hparams, rel_fro)
 from rank_gradient_compression_amd import PowerSGDState
 from synthetic import CONFIGS, BucketGenerator
 
@@ -100,3 +102,78 @@ def test_gpt_bucket_full_sampled_views():
     cfg = CONFIGS[3]
     log(f"case: {cfg.name} full size, {cfg.steps} steps, sampled views")
     _sampled(cfg, sample_views=[0, 3, 4, 39])
+
+
+def test_resnet50_bucket_bf16_wrapper_full_every_view_every_step():
+    cfg = CONFIGS[6]
+    log(f"case: {cfg.name} full size, {cfg.steps} steps, whole-bucket oracle for the first "
+        f"{WRAPPED_ORACLE_STEPS}, properties at every step")
+    views = cfg.views()
+    gen = BucketGenerator(cfg, "cuda")
+    hp = dict(cfg.hparams)
+    hp["compression_stats_logging_frequency"] = 0
+    gpu = PowerSGDState(**hp)
+    orc = oracle.OracleState(oracle_hparams(hp))
+    tol = TOL_WRAPPED[cfg.wrap]
+    e_prev = {}
+    for step in range(cfg.steps):
+        bucket = gen.bucket(step)
+        host = bucket.cpu().numpy()
+        gpu.compress_bucket_wrapped(bucket, views, cfg.wrap)
+        with_oracle = step < WRAPPED_ORACLE_STEPS
+        res = orc.compress_bucket_wrapped(host, views, cfg.wrap) if with_oracle else None
+        out = bucket.cpu().numpy()
+        rep = StepReport(step=step)
+        dec = gpu.decisions(0, len(views))
+        for vi, (off, shp) in enumerate(views):
+            size = numel(shp)
+            if not dec[vi]:  # the cast alone: bit-exact with numpy's / torch's
+                want = torch.from_numpy(host[off:off + size]).to(torch.bfloat16).float().numpy()
+                np.testing.assert_array_equal(out[off:off + size], want)
+                continue
+            e_prev[vi] = check_wrapped_properties(gpu, 0, vi, cfg.wrap, host[off:off + size],
+                                                  e_prev.get(vi), out[off:off + size])
+            if with_oracle:
+                compare_sampled(gpu, 0, vi, res.views[vi], bucket[off:off + size], tol, rep)
+        log(f"  step {step}: " + (", ".join(f"{k}={v:.2e}" for k, v in rep.worst.items())
+                                  if with_oracle else "properties hold"))
+
+
+def test_bert_large_bucket_fp16_wrapper_full_sampled_views():
+    cfg = CONFIGS[7]
+    log(f"case: {cfg.name} full size, {cfg.steps} steps, sampled views (oracle for the "
+        f"first {WRAPPED_ORACLE_STEPS} steps, properties at every step)")
+    views = cfg.views()
+    sample_views = [0, 4, 5, 369]
+    gen = BucketGenerator(cfg, "cuda")
+    hp = dict(cfg.hparams)
+    hp["compression_stats_logging_frequency"] = 0
+    gpu = PowerSGDState(**hp)
+    tol = TOL_WRAPPED[cfg.wrap]
+    tracks = {}
+    e_prev = {}
+    for step in range(cfg.steps):
+        bucket = gen.bucket(step)
+        host_in = {vi: bucket[off:off + numel(shp)].cpu() for vi, (off, shp) in
+                   enumerate(views) if vi in sample_views}
+        vec_in = [(off, bucket[off:off + numel(shp)].clone()) for off, shp in views
+                  if len(shp) < 2]
+        gpu.compress_bucket_wrapped(bucket, views, cfg.wrap)
+        torch.cuda.synchronize()
+        rep = StepReport(step=step)
+        for vi in sample_views:
+            off, shp = views[vi]
+            n, m, r = gpu.view_info(0, vi)
+            got = bucket[off:off + numel(shp)]
+            e_prev[vi] = check_wrapped_properties(gpu, 0, vi, cfg.wrap, host_in[vi].numpy(),
+                                                  e_prev.get(vi), got.cpu().numpy())
+            if step < WRAPPED_ORACLE_STEPS:
+                if vi not in tracks:
+                    tracks[vi] = TensorTrackWrapped(hp, vi, n, m, r, cfg.wrap)
+                vr = tracks[vi].step(host_in[vi].double().numpy(), step)
+                compare_sampled(gpu, 0, vi, vr, got, tol, rep)
+        for off, v in vec_in:  # vectors: the fp16 cast and back
+            got = bucket[off:off + v.numel()]
+            assert torch.equal(got, v.half().float())
+        log(f"  step {step}: " + (", ".join(f"{k}={v:.2e}" for k, v in rep.worst.items())
+                                  if rep.worst else "properties hold"))

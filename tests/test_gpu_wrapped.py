@@ -11,14 +11,13 @@ import pytest
 import torch
 
 import oracle
+from parity import TOL_WRAPPED as TOL
 from parity import log, oracle_hparams, rel_fro
 from rank_gradient_compression_amd import PowerSGDError, PowerSGDState
 from rank_gradient_compression_amd import powersgd as api
 from snapshot_format import parse
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"f16": 4 * 2.0 ** -11, "bf16": 4 * 2.0 ** -8}
 
 # aligned rows (300 x 260), a conv view, rows of 77 floats (unaligned access), rows of
 # 3 floats (scalar access), vectors and a matrix the rate test keeps whole
