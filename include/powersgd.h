@@ -162,11 +162,9 @@ POWERSGD_API powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_
  *                  layout change. No loss scaling: values beyond the 16-bit range
  *                  become inf and propagate.
  *
- * Before start_powerSGD_iter the call is the cast to 16 bits and back. The matrix-core
- * ranks are not supported here: matrix_approximation_rank must be <= 8.
+ * Before start_powerSGD_iter the call is the cast to 16 bits and back.
  * Errors: INVALID_ARG (as for powersgd_compress_bucket; compute_dtype not F16/BF16),
- * UNSUPPORTED (rank above 8), LAYOUT_CHANGED, OOM, HIP; returned before anything is
- * enqueued.
+ * LAYOUT_CHANGED, OOM, HIP; returned before anything is enqueued.
  */
 POWERSGD_API powersgd_status powersgd_compress_bucket_wrapped(powersgd_state* st,
                                                  int64_t bucket_index, int32_t is_last,

@@ -735,9 +735,6 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     auto pl = std::make_unique<BucketPlan>();
     powersgd_status b = build_plan(hp, numel, batched, std::move(keys), *pl);
     if (b != POWERSGD_OK) return b;
-    if (prec != kStF32 && pl->R > kMaxFusedGramRank)
-      return fail(POWERSGD_ERR_UNSUPPORTED,
-                  "the 16-bit wrapped hook supports matrix_approximation_rank <= 8");
     pl->st = prec;
     b = allocate_plan(*pl, ef, s);
     if (b != POWERSGD_OK) return b;
@@ -856,7 +853,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
       b.QT = pl.QT;
       b.found_inf = f16 ? found_inf_dev : nullptr;
       r = timed_launch(st, s, K_PASS2R, 0.0, "pass 2 reduce",
-                       [&] { return launch_pass2_reduce(R, b, s); });
+                       [&] { return launch_pass2_reduce(R, prec, b, s); });
       if (r != POWERSGD_OK) return r;
     }
   }
@@ -947,9 +944,6 @@ powersgd_status powersgd_compress_bucket_wrapped(powersgd_state* st, int64_t buc
     prec = kStBF16;
   else
     return fail(POWERSGD_ERR_INVALID_ARG, "compute_dtype must be F16 or BF16");
-  if (st->hp.matrix_approximation_rank > kMaxFusedGramRank)
-    return fail(POWERSGD_ERR_UNSUPPORTED,
-                "the 16-bit wrapped hook supports matrix_approximation_rank <= 8");
   std::vector<ViewKey> keys;
   powersgd_status vs = validate_views(views, nviews, numel, keys);
   if (vs != POWERSGD_OK) return vs;
@@ -1421,8 +1415,6 @@ powersgd_status read_bucket(const powersgd_hparams& hp, SnapReader& rd, int64_t 
   powersgd_status b = build_plan(hp, numel, batched != 0, std::move(keys), *out.plan);
   if (b != POWERSGD_OK) return b;
   BucketPlan& pl = *out.plan;
-  if (prec != kStF32 && pl.R > kMaxFusedGramRank)
-    return fail(POWERSGD_ERR_UNSUPPORTED, "snapshot: 16-bit state above rank 8");
   pl.st = prec;
   if (has_q && pl.tensors.empty()) return snap_bad("warm-start Q on a bucket with no compressed view");
   out.has_q = has_q != 0;

@@ -458,7 +458,7 @@ __device__ __forceinline__ void st_h4(uint16_t* p, int valid, const float (&x)[4
       return;
     }
 #pragma unroll
-    for (int a = 0; a < 3; ++a)
+    for (int a = 0; a < 4; ++a)
       if (a < valid) p[a] = static_cast<uint16_t>(o[a]);
   }
 }
@@ -1121,7 +1121,7 @@ __global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
 // a slot and, when there are more threads than float4, the row blocks (subset s takes
 // row blocks s, s + NS, ...), so one round of loads covers many row blocks. The
 // subsets are then added in subset order through LDS.
-template <int R>
+template <int R, int ST>
 __global__ void __launch_bounds__(kReduceThreads) k_pass2_reduce(Pass2ReduceArgs args) {
   if (args.found_inf != nullptr && *args.found_inf) return;
   constexpr int F4 = kColBlock * R / 4;
@@ -1183,7 +1183,7 @@ __global__ void __launch_bounds__(kReduceThreads) k_pass2_reduce(Pass2ReduceArgs
       const int col = t.b * kColBlock + f / R;
       const int k = f % R;
       if (col < d.m) {
-        const float q = (k < d.rank) ? vals[a] : 0.f;
+        const float q = (k < d.rank) ? rnd16<ST>(vals[a]) : 0.f;
         Qt[static_cast<int64_t>(col) * R + k] = q;
         if (args.QT != nullptr) args.QT[d.qtoff + static_cast<int64_t>(k) * d.mstride + col] = q;
       }
@@ -1377,7 +1377,7 @@ __device__ __forceinline__ mfma_f4 mfma16(float a, float b, mfma_f4 c) {
 // order through LDS at the end (red: 4 x NT x 4 x 64 floats). VEC: rows are 16-byte
 // aligned, so all loads of a chunk are issued from clamped addresses before any is
 // used, and invalid lanes are masked after.
-template <int R, bool F16, bool EF, bool VEC>
+template <int R, bool F16, bool EF, bool VEC, int ST>
 __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const TensorDesc& d,
                                                 const Tile& t, int lane, int wave, float* red) {
   constexpr int NT = R / 16;
@@ -1412,7 +1412,10 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
         bool rb;
         load_grad4_vec<F16>(args.bucket, d.boff + off, args.inv_scale, x[u], rb);
         if (ok[u] && rb) bad = 1;
-        if constexpr (EF) load_f4(Et + off, e[u]);
+        if constexpr (EF && ST != kStF32)
+          ld_h4<ST, kLdAligned>(args.Eh + d.eoff + off, 4, e[u]);
+        else if constexpr (EF)
+          load_f4(Et + off, e[u]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           load_f4(QTt + static_cast<int64_t>(16 * nt + cl) * d.mstride + colc, b[u][nt]);
@@ -1425,7 +1428,10 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
         if (ok[u]) {
           const int64_t off = static_cast<int64_t>(row) * m + col;
           load_grad4<F16>(args.bucket, d.boff + off, false, m - col, args.inv_scale, x[u], bad);
-          if constexpr (EF) load_f32x4(Et + off, false, m - col, e[u]);
+          if constexpr (EF && ST != kStF32)
+            ld_h4<ST, kLdScalar>(args.Eh + d.eoff + off, m - col, e[u]);
+          else if constexpr (EF)
+            load_f32x4(Et + off, false, m - col, e[u]);
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -1449,10 +1455,23 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         float v = x[u][a];
-        if constexpr (EF) v += e[u][a];
+        if constexpr (ST != kStF32) {
+          v = rnd16<ST>(v);  // the wrapper's cast; M' = G + E formed in 16 bits
+          if constexpr (EF) v = rnd16<ST>(v + e[u][a]);
+        } else if constexpr (EF) {
+          v += e[u][a];
+        }
         x[u][a] = ok[u] ? v : 0.f;
       }
-      if constexpr (EF && !F16) {
+      if constexpr (ST != kStF32) {
+        if (ok[u]) {
+          if constexpr (VEC)
+            st_h4<ST, kLdAligned>(args.Mh + d.eoff + static_cast<int64_t>(row) * m + col, 4, x[u]);
+          else
+            st_h4<ST, kLdScalar>(args.Mh + d.eoff + static_cast<int64_t>(row) * m + col, m - col,
+                                 x[u]);
+        }
+      } else if constexpr (EF && !F16) {
         if (ok[u]) store_f32x4(Mt + static_cast<int64_t>(row) * m + col, VEC, m - col, x[u]);
       }
     }
@@ -1482,7 +1501,8 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
       for (int w = 1; w < 4; ++w) sum += red[((w * NT + nt) * 4 + v) * 64 + lane];
       const int prow = r0 + 4 * h + v;
       const int k = 16 * nt + cl;
-      if (prow < r1) args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? sum : 0.f;
+      if (prow < r1)
+        args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? rnd16<ST>(sum) : 0.f;
     }
   }
 }
@@ -1496,7 +1516,7 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
 // next chunk's rows are requested before the MFMA phase of this one.
 constexpr int kPass1TileStride = kColBlock + 4;  // LDS row stride (floats), padded
 
-template <int R, bool F16, bool EF>
+template <int R, bool F16, bool EF, int ST>
 __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const TensorDesc& d,
                                                 const Tile& t, int lane, int wave, float* red,
                                                 float* tile) {
@@ -1531,7 +1551,10 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
       bool rb;
       load_grad4_vec<F16>(args.bucket, d.boff + rbase[i] + colc, args.inv_scale, xg[i], rb);
       if (rok[i] && k0 + 4 * lane < m && rb) bad = 1;
-      if constexpr (EF) load_f4(Et + rbase[i] + colc, xe[i]);
+      if constexpr (EF && ST != kStF32)
+        ld_h4<ST, kLdAligned>(args.Eh + d.eoff + rbase[i] + colc, 4, xe[i]);
+      else if constexpr (EF)
+        load_f4(Et + rbase[i] + colc, xe[i]);
     }
   };
   load_rows(0);
@@ -1544,10 +1567,17 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         float x = xg[i][a];
-        if constexpr (EF) x += xe[i][a];
+        if constexpr (ST != kStF32) {
+          x = rnd16<ST>(x);
+          if constexpr (EF) x = rnd16<ST>(x + xe[i][a]);
+        } else if constexpr (EF) {
+          x += xe[i][a];
+        }
         v[a] = (rok[i] && cok) ? x : 0.f;
       }
-      if constexpr (EF && !F16) {
+      if constexpr (ST != kStF32) {
+        if (rok[i] && cok) st_h4<ST, kLdAligned>(args.Mh + d.eoff + rbase[i] + col, 4, v);
+      } else if constexpr (EF && !F16) {
         if (rok[i] && cok) store_f32x4(Mt + rbase[i] + col, true, 4, v);
       }
       *reinterpret_cast<float4*>(tile + (4 * wave + i) * LS + 4 * lane) =
@@ -1596,12 +1626,13 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
       for (int w = 1; w < 4; ++w) sum += red[((w * NT + nt) * 4 + v) * 64 + lane];
       const int prow = r0 + 4 * h + v;
       const int k = 16 * nt + cl;
-      if (prow < r1) args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? sum : 0.f;
+      if (prow < r1)
+        args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? rnd16<ST>(sum) : 0.f;
     }
   }
 }
 
-template <int R, bool F16, bool EF>
+template <int R, bool F16, bool EF, int ST>
 __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
   static_assert(kMfmaPass1Rows == 16, "a workgroup owns one 16-row MFMA group");
   __shared__ float red[4 * (R / 16) * 4 * 64];
@@ -1616,15 +1647,15 @@ __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec)
-    pass1_mfma_rows<R, F16, EF>(args, d, t, lane, wave, red, tile);
+    pass1_mfma_rows<R, F16, EF, ST>(args, d, t, lane, wave, red, tile);
   else
-    pass1_mfma_body<R, F16, EF, false>(args, d, t, lane, wave, red);
+    pass1_mfma_body<R, F16, EF, false, ST>(args, d, t, lane, wave, red);
 }
 
 // Pass 2, Q = M'^T P: a wavefront owns 64 columns of the tile; lane group h takes row
 // 4 * step + h, lane cl the columns 4cl..4cl+3, so accumulator s holds the output
 // columns c0 + 4i + s (i = MFMA output row).
-template <int R, bool F16, bool EF, bool VEC>
+template <int R, bool F16, bool EF, bool VEC, int ST>
 __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const TensorDesc& d,
                                                 const Tile& t, int lane, int wave) {
   constexpr int NT = R / 16;
@@ -1653,7 +1684,9 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
     for (int u = 0; u < U; ++u) {
       const int row = rr + 4 * u + h;
       const int rowc = min(row, r1 - 1);
-      if constexpr (VEC) {
+      if constexpr (VEC && ST != kStF32) {
+        ld_h4<ST, kLdAligned>(args.Mh + d.eoff + static_cast<int64_t>(rowc) * m + colc, 4, x[u]);
+      } else if constexpr (VEC) {
         const int64_t off = static_cast<int64_t>(rowc) * m + colc;
         bool rb;
         load_grad4_vec<F16>(args.bucket, d.boff + off, args.inv_scale, x[u], rb);
@@ -1665,8 +1698,10 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
         }
       } else {
         if (row < r1 && col_ok) {
-          ld_mprime4<F16, EF, kLdScalar>(args.bucket, Et, d.boff, static_cast<int64_t>(row) * m + col,
-                                     m - col, args.inv_scale, x[u]);
+          ld_mprime4<F16, EF, kLdScalar, ST>(args.bucket, Et, d.boff,
+                                             static_cast<int64_t>(row) * m + col, m - col,
+                                             args.inv_scale, x[u],
+                                             ST != kStF32 ? args.Mh + d.eoff : nullptr);
         } else {
 #pragma unroll
           for (int a = 0; a < 4; ++a) x[u][a] = 0.f;
@@ -1703,7 +1738,7 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
         if (qcol < m) {
           const float val = acc[s4][nt][v];
           if (d.nrb == 1) {
-            const float q = (k < d.rank) ? val : 0.f;
+            const float q = (k < d.rank) ? rnd16<ST>(val) : 0.f;
             Qt[static_cast<int64_t>(qcol) * R + k] = q;
             args.QT[d.qtoff + static_cast<int64_t>(k) * d.mstride + qcol] = q;
           } else {
@@ -1715,7 +1750,7 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
   }
 }
 
-template <int R, bool F16, bool EF>
+template <int R, bool F16, bool EF, int ST>
 __global__ void __launch_bounds__(kThreads) k_pass2_mfma(Pass2Args args) {
   if (F16 && *args.found_inf) return;
   const int lane = threadIdx.x & 63;
@@ -1723,16 +1758,16 @@ __global__ void __launch_bounds__(kThreads) k_pass2_mfma(Pass2Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec)
-    pass2_mfma_body<R, F16, EF, true>(args, d, t, lane, wave);
+    pass2_mfma_body<R, F16, EF, true, ST>(args, d, t, lane, wave);
   else
-    pass2_mfma_body<R, F16, EF, false>(args, d, t, lane, wave);
+    pass2_mfma_body<R, F16, EF, false, ST>(args, d, t, lane, wave);
 }
 
 // Pass 3, M_hat = P Q^T and E = M' - M_hat, computed as (Q P^T)^T so that lane l
 // holds 4 consecutive columns (4h..4h+3) of row cl of each 16 x 16 output block.
 // MFMA K-step kq of lane group h uses rank index h * KQ + kq, so A and B fragments are
 // KQ consecutive floats of a Q row and of a P row.
-template <int R, bool F16, bool EF, bool VEC>
+template <int R, bool F16, bool EF, bool VEC, int ST>
 __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const TensorDesc& d,
                                                 const Tile& t, int lane, int wave) {
   constexpr int KQ = R / 4;
@@ -1776,7 +1811,11 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = c0 + 16 * g + 4 * h;
-        if constexpr (VEC) {
+        if constexpr (VEC && ST != kStF32) {
+          if constexpr (EF)
+            ld_h4<ST, kLdAligned>(args.Mh + d.eoff + static_cast<int64_t>(rowc) * m +
+                                      min(col, m - 4), 4, x[ur][g]);
+        } else if constexpr (VEC) {
           const int64_t off = static_cast<int64_t>(rowc) * m + min(col, m - 4);
           bool rb;
           load_grad4_vec<F16>(args.bucket, d.boff + off, args.inv_scale, x[ur][g], rb);
@@ -1788,8 +1827,10 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
           }
         } else {
           if (row < r1 && col < m)
-            ld_mprime4<F16, EF, kLdScalar>(args.bucket, Et, d.boff, static_cast<int64_t>(row) * m + col,
-                                       m - col, args.inv_scale, x[ur][g]);
+            ld_mprime4<F16, EF, kLdScalar, ST>(args.bucket, Et, d.boff,
+                                               static_cast<int64_t>(row) * m + col, m - col,
+                                               args.inv_scale, x[ur][g],
+                                               ST != kStF32 ? args.Mh + d.eoff : nullptr);
         }
       }
     }
@@ -1804,7 +1845,8 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
         const int col = c0 + 16 * g + 4 * h;
         if (row < r1 && col < m) {
           const int64_t off = static_cast<int64_t>(row) * m + col;
-          float mh[4] = {acc[0], acc[1], acc[2], acc[3]};
+          float mh[4] = {rnd16<ST>(acc[0]), rnd16<ST>(acc[1]), rnd16<ST>(acc[2]),
+                         rnd16<ST>(acc[3])};
           if constexpr (F16)
             store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, VEC, m - col, mh);
           else
@@ -1813,7 +1855,14 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
             float e[4];
 #pragma unroll
             for (int a = 0; a < 4; ++a) e[a] = x[ur][g][a] - mh[a];
-            store_f32x4(Et + off, VEC, m - col, e);
+            if constexpr (ST != kStF32) {
+              if constexpr (VEC)
+                st_h4<ST, kLdAligned>(args.Eh + d.eoff + off, 4, e);
+              else
+                st_h4<ST, kLdScalar>(args.Eh + d.eoff + off, m - col, e);
+            } else {
+              store_f32x4(Et + off, VEC, m - col, e);
+            }
           }
         }
       }
@@ -1830,7 +1879,7 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
 // requested before its MFMAs.
 constexpr int kPass3TileStride = kColBlock + 4;  // LDS row stride (floats), padded
 
-template <int R, bool F16, bool EF>
+template <int R, bool F16, bool EF, int ST>
 __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const TensorDesc& d,
                                                 const Tile& t, int lane, int wave,
                                                 float* tile) {
@@ -1869,8 +1918,10 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
         const int row = min(rr + RW * wave + i, r1 - 1);
-        ld_mprime4<F16, EF, kLdAligned>(args.bucket, Et, d.boff, static_cast<int64_t>(row) * m + crc, 4,
-                                  args.inv_scale, x[i]);
+        ld_mprime4<F16, EF, kLdAligned, ST>(args.bucket, Et, d.boff,
+                                            static_cast<int64_t>(row) * m + crc, 4,
+                                            args.inv_scale, x[i],
+                                            ST != kStF32 ? args.Mh + d.eoff : nullptr);
       }
     }
     float pb[UR][KQ];
@@ -1902,7 +1953,7 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
       const int row = rr + RW * wave + i;
       if (row < r1 && cr_ok) {
         const float4 v = *reinterpret_cast<const float4*>(tile + (RW * wave + i) * LS + 4 * lane);
-        const float mh[4] = {v.x, v.y, v.z, v.w};
+        const float mh[4] = {rnd16<ST>(v.x), rnd16<ST>(v.y), rnd16<ST>(v.z), rnd16<ST>(v.w)};
         const int64_t off = static_cast<int64_t>(row) * m + cr;
         if constexpr (F16)
           store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, true, 4, mh);
@@ -1912,7 +1963,10 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
           float e[4];
 #pragma unroll
           for (int a = 0; a < 4; ++a) e[a] = x[i][a] - mh[a];
-          store_f32x4(Et + off, true, 4, e);
+          if constexpr (ST != kStF32)
+            st_h4<ST, kLdAligned>(args.Eh + d.eoff + off, 4, e);
+          else
+            store_f32x4(Et + off, true, 4, e);
         }
       }
     }
@@ -1920,12 +1974,14 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
   }
 }
 
-template <int R, bool F16, bool EF>
+template <int R, bool F16, bool EF, int ST>
 __global__ void __launch_bounds__(kThreads) k_pass3_mfma(Pass3Args args) {
   if (F16 && *args.found_inf) return;
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
     if constexpr (F16)
       f16_unscale_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.inv_scale);
+    else if constexpr (ST != kStF32)
+      round_range<ST>(args.ftiles[blockIdx.x - args.ntiles], args.bucket);
     return;
   }
   __shared__ float tile[32 * kPass3TileStride];
@@ -1934,9 +1990,9 @@ __global__ void __launch_bounds__(kThreads) k_pass3_mfma(Pass3Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec)
-    pass3_mfma_rows<R, F16, EF>(args, d, t, lane, wave, tile);
+    pass3_mfma_rows<R, F16, EF, ST>(args, d, t, lane, wave, tile);
   else
-    pass3_mfma_body<R, F16, EF, false>(args, d, t, lane, wave);
+    pass3_mfma_body<R, F16, EF, false, ST>(args, d, t, lane, wave);
 }
 
 // ------------------------------------------------------------ orthogonalization
@@ -2178,15 +2234,32 @@ bool pass3_vec(bool f16, bool ef, int st, const Pass3Args& a, dim3 grid, hipStre
 }
 
 template <int R>
+bool pass1_mma(bool f16, bool ef, int st, const Pass1Args& a, dim3 grid, hipStream_t s) {
+#define PSGD_M1(F, E, S) k_pass1_mfma<R, F, E, S><<<grid, kThreads, 0, s>>>(a)
+  PSGD_VARIANTS(PSGD_M1)
+#undef PSGD_M1
+}
+
+template <int R>
+bool pass2_mma(bool f16, bool ef, int st, const Pass2Args& a, dim3 grid, hipStream_t s) {
+#define PSGD_M2(F, E, S) k_pass2_mfma<R, F, E, S><<<grid, kThreads, 0, s>>>(a)
+  PSGD_VARIANTS(PSGD_M2)
+#undef PSGD_M2
+}
+
+template <int R>
+bool pass3_mma(bool f16, bool ef, int st, const Pass3Args& a, dim3 grid, hipStream_t s) {
+#define PSGD_M3(F, E, S) k_pass3_mfma<R, F, E, S><<<grid, kThreads, 0, s>>>(a)
+  PSGD_VARIANTS(PSGD_M3)
+#undef PSGD_M3
+}
+
+template <int R>
 hipError_t pass1_r(bool f16, bool ef, int st, const Pass1Args& a, hipStream_t s) {
   const dim3 grid(a.ntiles + (f16 ? a.nftiles : 0));
   if (grid.x == 0) return hipSuccess;
   if constexpr (R >= kMfmaMinRank) {
-    if (st != kStF32) return hipErrorInvalidValue;  // 16-bit states: vector ranks only
-    if (f16 && ef) k_pass1_mfma<R, true, true><<<grid, kThreads, 0, s>>>(a);
-    else if (f16) k_pass1_mfma<R, true, false><<<grid, kThreads, 0, s>>>(a);
-    else if (ef) k_pass1_mfma<R, false, true><<<grid, kThreads, 0, s>>>(a);
-    else k_pass1_mfma<R, false, false><<<grid, kThreads, 0, s>>>(a);
+    if (!pass1_mma<R>(f16, ef, st, a, grid, s)) return hipErrorInvalidValue;
   } else {
     if (!pass1_vec<R>(f16, ef, st, a, grid, s)) return hipErrorInvalidValue;
   }
@@ -2198,11 +2271,7 @@ hipError_t pass2_r(bool f16, bool ef, int st, const Pass2Args& a, hipStream_t s)
   if (a.ntiles == 0) return hipSuccess;
   const dim3 grid(a.ntiles);
   if constexpr (R >= kMfmaMinRank) {
-    if (st != kStF32) return hipErrorInvalidValue;
-    if (f16 && ef) k_pass2_mfma<R, true, true><<<grid, kThreads, 0, s>>>(a);
-    else if (f16) k_pass2_mfma<R, true, false><<<grid, kThreads, 0, s>>>(a);
-    else if (ef) k_pass2_mfma<R, false, true><<<grid, kThreads, 0, s>>>(a);
-    else k_pass2_mfma<R, false, false><<<grid, kThreads, 0, s>>>(a);
+    if (!pass2_mma<R>(f16, ef, st, a, grid, s)) return hipErrorInvalidValue;
   } else {
     if (!pass2_vec<R>(f16, ef, st, a, grid, s)) return hipErrorInvalidValue;
   }
@@ -2215,11 +2284,7 @@ hipError_t pass3_r(bool f16, bool ef, int st, const Pass3Args& a, hipStream_t s)
   const dim3 grid(a.ntiles + ((f16 || st != kStF32) ? a.nftiles : 0));
   if (grid.x == 0) return hipSuccess;
   if constexpr (R >= kMfmaMinRank) {
-    if (st != kStF32) return hipErrorInvalidValue;
-    if (f16 && ef) k_pass3_mfma<R, true, true><<<grid, kThreads, 0, s>>>(a);
-    else if (f16) k_pass3_mfma<R, true, false><<<grid, kThreads, 0, s>>>(a);
-    else if (ef) k_pass3_mfma<R, false, true><<<grid, kThreads, 0, s>>>(a);
-    else k_pass3_mfma<R, false, false><<<grid, kThreads, 0, s>>>(a);
+    if (!pass3_mma<R>(f16, ef, st, a, grid, s)) return hipErrorInvalidValue;
   } else {
     if (!pass3_vec<R>(f16, ef, st, a, grid, s)) return hipErrorInvalidValue;
   }
@@ -2249,10 +2314,15 @@ hipError_t launch_pass2(int R, bool f16, bool ef, int st, const Pass2Args& a, hi
   PSGD_RANK_SWITCH(R, return pass2_r<RR>(f16, ef, st, a, s))
 }
 
-hipError_t launch_pass2_reduce(int R, const Pass2ReduceArgs& a, hipStream_t s) {
+hipError_t launch_pass2_reduce(int R, int st, const Pass2ReduceArgs& a, hipStream_t s) {
   if (a.ntiles == 0) return hipSuccess;
   PSGD_RANK_SWITCH(R, {
-    k_pass2_reduce<RR><<<dim3(a.ntiles), kReduceThreads, 0, s>>>(a);
+    if (st == kStF16)
+      k_pass2_reduce<RR, kStF16><<<dim3(a.ntiles), kReduceThreads, 0, s>>>(a);
+    else if (st == kStBF16)
+      k_pass2_reduce<RR, kStBF16><<<dim3(a.ntiles), kReduceThreads, 0, s>>>(a);
+    else
+      k_pass2_reduce<RR, kStF32><<<dim3(a.ntiles), kReduceThreads, 0, s>>>(a);
     return hipGetLastError();
   })
 }

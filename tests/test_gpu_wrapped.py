@@ -5,7 +5,8 @@ Tolerance: both sides round every materialized tensor to 16 bits; they differ on
 how the value before each rounding was accumulated (fp32 in the kernels, fp64 in the
 oracle), which moves a small fraction of results by one 16-bit ulp. The relative
 Frobenius difference of each quantity is held to 4u (u = 2^-11 for binary16, 2^-8 for
-bfloat16); the cast of uncompressed views is bit-exact."""
+bfloat16), E's relative to ||M'|| (it carries M_hat's rounding error, which does not
+shrink with E); the cast of uncompressed views is bit-exact."""
 import numpy as np
 import pytest
 import torch
@@ -37,7 +38,9 @@ def _hp(**kw):
     return base
 
 
-def _bucket(views, step, seed, rank, scale=1.0):
+def _bucket(views, step, seed, rank, scale=1.0, decay=None):
+    """Per matrix view: a fixed rank-k part (k = max(16, 2r)) with singular-value
+    weights 1/j, or decay^j when given, plus fresh N(0, 0.01^2) noise; vectors N(0, 1)."""
     out = torch.zeros(_numel(views), dtype=torch.float64)
     k = max(16, 2 * rank)
     for vi, (off, shp) in enumerate(views):
@@ -50,19 +53,22 @@ def _bucket(views, step, seed, rank, scale=1.0):
         g = torch.Generator().manual_seed(seed * 104729 + vi)
         u = torch.randn(n, k, generator=g, dtype=torch.float64)
         v = torch.randn(m, k, generator=g, dtype=torch.float64)
-        w = torch.tensor([1.0 / (j + 1) for j in range(k)], dtype=torch.float64)
+        w = torch.tensor([1.0 / (j + 1) if decay is None else decay ** j for j in range(k)],
+                         dtype=torch.float64)
         out[off:off + size] = ((u * w) @ v.T + 0.01 * torch.randn(
             n, m, generator=gs, dtype=torch.float64)).reshape(-1)
     return (out * scale).float()
 
 
-def _run(hp, dt, views, steps, seed=0, bucket_index=0, check_factors=True):
+def _run(hp, dt, views, steps, seed=0, bucket_index=0, check_factors=True, decay=None,
+         factor_scale=1.0):
+    """factor_scale widens the bound of the factors P and Q (not of M_hat and E)."""
     st = PowerSGDState(**hp)
     orc = oracle.OracleState(oracle_hparams(hp))
     tol = TOL[dt]
     r = hp["matrix_approximation_rank"]
     for t in range(steps):
-        x = _bucket(views, t, seed, r)
+        x = _bucket(views, t, seed, r, decay=decay)
         dev = x.cuda()
         st.compress_bucket_wrapped(dev, views, dt, bucket_index=bucket_index)
         res = orc.compress_bucket_wrapped(x.numpy(), views, dt, bucket_index=bucket_index)
@@ -92,22 +98,37 @@ def _run(hp, dt, views, steps, seed=0, bucket_index=0, check_factors=True):
                 rnd = oracle.round_f16 if dt == "f16" else oracle.round_bf16
                 assert np.all(rnd(p) == p) and np.all(rnd(q) == q)
             if vr.error is not None:
+                # E = rnd(M' - M_hat) inherits M_hat's rounding error, about u ||M'||
+                # whatever ||E|| is, so its difference is measured against ||M'||
                 e = st.error(bucket_index, vi).double().cpu().numpy()
-                ne, nm = np.linalg.norm(vr.error), np.linalg.norm(vr.m_prime)
-                errs["E"] = rel_fro(e, vr.error, nm if ne < 1e-3 * nm else None)
+                errs["E"] = rel_fro(e, vr.error, np.linalg.norm(vr.m_prime))
             for key, v in errs.items():
                 worst[key] = max(worst.get(key, 0.0), v)
-                assert v <= tol, (t, vi, key, v, (n, m, k))
+                bound = tol * factor_scale if key in ("P", "Q") else tol
+                assert v <= bound, (t, vi, key, v, (n, m, k))
         log(f"  step {t}: " + ", ".join(f"{k}={v:.2e}" for k, v in worst.items())
             + f" (tol {tol:.1e})")
     return st, orc
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
-@pytest.mark.parametrize("rank", [1, 2, 4, 8])
+@pytest.mark.parametrize("rank", [1, 2, 4, 8, 16, 32])
 def test_wrapped_parity(dt, rank):
+    """Ranks 16 and 32 run the matrix-core passes: at 16 the 300 x 260 view (rows
+    16-byte aligned) and the 130 x 77 view (not aligned) are compressed, at 32 the
+    300 x 260 view.
+
+    At these ranks the trailing columns of P and Q are ill-conditioned in 16 bits: their
+    rounding error is amplified by the gaps between neighbouring singular values, while
+    M_hat = P Q^T (the hook's output) is not. The inputs there decay geometrically
+    (0.85^j at rank 16, 0.92^j at rank 32: gaps and dynamic range both moderate) and P
+    and Q are held to 12u, M_hat and E to 4u. For scale: the same 16-bit steps with
+    float32 instead of fp64 products differ from the oracle by up to 2.7u (rank 16)
+    and 5.2u (rank 32) in P on these inputs, and by up to 8.2u at rank 16 with 1/j."""
     log(f"case: wrapped hook {dt}, rank {rank}")
-    _run(_hp(matrix_approximation_rank=rank), dt, VIEWS, steps=4, seed=rank)
+    decay = {16: 0.85, 32: 0.92}.get(rank)
+    _run(_hp(matrix_approximation_rank=rank), dt, VIEWS, steps=4, seed=rank, decay=decay,
+         factor_scale=3.0 if rank >= 16 else 1.0)
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
@@ -137,10 +158,6 @@ def test_wrapped_layout_and_argument_errors():
     with pytest.raises(PowerSGDError) as ei:
         st.compress_bucket(x.clone(), views, bucket_index=0)
     assert ei.value.status == api.POWERSGD_ERR_LAYOUT_CHANGED
-    hi = PowerSGDState(**_hp(matrix_approximation_rank=16))
-    with pytest.raises(PowerSGDError) as ei:
-        hi.compress_bucket_wrapped(x.clone(), views, "f16")
-    assert ei.value.status == api.POWERSGD_ERR_UNSUPPORTED
     lib = api.load_library()
     arr = api.make_views(views)
     assert lib.powersgd_compress_bucket_wrapped(st._state, 5, 1, x.data_ptr(), 0, x.numel(), arr,
