@@ -1750,6 +1750,118 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
   }
 }
 
+// Pass 2 for a 16-bit state on the 16-bit matrix cores (v_mfma_f32_16x16x16 f16, or
+// bf16_1k): M' and P hold 16-bit values, so their products are exact and the result
+// differs from the fp32 matrix cores only in the fp32 accumulation order, at a quarter
+// of the instructions. Lane l supplies A[l%16][4(l/16)..4(l/16)+3] and
+// B[4(l/16)..4(l/16)+3][l%16] (four 16-bit values in two registers); D as above. Lane
+// (h, cl) loads rows 4h..4h+3 of each 16-row step at columns c0 + 4cl..4cl+3 (four
+// 8-byte loads): column s of that 4 x 4 block is the A operand of MFMA s (output
+// columns c0 + 4i + s, as in pass2_mfma_body), and B holds the same four rows of P's
+// column 16nt + cl.
+typedef short mfma_s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 mfma_h16x4 __attribute__((ext_vector_type(4)));
+
+template <int ST>
+__device__ __forceinline__ mfma_f4 mfma16x16x16(uint2 a, uint2 b, mfma_f4 c) {
+  if constexpr (ST == kStBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mfma_s16x4, a),
+                                                     __builtin_bit_cast(mfma_s16x4, b), c, 0, 0,
+                                                     0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(mfma_h16x4, a),
+                                                 __builtin_bit_cast(mfma_h16x4, b), c, 0, 0, 0);
+}
+
+template <int R, int ST>
+__device__ __forceinline__ void pass2_mfma16_rows(const Pass2Args& args, const TensorDesc& d,
+                                                  const Tile& t, int lane, int wave) {
+  constexpr int NT = R / 16;
+  constexpr int U2 = 2;  // 16-row steps loaded before use
+  const int m = d.m;
+  const int r0 = t.a * d.rpb;
+  const int r1 = min(d.n, r0 + d.rpb);
+  const int h = lane >> 4;
+  const int cl = lane & 15;
+  const int c0 = t.b * kColBlock + 64 * wave;
+  if (c0 >= m) return;
+  const int col = c0 + 4 * cl;
+  const bool col_ok = col < m;
+  const int colc = min(col, m - 4);
+  const float* __restrict__ Pt = args.P + d.poff;
+  const uint16_t* __restrict__ Mt = args.Mh + d.eoff;
+  mfma_f4 acc[4][NT];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[s4][nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
+  for (int rr = r0; rr < r1; rr += 16 * U2) {
+    uint2 xm[U2][4];
+    float pv[U2][4][NT];
+#pragma unroll
+    for (int u = 0; u < U2; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rowc = min(rr + 16 * u + 4 * h + j, r1 - 1);
+        xm[u][j] = *reinterpret_cast<const uint2*>(Mt + static_cast<int64_t>(rowc) * m + colc);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          pv[u][j][nt] = Pt[static_cast<int64_t>(rowc) * R + 16 * nt + cl];
+      }
+#pragma unroll
+    for (int u = 0; u < U2; ++u) {
+      uint32_t pb[4][NT];  // 16-bit P values (exact: P is rounded where it is formed)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool rok = rr + 16 * u + 4 * h + j < r1;
+        if (!(rok && col_ok)) xm[u][j] = make_uint2(0u, 0u);  // +0 in both formats
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) pb[j][nt] = rok ? to_h16<ST>(pv[u][j][nt]) : 0u;
+      }
+      uint2 b[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        b[nt] = make_uint2(pb[0][nt] | (pb[1][nt] << 16), pb[2][nt] | (pb[3][nt] << 16));
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        // column s4 of the 4 x 4 block: element s4 of each row's four 16-bit values
+        uint32_t e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = (s4 < 2) ? xm[u][j].x : xm[u][j].y;
+          e[j] = (s4 & 1) ? (w >> 16) : (w & 0xFFFFu);
+        }
+        const uint2 a = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[s4][nt] = mfma16x16x16<ST>(a, b[nt], acc[s4][nt]);
+      }
+    }
+  }
+  float* Qt = args.Q + d.qoff;
+  float* part = args.partial + static_cast<int64_t>(d.pslot + t.b * d.nrb + t.a) * (kColBlock * R);
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int qcol = c0 + 16 * h + 4 * v + s4;
+        const int k = 16 * nt + cl;
+        if (qcol < m) {
+          const float val = acc[s4][nt][v];
+          if (d.nrb == 1) {
+            const float q = (k < d.rank) ? rnd16<ST>(val) : 0.f;
+            Qt[static_cast<int64_t>(qcol) * R + k] = q;
+            args.QT[d.qtoff + static_cast<int64_t>(k) * d.mstride + qcol] = q;
+          } else {
+            part[(qcol - t.b * kColBlock) * R + k] = val;
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int R, bool F16, bool EF, int ST>
 __global__ void __launch_bounds__(kThreads) k_pass2_mfma(Pass2Args args) {
   if (F16 && *args.found_inf) return;
@@ -1757,6 +1869,12 @@ __global__ void __launch_bounds__(kThreads) k_pass2_mfma(Pass2Args args) {
   const int wave = wave_index();
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
+  if constexpr (ST != kStF32) {
+    if (d.vec) {
+      pass2_mfma16_rows<R, ST>(args, d, t, lane, wave);
+      return;
+    }
+  }
   if (d.vec)
     pass2_mfma_body<R, F16, EF, true, ST>(args, d, t, lane, wave);
   else

@@ -141,6 +141,12 @@ CONFIGS: Dict[int, WorkloadConfig] = {
         notes="the BERT-large fp32 bucket, gradients x 2^-10, under "
               "fp16_compress_wrapper(powerSGD_hook); unscaled, the warm-started P = M'Q "
               "(about sigma^2, 1e6 here) would overflow binary16"),
+    8: WorkloadConfig(
+        name="gpt-bucket-r32-bf16-wrapper", shapes=_gpt_shapes(),
+        hparams=_hp(matrix_approximation_rank=32, orthogonalization_epsilon=1e-8),
+        steps=10, spectrum_rank=128, spectrum_power=0.5, seed=1003, wrap="bf16",
+        notes="the GPT-style fp32 bucket under bf16_compress_wrapper(powerSGD_hook), "
+              "rank 32 on the matrix cores"),
 }
 
 
