@@ -469,6 +469,74 @@ class OracleState:
         self._end_call(is_last, True)
         return result
 
+    def compress_bucket_batched_wrapped(self, bucket: np.ndarray, compute_dtype: str = "f16",
+                                        bucket_index: int = 0,
+                                        is_last: bool = True) -> StepResult:
+        """fp16_compress_wrapper or bf16_compress_wrapper around batched_powerSGD_hook
+        ("Default Communication Hooks"; "PowerSGD Hooks", batched_powerSGD_hook steps 1
+        to 9): the fp32 bucket is cast to 16 bits, zero-padded to the s x s matrix, the
+        hook's steps run with every formed tensor in 16 bits (oracle.lowp), and the
+        first numel entries of M_hat are cast back to fp32.
+
+        READING: as compress_bucket_batched (E over all s * s entries, no rate test,
+        rank min(r, s), view index 0 for the draw) and compress_bucket_wrapped (the
+        binary32 draw cast to 16 bits, no loss scaling); the memorized layout is
+        ("batched", numel, dtype).
+        """
+        from .lowp import ROUNDERS, compress_matrix_step_lowp
+
+        hp = self.hp
+        rnd = ROUNDERS[compute_dtype]
+        bucket = np.asarray(bucket)
+        if bucket.dtype != np.float32:
+            raise TypeError("the wrapped hook takes a float32 bucket")
+        numel = int(bucket.size)
+        g16 = rnd(bucket.astype(np.float64))          # the wrapper's cast
+        result = StepResult(output=bucket, output64=g16.copy(), found_inf=False,
+                            skipped=False, passthrough=False)
+        if self.iteration < hp.start_powerSGD_iter:
+            result.passthrough = True
+            result.output = g16.astype(np.float32)
+            self._end_call(is_last, False)
+            return result
+        layout = ("batched", numel, compute_dtype)
+        mem = self.buckets.get(bucket_index)
+        if mem is not None and mem.layout != layout:
+            if hp.use_error_feedback or hp.warm_start:
+                raise LayoutChanged(f"bucket {bucket_index} changed its layout")
+            mem = None
+        if mem is None:
+            mem = _BucketMemory(layout=layout, numel=numel)
+            self.buckets[bucket_index] = mem
+        s = batched_side(numel)
+        if s > 0:
+            eps = float(hp.orthogonalization_epsilon)
+            padded = np.zeros(s * s, dtype=np.float64)
+            padded[:numel] = g16
+            rank = effective_rank(s, s, hp.matrix_approximation_rank)
+            if hp.warm_start and 0 in mem.q:
+                q = mem.q[0]
+            else:
+                epoch = 0 if hp.warm_start else self.iteration
+                q = rnd(gram_schmidt(rnd(standard_normal_q0(s, rank, hp.random_seed,
+                                                            bucket_index, 0, epoch)), eps))
+            e_prev = mem.error.get(0) if hp.use_error_feedback else None
+            m_prime, p, q_new, m_hat, err = compress_matrix_step_lowp(
+                padded.reshape(s, s), e_prev, q, eps, hp.use_error_feedback, rnd)
+            if hp.use_error_feedback:
+                mem.error[0] = err
+            if hp.warm_start:
+                mem.q[0] = q_new
+            result.output64 = m_hat.reshape(-1)[:numel].copy()
+            result.views.append(ViewResult(compressed=True, n=s, m=s, rank=rank,
+                                           m_prime=m_prime, p=p, q=q_new, m_hat=m_hat,
+                                           error=err))
+            self.numel_comm += 2 * s * rank
+        self.numel_in += numel
+        result.output = result.output64.astype(np.float32)
+        self._end_call(is_last, True)
+        return result
+
     # ---- snapshot (checkpoint / resume) -------------------------------------------
     # The pages describe no PowerSGDState checkpoint (GradScaler.state_dict in
     # "Gradient Scaling" is the analogue). The byte format is the library's documented
@@ -489,10 +557,11 @@ class OracleState:
         (n, m, rank))."""
         hp = self.hp
         if mem.layout[:1] == ("batched",):
+            prec = mem.layout[2] if len(mem.layout) > 2 else None
             s = batched_side(mem.numel)
             if s == 0:
-                return True, None, [], []
-            return True, None, [(0, (s, s))], [(0, s, s, effective_rank(
+                return True, prec, [], []
+            return True, prec, [(0, (s, s))], [(0, s, s, effective_rank(
                 s, s, hp.matrix_approximation_rank))]
         prec = None
         views = list(mem.layout)
@@ -582,8 +651,7 @@ class OracleState:
                 raise ValueError("bucket indices not strictly ascending")
             prev = idx
             batched, pcode = variant & 1, (variant >> 8) & 3
-            if (numel < 0 or nviews < 0 or variant & ~0x301 or pcode == 3 or has_q > 1
-                    or (batched and pcode)):
+            if numel < 0 or nviews < 0 or variant & ~0x301 or pcode == 3 or has_q > 1:
                 raise ValueError("bad bucket record")
             prec = {0: None, 1: "f16", 2: "bf16"}[pcode]
             if has_q and not hp.warm_start:
@@ -599,7 +667,8 @@ class OracleState:
                 s = batched_side(numel)
                 if views != ([(0, (s, s))] if numel > 0 else []):
                     raise ValueError("batched bucket is not one s x s view")
-                mem = _BucketMemory(layout=("batched", numel), numel=numel)
+                layout = ("batched", numel) if prec is None else ("batched", numel, prec)
+                mem = _BucketMemory(layout=layout, numel=numel)
             else:
                 spans = []
                 for off, shp in views:

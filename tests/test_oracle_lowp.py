@@ -188,3 +188,73 @@ def test_wrapped_pass_through_and_layout(dt):
     other = "bf16" if dt == "f16" else "f16"
     with pytest.raises(oracle.LayoutChanged):
         st.compress_bucket_wrapped(x, views, other)
+
+
+# ------------------------------------------ the wrappers around batched_powerSGD_hook
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_batched_wrapped_single_nonzero_row_is_exact(dt):
+    """A 16-element bucket is one 4 x 4 matrix; a single nonzero row of small integers
+    is recovered exactly at rank 1 (no rounding anywhere) and E is zero."""
+    hp = oracle.HParams(matrix_approximation_rank=1, start_powerSGD_iter=0)
+    st = oracle.OracleState(hp)
+    x = np.zeros(16, dtype=np.float32)
+    x[8:12] = [3.0, -7.0, 12.0, 1.0]
+    for _ in range(2):
+        r = st.compress_bucket_batched_wrapped(x, dt)
+        np.testing.assert_array_equal(r.output, x)
+        np.testing.assert_array_equal(r.views[0].error, np.zeros((4, 4)))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_batched_wrapped_padding_truncation_and_feedback(dt):
+    rnd, u = RND[dt], U[dt]
+    hp = oracle.HParams(matrix_approximation_rank=2, start_powerSGD_iter=0)
+    st = oracle.OracleState(hp)
+    rng = np.random.default_rng(5)
+    numel, s = 90, 10
+    e_prev = None
+    for t in range(3):
+        x = rng.standard_normal(numel).astype(np.float32)
+        r = st.compress_bucket_batched_wrapped(x, dt)
+        vr = r.views[0]
+        assert r.output.shape == (numel,) and (vr.n, vr.m, vr.rank) == (s, s, 2)
+        g = np.zeros(s * s)
+        g[:numel] = rnd(x.astype(np.float64))
+        want_mp = rnd(g + e_prev.reshape(-1)) if e_prev is not None else g
+        np.testing.assert_array_equal(vr.m_prime.reshape(-1), want_mp)   # padding: G is 0
+        for a in (vr.p, vr.q, vr.m_hat, vr.error):
+            assert np.all(rnd(a) == a)
+        assert np.all(np.abs(vr.m_prime - (vr.m_hat + vr.error)) <= u * np.abs(vr.error) + 1e-300)
+        np.testing.assert_array_equal(r.output, vr.m_hat.reshape(-1)[:numel].astype(np.float32))
+        e_prev = vr.error
+    assert (st.numel_in, st.numel_comm) == (3 * numel, 3 * 2 * s * 2)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_batched_wrapped_is_the_fp64_batched_hook_within_the_16_bit_bound(dt):
+    u = U[dt]
+    hp = oracle.HParams(matrix_approximation_rank=2, start_powerSGD_iter=0)
+    a, b = oracle.OracleState(hp), oracle.OracleState(hp)
+    for t in range(4):
+        x = _low_rank(30, 30, 8, 40 + t).reshape(-1)[:880].astype(np.float32)
+        ra = a.compress_bucket_batched(x)
+        rb = b.compress_bucket_batched_wrapped(x, dt)
+        rel = np.linalg.norm(rb.output64 - ra.output64) / np.linalg.norm(ra.output64)
+        assert rel < 16 * u, (t, rel)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_batched_wrapped_pass_through_and_layout(dt):
+    hp = oracle.HParams(matrix_approximation_rank=1, start_powerSGD_iter=1)
+    st = oracle.OracleState(hp)
+    x = (np.arange(20, dtype=np.float32) * 0.1234567).astype(np.float32)
+    r = st.compress_bucket_batched_wrapped(x, dt, bucket_index=2)
+    assert r.passthrough
+    np.testing.assert_array_equal(r.output, RND[dt](x.astype(np.float64)).astype(np.float32))
+    st.compress_bucket_batched_wrapped(x, dt, bucket_index=2)
+    assert st.buckets[2].layout == ("batched", 20, dt)
+    with pytest.raises(oracle.LayoutChanged):
+        st.compress_bucket_batched(x, bucket_index=2)
+    with pytest.raises(oracle.LayoutChanged):
+        st.compress_bucket_wrapped(x, [(0, (4, 5))], dt, bucket_index=2)

@@ -237,7 +237,24 @@ def test_wrapped_buckets_record_their_precision(dt, code):
     struct.pack_into("<f", x, first_e, 1.0 + 2.0 ** -20)
     b.import_state(bytes(x))
     assert b.buckets[6].error[0][0, 0] == 1.0
-    # precision code 3 and a batched 16-bit bucket do not exist
-    for bad in (3 << 8, (code << 8) | 1, code << 10):
+    # precision code 3 and other bits do not exist
+    for bad in (3 << 8, code << 10, 1 << 4):
         with pytest.raises(ValueError):
             b.import_state(_corrupt(blob, 96, "<I", bad))
+
+
+@pytest.mark.parametrize("dt,code", [("f16", 1), ("bf16", 2)])
+def test_batched_wrapped_buckets_record_batched_and_precision(dt, code):
+    hp = _hp()
+    a = oracle.OracleState(hp)
+    for t in range(2):
+        a.compress_bucket_batched_wrapped(_bucket(t, 50), dt, bucket_index=9)
+    blob = a.export_state()
+    idx, numel, variant = struct.unpack_from("<qqI", blob, 80)
+    assert (idx, numel, variant) == (9, 50, 1 | (code << 8))
+    b = oracle.OracleState(hp)
+    b.import_state(blob)
+    assert b.export_state() == blob and b.buckets[9].layout == ("batched", 50, dt)
+    ra = a.compress_bucket_batched_wrapped(_bucket(2, 50), dt, bucket_index=9)
+    rb = b.compress_bucket_batched_wrapped(_bucket(2, 50), dt, bucket_index=9)
+    np.testing.assert_array_equal(ra.output, rb.output)
