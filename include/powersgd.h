@@ -211,6 +211,29 @@ POWERSGD_API powersgd_status powersgd_compress_bucket_batched(powersgd_state* st
                                                  float inv_loss_scale, int32_t* found_inf_dev,
                                                  void* stream);
 
+/*
+ * batched_powerSGD_hook wrapped by fp16_compress_wrapper or bf16_compress_wrapper ("DDP
+ * Communication Hooks -- PyTorch 1.11.0", sections "Default Communication Hooks" and
+ * "PowerSGD Hooks"): the fp32 bucket is cast to 16 bits and viewed, zero-padded, as
+ * the s x s matrix of powersgd_compress_bucket_batched; every tensor the hook forms is
+ * a 16-bit value as in powersgd_compress_bucket_wrapped, and the first numel entries
+ * of M_hat are cast back to fp32 in place.
+ *
+ *   bucket, numel, capacity  as for powersgd_compress_bucket_batched (fp32 only:
+ *                  capacity >= s * s elements; the call zero-fills the padding).
+ *   compute_dtype  POWERSGD_F16 or POWERSGD_BF16.
+ *   bucket_index, is_last, stream: as for powersgd_compress_bucket.
+ *
+ * Errors: INVALID_ARG (NULL state, NULL bucket with numel > 0, numel < 0, capacity
+ * below s * s, compute_dtype not F16/BF16), UNSUPPORTED (s above 2^31 - 1),
+ * LAYOUT_CHANGED, OOM, HIP; all returned before anything is enqueued.
+ */
+POWERSGD_API powersgd_status powersgd_compress_bucket_batched_wrapped(powersgd_state* st,
+                                                 int64_t bucket_index, int32_t is_last,
+                                                 float* bucket, powersgd_dtype compute_dtype,
+                                                 int64_t numel, int64_t capacity,
+                                                 void* stream);
+
 /* Static text for a status code. */
 POWERSGD_API const char* powersgd_status_string(powersgd_status s);
 
@@ -290,8 +313,8 @@ POWERSGD_API powersgd_status powersgd_get_stats(powersgd_state* st, int64_t* ite
  *   B bucket records, in ascending bucket_index:
  *     i64 bucket_index; i64 numel (the batched variant: the length before padding);
  *     u32 variant (bit 0: the batched variant; bits 8-9: the precision of a bucket
- *     compressed through powersgd_compress_bucket_wrapped, 1 binary16, 2 bfloat16, 0
- *     otherwise; other bits zero); u32 has_q (1: a warm-start Q follows for every
+ *     compressed through a wrapped entry point, 1 binary16, 2 bfloat16, 0 otherwise;
+ *     other bits zero); u32 has_q (1: a warm-start Q follows for every
  *     compressed view); i64 V = number of views;
  *     V view records: i64 offset; i64 ndim; ndim x i64 shape (the batched variant: one
  *     view, offset 0, shape (s, s), s = powersgd_batched_side(numel));

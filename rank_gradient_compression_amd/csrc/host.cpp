@@ -953,6 +953,33 @@ powersgd_status powersgd_compress_bucket_wrapped(powersgd_state* st, int64_t buc
 
 int64_t powersgd_batched_side(int64_t numel) { return batched_side(numel); }
 
+powersgd_status powersgd_compress_bucket_batched_wrapped(powersgd_state* st, int64_t bucket_index,
+                                                         int32_t is_last, float* bucket,
+                                                         powersgd_dtype compute_dtype,
+                                                         int64_t numel, int64_t capacity,
+                                                         void* stream) {
+  if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
+  if (numel < 0) return fail(POWERSGD_ERR_INVALID_ARG, "numel < 0");
+  if (numel > 0 && !bucket) return fail(POWERSGD_ERR_INVALID_ARG, "bucket is NULL");
+  int prec = kStF32;
+  if (compute_dtype == POWERSGD_F16)
+    prec = kStF16;
+  else if (compute_dtype == POWERSGD_BF16)
+    prec = kStBF16;
+  else
+    return fail(POWERSGD_ERR_INVALID_ARG, "compute_dtype must be F16 or BF16");
+  const int64_t side = batched_side(numel);
+  if (side > INT32_MAX) return fail(POWERSGD_ERR_UNSUPPORTED, "bucket too large for the batched view");
+  if (capacity < side * side)
+    return fail(POWERSGD_ERR_INVALID_ARG,
+                "capacity " + std::to_string(capacity) + " is below the padded square of " +
+                    std::to_string(side * side) + " elements");
+  std::vector<ViewKey> keys;
+  if (numel > 0) keys.push_back(ViewKey{0, {side, side}});
+  return run_call(st, bucket_index, is_last, bucket, false, numel, true, prec, keys, 1.0f,
+                  nullptr, stream);
+}
+
 powersgd_status powersgd_compress_bucket_batched(powersgd_state* st, int64_t bucket_index,
                                                  int32_t is_last, void* bucket,
                                                  powersgd_dtype dtype, int64_t numel,
@@ -1383,8 +1410,7 @@ powersgd_status read_bucket(const powersgd_hparams& hp, SnapReader& rd, int64_t 
   if (out.index <= prev_index) return snap_bad("bucket indices not strictly ascending");
   const uint32_t batched = variant & 1u;
   const int prec = static_cast<int>((variant >> 8) & 3u);
-  if (numel < 0 || nviews < 0 || (variant & ~0x301u) != 0 || prec == 3 || (batched && prec) ||
-      has_q > 1)
+  if (numel < 0 || nviews < 0 || (variant & ~0x301u) != 0 || prec == 3 || has_q > 1)
     return snap_bad("bad field in the record of bucket " + std::to_string(out.index));
   if (has_q && !hp.warm_start) return snap_bad("warm-start Q without warm start");
   // every view record takes at least 16 bytes

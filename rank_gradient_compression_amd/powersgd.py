@@ -36,6 +36,7 @@ EXPORTED = (
     "powersgd_get_kernel_times", "powersgd_kernel_name", "powersgd_classify_view",
     "powersgd_batched_side", "powersgd_compress_bucket_batched",
     "powersgd_state_export", "powersgd_state_import", "powersgd_compress_bucket_wrapped",
+    "powersgd_compress_bucket_batched_wrapped",
 )
 
 
@@ -93,6 +94,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "powersgd_batched_side": (i64, [i64]),
         "powersgd_compress_bucket_wrapped": (i32, [P, i64, i32, P, i32, i64,
                                                    ctypes.POINTER(powersgd_view), i32, P]),
+        "powersgd_compress_bucket_batched_wrapped": (i32, [P, i64, i32, P, i32, i64, i64, P]),
         "powersgd_compress_bucket_batched": (i32, [P, i64, i32, P, i32, i64, i64, f32, P, P]),
         "powersgd_status_string": (ctypes.c_char_p, [i32]),
         "powersgd_last_error": (ctypes.c_char_p, []),
@@ -186,6 +188,15 @@ def powersgd_compress_bucket_wrapped(state, bucket_index: int, is_last: bool,
     _check(load_library().powersgd_compress_bucket_wrapped(
         state, int(bucket_index), int(bool(is_last)), ctypes.c_void_p(bucket_ptr),
         int(compute_dtype), int(numel), arr, len(views),
+        ctypes.c_void_p(stream) if stream else None))
+
+
+def powersgd_compress_bucket_batched_wrapped(state, bucket_index: int, is_last: bool,
+                                             bucket_ptr: int, compute_dtype: int, numel: int,
+                                             capacity: int, stream: Optional[int]) -> None:
+    _check(load_library().powersgd_compress_bucket_batched_wrapped(
+        state, int(bucket_index), int(bool(is_last)), ctypes.c_void_p(bucket_ptr),
+        int(compute_dtype), int(numel), int(capacity),
         ctypes.c_void_p(stream) if stream else None))
 
 
@@ -363,6 +374,23 @@ class PowerSGDState:
         powersgd_compress_bucket_wrapped(self._state, bucket_index, is_last, bucket.data_ptr(),
                                          dt, bucket.numel(), list(views),
                                          self._stream_handle(stream))
+
+    def compress_bucket_batched_wrapped(self, buffer, compute_dtype: str = "f16",
+                                        numel: Optional[int] = None, bucket_index: int = 0,
+                                        is_last: bool = True, stream=None) -> None:
+        """batched_powerSGD_hook under fp16_compress_wrapper ("f16") or
+        bf16_compress_wrapper ("bf16") on the first `numel` elements of a float32
+        `buffer` holding at least powersgd_batched_side(numel) ** 2 elements."""
+        import torch
+        if not buffer.is_cuda or not buffer.is_contiguous() or buffer.dim() != 1:
+            raise ValueError("buffer must be a contiguous 1-D device tensor")
+        if buffer.dtype != torch.float32:
+            raise TypeError("the wrapped hook takes a float32 buffer")
+        dt = {"f16": POWERSGD_F16, "bf16": POWERSGD_BF16}[compute_dtype]
+        n = buffer.numel() if numel is None else int(numel)
+        powersgd_compress_bucket_batched_wrapped(self._state, bucket_index, is_last,
+                                                 buffer.data_ptr(), dt, n, buffer.numel(),
+                                                 self._stream_handle(stream))
 
     def compress_bucket_batched(self, buffer, numel: Optional[int] = None,
                                 bucket_index: int = 0, is_last: bool = True,

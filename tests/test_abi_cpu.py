@@ -157,6 +157,8 @@ def test_invalid_arguments_are_rejected_before_device_work(lib):
                                                 None, None) == api.POWERSGD_ERR_INVALID_ARG
     assert lib.powersgd_compress_bucket_wrapped(None, 0, 1, ctypes.c_void_p(16), 1, 16, views, 1,
                                                 None) == api.POWERSGD_ERR_INVALID_ARG
+    assert lib.powersgd_compress_bucket_batched_wrapped(None, 0, 1, ctypes.c_void_p(16), 1, 16,
+                                                        16, None) == api.POWERSGD_ERR_INVALID_ARG
     assert lib.powersgd_get_stats(None, None, None, None) == api.POWERSGD_ERR_INVALID_ARG
     size = ctypes.c_int64()
     assert lib.powersgd_state_export(None, None, 0, ctypes.byref(size),

@@ -220,3 +220,74 @@ def test_wrapped_snapshot_matches_the_oracle_and_resumes(dt, code):
     b.compress_bucket_wrapped(xb, VIEWS, dt, bucket_index=3)
     torch.cuda.synchronize()
     assert torch.equal(xa.view(torch.int32), xb.view(torch.int32))
+
+
+# ------------------------------------------ the wrappers around batched_powerSGD_hook
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("numel,rank", [(5000, 2), (16284, 4), (22400, 16), (22500, 32)])
+def test_batched_wrapped_parity_and_resume(dt, numel, rank):
+    """The bucket cast to 16 bits and viewed as one zero-padded s x s matrix. The
+    padding is NaN before every call (the library must zero it); ranks 16 and 32 use
+    the geometric inputs and the factor bound of test_wrapped_parity."""
+    s = oracle.batched_side(numel)
+    log(f"case: batched wrapped hook {dt}, numel {numel} -> {s} x {s}, rank {rank}")
+    hp = _hp(matrix_approximation_rank=rank)
+    st = PowerSGDState(**hp)
+    orc = oracle.OracleState(oracle_hparams(hp))
+    tol = TOL[dt]
+    fscale = 3.0 if rank >= 16 else 1.0
+    decay = {16: 0.85, 32: 0.92}.get(rank)
+    rnd = oracle.round_f16 if dt == "f16" else oracle.round_bf16
+    buf = torch.empty(s * s, device="cuda")
+    for t in range(3):
+        x = _bucket([(0, (s, s))], t, numel, rank, decay=decay)[:numel].contiguous()
+        buf[numel:].fill_(float("nan"))
+        buf[:numel].copy_(x.cuda())
+        st.compress_bucket_batched_wrapped(buf, dt, numel=numel)
+        res = orc.compress_bucket_batched_wrapped(x.numpy(), dt)
+        torch.cuda.synchronize()
+        vr = res.views[0]
+        assert st.view_info(0, 0) == (s, s, vr.rank)
+        out = buf[:numel].double().cpu().numpy()
+        assert np.all(rnd(out) == out)
+        p, q = st.factors(0, 0)
+        e = st.error(0, 0).double().cpu().numpy()
+        errs = {"out": rel_fro(out, res.output64),
+                "P": rel_fro(p.double().cpu().numpy(), vr.p),
+                "Q": rel_fro(q.double().cpu().numpy(), vr.q),
+                "E": rel_fro(e, vr.error, np.linalg.norm(vr.m_prime))}
+        for k, v in errs.items():
+            assert v <= (tol * fscale if k in ("P", "Q") else tol), (t, k, v)
+        log(f"  step {t}: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert st.stats() == (orc.iteration, orc.numel_in, orc.numel_comm)
+    # resume from the library's own snapshot: bitwise
+    blob = bytes(st.export_state())
+    b = PowerSGDState(**hp)
+    b.import_state(blob)
+    assert bytes(b.export_state()) == blob
+    x = _bucket([(0, (s, s))], 3, numel, rank, decay=decay)[:numel].contiguous().cuda()
+    bufs = [torch.zeros(s * s, device="cuda") for _ in range(2)]
+    for bb, state in zip(bufs, (st, b)):
+        bb[:numel].copy_(x)
+        state.compress_bucket_batched_wrapped(bb, dt, numel=numel)
+    torch.cuda.synchronize()
+    assert torch.equal(bufs[0][:numel].view(torch.int32), bufs[1][:numel].view(torch.int32))
+
+
+def test_batched_wrapped_errors():
+    log("case: batched wrapped hook errors")
+    st = PowerSGDState(**_hp())
+    x = torch.zeros(100, device="cuda")
+    with pytest.raises(PowerSGDError) as ei:
+        st.compress_bucket_batched_wrapped(x, "f16", numel=101)   # 11 x 11 > 100
+    assert ei.value.status == api.POWERSGD_ERR_INVALID_ARG
+    st.compress_bucket_batched_wrapped(x, "f16", numel=90)
+    with pytest.raises(PowerSGDError) as ei:
+        st.compress_bucket_batched_wrapped(x, "bf16", numel=90)
+    assert ei.value.status == api.POWERSGD_ERR_LAYOUT_CHANGED
+    with pytest.raises(PowerSGDError) as ei:
+        st.compress_bucket_batched(x, numel=90)
+    assert ei.value.status == api.POWERSGD_ERR_LAYOUT_CHANGED
+    with pytest.raises(TypeError):
+        st.compress_bucket_batched_wrapped(x.half(), "f16")
