@@ -21,9 +21,12 @@ from snapshot_format import parse
 pytestmark = pytest.mark.gpu
 
 # aligned rows (300 x 260), a conv view, rows of 77 floats (unaligned access), rows of
-# 3 floats (scalar access), vectors and a matrix the rate test keeps whole
+# 3 floats (scalar access), vectors and a matrix the rate test keeps whole; rows of
+# multiples of 8 floats take 8 columns per lane: 97 x 264 (two column blocks, the
+# second partial), 400 x 256 (several pass-2 row blocks) and 20 x 40 (narrow)
 VIEWS = [(0, (64, 3, 3, 3)), (1728, (64,)), (1792, (4, 4)), (1808, (300, 260)),
-         (79808, (130, 77)), (89818, (400, 3)), (91018, (7,))]
+         (79808, (130, 77)), (89818, (400, 3)), (91018, (7,)), (91025, (97, 264)),
+         (116633, (400, 256)), (219033, (20, 40))]
 
 
 def _numel(views):
