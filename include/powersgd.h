@@ -3,11 +3,14 @@
  *
  * The library compresses one data-parallel rank's flat gradient bucket in place
  * with PowerSGD, as described on "DDP Communication Hooks -- PyTorch 1.11.0",
- * section "PowerSGD Hooks" (powerSGD_hook, steps 1 to 3.7), with the state and
- * hyperparameters of section "PowerSGD State" and the same-shape batching switch
- * of the translated page's "Состояние PowerSGD" item 5. A float16 variant fuses the
- * loss-scale division and inf/NaN check of "torch.cuda.amp -- PyTorch 1.5.0",
- * section "Gradient Scaling" (GradScaler.unscale_ and step).
+ * section "PowerSGD Hooks" (powerSGD_hook, steps 1 to 3.7, and
+ * batched_powerSGD_hook), with the state and hyperparameters of section "PowerSGD
+ * State" and the same-shape batching switch of the translated page's "Состояние
+ * PowerSGD" item 5. A float16 variant fuses the loss-scale division and inf/NaN check
+ * of "torch.cuda.amp -- PyTorch 1.5.0", section "Gradient Scaling"
+ * (GradScaler.unscale_ and step); the fp16_compress_wrapper / bf16_compress_wrapper
+ * of section "Default Communication Hooks" run either hook with a 16-bit state. The
+ * state can be exported and imported as a byte string (checkpoint / resume).
  *
  * One rank: the allreduces of P, of Q and of the uncompressed tensors are the
  * identity, so no collective is issued.
