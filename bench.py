@@ -262,12 +262,14 @@ def main() -> int:
         for _, shp in views:
             comp, n, m, _r = api.powersgd_classify_view(hp_c, shp)
             comp_elems += n * m if comp else 0
+    ef = bool(cfg.hparams.get("use_error_feedback", True))
     if cfg.wrap:
-        # fp32 bucket, 16-bit M' and E: 8 + 2 + 8 per compressed element; the cast of
-        # the other views reads and writes fp32
-        algo_bytes = comp_elems * 18 + (cfg.numel - comp_elems) * 8
+        # fp32 bucket, 16-bit M' and E: 8 + 2 + 8 per compressed element (6 + 2 + 4
+        # without error feedback); the cast of the other views reads and writes fp32
+        algo_bytes = comp_elems * (18 if ef else 12) + (cfg.numel - comp_elems) * 8
     else:
-        per_elt = 28 if cfg.dtype == "f32" else 24
+        # fp32: 12 + 4 + 12 (4 + 4 + 4 without error feedback); fp16: 6 + 6 + 12 (2 + 2 + 2)
+        per_elt = (28 if ef else 12) if cfg.dtype == "f32" else (24 if ef else 6)
         algo_bytes = comp_elems * per_elt + (0 if cfg.dtype == "f32" or cfg.batched else
                                              (cfg.numel - comp_elems) * 6)
     step_frac = algo_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS

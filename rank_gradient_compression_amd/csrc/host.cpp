@@ -555,13 +555,15 @@ int64_t batched_side(int64_t numel) {
 }
 
 // Algorithmic bytes of each pass per compressed element (minimum traffic).
+// Minimum bytes per compressed element that each pass moves. Without error feedback
+// pass 3 only writes M_hat (M' is not read).
 double pass_bytes(int kind, bool f16, bool ef, int prec = kStF32) {
   if (prec != kStF32) {
     // fp32 bucket, 16-bit M' and E
     switch (kind) {
       case K_PASS1: return 4.0 + (ef ? 2.0 : 0.0) + 2.0;
       case K_PASS2: return 2.0;
-      case K_PASS3: return 2.0 + 4.0 + (ef ? 2.0 : 0.0);
+      case K_PASS3: return ef ? 2.0 + 4.0 + 2.0 : 4.0;
       default: return 0.0;
     }
   }
@@ -569,7 +571,7 @@ double pass_bytes(int kind, bool f16, bool ef, int prec = kStF32) {
   switch (kind) {
     case K_PASS1: return f16 ? (g + (ef ? 4.0 : 0.0)) : (ef ? 12.0 : 4.0);
     case K_PASS2: return f16 ? (g + (ef ? 4.0 : 0.0)) : 4.0;
-    case K_PASS3: return f16 ? (ef ? 12.0 : 4.0) : (ef ? 12.0 : 8.0);
+    case K_PASS3: return ef ? 12.0 : g;
     default: return 0.0;
   }
 }
