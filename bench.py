@@ -56,6 +56,35 @@ def load_traffic(kernel: str, workload: str):
         return None
 
 
+# dense matrix-core peaks of MI355X, TFLOP/s
+MFMA_PEAK_TFLOPS = {"F32": 157.3, "F16": 2500.0, "BF16": 2500.0}
+
+
+def load_mfma(kernel: str, workload: str):
+    """Matrix-core use of a kernel measured with rocprofv3 counters (profiles/), if the
+    measurement was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"mfma_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.split()[0] if v.split() else ""
+    from rank_gradient_compression_amd.rocprof_summary import source_hash
+    if vals.get("source_hash") != source_hash():
+        return None
+    try:
+        tflops = float(vals["mfma_tflops"])
+        dt = vals.get("mfma_dtype", "F32")
+        peak = MFMA_PEAK_TFLOPS.get(dt, MFMA_PEAK_TFLOPS["F32"])
+        return {"util_percent": float(vals["mfma_util_percent"]), "tflops": tflops,
+                "dtype": dt.lower(), "peak_tflops": peak, "frac": round(tflops / peak, 4)}
+    except (KeyError, ValueError):
+        return None
+
+
 def copy_bandwidth(torch, nbytes: int = 1 << 31, reps: int = 10) -> float:
     """GB/s of a plain device-to-device copy (bytes read + bytes written)."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -235,6 +264,11 @@ def main() -> int:
                     "traffic": traffic, "kernel": name,
                     "mean_launch_us": round(avg_s * 1e6, 3),
                     "algorithmic_bytes_per_launch": by / n}
+        if cfg.hparams["matrix_approximation_rank"] >= 16:
+            # the matrix-core passes: utilisation from rocprofv3 counters
+            mfma = {k: load_mfma(k, cfg.name)
+                    for k in ("pass1_mq", "pass2_mtp", "pass3_decompress_error")}
+            roofline["mfma"] = {k: v for k, v in mfma.items() if v is not None} or None
     if args.snapshot:
         torch.cuda.synchronize()
         t0 = time.perf_counter()

@@ -8,6 +8,12 @@
         it reads for the largest device-to-device copies in the same run (the copy
         dispatches whose counter value is within 1% of the largest), whose bytes are
         known: they read and write the same number of bytes.
+    python -m rank_gradient_compression_amd.rocprof_summary mean DIR KIND
+        mean launch duration (us) of one kernel kind from DIR/*kernel_stats.csv
+    python -m rank_gradient_compression_amd.rocprof_summary mfma UTIL_DIR MOPS_DIR KIND
+        matrix-core use of one kernel kind from two --pmc runs: the derived MfmaUtil
+        (percent of SIMD cycles with the matrix core busy), then the MFMA operation
+        counts SQ_INSTS_VALU_MFMA_MOPS_{F32,F16,BF16} (512 flops each).
 
 The traffic summary carries `source_hash`, a digest of the kernel sources, so a
 measurement is only used while the kernels it was taken on are unchanged.
@@ -66,6 +72,18 @@ def stats(directory: str) -> str:
     return "\n".join(lines)
 
 
+def mean_us(directory: str, kind: str) -> float:
+    """Mean duration (us) of one kernel kind's launches in DIR/*kernel_stats.csv."""
+    path = glob.glob(os.path.join(directory, "*kernel_stats.csv"))[0]
+    total = calls = 0.0
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if re.search(KIND_PATTERNS[kind], r["Name"]):
+                total += float(r["TotalDurationNs"])
+                calls += int(r["Calls"])
+    return total / calls / 1e3 if calls else 0.0
+
+
 def _counter_rows(directory: str):
     path = glob.glob(os.path.join(directory, "*counter_collection.csv"))[0]
     with open(path) as f:
@@ -114,11 +132,55 @@ def traffic_report(fetch_dir: str, write_dir: str, kind: str, workload: str,
     ])
 
 
+def _counter_by_name(directory: str, pattern: str):
+    path = glob.glob(os.path.join(directory, "*counter_collection.csv"))[0]
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if re.search(pattern, r["Kernel_Name"]):
+                out.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in out.items()}, {k: len(v) for k, v in out.items()}
+
+
+def mfma_report(util_dir: str, mops_dir: str, kind: str, workload: str, mean_us: float,
+                command_util: str, command_mops: str) -> str:
+    pat = KIND_PATTERNS[kind]
+    util, n_u = _counter_by_name(util_dir, pat)
+    mops, n_m = _counter_by_name(mops_dir, pat)
+    flops = 512.0 * sum(v for k, v in mops.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
+    lines = [
+        f"# matrix-core use per launch of {kind} on the {workload} workload",
+        f"# utilisation command: {command_util}",
+        f"# operations command: {command_mops}",
+        f"kernel_kind: {kind}",
+        f"workload: {workload}",
+        f"source_hash: {source_hash()}",
+        f"mfma_util_percent: {util.get('MfmaUtil', float('nan')):.2f}  "
+        f"(mean of {n_u.get('MfmaUtil', 0)} dispatches)",
+    ]
+    for k in sorted(mops):
+        lines.append(f"{k.lower()}_per_launch: {mops[k]:.0f}")
+    kinds = {k.rsplit("_", 1)[1]: v for k, v in mops.items()
+             if k.startswith("SQ_INSTS_VALU_MFMA_MOPS_")}
+    if kinds:
+        lines.append(f"mfma_dtype: {max(kinds, key=kinds.get)}")
+    lines.append(f"mfma_flops_per_launch: {flops:.0f}")
+    if mean_us > 0:
+        lines.append(f"mean_launch_us: {mean_us:.2f}  (kernel statistics of the same workload)")
+        lines.append(f"mfma_tflops: {flops / (mean_us * 1e-6) / 1e12:.2f}")
+    return "\n".join(lines)
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(stats(sys.argv[2]))
     elif sys.argv[1] == "traffic":
         print(traffic_report(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5],
                              int(sys.argv[6]), sys.argv[7], sys.argv[8]))
+    elif sys.argv[1] == "mfma":
+        print(mfma_report(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5],
+                          float(sys.argv[6]), sys.argv[7], sys.argv[8]))
+    elif sys.argv[1] == "mean":
+        print(f"{mean_us(sys.argv[2], sys.argv[3]):.3f}")
     elif sys.argv[1] == "hash":
         print(source_hash())

@@ -87,3 +87,39 @@ def test_workload_definitions():
         assert c.wrap in ("", "f16", "bf16")
         assert c.grad_scale > 0 and np.log2(c.grad_scale) == int(np.log2(c.grad_scale))
         assert not (c.wrap and c.dtype != "f32")
+
+
+def test_mfma_summary_and_its_hash_gate(tmp_path, monkeypatch):
+    util, mops = tmp_path / "u", tmp_path / "m"
+    util.mkdir()
+    mops.mkdir()
+    kern = "void psgd::kern::k_pass2_mfma<32, false, true, 2>(psgd::Pass2Args)"
+
+    def write(path, rows):
+        with open(path / "run_counter_collection.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name",
+                                              "Counter_Value"])
+            w.writeheader()
+            for name, c, v in rows:
+                w.writerow({"Kernel_Name": name, "Grid_Size": 1, "Counter_Name": c,
+                            "Counter_Value": v})
+
+    write(util, [(kern, "MfmaUtil", 10.0), (kern, "MfmaUtil", 14.0), ("other", "MfmaUtil", 99)])
+    write(mops, [(kern, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 1000.0),
+                 (kern, "SQ_INSTS_VALU_MFMA_MOPS_F32", 10.0)])
+    rep = rs.mfma_report(str(util), str(mops), "pass2_mtp", "wl", 2.0, "cu", "cm")
+    vals = {l.split(": ", 1)[0]: l.split(": ", 1)[1].split()[0] for l in rep.splitlines()
+            if ": " in l and not l.startswith("#")}
+    assert float(vals["mfma_util_percent"]) == 12.0
+    assert float(vals["mfma_flops_per_launch"]) == 512.0 * 1010.0
+    assert vals["mfma_dtype"] == "BF16"
+    assert float(vals["mfma_tflops"]) == pytest.approx(512.0 * 1010.0 / 2e-6 / 1e12, abs=0.01)
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "mfma_pass2_mtp_wl.txt").write_text(rep + "\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    got = bench.load_mfma("pass2_mtp", "wl")
+    assert got["dtype"] == "bf16" and got["peak_tflops"] == 2500.0
+    assert got["frac"] == pytest.approx(got["tflops"] / 2500.0, abs=1e-4)
+    (prof / "mfma_pass2_mtp_wl.txt").write_text(rep.replace(rs.source_hash(), "0" * 16))
+    assert bench.load_mfma("pass2_mtp", "wl") is None
