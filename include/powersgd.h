@@ -19,6 +19,15 @@
  * completion of that stream work plays the role of the hook's Future. Every
  * function returns before the device work completes unless stated otherwise.
  * A state is not thread-safe; distinct states are independent.
+ *
+ * Stream capture: the first compressing call of a bucket layout (and the first
+ * fp16 or wrapped call before start_powerSGD_iter) allocates, clears and uploads the
+ * layout's buffers and waits for its stream, so it cannot be captured. Every later
+ * call on that layout enqueues kernel launches only and may be captured into a HIP
+ * graph (kernel timing off). A replay repeats the captured launches with their
+ * arguments: the same bucket and found_inf pointers, loss scale and, without warm
+ * start, the same Q draw; the host-side iteration and statistics counters advance
+ * only on real calls. With warm start each replay is one hook step.
  */
 #ifndef POWERSGD_H
 #define POWERSGD_H
