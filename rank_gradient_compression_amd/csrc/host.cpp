@@ -151,6 +151,8 @@ struct BucketPlan {
   QInitJob* d_qinit = nullptr;
   bool allocated = false;
   bool q_ready = false;
+  // every tensor has 16-byte aligned rows (in d_td) at least 256 columns wide
+  bool all_wide = false;
 
   void release() {
     void* ptrs[] = {E, Eh, Mh, P, Praw, Q, QT, partial, gram, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
@@ -457,6 +459,8 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
     pl.max_qrows = std::max(pl.max_qrows, d.m);
     pl.tensors.push_back(d);
   }
+  pl.all_wide = !pl.tensors.empty();
+  for (const TensorDesc& d : pl.tensors) pl.all_wide = pl.all_wide && d.vec && d.lpr == 64;
   pl.e_floats = eoff;
   pl.p_floats = poff;
   pl.q_floats = qoff;
@@ -843,7 +847,9 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
     r = timed_launch(st, s, K_PASS2, ce * pass_bytes(K_PASS2, f16, ef, prec), "pass 2",
-                     [&] { return launch_pass2(R, f16, ef, prec, a, s); });
+                     [&] {
+                       return launch_pass2(R, f16, ef, prec, aligned && pl.all_wide, a, s);
+                     });
     if (r != POWERSGD_OK) return r;
     if (!fused && !pl.tiles2r.empty()) {
       Pass2ReduceArgs b{};

@@ -163,7 +163,11 @@ constexpr int kStBF16 = 2;
 // Launchers (kernels.hip). R is the padded rank (1, 2, 4, 8, 16 or 32); st the state
 // precision (a 16-bit state needs an fp32 bucket).
 hipError_t launch_pass1(int R, bool f16, bool ef, int st, const Pass1Args& a, hipStream_t s);
-hipError_t launch_pass2(int R, bool f16, bool ef, int st, const Pass2Args& a, hipStream_t s);
+// wide_only (16-bit state, vector ranks): every tensor of the table has 16-byte aligned
+// rows at least 256 columns wide, so a kernel compiled with that access mode alone can
+// run (fewer registers, more wavefronts in flight for the state's 8-byte accesses).
+hipError_t launch_pass2(int R, bool f16, bool ef, int st, bool wide_only, const Pass2Args& a,
+                        hipStream_t s);
 hipError_t launch_pass2_reduce(int R, int st, const Pass2ReduceArgs& a, hipStream_t s);
 hipError_t launch_pass3(int R, bool f16, bool ef, int st, const Pass3Args& a, hipStream_t s);
 hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs,

@@ -1098,7 +1098,9 @@ __device__ __forceinline__ void pass2_body(const Pass2Args& args, const TensorDe
   }
 }
 
-template <int R, int U, bool F16, bool EF, int ST>
+// WO: compiled with the wide aligned body only (the host launches it when every
+// tensor of the table takes that body; a tile of any other tensor is left alone).
+template <int R, int U, bool F16, bool EF, int ST, bool WO = false>
 __global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
   if (F16 && *args.found_inf) return;
   __shared__ float red[64 * 4 * R];
@@ -1106,7 +1108,10 @@ __global__ void __launch_bounds__(kThreads) k_pass2(Pass2Args args) {
   __shared__ float sP[kPass2StageFloats];
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
-  if (d.vec && d.lpr == 64)
+  if constexpr (WO) {
+    if (d.vec && d.lpr == 64)
+      pass2_body<R, U, F16, EF, kLdAligned, true, ST>(args, d, t, red, sh, sP);
+  } else if (d.vec && d.lpr == 64)
     pass2_body<R, U, F16, EF, kLdAligned, true, ST>(args, d, t, red, sh, sP);
   else if (d.vec)
     pass2_body<R, U, F16, EF, kLdAligned, false, ST>(args, d, t, red, sh, sP);
@@ -2384,14 +2389,34 @@ hipError_t pass1_r(bool f16, bool ef, int st, const Pass1Args& a, hipStream_t s)
   return hipGetLastError();
 }
 
+// The 16-bit state's pass 2 with the wide aligned body alone.
 template <int R>
-hipError_t pass2_r(bool f16, bool ef, int st, const Pass2Args& a, hipStream_t s) {
+bool pass2_wide16(bool ef, int st, const Pass2Args& a, dim3 grid, hipStream_t s) {
+  if (st == kStF16) {
+    if (ef) k_pass2<R, unroll2<R, kStF16>(), false, true, kStF16, true><<<grid, kThreads, 0, s>>>(a);
+    else k_pass2<R, unroll2<R, kStF16>(), false, false, kStF16, true><<<grid, kThreads, 0, s>>>(a);
+  } else if (st == kStBF16) {
+    if (ef) k_pass2<R, unroll2<R, kStBF16>(), false, true, kStBF16, true><<<grid, kThreads, 0, s>>>(a);
+    else k_pass2<R, unroll2<R, kStBF16>(), false, false, kStBF16, true><<<grid, kThreads, 0, s>>>(a);
+  } else {
+    return false;
+  }
+  return true;
+}
+
+template <int R>
+hipError_t pass2_r(bool f16, bool ef, int st, bool wide_only, const Pass2Args& a,
+                   hipStream_t s) {
   if (a.ntiles == 0) return hipSuccess;
   const dim3 grid(a.ntiles);
   if constexpr (R >= kMfmaMinRank) {
     if (!pass2_mma<R>(f16, ef, st, a, grid, s)) return hipErrorInvalidValue;
   } else {
-    if (!pass2_vec<R>(f16, ef, st, a, grid, s)) return hipErrorInvalidValue;
+    if (wide_only && !f16 && st != kStF32) {
+      if (!pass2_wide16<R>(ef, st, a, grid, s)) return hipErrorInvalidValue;
+    } else if (!pass2_vec<R>(f16, ef, st, a, grid, s)) {
+      return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
@@ -2428,8 +2453,9 @@ hipError_t launch_pass1(int R, bool f16, bool ef, int st, const Pass1Args& a, hi
   PSGD_RANK_SWITCH(R, return pass1_r<RR>(f16, ef, st, a, s))
 }
 
-hipError_t launch_pass2(int R, bool f16, bool ef, int st, const Pass2Args& a, hipStream_t s) {
-  PSGD_RANK_SWITCH(R, return pass2_r<RR>(f16, ef, st, a, s))
+hipError_t launch_pass2(int R, bool f16, bool ef, int st, bool wide_only, const Pass2Args& a,
+                        hipStream_t s) {
+  PSGD_RANK_SWITCH(R, return pass2_r<RR>(f16, ef, st, wide_only, a, s))
 }
 
 hipError_t launch_pass2_reduce(int R, int st, const Pass2ReduceArgs& a, hipStream_t s) {
