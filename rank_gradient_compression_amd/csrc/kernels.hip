@@ -692,15 +692,58 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
           acc[u][k] += x[u][0] * q[0][k] + x[u][1] * q[1][k] + x[u][2] * q[2][k] +
                        x[u][3] * q[3][k];
     }
-    // sum over the slot's threads inside the wavefront
-    const int wmask = lprw < 64 ? lprw : 64;
-    for (int mask = wmask >> 1; mask > 0; mask >>= 1) {
+    if (lprw >= 64) {
+      // sums over the whole wavefront: each of the first log2(U) exchanges halves the
+      // rows a lane holds (lanes with bit 32 >> s set keep the upper half and send the
+      // lower), then the one row left is summed over the remaining lane bits. Lane l
+      // ends with the sums of row uu(l); the lanes with the low bits clear write them.
+      constexpr int H = (U >= 2) + (U >= 4) + (U >= 8) + (U >= 16);
+      static_assert((1 << H) == U, "rows per lane must be a power of two");
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int s = 0; s < H; ++s) {
+        const int mask = 32 >> s;
+        const int half = (U >> s) / 2;
+        const bool up = (lane & mask) != 0;
 #pragma unroll
-        for (int k = 0; k < R; ++k) acc[u][k] += __shfl_xor(acc[u][k], mask);
-    }
-    if (lprw <= 64) {
+        for (int i = 0; i < half; ++i)
+#pragma unroll
+          for (int k = 0; k < R; ++k) {
+            const float lo = acc[i][k];
+            const float hi = acc[i + half][k];
+            acc[i][k] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, mask);
+          }
+      }
+      for (int mask = 32 >> H; mask > 0; mask >>= 1) {
+#pragma unroll
+        for (int k = 0; k < R; ++k) acc[0][k] += __shfl_xor(acc[0][k], mask);
+      }
+      int uu = 0;
+#pragma unroll
+      for (int s = 0; s < H; ++s) uu += (lane & (32 >> s)) ? (U >> (s + 1)) : 0;
+      const int row = rw + uu * slots + slot;
+      if ((lane & ((64 >> H) - 1)) == 0 && row < r1) {
+        if (lprw == 64) {
+          float pr[R];
+#pragma unroll
+          for (int k = 0; k < R; ++k) pr[k] = (k < d.rank) ? rnd16<ST>(acc[0][k]) : 0.f;
+          store_p_row<R>(args.P + d.poff, row, pr);
+          if constexpr (GRAM) gram_add<R>(gacc, pr);
+        } else {
+          // a slot spans wps wavefronts: park this wavefront's sums until the tile ends
+          const int wps = lprw >> 6;
+          float* dst = red + ((row - r0) * wps + (wave & (wps - 1))) * R;
+#pragma unroll
+          for (int k = 0; k < R; ++k) dst[k] = acc[0][k];
+        }
+      }
+    } else {
+      // a slot inside a wavefront: sum over its lprw lanes, its first lane writes
+      for (int mask = lprw >> 1; mask > 0; mask >>= 1) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int k = 0; k < R; ++k) acc[u][k] += __shfl_xor(acc[u][k], mask);
+      }
       if (g == 0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -712,17 +755,6 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
             store_p_row<R>(args.P + d.poff, row, pr);
             if constexpr (GRAM) gram_add<R>(gacc, pr);
           }
-        }
-      }
-    } else if (lane == 0) {
-      // a slot spans wps wavefronts: park this wavefront's sums until the tile ends
-      const int wps = lprw >> 6;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (rok[u]) {
-          float* dst = red + ((rw + u * slots + slot - r0) * wps + (wave & (wps - 1))) * R;
-#pragma unroll
-          for (int k = 0; k < R; ++k) dst[k] = acc[u][k];
         }
       }
     }
