@@ -213,7 +213,7 @@ hipError_t launch_unscale_only(const FlatTile* ftiles, int nftiles, void* bucket
 #define PSGD_PASS3_ROWS_H PSGD_PASS3_ROWS
 #endif
 #ifndef PSGD_TILES_PER_BUCKET
-#define PSGD_TILES_PER_BUCKET 4096  // work items aimed at per pass (before clamping)
+#define PSGD_TILES_PER_BUCKET 16384  // work items aimed at per pass (before clamping)
 #endif
 #ifndef PSGD_PASS2_TILE_SCALE
 #define PSGD_PASS2_TILE_SCALE 4  // pass-2 work items this many times larger (vector ranks)
