@@ -143,6 +143,7 @@ POWERSGD_API void powersgd_state_destroy(powersgd_state* st);
  * Errors are returned before anything is enqueued: INVALID_ARG (NULL state/bucket
  * or views with nviews > 0, numel < 0, view out of bounds, overlapping views,
  * ndim out of range, negative dimension, F16 without found_inf_dev, unknown dtype),
+ * UNSUPPORTED (a compressed view with more than 2^31 - 65537 rows or columns),
  * LAYOUT_CHANGED, OOM, HIP (launch failure; asynchronous faults surface at the
  * caller's next synchronization).
  */
@@ -214,7 +215,7 @@ POWERSGD_API int64_t powersgd_batched_side(int64_t numel);
  * Statistics count numel elements in and 2 * s * rank communicated per call.
  * Errors: INVALID_ARG (NULL state, NULL bucket with numel > 0, numel < 0, capacity
  * below s * s, F16 without found_inf_dev, unknown dtype), UNSUPPORTED (s above
- * 2^31 - 1), LAYOUT_CHANGED, OOM, HIP; all returned before anything is enqueued.
+ * 2^31 - 65537), LAYOUT_CHANGED, OOM, HIP; all returned before anything is enqueued.
  */
 POWERSGD_API powersgd_status powersgd_compress_bucket_batched(powersgd_state* st,
                                                  int64_t bucket_index, int32_t is_last,
@@ -237,7 +238,7 @@ POWERSGD_API powersgd_status powersgd_compress_bucket_batched(powersgd_state* st
  *   bucket_index, is_last, stream: as for powersgd_compress_bucket.
  *
  * Errors: INVALID_ARG (NULL state, NULL bucket with numel > 0, numel < 0, capacity
- * below s * s, compute_dtype not F16/BF16), UNSUPPORTED (s above 2^31 - 1),
+ * below s * s, compute_dtype not F16/BF16), UNSUPPORTED (s above 2^31 - 65537),
  * LAYOUT_CHANGED, OOM, HIP; all returned before anything is enqueued.
  */
 POWERSGD_API powersgd_status powersgd_compress_bucket_batched_wrapped(powersgd_state* st,

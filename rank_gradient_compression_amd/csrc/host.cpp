@@ -327,8 +327,8 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
       // the batched variant compresses its one square matrix without a rate test
       comp = batched ? (n > 0 && m > 0) : should_compress(n, m, rank, hp.min_compression_rate);
       if (comp) {
-        if (n > INT32_MAX || m > INT32_MAX)
-          return fail(POWERSGD_ERR_UNSUPPORTED, "matrix dimension above 2^31 - 1");
+        if (n > kMaxMatrixDim || m > kMaxMatrixDim)
+          return fail(POWERSGD_ERR_UNSUPPORTED, "matrix dimension above 2^31 - 65537");
         pl.view_n[v] = n;
         pl.view_m[v] = m;
         pl.view_rank[v] = static_cast<int32_t>(rank);
@@ -977,7 +977,7 @@ powersgd_status powersgd_compress_bucket_batched_wrapped(powersgd_state* st, int
   else
     return fail(POWERSGD_ERR_INVALID_ARG, "compute_dtype must be F16 or BF16");
   const int64_t side = batched_side(numel);
-  if (side > INT32_MAX) return fail(POWERSGD_ERR_UNSUPPORTED, "bucket too large for the batched view");
+  if (side > kMaxMatrixDim) return fail(POWERSGD_ERR_UNSUPPORTED, "bucket too large for the batched view");
   if (capacity < side * side)
     return fail(POWERSGD_ERR_INVALID_ARG,
                 "capacity " + std::to_string(capacity) + " is below the padded square of " +
@@ -1004,7 +1004,7 @@ powersgd_status powersgd_compress_bucket_batched(powersgd_state* st, int64_t buc
   if (f16 && !std::isfinite(inv_loss_scale))
     return fail(POWERSGD_ERR_INVALID_ARG, "inv_loss_scale must be finite");
   const int64_t side = batched_side(numel);
-  if (side > INT32_MAX) return fail(POWERSGD_ERR_UNSUPPORTED, "bucket too large for the batched view");
+  if (side > kMaxMatrixDim) return fail(POWERSGD_ERR_UNSUPPORTED, "bucket too large for the batched view");
   if (capacity < side * side)
     return fail(POWERSGD_ERR_INVALID_ARG,
                 "capacity " + std::to_string(capacity) + " is below the padded square of " +
@@ -1434,7 +1434,7 @@ powersgd_status read_bucket(const powersgd_hparams& hp, SnapReader& rd, int64_t 
   std::vector<ViewKey> keys;
   if (batched) {
     const int64_t side = batched_side(numel);
-    if (side > INT32_MAX) return fail(POWERSGD_ERR_UNSUPPORTED, "snapshot: batched bucket too large");
+    if (side > kMaxMatrixDim) return fail(POWERSGD_ERR_UNSUPPORTED, "snapshot: batched bucket too large");
     const bool ok = numel == 0 ? nviews == 0
                                : nviews == 1 && views[0].offset == 0 && views[0].ndim == 2 &&
                                      views[0].shape[0] == side && views[0].shape[1] == side;

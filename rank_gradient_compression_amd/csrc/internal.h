@@ -239,6 +239,10 @@ constexpr int kReduceThreads = 1024;
 // Vector ranks: floats of orthogonalized P rows a pass-2 workgroup keeps in LDS (the
 // plan keeps row blocks at or below kPass2StageFloats / R rows).
 constexpr int kPass2StageFloats = 4096;
+// Largest row or column count of a compressed matrix. The kernels index rows and
+// columns in 32 bits and address up to a few thousand rows past a work item's last row
+// before clamping (rows in flight times row slots), so the limit keeps that headroom.
+constexpr int64_t kMaxMatrixDim = 2147483647LL - 65536;
 // Rows per Gram partial of the separate Gram kernel.
 constexpr int kGramRows = 256;
 // Rows transformed by one workgroup of the orthogonalization kernel (each workgroup
