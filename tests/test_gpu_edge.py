@@ -301,3 +301,34 @@ def test_tall_narrow_matrices_keep_their_p_rows_in_lds():
     hp = _hp(matrix_approximation_rank=8, min_compression_rate=0.5)
     par = _run_parity(hp, [(5003, 4), (3001, 12), (2049, 9), (40,)], steps=3, seed=7)
     assert par.gpu.decisions(0, 4) == [1, 1, 1, 0]
+
+
+def test_matrix_dimension_limit_is_rejected_before_device_work():
+    """Rows and columns of a compressed matrix stop at 2^31 - 65537 (the kernels index
+    rows in 32 bits with headroom past a work item's end). The sizes below are only
+    claimed: every call returns its error before touching the 16-element buffer."""
+    log("case: matrix dimension limit")
+    lim = 2 ** 31 - 65537
+    st = PowerSGDState(matrix_approximation_rank=1, start_powerSGD_iter=0,
+                       compression_stats_logging_frequency=0)
+    buf = torch.zeros(16, device="cuda")
+    # a (lim + 1) x 8 view passes the rate test; the plan refuses it
+    with pytest.raises(PowerSGDError) as ei:
+        api.powersgd_compress_bucket(st._state, 0, True, buf.data_ptr(), api.POWERSGD_F32,
+                                     (lim + 1) * 8, [(0, (lim + 1, 8))], 1.0, None, None)
+    assert ei.value.status == api.POWERSGD_ERR_UNSUPPORTED
+    # batched view: side lim + 1 is refused; side lim passes that check and stops at
+    # the capacity check
+    assert api.powersgd_batched_side(lim * lim + 1) == lim + 1
+    with pytest.raises(PowerSGDError) as ei:
+        api.powersgd_compress_bucket_batched(st._state, 1, True, buf.data_ptr(),
+                                             api.POWERSGD_F32, lim * lim + 1, 2 ** 62, 1.0,
+                                             None, None)
+    assert ei.value.status == api.POWERSGD_ERR_UNSUPPORTED
+    with pytest.raises(PowerSGDError) as ei:
+        api.powersgd_compress_bucket_batched(st._state, 1, True, buf.data_ptr(),
+                                             api.POWERSGD_F32, lim * lim, 16, 1.0, None, None)
+    assert ei.value.status == api.POWERSGD_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(buf).item() == 0
+    assert st.stats()[0] == 0  # no call got as far as the iteration counter
