@@ -7,6 +7,7 @@ torch streams. There is no CPU fallback: if the library is missing, loading fail
 """
 from __future__ import annotations
 
+import array
 import ctypes
 import os
 from typing import Iterable, List, Optional, Sequence, Tuple
@@ -158,16 +159,49 @@ def powersgd_last_error() -> str:
     return load_library().powersgd_last_error().decode()
 
 
-def make_views(views: Sequence[Tuple[int, Sequence[int]]]):
-    arr = (powersgd_view * max(1, len(views)))()
+_VIEW_WORDS = 2 + POWERSGD_MAX_NDIM  # offset, ndim, shape[POWERSGD_MAX_NDIM] (int64 each)
+
+
+class PreparedViews:
+    """A views list marshalled once into the C array the library reads. Every function
+    that takes `views` also takes one of these, which spares a per-call conversion
+    when the same layout is compressed every step (as a DDP hook does per bucket)."""
+
+    __slots__ = ("array", "count")
+
+    def __init__(self, views: Sequence[Tuple[int, Sequence[int]]]):
+        self.array = _marshal_views(views)
+        self.count = len(views)
+
+    def __len__(self) -> int:
+        return self.count
+
+
+def _marshal_views(views) -> ctypes.Array:
+    n = len(views)
+    flat = [0] * (_VIEW_WORDS * max(1, n))
     for i, (off, shape) in enumerate(views):
-        if len(shape) > POWERSGD_MAX_NDIM:
+        nd = len(shape)
+        if nd > POWERSGD_MAX_NDIM:
             raise ValueError(f"view {i}: more than {POWERSGD_MAX_NDIM} dimensions")
-        arr[i].offset = int(off)
-        arr[i].ndim = len(shape)
-        for d, s in enumerate(shape):
-            arr[i].shape[d] = int(s)
-    return arr
+        b = i * _VIEW_WORDS
+        flat[b] = off
+        flat[b + 1] = nd
+        flat[b + 2:b + 2 + nd] = shape
+    # integers only (a float offset or dimension raises TypeError); the ctypes array
+    # keeps the buffer alive
+    return (powersgd_view * max(1, n)).from_buffer(array.array("q", flat))
+
+
+def _views_arg(views):
+    return views if isinstance(views, PreparedViews) else list(views)
+
+
+def make_views(views):
+    """The C array of powersgd_view for `views` ((offset, shape) pairs, or PreparedViews)."""
+    if isinstance(views, PreparedViews):
+        return views.array
+    return _marshal_views(views)
 
 
 def powersgd_compress_bucket(state, bucket_index: int, is_last: bool, bucket_ptr: int,
@@ -357,7 +391,7 @@ class PowerSGDState:
                         inv_loss_scale: float = 1.0, found_inf=None, stream=None) -> None:
         dtype, fi = self._bucket_args(bucket, found_inf)
         powersgd_compress_bucket(self._state, bucket_index, is_last, bucket.data_ptr(), dtype,
-                                 bucket.numel(), list(views), inv_loss_scale, fi,
+                                 bucket.numel(), _views_arg(views), inv_loss_scale, fi,
                                  self._stream_handle(stream))
 
     def compress_bucket_wrapped(self, bucket, views: Sequence[Tuple[int, Sequence[int]]],
@@ -372,7 +406,7 @@ class PowerSGDState:
             raise TypeError("the wrapped hook takes a float32 bucket")
         dt = {"f16": POWERSGD_F16, "bf16": POWERSGD_BF16}[compute_dtype]
         powersgd_compress_bucket_wrapped(self._state, bucket_index, is_last, bucket.data_ptr(),
-                                         dt, bucket.numel(), list(views),
+                                         dt, bucket.numel(), _views_arg(views),
                                          self._stream_handle(stream))
 
     def compress_bucket_batched_wrapped(self, buffer, compute_dtype: str = "f16",

@@ -189,3 +189,24 @@ def test_batched_side_is_bit_exact_with_oracle(lib):
     for n in ns:
         assert api.powersgd_batched_side(n) == batched_side(n), n
     assert api.powersgd_batched_side(-5) == 0
+
+
+def test_views_marshalling():
+    """make_views writes offset, ndim and the shape (zero-padded to POWERSGD_MAX_NDIM)
+    of every view; PreparedViews holds the same array; numpy integers and torch.Size
+    are accepted, non-integers and too many dimensions are not."""
+    import numpy as np
+    import torch
+    views = [(0, (4, 5)), (20, (3,)), (23, (2, 3, 4, 5, 1, 1, 1, 2)), (263, ())]
+    for arr in (api.make_views(views), api.make_views(api.PreparedViews(views))):
+        for i, (off, shape) in enumerate(views):
+            assert arr[i].offset == off and arr[i].ndim == len(shape)
+            assert list(arr[i].shape) == list(shape) + [0] * (api.POWERSGD_MAX_NDIM - len(shape))
+    assert len(api.PreparedViews(views)) == 4
+    arr = api.make_views([(np.int64(7), torch.Size([2, 3]))])
+    assert (arr[0].offset, arr[0].ndim, arr[0].shape[0], arr[0].shape[1]) == (7, 2, 2, 3)
+    with pytest.raises(TypeError):
+        api.make_views([(0.5, (2, 2))])
+    with pytest.raises(ValueError):
+        api.make_views([(0, (1,) * (api.POWERSGD_MAX_NDIM + 1))])
+    assert len(api.make_views([])) == 1  # an empty list still passes a valid pointer
