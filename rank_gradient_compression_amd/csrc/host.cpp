@@ -303,10 +303,11 @@ int64_t view_numel(const ViewKey& k) {
 }
 
 // Classification, rate decisions and work tables for one layout (host only).
-powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batched,
+powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batched, int prec,
                            std::vector<ViewKey>&& views, BucketPlan& pl) {
   pl.numel = numel;
   pl.batched = batched;
+  pl.st = prec;
   pl.views = std::move(views);
   const size_t nv = pl.views.size();
   pl.decision.assign(nv, 0);
@@ -355,6 +356,8 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
   const int64_t target =
       std::min<int64_t>(1 << 16, std::max<int64_t>(1 << 13, pl.compressed_elems / PSGD_TILES_PER_BUCKET));
   const int64_t unroll1 = pass1_unroll(R);
+  // pass 1 of a 16-bit state moves 8 B per element: twice as many work items
+  const int64_t target1 = prec != kStF32 ? std::max<int64_t>(1 << 13, target / 2) : target;
   const int64_t ng = static_cast<int64_t>(R) * (R + 1) / 2;
   const bool fused_gram = R <= kMaxFusedGramRank;
   int64_t goff = 0;
@@ -391,7 +394,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
         rows = kMfmaPass1Rows;
       } else {
         const int64_t slots = kThreads / d.lprw;
-        rows = round_up(std::max<int64_t>(1, (target + d.m - 1) / d.m), slots * unroll1);
+        rows = round_up(std::max<int64_t>(1, (target1 + d.m - 1) / d.m), slots * unroll1);
         rows = std::min<int64_t>(rows, round_up(d.n, slots));
         if (d.lprw > 64) {
           // the wavefront sums of every row of the tile are parked in LDS
@@ -739,9 +742,8 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
   }
   if (it == st->buckets.end()) {
     auto pl = std::make_unique<BucketPlan>();
-    powersgd_status b = build_plan(hp, numel, batched, std::move(keys), *pl);
+    powersgd_status b = build_plan(hp, numel, batched, prec, std::move(keys), *pl);
     if (b != POWERSGD_OK) return b;
-    pl->st = prec;
     b = allocate_plan(*pl, ef, s);
     if (b != POWERSGD_OK) return b;
     it = st->buckets.emplace(bucket_index, std::move(pl)).first;
@@ -1446,10 +1448,9 @@ powersgd_status read_bucket(const powersgd_hparams& hp, SnapReader& rd, int64_t 
     if (nviews > INT32_MAX) return snap_bad("too many views");
   }
   out.plan = std::make_unique<BucketPlan>();
-  powersgd_status b = build_plan(hp, numel, batched != 0, std::move(keys), *out.plan);
+  powersgd_status b = build_plan(hp, numel, batched != 0, prec, std::move(keys), *out.plan);
   if (b != POWERSGD_OK) return b;
   BucketPlan& pl = *out.plan;
-  pl.st = prec;
   if (has_q && pl.tensors.empty()) return snap_bad("warm-start Q on a bucket with no compressed view");
   out.has_q = has_q != 0;
   out.e_src.assign(pl.tensors.size(), nullptr);
