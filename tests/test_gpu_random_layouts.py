@@ -1,0 +1,77 @@
+"""GPU parity on seeded random bucket layouts: up to nine views mixing vectors, matrices
+of ragged sizes (1 to 699 rows, 1 to 1399 columns: widths below, at and above the
+lane and column-block sizes, unaligned rows) and 4-D conv-like views, at padded and
+unpadded ranks (1 to 8), rate thresholds 0.5 to 2 (0.5 admits 1 x m matrices, where
+r = min(n, m)), fp32 and fp16 AMP. Values are low-rank plus noise with singular values
+falling as 0.7^j, so P and Q are well determined and held to the same bound as M_hat
+and E."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from parity import BucketParity, log
+from synthetic import packed_views
+
+pytestmark = pytest.mark.gpu
+
+
+def _layout(rng):
+    shapes = []
+    for _ in range(int(rng.integers(1, 10))):
+        kind = rng.random()
+        if kind < 0.25:
+            shapes.append((int(rng.integers(1, 3000)),))
+        elif kind < 0.8:
+            shapes.append((int(rng.integers(1, 700)), int(rng.integers(1, 1400))))
+        else:
+            shapes.append((int(rng.integers(1, 130)), int(rng.integers(1, 40)),
+                           int(rng.integers(1, 4)), int(rng.integers(1, 4))))
+    return shapes
+
+
+def _bucket(shapes, step, seed, scale=1.0):
+    """Per matrix view: a fixed part sum_j 0.7^j u_j v_j^T (j < min(16, n, m), u and v
+    N(0, 1) per view) plus fresh N(0, 0.01^2) noise each step; vectors N(0, 1)."""
+    parts = []
+    for vi, shp in enumerate(shapes):
+        size = math.prod(shp)
+        gs = torch.Generator().manual_seed(seed * 7919 + step * 131 + vi)
+        if len(shp) < 2:
+            parts.append(torch.randn(size, generator=gs, dtype=torch.float64))
+            continue
+        n, m = shp[0], size // shp[0]
+        k = min(16, n, m)
+        g = torch.Generator().manual_seed(seed * 104729 + vi)
+        u = torch.randn(n, k, generator=g, dtype=torch.float64)
+        v = torch.randn(m, k, generator=g, dtype=torch.float64)
+        w = 0.7 ** torch.arange(k, dtype=torch.float64)
+        parts.append(((u * w) @ v.T + 0.01 * torch.randn(n, m, generator=gs,
+                                                         dtype=torch.float64)).reshape(-1))
+    return (torch.cat(parts) * scale).float()
+
+
+RANKS = [1, 2, 3, 4, 5, 8, 1, 2, 3, 4, 6, 7]
+RATES = [2.0, 2.0, 1.0, 2.0, 0.5, 2.0, 0.5, 2.0, 2.0, 1.0, 2.0, 1.5]
+CASES = [(seed, RANKS[seed], RATES[seed], "f32") for seed in range(12)] + \
+        [(12, 2, 2.0, "f16"), (13, 4, 1.0, "f16"), (14, 1, 0.5, "f16")]
+
+
+@pytest.mark.parametrize("seed,rank,rate,dtype", CASES)
+def test_random_layout(seed, rank, rate, dtype):
+    rng = np.random.default_rng(1000 + seed)
+    shapes = _layout(rng)
+    log(f"case: random layout {seed}, rank {rank}, rate {rate}, {dtype}: {shapes}")
+    hp = dict(matrix_approximation_rank=rank, start_powerSGD_iter=0, min_compression_rate=rate,
+              use_error_feedback=True, warm_start=True,
+              orthogonalization_epsilon=0.0 if rank <= 4 else 1e-8, random_seed=seed,
+              compression_stats_logging_frequency=0)
+    par = BucketParity(hp, packed_views(shapes), dtype)
+    scale = 1024.0 if dtype == "f16" else 1.0  # a power-of-two loss scale
+    for step in range(3):
+        b = _bucket(shapes, step, seed, scale)
+        if dtype == "f16":
+            b = b.to(torch.float16)
+        rep = par.step(b, step, inv_loss_scale=1.0 / scale)
+        log(f"  step {step}: " + ", ".join(f"{k}={v:.2e}" for k, v in rep.worst.items()))
