@@ -2,8 +2,8 @@
 of ragged sizes (1 to 699 rows, 1 to 1399 columns: widths below, at and above the
 lane and column-block sizes, unaligned rows) and 4-D conv-like views, at padded and
 unpadded ranks (1 to 8), rate thresholds 0.5 to 2 (0.5 admits 1 x m matrices, where
-r = min(n, m)), fp32 and fp16 AMP, and the fp16/bf16 wrapped hook checked step by step
-from the oracle's state. Values are low-rank plus noise with singular values falling
+r = min(n, m)), fp32 and fp16 AMP, ranks 16 and 32 on the matrix cores, and the
+fp16/bf16 wrapped hook checked step by step from the oracle's state. Values are low-rank plus noise with singular values falling
 as 0.7^j, so P and Q are well determined and held to the same bound as M_hat and E."""
 import math
 
@@ -31,9 +31,9 @@ def _layout(rng):
     return shapes
 
 
-def _bucket(shapes, step, seed, scale=1.0):
-    """Per matrix view: a fixed part sum_j 0.7^j u_j v_j^T (j < min(16, n, m), u and v
-    N(0, 1) per view) plus fresh N(0, 0.01^2) noise each step; vectors N(0, 1)."""
+def _bucket(shapes, step, seed, scale=1.0, kmax=16, decay=0.7):
+    """Per matrix view: a fixed part sum_j decay^j u_j v_j^T (j < min(kmax, n, m), u and
+    v N(0, 1) per view) plus fresh N(0, 0.01^2) noise each step; vectors N(0, 1)."""
     parts = []
     for vi, shp in enumerate(shapes):
         size = math.prod(shp)
@@ -42,11 +42,11 @@ def _bucket(shapes, step, seed, scale=1.0):
             parts.append(torch.randn(size, generator=gs, dtype=torch.float64))
             continue
         n, m = shp[0], size // shp[0]
-        k = min(16, n, m)
+        k = min(kmax, n, m)
         g = torch.Generator().manual_seed(seed * 104729 + vi)
         u = torch.randn(n, k, generator=g, dtype=torch.float64)
         v = torch.randn(m, k, generator=g, dtype=torch.float64)
-        w = 0.7 ** torch.arange(k, dtype=torch.float64)
+        w = decay ** torch.arange(k, dtype=torch.float64)
         parts.append(((u * w) @ v.T + 0.01 * torch.randn(n, m, generator=gs,
                                                          dtype=torch.float64)).reshape(-1))
     return (torch.cat(parts) * scale).float()
@@ -124,3 +124,26 @@ def test_random_layout_wrapped_stepwise(seed, rank, rate, dt):
             for key, v in errs.items():
                 assert v <= tol, (t, vi, key, v, shp)
         log(f"  step {t}: within {tol:.1e}")
+
+
+MFMA_CASES = [(30, 16, 2.0, "f32"), (31, 32, 2.0, "f32"), (32, 32, 1.0, "f32"), (33, 16, 2.0, "f16")]
+
+
+@pytest.mark.parametrize("seed,rank,rate,dtype", MFMA_CASES)
+def test_random_layout_matrix_cores(seed, rank, rate, dtype):
+    """Ranks 16 and 32 (the matrix-core passes) on random layouts; the spectrum falls as
+    0.9^j over up to 64 components, so the 32nd value stays well above the noise."""
+    rng = np.random.default_rng(1000 + seed)
+    shapes = _layout(rng)
+    log(f"case: random layout {seed}, rank {rank}, rate {rate}, {dtype}: {shapes}")
+    hp = dict(matrix_approximation_rank=rank, start_powerSGD_iter=0, min_compression_rate=rate,
+              use_error_feedback=True, warm_start=True, orthogonalization_epsilon=1e-8,
+              random_seed=seed, compression_stats_logging_frequency=0)
+    par = BucketParity(hp, packed_views(shapes), dtype)
+    scale = 256.0 if dtype == "f16" else 1.0
+    for step in range(3):
+        b = _bucket(shapes, step, seed, scale, kmax=64, decay=0.9)
+        if dtype == "f16":
+            b = b.to(torch.float16)
+        rep = par.step(b, step, inv_loss_scale=1.0 / scale)
+        log(f"  step {step}: " + ", ".join(f"{k}={v:.2e}" for k, v in rep.worst.items()))
