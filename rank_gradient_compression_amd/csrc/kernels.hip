@@ -1621,26 +1621,33 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
           make_float4(v[0], v[1], v[2], v[3]);
     }
     if (k0 + kColBlock < m) load_rows(k0 + kColBlock);
+    // this chunk's Q^T fragments do not depend on the tile: request them before the
+    // barrier so their latency overlaps it
+    float b[4][NT][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kc = 64 * wave + 16 * u + 4 * h;
+      const int colc = min(k0 + kc, m - 4);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        load_f4(QTt + static_cast<int64_t>(16 * nt + cl) * d.mstride + colc, b[u][nt]);
+    }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int kc = 64 * wave + 16 * u + 4 * h;  // column inside the chunk
-      const int colc = min(k0 + kc, m - 4);
       const float4 av = *reinterpret_cast<const float4*>(tile + cl * LS + kc);
       const float a4[4] = {av.x, av.y, av.z, av.w};
-      float b[NT][4];
+      if (k0 + kc >= m) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        load_f4(QTt + static_cast<int64_t>(16 * nt + cl) * d.mstride + colc, b[nt]);
-        if (k0 + kc >= m) {
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int a = 0; a < 4; ++a) b[nt][a] = 0.f;
-        }
+          for (int a = 0; a < 4; ++a) b[u][nt][a] = 0.f;
       }
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(a4[s4], b[nt][s4], acc[nt]);
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(a4[s4], b[u][nt][s4], acc[nt]);
     }
     __syncthreads();  // the tile is rewritten by the next chunk
   }
