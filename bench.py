@@ -160,7 +160,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         eprint("bench.py measures one GPU only: the compression step runs on one rank and "
-               "this build issues no collectives; run with --gpus 1.")
+               "the library issues no collectives; run with --gpus 1.")
         return 2
 
     import torch
