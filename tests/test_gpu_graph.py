@@ -73,3 +73,54 @@ def test_steady_state_call_replays_bitwise(name, rank, wrap):
             assert torch.equal(qa.view(torch.int32), qb.view(torch.int32)), (t, vi)
         log(f"  replay {t}: bucket, E and Q bitwise equal to the eager step")
     assert np.isfinite(buf_a.cpu().numpy()).all()
+
+
+def test_amp_call_replays_bitwise_with_an_inf_step():
+    """The fp16 AMP call (fused unscale and inf check) replayed from a graph, the caller
+    clearing found_inf with a fill kernel before each replay; replay 3 carries an inf,
+    so that step is skipped on both sides and found_inf reads 1 only there."""
+    log("case: graph replay, AMP fp16 rank 2 with an inf step")
+    hp = dict(matrix_approximation_rank=2, start_powerSGD_iter=0, warm_start=True,
+              use_error_feedback=True, orthogonalization_epsilon=0.0,
+              compression_stats_logging_frequency=0)
+    a, b = PowerSGDState(**hp), PowerSGDState(**hp)
+    scale = 1024.0
+    xs = [(x * scale).half() for x in _inputs(6, 11)]
+    xs[3][5000] = float("inf")
+    buf_a = torch.empty(NUMEL, dtype=torch.float16, device="cuda")
+    buf_b = torch.empty(NUMEL, dtype=torch.float16, device="cuda")
+    fa = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fb = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def call(st, buf, found, stream=None):
+        st.compress_bucket(buf, VIEWS, inv_loss_scale=1.0 / scale, found_inf=found, stream=stream)
+
+    for st, buf, found in ((a, buf_a, fa), (b, buf_b, fb)):  # allocation and tables
+        buf.copy_(xs[0])
+        call(st, buf, found)
+    torch.cuda.synchronize()
+    assert int(fa.item()) == 0 and int(fb.item()) == 0
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    buf_a.copy_(xs[1])
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        call(a, buf_a, fa, stream=s)
+    for t in range(1, 6):
+        buf_a.copy_(xs[t])
+        fa.zero_()
+        graph.replay()
+        buf_b.copy_(xs[t])
+        fb.zero_()
+        call(b, buf_b, fb)
+        torch.cuda.synchronize()
+        assert int(fa.item()) == int(fb.item()) == int(t == 3), t
+        assert torch.equal(buf_a.view(torch.int16), buf_b.view(torch.int16)), t
+        for vi in (2, 4):
+            ea, eb = a.error(0, vi), b.error(0, vi)
+            _, qa = a.factors(0, vi)
+            _, qb = b.factors(0, vi)
+            torch.cuda.synchronize()
+            assert torch.equal(ea.view(torch.int32), eb.view(torch.int32)), (t, vi)
+            assert torch.equal(qa.view(torch.int32), qb.view(torch.int32)), (t, vi)
+        log(f"  replay {t}: found_inf {int(fa.item())}; bucket, E and Q bitwise equal")
