@@ -124,3 +124,46 @@ def test_amp_call_replays_bitwise_with_an_inf_step():
             assert torch.equal(ea.view(torch.int32), eb.view(torch.int32)), (t, vi)
             assert torch.equal(qa.view(torch.int32), qb.view(torch.int32)), (t, vi)
         log(f"  replay {t}: found_inf {int(fa.item())}; bucket, E and Q bitwise equal")
+
+
+def test_batched_call_replays_bitwise():
+    """batched_powerSGD_hook replayed from a graph: the zero padding of the square matrix
+    is written by a kernel on every call, so the captured call redoes it; the first
+    numel elements (the result) and the padding both match the eager steps bitwise."""
+    log("case: graph replay, batched rank 1")
+    hp = dict(matrix_approximation_rank=1, start_powerSGD_iter=0, warm_start=True,
+              use_error_feedback=True, orthogonalization_epsilon=0.0,
+              compression_stats_logging_frequency=0)
+    a, b = PowerSGDState(**hp), PowerSGDState(**hp)
+    xs = _inputs(6, 13)
+    side = 1
+    while side * side < NUMEL:
+        side += 1
+    buf_a = torch.full((side * side,), 7.0, device="cuda")
+    buf_b = torch.full((side * side,), 7.0, device="cuda")
+    for st, buf in ((a, buf_a), (b, buf_b)):
+        buf[:NUMEL].copy_(xs[0])
+        st.compress_bucket_batched(buf, numel=NUMEL)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    buf_a[:NUMEL].copy_(xs[1])
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        a.compress_bucket_batched(buf_a, numel=NUMEL, stream=s)
+    for t in range(1, 6):
+        buf_a[:NUMEL].copy_(xs[t])
+        buf_a[NUMEL:].fill_(3.0)  # the call must clear the padding itself
+        graph.replay()
+        buf_b[:NUMEL].copy_(xs[t])
+        buf_b[NUMEL:].fill_(5.0)
+        b.compress_bucket_batched(buf_b, numel=NUMEL)
+        torch.cuda.synchronize()
+        assert torch.equal(buf_a.view(torch.int32), buf_b.view(torch.int32)), t
+        ea, eb = a.error(0, 0), b.error(0, 0)
+        _, qa = a.factors(0, 0)
+        _, qb = b.factors(0, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(ea.view(torch.int32), eb.view(torch.int32)), t
+        assert torch.equal(qa.view(torch.int32), qb.view(torch.int32)), t
+        log(f"  replay {t}: buffer, E and Q bitwise equal to the eager step")
