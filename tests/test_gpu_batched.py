@@ -188,3 +188,21 @@ def test_batched_resnet_bucket_full_size():
     log(f"case: {cfg.name} at full size, 3 steps")
     _run(dict(cfg.hparams, compression_stats_logging_frequency=0), cfg.numel, steps=3,
          bucket_fn=lambda step: gen.bucket(step))
+
+
+def _random_batched_cases():
+    """Seeded bucket sizes from 2 to 200 000 elements (squares, one past a square, primes
+    and arbitrary sizes, so the padding runs from 0 to almost 2s) with ranks 1 to 8."""
+    rng = np.random.default_rng(2024)
+    sizes = [int(x) for x in rng.integers(2, 200_000, size=5)] + [317 * 317, 317 * 317 + 1,
+                                                                   199_999, 65_521]
+    ranks = [1, 2, 3, 4, 5, 8, 2, 4, 1]
+    return list(zip(sizes, ranks))
+
+
+@pytest.mark.parametrize("numel,rank", _random_batched_cases())
+def test_batched_parity_seeded_sizes(numel, rank):
+    s = oracle.batched_side(numel)
+    log(f"case: batched, seeded size {numel} -> {s} x {s} ({s * s - numel} padded), r = {rank}")
+    _run(_hp(matrix_approximation_rank=rank, orthogonalization_epsilon=0.0 if rank <= 4 else 1e-8),
+         numel, steps=3, seed=numel % 9973)
