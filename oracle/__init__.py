@@ -10,7 +10,11 @@ Parity status per function (what pins each one is listed in the tests):
   rng.standard_normal_q0 .............. pinned (layout/key invariants, distribution)
   powersgd.should_compress ............ pinned (brute-force integer arithmetic)
   powersgd.gram_schmidt ............... pinned (QR uniqueness, Householder QR,
-                                        closed forms for epsilon > 0)
+                                        closed forms for epsilon > 0, a 200-bit
+                                        mpmath run at condition number 1e14, the
+                                        rank-deficient trajectory's E = 0)
+  ddarith (double-double steps) ....... pinned (exact rationals for TwoSum,
+                                        TwoProduct, sums and dot products)
   OracleState.compress_bucket ......... pinned (rational projection, hand-worked
                                         example, invariants, Eckart-Young limit)
   powersgd.batched_side ............... pinned (brute force over integers)

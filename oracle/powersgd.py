@@ -29,8 +29,9 @@ by an exact power-of-two factor and written back unscaled in fp16 with
 round-to-nearest-even, and on inf/NaN the bucket and all state stay untouched while
 the iteration still advances.
 
-Everything is float64 on the host; the only library routine used as a step is the
-matrix product (numpy's `@`).
+Everything is float64 on the host, except Gram-Schmidt, which runs in double-double
+arithmetic (oracle.ddarith) and rounds its result to float64; the only library
+routine used as a step is the matrix product (numpy's `@`).
 """
 from __future__ import annotations
 
@@ -114,15 +115,32 @@ def gram_schmidt(x: np.ndarray, epsilon: float) -> np.ndarray:
     `orthogonalization_epsilon`: each column is divided by (its 2-norm + epsilon),
     which is what keeps an all-zero column from dividing by zero. After column i is
     normalized, its projection is removed from every later column.
+
+    READING of "orthogonalizes" (the method's exact Gram-Schmidt): the steps run in
+    double-double arithmetic (oracle.ddarith) on the binary64 input, and the result is
+    rounded to binary64. Modified Gram-Schmidt in a precision u loses orthogonality in
+    proportion to u times the condition number of x; warm-started steps on a matrix of
+    rank below r drive that condition number of P past 1e12, where binary64 steps no
+    longer give orthonormal columns while about 106-bit steps still do to 1e-18.
     """
-    q = np.array(x, dtype=np.float64, copy=True)
-    r = q.shape[1]
-    for i in range(r):
-        col = q[:, i]
-        q[:, i] = col / (math.sqrt(float(col @ col)) + epsilon)
-        for j in range(i + 1, r):
-            q[:, j] = q[:, j] - float(q[:, i] @ q[:, j]) * q[:, i]
-    return q
+    from . import ddarith as dd
+    xh = np.array(x, dtype=np.float64, copy=True)
+    r = xh.shape[1] if xh.ndim == 2 else 0
+    hi = [xh[:, j].copy() for j in range(r)]
+    lo = [np.zeros_like(xh[:, 0]) for _ in range(r)] if r else []
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        for i in range(r):
+            nh, nl = dd.dd_dot(hi[i], lo[i], hi[i], lo[i])
+            ih, il = dd.inverse_norm_plus(nh, nl, float(epsilon))
+            hi[i], lo[i] = dd.dd_mul(hi[i], lo[i], ih, il)
+            for j in range(i + 1, r):
+                ch, cl = dd.dd_dot(hi[i], lo[i], hi[j], lo[j])
+                ph, pl = dd.dd_mul(hi[i], lo[i], -ch, -cl)
+                hi[j], lo[j] = dd.dd_add(hi[j], lo[j], ph, pl)
+    out = np.empty_like(xh)
+    for j in range(r):
+        out[:, j] = hi[j] + lo[j]
+    return out
 
 
 @dataclass
