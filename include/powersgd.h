@@ -68,14 +68,14 @@ typedef enum { POWERSGD_F32 = 0, POWERSGD_F16 = 1, POWERSGD_BF16 = 2 } powersgd_
  */
 typedef struct {
   int32_t matrix_approximation_rank;            /* r; default 1; 1..POWERSGD_MAX_RANK  */
-  int32_t use_error_feedback;                   /* default 1                           */
   int64_t start_powerSGD_iter;                  /* default 1000; >= 0                  */
   double min_compression_rate;                  /* default 2; any finite value         */
+  int32_t use_error_feedback;                   /* default 1                           */
   int32_t warm_start;                           /* default 1                           */
-  int32_t batch_tensors_with_same_shape;        /* default 0                           */
   double orthogonalization_epsilon;             /* default 0; >= 0, finite             */
   uint64_t random_seed;                         /* default 0                           */
   int64_t compression_stats_logging_frequency;  /* default 10000; <= 0 disables logs   */
+  int32_t batch_tensors_with_same_shape;        /* default 0                           */
 } powersgd_hparams;
 
 /*
@@ -87,8 +87,8 @@ typedef struct {
  */
 typedef struct {
   int64_t offset;
-  int64_t ndim;
-  int64_t shape[POWERSGD_MAX_NDIM];
+  int32_t ndim;                        /* 0..POWERSGD_MAX_NDIM */
+  int64_t shape[POWERSGD_MAX_NDIM];    /* entries past ndim are ignored */
 } powersgd_view;
 
 /* Fills hp with the defaults printed in the PowerSGDState signature. Never fails
@@ -296,6 +296,69 @@ POWERSGD_API powersgd_status powersgd_copy_factors(powersgd_state* st, int64_t b
  * `stream`. NOT_FOUND without error feedback. */
 POWERSGD_API powersgd_status powersgd_copy_error(powersgd_state* st, int64_t bucket_index,
                                     int32_t view, float* e_dev, void* stream);
+
+/*
+ * The factors of compressed view v after the bucket's latest call ("PowerSGD Hooks",
+ * powerSGD_hook steps 3.4 and 3.5: P after Gram-Schmidt and Q = M'^T P, which the
+ * state memorizes as the next warm-start Q). On return *P_dev points to n x r fp32
+ * values (row-major, row stride r) and *Q_dev to m x r (row stride r), r = min(rank,
+ * n, m); *n, *m, *r receive the shape. Any output pointer may be NULL.
+ *
+ * The pointers are state-owned device memory holding a copy taken for this call: the
+ * copies are enqueued on the stream of the bucket's latest compressing call, behind
+ * that call's work, so the values may be read once that stream has reached this
+ * point. The memory stays valid until the bucket's state is released (state
+ * destroyed, snapshot imported, or the bucket_index given a new layout); its contents
+ * change only at the next get_factors call for the same view. The first call for a
+ * view allocates (not graph-capturable); later calls enqueue copies only.
+ * Errors: INVALID_ARG (NULL state, view out of range), NOT_FOUND (bucket never
+ * compressed, or view not compressed), OOM, HIP.
+ */
+POWERSGD_API powersgd_status powersgd_get_factors(powersgd_state* st, int64_t bucket_index,
+                                                  int32_t view, const float** P_dev,
+                                                  const float** Q_dev, int64_t* n, int64_t* m,
+                                                  int32_t* r);
+
+/*
+ * The error-feedback memory of a bucket ("PowerSGD Hooks", first warning: memory of
+ * the size of the gradients, E = M' - M_hat after each call) laid out like the bucket:
+ * *E_dev points to one fp32 value per bucket element (numel elements; the batched
+ * variant: its s x s padded matrix), E of each compressed view at that view's
+ * offset, zero elsewhere (uncompressed views carry no error on one rank). A 16-bit
+ * state's values are widened exactly.
+ *
+ * The pointer is state-owned device memory filled for this call on the stream of the
+ * bucket's latest compressing call, behind that call's work; it stays valid until the
+ * bucket's state is released and its contents change only at the next get_error call
+ * on the bucket. The first call allocates (not graph-capturable).
+ * Errors: INVALID_ARG (NULL state or E_dev), NOT_FOUND (bucket never compressed, or
+ * error feedback off), OOM, HIP.
+ */
+POWERSGD_API powersgd_status powersgd_get_error(powersgd_state* st, int64_t bucket_index,
+                                                const float** E_dev);
+
+/*
+ * The raw initial draw of Q ("PowerSGD Hooks", powerSGD_hook step 3.1: Q initialized
+ * from a standard normal distribution, before its orthogonalization) for view `view`
+ * of bucket `bucket_index`, exactly as a compressing call draws it: entry e of the
+ * row-major m x rank matrix is output word e mod 4 of Philox4x64-10 (Salmon et al.,
+ * SC 2011) with counter (e div 4, view, epoch, 0) and key (random_seed, bucket_index);
+ * words (w0, w1) and (w2, w3) give Box-Muller pairs with u = ((w_even >> 11) + 1) *
+ * 2^-53 and v = (w_odd >> 11) * 2^-53 in binary64, rounded to binary32. A compressing
+ * call uses epoch 0 under warm start and the iteration counter otherwise.
+ *
+ *   out_dev    device, m * rank floats (row-major, row stride rank), caller-owned.
+ *   words_dev  device, 4 * ceil(m * rank / 4) uint64 Philox output words in counter
+ *              order, caller-owned; may be NULL.
+ *   stream     hipStream_t (NULL = the legacy default stream).
+ * Runs on the calling thread's current HIP device. Stateless; allocates nothing. Errors: INVALID_ARG (m < 0, rank < 1, view < 0,
+ * NULL out_dev with m > 0), UNSUPPORTED (rank above POWERSGD_MAX_RANK or m above
+ * 2^31 - 65537), HIP.
+ */
+POWERSGD_API powersgd_status powersgd_draw_q0(uint64_t random_seed, int64_t bucket_index,
+                                              int32_t view, uint64_t epoch, int64_t m,
+                                              int32_t rank, float* out_dev,
+                                              uint64_t* words_dev, void* stream);
 
 /*
  * Iteration counter and compression statistics ("PowerSGD State",

@@ -136,6 +136,7 @@ struct BucketPlan {
   float* QT = nullptr;  // matrix-core ranks: Q transposed
   float* partial = nullptr;
   double* gram = nullptr;
+  double* tmat = nullptr;  // the r x r transform of each orthogonalization job
   Tile* d_pgram_tiles = nullptr;
   Tile* d_qgram_tiles = nullptr;
   TensorDesc* d_td = nullptr;         // rows vector-aligned where possible
@@ -149,26 +150,35 @@ struct BucketPlan {
   OrthJob* d_pjobs = nullptr;
   OrthJob* d_qjobs = nullptr;
   QInitJob* d_qinit = nullptr;
+  // introspection copies (allocated on first use): the bucket-shaped E of
+  // powersgd_get_error and the compact factors of powersgd_get_factors
+  float* intro_E = nullptr;
+  float* intro_PQ = nullptr;
+  std::vector<int64_t> intro_off;  // per tensor: first float of its compact P, then Q
+  hipStream_t last_stream = nullptr;  // stream of the latest compressing call
   bool allocated = false;
   bool q_ready = false;
   // every tensor has 16-byte aligned rows (in d_td) at least 256 columns wide
   bool all_wide = false;
 
   void release() {
-    void* ptrs[] = {E, Eh, Mh, P, Praw, Q, QT, partial, gram, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
+    void* ptrs[] = {E, Eh, Mh, P, Praw, Q, QT, partial, gram, tmat, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
                     d_tiles1, d_tiles2, d_tiles3, d_tiles2r, d_flat_unc, d_flat_all, d_pjobs, d_qjobs,
-                    d_qinit};
+                    d_qinit, intro_E, intro_PQ};
     for (void* p : ptrs)
       if (p) (void)hipFree(p);
     E = P = Praw = Q = QT = partial = nullptr;
     Eh = Mh = nullptr;
     gram = nullptr;
+    tmat = nullptr;
     d_pgram_tiles = d_qgram_tiles = nullptr;
     d_td = d_td_scalar = nullptr;
     d_tiles1 = d_tiles2 = d_tiles3 = d_tiles2r = nullptr;
     d_flat_unc = d_flat_all = nullptr;
     d_pjobs = d_qjobs = nullptr;
     d_qinit = nullptr;
+    intro_E = intro_PQ = nullptr;
+    intro_off.clear();
     allocated = false;
   }
   ~BucketPlan() { release(); }
@@ -416,7 +426,8 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
       if (!fused_gram)
         for (int32_t pp = 0; pp < nparts; ++pp)
           pl.pgram_tiles.push_back(Tile{static_cast<int32_t>(pl.pjobs.size() - 1), pp, 0, 0});
-      goff += nparts * ng;
+      // pass 1's partials are fp64; the Gram kernel's are double-double
+      goff += nparts * ng * (fused_gram ? 1 : 2);
     }
     // pass 2 / pass 3: (row block) x (256-column block)
     const int64_t width = std::min<int64_t>(d.m, kColBlock);
@@ -454,7 +465,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
           OrthJob{d.qoff, goff, d.qtoff, d.m, d.rank, nparts, kGramRows, d.mstride, 0});
       for (int32_t pp = 0; pp < nparts; ++pp)
         pl.qgram_tiles.push_back(Tile{static_cast<int32_t>(pl.qjobs.size() - 1), pp, 0, 0});
-      goff += nparts * ng;
+      goff += nparts * ng * 2;  // double-double partials
     }
     pl.qinit.push_back(QInitJob{d.qoff, d.m, d.rank, d.view, 0});
     pl.max_qcount = std::max<int64_t>(pl.max_qcount, static_cast<int64_t>(d.m) * d.rank);
@@ -495,6 +506,8 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   ok = ok && alloc(reinterpret_cast<void**>(&pl.QT), pl.qt_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.partial), pl.partial_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.gram), pl.gram_doubles * sizeof(double));
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.tmat),
+                   pl.tensors.size() * static_cast<size_t>(pl.R) * pl.R * sizeof(double));
 
   if (!ok) {
     pl.release();
@@ -749,6 +762,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     it = st->buckets.emplace(bucket_index, std::move(pl)).first;
   }
   BucketPlan& pl = *it->second;
+  pl.last_stream = s;
   const int R = pl.R;
   const int nt = static_cast<int>(pl.tensors.size());
   const bool aligned = (base % 16) == 0;
@@ -777,8 +791,8 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
       });
       if (r != POWERSGD_OK) return r;
       r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize Q", [&] {
-        return launch_orth(R, pl.d_qjobs, nt, pl.max_qrows, pl.Q, pl.QT, pl.gram, eps, nullptr,
-                           prec, s);
+        return launch_orth(R, pl.d_qjobs, nt, pl.max_qrows, pl.Q, pl.QT, pl.gram, pl.tmat, eps,
+                           nullptr, prec, s);
       });
       if (r != POWERSGD_OK) return r;
     }
@@ -826,8 +840,8 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     }
     if (!fused) {
       r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize P", [&] {
-        return launch_orth(R, pl.d_pjobs, nt, pl.max_prows, pl.P, nullptr, pl.gram, eps,
-                           f16 ? found_inf_dev : nullptr, prec, s);
+        return launch_orth(R, pl.d_pjobs, nt, pl.max_prows, pl.P, nullptr, pl.gram, pl.tmat,
+                           eps, f16 ? found_inf_dev : nullptr, prec, s);
       });
       if (r != POWERSGD_OK) return r;
     }
@@ -1135,6 +1149,98 @@ powersgd_status powersgd_copy_error(powersgd_state* st, int64_t bucket_index, in
   return POWERSGD_OK;
 }
 
+powersgd_status powersgd_get_factors(powersgd_state* st, int64_t bucket_index, int32_t view,
+                                     const float** P_dev, const float** Q_dev, int64_t* n,
+                                     int64_t* m, int32_t* r) {
+  BucketPlan* pl = nullptr;
+  const TensorDesc* d = nullptr;
+  powersgd_status rs = find_tensor(st, bucket_index, view, &pl, &d);
+  if (rs != POWERSGD_OK) return rs;
+  HipDeviceGuard guard(st->device);
+  if (!guard.ok) return fail(POWERSGD_ERR_HIP, "hipSetDevice failed");
+  if (!pl->intro_PQ) {
+    // one compact n x rank P and m x rank Q per tensor, in tensor order
+    std::vector<int64_t> off;
+    int64_t total = 0;
+    for (const TensorDesc& t : pl->tensors) {
+      off.push_back(total);
+      total += (static_cast<int64_t>(t.n) + t.m) * t.rank;
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, std::max<int64_t>(total, 1) * sizeof(float)) != hipSuccess)
+      return fail(POWERSGD_ERR_OOM, "allocation of the factor copies failed");
+    pl->intro_PQ = static_cast<float*>(p);
+    pl->intro_off = std::move(off);
+  }
+  const int32_t t = pl->view_tensor[view];
+  float* pc = pl->intro_PQ + pl->intro_off[t];
+  float* qc = pc + static_cast<int64_t>(d->n) * d->rank;
+  hipStream_t s = pl->last_stream;
+  const size_t R = pl->R;
+  hipError_t e = hipMemcpy2DAsync(pc, d->rank * sizeof(float), pl->P + d->poff,
+                                  R * sizeof(float), d->rank * sizeof(float), d->n,
+                                  hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpy2DAsync(qc, d->rank * sizeof(float), pl->Q + d->qoff, R * sizeof(float),
+                         d->rank * sizeof(float), d->m, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "copy of the factors");
+  if (P_dev) *P_dev = pc;
+  if (Q_dev) *Q_dev = qc;
+  if (n) *n = d->n;
+  if (m) *m = d->m;
+  if (r) *r = d->rank;
+  return POWERSGD_OK;
+}
+
+powersgd_status powersgd_get_error(powersgd_state* st, int64_t bucket_index, const float** E_dev) {
+  if (!st || !E_dev) return fail(POWERSGD_ERR_INVALID_ARG, "NULL argument");
+  auto it = st->buckets.find(bucket_index);
+  if (it == st->buckets.end()) return fail(POWERSGD_ERR_NOT_FOUND, "bucket never compressed");
+  BucketPlan& pl = *it->second;
+  if (!pl.E && !pl.Eh) return fail(POWERSGD_ERR_NOT_FOUND, "error feedback is off");
+  HipDeviceGuard guard(st->device);
+  if (!guard.ok) return fail(POWERSGD_ERR_HIP, "hipSetDevice failed");
+  // the batched variant's bucket is its s x s padded matrix
+  const int64_t len = pl.batched ? (pl.tensors.empty() ? 0 : view_numel(pl.views[0]))
+                                 : pl.numel;
+  if (!pl.intro_E) {
+    void* p = nullptr;
+    if (hipMalloc(&p, std::max<int64_t>(len, 1) * sizeof(float)) != hipSuccess)
+      return fail(POWERSGD_ERR_OOM, "allocation of the bucket-shaped error failed");
+    pl.intro_E = static_cast<float*>(p);
+  }
+  hipStream_t s = pl.last_stream;
+  hipError_t e = launch_fill_zero(pl.intro_E, false, 0, len, s);
+  for (const TensorDesc& d : pl.tensors) {
+    if (e != hipSuccess) break;
+    const int64_t cnt = static_cast<int64_t>(d.n) * d.m;
+    if (pl.Eh)
+      e = launch_widen16(pl.Eh + d.eoff, pl.intro_E + d.boff, cnt, pl.st, s);
+    else
+      e = hipMemcpyAsync(pl.intro_E + d.boff, pl.E + d.eoff, cnt * sizeof(float),
+                         hipMemcpyDeviceToDevice, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "fill of the bucket-shaped error");
+  *E_dev = pl.intro_E;
+  return POWERSGD_OK;
+}
+
+powersgd_status powersgd_draw_q0(uint64_t random_seed, int64_t bucket_index, int32_t view,
+                                 uint64_t epoch, int64_t m, int32_t rank, float* out_dev,
+                                 uint64_t* words_dev, void* stream) {
+  if (m < 0) return fail(POWERSGD_ERR_INVALID_ARG, "m < 0");
+  if (rank < 1) return fail(POWERSGD_ERR_INVALID_ARG, "rank < 1");
+  if (view < 0) return fail(POWERSGD_ERR_INVALID_ARG, "view < 0");
+  if (rank > POWERSGD_MAX_RANK) return fail(POWERSGD_ERR_UNSUPPORTED, "rank above 32");
+  if (m > kMaxMatrixDim) return fail(POWERSGD_ERR_UNSUPPORTED, "m above 2^31 - 65537");
+  if (m > 0 && !out_dev) return fail(POWERSGD_ERR_INVALID_ARG, "out_dev is NULL");
+  hipError_t e = launch_qdraw(m, rank, view, out_dev, words_dev, random_seed,
+                              static_cast<uint64_t>(bucket_index), epoch,
+                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "initial Q draw");
+  return POWERSGD_OK;
+}
+
 powersgd_status powersgd_get_stats(powersgd_state* st, int64_t* iteration, int64_t* numel_in,
                                    int64_t* numel_comm) {
   if (!st) return fail(POWERSGD_ERR_INVALID_ARG, "state is NULL");
@@ -1428,8 +1534,10 @@ powersgd_status read_bucket(const powersgd_hparams& hp, SnapReader& rd, int64_t 
   std::vector<powersgd_view> views(static_cast<size_t>(nviews));
   for (powersgd_view& pv : views) {
     std::memset(&pv, 0, sizeof(pv));
-    if (!rd.get(pv.offset) || !rd.get(pv.ndim)) return snap_bad("truncated view record");
-    if (pv.ndim < 0 || pv.ndim > POWERSGD_MAX_NDIM) return snap_bad("view ndim out of range");
+    int64_t ndim = 0;  // an i64 in the snapshot, an int32 in powersgd_view
+    if (!rd.get(pv.offset) || !rd.get(ndim)) return snap_bad("truncated view record");
+    if (ndim < 0 || ndim > POWERSGD_MAX_NDIM) return snap_bad("view ndim out of range");
+    pv.ndim = static_cast<int32_t>(ndim);
     for (int64_t d = 0; d < pv.ndim; ++d)
       if (!rd.get(pv.shape[d])) return snap_bad("truncated view shape");
   }

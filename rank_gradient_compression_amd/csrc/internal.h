@@ -173,12 +173,18 @@ hipError_t launch_pass3(int R, bool f16, bool ef, int st, const Pass3Args& a, hi
 hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs,
                        const float* base, double* gram, const int32_t* found_inf,
                        hipStream_t s);
+// Gram-Schmidt of each job's block from its double-double Gram partials: the r x r
+// transforms (tmat: R x R fp64 per job) in one launch, then X <- X T.
 hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, int max_rows, float* base,
-                       float* tbase, const double* gram, double eps,
+                       float* tbase, const double* gram, double* tmat, double eps,
                        const int32_t* found_inf, int st, hipStream_t s);
 hipError_t launch_qinit(int R, const QInitJob* jobs, int njobs, int64_t max_count,
                         float* Q, uint64_t seed, uint64_t bucket_key, uint64_t epoch, int st,
                         hipStream_t s);
+// The raw m x rank draw of one view (row stride rank) and, when words is not null, its
+// Philox output words (4 per counter block).
+hipError_t launch_qdraw(int64_t m, int rank, int view, float* out, uint64_t* words,
+                        uint64_t seed, uint64_t bucket_key, uint64_t epoch, hipStream_t s);
 // 16-bit state outside the compressed views: x <- x rounded to st's precision, in place
 // over fp32 ranges (the wrapper's cast and cast back).
 hipError_t launch_round_only(const FlatTile* ftiles, int nftiles, void* bucket, int st,

@@ -803,10 +803,88 @@ __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
 
 // ------------------------------------------------------------ orthogonalization
 //
-// Gram-Schmidt with epsilon (step 3.4) evaluated on the Gram matrix: every vector
-// the recurrence forms is a combination P c of the columns of P, so its norm and
-// its dot products are c^T G c' with G = P^T P. The recurrence runs on the r x r
-// coefficient vectors in fp64 and the result is applied once, P <- P T, in fp64.
+// Gram-Schmidt with epsilon (step 3.4) needs only the inner products of the columns
+// of P, so it can run on any vectors that have the same inner products. The columns
+// of the upper-triangular Cholesky factor C of the Gram matrix G = P^T P = C^T C are
+// such vectors: r of them, r entries long. The recurrence runs on them in fp64 while
+// the same linear steps are applied to coefficient vectors, which gives the r x r
+// transform T with orthogonalized P = P T (applied once, in fp64). Modified
+// Gram-Schmidt loses orthogonality in proportion to cond(C) = cond(P), not to its
+// square, and C is factored in double-double arithmetic.
+//
+// G arrives as partial sums over row blocks. Products of binary32 values are exact
+// in binary64, so only the sums round: pass 1 accumulates fp64 partials for ranks <= 8;
+// the Gram kernel (matrix-core ranks, and the initial Q at every rank) accumulates
+// double-double ones. An fp64 sum rounds by about sqrt(n) 2^-53 of the diagonal, so a
+// Cholesky pivot below kCholTau of its diagonal entry is not resolved by it: the Gram
+// matrix of that P is then recomputed in double-double from P's rows. This happens for
+// (numerically) rank-deficient P, e.g. M' of rank below r.
+
+constexpr double kCholTau = 0x1p-36;
+
+// Double-double arithmetic (Dekker 1971; Knuth, TAOCP vol. 2, 4.2.2): a value is the
+// unevaluated sum hi + lo with |lo| <= ulp(hi) / 2.
+struct DD {
+  double hi, lo;
+};
+
+// s + e = a + b exactly.
+__device__ __forceinline__ DD dd_two_sum(double a, double b) {
+  const double s = a + b;
+  const double bv = s - a;
+  const double e = (a - (s - bv)) + (b - bv);
+  return DD{s, e};
+}
+
+// s + e = a + b exactly, for |a| >= |b|.
+__device__ __forceinline__ DD dd_fast_two_sum(double a, double b) {
+  const double s = a + b;
+  return DD{s, b - (s - a)};
+}
+
+__device__ __forceinline__ DD dd_add(DD a, DD b) {
+  DD s = dd_two_sum(a.hi, b.hi);
+  const DD t = dd_two_sum(a.lo, b.lo);
+  s.lo += t.hi;
+  s = dd_fast_two_sum(s.hi, s.lo);
+  s.lo += t.lo;
+  return dd_fast_two_sum(s.hi, s.lo);
+}
+
+__device__ __forceinline__ DD dd_add_d(DD a, double b) {
+  DD s = dd_two_sum(a.hi, b);
+  s.lo += a.lo;
+  return dd_fast_two_sum(s.hi, s.lo);
+}
+
+// The exact product of two doubles is p + fma(a, b, -p); the cross terms of the low
+// parts are added to that error term.
+__device__ __forceinline__ DD dd_mul(DD a, DD b) {
+  const double p = a.hi * b.hi;
+  double e = fma(a.hi, b.hi, -p);
+  e = fma(a.hi, b.lo, e);
+  e = fma(a.lo, b.hi, e);
+  return dd_fast_two_sum(p, e);
+}
+
+__device__ __forceinline__ DD dd_neg(DD a) { return DD{-a.hi, -a.lo}; }
+
+// a / b, b != 0: the fp64 quotient and two corrections from the remainder.
+__device__ __forceinline__ DD dd_div(DD a, DD b) {
+  const double q1 = a.hi / b.hi;
+  DD r = dd_add(a, dd_neg(dd_mul(DD{q1, 0.0}, b)));
+  const double q2 = r.hi / b.hi;
+  r = dd_add(r, dd_neg(dd_mul(DD{q2, 0.0}, b)));
+  const double q3 = r.hi / b.hi;
+  return dd_add_d(dd_fast_two_sum(q1, q2), q3);
+}
+
+// sqrt(a), a.hi > 0: one Newton step from the fp64 root.
+__device__ __forceinline__ DD dd_sqrt(DD a) {
+  const double x = sqrt(a.hi);
+  const DD r = dd_add(a, dd_neg(dd_mul(DD{x, 0.0}, DD{x, 0.0})));
+  return dd_fast_two_sum(x, r.hi / (2.0 * x));
+}
 
 // Lanes that share one Gram entry when the orthogonalization sums the partials: the
 // largest power of two with NG * GS <= 256 threads, at most a wavefront (1 = a thread
@@ -821,19 +899,33 @@ constexpr int orth_group_size() {
 // Working set of the orthogonalization of one matrix (LDS).
 template <int R>
 struct OrthShared {
-  double G[R][R + 1];  // Gram matrix (rows padded: lane j reads row j without bank conflicts)
-  double T[R][R];      // P <- P T
-  double C[R];     // coefficients of the column being normalized
-  double W[R];     // G q_i in coefficients
+  double Gh[R][R + 1];  // Gram matrix, then its Cholesky factor (upper); high parts
+  double Gl[R][R + 1];  // low parts (rows padded: lane j reads row j without conflicts)
+  double D[R];          // diagonal of the Gram matrix before factoring
+  double T[R][R];       // P <- P T
+  double Y[R];          // the normalized column being removed
+  double Cc[R];         // its coefficient vector
+  double Sh[kThreads];  // row-sum partials of a Gram matrix recomputed from P (high)
+  double Sl[kThreads];  // (low)
+  int redo;             // the fp64 Gram matrix did not resolve a pivot
 };
 
-// Sums the job's Gram partials into sh.G (every thread of the workgroup takes part;
-// ends with a barrier). `issued` runs once the first loads of partials are in flight
-// and before any is used, so a caller can queue loads of its own behind them.
-// Small ranks: a group of GS lanes of one wavefront per Gram entry, lane i adding
-// partials i, i + GS, ... (8 loads in flight), then a butterfly over the group.
-// Larger ranks: a thread per entry, the partials in order, 8 loads of each of its
-// entries in flight.
+__device__ __forceinline__ void tri_entry(int e, int R, int& a, int& b) {
+  int rem = e;
+  a = 0;
+  while (rem >= R - a) {
+    rem -= R - a;
+    ++a;
+  }
+  b = a + rem;
+}
+
+// Sums the job's fp64 Gram partials into sh.Gh (sh.Gl = 0); every thread of the
+// workgroup takes part and it ends with a barrier. `issued` runs once the first loads
+// of partials are in flight and before any is used, so a caller can queue loads of its
+// own behind them. Small ranks: a group of GS lanes of one wavefront per Gram entry,
+// lane i adding partials i, i + GS, ... (8 loads in flight), then a butterfly over the
+// group. Larger ranks: a thread per entry, the partials in order.
 template <int R, typename Issued>
 __device__ __forceinline__ void orth_gram_sum(const OrthJob& j, const double* __restrict__ gram,
                                               OrthShared<R>& sh, Issued issued) {
@@ -841,14 +933,12 @@ __device__ __forceinline__ void orth_gram_sum(const OrthJob& j, const double* __
   constexpr int GS = orth_group_size<R>();
   const int tid = threadIdx.x;
   auto store_entry = [&](int e, double v) {
-    int a = 0, rem = e;
-    while (rem >= R - a) {
-      rem -= R - a;
-      ++a;
-    }
-    const int b = a + rem;
-    sh.G[a][b] = v;
-    sh.G[b][a] = v;
+    int a, b;
+    tri_entry(e, R, a, b);
+    sh.Gh[a][b] = v;
+    sh.Gh[b][a] = v;
+    sh.Gl[a][b] = 0.0;
+    sh.Gl[b][a] = 0.0;
   };
   if constexpr (GS > 1) {
     const int e = min(tid / GS, NG - 1);  // threads past the last entry mirror it
@@ -906,55 +996,155 @@ __device__ __forceinline__ void orth_gram_sum(const OrthJob& j, const double* __
   __syncthreads();
 }
 
-// The recurrence on r x r coefficient vectors, from sh.G into sh.T. Wavefront 0 runs
-// it alone: LDS accesses of one wavefront take effect in program order, so its steps
-// need no workgroup barrier (wave barriers only keep the compiler from reordering);
-// one barrier at the end publishes sh.T to the workgroup.
+// Sums the job's double-double Gram partials (partial p: NG high parts, then NG low
+// parts, at goff + 2 NG p) into sh.Gh / sh.Gl, a thread per entry, partials in order.
+// Every thread takes part; ends with a barrier.
 template <int R>
-__device__ __forceinline__ void orth_transform(int rank, double eps, OrthShared<R>& sh) {
+__device__ __forceinline__ void orth_gram_sum_dd(const OrthJob& j, const double* __restrict__ gram,
+                                                 OrthShared<R>& sh) {
+  constexpr int NG = gram_size<R>();
+  for (int e = threadIdx.x; e < NG; e += blockDim.x) {
+    DD s{0.0, 0.0};
+    const double* src = gram + j.goff + e;
+    for (int p = 0; p < j.nparts; ++p)
+      s = dd_add(s, DD{src[static_cast<int64_t>(p) * 2 * NG], src[static_cast<int64_t>(p) * 2 * NG + NG]});
+    int a, b;
+    tri_entry(e, R, a, b);
+    sh.Gh[a][b] = s.hi;
+    sh.Gh[b][a] = s.hi;
+    sh.Gl[a][b] = s.lo;
+    sh.Gl[b][a] = s.lo;
+  }
+  __syncthreads();
+}
+
+// The Gram matrix of the `rows` x R block X (row stride R, binary32) in double-double,
+// read directly: thread t sums entry t / S over the rows t % S, t % S + S, ... (S =
+// threads per entry), then the S sums of an entry are added in order. Every thread of
+// the workgroup takes part; ends with a barrier.
+template <int R>
+__device__ __forceinline__ void orth_gram_rows_dd(const float* __restrict__ X, int rows,
+                                                  OrthShared<R>& sh) {
+  constexpr int NG = gram_size<R>();
+  constexpr int S = kThreads / NG;
+  static_assert(S >= 1, "one thread per Gram entry at least");
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  if (tid < 64) {
-    // lane c owns column c
-    double cvec[R];
+  const int e = tid / S;
+  const int ph = tid - e * S;
+  if (e < NG) {
+    int a, b;
+    tri_entry(e, R, a, b);
+    DD s{0.0, 0.0};
+    for (int row = ph; row < rows; row += S) {
+      const float* x = X + static_cast<int64_t>(row) * R;
+      s = dd_add_d(s, static_cast<double>(x[a]) * static_cast<double>(x[b]));  // exact
+    }
+    sh.Sh[tid] = s.hi;
+    sh.Sl[tid] = s.lo;
+  }
+  __syncthreads();
+  if (tid < NG) {
+    DD s{0.0, 0.0};
+    for (int i = 0; i < S; ++i) s = dd_add(s, DD{sh.Sh[tid * S + i], sh.Sl[tid * S + i]});
+    int a, b;
+    tri_entry(tid, R, a, b);
+    sh.Gh[a][b] = s.hi;
+    sh.Gh[b][a] = s.hi;
+    sh.Gl[a][b] = s.lo;
+    sh.Gl[b][a] = s.lo;
+  }
+  __syncthreads();
+}
+
+// Cholesky factor of the leading rank x rank block of G (sh.Gh + sh.Gl) in
+// double-double, in place in the upper triangle, by wavefront 0 alone (its LDS
+// accesses take effect in program order; wave barriers only keep the compiler from
+// reordering). Lane j owns column j. A pivot that is not positive gives a zero row
+// (the column adds no new direction: it is exactly dependent, or zero). With tau > 0,
+// sh.redo is set when a pivot falls below tau times its diagonal entry (only for a
+// column that is not zero). No workgroup barrier: callers synchronize.
+template <int R>
+__device__ __forceinline__ void orth_cholesky(int rank, double tau, OrthShared<R>& sh) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x >= 64) return;
+  if (lane < R) sh.D[lane] = sh.Gh[lane][lane];
+  int redo = 0;
+  __builtin_amdgcn_wave_barrier();
+  for (int k = 0; k < rank; ++k) {
+    const DD d{sh.Gh[k][k], sh.Gl[k][k]};
+    const bool pos = d.hi > 0.0;
+    if (tau > 0.0 && sh.D[k] > 0.0 && !(d.hi >= tau * sh.D[k])) redo = 1;
+    const DD piv = pos ? dd_sqrt(d) : DD{0.0, 0.0};
+    __builtin_amdgcn_wave_barrier();
+    // row k of the factor: C_kj = G_kj / C_kk (lane j), C_kk (lane k)
+    if (lane >= k && lane < rank) {
+      DD c{0.0, 0.0};
+      if (pos) c = lane == k ? piv : dd_div(DD{sh.Gh[k][lane], sh.Gl[k][lane]}, piv);
+      sh.Gh[k][lane] = c.hi;
+      sh.Gl[k][lane] = c.lo;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // trailing block: G_ij -= C_ki C_kj for k < i <= j (lane j updates column j)
+    if (lane > k && lane < rank) {
+      const DD ckj{sh.Gh[k][lane], sh.Gl[k][lane]};
+      for (int i = k + 1; i <= lane; ++i) {
+        const DD cki{sh.Gh[k][i], sh.Gl[k][i]};
+        const DD g = dd_add(DD{sh.Gh[i][lane], sh.Gl[i][lane]}, dd_neg(dd_mul(cki, ckj)));
+        sh.Gh[i][lane] = g.hi;
+        sh.Gl[i][lane] = g.lo;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (lane == 0 && tau > 0.0) sh.redo = redo;
+}
+
+// Gram-Schmidt with epsilon on the columns of the factor (sh.Gh, upper triangle; the
+// high parts, rounded to fp64), carrying coefficient vectors: column i is divided by
+// (|column| + eps), then removed from every later column with the dot product, exactly
+// the steps of the pages' recurrence. Writes the coefficients to sh.T (columns past
+// the rank: the unit vector, so those P columns, kept at zero, stay zero). Run by
+// wavefront 0, lane j owning column j; ends with a workgroup barrier.
+template <int R>
+__device__ __forceinline__ void orth_from_factor(int rank, double eps, OrthShared<R>& sh) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    double y[R], c[R];
 #pragma unroll
-    for (int l = 0; l < R; ++l) cvec[l] = (l == lane) ? 1.0 : 0.0;
+    for (int l = 0; l < R; ++l) {
+      c[l] = (l == lane) ? 1.0 : 0.0;
+      y[l] = (lane < rank && l <= lane) ? sh.Gh[l][min(lane, R - 1)] : 0.0;
+    }
     for (int i = 0; i < rank; ++i) {
       if (lane == i) {
+        double nn = 0.0;
 #pragma unroll
-        for (int l = 0; l < R; ++l) sh.C[l] = cvec[l];
+        for (int l = 0; l < R; ++l) nn += y[l] * y[l];
+        const double inv = 1.0 / (sqrt(nn) + eps);
+#pragma unroll
+        for (int l = 0; l < R; ++l) {
+          y[l] *= inv;
+          c[l] *= inv;
+          sh.Y[l] = y[l];
+          sh.Cc[l] = c[l];
+        }
       }
       __builtin_amdgcn_wave_barrier();
-      double w = 0.0;  // (G c_i)_lane
-      if (lane < R) {
+      if (lane > i && lane < rank) {
+        double coef = 0.0;
 #pragma unroll
-        for (int l = 0; l < R; ++l) w += sh.G[lane][l] * sh.C[l];
-      }
-      double nn = (lane < R) ? sh.C[lane] * w : 0.0;
+        for (int l = 0; l < R; ++l) coef += y[l] * sh.Y[l];
 #pragma unroll
-      for (int mask = 32; mask >= 1; mask >>= 1) nn += __shfl_xor(nn, mask);
-      // |v_i|^2 = c_i^T G c_i; q_i = v_i / (|v_i| + eps)
-      const double inv = 1.0 / (sqrt(nn > 0.0 ? nn : 0.0) + eps);
-      if (lane < R) sh.W[lane] = w * inv;  // G q_i (in coefficients)
-      __builtin_amdgcn_wave_barrier();
-      if (lane < rank) {
-        if (lane == i) {
-#pragma unroll
-          for (int l = 0; l < R; ++l) cvec[l] *= inv;
-        } else if (lane > i) {
-          // <q_i, v_lane> = c_lane^T G c_i / (|v_i| + eps); v_lane -= <q_i, v_lane> q_i
-          double coef = 0.0;
-#pragma unroll
-          for (int l = 0; l < R; ++l) coef += cvec[l] * sh.W[l];
-#pragma unroll
-          for (int l = 0; l < R; ++l) cvec[l] -= coef * (sh.C[l] * inv);
+        for (int l = 0; l < R; ++l) {
+          y[l] -= coef * sh.Y[l];
+          c[l] -= coef * sh.Cc[l];
         }
       }
       __builtin_amdgcn_wave_barrier();
     }
     if (lane < R) {
 #pragma unroll
-      for (int l = 0; l < R; ++l) sh.T[l][lane] = cvec[l];
+      for (int l = 0; l < R; ++l) sh.T[l][lane] = c[l];
     }
   }
   __syncthreads();
@@ -1001,7 +1191,15 @@ __device__ __forceinline__ void pass2_orth_rows(const Pass2Args& args, const Ten
   __builtin_amdgcn_sched_barrier(0);
   const OrthJob j{d.poff, d.goff, -1, d.n, d.rank, (d.n + d.rpb1 - 1) / d.rpb1, d.rpb1, 0, 0};
   orth_gram_sum<R>(j, args.gram, sh, issued);
-  orth_transform<R>(d.rank, args.eps, sh);
+  orth_cholesky<R>(d.rank, kCholTau, sh);
+  __syncthreads();
+  if (sh.redo) {
+    // an fp64 pivot was not resolved: the Gram matrix again, in double-double from P
+    orth_gram_rows_dd<R>(Pt, d.n, sh);
+    orth_cholesky<R>(d.rank, 0.0, sh);
+    __syncthreads();
+  }
+  orth_from_factor<R>(d.rank, args.eps, sh);
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int row = r0 + tid + i * kThreads;
@@ -2159,7 +2357,8 @@ __global__ void __launch_bounds__(kThreads) k_pass3_mfma(Pass3Args args) {
 
 // ------------------------------------------------------------ orthogonalization
 
-// Gram partials of one row chunk of a job, staged through LDS.
+// Gram partials of one row chunk of a job, staged through LDS, as double-double sums
+// of the exact products: partial p holds NG high parts, then NG low parts.
 template <int R>
 __global__ void __launch_bounds__(kThreads)
     k_gram(const Tile* __restrict__ tiles, const OrthJob* __restrict__ jobs,
@@ -2175,36 +2374,52 @@ __global__ void __launch_bounds__(kThreads)
   const float* X = base + j.off + static_cast<int64_t>(r0) * R;
   for (int f = threadIdx.x; f < nr * R; f += kThreads) xs[f] = X[f];
   __syncthreads();
-  double* out = gram + j.goff + static_cast<int64_t>(t.a) * NG;
+  double* out = gram + j.goff + static_cast<int64_t>(t.a) * 2 * NG;
   for (int e = threadIdx.x; e < NG; e += kThreads) {
-    // entry e of the packed triangle -> (a, b)
-    int a = 0, rem = e;
-    while (rem >= R - a) {
-      rem -= R - a;
-      ++a;
-    }
-    const int b = a + rem;
-    double s = 0.0;
+    int a, b;
+    tri_entry(e, R, a, b);
+    DD s{0.0, 0.0};
     for (int r = 0; r < nr; ++r)
-      s += static_cast<double>(xs[r * R + a]) * static_cast<double>(xs[r * R + b]);
-    out[e] = s;
+      s = dd_add_d(s, static_cast<double>(xs[r * R + a]) * static_cast<double>(xs[r * R + b]));
+    out[e] = s.hi;
+    out[NG + e] = s.lo;
   }
 }
 
+// The transform T of one job (one workgroup per job): its double-double Gram partials
+// summed, factored, and the recurrence run on the factor. T goes to tmat (R x R fp64
+// per job, job after job).
+template <int R>
+__global__ void __launch_bounds__(kThreads)
+    k_orth_t(const OrthJob* __restrict__ jobs, const double* __restrict__ gram,
+             double* __restrict__ tmat, double eps, const int32_t* __restrict__ found_inf) {
+  if (found_inf != nullptr && *found_inf) return;
+  __shared__ OrthShared<R> sh;
+  const OrthJob j = jobs[blockIdx.x];
+  orth_gram_sum_dd<R>(j, gram, sh);
+  orth_cholesky<R>(j.rank, 0.0, sh);
+  __syncthreads();
+  orth_from_factor<R>(j.rank, eps, sh);
+  double* dst = tmat + static_cast<int64_t>(blockIdx.x) * R * R;
+  for (int f = threadIdx.x; f < R * R; f += kThreads) dst[f] = sh.T[f / R][f % R];
+}
+
+// X <- X T in fp64, rounded to fp32 (and to the state's 16 bits), for kOrthRows rows of
+// a job per workgroup (several rows loaded before any is transformed); with toff >= 0
+// the result is also written transposed.
 template <int R, int ST>
 __global__ void __launch_bounds__(kThreads)
     k_orth(const OrthJob* __restrict__ jobs, float* __restrict__ base, float* __restrict__ tbase,
-           const double* __restrict__ gram, double eps, const int32_t* __restrict__ found_inf) {
+           const double* __restrict__ tmat, const int32_t* __restrict__ found_inf) {
   if (found_inf != nullptr && *found_inf) return;
-  __shared__ OrthShared<R> sh;
+  __shared__ double T[R][R];
   const OrthJob j = jobs[blockIdx.y];
   const int tid = threadIdx.x;
   const int row_begin = blockIdx.x * kOrthRows;
   if (row_begin >= j.rows) return;
-  orth_gram_sum<R>(j, gram, sh, [] {});
-  orth_transform<R>(j.rank, eps, sh);
-  // 3. P <- P T in fp64, rounded to fp32 (and to the state's 16 bits), for this
-  //    workgroup's rows; several rows are loaded before any is transformed.
+  const double* src = tmat + static_cast<int64_t>(blockIdx.y) * R * R;
+  for (int f = tid; f < R * R; f += kThreads) T[f / R][f % R] = src[f];
+  __syncthreads();
   float* X = base + j.off;
   const int row_end = min(j.rows, row_begin + kOrthRows);
   constexpr int B = R <= 8 ? 4 : 1;
@@ -2229,7 +2444,7 @@ __global__ void __launch_bounds__(kThreads)
       for (int k = 0; k < R; ++k) {
         double s = 0.0;
 #pragma unroll
-        for (int l = 0; l < R; ++l) s += static_cast<double>(x[b][l]) * sh.T[l][k];
+        for (int l = 0; l < R; ++l) s += static_cast<double>(x[b][l]) * T[l][k];
         const float v = rnd16<ST>(static_cast<float>(s));
         dst[k] = v;
         if (j.toff >= 0) tbase[j.toff + static_cast<int64_t>(k) * j.tstride + row] = v;
@@ -2277,17 +2492,24 @@ __device__ __forceinline__ void box_muller(uint64_t we, uint64_t wo, double& z0,
   z1 = radius * sin(angle);
 }
 
+// Draw of one job: block b of the m x rank matrix is Philox counter (b, view, epoch, 0)
+// under key (seed, bucket_key); entry e = 4b + a is word a, via Box-Muller on the word
+// pairs, stored at Q[qoff + (e / rank) * R + e % rank]. words (optional) receives the
+// raw Philox output words in counter order.
 template <int ST>
-__global__ void __launch_bounds__(256)
-    k_qinit(const QInitJob* __restrict__ jobs, float* __restrict__ Q, int R, uint64_t seed,
-            uint64_t bucket_key, uint64_t epoch) {
-  const QInitJob j = jobs[blockIdx.y];
+__device__ __forceinline__ void qinit_job(const QInitJob& j, float* __restrict__ Q, int R,
+                                          uint64_t seed, uint64_t bucket_key, uint64_t epoch,
+                                          int64_t first, int64_t stride,
+                                          uint64_t* __restrict__ words) {
   const int64_t count = static_cast<int64_t>(j.m) * j.rank;
   const int64_t nblocks = (count + 3) / 4;
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; b < nblocks;
-       b += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+  for (int64_t b = first; b < nblocks; b += stride) {
     uint64_t w[4] = {static_cast<uint64_t>(b), static_cast<uint64_t>(j.view), epoch, 0};
     philox4x64_10(w, seed, bucket_key);
+    if (words) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) words[4 * b + a] = w[a];
+    }
     double z[4];
     box_muller(w[0], w[1], z[0], z[1]);
     box_muller(w[2], w[3], z[2], z[3]);
@@ -2301,6 +2523,24 @@ __global__ void __launch_bounds__(256)
       }
     }
   }
+}
+
+template <int ST>
+__global__ void __launch_bounds__(256)
+    k_qinit(const QInitJob* __restrict__ jobs, float* __restrict__ Q, int R, uint64_t seed,
+            uint64_t bucket_key, uint64_t epoch) {
+  qinit_job<ST>(jobs[blockIdx.y], Q, R, seed, bucket_key, epoch,
+                static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x,
+                static_cast<int64_t>(gridDim.x) * blockDim.x, nullptr);
+}
+
+// One view's draw with the job passed by value (introspection; row stride = rank).
+__global__ void __launch_bounds__(256)
+    k_qdraw(QInitJob j, float* __restrict__ Q, uint64_t seed, uint64_t bucket_key,
+            uint64_t epoch, uint64_t* __restrict__ words) {
+  qinit_job<kStF32>(j, Q, j.rank, seed, bucket_key, epoch,
+                    static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x,
+                    static_cast<int64_t>(gridDim.x) * blockDim.x, words);
 }
 
 // ------------------------------------------------------- fp16 pass-through only
@@ -2525,17 +2765,20 @@ hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs
 }
 
 hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, int max_rows, float* base,
-                       float* tbase, const double* gram, double eps,
+                       float* tbase, const double* gram, double* tmat, double eps,
                        const int32_t* found_inf, int st, hipStream_t s) {
   if (njobs == 0) return hipSuccess;
   const dim3 grid((max_rows + kOrthRows - 1) / kOrthRows, njobs);
   PSGD_RANK_SWITCH(R, {
+    k_orth_t<RR><<<dim3(njobs), kThreads, 0, s>>>(jobs, gram, tmat, eps, found_inf);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (st == kStF16)
-      k_orth<RR, kStF16><<<grid, kThreads, 0, s>>>(jobs, base, tbase, gram, eps, found_inf);
+      k_orth<RR, kStF16><<<grid, kThreads, 0, s>>>(jobs, base, tbase, tmat, found_inf);
     else if (st == kStBF16)
-      k_orth<RR, kStBF16><<<grid, kThreads, 0, s>>>(jobs, base, tbase, gram, eps, found_inf);
+      k_orth<RR, kStBF16><<<grid, kThreads, 0, s>>>(jobs, base, tbase, tmat, found_inf);
     else
-      k_orth<RR, kStF32><<<grid, kThreads, 0, s>>>(jobs, base, tbase, gram, eps, found_inf);
+      k_orth<RR, kStF32><<<grid, kThreads, 0, s>>>(jobs, base, tbase, tmat, found_inf);
     return hipGetLastError();
   })
 }
@@ -2553,6 +2796,17 @@ hipError_t launch_qinit(int R, const QInitJob* jobs, int njobs, int64_t max_coun
     k_qinit<kStBF16><<<grid, 256, 0, s>>>(jobs, Q, R, seed, bucket_key, epoch);
   else
     k_qinit<kStF32><<<grid, 256, 0, s>>>(jobs, Q, R, seed, bucket_key, epoch);
+  return hipGetLastError();
+}
+
+hipError_t launch_qdraw(int64_t m, int rank, int view, float* out, uint64_t* words,
+                       uint64_t seed, uint64_t bucket_key, uint64_t epoch, hipStream_t s) {
+  const int64_t count = m * rank;
+  if (count <= 0) return hipSuccess;
+  const int64_t blocks = ((count + 3) / 4 + 255) / 256;
+  const QInitJob j{0, static_cast<int32_t>(m), rank, view, 0};
+  k_qdraw<<<dim3(static_cast<unsigned>(blocks < 1024 ? blocks : 1024)), 256, 0, s>>>(
+      j, out, seed, bucket_key, epoch, words);
   return hipGetLastError();
 }
 

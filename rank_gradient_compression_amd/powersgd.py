@@ -37,28 +37,29 @@ EXPORTED = (
     "powersgd_get_kernel_times", "powersgd_kernel_name", "powersgd_classify_view",
     "powersgd_batched_side", "powersgd_compress_bucket_batched",
     "powersgd_state_export", "powersgd_state_import", "powersgd_compress_bucket_wrapped",
-    "powersgd_compress_bucket_batched_wrapped",
+    "powersgd_compress_bucket_batched_wrapped", "powersgd_get_factors", "powersgd_get_error",
+    "powersgd_draw_q0",
 )
 
 
 class powersgd_hparams(ctypes.Structure):
     _fields_ = [
         ("matrix_approximation_rank", ctypes.c_int32),
-        ("use_error_feedback", ctypes.c_int32),
         ("start_powerSGD_iter", ctypes.c_int64),
         ("min_compression_rate", ctypes.c_double),
+        ("use_error_feedback", ctypes.c_int32),
         ("warm_start", ctypes.c_int32),
-        ("batch_tensors_with_same_shape", ctypes.c_int32),
         ("orthogonalization_epsilon", ctypes.c_double),
         ("random_seed", ctypes.c_uint64),
         ("compression_stats_logging_frequency", ctypes.c_int64),
+        ("batch_tensors_with_same_shape", ctypes.c_int32),
     ]
 
 
 class powersgd_view(ctypes.Structure):
     _fields_ = [
         ("offset", ctypes.c_int64),
-        ("ndim", ctypes.c_int64),
+        ("ndim", ctypes.c_int32),
         ("shape", ctypes.c_int64 * POWERSGD_MAX_NDIM),
     ]
 
@@ -104,6 +105,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                          ctypes.POINTER(i64), ctypes.POINTER(i32)]),
         "powersgd_copy_factors": (i32, [P, i64, i32, P, P, P]),
         "powersgd_copy_error": (i32, [P, i64, i32, P, P]),
+        "powersgd_get_factors": (i32, [P, i64, i32, ctypes.POINTER(P), ctypes.POINTER(P),
+                                       ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                       ctypes.POINTER(i32)]),
+        "powersgd_get_error": (i32, [P, i64, ctypes.POINTER(P)]),
+        "powersgd_draw_q0": (i32, [ctypes.c_uint64, i64, i32, ctypes.c_uint64, i64, i32, P, P,
+                                   P]),
         "powersgd_get_stats": (i32, [P, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                      ctypes.POINTER(i64)]),
         "powersgd_set_timing": (i32, [P, i32]),
@@ -159,7 +166,10 @@ def powersgd_last_error() -> str:
     return load_library().powersgd_last_error().decode()
 
 
-_VIEW_WORDS = 2 + POWERSGD_MAX_NDIM  # offset, ndim, shape[POWERSGD_MAX_NDIM] (int64 each)
+# offset, ndim, shape[POWERSGD_MAX_NDIM] as 64-bit words: ndim is an int32 followed by
+# four bytes of alignment padding, so on this little-endian target the word holding it
+# carries its value in the low half and zero in the padding
+_VIEW_WORDS = 2 + POWERSGD_MAX_NDIM
 
 
 class PreparedViews:
@@ -273,6 +283,34 @@ def powersgd_copy_error(state, bucket_index: int, view: int, e_ptr: int,
                         stream: Optional[int]) -> None:
     _check(load_library().powersgd_copy_error(
         state, bucket_index, view, ctypes.c_void_p(e_ptr),
+        ctypes.c_void_p(stream) if stream else None))
+
+
+def powersgd_get_factors(state, bucket_index: int, view: int) -> Tuple[int, int, int, int, int]:
+    """(P pointer, Q pointer, n, m, r): state-owned device copies of the view's factors,
+    enqueued on the stream of the bucket's latest call."""
+    p, q = ctypes.c_void_p(), ctypes.c_void_p()
+    n, m, r = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    _check(load_library().powersgd_get_factors(state, bucket_index, view, ctypes.byref(p),
+                                               ctypes.byref(q), ctypes.byref(n),
+                                               ctypes.byref(m), ctypes.byref(r)))
+    return p.value or 0, q.value or 0, n.value, m.value, r.value
+
+
+def powersgd_get_error(state, bucket_index: int) -> int:
+    """Device pointer to the state-owned, bucket-shaped fp32 error memory."""
+    e = ctypes.c_void_p()
+    _check(load_library().powersgd_get_error(state, bucket_index, ctypes.byref(e)))
+    return e.value or 0
+
+
+def powersgd_draw_q0(random_seed: int, bucket_index: int, view: int, epoch: int, m: int,
+                     rank: int, out_ptr: int, words_ptr: Optional[int],
+                     stream: Optional[int]) -> None:
+    _check(load_library().powersgd_draw_q0(
+        int(random_seed) & 0xFFFFFFFFFFFFFFFF, int(bucket_index), int(view),
+        int(epoch) & 0xFFFFFFFFFFFFFFFF, int(m), int(rank), ctypes.c_void_p(out_ptr),
+        ctypes.c_void_p(words_ptr) if words_ptr else None,
         ctypes.c_void_p(stream) if stream else None))
 
 

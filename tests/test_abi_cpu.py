@@ -82,6 +82,42 @@ def test_struct_layouts_match_the_header(lib, tmp_path):
         assert offs[len(fields_h) + j] == getattr(api.powersgd_view, f).offset, f
 
 
+def test_struct_field_order_is_the_boundary_contract(lib):
+    """powersgd_hparams lists the PowerSGDState hyperparameters in the order of the
+    boundary contract (rank, start iteration, rate, error feedback, warm start,
+    epsilon, seed, logging frequency, same-shape batching), and powersgd_view is
+    {int64 offset; int32 ndim; int64 shape[8]}, as compiled by gcc from the header."""
+    assert [f for f, _ in api.powersgd_hparams._fields_] == [
+        "matrix_approximation_rank", "start_powerSGD_iter", "min_compression_rate",
+        "use_error_feedback", "warm_start", "orthogonalization_epsilon", "random_seed",
+        "compression_stats_logging_frequency", "batch_tensors_with_same_shape"]
+    assert [t for _, t in api.powersgd_hparams._fields_] == [
+        ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_double, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32]
+    assert [(f, t) for f, t in api.powersgd_view._fields_] == [
+        ("offset", ctypes.c_int64), ("ndim", ctypes.c_int32),
+        ("shape", ctypes.c_int64 * api.POWERSGD_MAX_NDIM)]
+    # offsets ascend in declaration order (the gcc comparison is in the test above)
+    offs = [getattr(api.powersgd_hparams, f).offset for f, _ in api.powersgd_hparams._fields_]
+    assert offs == sorted(offs)
+
+
+def test_introspection_arguments_are_checked_without_a_device(lib):
+    p, q = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.powersgd_get_factors(None, 0, 0, ctypes.byref(p), ctypes.byref(q), None, None,
+                                    None) == api.POWERSGD_ERR_INVALID_ARG
+    assert lib.powersgd_get_error(None, 0, ctypes.byref(p)) == api.POWERSGD_ERR_INVALID_ARG
+    buf = ctypes.c_void_p(256)  # never dereferenced: every case fails before any launch
+    for args, status in (((0, 0, 0, 0, -1, 4, buf, None, None), api.POWERSGD_ERR_INVALID_ARG),
+                         ((0, 0, 0, 0, 8, 0, buf, None, None), api.POWERSGD_ERR_INVALID_ARG),
+                         ((0, 0, -1, 0, 8, 4, buf, None, None), api.POWERSGD_ERR_INVALID_ARG),
+                         ((0, 0, 0, 0, 8, 33, buf, None, None), api.POWERSGD_ERR_UNSUPPORTED),
+                         ((0, 0, 0, 0, 2 ** 31, 4, buf, None, None),
+                          api.POWERSGD_ERR_UNSUPPORTED),
+                         ((0, 0, 0, 0, 8, 4, None, None, None), api.POWERSGD_ERR_INVALID_ARG)):
+        assert lib.powersgd_draw_q0(*args) == status, args
+
+
 def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert api.status_string(s) and "unknown" not in api.status_string(s)
