@@ -369,6 +369,52 @@ POWERSGD_API powersgd_status powersgd_draw_q0(uint64_t random_seed, int64_t buck
 POWERSGD_API powersgd_status powersgd_get_stats(powersgd_state* st, int64_t* iteration,
                                    int64_t* numel_in, int64_t* numel_comm);
 
+/* --- without allocation ------------------------------------------------------- */
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): one compression step of a single
+ * n x m fp32 matrix, with the state held by the caller. It computes what
+ * powersgd_compress_bucket computes for a bucket holding only this matrix (the same
+ * kernels, work items and order of every sum, so the results are bitwise equal),
+ * except that there is no min_compression_rate test and no iteration counter or
+ * statistics: every call compresses, at rank r = min(matrix_approximation_rank, n, m).
+ *
+ *   hp            hyperparameters (host, read during the call): rank, epsilon and
+ *                 random_seed are used; error feedback follows E, warm start q_valid.
+ *   bucket_index, view, epoch  the key of the initial Q draw when q_valid is 0
+ *                 (see powersgd_draw_q0; a compressing call uses view = the view's
+ *                 index in its bucket and epoch = 0 under warm start).
+ *   M             device, n * m fp32, row-major, caller-owned: the gradient in, M_hat
+ *                 = P Q^T out (in place).
+ *   E             device, n * m fp32, caller-owned error memory (zero before the
+ *                 first step): M' = G + E in, E = M' - M_hat out. NULL: no error
+ *                 feedback (M' = G).
+ *   Q             device, m * r fp32, row-major, caller-owned: in, the warm-start Q
+ *                 when q_valid != 0 (otherwise not read); out, Q = M'^T P, the next
+ *                 warm-start Q.
+ *   P             device, n * r fp32, row-major, caller-owned output: the
+ *                 orthogonalized P; may be NULL.
+ *   stream        hipStream_t (NULL = the legacy default stream); the current HIP
+ *                 device's copy of the working array is used.
+ *
+ * Every pointer must be 4-byte aligned. No device memory is allocated or freed: the
+ * work items, padded factors, Gram partials and partial sums live in a fixed array
+ * of 64 MiB per device (allocated when the library is loaded, held until the process
+ * ends), which fits every matrix of up to 16384 x 16384 at any rank. All calls on one
+ * device share that array: calls that overlap on a device (several streams or
+ * threads) race and must be serialized by the caller. Only kernel launches are
+ * enqueued (no memset, no copy from host memory), so a call can be captured in a HIP
+ * graph; a replay repeats the captured pointers and q_valid.
+ * Errors, before anything is enqueued: INVALID_ARG (NULL hp or M or Q, n or m < 1,
+ * misaligned pointer, hyperparameters as for powersgd_state_create), UNSUPPORTED
+ * (rank above POWERSGD_MAX_RANK, a matrix whose working memory exceeds the array),
+ * HIP (no device, launch failure).
+ */
+POWERSGD_API powersgd_status powersgd_compress_matrix_noalloc(
+    const powersgd_hparams* hp, int64_t bucket_index, int32_t view, uint64_t epoch, float* M,
+    int64_t n, int64_t m, float* E, float* Q, int32_t q_valid, float* P, void* stream);
+
 /* --- state snapshot (checkpoint / resume) ------------------------------------- */
 
 /*

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libpowersgd.so"
-SOURCES = ["host.cpp", "kernels.hip"]
+SOURCES = ["host.cpp", "kernels.hip", "noalloc.hip"]
 
 # Packed fp32 instructions are switched off for every HIP translation unit.
 HIP_FLAGS = [

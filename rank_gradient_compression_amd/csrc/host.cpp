@@ -598,6 +598,42 @@ double pass_bytes(int kind, bool f16, bool ef, int prec = kStF32) {
 
 }  // namespace
 
+namespace psgd {
+
+powersgd_status report_error(powersgd_status s, const char* msg) { return fail(s, msg); }
+
+powersgd_status matrix_layout(const powersgd_hparams& hp, int64_t n, int64_t m,
+                              MatrixLayout& out) {
+  if (n <= 0 || m <= 0) return fail(POWERSGD_ERR_INVALID_ARG, "the matrix is empty");
+  if (n > kMaxMatrixDim || m > kMaxMatrixDim)
+    return fail(POWERSGD_ERR_UNSUPPORTED, "matrix dimension above 2^31 - 65537");
+  BucketPlan pl;
+  std::vector<ViewKey> keys{ViewKey{0, {n, m}}};
+  // the batched variant's plan: one matrix, no rate test
+  powersgd_status b = build_plan(hp, n * m, true, kStF32, std::move(keys), pl);
+  if (b != POWERSGD_OK) return b;
+  out.d = pl.tensors[0];
+  out.R = pl.R;
+  out.pjob = pl.pjobs[0];
+  out.qjob = pl.qjobs[0];
+  out.qinit = pl.qinit[0];
+  out.ntiles1 = static_cast<int32_t>(pl.tiles1.size());
+  out.ntiles2 = static_cast<int32_t>(pl.tiles2.size());
+  out.ntiles3 = static_cast<int32_t>(pl.tiles3.size());
+  out.ntiles2r = static_cast<int32_t>(pl.tiles2r.size());
+  out.npgram = static_cast<int32_t>(pl.pgram_tiles.size());
+  out.nqgram = static_cast<int32_t>(pl.qgram_tiles.size());
+  out.nrb3 = out.d.ncb > 0 ? out.ntiles3 / out.d.ncb : 0;
+  out.p_floats = pl.p_floats;
+  out.q_floats = pl.q_floats;
+  out.qt_floats = pl.qt_floats;
+  out.partial_floats = pl.partial_floats;
+  out.gram_doubles = pl.gram_doubles;
+  return POWERSGD_OK;
+}
+
+}  // namespace psgd
+
 // ============================================================================ ABI
 
 extern "C" {

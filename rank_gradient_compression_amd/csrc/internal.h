@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
+#include "powersgd.h"
+
 namespace psgd {
 
 // Column block width of pass 2 and pass 3: 64 lanes x 4 consecutive columns.
@@ -254,5 +258,24 @@ constexpr int kGramRows = 256;
 // Rows transformed by one workgroup of the orthogonalization kernel (each workgroup
 // recomputes the small r x r transform from the Gram partials).
 constexpr int kOrthRows = 1024;
+
+// One n x m matrix as the bucket plan lays out a bucket that holds only that matrix
+// (every buffer offset is 0; compressed without the rate test at rank min(r, n, m)):
+// its descriptor, its orthogonalization and draw jobs, the work-item counts of each
+// pass and the sizes of the working buffers. Host only (host.cpp).
+struct MatrixLayout {
+  TensorDesc d;
+  int R;                                      // padded rank
+  OrthJob pjob, qjob;                         // Gram-Schmidt of P and of the draw of Q
+  QInitJob qinit;
+  int32_t ntiles1, ntiles2, ntiles3, ntiles2r, npgram, nqgram;
+  int32_t nrb3;                               // pass-3 row blocks
+  int64_t p_floats, q_floats, qt_floats, partial_floats, gram_doubles;
+};
+powersgd_status matrix_layout(const powersgd_hparams& hp, int64_t n, int64_t m,
+                              MatrixLayout& out);
+
+// Records `msg` as the calling thread's powersgd_last_error detail and returns s.
+powersgd_status report_error(powersgd_status s, const char* msg);
 
 }  // namespace psgd

@@ -38,7 +38,7 @@ EXPORTED = (
     "powersgd_batched_side", "powersgd_compress_bucket_batched",
     "powersgd_state_export", "powersgd_state_import", "powersgd_compress_bucket_wrapped",
     "powersgd_compress_bucket_batched_wrapped", "powersgd_get_factors", "powersgd_get_error",
-    "powersgd_draw_q0",
+    "powersgd_draw_q0", "powersgd_compress_matrix_noalloc",
 )
 
 
@@ -111,6 +111,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "powersgd_get_error": (i32, [P, i64, ctypes.POINTER(P)]),
         "powersgd_draw_q0": (i32, [ctypes.c_uint64, i64, i32, ctypes.c_uint64, i64, i32, P, P,
                                    P]),
+        "powersgd_compress_matrix_noalloc": (i32, [ctypes.POINTER(powersgd_hparams), i64, i32,
+                                                   ctypes.c_uint64, P, i64, i64, P, P, i32, P,
+                                                   P]),
         "powersgd_get_stats": (i32, [P, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                      ctypes.POINTER(i64)]),
         "powersgd_set_timing": (i32, [P, i32]),
@@ -311,6 +314,17 @@ def powersgd_draw_q0(random_seed: int, bucket_index: int, view: int, epoch: int,
         int(random_seed) & 0xFFFFFFFFFFFFFFFF, int(bucket_index), int(view),
         int(epoch) & 0xFFFFFFFFFFFFFFFF, int(m), int(rank), ctypes.c_void_p(out_ptr),
         ctypes.c_void_p(words_ptr) if words_ptr else None,
+        ctypes.c_void_p(stream) if stream else None))
+
+
+def powersgd_compress_matrix_noalloc(hp: powersgd_hparams, bucket_index: int, view: int,
+                                     epoch: int, m_ptr: int, n: int, m: int,
+                                     e_ptr: Optional[int], q_ptr: int, q_valid: bool,
+                                     p_ptr: Optional[int], stream: Optional[int]) -> None:
+    _check(load_library().powersgd_compress_matrix_noalloc(
+        ctypes.byref(hp), int(bucket_index), int(view), int(epoch) & 0xFFFFFFFFFFFFFFFF,
+        ctypes.c_void_p(m_ptr), int(n), int(m), ctypes.c_void_p(e_ptr) if e_ptr else None,
+        ctypes.c_void_p(q_ptr), int(bool(q_valid)), ctypes.c_void_p(p_ptr) if p_ptr else None,
         ctypes.c_void_p(stream) if stream else None))
 
 
