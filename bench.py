@@ -307,6 +307,17 @@ def algorithmic_bytes(cfg, comp_elems: int, per_elt_f32: float = 28.0):
     return comp_elems * (24 if ef else 6) + (0 if cfg.batched else (cfg.numel - comp_elems) * 6)
 
 
+def moved_bytes(cfg, comp_elems: int):
+    """Bytes the library's three passes actually move: an fp32 bucket with error
+    feedback keeps M' in the error memory's place and rebuilds the error from it, so
+    pass 3 only writes M_hat (12 + 4 + 4 per compressed element); the other variants
+    move their algorithmic bytes."""
+    ef = bool(cfg.hparams.get("use_error_feedback", True))
+    if cfg.dtype == "f32" and not cfg.wrap and ef:
+        return comp_elems * 20
+    return algorithmic_bytes(cfg, comp_elems)
+
+
 def compressed_elements(cfg, side: int) -> int:
     from rank_gradient_compression_amd import powersgd as api
     if cfg.batched:
@@ -417,6 +428,8 @@ def main() -> int:
     comp_elems = compressed_elements(cfg, side)
     algo_bytes = algorithmic_bytes(cfg, comp_elems)
     step_frac = algo_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+    moved = moved_bytes(cfg, comp_elems)
+    moved_frac = moved / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
 
     # Other workloads, for context (stderr and a summary object): the ResNet-50-shaped
     # bucket warm (its 74 MB bucket and E stay in the 256 MB last-level cache between
@@ -433,10 +446,13 @@ def main() -> int:
             w2.close()
             gbs = c.numel * c.element_bytes / (med * 1e-3) / 1e9
             frac = algorithmic_bytes(c, ce) / (med * 1e-3) / 1e9 / HBM_PEAK_GBS
+            mfrac = moved_bytes(c, ce) / (med * 1e-3) / 1e9 / HBM_PEAK_GBS
             secondary[key] = {"ms_per_step": round(med, 5), "GBps": round(gbs, 1),
-                              "step_hbm_roofline_frac": round(frac, 4)}
+                              "step_hbm_roofline_frac": round(frac, 4),
+                              "step_moved_frac": round(mfrac, 4)}
             eprint(f"[bench] {key}: median {med * 1e3:.1f} us/step, {gbs:.0f} GB/s gradient, "
-                   f"{frac * 100:.1f}% of 8 TB/s on the three-pass byte count")
+                   f"{frac * 100:.1f}% of 8 TB/s on the three-pass byte count, "
+                   f"{mfrac * 100:.1f}% on the bytes moved")
         del flush
         torch.cuda.empty_cache()
 
@@ -457,6 +473,8 @@ def main() -> int:
                              f"{args.steps} steps after {args.warmup} warmup steps each",
                    "step_hbm_roofline_frac": round(step_frac, 4),
                    "step_algorithmic_bytes": algo_bytes,
+                   "step_moved_bytes": moved,
+                   "step_moved_frac": round(moved_frac, 4),
                    "measured_copy_GBps": round(copy_gbs, 1)},
         "roofline": roofline,
         "secondary": secondary or None,

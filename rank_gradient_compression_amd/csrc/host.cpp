@@ -156,6 +156,11 @@ struct BucketPlan {
   float* intro_PQ = nullptr;
   std::vector<int64_t> intro_off;  // per tensor: first float of its compact P, then Q
   hipStream_t last_stream = nullptr;  // stream of the latest compressing call
+  // E's place (fp32 error memory) holds the error itself (true: before the first call,
+  // after an import, after an fp16 call) or M' of the previous fp32 call, whose error is
+  // rebuilt from it and the step's P and Q (false)
+  bool w_holds_e = true;
+  float* Emat = nullptr;  // the materialized error for introspection and export
   bool allocated = false;
   bool q_ready = false;
   // every tensor has 16-byte aligned rows (in d_td) at least 256 columns wide
@@ -164,7 +169,7 @@ struct BucketPlan {
   void release() {
     void* ptrs[] = {E, Eh, Mh, P, Praw, Q, QT, partial, gram, tmat, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
                     d_tiles1, d_tiles2, d_tiles3, d_tiles2r, d_flat_unc, d_flat_all, d_pjobs, d_qjobs,
-                    d_qinit, intro_E, intro_PQ};
+                    d_qinit, intro_E, intro_PQ, Emat};
     for (void* p : ptrs)
       if (p) (void)hipFree(p);
     E = P = Praw = Q = QT = partial = nullptr;
@@ -177,7 +182,7 @@ struct BucketPlan {
     d_flat_unc = d_flat_all = nullptr;
     d_pjobs = d_qjobs = nullptr;
     d_qinit = nullptr;
-    intro_E = intro_PQ = nullptr;
+    intro_E = intro_PQ = Emat = nullptr;
     intro_off.clear();
     allocated = false;
   }
@@ -588,12 +593,54 @@ double pass_bytes(int kind, bool f16, bool ef, int prec = kStF32) {
     }
   }
   const double g = f16 ? 2.0 : 4.0;
+  // fp32 with error feedback: pass 1 reads G and M'_prev and writes M' (12), pass 2
+  // reads M' (4), pass 3 writes M_hat (4)
   switch (kind) {
     case K_PASS1: return f16 ? (g + (ef ? 4.0 : 0.0)) : (ef ? 12.0 : 4.0);
     case K_PASS2: return f16 ? (g + (ef ? 4.0 : 0.0)) : 4.0;
-    case K_PASS3: return ef ? 12.0 : g;
+    case K_PASS3: return (ef && f16) ? 12.0 : g;
     default: return 0.0;
   }
+}
+
+}  // namespace
+
+namespace {
+
+// The error E = M'_prev - P Q^T of every tensor of an fp32 plan whose E's place holds
+// M'_prev, written to dst (E's layout; dst may be pl.E itself), on stream s.
+powersgd_status materialize_error(BucketPlan& pl, float* dst, hipStream_t s) {
+  Pass3Args a{};
+  a.tiles = pl.d_tiles3;
+  a.ntiles = static_cast<int32_t>(pl.tiles3.size());
+  a.td = pl.d_td;
+  a.E = pl.E;
+  a.P = pl.P;
+  a.Q = pl.Q;
+  a.inv_scale = 1.0f;
+  a.Eout = dst;
+  const hipError_t e = launch_error_materialize(pl.R, a, s);
+  if (e != hipSuccess) return hip_fail(e, "error materialization");
+  return POWERSGD_OK;
+}
+
+// Device memory holding the error of an fp32 plan, E's layout: E's place itself, or a
+// copy materialized on stream s.
+powersgd_status error_source(BucketPlan& pl, hipStream_t s, const float** out) {
+  if (pl.w_holds_e) {
+    *out = pl.E;
+    return POWERSGD_OK;
+  }
+  if (!pl.Emat) {
+    void* p = nullptr;
+    if (hipMalloc(&p, std::max<int64_t>(pl.e_floats, 1) * sizeof(float)) != hipSuccess)
+      return fail(POWERSGD_ERR_OOM, "allocation of the materialized error failed");
+    pl.Emat = static_cast<float*>(p);
+  }
+  powersgd_status r = materialize_error(pl, pl.Emat, s);
+  if (r != POWERSGD_OK) return r;
+  *out = pl.Emat;
+  return POWERSGD_OK;
 }
 
 }  // namespace
@@ -811,6 +858,16 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
   const bool fused = R <= kMaxFusedGramRank;
   const uint64_t bucket_key = static_cast<uint64_t>(bucket_index);
   powersgd_status r = POWERSGD_OK;
+  // an fp32 call with error feedback keeps M' in E's place; it rebuilds the previous
+  // error from M'_prev, P and the warm-start Q unless E's place holds the error itself
+  const bool sm = ef && !f16 && prec == kStF32;
+  if (ef && pl.E && !pl.w_holds_e && nt > 0 && (!sm || !hp.warm_start)) {
+    // this call cannot rebuild (fp16, or a fresh Q draw replaces the Q it would need):
+    // the error itself goes into E's place first
+    r = materialize_error(pl, pl.E, s);
+    if (r != POWERSGD_OK) return r;
+    pl.w_holds_e = true;
+  }
 
   if (nt > 0) {
     // Step 3.1: a fresh orthogonalized N(0, 1) draw when there is no warm Q.
@@ -855,6 +912,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.Q = pl.Q;
     a.QT = pl.QT;
     a.P = fused ? pl.Praw : pl.P;
+    a.Pe = (sm && !pl.w_holds_e) ? pl.P : nullptr;
     a.gram = pl.gram;
     a.Eh = pl.Eh;
     a.Mh = pl.Mh;
@@ -941,6 +999,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     if (r != POWERSGD_OK) return r;
   }
   pl.q_ready = hp.warm_start != 0;
+  if (sm && nt > 0) pl.w_holds_e = false;
 
   st->numel_in += pl.all_elems;
   st->numel_comm += pl.comm_elems;
@@ -1178,7 +1237,10 @@ powersgd_status powersgd_copy_error(powersgd_state* st, int64_t bucket_index, in
     if (e != hipSuccess) return hip_fail(e, "copy of E");
     return POWERSGD_OK;
   }
-  hipError_t e = hipMemcpyAsync(e_dev, pl->E + d->eoff,
+  const float* src = nullptr;
+  r = error_source(*pl, static_cast<hipStream_t>(stream), &src);
+  if (r != POWERSGD_OK) return r;
+  hipError_t e = hipMemcpyAsync(e_dev, src + d->eoff,
                                 static_cast<size_t>(d->n) * d->m * sizeof(float),
                                 hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "copy of E");
@@ -1246,6 +1308,11 @@ powersgd_status powersgd_get_error(powersgd_state* st, int64_t bucket_index, con
     pl.intro_E = static_cast<float*>(p);
   }
   hipStream_t s = pl.last_stream;
+  const float* src = nullptr;
+  if (pl.E) {
+    powersgd_status rs = error_source(pl, s, &src);
+    if (rs != POWERSGD_OK) return rs;
+  }
   hipError_t e = launch_fill_zero(pl.intro_E, false, 0, len, s);
   for (const TensorDesc& d : pl.tensors) {
     if (e != hipSuccess) break;
@@ -1253,7 +1320,7 @@ powersgd_status powersgd_get_error(powersgd_state* st, int64_t bucket_index, con
     if (pl.Eh)
       e = launch_widen16(pl.Eh + d.eoff, pl.intro_E + d.boff, cnt, pl.st, s);
     else
-      e = hipMemcpyAsync(pl.intro_E + d.boff, pl.E + d.eoff, cnt * sizeof(float),
+      e = hipMemcpyAsync(pl.intro_E + d.boff, src + d.eoff, cnt * sizeof(float),
                          hipMemcpyDeviceToDevice, s);
   }
   if (e != hipSuccess) return hip_fail(e, "fill of the bucket-shaped error");
@@ -1527,7 +1594,8 @@ void write_snapshot(const powersgd_state* st, SnapWriter& w, ExportCopies* copie
             copies->epieces.push_back(
                 ExportCopies::EPiece{ebuf, d.eoff, static_cast<int64_t>(d.n) * d.m, pl.st, dst});
           else
-            copies->segs.push_back(CopySeg{pl.E + d.eoff, dst, bytes});
+            copies->segs.push_back(
+                CopySeg{(pl.w_holds_e ? pl.E : pl.Emat) + d.eoff, dst, bytes});
         }
       }
       if (has_q) {
@@ -1691,6 +1759,15 @@ powersgd_status powersgd_state_export(powersgd_state* st, void* host_buf, int64_
                                               std::to_string(measure.pos) + " bytes");
   HipDeviceGuard guard(st->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // fp32 buckets whose E's place holds M': their error, materialized for the copies
+  for (auto& kv : st->buckets) {
+    BucketPlan& pl = *kv.second;
+    if (pl.E && !pl.w_holds_e) {
+      const float* src = nullptr;
+      powersgd_status r = error_source(pl, s, &src);
+      if (r != POWERSGD_OK) return r;
+    }
+  }
   SnapWriter w;
   w.base = static_cast<uint8_t*>(host_buf);
   ExportCopies copies;

@@ -102,6 +102,11 @@ struct Pass1Args {
   float* E;
   const float* Q;
   float* P;
+  // fp32 buckets with error feedback keep M' of the previous step in E's place; its error
+  // is rebuilt as E = M'_prev - Pe Q^T with Pe the previous orthogonalized P (Q being the
+  // warm-start Q). Null when E's place holds the error itself (first call, after an
+  // import, without warm start).
+  const float* Pe;
   const float* QT;         // matrix-core ranks: Q^T (B fragments as 16-byte loads)
   double* gram;            // P Gram partials (ranks <= 8: computed here)
   uint16_t* Eh;            // 16-bit state: E (E's offsets)
@@ -154,6 +159,7 @@ struct Pass3Args {
   const uint16_t* Mh;      // 16-bit state: M' (E's offsets)
   float inv_scale;
   const int32_t* found_inf;
+  float* Eout;             // error materialization: E = M' - P Q^T written here (E's offsets)
 };
 
 // Precision of the state a bucket keeps: kStF32 for the hook on fp32 or fp16 buckets;
@@ -174,6 +180,10 @@ hipError_t launch_pass2(int R, bool f16, bool ef, int st, bool wide_only, const 
                         hipStream_t s);
 hipError_t launch_pass2_reduce(int R, int st, const Pass2ReduceArgs& a, hipStream_t s);
 hipError_t launch_pass3(int R, bool f16, bool ef, int st, const Pass3Args& a, hipStream_t s);
+// fp32 state with error feedback: the error E = M' - P Q^T of every tensor, from the M'
+// kept in E's place (a.E) and the step's P and Q, into a.Eout (E's layout; may be a.E),
+// with pass 3's tiling and arithmetic, so the values are the ones pass 3's M_hat implies.
+hipError_t launch_error_materialize(int R, const Pass3Args& a, hipStream_t s);
 hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs,
                        const float* base, double* gram, const int32_t* found_inf,
                        hipStream_t s);

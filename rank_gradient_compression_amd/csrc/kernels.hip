@@ -10,24 +10,29 @@
 //   Streaming passes share one tiling: (row block x 256-column block) work items;
 //   a lane owns 4 consecutive columns (16-byte accesses) and keeps several rows of
 //   loads in flight; narrow matrices pack several rows into one wavefront.
-//   pass 1  M' = G (+ E); fp32 writes M' back in place; P = M' Q. A workgroup owns
-//           whole rows, so each dot product is finished inside it (shuffles, then
-//           LDS across wavefronts). fp16: x * inv_scale and an OR of "not finite"
-//           into found_inf.
-//   orth    Gram-Schmidt with epsilon on P (and on the initial Q draw) from fp64 Gram
-//           partials (pass 1 accumulates them for ranks <= 8, a small LDS-staged
-//           kernel otherwise): the partials are summed in a fixed order, the
-//           recurrence runs on r x r coefficient vectors (lane j owns column j) and
-//           P <- P T is applied in fp64. Ranks <= 8 do this in the prologue of every
-//           pass-2 workgroup for its own rows; larger ranks in a kernel of its own.
+//   error memory  an fp32 bucket with error feedback keeps, in E's place, M' of the
+//           previous step instead of E = M' - M_hat: with the step's P and Q (which
+//           the state keeps anyway) the error is rebuilt exactly, as E = M'_prev -
+//           P Q^T with the very arithmetic pass 3 uses for M_hat. Pass 3 then only
+//           writes M_hat (4 bytes per element instead of 12). fp16 buckets, whose
+//           step may be skipped after pass 1 has run, and 16-bit states keep E.
+//   pass 1  M' = G (+ E); fp32: E rebuilt from M'_prev, and M' written over it;
+//           P = M' Q. A workgroup owns whole rows, so each dot product is finished
+//           inside it (shuffles, then LDS across wavefronts). fp16: x * inv_scale and
+//           an OR of "not finite" into found_inf.
+//   orth    Gram-Schmidt with epsilon on P (and on the initial Q draw), run on the
+//           columns of the Cholesky factor of P^T P (see the orthogonalization
+//           section); ranks <= 8 do this in the prologue of every pass-2 workgroup
+//           for its own rows from pass 1's Gram partials, larger ranks in kernels of
+//           their own.
 //   pass 2  Q = M'^T P. A workgroup owns a 256-column block of a row block; its row
 //           slots and wavefronts are combined in a fixed order; tensors with several
 //           row blocks write one partial per block, summed in a fixed order by the
 //           pass-3 workgroups of that column block (vector ranks) or by a small
 //           kernel of its own (matrix-core ranks): deterministic, no atomics, no
 //           inter-workgroup fences (the kernel boundary publishes the partials).
-//   pass 3  M_hat = P Q^T written into the bucket (fp16: round to nearest even),
-//           E = M' - M_hat.
+//   pass 3  M_hat = P Q^T written into the bucket (fp16: round to nearest even); fp16
+//           and 16-bit states also E = M' - M_hat.
 //   q_init  Philox4x64-10 + Box-Muller draw of the initial Q (counter layout in
 //           the public header's companion documentation).
 #include <hip/hip_fp16.h>
@@ -551,6 +556,28 @@ __device__ __forceinline__ void store_p_row(float* __restrict__ Pt, int row,
   }
 }
 
+// M_hat = P Q^T for 4 consecutive columns of one row (vector ranks): one fused
+// multiply-add chain in rank order per value. Pass 3 writes these values and the error
+// memory of an fp32 state is rebuilt from them (E = M' - M_hat), so every user computes
+// them here.
+template <int R>
+__device__ __forceinline__ void mhat4(const float (&p)[R], const float (&q)[4][R],
+                                      float (&mh)[4]) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    float s = p[0] * q[a][0];
+#pragma unroll
+    for (int k = 1; k < R; ++k) s = __builtin_fmaf(p[k], q[a][k], s);
+    mh[a] = s;
+  }
+}
+
+// An fp32 bucket with error feedback keeps M' of the previous step in E's place (the
+// error is rebuilt from it and the step's factors); fp16 buckets and 16-bit states keep
+// the error itself.
+template <bool F16, bool EF, int ST>
+constexpr bool stored_mprime() { return EF && !F16 && ST == kStF32; }
+
 // ----------------------------------------------------------------------- pass 1
 
 __device__ void f16_check_range(const FlatTile ft, const void* bucket,
@@ -626,16 +653,22 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
   const int r1 = min(d.n, r0 + d.rpb1);
   const float* __restrict__ Qt = args.Q + d.qoff;
   float* __restrict__ Et = args.E + d.eoff;
-  float* __restrict__ Mt = static_cast<float*>(args.bucket) + d.boff;
+  constexpr bool SM = stored_mprime<F16, EF, ST>();
+  // E's place holds M'_prev: rebuild E = M'_prev - Pe Q^T (Q is the warm-start Q)
+  const bool rebuild = SM && args.Pe != nullptr;
   int bad = 0;
   for (int rw = r0; rw < r1; rw += slots * U) {
     int64_t rbase[U];
     bool rok[U];
+    float pe[U][R];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = rw + u * slots + slot;
       rok[u] = row < r1;
       rbase[u] = static_cast<int64_t>(min(row, r1 - 1)) * m;
+      if constexpr (SM) {
+        if (rebuild) load_p_row<R>(args.Pe + d.poff, min(row, r1 - 1), pe[u]);
+      }
     }
     float acc[U][R];
 #pragma unroll
@@ -676,12 +709,23 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
         float e[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) ld_f32x4<LD>(Et + rbase[u] + c, valid, e[u]);
+        if constexpr (SM) {
+          if (rebuild) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+              float mh[4];
+              mhat4<R>(pe[u], q, mh);
+#pragma unroll
+              for (int a = 0; a < 4; ++a) e[u][a] = e[u][a] - mh[a];
+            }
+          }
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
           for (int a = 0; a < 4; ++a) x[u][a] += e[u][a];
-          if constexpr (!F16) {
-            if (rok[u]) st_f32x4<LD>(Mt + rbase[u] + c, valid, x[u]);
+          if constexpr (SM) {
+            if (rok[u]) st_f32x4<LD>(Et + rbase[u] + c, valid, x[u]);  // M' in E's place
           }
         }
       }
@@ -1152,14 +1196,18 @@ __device__ __forceinline__ void orth_from_factor(int rank, double eps, OrthShare
 
 // ----------------------------------------------------------------------- pass 2
 
-// M' at element `off` of a matrix (fp32 with error feedback: the bucket already holds
-// M', written by pass 1; fp16: unscaled gradient plus E; 16-bit state: M' from Mt).
+// M' at element `off` of a matrix (fp32 with error feedback: pass 1 wrote M' into E's
+// place; fp16: unscaled gradient plus E; 16-bit state: M' from Mt).
 template <bool F16, bool EF, int LD, int ST = kStF32>
 __device__ __forceinline__ void ld_mprime4(const void* bucket, const float* Et, int64_t boff,
                                            int64_t off, int valid, float inv_scale,
                                            float (&x)[4], const uint16_t* Mt = nullptr) {
   if constexpr (ST != kStF32) {
     ld_h4<ST, LD>(Mt + off, valid, x);  // a 16-bit state keeps M' of pass 1
+    return;
+  }
+  if constexpr (stored_mprime<F16, EF, ST>()) {
+    ld_f32x4<LD>(Et + off, valid, x);  // pass 1 left M' in E's place
     return;
   }
   bool rb;
@@ -1504,15 +1552,20 @@ __device__ __forceinline__ void pass3_q_from_partials(const Pass3Args& args, con
 }
 
 // M_hat = P Q^T into the bucket and E = M' - M_hat over one tile. All loads of an
-// iteration come from rows clamped into the tile; stores are kept to real rows.
-template <int R, int U, bool F16, bool EF, int LD, bool WIDE, int ST>
+// iteration come from rows clamped into the tile; stores are kept to real rows. An fp32
+// state with error feedback writes M_hat only (its error is rebuilt from M' and the
+// factors); MAT (the error materialization) writes E = M' - M_hat to Eout instead of
+// M_hat to the bucket, with the same M_hat.
+template <int R, int U, bool F16, bool EF, int LD, bool WIDE, int ST, bool MAT = false>
 __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDesc& d,
                                            const Tile& t, float* qred) {
+  constexpr bool SM = stored_mprime<F16, EF, ST>();
+  constexpr bool LOADX = EF && (!SM || MAT);  // M' is read
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
   const LaneGeom L = tile_geom<WIDE>(d, t.b, lane);
   float q[4][R];
-  if (d.nrb > 1) {
+  if (d.nrb > 1 && !MAT) {
     pass3_q_from_partials<R, ST>(args, d, t, L, lane, wave, qred, q);
   } else {
     load_q_rows<R>(args.Q + d.qoff, L.c, d.m, q);
@@ -1529,10 +1582,11 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int rowc = min(rw + u * stride + L.slot, r1 - 1);
-      ld_mprime4<F16, EF, LD, ST>(args.bucket, Et, d.boff,
-                                   static_cast<int64_t>(rowc) * d.m + L.c, L.valid,
-                                   args.inv_scale, x[u],
-                                   ST != kStF32 ? args.Mh + d.eoff : nullptr);
+      if constexpr (LOADX)
+        ld_mprime4<F16, EF, LD, ST>(args.bucket, Et, d.boff,
+                                     static_cast<int64_t>(rowc) * d.m + L.c, L.valid,
+                                     args.inv_scale, x[u],
+                                     ST != kStF32 ? args.Mh + d.eoff : nullptr);
       if constexpr (WIDE)
         load_p_row_uniform<R>(Pt, __builtin_amdgcn_readfirstlane(rowc), p[u]);
       else
@@ -1544,18 +1598,21 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
       if (row >= r1) continue;
       const int64_t off = static_cast<int64_t>(row) * d.m + L.c;
       float mh[4];
+      mhat4<R>(p[u], q, mh);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        float s = 0.f;
+      for (int a = 0; a < 4; ++a) mh[a] = rnd16<ST>(mh[a]);
+      if constexpr (MAT) {
+        float e[4];
 #pragma unroll
-        for (int k = 0; k < R; ++k) s += p[u][k] * q[a][k];
-        mh[a] = rnd16<ST>(s);
+        for (int a = 0; a < 4; ++a) e[a] = x[u][a] - mh[a];
+        st_f32x4<LD>(args.Eout + d.eoff + off, L.valid, e);
+        continue;
       }
       if constexpr (F16)
         st_f16x4<LD>(static_cast<uint16_t*>(args.bucket) + d.boff + off, L.valid, mh);
       else
         st_f32x4<LD>(static_cast<float*>(args.bucket) + d.boff + off, L.valid, mh);
-      if constexpr (EF) {
+      if constexpr (EF && !SM) {
         float e[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) e[a] = x[u][a] - mh[a];
@@ -1568,10 +1625,24 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
   }
 }
 
-template <int R, int U, bool F16, bool EF, int ST>
+template <int R, int U, bool F16, bool EF, int ST, bool MAT = false>
 __global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
   if (F16 && *args.found_inf) return;
   __shared__ float qred[4 * 4 * R * 64];
+  if constexpr (MAT) {
+    if (static_cast<int>(blockIdx.x) >= args.ntiles) return;
+    const Tile t = args.tiles[blockIdx.x];
+    const TensorDesc d = args.td[t.tensor];
+    if (d.vec && d.lpr == 64)
+      pass3_body<R, U, F16, EF, kLdAligned, true, ST, true>(args, d, t, qred);
+    else if (d.vec)
+      pass3_body<R, U, F16, EF, kLdAligned, false, ST, true>(args, d, t, qred);
+    else if (d.m >= 4)
+      pass3_body<R, U, F16, EF, kLdUnaligned, false, ST, true>(args, d, t, qred);
+    else
+      pass3_body<R, U, F16, EF, kLdScalar, false, ST, true>(args, d, t, qred);
+    return;
+  }
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
     if constexpr (F16)
       f16_unscale_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.inv_scale);
@@ -1626,8 +1697,25 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
   const bool row_ok = row < r1;
   const int rowc = min(row, r1 - 1);
   float* __restrict__ Et = args.E + d.eoff;
-  float* __restrict__ Mt = static_cast<float*>(args.bucket) + d.boff;
   const float* __restrict__ QTt = args.QT + d.qtoff;
+  constexpr bool SM = stored_mprime<F16, EF, ST>();
+  constexpr int KQ = R / 4;
+  // E's place holds M'_prev: E = M'_prev - Pe Q^T, with pass 3's matrix-core steps (lane
+  // (h, cl) holds columns 4h..4h+3 of a 16-column group of row cl, which is this body's
+  // element layout)
+  const bool rebuild = SM && args.Pe != nullptr;
+  float pe[KQ];
+  if constexpr (SM) {
+    if (rebuild) {
+#pragma unroll
+      for (int k4 = 0; k4 < KQ / 4; ++k4) {
+        float w[4];
+        load_f4(args.Pe + d.poff + static_cast<int64_t>(rowc) * R + h * KQ + 4 * k4, w);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) pe[4 * k4 + a] = w[a];
+      }
+    }
+  }
   mfma_f4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
@@ -1687,6 +1775,24 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
             for (int a = 0; a < 4; ++a) b[u][nt][a] = 0.f;
         }
       }
+      if constexpr (SM) {
+        if (rebuild) {
+          const int qcol = min(k0 + 16 * u + cl, m - 1);
+          float qa[KQ];
+#pragma unroll
+          for (int k4 = 0; k4 < KQ / 4; ++k4) {
+            float w[4];
+            load_f4(args.Q + d.qoff + static_cast<int64_t>(qcol) * R + h * KQ + 4 * k4, w);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) qa[4 * k4 + a] = w[a];
+          }
+          mfma_f4 mh = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kq = 0; kq < KQ; ++kq) mh = mfma16(qa[kq], pe[kq], mh);
+#pragma unroll
+          for (int a = 0; a < 4; ++a) e[u][a] = e[u][a] - mh[a];
+        }
+      }
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         float v = x[u][a];
@@ -1706,8 +1812,8 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
             st_h4<ST, kLdScalar>(args.Mh + d.eoff + static_cast<int64_t>(row) * m + col, m - col,
                                  x[u]);
         }
-      } else if constexpr (EF && !F16) {
-        if (ok[u]) store_f32x4(Mt + static_cast<int64_t>(row) * m + col, VEC, m - col, x[u]);
+      } else if constexpr (SM) {
+        if (ok[u]) store_f32x4(Et + static_cast<int64_t>(row) * m + col, VEC, m - col, x[u]);
       }
     }
 #pragma unroll
@@ -1754,7 +1860,7 @@ constexpr int kPass1TileStride = kColBlock + 4;  // LDS row stride (floats), pad
 template <int R, bool F16, bool EF, int ST>
 __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const TensorDesc& d,
                                                 const Tile& t, int lane, int wave, float* red,
-                                                float* tile) {
+                                                float* tile, float* mh_tile) {
   constexpr int NT = R / 16;
   constexpr int LS = kPass1TileStride;
   const int m = d.m;
@@ -1763,8 +1869,49 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
   const int h = lane >> 4;
   const int cl = lane & 15;
   float* __restrict__ Et = args.E + d.eoff;
-  float* __restrict__ Mt = static_cast<float*>(args.bucket) + d.boff;
   const float* __restrict__ QTt = args.QT + d.qtoff;
+  constexpr bool SM = stored_mprime<F16, EF, ST>();
+  constexpr int KQ = R / 4;
+  // E's place holds M'_prev: E = M'_prev - Pe Q^T. A chunk's M_hat_prev is formed with
+  // pass 3's matrix-core steps (wavefront w: the chunk's columns 64w..64w+63, lane (h,
+  // cl) columns 4h..4h+3 of each 16-column group of row cl) into the LDS tile mh_tile,
+  // one chunk ahead, between the barriers that already separate the phases; the row
+  // phase reads its rows back from there.
+  const bool rebuild = SM && args.Pe != nullptr;
+  float pe[KQ];
+  auto rebuild_chunk = [&](int kc0) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int qcol = min(kc0 + 64 * wave + 16 * g + cl, m - 1);
+      float qa[KQ];
+#pragma unroll
+      for (int k4 = 0; k4 < KQ / 4; ++k4) {
+        float w[4];
+        load_f4(args.Q + d.qoff + static_cast<int64_t>(qcol) * R + h * KQ + 4 * k4, w);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) qa[4 * k4 + a] = w[a];
+      }
+      mfma_f4 mh = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) mh = mfma16(qa[kq], pe[kq], mh);
+      *reinterpret_cast<float4*>(mh_tile + cl * kPass1TileStride + 64 * wave + 16 * g + 4 * h) =
+          make_float4(mh[0], mh[1], mh[2], mh[3]);
+    }
+  };
+  if constexpr (SM) {
+    if (rebuild) {
+      const int prow = min(r0 + cl, r1 - 1);
+#pragma unroll
+      for (int k4 = 0; k4 < KQ / 4; ++k4) {
+        float w[4];
+        load_f4(args.Pe + d.poff + static_cast<int64_t>(prow) * R + h * KQ + 4 * k4, w);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) pe[4 * k4 + a] = w[a];
+      }
+      rebuild_chunk(0);
+      __syncthreads();
+    }
+  }
   mfma_f4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
@@ -1799,6 +1946,16 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float v[4];
+      if constexpr (SM) {
+        if (rebuild) {
+          const float4 mh =
+              *reinterpret_cast<const float4*>(mh_tile + (4 * wave + i) * kPass1TileStride + 4 * lane);
+          xe[i][0] = xe[i][0] - mh.x;
+          xe[i][1] = xe[i][1] - mh.y;
+          xe[i][2] = xe[i][2] - mh.z;
+          xe[i][3] = xe[i][3] - mh.w;
+        }
+      }
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         float x = xg[i][a];
@@ -1812,8 +1969,8 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
       }
       if constexpr (ST != kStF32) {
         if (rok[i] && cok) st_h4<ST, kLdAligned>(args.Mh + d.eoff + rbase[i] + col, 4, v);
-      } else if constexpr (EF && !F16) {
-        if (rok[i] && cok) store_f32x4(Mt + rbase[i] + col, true, 4, v);
+      } else if constexpr (SM) {
+        if (rok[i] && cok) store_f32x4(Et + rbase[i] + col, true, 4, v);  // M' in E's place
       }
       *reinterpret_cast<float4*>(tile + (4 * wave + i) * LS + 4 * lane) =
           make_float4(v[0], v[1], v[2], v[3]);
@@ -1847,7 +2004,12 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(a4[s4], b[u][nt][s4], acc[nt]);
     }
-    __syncthreads();  // the tile is rewritten by the next chunk
+    if constexpr (SM) {
+      // the next chunk's M_hat_prev: this chunk's row phase read mh_tile before the
+      // barrier above
+      if (rebuild && k0 + kColBlock < m) rebuild_chunk(k0 + kColBlock);
+    }
+    __syncthreads();  // the tiles are rewritten by the next chunk
   }
   if constexpr (F16) {
     if (__any(bad) && lane == 0) atomicOr(args.found_inf, 1);
@@ -1877,8 +2039,12 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
 template <int R, bool F16, bool EF, int ST>
 __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
   static_assert(kMfmaPass1Rows == 16, "a workgroup owns one 16-row MFMA group");
-  __shared__ float red[4 * (R / 16) * 4 * 64];
+  // the wavefronts' partial P (4 x NT x 4 x 64 floats) go through the M' tile once the
+  // last chunk's barrier has freed it
+  static_assert(4 * (R / 16) * 4 * 64 <= 16 * kPass1TileStride, "partial P fits the tile");
   __shared__ float tile[16 * kPass1TileStride];
+  __shared__ float mh_tile[stored_mprime<F16, EF, ST>() ? 16 * kPass1TileStride : 1];
+  float* red = tile;
   const int lane = threadIdx.x & 63;
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
     if constexpr (F16)
@@ -1889,7 +2055,7 @@ __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec)
-    pass1_mfma_rows<R, F16, EF, ST>(args, d, t, lane, wave, red, tile);
+    pass1_mfma_rows<R, F16, EF, ST>(args, d, t, lane, wave, red, tile, mh_tile);
   else
     pass1_mfma_body<R, F16, EF, false, ST>(args, d, t, lane, wave, red);
 }
@@ -1930,13 +2096,17 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
         ld_h4<ST, kLdAligned>(args.Mh + d.eoff + static_cast<int64_t>(rowc) * m + colc, 4, x[u]);
       } else if constexpr (VEC) {
         const int64_t off = static_cast<int64_t>(rowc) * m + colc;
-        bool rb;
-        load_grad4_vec<F16>(args.bucket, d.boff + off, args.inv_scale, x[u], rb);
-        if constexpr (F16 && EF) {
-          float e[4];
-          load_f4(Et + off, e);
+        if constexpr (stored_mprime<F16, EF, ST>()) {
+          load_f4(Et + off, x[u]);  // pass 1 left M' in E's place
+        } else {
+          bool rb;
+          load_grad4_vec<F16>(args.bucket, d.boff + off, args.inv_scale, x[u], rb);
+          if constexpr (F16 && EF) {
+            float e[4];
+            load_f4(Et + off, e);
 #pragma unroll
-          for (int a = 0; a < 4; ++a) x[u][a] += e[a];
+            for (int a = 0; a < 4; ++a) x[u][a] += e[a];
+          }
         }
       } else {
         if (row < r1 && col_ok) {
@@ -2127,9 +2297,11 @@ __global__ void __launch_bounds__(kThreads) k_pass2_mfma(Pass2Args args) {
 // holds 4 consecutive columns (4h..4h+3) of row cl of each 16 x 16 output block.
 // MFMA K-step kq of lane group h uses rank index h * KQ + kq, so A and B fragments are
 // KQ consecutive floats of a Q row and of a P row.
-template <int R, bool F16, bool EF, bool VEC, int ST>
+template <int R, bool F16, bool EF, bool VEC, int ST, bool MAT = false>
 __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const TensorDesc& d,
                                                 const Tile& t, int lane, int wave) {
+  constexpr bool SM = stored_mprime<F16, EF, ST>();
+  constexpr bool LOADX = EF && (!SM || MAT);  // M' is read
   constexpr int KQ = R / 4;
   constexpr int UR = 2;  // 16-row steps loaded before use
   const int m = d.m;
@@ -2171,10 +2343,14 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = c0 + 16 * g + 4 * h;
-        if constexpr (VEC && ST != kStF32) {
+        if constexpr (!LOADX) {
+          // M' is not needed
+        } else if constexpr (VEC && ST != kStF32) {
           if constexpr (EF)
             ld_h4<ST, kLdAligned>(args.Mh + d.eoff + static_cast<int64_t>(rowc) * m +
                                       min(col, m - 4), 4, x[ur][g]);
+        } else if constexpr (VEC && SM) {
+          load_f4(Et + static_cast<int64_t>(rowc) * m + min(col, m - 4), x[ur][g]);
         } else if constexpr (VEC) {
           const int64_t off = static_cast<int64_t>(rowc) * m + min(col, m - 4);
           bool rb;
@@ -2207,11 +2383,18 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
           const int64_t off = static_cast<int64_t>(row) * m + col;
           float mh[4] = {rnd16<ST>(acc[0]), rnd16<ST>(acc[1]), rnd16<ST>(acc[2]),
                          rnd16<ST>(acc[3])};
+          if constexpr (MAT) {
+            float e[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) e[a] = x[ur][g][a] - mh[a];
+            store_f32x4(args.Eout + d.eoff + off, VEC, m - col, e);
+            continue;
+          }
           if constexpr (F16)
             store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, VEC, m - col, mh);
           else
             store_f32x4(static_cast<float*>(args.bucket) + d.boff + off, VEC, m - col, mh);
-          if constexpr (EF) {
+          if constexpr (EF && !SM) {
             float e[4];
 #pragma unroll
             for (int a = 0; a < 4; ++a) e[a] = x[ur][g][a] - mh[a];
@@ -2239,10 +2422,12 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
 // requested before its MFMAs.
 constexpr int kPass3TileStride = kColBlock + 4;  // LDS row stride (floats), padded
 
-template <int R, bool F16, bool EF, int ST>
+template <int R, bool F16, bool EF, int ST, bool MAT = false>
 __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const TensorDesc& d,
                                                 const Tile& t, int lane, int wave,
                                                 float* tile) {
+  constexpr bool SM = stored_mprime<F16, EF, ST>();
+  constexpr bool LOADX = EF && (!SM || MAT);  // M' is read
   constexpr int KQ = R / 4;
   constexpr int UR = 2;         // 16-row MFMA groups per step
   constexpr int SR = 16 * UR;   // rows per step
@@ -2274,7 +2459,7 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
   }
   for (int rr = r0; rr < r1; rr += SR) {
     float x[RW][4];
-    if constexpr (EF) {
+    if constexpr (LOADX) {
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
         const int row = min(rr + RW * wave + i, r1 - 1);
@@ -2315,11 +2500,18 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
         const float4 v = *reinterpret_cast<const float4*>(tile + (RW * wave + i) * LS + 4 * lane);
         const float mh[4] = {rnd16<ST>(v.x), rnd16<ST>(v.y), rnd16<ST>(v.z), rnd16<ST>(v.w)};
         const int64_t off = static_cast<int64_t>(row) * m + cr;
+        if constexpr (MAT) {
+          float e[4];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) e[a] = x[i][a] - mh[a];
+          store_f32x4(args.Eout + d.eoff + off, true, 4, e);
+          continue;
+        }
         if constexpr (F16)
           store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, true, 4, mh);
         else
           store_f32x4(static_cast<float*>(args.bucket) + d.boff + off, true, 4, mh);
-        if constexpr (EF) {
+        if constexpr (EF && !SM) {
           float e[4];
 #pragma unroll
           for (int a = 0; a < 4; ++a) e[a] = x[i][a] - mh[a];
@@ -2334,11 +2526,13 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
   }
 }
 
-template <int R, bool F16, bool EF, int ST>
+template <int R, bool F16, bool EF, int ST, bool MAT = false>
 __global__ void __launch_bounds__(kThreads) k_pass3_mfma(Pass3Args args) {
   if (F16 && *args.found_inf) return;
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
-    if constexpr (F16)
+    if constexpr (MAT)
+      return;
+    else if constexpr (F16)
       f16_unscale_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.inv_scale);
     else if constexpr (ST != kStF32)
       round_range<ST>(args.ftiles[blockIdx.x - args.ntiles], args.bucket);
@@ -2350,9 +2544,9 @@ __global__ void __launch_bounds__(kThreads) k_pass3_mfma(Pass3Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec)
-    pass3_mfma_rows<R, F16, EF, ST>(args, d, t, lane, wave, tile);
+    pass3_mfma_rows<R, F16, EF, ST, MAT>(args, d, t, lane, wave, tile);
   else
-    pass3_mfma_body<R, F16, EF, false, ST>(args, d, t, lane, wave);
+    pass3_mfma_body<R, F16, EF, false, ST, MAT>(args, d, t, lane, wave);
 }
 
 // ------------------------------------------------------------ orthogonalization
@@ -2752,6 +2946,18 @@ hipError_t launch_pass2_reduce(int R, int st, const Pass2ReduceArgs& a, hipStrea
 
 hipError_t launch_pass3(int R, bool f16, bool ef, int st, const Pass3Args& a, hipStream_t s) {
   PSGD_RANK_SWITCH(R, return pass3_r<RR>(f16, ef, st, a, s))
+}
+
+hipError_t launch_error_materialize(int R, const Pass3Args& a, hipStream_t s) {
+  if (a.ntiles == 0) return hipSuccess;
+  const dim3 grid(a.ntiles);
+  PSGD_RANK_SWITCH(R, {
+    if constexpr (RR >= kMfmaMinRank)
+      k_pass3_mfma<RR, false, true, kStF32, true><<<grid, kThreads, 0, s>>>(a);
+    else
+      k_pass3<RR, unroll3<RR, kStF32>(), false, true, kStF32, true><<<grid, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+  })
 }
 
 hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs,

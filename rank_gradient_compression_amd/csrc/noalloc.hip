@@ -304,6 +304,12 @@ extern "C" POWERSGD_API powersgd_status powersgd_compress_matrix_noalloc(
     a.partial = c.partial;
     a.inv_scale = 1.0f;
     if (!check(launch_pass3(R, false, ef, kStF32, a, s), "pass 3 launch")) return POWERSGD_ERR_HIP;
+    if (ef) {
+      // pass 1 left M' in E's place (the caller's E): the error itself goes back there
+      a.Eout = E;
+      if (!check(launch_error_materialize(R, a, s), "error materialization launch"))
+        return POWERSGD_ERR_HIP;
+    }
   }
   k_noalloc_out<<<grid_for((P ? L.d.n : 0) * static_cast<int64_t>(r) +
                            static_cast<int64_t>(L.d.m) * r), 256, 0, s>>>(
