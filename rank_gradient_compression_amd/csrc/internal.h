@@ -248,11 +248,11 @@ constexpr int kPass1SlotSums = 544;
 // separate Gram kernel reads P.
 constexpr int kMaxFusedGramRank = 8;
 // Padded ranks from this value up run the three passes on matrix cores
-// (v_mfma_f32_16x16x4f32): pass-1 row blocks are 16 rows (the four wavefronts split
-// the columns), pass 2 and pass 3 tiles are kMfmaRowBlock rows x 256 columns (64 per
-// wavefront).
+// (v_mfma_f32_16x16x4f32): pass-1 row blocks are 32 rows, two MFMA row groups of 16
+// (the four wavefronts split the columns, and each Q^T fragment serves both groups),
+// pass 2 and pass 3 tiles are kMfmaRowBlock rows x 256 columns (64 per wavefront).
 constexpr int kMfmaMinRank = 16;
-constexpr int kMfmaPass1Rows = 16;
+constexpr int kMfmaPass1Rows = 32;
 constexpr int kMfmaRowBlock = 1024;
 // Threads per workgroup of the pass-2 partial reduction.
 constexpr int kReduceThreads = 1024;

@@ -1685,12 +1685,13 @@ __device__ __forceinline__ mfma_f4 mfma16(float a, float b, mfma_f4 c) {
 // used, and invalid lanes are masked after.
 template <int R, bool F16, bool EF, bool VEC, int ST>
 __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const TensorDesc& d,
-                                                const Tile& t, int lane, int wave, float* red) {
+                                                const Tile& t, int grp, int lane, int wave,
+                                                float* red) {
   constexpr int NT = R / 16;
   constexpr int U = 4;
   const int m = d.m;
-  const int r0 = t.a * d.rpb1;
-  const int r1 = min(d.n, r0 + d.rpb1);
+  const int r0 = t.a * d.rpb1 + 16 * grp;  // the work item's row group grp
+  const int r1 = min(min(d.n, t.a * d.rpb1 + d.rpb1), r0 + 16);
   const int h = lane >> 4;
   const int cl = lane & 15;
   const int row = r0 + cl;
@@ -1832,36 +1833,41 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[((wave * NT + nt) * 4 + v) * 64 + lane] = acc[nt][v];
   __syncthreads();
-  if (wave != 0) return;
+  if (wave == 0) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float sum = red[(nt * 4 + v) * 64 + lane];
+      for (int v = 0; v < 4; ++v) {
+        float sum = red[(nt * 4 + v) * 64 + lane];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) sum += red[((w * NT + nt) * 4 + v) * 64 + lane];
-      const int prow = r0 + 4 * h + v;
-      const int k = 16 * nt + cl;
-      if (prow < r1)
-        args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? rnd16<ST>(sum) : 0.f;
+        for (int w = 1; w < 4; ++w) sum += red[((w * NT + nt) * 4 + v) * 64 + lane];
+        const int prow = r0 + 4 * h + v;
+        const int k = 16 * nt + cl;
+        if (prow < r1)
+          args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? rnd16<ST>(sum) : 0.f;
+      }
     }
   }
 }
 
 // Pass 1 on matrix cores with row-contiguous memory traffic (rows 16-byte aligned): the
-// workgroup's 16 rows are processed in 256-column chunks. Row phase: wavefront w loads
-// rows 4w..4w+3 of the chunk (lane l: columns 4l..4l+3, 1 KB of a row per load), forms
-// M' (fp32 with error feedback: stored back the same way) and writes it to an LDS
-// tile. MFMA phase: wavefront w takes the chunk's columns 64w..64w+63 (four K-steps of
-// 16) from the tile, with the matching 16 bytes of Q^T rows 16nt + cl per K-step. The
-// next chunk's rows are requested before the MFMA phase of this one.
+// workgroup's MT groups of 16 rows are processed in 256-column chunks. Row phase:
+// wavefront w loads rows 4MT w .. 4MT w + 4MT - 1 of the chunk (lane l: columns
+// 4l..4l+3, 1 KB of a row per load), forms M' (fp32 with error feedback: stored back the
+// same way) and writes it to an LDS tile. MFMA phase: wavefront w takes the chunk's
+// columns 64w..64w+63 (four K-steps of 16) of every row group, with the matching 16
+// bytes of Q^T rows 16nt + cl per K-step, loaded once for all MT groups. The next
+// chunk's rows are requested before the MFMA phase of this one.
 constexpr int kPass1TileStride = kColBlock + 4;  // LDS row stride (floats), padded
+constexpr int kPass1Groups = kMfmaPass1Rows / 16;
 
 template <int R, bool F16, bool EF, int ST>
 __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const TensorDesc& d,
                                                 const Tile& t, int lane, int wave, float* red,
                                                 float* tile, float* mh_tile) {
   constexpr int NT = R / 16;
+  constexpr int MT = kPass1Groups;
+  constexpr int RW = 4 * MT;  // rows per wavefront in the row phase
   constexpr int LS = kPass1TileStride;
   const int m = d.m;
   const int r0 = t.a * d.rpb1;
@@ -1874,11 +1880,12 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
   constexpr int KQ = R / 4;
   // E's place holds M'_prev: E = M'_prev - Pe Q^T. A chunk's M_hat_prev is formed with
   // pass 3's matrix-core steps (wavefront w: the chunk's columns 64w..64w+63, lane (h,
-  // cl) columns 4h..4h+3 of each 16-column group of row cl) into the LDS tile mh_tile,
-  // one chunk ahead, between the barriers that already separate the phases; the row
-  // phase reads its rows back from there.
+  // cl) columns 4h..4h+3 of each 16-column group of row cl of a row group; the Q
+  // operand is loaded once for the MT groups) into the LDS tile mh_tile, one chunk
+  // ahead, between the barriers that already separate the phases; the row phase reads
+  // its rows back from there.
   const bool rebuild = SM && args.Pe != nullptr;
-  float pe[KQ];
+  float pe[MT][KQ];
   auto rebuild_chunk = [&](int kc0) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -1891,45 +1898,54 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
 #pragma unroll
         for (int a = 0; a < 4; ++a) qa[4 * k4 + a] = w[a];
       }
-      mfma_f4 mh = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kq = 0; kq < KQ; ++kq) mh = mfma16(qa[kq], pe[kq], mh);
-      *reinterpret_cast<float4*>(mh_tile + cl * kPass1TileStride + 64 * wave + 16 * g + 4 * h) =
-          make_float4(mh[0], mh[1], mh[2], mh[3]);
+      for (int mt = 0; mt < MT; ++mt) {
+        mfma_f4 mh = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) mh = mfma16(qa[kq], pe[mt][kq], mh);
+        *reinterpret_cast<float4*>(mh_tile + (16 * mt + cl) * LS + 64 * wave + 16 * g + 4 * h) =
+            make_float4(mh[0], mh[1], mh[2], mh[3]);
+      }
     }
   };
   if constexpr (SM) {
     if (rebuild) {
-      const int prow = min(r0 + cl, r1 - 1);
 #pragma unroll
-      for (int k4 = 0; k4 < KQ / 4; ++k4) {
-        float w[4];
-        load_f4(args.Pe + d.poff + static_cast<int64_t>(prow) * R + h * KQ + 4 * k4, w);
+      for (int mt = 0; mt < MT; ++mt) {
+        const int prow = min(r0 + 16 * mt + cl, r1 - 1);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) pe[4 * k4 + a] = w[a];
+        for (int k4 = 0; k4 < KQ / 4; ++k4) {
+          float w[4];
+          load_f4(args.Pe + d.poff + static_cast<int64_t>(prow) * R + h * KQ + 4 * k4, w);
+#pragma unroll
+          for (int a = 0; a < 4; ++a) pe[mt][4 * k4 + a] = w[a];
+        }
       }
       rebuild_chunk(0);
       __syncthreads();
     }
   }
-  mfma_f4 acc[NT];
+  mfma_f4 acc[MT][NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
   int bad = 0;
-  // row phase geometry: rows 4w..4w+3 of the group, columns 4l..4l+3 of the chunk
-  int64_t rbase[4];
-  bool rok[4];
+  // row phase geometry: rows RW w .. RW w + RW - 1 of the work item, columns 4l..4l+3
+  // of the chunk
+  int64_t rbase[RW];
+  bool rok[RW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = r0 + 4 * wave + i;
+  for (int i = 0; i < RW; ++i) {
+    const int row = r0 + RW * wave + i;
     rok[i] = row < r1;
     rbase[i] = static_cast<int64_t>(min(row, r1 - 1)) * m;
   }
-  float xg[4][4], xe[4][4];
+  float xg[RW][4], xe[RW][4];
   auto load_rows = [&](int k0) {
     const int colc = min(k0 + 4 * lane, m - 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < RW; ++i) {
       bool rb;
       load_grad4_vec<F16>(args.bucket, d.boff + rbase[i] + colc, args.inv_scale, xg[i], rb);
       if (rok[i] && k0 + 4 * lane < m && rb) bad = 1;
@@ -1944,12 +1960,12 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
     const int col = k0 + 4 * lane;
     const bool cok = col < m;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < RW; ++i) {
       float v[4];
       if constexpr (SM) {
         if (rebuild) {
           const float4 mh =
-              *reinterpret_cast<const float4*>(mh_tile + (4 * wave + i) * kPass1TileStride + 4 * lane);
+              *reinterpret_cast<const float4*>(mh_tile + (RW * wave + i) * LS + 4 * lane);
           xe[i][0] = xe[i][0] - mh.x;
           xe[i][1] = xe[i][1] - mh.y;
           xe[i][2] = xe[i][2] - mh.z;
@@ -1972,7 +1988,7 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
       } else if constexpr (SM) {
         if (rok[i] && cok) store_f32x4(Et + rbase[i] + col, true, 4, v);  // M' in E's place
       }
-      *reinterpret_cast<float4*>(tile + (4 * wave + i) * LS + 4 * lane) =
+      *reinterpret_cast<float4*>(tile + (RW * wave + i) * LS + 4 * lane) =
           make_float4(v[0], v[1], v[2], v[3]);
     }
     if (k0 + kColBlock < m) load_rows(k0 + kColBlock);
@@ -1991,8 +2007,6 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int kc = 64 * wave + 16 * u + 4 * h;  // column inside the chunk
-      const float4 av = *reinterpret_cast<const float4*>(tile + cl * LS + kc);
-      const float a4[4] = {av.x, av.y, av.z, av.w};
       if (k0 + kc >= m) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -2000,9 +2014,15 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
           for (int a = 0; a < 4; ++a) b[u][nt][a] = 0.f;
       }
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
+      for (int mt = 0; mt < MT; ++mt) {
+        const float4 av = *reinterpret_cast<const float4*>(tile + (16 * mt + cl) * LS + kc);
+        const float a4[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(a4[s4], b[u][nt][s4], acc[nt]);
+        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            acc[mt][nt] = mfma16(a4[s4], b[u][nt][s4], acc[mt][nt]);
+      }
     }
     if constexpr (SM) {
       // the next chunk's M_hat_prev: this chunk's row phase read mh_tile before the
@@ -2014,21 +2034,25 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
   if constexpr (F16) {
     if (__any(bad) && lane == 0) atomicOr(args.found_inf, 1);
   }
-  // partial P of every wavefront to LDS; wavefront 0 adds them in order
+  // partial P of every wavefront to LDS; the (row group, column group) pairs are split
+  // over the wavefronts, each adding the four partials in wavefront order
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[((wave * NT + nt) * 4 + v) * 64 + lane] = acc[nt][v];
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        red[(((wave * MT + mt) * NT + nt) * 4 + v) * 64 + lane] = acc[mt][nt][v];
   __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int pr = wave; pr < MT * NT; pr += 4) {
+    const int mt = pr / NT;
+    const int nt = pr - mt * NT;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float sum = red[(nt * 4 + v) * 64 + lane];
+      float sum = red[((mt * NT + nt) * 4 + v) * 64 + lane];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) sum += red[((w * NT + nt) * 4 + v) * 64 + lane];
-      const int prow = r0 + 4 * h + v;
+      for (int w = 1; w < 4; ++w) sum += red[(((w * MT + mt) * NT + nt) * 4 + v) * 64 + lane];
+      const int prow = r0 + 16 * mt + 4 * h + v;
       const int k = 16 * nt + cl;
       if (prow < r1)
         args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? rnd16<ST>(sum) : 0.f;
@@ -2038,12 +2062,13 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
 
 template <int R, bool F16, bool EF, int ST>
 __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
-  static_assert(kMfmaPass1Rows == 16, "a workgroup owns one 16-row MFMA group");
-  // the wavefronts' partial P (4 x NT x 4 x 64 floats) go through the M' tile once the
-  // last chunk's barrier has freed it
-  static_assert(4 * (R / 16) * 4 * 64 <= 16 * kPass1TileStride, "partial P fits the tile");
-  __shared__ float tile[16 * kPass1TileStride];
-  __shared__ float mh_tile[stored_mprime<F16, EF, ST>() ? 16 * kPass1TileStride : 1];
+  static_assert(kMfmaPass1Rows % 16 == 0, "a workgroup owns whole 16-row MFMA groups");
+  // the wavefronts' partial P (4 x MT x NT x 4 x 64 floats) go through the M' tile once
+  // the last chunk's barrier has freed it
+  static_assert(4 * kPass1Groups * (R / 16) * 4 * 64 <= kMfmaPass1Rows * kPass1TileStride,
+                "partial P fits the tile");
+  __shared__ float tile[kMfmaPass1Rows * kPass1TileStride];
+  __shared__ float mh_tile[stored_mprime<F16, EF, ST>() ? kMfmaPass1Rows * kPass1TileStride : 1];
   float* red = tile;
   const int lane = threadIdx.x & 63;
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
@@ -2054,10 +2079,15 @@ __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
   const int wave = wave_index();
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
-  if (d.vec)
+  if (d.vec) {
     pass1_mfma_rows<R, F16, EF, ST>(args, d, t, lane, wave, red, tile, mh_tile);
-  else
-    pass1_mfma_body<R, F16, EF, false, ST>(args, d, t, lane, wave, red);
+  } else {
+    // one row group after the other (the partial-P area is reused)
+    for (int grp = 0; grp < kPass1Groups && t.a * d.rpb1 + 16 * grp < d.n; ++grp) {
+      if (grp) __syncthreads();
+      pass1_mfma_body<R, F16, EF, false, ST>(args, d, t, grp, lane, wave, red);
+    }
+  }
 }
 
 // Pass 2, Q = M'^T P: a wavefront owns 64 columns of the tile; lane group h takes row
