@@ -1864,7 +1864,7 @@ constexpr int kPass1Groups = kMfmaPass1Rows / 16;
 template <int R, bool F16, bool EF, int ST>
 __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const TensorDesc& d,
                                                 const Tile& t, int lane, int wave, float* red,
-                                                float* tile, float* mh_tile) {
+                                                float* tile, float* mh_tile, float* qx_tile) {
   constexpr int NT = R / 16;
   constexpr int MT = kPass1Groups;
   constexpr int RW = 4 * MT;  // rows per wavefront in the row phase
@@ -1878,26 +1878,53 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
   const float* __restrict__ QTt = args.QT + d.qtoff;
   constexpr bool SM = stored_mprime<F16, EF, ST>();
   constexpr int KQ = R / 4;
+  // Q^T fragments of a chunk: lane (h, cl) holds rows 16nt + cl, columns 16u + 4h..4h+3
+  // of wavefront w's 64 columns; loaded one chunk ahead
+  auto load_b = [&](int k0, float (&bq)[4][NT][4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int colc = min(k0 + 64 * wave + 16 * u + 4 * h, m - 4);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        load_f4(QTt + static_cast<int64_t>(16 * nt + cl) * d.mstride + colc, bq[u][nt]);
+    }
+  };
   // E's place holds M'_prev: E = M'_prev - Pe Q^T. A chunk's M_hat_prev is formed with
   // pass 3's matrix-core steps (wavefront w: the chunk's columns 64w..64w+63, lane (h,
-  // cl) columns 4h..4h+3 of each 16-column group of row cl of a row group; the Q
-  // operand is loaded once for the MT groups) into the LDS tile mh_tile, one chunk
-  // ahead, between the barriers that already separate the phases; the row phase reads
-  // its rows back from there.
+  // cl) columns 4h..4h+3 of each 16-column group of row cl of a row group) into the LDS
+  // tile mh_tile, one chunk ahead, between the barriers that already separate the
+  // phases; the row phase reads its rows back from there. The Q operand (lane (h, cl):
+  // column cl of the group, ranks h R/4 .. h R/4 + R/4 - 1) is the chunk's Q^T
+  // fragments transposed through the wavefront's own LDS region qx (16 columns x QS
+  // floats), the same values pass 3 read as Q.
+  constexpr int QS = R + 4;
+  float* qx = qx_tile + wave * 16 * QS;
   const bool rebuild = SM && args.Pe != nullptr;
   float pe[MT][KQ];
-  auto rebuild_chunk = [&](int kc0) {
+  auto rebuild_chunk = [&](const float (&bq)[4][NT][4]) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int qcol = min(kc0 + 64 * wave + 16 * g + cl, m - 1);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) qx[(4 * h + s4) * QS + 16 * nt + cl] = bq[g][nt][s4];
+      // the wavefront's LDS accesses take effect in program order; the fences keep
+      // the compiler from moving them across
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       float qa[KQ];
 #pragma unroll
       for (int k4 = 0; k4 < KQ / 4; ++k4) {
-        float w[4];
-        load_f4(args.Q + d.qoff + static_cast<int64_t>(qcol) * R + h * KQ + 4 * k4, w);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) qa[4 * k4 + a] = w[a];
+        const float4 w = *reinterpret_cast<const float4*>(qx + cl * QS + h * KQ + 4 * k4);
+        qa[4 * k4 + 0] = w.x;
+        qa[4 * k4 + 1] = w.y;
+        qa[4 * k4 + 2] = w.z;
+        qa[4 * k4 + 3] = w.w;
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         mfma_f4 mh = {0.f, 0.f, 0.f, 0.f};
@@ -1908,6 +1935,8 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
       }
     }
   };
+  float b[4][NT][4];
+  load_b(0, b);
   if constexpr (SM) {
     if (rebuild) {
 #pragma unroll
@@ -1921,7 +1950,7 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
           for (int a = 0; a < 4; ++a) pe[mt][4 * k4 + a] = w[a];
         }
       }
-      rebuild_chunk(0);
+      rebuild_chunk(b);
       __syncthreads();
     }
   }
@@ -1992,17 +2021,9 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
           make_float4(v[0], v[1], v[2], v[3]);
     }
     if (k0 + kColBlock < m) load_rows(k0 + kColBlock);
-    // this chunk's Q^T fragments do not depend on the tile: request them before the
-    // barrier so their latency overlaps it
-    float b[4][NT][4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kc = 64 * wave + 16 * u + 4 * h;
-      const int colc = min(k0 + kc, m - 4);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        load_f4(QTt + static_cast<int64_t>(16 * nt + cl) * d.mstride + colc, b[u][nt]);
-    }
+    // the next chunk's Q^T fragments (clamped in bounds after the last chunk)
+    float bn[4][NT][4];
+    load_b(k0 + kColBlock, bn);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -2027,9 +2048,15 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
     if constexpr (SM) {
       // the next chunk's M_hat_prev: this chunk's row phase read mh_tile before the
       // barrier above
-      if (rebuild && k0 + kColBlock < m) rebuild_chunk(k0 + kColBlock);
+      if (rebuild && k0 + kColBlock < m) rebuild_chunk(bn);
     }
     __syncthreads();  // the tiles are rewritten by the next chunk
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) b[u][nt][a] = bn[u][nt][a];
   }
   if constexpr (F16) {
     if (__any(bad) && lane == 0) atomicOr(args.found_inf, 1);
@@ -2069,6 +2096,7 @@ __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
                 "partial P fits the tile");
   __shared__ float tile[kMfmaPass1Rows * kPass1TileStride];
   __shared__ float mh_tile[stored_mprime<F16, EF, ST>() ? kMfmaPass1Rows * kPass1TileStride : 1];
+  __shared__ float qx_tile[stored_mprime<F16, EF, ST>() ? 4 * 16 * (R + 4) : 1];
   float* red = tile;
   const int lane = threadIdx.x & 63;
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
@@ -2080,7 +2108,7 @@ __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
   const Tile t = args.tiles[blockIdx.x];
   const TensorDesc d = args.td[t.tensor];
   if (d.vec) {
-    pass1_mfma_rows<R, F16, EF, ST>(args, d, t, lane, wave, red, tile, mh_tile);
+    pass1_mfma_rows<R, F16, EF, ST>(args, d, t, lane, wave, red, tile, mh_tile, qx_tile);
   } else {
     // one row group after the other (the partial-P area is reused)
     for (int grp = 0; grp < kPass1Groups && t.a * d.rpb1 + 16 * grp < d.n; ++grp) {
