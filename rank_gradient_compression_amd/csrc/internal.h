@@ -265,9 +265,10 @@ constexpr int kPass2StageFloats = 4096;
 constexpr int64_t kMaxMatrixDim = 2147483647LL - 65536;
 // Rows per Gram partial of the separate Gram kernel.
 constexpr int kGramRows = 256;
-// Rows transformed by one workgroup of the orthogonalization kernel (each workgroup
-// recomputes the small r x r transform from the Gram partials).
+// Rows transformed by one workgroup of the orthogonalization kernel, by padded rank
+// (matrix-core ranks: a row per thread).
 constexpr int kOrthRows = 1024;
+constexpr int orth_rows(int R) { return R >= kMfmaMinRank ? kThreads : kOrthRows; }
 
 // One n x m matrix as the bucket plan lays out a bucket that holds only that matrix
 // (every buffer offset is 0; compressed without the rate test at rank min(r, n, m)):

@@ -1041,7 +1041,8 @@ __device__ __forceinline__ void orth_gram_sum(const OrthJob& j, const double* __
 }
 
 // Sums the job's double-double Gram partials (partial p: NG high parts, then NG low
-// parts, at goff + 2 NG p) into sh.Gh / sh.Gl, a thread per entry, partials in order.
+// parts, at goff + 2 NG p) into sh.Gh / sh.Gl, a thread per entry, partials in order
+// (loaded eight at a time).
 // Every thread takes part; ends with a barrier.
 template <int R>
 __device__ __forceinline__ void orth_gram_sum_dd(const OrthJob& j, const double* __restrict__ gram,
@@ -1050,8 +1051,18 @@ __device__ __forceinline__ void orth_gram_sum_dd(const OrthJob& j, const double*
   for (int e = threadIdx.x; e < NG; e += blockDim.x) {
     DD s{0.0, 0.0};
     const double* src = gram + j.goff + e;
-    for (int p = 0; p < j.nparts; ++p)
-      s = dd_add(s, DD{src[static_cast<int64_t>(p) * 2 * NG], src[static_cast<int64_t>(p) * 2 * NG + NG]});
+    for (int p0 = 0; p0 < j.nparts; p0 += 8) {
+      double vh[8], vl[8];  // eight partials in flight, then added in order
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int64_t p = min(p0 + q, j.nparts - 1);
+        vh[q] = src[p * 2 * NG];
+        vl[q] = src[p * 2 * NG + NG];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (p0 + q < j.nparts) s = dd_add(s, DD{vh[q], vl[q]});
+    }
     int a, b;
     tri_entry(e, R, a, b);
     sh.Gh[a][b] = s.hi;
@@ -1141,6 +1152,43 @@ __device__ __forceinline__ void orth_cholesky(int rank, double tau, OrthShared<R
     __builtin_amdgcn_wave_barrier();
   }
   if (lane == 0 && tau > 0.0) sh.redo = redo;
+}
+
+// The factor of orth_cholesky without the pivot check (tau = 0), with the same
+// operations on every entry in the same order, but each column step spread over the
+// whole workgroup: the lanes of wavefront 0 form row k, then every thread updates
+// entries of the trailing block. Every thread takes part; ends with a barrier.
+template <int R>
+__device__ __forceinline__ void orth_cholesky_wg(int rank, OrthShared<R>& sh) {
+  const int tid = threadIdx.x;
+  for (int k = 0; k < rank; ++k) {
+    if (tid >= k && tid < rank) {
+      const DD d{sh.Gh[k][k], sh.Gl[k][k]};
+      const bool pos = d.hi > 0.0;
+      DD c{0.0, 0.0};
+      if (pos) {
+        const DD piv = dd_sqrt(d);
+        c = tid == k ? piv : dd_div(DD{sh.Gh[k][tid], sh.Gl[k][tid]}, piv);
+      }
+      sh.Gh[k][tid] = c.hi;
+      sh.Gl[k][tid] = c.lo;
+    }
+    __syncthreads();
+    // G_ij -= C_ki C_kj for k < i <= j < rank
+    const int w = rank - k - 1;
+    for (int e = tid; e < w * w; e += blockDim.x) {
+      const int i = k + 1 + e / w;
+      const int jj = k + 1 + e % w;
+      if (i <= jj) {
+        const DD cki{sh.Gh[k][i], sh.Gl[k][i]};
+        const DD ckj{sh.Gh[k][jj], sh.Gl[k][jj]};
+        const DD g = dd_add(DD{sh.Gh[i][jj], sh.Gl[i][jj]}, dd_neg(dd_mul(cki, ckj)));
+        sh.Gh[i][jj] = g.hi;
+        sh.Gl[i][jj] = g.lo;
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // Gram-Schmidt with epsilon on the columns of the factor (sh.Gh, upper triangle; the
@@ -2611,6 +2659,36 @@ __global__ void __launch_bounds__(kThreads) k_pass3_mfma(Pass3Args args) {
 
 // Gram partials of one row chunk of a job, staged through LDS, as double-double sums
 // of the exact products: partial p holds NG high parts, then NG low parts.
+// Matrix-core ranks: a thread owns a 4 x 4 block of entries (column groups ga <= gb)
+// and one of S row phases (rows ph, ph + S, ...), adding each exact product to a
+// binary64 sum with TwoSum and the rounding errors to a second sum (Ogita, Rump and
+// Oishi, "Accurate sum and dot product", algorithm Sum2); the S sums of an entry are
+// then added in phase order through LDS, eight entries of every block at a time.
+// Vector ranks: a thread per entry, rows in order.
+template <int R>
+constexpr int gram_blocks() {
+  return (R / 4) * (R / 4 + 1) / 2;
+}
+template <int R>
+constexpr int gram_lds_floats() {
+  if constexpr (R >= kMfmaMinRank) {
+    constexpr int comb = gram_blocks<R>() * (kThreads / gram_blocks<R>()) * 8 * 2 * 2;
+    return comb > kGramRows * R ? comb : kGramRows * R;
+  } else {
+    return kGramRows * R;
+  }
+}
+
+__device__ __forceinline__ void gram_block_of(int blk, int nb, int& ga, int& gb) {
+  int rem = blk;
+  ga = 0;
+  while (rem >= nb - ga) {
+    rem -= nb - ga;
+    ++ga;
+  }
+  gb = ga + rem;
+}
+
 template <int R>
 __global__ void __launch_bounds__(kThreads)
     k_gram(const Tile* __restrict__ tiles, const OrthJob* __restrict__ jobs,
@@ -2618,23 +2696,89 @@ __global__ void __launch_bounds__(kThreads)
            const int32_t* __restrict__ found_inf) {
   if (found_inf != nullptr && *found_inf) return;
   constexpr int NG = gram_size<R>();
-  __shared__ float xs[kGramRows * R];
+  __shared__ __align__(16) float xs[gram_lds_floats<R>()];
   const Tile t = tiles[blockIdx.x];
   const OrthJob j = jobs[t.tensor];
   const int r0 = t.a * j.rpp;
   const int nr = min(j.rpp, j.rows - r0);
   const float* X = base + j.off + static_cast<int64_t>(r0) * R;
-  for (int f = threadIdx.x; f < nr * R; f += kThreads) xs[f] = X[f];
-  __syncthreads();
   double* out = gram + j.goff + static_cast<int64_t>(t.a) * 2 * NG;
-  for (int e = threadIdx.x; e < NG; e += kThreads) {
-    int a, b;
-    tri_entry(e, R, a, b);
-    DD s{0.0, 0.0};
-    for (int r = 0; r < nr; ++r)
-      s = dd_add_d(s, static_cast<double>(xs[r * R + a]) * static_cast<double>(xs[r * R + b]));
-    out[e] = s.hi;
-    out[NG + e] = s.lo;
+  const int tid = threadIdx.x;
+  if constexpr (R >= kMfmaMinRank) {
+    constexpr int NB = R / 4;
+    constexpr int NBLK = gram_blocks<R>();
+    constexpr int S = kThreads / NBLK;
+    static_assert(S >= 1, "a row phase per block at least");
+    // rows are 16-byte aligned (R and the job offset are multiples of 4)
+    for (int f = tid; f < nr * R / 4; f += kThreads)
+      *reinterpret_cast<float4*>(xs + 4 * f) = *reinterpret_cast<const float4*>(X + 4 * f);
+    __syncthreads();
+    const int blk = tid / S;
+    const int ph = tid - blk * S;
+    int ga = 0, gb = 0;
+    if (blk < NBLK) gram_block_of(blk, NB, ga, gb);
+    double sh[16], sc[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sh[q] = sc[q] = 0.0;
+    if (blk < NBLK) {
+      for (int r = ph; r < nr; r += S) {
+        const float4 va = *reinterpret_cast<const float4*>(xs + r * R + 4 * ga);
+        const float4 vb = *reinterpret_cast<const float4*>(xs + r * R + 4 * gb);
+        const double a[4] = {va.x, va.y, va.z, va.w};
+        const double b[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const DD u = dd_two_sum(sh[4 * i + q], a[i] * b[q]);  // the product is exact
+            sh[4 * i + q] = u.hi;
+            sc[4 * i + q] += u.lo;
+          }
+      }
+    }
+    __syncthreads();  // the staged rows are no longer needed: their LDS takes the sums
+    double* red = reinterpret_cast<double*>(xs);
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      if (blk < NBLK) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const DD v = dd_two_sum(sh[8 * half + q], sc[8 * half + q]);
+          red[((blk * 8 + q) * S + ph) * 2] = v.hi;
+          red[((blk * 8 + q) * S + ph) * 2 + 1] = v.lo;
+        }
+      }
+      __syncthreads();
+      for (int idx = tid; idx < NBLK * 8; idx += kThreads) {
+        const int b2 = idx / 8;
+        const int k = 8 * half + (idx - b2 * 8);
+        int ga2, gb2;
+        gram_block_of(b2, NB, ga2, gb2);
+        const int a = 4 * ga2 + k / 4;
+        const int b = 4 * gb2 + k % 4;
+        if (a <= b) {
+          DD sum{red[idx * S * 2], red[idx * S * 2 + 1]};
+          for (int p = 1; p < S; ++p)
+            sum = dd_add(sum, DD{red[(idx * S + p) * 2], red[(idx * S + p) * 2 + 1]});
+          const int e = a * R - a * (a - 1) / 2 + (b - a);  // upper-triangle index
+          out[e] = sum.hi;
+          out[NG + e] = sum.lo;
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    for (int f = tid; f < nr * R; f += kThreads) xs[f] = X[f];
+    __syncthreads();
+    for (int e = tid; e < NG; e += kThreads) {
+      int a, b;
+      tri_entry(e, R, a, b);
+      DD s{0.0, 0.0};
+      for (int r = 0; r < nr; ++r)
+        s = dd_add_d(s, static_cast<double>(xs[r * R + a]) * static_cast<double>(xs[r * R + b]));
+      out[e] = s.hi;
+      out[NG + e] = s.lo;
+    }
   }
 }
 
@@ -2649,16 +2793,17 @@ __global__ void __launch_bounds__(kThreads)
   __shared__ OrthShared<R> sh;
   const OrthJob j = jobs[blockIdx.x];
   orth_gram_sum_dd<R>(j, gram, sh);
-  orth_cholesky<R>(j.rank, 0.0, sh);
-  __syncthreads();
+  orth_cholesky_wg<R>(j.rank, sh);
   orth_from_factor<R>(j.rank, eps, sh);
   double* dst = tmat + static_cast<int64_t>(blockIdx.x) * R * R;
   for (int f = threadIdx.x; f < R * R; f += kThreads) dst[f] = sh.T[f / R][f % R];
 }
 
-// X <- X T in fp64, rounded to fp32 (and to the state's 16 bits), for kOrthRows rows of
-// a job per workgroup (several rows loaded before any is transformed); with toff >= 0
-// the result is also written transposed.
+// X <- X T in fp64, rounded to fp32 (and to the state's 16 bits), for orth_rows(R) rows
+// of a job per workgroup; with toff >= 0 the result is also written transposed. Each
+// output is one fp64 chain over l = 0..R-1; matrix-core ranks: a row per thread, four
+// outputs at a time; vector ranks: four rows per thread loaded before any is
+// transformed.
 template <int R, int ST>
 __global__ void __launch_bounds__(kThreads)
     k_orth(const OrthJob* __restrict__ jobs, float* __restrict__ base, float* __restrict__ tbase,
@@ -2667,39 +2812,67 @@ __global__ void __launch_bounds__(kThreads)
   __shared__ double T[R][R];
   const OrthJob j = jobs[blockIdx.y];
   const int tid = threadIdx.x;
-  const int row_begin = blockIdx.x * kOrthRows;
+  const int row_begin = blockIdx.x * orth_rows(R);
   if (row_begin >= j.rows) return;
   const double* src = tmat + static_cast<int64_t>(blockIdx.y) * R * R;
   for (int f = tid; f < R * R; f += kThreads) T[f / R][f % R] = src[f];
   __syncthreads();
   float* X = base + j.off;
-  const int row_end = min(j.rows, row_begin + kOrthRows);
-  constexpr int B = R <= 8 ? 4 : 1;
-  for (int row0 = row_begin + tid; row0 < row_end; row0 += kThreads * B) {
-    float x[B][R];
+  const int row_end = min(j.rows, row_begin + orth_rows(R));
+  if constexpr (R >= kMfmaMinRank) {
+    const int row = row_begin + tid;
+    if (row >= row_end) return;
+    float x[R];
+    load_p_row<R>(X, row, x);
+    float* dst = X + static_cast<int64_t>(row) * R;
+#pragma unroll 1
+    for (int k0 = 0; k0 < R; k0 += 4) {
+      double s[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const int row = row0 + b * kThreads;
-      if (row < row_end) {
-        load_p_row<R>(X, row, x[b]);
-      } else {
+      for (int l = 0; l < R; ++l) {
+        const double xl = static_cast<double>(x[l]);
 #pragma unroll
-        for (int l = 0; l < R; ++l) x[b][l] = 0.f;
+        for (int q = 0; q < 4; ++q) s[q] += xl * T[l][k0 + q];
+      }
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = rnd16<ST>(static_cast<float>(s[q]));
+      *reinterpret_cast<float4*>(dst + k0) = make_float4(v[0], v[1], v[2], v[3]);
+      if (j.toff >= 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          tbase[j.toff + static_cast<int64_t>(k0 + q) * j.tstride + row] = v[q];
       }
     }
+    return;
+  } else {
+    constexpr int B = 4;
+    for (int row0 = row_begin + tid; row0 < row_end; row0 += kThreads * B) {
+      float x[B][R];
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const int row = row0 + b * kThreads;
-      if (row >= row_end) continue;
-      float* dst = X + static_cast<int64_t>(row) * R;
+      for (int b = 0; b < B; ++b) {
+        const int row = row0 + b * kThreads;
+        if (row < row_end) {
+          load_p_row<R>(X, row, x[b]);
+        } else {
+#pragma unroll
+          for (int l = 0; l < R; ++l) x[b][l] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const int row = row0 + b * kThreads;
+        if (row >= row_end) continue;
+        float* dst = X + static_cast<int64_t>(row) * R;
 #pragma unroll 1
-      for (int k = 0; k < R; ++k) {
-        double s = 0.0;
+        for (int k = 0; k < R; ++k) {
+          double s = 0.0;
 #pragma unroll
-        for (int l = 0; l < R; ++l) s += static_cast<double>(x[b][l]) * T[l][k];
-        const float v = rnd16<ST>(static_cast<float>(s));
-        dst[k] = v;
-        if (j.toff >= 0) tbase[j.toff + static_cast<int64_t>(k) * j.tstride + row] = v;
+          for (int l = 0; l < R; ++l) s += static_cast<double>(x[b][l]) * T[l][k];
+          const float v = rnd16<ST>(static_cast<float>(s));
+          dst[k] = v;
+          if (j.toff >= 0) tbase[j.toff + static_cast<int64_t>(k) * j.tstride + row] = v;
+        }
       }
     }
   }
@@ -3032,7 +3205,7 @@ hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, int max_rows, floa
                        float* tbase, const double* gram, double* tmat, double eps,
                        const int32_t* found_inf, int st, hipStream_t s) {
   if (njobs == 0) return hipSuccess;
-  const dim3 grid((max_rows + kOrthRows - 1) / kOrthRows, njobs);
+  const dim3 grid((max_rows + orth_rows(R) - 1) / orth_rows(R), njobs);
   PSGD_RANK_SWITCH(R, {
     k_orth_t<RR><<<dim3(njobs), kThreads, 0, s>>>(jobs, gram, tmat, eps, found_inf);
     hipError_t e = hipGetLastError();
