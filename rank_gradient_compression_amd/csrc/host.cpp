@@ -156,10 +156,12 @@ struct BucketPlan {
   float* intro_PQ = nullptr;
   std::vector<int64_t> intro_off;  // per tensor: first float of its compact P, then Q
   hipStream_t last_stream = nullptr;  // stream of the latest compressing call
-  // E's place (fp32 error memory) holds the error itself (true: before the first call,
-  // after an import, after an fp16 call) or M' of the previous fp32 call, whose error is
-  // rebuilt from it and the step's P and Q (false)
+  // E's place (fp32 error memory) is known to hold the error itself (true: before the
+  // first call, after an import, after a materialization in place); false after a call
+  // that keeps M' there (an fp16 step skipped for inf leaves the error in place: the
+  // device flag wflag says which, for the kernels)
   bool w_holds_e = true;
+  int32_t* wflag = nullptr;  // device: non-zero while E's place holds the error itself
   float* Emat = nullptr;  // the materialized error for introspection and export
   bool allocated = false;
   bool q_ready = false;
@@ -169,7 +171,7 @@ struct BucketPlan {
   void release() {
     void* ptrs[] = {E, Eh, Mh, P, Praw, Q, QT, partial, gram, tmat, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
                     d_tiles1, d_tiles2, d_tiles3, d_tiles2r, d_flat_unc, d_flat_all, d_pjobs, d_qjobs,
-                    d_qinit, intro_E, intro_PQ, Emat};
+                    d_qinit, intro_E, intro_PQ, Emat, wflag};
     for (void* p : ptrs)
       if (p) (void)hipFree(p);
     E = P = Praw = Q = QT = partial = nullptr;
@@ -183,6 +185,7 @@ struct BucketPlan {
     d_pjobs = d_qjobs = nullptr;
     d_qinit = nullptr;
     intro_E = intro_PQ = Emat = nullptr;
+    wflag = nullptr;
     intro_off.clear();
     allocated = false;
   }
@@ -513,6 +516,7 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   ok = ok && alloc(reinterpret_cast<void**>(&pl.gram), pl.gram_doubles * sizeof(double));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.tmat),
                    pl.tensors.size() * static_cast<size_t>(pl.R) * pl.R * sizeof(double));
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.wflag), pl.E ? sizeof(int32_t) : 0);
 
   if (!ok) {
     pl.release();
@@ -527,6 +531,7 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
     e = hipMemsetAsync(pl.Praw, 0, pl.p_floats * sizeof(float), s);
   if (pl.Q && e == hipSuccess) e = hipMemsetAsync(pl.Q, 0, pl.q_floats * sizeof(float), s);
   if (pl.QT && e == hipSuccess) e = hipMemsetAsync(pl.QT, 0, pl.qt_floats * sizeof(float), s);
+  if (pl.wflag && e == hipSuccess) e = launch_set_flag(pl.wflag, 1, s);  // E = 0 in place
 
   if (e != hipSuccess) {
     pl.release();
@@ -593,12 +598,13 @@ double pass_bytes(int kind, bool f16, bool ef, int prec = kStF32) {
     }
   }
   const double g = f16 ? 2.0 : 4.0;
-  // fp32 with error feedback: pass 1 reads G and M'_prev and writes M' (12), pass 2
-  // reads M' (4), pass 3 writes M_hat (4)
+  // fp32 state with error feedback: pass 1 reads G and M'_prev and writes M' (g + 8),
+  // pass 2 reads M' (4), pass 3 writes M_hat (g); fp16 buckets add the inf check (2,
+  // counted with the fp16 check kernel)
   switch (kind) {
-    case K_PASS1: return f16 ? (g + (ef ? 4.0 : 0.0)) : (ef ? 12.0 : 4.0);
-    case K_PASS2: return f16 ? (g + (ef ? 4.0 : 0.0)) : 4.0;
-    case K_PASS3: return (ef && f16) ? 12.0 : g;
+    case K_PASS1: return ef ? g + 8.0 : g;
+    case K_PASS2: return ef ? 4.0 : g;
+    case K_PASS3: return g;
     default: return 0.0;
   }
 }
@@ -607,8 +613,9 @@ double pass_bytes(int kind, bool f16, bool ef, int prec = kStF32) {
 
 namespace {
 
-// The error E = M'_prev - P Q^T of every tensor of an fp32 plan whose E's place holds
-// M'_prev, written to dst (E's layout; dst may be pl.E itself), on stream s.
+// The error of every tensor of a plan keeping M' in E's place, written to dst (E's
+// layout; dst may be pl.E itself), on stream s: E = M'_prev - P Q^T, or E's place as it
+// is while the device flag says it holds the error.
 powersgd_status materialize_error(BucketPlan& pl, float* dst, hipStream_t s) {
   Pass3Args a{};
   a.tiles = pl.d_tiles3;
@@ -619,6 +626,7 @@ powersgd_status materialize_error(BucketPlan& pl, float* dst, hipStream_t s) {
   a.Q = pl.Q;
   a.inv_scale = 1.0f;
   a.Eout = dst;
+  a.wflag = pl.wflag;  // E's place may still hold the error itself (a skipped fp16 step)
   const hipError_t e = launch_error_materialize(pl.R, a, s);
   if (e != hipSuccess) return hip_fail(e, "error materialization");
   return POWERSGD_OK;
@@ -858,14 +866,17 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
   const bool fused = R <= kMaxFusedGramRank;
   const uint64_t bucket_key = static_cast<uint64_t>(bucket_index);
   powersgd_status r = POWERSGD_OK;
-  // an fp32 call with error feedback keeps M' in E's place; it rebuilds the previous
-  // error from M'_prev, P and the warm-start Q unless E's place holds the error itself
-  const bool sm = ef && !f16 && prec == kStF32;
+  // a call with error feedback and an fp32 state keeps M' in E's place; it rebuilds the
+  // previous error from M'_prev, P and the warm-start Q unless E's place holds the error
+  // itself
+  const bool sm = ef && prec == kStF32;
   if (ef && pl.E && !pl.w_holds_e && nt > 0 && (!sm || !hp.warm_start)) {
-    // this call cannot rebuild (fp16, or a fresh Q draw replaces the Q it would need):
-    // the error itself goes into E's place first
+    // this call cannot rebuild (a fresh Q draw replaces the Q it would need): the error
+    // itself goes into E's place first
     r = materialize_error(pl, pl.E, s);
     if (r != POWERSGD_OK) return r;
+    const hipError_t e = launch_set_flag(pl.wflag, 1, s);
+    if (e != hipSuccess) return hip_fail(e, "error flag");
     pl.w_holds_e = true;
   }
 
@@ -899,26 +910,38 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
       if (e != hipSuccess) return hip_fail(e, "padding fill");
     }
   }
-  // Pass 1 (+ fp16 inf check of every view).
+  // fp16 with M' kept in E's place: the inf check of every view comes first, so that a
+  // step to be skipped writes nothing (pass 1 would overwrite M'_prev).
+  const bool precheck = f16 && sm;
+  if (precheck) {
+    const double all = static_cast<double>(pl.all_elems);
+    r = timed_launch(st, s, K_UNSCALE, all * 2.0, "fp16 check", [&] {
+      return launch_unscale_only(pl.d_flat_all, static_cast<int>(pl.flat_all.size()), bucket,
+                                 inv_loss_scale, found_inf_dev, true, s);
+    });
+    if (r != POWERSGD_OK) return r;
+  }
+  // Pass 1 (+ fp16 inf check of every view when it did not run above).
   {
     Pass1Args a{};
     a.tiles = pl.d_tiles1;
     a.ntiles = static_cast<int32_t>(pl.tiles1.size());
     a.ftiles = pl.d_flat_unc;
-    a.nftiles = static_cast<int32_t>(pl.flat_unc.size());
+    a.nftiles = precheck ? 0 : static_cast<int32_t>(pl.flat_unc.size());
     a.td = td;
     a.bucket = bucket;
     a.E = pl.E;
     a.Q = pl.Q;
     a.QT = pl.QT;
     a.P = fused ? pl.Praw : pl.P;
-    a.Pe = (sm && !pl.w_holds_e) ? pl.P : nullptr;
+    a.Pe = sm ? pl.P : nullptr;  // the kernels skip the rebuild while wflag is set
+    a.wflag = sm ? pl.wflag : nullptr;
     a.gram = pl.gram;
     a.Eh = pl.Eh;
     a.Mh = pl.Mh;
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
-    const double bytes = ce * pass_bytes(K_PASS1, f16, ef, prec) + (f16 ? ue * 2.0 : 0.0);
+    const double bytes = ce * pass_bytes(K_PASS1, f16, ef, prec) + (f16 && !precheck ? ue * 2.0 : 0.0);
     r = timed_launch(st, s, K_PASS1, bytes, "pass 1",
                      [&] { return launch_pass1(R, f16, ef, prec, a, s); });
     if (r != POWERSGD_OK) return r;
@@ -992,6 +1015,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.Mh = pl.Mh;
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
+    a.wflag = sm ? pl.wflag : nullptr;  // cleared by the pass once the step runs
     const double bytes = ce * pass_bytes(K_PASS3, f16, ef, prec) +
                          (f16 ? ue * 4.0 : (prec != kStF32 ? ue * 8.0 : 0.0));
     r = timed_launch(st, s, K_PASS3, bytes, "pass 3",

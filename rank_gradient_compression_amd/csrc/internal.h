@@ -107,6 +107,9 @@ struct Pass1Args {
   // warm-start Q). Null when E's place holds the error itself (first call, after an
   // import, without warm start).
   const float* Pe;
+  // With Pe: device flag, non-zero while E's place still holds the error itself (then
+  // nothing is rebuilt); pass 3 of a step that ran clears it.
+  const int32_t* wflag;
   const float* QT;         // matrix-core ranks: Q^T (B fragments as 16-byte loads)
   double* gram;            // P Gram partials (ranks <= 8: computed here)
   uint16_t* Eh;            // 16-bit state: E (E's offsets)
@@ -160,6 +163,10 @@ struct Pass3Args {
   float inv_scale;
   const int32_t* found_inf;
   float* Eout;             // error materialization: E = M' - P Q^T written here (E's offsets)
+  // Buckets keeping M' in E's place: the device flag that says E's place still holds the
+  // error itself. Pass 3 of a step that ran clears it; the materialization reads it (set:
+  // the error is copied as it is). Null: E's place holds M'.
+  int32_t* wflag;
 };
 
 // Precision of the state a bucket keeps: kStF32 for the hook on fp32 or fp16 buckets;
@@ -184,6 +191,8 @@ hipError_t launch_pass3(int R, bool f16, bool ef, int st, const Pass3Args& a, hi
 // kept in E's place (a.E) and the step's P and Q, into a.Eout (E's layout; may be a.E),
 // with pass 3's tiling and arithmetic, so the values are the ones pass 3's M_hat implies.
 hipError_t launch_error_materialize(int R, const Pass3Args& a, hipStream_t s);
+// *flag = value (one thread; no memset node, so it can sit in a captured graph).
+hipError_t launch_set_flag(int32_t* flag, int32_t value, hipStream_t s);
 hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs,
                        const float* base, double* gram, const int32_t* found_inf,
                        hipStream_t s);

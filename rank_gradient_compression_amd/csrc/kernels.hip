@@ -572,19 +572,56 @@ __device__ __forceinline__ void mhat4(const float (&p)[R], const float (&q)[4][R
   }
 }
 
-// An fp32 bucket with error feedback keeps M' of the previous step in E's place (the
-// error is rebuilt from it and the step's factors); fp16 buckets and 16-bit states keep
-// the error itself.
+// With error feedback and an fp32 state (fp32 or fp16 buckets), E's place keeps M' of
+// the previous step (the error is rebuilt from it and the step's factors); 16-bit states
+// keep the error itself.
 template <bool F16, bool EF, int ST>
-constexpr bool stored_mprime() { return EF && !F16 && ST == kStF32; }
+constexpr bool stored_mprime() { return EF && ST == kStF32; }
+
+// Whether pass 1 rebuilds the previous error from M'_prev in E's place: a state keeping
+// M', given the previous factors, unless E's place still holds the error itself.
+__device__ __forceinline__ bool rebuild_error(const Pass1Args& a) {
+  return a.Pe != nullptr && !(a.wflag != nullptr && *a.wflag != 0);
+}
+
+// Whether E's place holds the error itself at a materialization.
+__device__ __forceinline__ bool holds_error(const Pass3Args& a) {
+  return a.wflag != nullptr && *a.wflag != 0;
+}
+
+// Pass 3 of a step that ran (after its inf check) marks E's place as holding M': one
+// lane of workgroup 0 (a vector store).
+template <bool F16, bool EF, int ST, bool MAT>
+__device__ __forceinline__ void mark_mprime(const Pass3Args& a) {
+  if constexpr (stored_mprime<F16, EF, ST>() && !MAT) {
+    if (a.wflag != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *a.wflag = 0;
+  }
+}
 
 // ----------------------------------------------------------------------- pass 1
+
+// inf/NaN check of an fp16 range: the values before the first 16-byte boundary one
+// by one, then eight per 16-byte load, then the tail.
+__device__ __forceinline__ int f16_pair_not_finite(uint32_t w) {
+  return ((w & 0x7C00u) == 0x7C00u || (w & 0x7C000000u) == 0x7C000000u) ? 1 : 0;
+}
 
 __device__ void f16_check_range(const FlatTile ft, const void* bucket,
                                 int32_t* found_inf) {
   const uint16_t* h = static_cast<const uint16_t*>(bucket) + ft.start;
+  const int64_t mis = static_cast<int64_t>((reinterpret_cast<uintptr_t>(h) >> 1) & 7);
+  const int64_t head = min(ft.len, (8 - mis) & 7);
+  const int64_t nv = (ft.len - head) / 8;
   int bad = 0;
-  for (int64_t i = threadIdx.x; i < ft.len; i += blockDim.x)
+  for (int64_t i = threadIdx.x; i < head; i += blockDim.x)
+    bad |= half_bits_not_finite(h[i]) ? 1 : 0;
+  const uint4* v = reinterpret_cast<const uint4*>(h + head);
+  for (int64_t i = threadIdx.x; i < nv; i += blockDim.x) {
+    const uint4 w = v[i];
+    bad |= f16_pair_not_finite(w.x) | f16_pair_not_finite(w.y) | f16_pair_not_finite(w.z) |
+           f16_pair_not_finite(w.w);
+  }
+  for (int64_t i = head + 8 * nv + threadIdx.x; i < ft.len; i += blockDim.x)
     bad |= half_bits_not_finite(h[i]) ? 1 : 0;
   if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(found_inf, 1);
 }
@@ -655,7 +692,7 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
   float* __restrict__ Et = args.E + d.eoff;
   constexpr bool SM = stored_mprime<F16, EF, ST>();
   // E's place holds M'_prev: rebuild E = M'_prev - Pe Q^T (Q is the warm-start Q)
-  const bool rebuild = SM && args.Pe != nullptr;
+  const bool rebuild = SM && rebuild_error(args);
   int bad = 0;
   for (int rw = r0; rw < r1; rw += slots * U) {
     int64_t rbase[U];
@@ -830,6 +867,10 @@ template <int R, int U, bool F16, bool EF, int ST>
 __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
   __shared__ float red[kPass1SlotSums * R];
   __shared__ double gred[kThreads / 64][pass1_ng<R>()];
+  if constexpr (F16 && stored_mprime<F16, EF, ST>()) {
+    // the bucket's inf check ran before this pass: a skipped step writes nothing
+    if (*args.found_inf) return;
+  }
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
     if constexpr (F16)
       f16_check_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.found_inf);
@@ -1609,6 +1650,7 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
                                            const Tile& t, float* qred) {
   constexpr bool SM = stored_mprime<F16, EF, ST>();
   constexpr bool LOADX = EF && (!SM || MAT);  // M' is read
+  const bool we = MAT && holds_error(args);  // materialization: E's place holds E
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
   const LaneGeom L = tile_geom<WIDE>(d, t.b, lane);
@@ -1652,7 +1694,7 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
       if constexpr (MAT) {
         float e[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) e[a] = x[u][a] - mh[a];
+        for (int a = 0; a < 4; ++a) e[a] = we ? x[u][a] : x[u][a] - mh[a];
         st_f32x4<LD>(args.Eout + d.eoff + off, L.valid, e);
         continue;
       }
@@ -1676,6 +1718,7 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
 template <int R, int U, bool F16, bool EF, int ST, bool MAT = false>
 __global__ void __launch_bounds__(kThreads) k_pass3(Pass3Args args) {
   if (F16 && *args.found_inf) return;
+  mark_mprime<F16, EF, ST, MAT>(args);
   __shared__ float qred[4 * 4 * R * 64];
   if constexpr (MAT) {
     if (static_cast<int>(blockIdx.x) >= args.ntiles) return;
@@ -1752,7 +1795,7 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
   // E's place holds M'_prev: E = M'_prev - Pe Q^T, with pass 3's matrix-core steps (lane
   // (h, cl) holds columns 4h..4h+3 of a 16-column group of row cl, which is this body's
   // element layout)
-  const bool rebuild = SM && args.Pe != nullptr;
+  const bool rebuild = SM && rebuild_error(args);
   float pe[KQ];
   if constexpr (SM) {
     if (rebuild) {
@@ -1947,7 +1990,7 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
   // floats), the same values pass 3 read as Q.
   constexpr int QS = R + 4;
   float* qx = qx_tile + wave * 16 * QS;
-  const bool rebuild = SM && args.Pe != nullptr;
+  const bool rebuild = SM && rebuild_error(args);
   float pe[MT][KQ];
   auto rebuild_chunk = [&](const float (&bq)[4][NT][4]) {
 #pragma unroll
@@ -2147,6 +2190,10 @@ __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
   __shared__ float qx_tile[stored_mprime<F16, EF, ST>() ? 4 * 16 * (R + 4) : 1];
   float* red = tile;
   const int lane = threadIdx.x & 63;
+  if constexpr (F16 && stored_mprime<F16, EF, ST>()) {
+    // the bucket's inf check ran before this pass: a skipped step writes nothing
+    if (*args.found_inf) return;
+  }
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
     if constexpr (F16)
       f16_check_range(args.ftiles[blockIdx.x - args.ntiles], args.bucket, args.found_inf);
@@ -2191,9 +2238,9 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
   for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[s4][nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
-  for (int rr = r0; rr < r1; rr += 4 * U) {
-    float x[U][4];
-    float p[U][NT];
+  // the operands of the 4U-row step at rr (the next step's are requested before this
+  // step's MFMAs)
+  auto load_step = [&](int rr, float (&x)[U][4], float (&p)[U][NT]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = rr + 4 * u + h;
@@ -2228,6 +2275,8 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) p[u][nt] = Pt[static_cast<int64_t>(rowc) * R + 16 * nt + cl];
     }
+  };
+  auto compute_step = [&](int rr, float (&x)[U][4], float (&p)[U][NT]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool rok = rr + 4 * u + h < r1;
@@ -2242,6 +2291,21 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
       for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[s4][nt] = mfma16(x[u][s4], p[u][nt], acc[s4][nt]);
+  };
+  // two register sets in turn: a step's MFMAs run while the next step's loads are in
+  // flight. On the 16-byte path the loads need no branch (clamped rows) and the
+  // scheduling barriers keep the compiler from moving them next to their use.
+  float xa[U][4], xb[U][4];
+  float pa[U][NT], pb[U][NT];
+  load_step(r0, xa, pa);
+  for (int rr = r0; rr < r1; rr += 8 * U) {
+    if (VEC || rr + 4 * U < r1) load_step(rr + 4 * U, xb, pb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_step(rr, xa, pa);
+    if (rr + 4 * U >= r1) break;
+    if (VEC || rr + 8 * U < r1) load_step(rr + 8 * U, xa, pa);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_step(rr + 4 * U, xb, pb);
   }
   float* Qt = args.Q + d.qoff;
   float* part = args.partial + static_cast<int64_t>(d.pslot + t.b * d.nrb + t.a) * (kColBlock * R);
@@ -2408,6 +2472,7 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
                                                 const Tile& t, int lane, int wave) {
   constexpr bool SM = stored_mprime<F16, EF, ST>();
   constexpr bool LOADX = EF && (!SM || MAT);  // M' is read
+  const bool we = MAT && holds_error(args);  // materialization: E's place holds E
   constexpr int KQ = R / 4;
   constexpr int UR = 2;  // 16-row steps loaded before use
   const int m = d.m;
@@ -2492,7 +2557,7 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
           if constexpr (MAT) {
             float e[4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) e[a] = x[ur][g][a] - mh[a];
+            for (int a = 0; a < 4; ++a) e[a] = we ? x[ur][g][a] : x[ur][g][a] - mh[a];
             store_f32x4(args.Eout + d.eoff + off, VEC, m - col, e);
             continue;
           }
@@ -2534,6 +2599,7 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
                                                 float* tile) {
   constexpr bool SM = stored_mprime<F16, EF, ST>();
   constexpr bool LOADX = EF && (!SM || MAT);  // M' is read
+  const bool we = MAT && holds_error(args);  // materialization: E's place holds E
   constexpr int KQ = R / 4;
   constexpr int UR = 2;         // 16-row MFMA groups per step
   constexpr int SR = 16 * UR;   // rows per step
@@ -2563,6 +2629,22 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
       for (int a = 0; a < 4; ++a) qa[g][4 * k4 + a] = w[a];
     }
   }
+  // P rows of the step at rr (the next step's are requested before this step's MFMAs)
+  auto load_pb = [&](int rr, float (&pb)[UR][KQ]) {
+#pragma unroll
+    for (int ur = 0; ur < UR; ++ur) {
+      const int rowc = min(rr + 16 * ur + cl, r1 - 1);
+#pragma unroll
+      for (int k4 = 0; k4 < KQ / 4; ++k4) {
+        float w[4];
+        load_f4(Pt + static_cast<int64_t>(rowc) * R + h * KQ + 4 * k4, w);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) pb[ur][4 * k4 + a] = w[a];
+      }
+    }
+  };
+  float pb[UR][KQ];
+  load_pb(r0, pb);
   for (int rr = r0; rr < r1; rr += SR) {
     float x[RW][4];
     if constexpr (LOADX) {
@@ -2575,18 +2657,8 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
                                             ST != kStF32 ? args.Mh + d.eoff : nullptr);
       }
     }
-    float pb[UR][KQ];
-#pragma unroll
-    for (int ur = 0; ur < UR; ++ur) {
-      const int rowc = min(rr + 16 * ur + cl, r1 - 1);
-#pragma unroll
-      for (int k4 = 0; k4 < KQ / 4; ++k4) {
-        float w[4];
-        load_f4(Pt + static_cast<int64_t>(rowc) * R + h * KQ + 4 * k4, w);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) pb[ur][4 * k4 + a] = w[a];
-      }
-    }
+    float pbn[UR][KQ];
+    if (rr + SR < r1) load_pb(rr + SR, pbn);
 #pragma unroll
     for (int ur = 0; ur < UR; ++ur) {
 #pragma unroll
@@ -2609,7 +2681,7 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
         if constexpr (MAT) {
           float e[4];
 #pragma unroll
-          for (int a = 0; a < 4; ++a) e[a] = x[i][a] - mh[a];
+          for (int a = 0; a < 4; ++a) e[a] = we ? x[i][a] : x[i][a] - mh[a];
           store_f32x4(args.Eout + d.eoff + off, true, 4, e);
           continue;
         }
@@ -2629,12 +2701,17 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
       }
     }
     __syncthreads();  // the tile is rewritten by the next step
+#pragma unroll
+    for (int ur = 0; ur < UR; ++ur)
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) pb[ur][kq] = pbn[ur][kq];
   }
 }
 
 template <int R, bool F16, bool EF, int ST, bool MAT = false>
 __global__ void __launch_bounds__(kThreads) k_pass3_mfma(Pass3Args args) {
   if (F16 && *args.found_inf) return;
+  mark_mprime<F16, EF, ST, MAT>(args);
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
     if constexpr (MAT)
       return;
@@ -2970,6 +3047,10 @@ __global__ void __launch_bounds__(256)
 
 // ------------------------------------------------------- fp16 pass-through only
 
+__global__ void __launch_bounds__(64) k_set_flag(int32_t* flag, int32_t value) {
+  if (threadIdx.x == 0) *flag = value;
+}
+
 __global__ void __launch_bounds__(256)
     k_f16_check(const FlatTile* __restrict__ ft, const void* bucket, int32_t* found_inf) {
   f16_check_range(ft[blockIdx.x], bucket, found_inf);
@@ -3277,6 +3358,11 @@ hipError_t launch_fill_zero(void* base, bool f16, int64_t start, int64_t count, 
   const int64_t blocks = (count + 255) / 256;
   k_fill_zero<<<dim3(static_cast<unsigned>(blocks < 1024 ? blocks : 1024)), 256, 0, s>>>(
       base, f16 ? 2 : 4, start, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_flag(int32_t* flag, int32_t value, hipStream_t s) {
+  k_set_flag<<<dim3(1), 64, 0, s>>>(flag, value);
   return hipGetLastError();
 }
 

@@ -177,6 +177,52 @@ def test_fp16_nan_and_negative_inf_skip(bad):
     _run_parity(_hp(), shapes, steps=3, dtype="f16", inv_scale=2.0 ** -10, bucket_fn=fn)
 
 
+@pytest.mark.parametrize("rank", [2, 32])
+def test_fp16_skips_on_the_first_call_and_in_a_row(rank):
+    """An fp16 bucket keeps M' in the error memory's place once a step has run; a step
+    skipped for inf must leave every piece of state as it was, including on the very
+    first call (the error memory still holds the error itself) and for two calls in a
+    row. The oracle decides which steps are skipped."""
+    log(f"case: fp16, r={rank}, inf at steps 0, 3 and 4 of 7")
+    shapes = [(96, 160), (40,), (300, 64)]
+    bad_steps = {0, 3, 4}
+
+    def fn(step):
+        b = _rand_bucket(shapes, 90 + step, scale=50.0)
+        if step in bad_steps:
+            b[100 + 7 * step] = float("inf")
+        return b
+    par = _run_parity(_hp(matrix_approximation_rank=rank, min_compression_rate=1.0), shapes,
+                      steps=7, dtype="f16", inv_scale=2.0 ** -10, bucket_fn=fn)
+    assert par.gpu.decisions(0, 3) == [1, 0, 1]
+
+
+def test_fp16_skip_right_after_an_import():
+    """Import puts the error itself back in the error memory's place; a skipped fp16
+    step right after it must leave it there, and the next step continues from it."""
+    log("case: fp16, r=2: 2 steps, export, import into a fresh state, inf, 2 more steps")
+    shapes = [(128, 96), (24,)]
+    views = packed_views(shapes)
+    hp = _hp(min_compression_rate=1.0)
+    par = BucketParity(hp, views, "f16")
+    scale = 2.0 ** -10
+    for step in range(2):
+        par.step(_rand_bucket(shapes, 300 + step, scale=50.0).to(torch.float16), step,
+                 inv_loss_scale=scale)
+    blob = par.gpu.export_state()
+    fresh = PowerSGDState(**hp)
+    fresh.import_state(blob)
+    par.gpu = fresh
+    for step in range(2, 5):
+        b = _rand_bucket(shapes, 300 + step, scale=50.0)
+        if step == 2:
+            b[5] = float("inf")
+        rep = par.step(b.to(torch.float16), step, inv_loss_scale=scale)
+        log(f"  step {step}: " + ", ".join(f"{k}={v:.2e}" for k, v in rep.worst.items())
+            + (" (inf: skipped)" if rep.found_inf else ""))
+        assert rep.found_inf == (step == 2)
+
+
 def test_misaligned_bucket_base_pointer():
     log("case: bucket starts 1 element into an allocation (scalar path)")
     shapes = [(64, 64), (48, 100), (7,)]
