@@ -616,11 +616,17 @@ __device__ void f16_check_range(const FlatTile ft, const void* bucket,
   for (int64_t i = threadIdx.x; i < head; i += blockDim.x)
     bad |= half_bits_not_finite(h[i]) ? 1 : 0;
   const uint4* v = reinterpret_cast<const uint4*>(h + head);
-  for (int64_t i = threadIdx.x; i < nv; i += blockDim.x) {
-    const uint4 w = v[i];
-    bad |= f16_pair_not_finite(w.x) | f16_pair_not_finite(w.y) | f16_pair_not_finite(w.z) |
+  auto check8 = [](const uint4 w) {
+    return f16_pair_not_finite(w.x) | f16_pair_not_finite(w.y) | f16_pair_not_finite(w.z) |
            f16_pair_not_finite(w.w);
+  };
+  const int64_t bd = blockDim.x;
+  int64_t i = threadIdx.x;
+  for (; i + 3 * bd < nv; i += 4 * bd) {  // four loads in flight
+    const uint4 w0 = v[i], w1 = v[i + bd], w2 = v[i + 2 * bd], w3 = v[i + 3 * bd];
+    bad |= check8(w0) | check8(w1) | check8(w2) | check8(w3);
   }
+  for (; i < nv; i += bd) bad |= check8(v[i]);
   for (int64_t i = head + 8 * nv + threadIdx.x; i < ft.len; i += blockDim.x)
     bad |= half_bits_not_finite(h[i]) ? 1 : 0;
   if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(found_inf, 1);
@@ -2079,19 +2085,25 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
   for (int k0 = 0; k0 < m; k0 += kColBlock) {
     const int col = k0 + 4 * lane;
     const bool cok = col < m;
+    if constexpr (SM) {
+      if (rebuild) {
+        // the wavefront's rows of M_hat_prev, all requested before the first is used
+        float4 mh[RW];
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+          mh[i] = *reinterpret_cast<const float4*>(mh_tile + (RW * wave + i) * LS + 4 * lane);
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+          xe[i][0] = xe[i][0] - mh[i].x;
+          xe[i][1] = xe[i][1] - mh[i].y;
+          xe[i][2] = xe[i][2] - mh[i].z;
+          xe[i][3] = xe[i][3] - mh[i].w;
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       float v[4];
-      if constexpr (SM) {
-        if (rebuild) {
-          const float4 mh =
-              *reinterpret_cast<const float4*>(mh_tile + (RW * wave + i) * LS + 4 * lane);
-          xe[i][0] = xe[i][0] - mh.x;
-          xe[i][1] = xe[i][1] - mh.y;
-          xe[i][2] = xe[i][2] - mh.z;
-          xe[i][3] = xe[i][3] - mh.w;
-        }
-      }
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         float x = xg[i][a];
@@ -2671,11 +2683,16 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
       }
     }
     __syncthreads();
+    // the wavefront's rows of the tile, all requested before the first is stored
+    float4 tv[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+      tv[i] = *reinterpret_cast<const float4*>(tile + (RW * wave + i) * LS + 4 * lane);
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       const int row = rr + RW * wave + i;
       if (row < r1 && cr_ok) {
-        const float4 v = *reinterpret_cast<const float4*>(tile + (RW * wave + i) * LS + 4 * lane);
+        const float4 v = tv[i];
         const float mh[4] = {rnd16<ST>(v.x), rnd16<ST>(v.y), rnd16<ST>(v.z), rnd16<ST>(v.w)};
         const int64_t off = static_cast<int64_t>(row) * m + cr;
         if constexpr (MAT) {
