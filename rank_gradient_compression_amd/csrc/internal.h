@@ -278,6 +278,9 @@ constexpr int kGramRows = 256;
 // (matrix-core ranks: a row per thread).
 constexpr int kOrthRows = 1024;
 constexpr int orth_rows(int R) { return R >= kMfmaMinRank ? kThreads : kOrthRows; }
+// Threads of the workgroup that computes one matrix's transform T (a thread per element
+// of the 32 x 32 factor in the recurrence).
+constexpr int kOrthThreads = 1024;
 
 // One n x m matrix as the bucket plan lays out a bucket that holds only that matrix
 // (every buffer offset is 0; compressed without the rate test at rank min(r, n, m)):

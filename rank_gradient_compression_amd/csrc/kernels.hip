@@ -977,6 +977,14 @@ __device__ __forceinline__ DD dd_sqrt(DD a) {
   return dd_fast_two_sum(x, r.hi / (2.0 * x));
 }
 
+// 1 / sqrt(a), a.hi > 0: one Newton step for the reciprocal root from the fp64 value
+// x, y = x + x (1 - a x^2) / 2 (the relative error squares: about 2^-104).
+__device__ __forceinline__ DD dd_rsqrt(DD a) {
+  const double x = 1.0 / sqrt(a.hi);
+  const DD e = dd_add(DD{1.0, 0.0}, dd_neg(dd_mul(a, dd_mul(DD{x, 0.0}, DD{x, 0.0}))));
+  return dd_add_d(DD{x, 0.0}, 0.5 * x * e.hi);
+}
+
 // Lanes that share one Gram entry when the orthogonalization sums the partials: the
 // largest power of two with NG * GS <= 256 threads, at most a wavefront (1 = a thread
 // per entry).
@@ -1089,33 +1097,48 @@ __device__ __forceinline__ void orth_gram_sum(const OrthJob& j, const double* __
 
 // Sums the job's double-double Gram partials (partial p: NG high parts, then NG low
 // parts, at goff + 2 NG p) into sh.Gh / sh.Gl, a thread per entry, partials in order
-// (loaded eight at a time).
+// (several at a time for all the thread's entries at once; NTH threads).
 // Every thread takes part; ends with a barrier.
-template <int R>
+template <int R, int NTH>
 __device__ __forceinline__ void orth_gram_sum_dd(const OrthJob& j, const double* __restrict__ gram,
                                                  OrthShared<R>& sh) {
   constexpr int NG = gram_size<R>();
-  for (int e = threadIdx.x; e < NG; e += blockDim.x) {
-    DD s{0.0, 0.0};
-    const double* src = gram + j.goff + e;
-    for (int p0 = 0; p0 < j.nparts; p0 += 8) {
-      double vh[8], vl[8];  // eight partials in flight, then added in order
+  constexpr int PER = (NG + NTH - 1) / NTH;  // entries per thread
+  constexpr int B = PER == 1 ? 16 : 8;       // partials per entry in flight
+  const int tid = threadIdx.x;
+  DD s[PER];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+  for (int i = 0; i < PER; ++i) s[i] = DD{0.0, 0.0};
+  for (int p0 = 0; p0 < j.nparts; p0 += B) {
+    // B partials of every entry the thread owns in flight, then added in order
+    double vh[PER][B], vl[PER][B];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const double* src = gram + j.goff + min(tid + i * NTH, NG - 1);
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
         const int64_t p = min(p0 + q, j.nparts - 1);
-        vh[q] = src[p * 2 * NG];
-        vl[q] = src[p * 2 * NG + NG];
+        vh[i][q] = src[p * 2 * NG];
+        vl[i][q] = src[p * 2 * NG + NG];
       }
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (p0 + q < j.nparts) s = dd_add(s, DD{vh[q], vl[q]});
     }
-    int a, b;
-    tri_entry(e, R, a, b);
-    sh.Gh[a][b] = s.hi;
-    sh.Gh[b][a] = s.hi;
-    sh.Gl[a][b] = s.lo;
-    sh.Gl[b][a] = s.lo;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+#pragma unroll
+      for (int q = 0; q < B; ++q)
+        if (p0 + q < j.nparts) s[i] = dd_add(s[i], DD{vh[i][q], vl[i][q]});
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + i * NTH;
+    if (e < NG) {
+      int a, b;
+      tri_entry(e, R, a, b);
+      sh.Gh[a][b] = s[i].hi;
+      sh.Gh[b][a] = s[i].hi;
+      sh.Gl[a][b] = s[i].lo;
+      sh.Gl[b][a] = s[i].lo;
+    }
   }
   __syncthreads();
 }
@@ -1201,22 +1224,20 @@ __device__ __forceinline__ void orth_cholesky(int rank, double tau, OrthShared<R
   if (lane == 0 && tau > 0.0) sh.redo = redo;
 }
 
-// The factor of orth_cholesky without the pivot check (tau = 0), with the same
-// operations on every entry in the same order, but each column step spread over the
-// whole workgroup: the lanes of wavefront 0 form row k, then every thread updates
-// entries of the trailing block. Every thread takes part; ends with a barrier.
+// The factor of orth_cholesky without the pivot check (tau = 0), each column step
+// spread over the whole workgroup: the lanes of wavefront 0 form row k (the row times
+// the reciprocal root of the pivot, in double-double), then every thread updates
+// entries of the trailing block (the same operations as orth_cholesky). Every thread
+// takes part; ends with a barrier.
 template <int R>
 __device__ __forceinline__ void orth_cholesky_wg(int rank, OrthShared<R>& sh) {
   const int tid = threadIdx.x;
   for (int k = 0; k < rank; ++k) {
     if (tid >= k && tid < rank) {
+      // C_kj = G_kj / sqrt(G_kk) as G_kj times the reciprocal root (C_kk = G_kk times it)
       const DD d{sh.Gh[k][k], sh.Gl[k][k]};
-      const bool pos = d.hi > 0.0;
       DD c{0.0, 0.0};
-      if (pos) {
-        const DD piv = dd_sqrt(d);
-        c = tid == k ? piv : dd_div(DD{sh.Gh[k][tid], sh.Gl[k][tid]}, piv);
-      }
+      if (d.hi > 0.0) c = dd_mul(DD{sh.Gh[k][tid], sh.Gl[k][tid]}, dd_rsqrt(d));
       sh.Gh[k][tid] = c.hi;
       sh.Gl[k][tid] = c.lo;
     }
@@ -1286,6 +1307,49 @@ __device__ __forceinline__ void orth_from_factor(int rank, double eps, OrthShare
       for (int l = 0; l < R; ++l) sh.T[l][lane] = c[l];
     }
   }
+  __syncthreads();
+}
+
+// The recurrence of orth_from_factor with a thread per element: thread t takes element
+// l = t % R of column j = t / R (R * R threads at least). A column's norm and its dot
+// products are shuffle-tree sums over its R lanes (one aligned group of a wavefront);
+// the normalized column and its coefficients go through LDS, alternating between two
+// buffers, so a step needs one barrier. Writes sh.T; ends with a barrier.
+template <int R>
+__device__ __forceinline__ void orth_from_factor_wg(int rank, double eps, OrthShared<R>& sh,
+                                                    double (*ybuf)[2][R]) {
+  const int tid = threadIdx.x;
+  const int j = tid / R;
+  const int l = tid - j * R;
+  const bool mine = j < R;
+  double y = 0.0, c = 0.0;
+  if (mine) {
+    c = (l == j) ? 1.0 : 0.0;
+    y = (j < rank && l <= j) ? sh.Gh[l][j] : 0.0;
+  }
+  auto group_sum = [](double v) {
+#pragma unroll
+    for (int mask = R / 2; mask >= 1; mask >>= 1) v += __shfl_xor(v, mask);
+    return v;
+  };
+  for (int i = 0; i < rank; ++i) {
+    double(*buf)[R] = ybuf[i & 1];
+    if (j == i) {
+      const double inv = 1.0 / (sqrt(group_sum(y * y)) + eps);
+      y *= inv;
+      c *= inv;
+      buf[0][l] = y;
+      buf[1][l] = c;
+    }
+    __syncthreads();
+    if (mine && j > i && j < rank) {
+      const double yi = buf[0][l];
+      const double coef = group_sum(y * yi);
+      y -= coef * yi;
+      c -= coef * buf[1][l];
+    }
+  }
+  if (mine) sh.T[l][j] = c;
   __syncthreads();
 }
 
@@ -2876,21 +2940,23 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-// The transform T of one job (one workgroup per job): its double-double Gram partials
-// summed, factored, and the recurrence run on the factor. T goes to tmat (R x R fp64
-// per job, job after job).
+// The transform T of one job (one workgroup of kOrthThreads per job): its
+// double-double Gram partials summed, factored, and the recurrence run on the factor.
+// T goes to tmat (R x R fp64 per job, job after job).
 template <int R>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kOrthThreads)
     k_orth_t(const OrthJob* __restrict__ jobs, const double* __restrict__ gram,
              double* __restrict__ tmat, double eps, const int32_t* __restrict__ found_inf) {
+  static_assert(kOrthThreads >= R * R, "a thread per element of the factor");
   if (found_inf != nullptr && *found_inf) return;
   __shared__ OrthShared<R> sh;
+  __shared__ double ybuf[2][2][R];
   const OrthJob j = jobs[blockIdx.x];
-  orth_gram_sum_dd<R>(j, gram, sh);
+  orth_gram_sum_dd<R, kOrthThreads>(j, gram, sh);
   orth_cholesky_wg<R>(j.rank, sh);
-  orth_from_factor<R>(j.rank, eps, sh);
+  orth_from_factor_wg<R>(j.rank, eps, sh, ybuf);
   double* dst = tmat + static_cast<int64_t>(blockIdx.x) * R * R;
-  for (int f = threadIdx.x; f < R * R; f += kThreads) dst[f] = sh.T[f / R][f % R];
+  for (int f = threadIdx.x; f < R * R; f += kOrthThreads) dst[f] = sh.T[f / R][f % R];
 }
 
 // X <- X T in fp64, rounded to fp32 (and to the state's 16 bits), for orth_rows(R) rows
@@ -3305,7 +3371,7 @@ hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, int max_rows, floa
   if (njobs == 0) return hipSuccess;
   const dim3 grid((max_rows + orth_rows(R) - 1) / orth_rows(R), njobs);
   PSGD_RANK_SWITCH(R, {
-    k_orth_t<RR><<<dim3(njobs), kThreads, 0, s>>>(jobs, gram, tmat, eps, found_inf);
+    k_orth_t<RR><<<dim3(njobs), kOrthThreads, 0, s>>>(jobs, gram, tmat, eps, found_inf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (st == kStF16)
