@@ -124,6 +124,7 @@ struct BucketPlan {
   int64_t max_qcount = 0;
   int max_prows = 0, max_qrows = 0;
   int64_t e_floats = 0, p_floats = 0, q_floats = 0, partial_floats = 0, gram_doubles = 0;
+  int64_t ppart_floats = 0;  // matrix-core ranks: pass 1's column-group partials of P
   int64_t qt_floats = 0;
 
   // device memory
@@ -132,6 +133,7 @@ struct BucketPlan {
   uint16_t* Mh = nullptr;  // 16-bit state: M' of the current call
   float* P = nullptr;
   float* Praw = nullptr;  // vector ranks: P as pass 1 writes it (pass 2 orthogonalizes)
+  float* Ppart = nullptr;  // matrix-core ranks: pass 1's column-group partials of P
   float* Q = nullptr;
   float* QT = nullptr;  // matrix-core ranks: Q transposed
   float* partial = nullptr;
@@ -169,12 +171,12 @@ struct BucketPlan {
   bool all_wide = false;
 
   void release() {
-    void* ptrs[] = {E, Eh, Mh, P, Praw, Q, QT, partial, gram, tmat, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
+    void* ptrs[] = {E, Eh, Mh, P, Praw, Ppart, Q, QT, partial, gram, tmat, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
                     d_tiles1, d_tiles2, d_tiles3, d_tiles2r, d_flat_unc, d_flat_all, d_pjobs, d_qjobs,
                     d_qinit, intro_E, intro_PQ, Emat, wflag};
     for (void* p : ptrs)
       if (p) (void)hipFree(p);
-    E = P = Praw = Q = QT = partial = nullptr;
+    E = P = Praw = Ppart = Q = QT = partial = nullptr;
     Eh = Mh = nullptr;
     gram = nullptr;
     tmat = nullptr;
@@ -379,7 +381,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
   const int64_t ng = static_cast<int64_t>(R) * (R + 1) / 2;
   const bool fused_gram = R <= kMaxFusedGramRank;
   int64_t goff = 0;
-  int64_t eoff = 0, poff = 0, qoff = 0, qtoff = 0;
+  int64_t eoff = 0, poff = 0, qoff = 0, qtoff = 0, p1off = 0;
   int32_t pslot = 0;
   for (size_t v = 0; v < nv; ++v) {
     if (!pl.decision[v]) continue;
@@ -404,7 +406,8 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
     }
     const int32_t ti = static_cast<int32_t>(pl.tensors.size());
     // pass 1: whole rows; slots of lprw threads sweep 4 * lprw columns at a time
-    // (matrix-core ranks: 16 rows per wavefront)
+    // (matrix-core ranks: 32-row blocks split into groups of kPass1Cols columns, the
+    // groups of a row block next to each other in the table, each writing a partial P)
     d.lprw = pow2_ceil(static_cast<int>((std::min<int64_t>(d.m, 4 * kThreads) + 3) / 4));
     {
       int64_t rows;
@@ -422,15 +425,25 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
         }
       }
       d.rpb1 = static_cast<int32_t>(rows);
+      d.ncg1 = 1;
+      d.p1off = 0;
+      if (R >= kMfmaMinRank) {
+        d.ncg1 = static_cast<int32_t>((d.m + kPass1Cols - 1) / kPass1Cols);
+        d.p1off = p1off;
+        p1off += round_up(static_cast<int64_t>(d.ncg1) * d.n * R, 64);
+      }
       for (int64_t r0 = 0, rb = 0; r0 < d.n; r0 += rows, ++rb)
-        pl.tiles1.push_back(Tile{ti, static_cast<int32_t>(rb), 0, 0});
+        for (int32_t cg = 0; cg < d.ncg1; ++cg)
+          pl.tiles1.push_back(Tile{ti, static_cast<int32_t>(rb), cg, 0});
     }
     // Gram partials of P: one per pass-1 row block (fused) or per kGramRows rows
     {
       const int32_t rpp = fused_gram ? d.rpb1 : kGramRows;
       const int32_t nparts = static_cast<int32_t>((d.n + rpp - 1) / rpp);
       d.goff = goff;
-      pl.pjobs.push_back(OrthJob{d.poff, goff, -1, d.n, d.rank, nparts, rpp, 0, 0});
+      // matrix-core ranks: the Gram kernel first sums pass 1's column-group partials
+      pl.pjobs.push_back(OrthJob{d.poff, goff, -1, d.n, d.rank, nparts, rpp, 0,
+                                 R >= kMfmaMinRank ? d.ncg1 : 0, d.p1off});
       if (!fused_gram)
         for (int32_t pp = 0; pp < nparts; ++pp)
           pl.pgram_tiles.push_back(Tile{static_cast<int32_t>(pl.pjobs.size() - 1), pp, 0, 0});
@@ -470,7 +483,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
     {
       const int32_t nparts = static_cast<int32_t>((d.m + kGramRows - 1) / kGramRows);
       pl.qjobs.push_back(
-          OrthJob{d.qoff, goff, d.qtoff, d.m, d.rank, nparts, kGramRows, d.mstride, 0});
+          OrthJob{d.qoff, goff, d.qtoff, d.m, d.rank, nparts, kGramRows, d.mstride, 0, 0});
       for (int32_t pp = 0; pp < nparts; ++pp)
         pl.qgram_tiles.push_back(Tile{static_cast<int32_t>(pl.qjobs.size() - 1), pp, 0, 0});
       goff += nparts * ng * 2;  // double-double partials
@@ -487,6 +500,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
   pl.p_floats = poff;
   pl.q_floats = qoff;
   pl.partial_floats = static_cast<int64_t>(pslot) * kColBlock * R;
+  pl.ppart_floats = p1off;
   pl.gram_doubles = goff;
   pl.qt_floats = qtoff;
   return POWERSGD_OK;
@@ -513,6 +527,7 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   ok = ok && alloc(reinterpret_cast<void**>(&pl.Q), pl.q_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.QT), pl.qt_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.partial), pl.partial_floats * sizeof(float));
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.Ppart), pl.ppart_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.gram), pl.gram_doubles * sizeof(double));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.tmat),
                    pl.tensors.size() * static_cast<size_t>(pl.R) * pl.R * sizeof(double));
@@ -683,6 +698,7 @@ powersgd_status matrix_layout(const powersgd_hparams& hp, int64_t n, int64_t m,
   out.q_floats = pl.q_floats;
   out.qt_floats = pl.qt_floats;
   out.partial_floats = pl.partial_floats;
+  out.ppart_floats = pl.ppart_floats;
   out.gram_doubles = pl.gram_doubles;
   return POWERSGD_OK;
 }
@@ -891,7 +907,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
       if (r != POWERSGD_OK) return r;
       r = timed_launch(st, s, K_GRAM, 0.0, "Gram of Q", [&] {
         return launch_gram(R, pl.d_qgram_tiles, static_cast<int>(pl.qgram_tiles.size()),
-                           pl.d_qjobs, pl.Q, pl.gram, nullptr, s);
+                           pl.d_qjobs, pl.Q, nullptr, pl.gram, nullptr, prec, s);
       });
       if (r != POWERSGD_OK) return r;
       r = timed_launch(st, s, K_ORTH, 0.0, "orthogonalize Q", [&] {
@@ -934,6 +950,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.Q = pl.Q;
     a.QT = pl.QT;
     a.P = fused ? pl.Praw : pl.P;
+    a.Ppart = pl.Ppart;
     a.Pe = sm ? pl.P : nullptr;  // the kernels skip the rebuild while wflag is set
     a.wflag = sm ? pl.wflag : nullptr;
     a.gram = pl.gram;
@@ -951,7 +968,8 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     if (!pl.pgram_tiles.empty()) {
       r = timed_launch(st, s, K_GRAM, 0.0, "Gram of P", [&] {
         return launch_gram(R, pl.d_pgram_tiles, static_cast<int>(pl.pgram_tiles.size()),
-                           pl.d_pjobs, pl.P, pl.gram, f16 ? found_inf_dev : nullptr, s);
+                           pl.d_pjobs, pl.P, pl.Ppart, pl.gram, f16 ? found_inf_dev : nullptr,
+                           prec, s);
       });
       if (r != POWERSGD_OK) return r;
     }

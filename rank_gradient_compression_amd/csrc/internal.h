@@ -45,6 +45,8 @@ struct TensorDesc {
   int32_t nrb;    // pass 2/3: row blocks
   int32_t ncb;    // pass 2/3: 256-column blocks
   int32_t pslot;  // first pass-2 partial slot (nrb * ncb slots when nrb > 1)
+  int32_t ncg1;   // matrix-core ranks: pass-1 column groups of kPass1Cols columns
+  int64_t p1off;  // matrix-core ranks: first float of its pass-1 partial P (ncg1 x n x R)
 };
 
 // Work item of the streaming passes: row block `a` (and column block `b` in
@@ -74,7 +76,9 @@ struct OrthJob {
   int32_t nparts;
   int32_t rpp;
   int32_t tstride;
-  int32_t pad;
+  int32_t ncg;      // > 0: the rows are the sum of ncg partials at part (group-major,
+                    // rows x R each), which the Gram kernel adds and writes to off
+  int64_t part;
 };
 
 // Packed upper-triangle index of Gram entry (i, j), i <= j < R.
@@ -102,6 +106,9 @@ struct Pass1Args {
   float* E;
   const float* Q;
   float* P;
+  // matrix-core ranks: P of each (row block, column group) work item, a partial sum
+  // over the group's columns, at p1off + (group * n + row) * R
+  float* Ppart;
   // fp32 buckets with error feedback keep M' of the previous step in E's place; its error
   // is rebuilt as E = M'_prev - Pe Q^T with Pe the previous orthogonalized P (Q being the
   // warm-start Q). Null when E's place holds the error itself (first call, after an
@@ -193,9 +200,12 @@ hipError_t launch_pass3(int R, bool f16, bool ef, int st, const Pass3Args& a, hi
 hipError_t launch_error_materialize(int R, const Pass3Args& a, hipStream_t s);
 // *flag = value (one thread; no memset node, so it can sit in a captured graph).
 hipError_t launch_set_flag(int32_t* flag, int32_t value, hipStream_t s);
+// Double-double Gram partials of each job's rows (one work item per kGramRows rows).
+// Jobs with ncg > 0 first form their rows as the sum of the pass-1 partials at part
+// (in group order, rounded to the state's precision st) and write them to base.
 hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs,
-                       const float* base, double* gram, const int32_t* found_inf,
-                       hipStream_t s);
+                       float* base, const float* part, double* gram,
+                       const int32_t* found_inf, int st, hipStream_t s);
 // Gram-Schmidt of each job's block from its double-double Gram partials: the r x r
 // transforms (tmat: R x R fp64 per job) in one launch, then X <- X T.
 hipError_t launch_orth(int R, const OrthJob* jobs, int njobs, int max_rows, float* base,
@@ -262,6 +272,10 @@ constexpr int kMaxFusedGramRank = 8;
 // pass 2 and pass 3 tiles are kMfmaRowBlock rows x 256 columns (64 per wavefront).
 constexpr int kMfmaMinRank = 16;
 constexpr int kMfmaPass1Rows = 32;
+// Matrix-core pass 1 splits rows into groups of this many columns (the work items of a
+// row block run side by side, so the running workgroups read neighbouring rows); each
+// writes a partial P, summed in the Gram kernel.
+constexpr int kPass1Cols = 2048;
 constexpr int kMfmaRowBlock = 1024;
 // Threads per workgroup of the pass-2 partial reduction.
 constexpr int kReduceThreads = 1024;
@@ -293,7 +307,7 @@ struct MatrixLayout {
   QInitJob qinit;
   int32_t ntiles1, ntiles2, ntiles3, ntiles2r, npgram, nqgram;
   int32_t nrb3;                               // pass-3 row blocks
-  int64_t p_floats, q_floats, qt_floats, partial_floats, gram_doubles;
+  int64_t p_floats, q_floats, qt_floats, partial_floats, gram_doubles, ppart_floats;
 };
 powersgd_status matrix_layout(const powersgd_hparams& hp, int64_t n, int64_t m,
                               MatrixLayout& out);

@@ -1855,6 +1855,9 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
   const int r1 = min(min(d.n, t.a * d.rpb1 + d.rpb1), r0 + 16);
   const int h = lane >> 4;
   const int cl = lane & 15;
+  // the work item's column group: columns c0 .. c1 - 1 (its P is a partial sum)
+  const int c0 = t.b * kPass1Cols;
+  const int c1 = min(m, c0 + kPass1Cols);
   const int row = r0 + cl;
   const bool row_ok = row < r1;
   const int rowc = min(row, r1 - 1);
@@ -1882,7 +1885,7 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f4{0.f, 0.f, 0.f, 0.f};
   int bad = 0;
-  for (int k0 = 64 * wave; k0 < m; k0 += 256) {
+  for (int k0 = c0 + 64 * wave; k0 < c1; k0 += 256) {
     float x[U][4];
     float e[U][4];
     float b[U][NT][4];
@@ -2005,7 +2008,7 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
         const int prow = r0 + 4 * h + v;
         const int k = 16 * nt + cl;
         if (prow < r1)
-          args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? rnd16<ST>(sum) : 0.f;
+          args.Ppart[d.p1off + (static_cast<int64_t>(t.b) * d.n + prow) * R + k] = (k < d.rank) ? sum : 0.f;
       }
     }
   }
@@ -2035,6 +2038,9 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
   const int r1 = min(d.n, r0 + d.rpb1);
   const int h = lane >> 4;
   const int cl = lane & 15;
+  // the work item's column group: columns c0 .. c1 - 1 (its P is a partial sum)
+  const int c0 = t.b * kPass1Cols;
+  const int c1 = min(m, c0 + kPass1Cols);
   float* __restrict__ Et = args.E + d.eoff;
   const float* __restrict__ QTt = args.QT + d.qtoff;
   constexpr bool SM = stored_mprime<F16, EF, ST>();
@@ -2097,7 +2103,7 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
     }
   };
   float b[4][NT][4];
-  load_b(0, b);
+  load_b(c0, b);
   if constexpr (SM) {
     if (rebuild) {
 #pragma unroll
@@ -2145,8 +2151,8 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
         load_f4(Et + rbase[i] + colc, xe[i]);
     }
   };
-  load_rows(0);
-  for (int k0 = 0; k0 < m; k0 += kColBlock) {
+  load_rows(c0);
+  for (int k0 = c0; k0 < c1; k0 += kColBlock) {
     const int col = k0 + 4 * lane;
     const bool cok = col < m;
     if constexpr (SM) {
@@ -2187,7 +2193,7 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
       *reinterpret_cast<float4*>(tile + (RW * wave + i) * LS + 4 * lane) =
           make_float4(v[0], v[1], v[2], v[3]);
     }
-    if (k0 + kColBlock < m) load_rows(k0 + kColBlock);
+    if (k0 + kColBlock < c1) load_rows(k0 + kColBlock);
     // the next chunk's Q^T fragments (clamped in bounds after the last chunk)
     float bn[4][NT][4];
     load_b(k0 + kColBlock, bn);
@@ -2215,7 +2221,7 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
     if constexpr (SM) {
       // the next chunk's M_hat_prev: this chunk's row phase read mh_tile before the
       // barrier above
-      if (rebuild && k0 + kColBlock < m) rebuild_chunk(bn);
+      if (rebuild && k0 + kColBlock < c1) rebuild_chunk(bn);
     }
     __syncthreads();  // the tiles are rewritten by the next chunk
 #pragma unroll
@@ -2249,7 +2255,7 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
       const int prow = r0 + 16 * mt + 4 * h + v;
       const int k = 16 * nt + cl;
       if (prow < r1)
-        args.P[d.poff + static_cast<int64_t>(prow) * R + k] = (k < d.rank) ? rnd16<ST>(sum) : 0.f;
+        args.Ppart[d.p1off + (static_cast<int64_t>(t.b) * d.n + prow) * R + k] = (k < d.rank) ? sum : 0.f;
     }
   }
 }
@@ -2816,7 +2822,9 @@ __global__ void __launch_bounds__(kThreads) k_pass3_mfma(Pass3Args args) {
 // ------------------------------------------------------------ orthogonalization
 
 // Gram partials of one row chunk of a job, staged through LDS, as double-double sums
-// of the exact products: partial p holds NG high parts, then NG low parts.
+// of the exact products: partial p holds NG high parts, then NG low parts. A job whose
+// rows are pass 1's column-group partials sums them first (in group order, rounded to
+// the state's precision) and writes the result as its rows.
 // Matrix-core ranks: a thread owns a 4 x 4 block of entries (column groups ga <= gb)
 // and one of S row phases (rows ph, ph + S, ...), adding each exact product to a
 // binary64 sum with TwoSum and the rounding errors to a second sum (Ogita, Rump and
@@ -2847,11 +2855,11 @@ __device__ __forceinline__ void gram_block_of(int blk, int nb, int& ga, int& gb)
   gb = ga + rem;
 }
 
-template <int R>
+template <int R, int ST>
 __global__ void __launch_bounds__(kThreads)
     k_gram(const Tile* __restrict__ tiles, const OrthJob* __restrict__ jobs,
-           const float* __restrict__ base, double* __restrict__ gram,
-           const int32_t* __restrict__ found_inf) {
+           float* __restrict__ base, const float* __restrict__ part,
+           double* __restrict__ gram, const int32_t* __restrict__ found_inf) {
   if (found_inf != nullptr && *found_inf) return;
   constexpr int NG = gram_size<R>();
   __shared__ __align__(16) float xs[gram_lds_floats<R>()];
@@ -2859,7 +2867,7 @@ __global__ void __launch_bounds__(kThreads)
   const OrthJob j = jobs[t.tensor];
   const int r0 = t.a * j.rpp;
   const int nr = min(j.rpp, j.rows - r0);
-  const float* X = base + j.off + static_cast<int64_t>(r0) * R;
+  float* X = base + j.off + static_cast<int64_t>(r0) * R;
   double* out = gram + j.goff + static_cast<int64_t>(t.a) * 2 * NG;
   const int tid = threadIdx.x;
   if constexpr (R >= kMfmaMinRank) {
@@ -2867,9 +2875,28 @@ __global__ void __launch_bounds__(kThreads)
     constexpr int NBLK = gram_blocks<R>();
     constexpr int S = kThreads / NBLK;
     static_assert(S >= 1, "a row phase per block at least");
-    // rows are 16-byte aligned (R and the job offset are multiples of 4)
-    for (int f = tid; f < nr * R / 4; f += kThreads)
-      *reinterpret_cast<float4*>(xs + 4 * f) = *reinterpret_cast<const float4*>(X + 4 * f);
+    // rows are 16-byte aligned (R and the job offsets are multiples of 4)
+    if (j.ncg > 0) {
+      // P = the sum of the pass-1 partials, group after group, rounded once
+      const float* src = part + j.part + static_cast<int64_t>(r0) * R;
+      const int64_t gstride = static_cast<int64_t>(j.rows) * R;
+      for (int f = tid; f < nr * R / 4; f += kThreads) {
+        float4 v = *reinterpret_cast<const float4*>(src + 4 * f);
+        for (int g = 1; g < j.ncg; ++g) {
+          const float4 w = *reinterpret_cast<const float4*>(src + g * gstride + 4 * f);
+          v.x += w.x;
+          v.y += w.y;
+          v.z += w.z;
+          v.w += w.w;
+        }
+        v = make_float4(rnd16<ST>(v.x), rnd16<ST>(v.y), rnd16<ST>(v.z), rnd16<ST>(v.w));
+        *reinterpret_cast<float4*>(X + 4 * f) = v;
+        *reinterpret_cast<float4*>(xs + 4 * f) = v;
+      }
+    } else {
+      for (int f = tid; f < nr * R / 4; f += kThreads)
+        *reinterpret_cast<float4*>(xs + 4 * f) = *reinterpret_cast<const float4*>(X + 4 * f);
+    }
     __syncthreads();
     const int blk = tid / S;
     const int ph = tid - blk * S;
@@ -3356,11 +3383,16 @@ hipError_t launch_error_materialize(int R, const Pass3Args& a, hipStream_t s) {
 }
 
 hipError_t launch_gram(int R, const Tile* tiles, int ntiles, const OrthJob* jobs,
-                       const float* base, double* gram, const int32_t* found_inf,
-                       hipStream_t s) {
+                       float* base, const float* part, double* gram,
+                       const int32_t* found_inf, int st, hipStream_t s) {
   if (ntiles == 0) return hipSuccess;
   PSGD_RANK_SWITCH(R, {
-    k_gram<RR><<<dim3(ntiles), kThreads, 0, s>>>(tiles, jobs, base, gram, found_inf);
+    if (st == kStF16)
+      k_gram<RR, kStF16><<<dim3(ntiles), kThreads, 0, s>>>(tiles, jobs, base, part, gram, found_inf);
+    else if (st == kStBF16)
+      k_gram<RR, kStBF16><<<dim3(ntiles), kThreads, 0, s>>>(tiles, jobs, base, part, gram, found_inf);
+    else
+      k_gram<RR, kStF32><<<dim3(ntiles), kThreads, 0, s>>>(tiles, jobs, base, part, gram, found_inf);
     return hipGetLastError();
   })
 }

@@ -51,7 +51,7 @@ struct Carve {
   OrthJob* qjob;
   QInitJob* qinit;
   Tile *tiles1, *tiles2, *tiles3, *tiles2r, *pgram, *qgram;
-  float *P, *Praw, *Q, *QT, *partial;
+  float *P, *Praw, *Ppart, *Q, *QT, *partial;
   double *gram, *tmat;
   size_t bytes;
 };
@@ -77,6 +77,7 @@ Carve carve(unsigned char* base, const MatrixLayout& L) {
   c.P = reinterpret_cast<float*>(take(sizeof(float) * L.p_floats));
   c.Praw = reinterpret_cast<float*>(
       take(L.R <= kMaxFusedGramRank ? sizeof(float) * L.p_floats : 0));
+  c.Ppart = reinterpret_cast<float*>(take(sizeof(float) * L.ppart_floats));
   c.Q = reinterpret_cast<float*>(take(sizeof(float) * L.q_floats));
   c.QT = reinterpret_cast<float*>(take(sizeof(float) * L.qt_floats));
   c.partial = reinterpret_cast<float*>(take(sizeof(float) * L.partial_floats));
@@ -109,8 +110,9 @@ __global__ void __launch_bounds__(256) k_noalloc_setup(SetupArgs a) {
     *a.c.qinit = a.qinit;
   }
   const int32_t nrb = a.d.nrb;
+  const int32_t ncg1 = a.d.ncg1;  // pass 1: the column groups of a row block in a row
   for (int64_t i = i0; i < a.ntiles1; i += stride)
-    a.c.tiles1[i] = Tile{0, static_cast<int32_t>(i), 0, 0};
+    a.c.tiles1[i] = Tile{0, static_cast<int32_t>(i / ncg1), static_cast<int32_t>(i % ncg1), 0};
   for (int64_t i = i0; i < a.ntiles2; i += stride)
     a.c.tiles2[i] = Tile{0, static_cast<int32_t>(i % nrb), static_cast<int32_t>(i / nrb), 0};
   for (int64_t i = i0; i < a.ntiles3; i += stride)
@@ -236,7 +238,7 @@ extern "C" POWERSGD_API powersgd_status powersgd_compress_matrix_noalloc(
     if (!check(launch_qinit(R, c.qinit, 1, static_cast<int64_t>(L.d.m) * r, c.Q,
                             hp->random_seed, static_cast<uint64_t>(bucket_index), epoch,
                             kStF32, s), "q_init launch") ||
-        !check(launch_gram(R, c.qgram, L.nqgram, c.qjob, c.Q, c.gram, nullptr, s),
+        !check(launch_gram(R, c.qgram, L.nqgram, c.qjob, c.Q, nullptr, c.gram, nullptr, kStF32, s),
                "Gram of Q launch") ||
         !check(launch_orth(R, c.qjob, 1, L.d.m, c.Q, c.QT, c.gram, c.tmat, eps, nullptr,
                            kStF32, s), "orthogonalize Q launch"))
@@ -252,12 +254,13 @@ extern "C" POWERSGD_API powersgd_status powersgd_compress_matrix_noalloc(
     a.Q = c.Q;
     a.QT = c.QT;
     a.P = fused ? c.Praw : c.P;
+    a.Ppart = c.Ppart;
     a.gram = c.gram;
     a.inv_scale = 1.0f;
     if (!check(launch_pass1(R, false, ef, kStF32, a, s), "pass 1 launch")) return POWERSGD_ERR_HIP;
   }
   if (!fused) {
-    if (!check(launch_gram(R, c.pgram, L.npgram, c.pjob, c.P, c.gram, nullptr, s),
+    if (!check(launch_gram(R, c.pgram, L.npgram, c.pjob, c.P, c.Ppart, c.gram, nullptr, kStF32, s),
                "Gram of P launch") ||
         !check(launch_orth(R, c.pjob, 1, L.d.n, c.P, nullptr, c.gram, c.tmat, eps, nullptr,
                            kStF32, s), "orthogonalize P launch"))
