@@ -2374,20 +2374,32 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[s4][nt] = mfma16(x[u][s4], p[u][nt], acc[s4][nt]);
   };
-  // two register sets in turn: a step's MFMAs run while the next step's loads are in
-  // flight. On the 16-byte path the loads need no branch (clamped rows) and the
-  // scheduling barriers keep the compiler from moving them next to their use.
-  float xa[U][4], xb[U][4];
-  float pa[U][NT], pb[U][NT];
-  load_step(r0, xa, pa);
-  for (int rr = r0; rr < r1; rr += 8 * U) {
-    if (VEC || rr + 4 * U < r1) load_step(rr + 4 * U, xb, pb);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_step(rr, xa, pa);
-    if (rr + 4 * U >= r1) break;
-    if (VEC || rr + 8 * U < r1) load_step(rr + 8 * U, xa, pa);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_step(rr + 4 * U, xb, pb);
+  if constexpr (ST == kStF32) {
+    // two register sets in turn: a step's MFMAs run while the next step's loads are in
+    // flight. On the 16-byte path the loads need no branch (clamped rows) and the
+    // scheduling barriers keep the compiler from moving them next to their use.
+    // Steps go in pairs; a pair's second step past the last row is masked to zero (its
+    // loads are clamped), so the loop has no exit between the two halves.
+    float xa[U][4], xb[U][4];
+    float pa[U][NT], pb[U][NT];
+    load_step(r0, xa, pa);
+    for (int rr = r0; rr < r1; rr += 8 * U) {
+      if (VEC || rr + 4 * U < r1) load_step(rr + 4 * U, xb, pb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_step(rr, xa, pa);
+      if (VEC || rr + 8 * U < r1) load_step(rr + 8 * U, xa, pa);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_step(rr + 4 * U, xb, pb);
+    }
+  } else {
+    // a 16-bit state's rows without 16-byte alignment: one register set, so the kernel
+    // that also holds the 16-bit body keeps its occupancy
+    for (int rr = r0; rr < r1; rr += 4 * U) {
+      float x[U][4];
+      float p[U][NT];
+      load_step(rr, x, p);
+      compute_step(rr, x, p);
+    }
   }
   float* Qt = args.Q + d.qoff;
   float* part = args.partial + static_cast<int64_t>(d.pslot + t.b * d.nrb + t.a) * (kColBlock * R);
@@ -2538,11 +2550,13 @@ __global__ void __launch_bounds__(kThreads) k_pass2_mfma(Pass2Args args) {
       pass2_mfma16_rows<R, ST>(args, d, t, lane, wave);
       return;
     }
+  } else {
+    if (d.vec) {
+      pass2_mfma_body<R, F16, EF, true, ST>(args, d, t, lane, wave);
+      return;
+    }
   }
-  if (d.vec)
-    pass2_mfma_body<R, F16, EF, true, ST>(args, d, t, lane, wave);
-  else
-    pass2_mfma_body<R, F16, EF, false, ST>(args, d, t, lane, wave);
+  pass2_mfma_body<R, F16, EF, false, ST>(args, d, t, lane, wave);
 }
 
 // Pass 3, M_hat = P Q^T and E = M' - M_hat, computed as (Q P^T)^T so that lane l
