@@ -2,7 +2,8 @@
 blocks, a partial fifth block (1100 columns), rows that are not 16-byte multiples
 (1030 and 4099 columns: unaligned access), several row blocks per matrix, every
 vector rank, fp32, fp16 AMP and the 16-bit wrapped state (checked step by step from
-the oracle's state), and a bucket that starts one element into its allocation."""
+the oracle's state), the matrix-core ranks' column groups, and a bucket that starts
+one element into its allocation."""
 import numpy as np
 import pytest
 import torch
@@ -80,15 +81,35 @@ def test_wide_wrapped_stepwise(dt, rank, shapes):
             + f" (tol {tol:.1e})")
 
 
-def test_wide_misaligned_bucket():
-    log("case: wide matrices, bucket one element into its allocation, rank 4")
-    views = packed_views(WIDE)
-    hp = dict(matrix_approximation_rank=4, start_powerSGD_iter=0, min_compression_rate=2.0,
+# Matrix-core ranks split each 32-row block into groups of 2048 columns whose partial P
+# are summed in the Gram kernel: two and three groups with a short last one (2052,
+# 4608, 2060 columns), rows that are not 16-byte multiples (4099 and 6150 columns: the
+# scalar-access body, also split into groups), several row blocks with a ragged tail.
+MC_WIDE = [(77, 4608), (64,), (40, 2052), (96, 4099), (9,), (300, 6150), (2100, 2060)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("rank", [16, 32])
+def test_wide_matrix_cores(rank, dtype):
+    from test_gpu_edge import _hp as edge_hp, _rand_bucket, _run_parity
+    log(f"case: matrix cores, rank {rank}, {dtype}, rows of up to 6150 columns, 3 steps")
+    scale = 50.0 if dtype == "f16" else 1.0
+    _run_parity(edge_hp(matrix_approximation_rank=rank, min_compression_rate=1.0,
+                        orthogonalization_epsilon=1e-8), MC_WIDE, steps=3, dtype=dtype,
+                inv_scale=2.0 ** -10 if dtype == "f16" else 1.0,
+                bucket_fn=lambda t: _rand_bucket(MC_WIDE, 500 + t, scale))
+
+
+@pytest.mark.parametrize("rank,shapes", [(4, WIDE), (32, MC_WIDE)], ids=["r4", "r32"])
+def test_wide_misaligned_bucket(rank, shapes):
+    log(f"case: wide matrices, bucket one element into its allocation, rank {rank}")
+    views = packed_views(shapes)
+    hp = dict(matrix_approximation_rank=rank, start_powerSGD_iter=0, min_compression_rate=2.0,
               use_error_feedback=True, warm_start=True, orthogonalization_epsilon=0.0,
               random_seed=5, compression_stats_logging_frequency=0)
     st = PowerSGDState(**hp)
     orc = oracle.OracleState(oracle.HParams(**hp))
-    numel = views[-1][0] + 33 * 4099
+    numel = views[-1][0] + int(np.prod(shapes[-1]))
     for step in range(3):
         g = torch.Generator().manual_seed(200 + step)
         b = torch.randn(numel, generator=g)
