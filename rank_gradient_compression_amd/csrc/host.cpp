@@ -464,6 +464,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
     // work items are larger (fewer of them pay that prologue) and its rows fit in LDS
     int64_t rpb = row_block(fused_gram ? std::min<int64_t>(1 << 16, target * PSGD_PASS2_TILE_SCALE)
                                        : target);
+    if (R >= kMfmaMinRank) rpb = std::min<int64_t>(kMfmaPass2Rows, round_up(d.n, 16));
     if (fused_gram) rpb = std::min<int64_t>(rpb, kPass2StageFloats / R);
     d.rpb = static_cast<int32_t>(rpb);
     d.nrb = static_cast<int32_t>((d.n + rpb - 1) / rpb);

@@ -269,7 +269,8 @@ constexpr int kMaxFusedGramRank = 8;
 // Padded ranks from this value up run the three passes on matrix cores
 // (v_mfma_f32_16x16x4f32): pass-1 row blocks are 32 rows, two MFMA row groups of 16
 // (the four wavefronts split the columns, and each Q^T fragment serves both groups),
-// pass 2 and pass 3 tiles are kMfmaRowBlock rows x 256 columns (64 per wavefront).
+// pass 2 tiles are kMfmaPass2Rows and pass 3 tiles kMfmaRowBlock rows x 256 columns
+// (64 per wavefront).
 constexpr int kMfmaMinRank = 16;
 constexpr int kMfmaPass1Rows = 32;
 // Matrix-core pass 1 splits rows into groups of this many columns (the work items of a
@@ -277,6 +278,9 @@ constexpr int kMfmaPass1Rows = 32;
 // writes a partial P, summed in the Gram kernel.
 constexpr int kPass1Cols = 2048;
 constexpr int kMfmaRowBlock = 1024;
+// Matrix-core pass 2 row blocks: twice the pass-3 ones, half the Q partial slots to
+// write and to sum.
+constexpr int kMfmaPass2Rows = 2048;
 // Threads per workgroup of the pass-2 partial reduction.
 constexpr int kReduceThreads = 1024;
 // Vector ranks: floats of orthogonalized P rows a pass-2 workgroup keeps in LDS (the
