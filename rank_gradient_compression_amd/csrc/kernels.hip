@@ -10,16 +10,19 @@
 //   Streaming passes share one tiling: (row block x 256-column block) work items;
 //   a lane owns 4 consecutive columns (16-byte accesses) and keeps several rows of
 //   loads in flight; narrow matrices pack several rows into one wavefront.
-//   error memory  an fp32 bucket with error feedback keeps, in E's place, M' of the
-//           previous step instead of E = M' - M_hat: with the step's P and Q (which
-//           the state keeps anyway) the error is rebuilt exactly, as E = M'_prev -
-//           P Q^T with the very arithmetic pass 3 uses for M_hat. Pass 3 then only
-//           writes M_hat (4 bytes per element instead of 12). fp16 buckets, whose
-//           step may be skipped after pass 1 has run, and 16-bit states keep E.
-//   pass 1  M' = G (+ E); fp32: E rebuilt from M'_prev, and M' written over it;
-//           P = M' Q. A workgroup owns whole rows, so each dot product is finished
-//           inside it (shuffles, then LDS across wavefronts). fp16: x * inv_scale and
-//           an OR of "not finite" into found_inf.
+//   error memory  with error feedback and an fp32 state (fp32 or fp16 buckets), E's
+//           place keeps M' of the previous step instead of E = M' - M_hat: with the
+//           step's P and Q (which the state keeps anyway) the error is rebuilt exactly,
+//           as E = M'_prev - P Q^T with the very arithmetic pass 3 uses for M_hat. Pass
+//           3 then only writes M_hat. A device flag says when E's place still holds
+//           the error itself; fp16 buckets check the whole bucket for inf first, so a
+//           skipped step writes nothing. 16-bit states keep E.
+//   pass 1  M' = G (+ E), the error rebuilt from M'_prev and M' written over it;
+//           P = M' Q. Vector ranks: a workgroup owns whole rows, so each dot product is
+//           finished inside it (shuffles, then LDS across wavefronts); matrix-core
+//           ranks: 32 rows x 2048 columns per workgroup, a partial P per column group,
+//           summed by the Gram kernel. fp16: x * inv_scale (and an OR of "not finite"
+//           into found_inf when no check ran before).
 //   orth    Gram-Schmidt with epsilon on P (and on the initial Q draw), run on the
 //           columns of the Cholesky factor of P^T P (see the orthogonalization
 //           section); ranks <= 8 do this in the prologue of every pass-2 workgroup
@@ -31,8 +34,8 @@
 //           pass-3 workgroups of that column block (vector ranks) or by a small
 //           kernel of its own (matrix-core ranks): deterministic, no atomics, no
 //           inter-workgroup fences (the kernel boundary publishes the partials).
-//   pass 3  M_hat = P Q^T written into the bucket (fp16: round to nearest even); fp16
-//           and 16-bit states also E = M' - M_hat.
+//   pass 3  M_hat = P Q^T written into the bucket (fp16: round to nearest even);
+//           16-bit states, which keep the error itself, also E = M' - M_hat.
 //   q_init  Philox4x64-10 + Box-Muller draw of the initial Q (counter layout in
 //           the public header's companion documentation).
 #include <hip/hip_fp16.h>
@@ -1836,9 +1839,10 @@ __device__ __forceinline__ mfma_f4 mfma16(float a, float b, mfma_f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Pass 1, P = M' Q: a workgroup owns 16 rows. Wavefront w takes the 64-column chunks
-// w, w + 4, w + 8, ... (U = 4 K-steps of 16 columns each), so in every round the
-// workgroup reads a contiguous 1 KB of each of its rows; lane group h loads columns
+// Pass 1, P = M' Q, for rows that are not 16-byte aligned (or a bucket that is not): the
+// 16-row group grp of the work item's rows, over its column group. Wavefront w takes
+// the 64-column chunks w, w + 4, w + 8, ... of the group (U = 4 K-steps of 16 columns
+// each), so in every round the workgroup reads a contiguous 1 KB of each of its rows; lane group h loads columns
 // 4h..4h+3 of a K-step (one 16-byte load per four MFMA K-steps) and the matching 16
 // bytes of Q^T rows 16nt + cl. The wavefronts' partial P are added in wavefront
 // order through LDS at the end (red: 4 x NT x 4 x 64 floats). VEC: rows are 16-byte
