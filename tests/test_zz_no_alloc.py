@@ -44,6 +44,9 @@ def _same(name, a, b):
     (4, 0.0, [(700, 900), (300, 130)]),
     (3, 1e-8, [(513, 257), (64, 200)]),
     (32, 1e-8, [(1024, 600), (256, 300)]),
+    # matrix-core column groups: three (4616 columns), then two on rows that are not
+    # 16-byte multiples (2051 columns)
+    (32, 0.0, [(200, 4616), (96, 2051)]),
 ])
 def test_noalloc_matches_the_allocating_entry_point(rank, eps, shapes):
     hp = _hp(rank, eps)
