@@ -2900,12 +2900,20 @@ __global__ void __launch_bounds__(kThreads)
       const int64_t gstride = static_cast<int64_t>(j.rows) * R;
       for (int f = tid; f < nr * R / 4; f += kThreads) {
         float4 v = *reinterpret_cast<const float4*>(src + 4 * f);
-        for (int g = 1; g < j.ncg; ++g) {
-          const float4 w = *reinterpret_cast<const float4*>(src + g * gstride + 4 * f);
-          v.x += w.x;
-          v.y += w.y;
-          v.z += w.z;
-          v.w += w.w;
+        for (int g0 = 1; g0 < j.ncg; g0 += 8) {
+          float4 w[8];  // eight groups' partials in flight, then added in group order
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            w[i] = *reinterpret_cast<const float4*>(src + min(g0 + i, j.ncg - 1) * gstride + 4 * f);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if (g0 + i < j.ncg) {
+              v.x += w[i].x;
+              v.y += w[i].y;
+              v.z += w[i].z;
+              v.w += w[i].w;
+            }
+          }
         }
         v = make_float4(rnd16<ST>(v.x), rnd16<ST>(v.y), rnd16<ST>(v.z), rnd16<ST>(v.w));
         *reinterpret_cast<float4*>(X + 4 * f) = v;
