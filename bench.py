@@ -308,14 +308,16 @@ def algorithmic_bytes(cfg, comp_elems: int, per_elt_f32: float = 28.0):
 
 
 def moved_bytes(cfg, comp_elems: int):
-    """Bytes the library actually moves per step: with error feedback and an fp32 state
-    the error memory's place keeps M' and the error is rebuilt from it, so pass 3 only
-    writes M_hat. fp32 buckets: 12 + 4 + 4 per compressed element; fp16 buckets: the
-    inf check of the whole bucket first (2 per element), then 10 + 4 + 2, and the
-    unscale of the uncompressed views (2 + 2). The other variants move their
-    algorithmic bytes."""
+    """Bytes the library actually moves per step: with error feedback the error memory's
+    place keeps M' and the error is rebuilt from it, so pass 3 only writes M_hat. fp32
+    buckets: 12 + 4 + 4 per compressed element; fp16 buckets: the inf check of the whole
+    bucket first (2 per element), then 10 + 4 + 2, and the unscale of the uncompressed
+    views (2 + 2); the wrapped hook (16-bit M'): 8 + 2 + 4 and the cast of the
+    uncompressed views (4 + 4). Without error feedback: the algorithmic bytes."""
     ef = bool(cfg.hparams.get("use_error_feedback", True))
-    if not cfg.wrap and ef:
+    if cfg.wrap and ef:
+        return comp_elems * 14 + (cfg.numel - comp_elems) * 8
+    if ef:
         if cfg.dtype == "f32":
             return comp_elems * 20
         unc = 0 if cfg.batched else cfg.numel - comp_elems

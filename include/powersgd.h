@@ -162,8 +162,10 @@ POWERSGD_API powersgd_status powersgd_compress_bucket(powersgd_state* st, int64_
  * nearest even where it is formed: the cast gradient, M' = G + E, P = M'Q, P after
  * Gram-Schmidt, Q = M'^T P, M_hat = P Q^T and E = M' - M_hat (also the initial draw of
  * Q, cast from its binary32 value); sums and products accumulate in fp32 (the
- * Gram-Schmidt recurrence in fp64). The bucket's error memory E and the M' of a call
- * are 16-bit arrays; the warm-start Q holds 16-bit values.
+ * Gram-Schmidt recurrence in fp64). The bucket's error memory is a 16-bit array; with
+ * error feedback it keeps M' of the latest call, from which the next call rebuilds E =
+ * M' - M_hat with the same roundings (without, M' has a 16-bit array of its own); the
+ * warm-start Q holds 16-bit values.
  *
  *   bucket         device pointer to numel fp32 gradients, caller-owned; compressed
  *                  views receive M_hat, uncompressed views their 16-bit cast (both as

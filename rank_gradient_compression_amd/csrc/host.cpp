@@ -129,8 +129,8 @@ struct BucketPlan {
 
   // device memory
   float* E = nullptr;
-  uint16_t* Eh = nullptr;  // 16-bit state: E
-  uint16_t* Mh = nullptr;  // 16-bit state: M' of the current call
+  uint16_t* Eh = nullptr;  // 16-bit state with error feedback: E's place (M' or the error)
+  uint16_t* Mh = nullptr;  // 16-bit state without error feedback: M' of the current call
   float* P = nullptr;
   float* Praw = nullptr;  // vector ranks: P as pass 1 writes it (pass 2 orthogonalizes)
   float* Ppart = nullptr;  // matrix-core ranks: pass 1's column-group partials of P
@@ -158,10 +158,10 @@ struct BucketPlan {
   float* intro_PQ = nullptr;
   std::vector<int64_t> intro_off;  // per tensor: first float of its compact P, then Q
   hipStream_t last_stream = nullptr;  // stream of the latest compressing call
-  // E's place (fp32 error memory) is known to hold the error itself (true: before the
-  // first call, after an import, after a materialization in place); false after a call
-  // that keeps M' there (an fp16 step skipped for inf leaves the error in place: the
-  // device flag wflag says which, for the kernels)
+  // E's place (the error memory, fp32 or 16-bit) is known to hold the error itself
+  // (true: before the first call, after an import, after a materialization in place);
+  // false after a call that keeps M' there (an fp16 step skipped for inf leaves the
+  // error in place: the device flag wflag says which, for the kernels)
   bool w_holds_e = true;
   int32_t* wflag = nullptr;  // device: non-zero while E's place holds the error itself
   float* Emat = nullptr;  // the materialized error for introspection and export
@@ -169,6 +169,12 @@ struct BucketPlan {
   bool q_ready = false;
   // every tensor has 16-byte aligned rows (in d_td) at least 256 columns wide
   bool all_wide = false;
+
+  // A 16-bit state's M' of the call, as the passes read and write it: E's place with
+  // error feedback (pass 1 replaces M'_prev there), the separate array without.
+  uint16_t* mprime16() const { return Eh ? Eh : Mh; }
+  // E's place holds M' of the previous call (a state with error feedback)
+  bool keeps_mprime() const { return E != nullptr || Eh != nullptr; }
 
   void release() {
     void* ptrs[] = {E, Eh, Mh, P, Praw, Ppart, Q, QT, partial, gram, tmat, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
@@ -521,7 +527,8 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
                    (need_e && !h16) ? pl.e_floats * sizeof(float) : 0);
   ok = ok && alloc(reinterpret_cast<void**>(&pl.Eh),
                    (need_e && h16) ? pl.e_floats * sizeof(uint16_t) : 0);
-  ok = ok && alloc(reinterpret_cast<void**>(&pl.Mh), h16 ? pl.e_floats * sizeof(uint16_t) : 0);
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.Mh),
+                   (h16 && !need_e) ? pl.e_floats * sizeof(uint16_t) : 0);
   ok = ok && alloc(reinterpret_cast<void**>(&pl.P), pl.p_floats * sizeof(float));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.Praw),
                    pl.R <= kMaxFusedGramRank ? pl.p_floats * sizeof(float) : 0);
@@ -532,7 +539,7 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   ok = ok && alloc(reinterpret_cast<void**>(&pl.gram), pl.gram_doubles * sizeof(double));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.tmat),
                    pl.tensors.size() * static_cast<size_t>(pl.R) * pl.R * sizeof(double));
-  ok = ok && alloc(reinterpret_cast<void**>(&pl.wflag), pl.E ? sizeof(int32_t) : 0);
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.wflag), (pl.E || pl.Eh) ? sizeof(int32_t) : 0);
 
   if (!ok) {
     pl.release();
@@ -600,16 +607,16 @@ int64_t batched_side(int64_t numel) {
   return s;
 }
 
-// Algorithmic bytes of each pass per compressed element (minimum traffic).
 // Minimum bytes per compressed element that each pass moves. Without error feedback
 // pass 3 only writes M_hat (M' is not read).
 double pass_bytes(int kind, bool f16, bool ef, int prec = kStF32) {
   if (prec != kStF32) {
-    // fp32 bucket, 16-bit M' and E
+    // fp32 bucket, 16-bit M' (in E's place with error feedback): pass 1 reads G (and
+    // M'_prev) and writes M', pass 2 reads M', pass 3 writes M_hat
     switch (kind) {
       case K_PASS1: return 4.0 + (ef ? 2.0 : 0.0) + 2.0;
       case K_PASS2: return 2.0;
-      case K_PASS3: return ef ? 2.0 + 4.0 + 2.0 : 4.0;
+      case K_PASS3: return 4.0;
       default: return 0.0;
     }
   }
@@ -629,29 +636,33 @@ double pass_bytes(int kind, bool f16, bool ef, int prec = kStF32) {
 
 namespace {
 
-// The error of every tensor of a plan keeping M' in E's place, written to dst (E's
-// layout; dst may be pl.E itself), on stream s: E = M'_prev - P Q^T, or E's place as it
-// is while the device flag says it holds the error.
+// The error of every tensor of a plan keeping M' in E's place, on stream s: E = M'_prev -
+// P Q^T with pass 3's rounding, or E's place as it is while the device flag says it holds
+// the error. Written as binary32 to dst (E's layout; an fp32 plan may pass pl.E itself),
+// or, for a 16-bit plan with dst NULL, back into E's place in 16 bits.
 powersgd_status materialize_error(BucketPlan& pl, float* dst, hipStream_t s) {
   Pass3Args a{};
   a.tiles = pl.d_tiles3;
   a.ntiles = static_cast<int32_t>(pl.tiles3.size());
   a.td = pl.d_td;
   a.E = pl.E;
+  a.Eh = pl.Eh;
+  a.Mh = pl.Eh;  // a 16-bit plan's M'_prev
   a.P = pl.P;
   a.Q = pl.Q;
   a.inv_scale = 1.0f;
   a.Eout = dst;
   a.wflag = pl.wflag;  // E's place may still hold the error itself (a skipped fp16 step)
-  const hipError_t e = launch_error_materialize(pl.R, a, s);
+  const hipError_t e = launch_error_materialize(pl.R, pl.st, a, s);
   if (e != hipSuccess) return hip_fail(e, "error materialization");
   return POWERSGD_OK;
 }
 
-// Device memory holding the error of an fp32 plan, E's layout: E's place itself, or a
-// copy materialized on stream s.
+// Device memory holding the error of a plan as binary32, E's layout: an fp32 plan's E's
+// place itself while it holds the error, else a copy materialized on stream s (a 16-bit
+// plan whose E's place holds the error is widened by the callers instead).
 powersgd_status error_source(BucketPlan& pl, hipStream_t s, const float** out) {
-  if (pl.w_holds_e) {
+  if (pl.w_holds_e && pl.E) {
     *out = pl.E;
     return POWERSGD_OK;
   }
@@ -883,11 +894,10 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
   const bool fused = R <= kMaxFusedGramRank;
   const uint64_t bucket_key = static_cast<uint64_t>(bucket_index);
   powersgd_status r = POWERSGD_OK;
-  // a call with error feedback and an fp32 state keeps M' in E's place; it rebuilds the
-  // previous error from M'_prev, P and the warm-start Q unless E's place holds the error
-  // itself
-  const bool sm = ef && prec == kStF32;
-  if (ef && pl.E && !pl.w_holds_e && nt > 0 && (!sm || !hp.warm_start)) {
+  // a call with error feedback keeps M' in E's place; it rebuilds the previous error
+  // from M'_prev, P and the warm-start Q unless E's place holds the error itself
+  const bool sm = ef;
+  if (ef && pl.keeps_mprime() && !pl.w_holds_e && nt > 0 && !hp.warm_start) {
     // this call cannot rebuild (a fresh Q draw replaces the Q it would need): the error
     // itself goes into E's place first
     r = materialize_error(pl, pl.E, s);
@@ -956,7 +966,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.wflag = sm ? pl.wflag : nullptr;
     a.gram = pl.gram;
     a.Eh = pl.Eh;
-    a.Mh = pl.Mh;
+    a.Mh = pl.mprime16();
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
     const double bytes = ce * pass_bytes(K_PASS1, f16, ef, prec) + (f16 && !precheck ? ue * 2.0 : 0.0);
@@ -995,7 +1005,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.Q = pl.Q;
     a.QT = pl.QT;
     a.partial = pl.partial;
-    a.Mh = pl.Mh;
+    a.Mh = pl.mprime16();
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
     r = timed_launch(st, s, K_PASS2, ce * pass_bytes(K_PASS2, f16, ef, prec), "pass 2",
@@ -1031,7 +1041,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.Q = pl.Q;
     a.partial = pl.partial;  // vector ranks sum the pass-2 partials here
     a.Eh = pl.Eh;
-    a.Mh = pl.Mh;
+    a.Mh = pl.mprime16();
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
     a.wflag = sm ? pl.wflag : nullptr;  // cleared by the pass once the step runs
@@ -1273,8 +1283,8 @@ powersgd_status powersgd_copy_error(powersgd_state* st, int64_t bucket_index, in
   if (!pl->E && !pl->Eh) return fail(POWERSGD_ERR_NOT_FOUND, "error feedback is off");
   if (!e_dev) return fail(POWERSGD_ERR_INVALID_ARG, "e_dev is NULL");
   HipDeviceGuard guard(st->device);
-  if (pl->Eh) {
-    // a 16-bit state: its values widened to fp32
+  if (pl->Eh && pl->w_holds_e) {
+    // a 16-bit state holding the error itself: its values widened to fp32
     hipError_t e = launch_widen16(pl->Eh + d->eoff, e_dev, static_cast<int64_t>(d->n) * d->m,
                                   pl->st, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "copy of E");
@@ -1352,7 +1362,9 @@ powersgd_status powersgd_get_error(powersgd_state* st, int64_t bucket_index, con
   }
   hipStream_t s = pl.last_stream;
   const float* src = nullptr;
-  if (pl.E) {
+  // a 16-bit state holding the error itself is widened; otherwise the binary32 error
+  const bool widen = pl.Eh && pl.w_holds_e;
+  if (!widen) {
     powersgd_status rs = error_source(pl, s, &src);
     if (rs != POWERSGD_OK) return rs;
   }
@@ -1360,7 +1372,7 @@ powersgd_status powersgd_get_error(powersgd_state* st, int64_t bucket_index, con
   for (const TensorDesc& d : pl.tensors) {
     if (e != hipSuccess) break;
     const int64_t cnt = static_cast<int64_t>(d.n) * d.m;
-    if (pl.Eh)
+    if (widen)
       e = launch_widen16(pl.Eh + d.eoff, pl.intro_E + d.boff, cnt, pl.st, s);
     else
       e = hipMemcpyAsync(pl.intro_E + d.boff, src + d.eoff, cnt * sizeof(float),
@@ -1613,7 +1625,11 @@ void write_snapshot(const powersgd_state* st, SnapWriter& w, ExportCopies* copie
       for (int64_t d : k.shape) w.put<int64_t>(d);
     }
     size_t qbuf = 0, ebuf = 0;
-    if (copies && ef && pl.st != kStF32 && pl.e_floats > 0) {
+    // a 16-bit E's place holding the error itself goes over in 16 bits and is widened on
+    // the host; any other error comes from binary32 memory (E's place, or the error the
+    // export materialized first)
+    const bool e16 = pl.st != kStF32 && pl.w_holds_e;
+    if (copies && ef && e16 && pl.e_floats > 0) {
       copies->ebufs.emplace_back(static_cast<size_t>(pl.e_floats));
       ebuf = copies->ebufs.size() - 1;
       copies->segs.push_back(CopySeg{pl.Eh, reinterpret_cast<uint8_t*>(copies->ebufs[ebuf].data()),
@@ -1633,7 +1649,7 @@ void write_snapshot(const powersgd_state* st, SnapWriter& w, ExportCopies* copie
         const int64_t bytes = static_cast<int64_t>(d.n) * d.m * 4;
         uint8_t* dst = w.take(bytes);
         if (copies && bytes > 0) {
-          if (pl.st != kStF32)  // widened to binary32 after the transfer
+          if (e16)  // widened to binary32 after the transfer
             copies->epieces.push_back(
                 ExportCopies::EPiece{ebuf, d.eoff, static_cast<int64_t>(d.n) * d.m, pl.st, dst});
           else
@@ -1802,10 +1818,10 @@ powersgd_status powersgd_state_export(powersgd_state* st, void* host_buf, int64_
                                               std::to_string(measure.pos) + " bytes");
   HipDeviceGuard guard(st->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // fp32 buckets whose E's place holds M': their error, materialized for the copies
+  // buckets whose E's place holds M': their error, materialized for the copies
   for (auto& kv : st->buckets) {
     BucketPlan& pl = *kv.second;
-    if (pl.E && !pl.w_holds_e) {
+    if (pl.keeps_mprime() && !pl.w_holds_e) {
       const float* src = nullptr;
       powersgd_status r = error_source(pl, s, &src);
       if (r != POWERSGD_OK) return r;

@@ -109,18 +109,19 @@ struct Pass1Args {
   // matrix-core ranks: P of each (row block, column group) work item, a partial sum
   // over the group's columns, at p1off + (group * n + row) * R
   float* Ppart;
-  // fp32 buckets with error feedback keep M' of the previous step in E's place; its error
-  // is rebuilt as E = M'_prev - Pe Q^T with Pe the previous orthogonalized P (Q being the
-  // warm-start Q). Null when E's place holds the error itself (first call, after an
-  // import, without warm start).
+  // With error feedback E's place keeps M' of the previous step (binary32 in E, or 16
+  // bits in Eh); its error is rebuilt as E = M'_prev - Pe Q^T (with pass 3's rounding)
+  // with Pe the previous orthogonalized P (Q being the warm-start Q). Null when E's
+  // place holds the error itself (first call, after an import, without warm start).
   const float* Pe;
   // With Pe: device flag, non-zero while E's place still holds the error itself (then
   // nothing is rebuilt); pass 3 of a step that ran clears it.
   const int32_t* wflag;
   const float* QT;         // matrix-core ranks: Q^T (B fragments as 16-byte loads)
   double* gram;            // P Gram partials (ranks <= 8: computed here)
-  uint16_t* Eh;            // 16-bit state: E (E's offsets)
-  uint16_t* Mh;            // 16-bit state: M' written here (E's offsets)
+  uint16_t* Eh;            // 16-bit state: E's place (E's offsets)
+  uint16_t* Mh;            // 16-bit state: M' written here (E's offsets; Eh itself with
+                           // error feedback)
   float inv_scale;
   int32_t* found_inf;
 };
@@ -138,7 +139,7 @@ struct Pass2Args {
   float* Q;
   float* QT;               // matrix-core ranks: Q^T, written next to Q (else null)
   float* partial;
-  const uint16_t* Mh;      // 16-bit state: M' (E's offsets)
+  const uint16_t* Mh;      // 16-bit state: M' (E's offsets; E's place with error feedback)
   float inv_scale;
   const int32_t* found_inf;
 };
@@ -165,11 +166,13 @@ struct Pass3Args {
   const float* P;
   float* Q;                // vector ranks: written here for tensors split into row blocks
   const float* partial;    // vector ranks: pass-2 partial slots (summed here)
-  uint16_t* Eh;            // 16-bit state: E (E's offsets)
-  const uint16_t* Mh;      // 16-bit state: M' (E's offsets)
+  uint16_t* Eh;            // 16-bit state: E's place (E's offsets)
+  const uint16_t* Mh;      // 16-bit state: M' (E's offsets; Eh itself with error feedback)
   float inv_scale;
   const int32_t* found_inf;
-  float* Eout;             // error materialization: E = M' - P Q^T written here (E's offsets)
+  // error materialization: E = M' - P Q^T written here as binary32 (E's offsets); a
+  // 16-bit state with Eout null writes it back into Eh in 16 bits
+  float* Eout;
   // Buckets keeping M' in E's place: the device flag that says E's place still holds the
   // error itself. Pass 3 of a step that ran clears it; the materialization reads it (set:
   // the error is copied as it is). Null: E's place holds M'.
@@ -194,10 +197,12 @@ hipError_t launch_pass2(int R, bool f16, bool ef, int st, bool wide_only, const 
                         hipStream_t s);
 hipError_t launch_pass2_reduce(int R, int st, const Pass2ReduceArgs& a, hipStream_t s);
 hipError_t launch_pass3(int R, bool f16, bool ef, int st, const Pass3Args& a, hipStream_t s);
-// fp32 state with error feedback: the error E = M' - P Q^T of every tensor, from the M'
-// kept in E's place (a.E) and the step's P and Q, into a.Eout (E's layout; may be a.E),
-// with pass 3's tiling and arithmetic, so the values are the ones pass 3's M_hat implies.
-hipError_t launch_error_materialize(int R, const Pass3Args& a, hipStream_t s);
+// A state with error feedback (precision st): the error E = M' - P Q^T of every tensor,
+// from the M' kept in E's place (a.E, or a.Mh = a.Eh for a 16-bit state) and the step's
+// P and Q, into a.Eout (binary32, E's layout; may be a.E) or, for a 16-bit state with
+// a.Eout null, back into a.Eh, with pass 3's tiling and arithmetic, so the values are
+// the ones pass 3's M_hat implies.
+hipError_t launch_error_materialize(int R, int st, const Pass3Args& a, hipStream_t s);
 // *flag = value (one thread; no memset node, so it can sit in a captured graph).
 hipError_t launch_set_flag(int32_t* flag, int32_t value, hipStream_t s);
 // Double-double Gram partials of each job's rows (one work item per kGramRows rows).

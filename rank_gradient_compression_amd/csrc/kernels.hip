@@ -10,13 +10,14 @@
 //   Streaming passes share one tiling: (row block x 256-column block) work items;
 //   a lane owns 4 consecutive columns (16-byte accesses) and keeps several rows of
 //   loads in flight; narrow matrices pack several rows into one wavefront.
-//   error memory  with error feedback and an fp32 state (fp32 or fp16 buckets), E's
-//           place keeps M' of the previous step instead of E = M' - M_hat: with the
-//           step's P and Q (which the state keeps anyway) the error is rebuilt exactly,
-//           as E = M'_prev - P Q^T with the very arithmetic pass 3 uses for M_hat. Pass
-//           3 then only writes M_hat. A device flag says when E's place still holds
-//           the error itself; fp16 buckets check the whole bucket for inf first, so a
-//           skipped step writes nothing. 16-bit states keep E.
+//   error memory  with error feedback, E's place keeps M' of the previous step
+//           instead of E = M' - M_hat (binary32 for an fp32 state, 16 bits for the
+//           wrappers' 16-bit states): with the step's P and Q (which the state keeps
+//           anyway) the error is rebuilt exactly, as E = M'_prev - P Q^T with the very
+//           arithmetic and rounding pass 3 uses for M_hat. Pass 3 then only writes
+//           M_hat. A device flag says when E's place still holds the error itself;
+//           fp16 buckets check the whole bucket for inf first, so a skipped step
+//           writes nothing.
 //   pass 1  M' = G (+ E), the error rebuilt from M'_prev and M' written over it;
 //           P = M' Q. Vector ranks: a workgroup owns whole rows, so each dot product is
 //           finished inside it (shuffles, then LDS across wavefronts); matrix-core
@@ -34,8 +35,7 @@
 //           pass-3 workgroups of that column block (vector ranks) or by a small
 //           kernel of its own (matrix-core ranks): deterministic, no atomics, no
 //           inter-workgroup fences (the kernel boundary publishes the partials).
-//   pass 3  M_hat = P Q^T written into the bucket (fp16: round to nearest even);
-//           16-bit states, which keep the error itself, also E = M' - M_hat.
+//   pass 3  M_hat = P Q^T written into the bucket (fp16: round to nearest even).
 //   q_init  Philox4x64-10 + Box-Muller draw of the initial Q (counter layout in
 //           the public header's companion documentation).
 #include <hip/hip_fp16.h>
@@ -392,16 +392,17 @@ __device__ __forceinline__ void ld_q4(const float* __restrict__ Q, int c, int va
 // The wrapped hook keeps M' and E as 16-bit values (binary16 or bfloat16), rounded to
 // nearest even wherever a value is formed; arithmetic stays in fp32.
 
-// bfloat16 bits of x rounded to nearest even: add half an ulp of the result (less one,
-// plus the kept part's lowest bit, which breaks ties toward even) and keep the upper
-// half of the binary32 pattern; overflow carries into the exponent and gives inf. NaN
-// stays a quiet NaN.
+// bfloat16 bits of x rounded to nearest even (ties to the even significand), +-inf past
+// the largest finite value, a NaN kept a quiet NaN with its sign and upper payload bits:
+// the compiler's __bf16 conversion, one v_cvt_pk_bf16_f32 on gfx950 (which equals
+// adding 0x7FFF plus the kept part's lowest bit to the binary32 pattern and keeping its
+// upper half, for every non-NaN input).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
+
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 template <int ST>
 __device__ __forceinline__ uint16_t to_h16(float x) {
@@ -452,19 +453,31 @@ __device__ __forceinline__ void ld_h4(const uint16_t* p, int valid, float (&x)[4
   }
 }
 
+// Two values rounded to the state's precision, packed (a in the low half): bfloat16
+// pairs take one conversion instruction.
+template <int ST>
+__device__ __forceinline__ uint32_t pack_h16x2(float a, float b) {
+  if constexpr (ST == kStBF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
+  else
+    return static_cast<uint32_t>(to_h16<ST>(a)) | (static_cast<uint32_t>(to_h16<ST>(b)) << 16);
+}
+
 // Rounds 4 values to the state's precision and stores the first `valid` of them.
 template <int ST, int LD>
 __device__ __forceinline__ void st_h4(uint16_t* p, int valid, const float (&x)[4]) {
-  uint32_t o[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) o[a] = to_h16<ST>(x[a]);
   if constexpr (LD == kLdAligned) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+    *reinterpret_cast<uint2*>(p) =
+        make_uint2(pack_h16x2<ST>(x[0], x[1]), pack_h16x2<ST>(x[2], x[3]));
   } else {
     if (LD == kLdUnaligned && valid >= 4) {
-      *reinterpret_cast<u32x2u*>(p) = u32x2u{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+      *reinterpret_cast<u32x2u*>(p) =
+          u32x2u{pack_h16x2<ST>(x[0], x[1]), pack_h16x2<ST>(x[2], x[3])};
       return;
     }
+    uint32_t o[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) o[a] = to_h16<ST>(x[a]);
 #pragma unroll
     for (int a = 0; a < 4; ++a)
       if (a < valid) p[a] = static_cast<uint16_t>(o[a]);
@@ -575,11 +588,22 @@ __device__ __forceinline__ void mhat4(const float (&p)[R], const float (&q)[4][R
   }
 }
 
-// With error feedback and an fp32 state (fp32 or fp16 buckets), E's place keeps M' of
-// the previous step (the error is rebuilt from it and the step's factors); 16-bit states
-// keep the error itself.
+// With error feedback, E's place keeps M' of the previous step and the error is rebuilt
+// from it and the step's factors: in binary32 for an fp32 state (fp32 or fp16 buckets),
+// in the state's 16 bits for the wrappers' 16-bit states.
 template <bool F16, bool EF, int ST>
-constexpr bool stored_mprime() { return EF && ST == kStF32; }
+constexpr bool stored_mprime() { return EF; }
+
+// The previous error rebuilt from M'_prev (w) and M_hat_prev = P Q^T (mh, as the
+// matrix product left it) with pass 3's rounding: w - mh for an fp32 state; a 16-bit
+// state's pass 3 rounded M_hat to 16 bits and the error M' - M_hat again.
+template <int ST>
+__device__ __forceinline__ float rebuilt_error(float w, float mh) {
+  if constexpr (ST == kStF32)
+    return w - mh;
+  else
+    return rnd16<ST>(w - rnd16<ST>(mh));
+}
 
 // Whether pass 1 rebuilds the previous error from M'_prev in E's place: a state keeping
 // M', given the previous factors, unless E's place still holds the error itself.
@@ -599,6 +623,20 @@ __device__ __forceinline__ void mark_mprime(const Pass3Args& a) {
   if constexpr (stored_mprime<F16, EF, ST>() && !MAT) {
     if (a.wflag != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *a.wflag = 0;
   }
+}
+
+// A materialized error (4 values from element off of E's layout): binary32 into Eout,
+// or, for a 16-bit state called without Eout, back into E's place in its 16 bits.
+template <int ST, int LD>
+__device__ __forceinline__ void store_materialized(const Pass3Args& a, int64_t off, int valid,
+                                                   const float (&e)[4]) {
+  if constexpr (ST != kStF32) {
+    if (a.Eout == nullptr) {
+      st_h4<ST, LD>(a.Eh + off, valid, e);
+      return;
+    }
+  }
+  st_f32x4<LD>(a.Eout + off, valid, e);
 }
 
 // ----------------------------------------------------------------------- pass 1
@@ -734,10 +772,20 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
       }
       if constexpr (ST != kStF32) {
         // the wrapper's cast, then M' = G + E formed in 16 bits and kept for passes 2, 3
+        // (with error feedback Mh is E's place itself: M' replaces M'_prev there)
         if constexpr (EF) {
           float e[U][4];
 #pragma unroll
           for (int u = 0; u < U; ++u) ld_h4<ST, LD>(args.Eh + d.eoff + rbase[u] + c, valid, e[u]);
+          if (rebuild) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+              float mh[4];
+              mhat4<R>(pe[u], q, mh);
+#pragma unroll
+              for (int a = 0; a < 4; ++a) e[u][a] = rebuilt_error<ST>(e[u][a], mh[a]);
+            }
+          }
 #pragma unroll
           for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -755,24 +803,20 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
         float e[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) ld_f32x4<LD>(Et + rbase[u] + c, valid, e[u]);
-        if constexpr (SM) {
-          if (rebuild) {
+        if (rebuild) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-              float mh[4];
-              mhat4<R>(pe[u], q, mh);
+          for (int u = 0; u < U; ++u) {
+            float mh[4];
+            mhat4<R>(pe[u], q, mh);
 #pragma unroll
-              for (int a = 0; a < 4; ++a) e[u][a] = e[u][a] - mh[a];
-            }
+            for (int a = 0; a < 4; ++a) e[u][a] = rebuilt_error<ST>(e[u][a], mh[a]);
           }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
           for (int a = 0; a < 4; ++a) x[u][a] += e[u][a];
-          if constexpr (SM) {
-            if (rok[u]) st_f32x4<LD>(Et + rbase[u] + c, valid, x[u]);  // M' in E's place
-          }
+          if (rok[u]) st_f32x4<LD>(Et + rbase[u] + c, valid, x[u]);  // M' in E's place
         }
       }
 #pragma unroll
@@ -1358,8 +1402,9 @@ __device__ __forceinline__ void orth_from_factor_wg(int rank, double eps, OrthSh
 
 // ----------------------------------------------------------------------- pass 2
 
-// M' at element `off` of a matrix (fp32 with error feedback: pass 1 wrote M' into E's
-// place; fp16: unscaled gradient plus E; 16-bit state: M' from Mt).
+// M' at element `off` of a matrix (fp32 state with error feedback: pass 1 wrote M' into
+// E's place; without: the (unscaled) gradient; 16-bit state: M' from Mt, which is E's
+// place with error feedback).
 template <bool F16, bool EF, int LD, int ST = kStF32>
 __device__ __forceinline__ void ld_mprime4(const void* bucket, const float* Et, int64_t boff,
                                            int64_t off, int valid, float inv_scale,
@@ -1374,12 +1419,6 @@ __device__ __forceinline__ void ld_mprime4(const void* bucket, const float* Et, 
   }
   bool rb;
   ld_grad4<F16, LD>(bucket, boff + off, valid, inv_scale, x, rb);
-  if constexpr (F16 && EF) {
-    float e[4];
-    ld_f32x4<LD>(Et + off, valid, e);
-#pragma unroll
-    for (int a = 0; a < 4; ++a) x[a] += e[a];
-  }
 }
 
 // Gram-Schmidt of P (step 3.4) for the rows of one pass-2 tile: the workgroup sums the
@@ -1721,8 +1760,8 @@ __device__ __forceinline__ void pass3_q_from_partials(const Pass3Args& args, con
 template <int R, int U, bool F16, bool EF, int LD, bool WIDE, int ST, bool MAT = false>
 __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDesc& d,
                                            const Tile& t, float* qred) {
-  constexpr bool SM = stored_mprime<F16, EF, ST>();
-  constexpr bool LOADX = EF && (!SM || MAT);  // M' is read
+  // M' is read only to materialize the error (E's place holds it with error feedback)
+  constexpr bool LOADX = EF && MAT;
   const bool we = MAT && holds_error(args);  // materialization: E's place holds E
   const int lane = threadIdx.x & 63;
   const int wave = wave_index();
@@ -1767,23 +1806,14 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
       if constexpr (MAT) {
         float e[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) e[a] = we ? x[u][a] : x[u][a] - mh[a];
-        st_f32x4<LD>(args.Eout + d.eoff + off, L.valid, e);
+        for (int a = 0; a < 4; ++a) e[a] = we ? x[u][a] : rebuilt_error<ST>(x[u][a], mh[a]);
+        store_materialized<ST, LD>(args, d.eoff + off, L.valid, e);
         continue;
       }
       if constexpr (F16)
         st_f16x4<LD>(static_cast<uint16_t*>(args.bucket) + d.boff + off, L.valid, mh);
       else
         st_f32x4<LD>(static_cast<float*>(args.bucket) + d.boff + off, L.valid, mh);
-      if constexpr (EF && !SM) {
-        float e[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) e[a] = x[u][a] - mh[a];
-        if constexpr (ST != kStF32)
-          st_h4<ST, LD>(args.Eh + d.eoff + off, L.valid, e);  // rounds E to 16 bits
-        else
-          st_f32x4<LD>(Et + off, L.valid, e);
-      }
     }
   }
 }
@@ -1959,7 +1989,7 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
 #pragma unroll
           for (int kq = 0; kq < KQ; ++kq) mh = mfma16(qa[kq], pe[kq], mh);
 #pragma unroll
-          for (int a = 0; a < 4; ++a) e[u][a] = e[u][a] - mh[a];
+          for (int a = 0; a < 4; ++a) e[u][a] = rebuilt_error<ST>(e[u][a], mh[a]);
         }
       }
 #pragma unroll
@@ -2168,10 +2198,10 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
           mh[i] = *reinterpret_cast<const float4*>(mh_tile + (RW * wave + i) * LS + 4 * lane);
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
-          xe[i][0] = xe[i][0] - mh[i].x;
-          xe[i][1] = xe[i][1] - mh[i].y;
-          xe[i][2] = xe[i][2] - mh[i].z;
-          xe[i][3] = xe[i][3] - mh[i].w;
+          xe[i][0] = rebuilt_error<ST>(xe[i][0], mh[i].x);
+          xe[i][1] = rebuilt_error<ST>(xe[i][1], mh[i].y);
+          xe[i][2] = rebuilt_error<ST>(xe[i][2], mh[i].z);
+          xe[i][3] = rebuilt_error<ST>(xe[i][3], mh[i].w);
         }
       }
     }
@@ -2490,18 +2520,18 @@ __device__ __forceinline__ void pass2_mfma16_rows(const Pass2Args& args, const T
       }
 #pragma unroll
     for (int u = 0; u < U2; ++u) {
-      uint32_t pb[4][NT];  // 16-bit P values (exact: P is rounded where it is formed)
+      float pz[4][NT];  // P values (16-bit exact: P is rounded where it is formed)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bool rok = rr + 16 * u + 4 * h + j < r1;
         if (!(rok && col_ok)) xm[u][j] = make_uint2(0u, 0u);  // +0 in both formats
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) pb[j][nt] = rok ? to_h16<ST>(pv[u][j][nt]) : 0u;
+        for (int nt = 0; nt < NT; ++nt) pz[j][nt] = rok ? pv[u][j][nt] : 0.f;
       }
       uint2 b[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        b[nt] = make_uint2(pb[0][nt] | (pb[1][nt] << 16), pb[2][nt] | (pb[3][nt] << 16));
+        b[nt] = make_uint2(pack_h16x2<ST>(pz[0][nt], pz[1][nt]), pack_h16x2<ST>(pz[2][nt], pz[3][nt]));
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         // column s4 of the 4 x 4 block: element s4 of each row's four 16-bit values
@@ -2570,8 +2600,8 @@ __global__ void __launch_bounds__(kThreads) k_pass2_mfma(Pass2Args args) {
 template <int R, bool F16, bool EF, bool VEC, int ST, bool MAT = false>
 __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const TensorDesc& d,
                                                 const Tile& t, int lane, int wave) {
-  constexpr bool SM = stored_mprime<F16, EF, ST>();
-  constexpr bool LOADX = EF && (!SM || MAT);  // M' is read
+  // M' is read only to materialize the error (E's place holds it with error feedback)
+  constexpr bool LOADX = EF && MAT;
   const bool we = MAT && holds_error(args);  // materialization: E's place holds E
   constexpr int KQ = R / 4;
   constexpr int UR = 2;  // 16-row steps loaded before use
@@ -2617,21 +2647,10 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
         if constexpr (!LOADX) {
           // M' is not needed
         } else if constexpr (VEC && ST != kStF32) {
-          if constexpr (EF)
-            ld_h4<ST, kLdAligned>(args.Mh + d.eoff + static_cast<int64_t>(rowc) * m +
-                                      min(col, m - 4), 4, x[ur][g]);
-        } else if constexpr (VEC && SM) {
-          load_f4(Et + static_cast<int64_t>(rowc) * m + min(col, m - 4), x[ur][g]);
+          ld_h4<ST, kLdAligned>(args.Mh + d.eoff + static_cast<int64_t>(rowc) * m +
+                                    min(col, m - 4), 4, x[ur][g]);
         } else if constexpr (VEC) {
-          const int64_t off = static_cast<int64_t>(rowc) * m + min(col, m - 4);
-          bool rb;
-          load_grad4_vec<F16>(args.bucket, d.boff + off, args.inv_scale, x[ur][g], rb);
-          if constexpr (F16 && EF) {
-            float e[4];
-            load_f4(Et + off, e);
-#pragma unroll
-            for (int a = 0; a < 4; ++a) x[ur][g][a] += e[a];
-          }
+          load_f4(Et + static_cast<int64_t>(rowc) * m + min(col, m - 4), x[ur][g]);
         } else {
           if (row < r1 && col < m)
             ld_mprime4<F16, EF, kLdScalar, ST>(args.bucket, Et, d.boff,
@@ -2657,27 +2676,15 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
           if constexpr (MAT) {
             float e[4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) e[a] = we ? x[ur][g][a] : x[ur][g][a] - mh[a];
-            store_f32x4(args.Eout + d.eoff + off, VEC, m - col, e);
+            for (int a = 0; a < 4; ++a)
+              e[a] = we ? x[ur][g][a] : rebuilt_error<ST>(x[ur][g][a], mh[a]);
+            store_materialized<ST, VEC ? kLdAligned : kLdScalar>(args, d.eoff + off, m - col, e);
             continue;
           }
           if constexpr (F16)
             store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, VEC, m - col, mh);
           else
             store_f32x4(static_cast<float*>(args.bucket) + d.boff + off, VEC, m - col, mh);
-          if constexpr (EF && !SM) {
-            float e[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) e[a] = x[ur][g][a] - mh[a];
-            if constexpr (ST != kStF32) {
-              if constexpr (VEC)
-                st_h4<ST, kLdAligned>(args.Eh + d.eoff + off, 4, e);
-              else
-                st_h4<ST, kLdScalar>(args.Eh + d.eoff + off, m - col, e);
-            } else {
-              store_f32x4(Et + off, VEC, m - col, e);
-            }
-          }
         }
       }
     }
@@ -2697,8 +2704,8 @@ template <int R, bool F16, bool EF, int ST, bool MAT = false>
 __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const TensorDesc& d,
                                                 const Tile& t, int lane, int wave,
                                                 float* tile) {
-  constexpr bool SM = stored_mprime<F16, EF, ST>();
-  constexpr bool LOADX = EF && (!SM || MAT);  // M' is read
+  // M' is read only to materialize the error (E's place holds it with error feedback)
+  constexpr bool LOADX = EF && MAT;
   const bool we = MAT && holds_error(args);  // materialization: E's place holds E
   constexpr int KQ = R / 4;
   constexpr int UR = 2;         // 16-row MFMA groups per step
@@ -2786,23 +2793,14 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
         if constexpr (MAT) {
           float e[4];
 #pragma unroll
-          for (int a = 0; a < 4; ++a) e[a] = we ? x[i][a] : x[i][a] - mh[a];
-          store_f32x4(args.Eout + d.eoff + off, true, 4, e);
+          for (int a = 0; a < 4; ++a) e[a] = we ? x[i][a] : rebuilt_error<ST>(x[i][a], mh[a]);
+          store_materialized<ST, kLdAligned>(args, d.eoff + off, 4, e);
           continue;
         }
         if constexpr (F16)
           store_f16x4(static_cast<uint16_t*>(args.bucket) + d.boff + off, true, 4, mh);
         else
           store_f32x4(static_cast<float*>(args.bucket) + d.boff + off, true, 4, mh);
-        if constexpr (EF && !SM) {
-          float e[4];
-#pragma unroll
-          for (int a = 0; a < 4; ++a) e[a] = x[i][a] - mh[a];
-          if constexpr (ST != kStF32)
-            st_h4<ST, kLdAligned>(args.Eh + d.eoff + off, 4, e);
-          else
-            store_f32x4(Et + off, true, 4, e);
-        }
       }
     }
     __syncthreads();  // the tile is rewritten by the next step
@@ -3396,14 +3394,24 @@ hipError_t launch_pass3(int R, bool f16, bool ef, int st, const Pass3Args& a, hi
   PSGD_RANK_SWITCH(R, return pass3_r<RR>(f16, ef, st, a, s))
 }
 
-hipError_t launch_error_materialize(int R, const Pass3Args& a, hipStream_t s) {
+template <int R, int ST>
+void materialize_r(const Pass3Args& a, dim3 grid, hipStream_t s) {
+  if constexpr (R >= kMfmaMinRank)
+    k_pass3_mfma<R, false, true, ST, true><<<grid, kThreads, 0, s>>>(a);
+  else
+    k_pass3<R, unroll3<R, ST>(), false, true, ST, true><<<grid, kThreads, 0, s>>>(a);
+}
+
+hipError_t launch_error_materialize(int R, int st, const Pass3Args& a, hipStream_t s) {
   if (a.ntiles == 0) return hipSuccess;
   const dim3 grid(a.ntiles);
   PSGD_RANK_SWITCH(R, {
-    if constexpr (RR >= kMfmaMinRank)
-      k_pass3_mfma<RR, false, true, kStF32, true><<<grid, kThreads, 0, s>>>(a);
+    if (st == kStF16)
+      materialize_r<RR, kStF16>(a, grid, s);
+    else if (st == kStBF16)
+      materialize_r<RR, kStBF16>(a, grid, s);
     else
-      k_pass3<RR, unroll3<RR, kStF32>(), false, true, kStF32, true><<<grid, kThreads, 0, s>>>(a);
+      materialize_r<RR, kStF32>(a, grid, s);
     return hipGetLastError();
   })
 }

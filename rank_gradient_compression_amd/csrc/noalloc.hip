@@ -310,7 +310,7 @@ extern "C" POWERSGD_API powersgd_status powersgd_compress_matrix_noalloc(
     if (ef) {
       // pass 1 left M' in E's place (the caller's E): the error itself goes back there
       a.Eout = E;
-      if (!check(launch_error_materialize(R, a, s), "error materialization launch"))
+      if (!check(launch_error_materialize(R, kStF32, a, s), "error materialization launch"))
         return POWERSGD_ERR_HIP;
     }
   }

@@ -225,6 +225,41 @@ def test_wrapped_snapshot_matches_the_oracle_and_resumes(dt, code):
     assert torch.equal(xa.view(torch.int32), xb.view(torch.int32))
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("rank", [2, 8, 16, 32])
+def test_wrapped_error_rebuild_is_bitwise(dt, rank):
+    """With error feedback the 16-bit state keeps M' in the error's place and the next
+    call rebuilds E = rnd(M' - rnd(P Q^T)) from it. A state that is exported and
+    imported after every call holds the error itself and never rebuilds; both must
+    produce the same bits: outputs, errors and snapshots (the rows of 260, 77 and 3
+    floats take the aligned, unaligned and scalar paths; ranks 16 and 32 the matrix
+    cores)."""
+    log(f"case: wrapped {dt} rank {rank}, rebuilt error against the imported error")
+    hp = _hp(matrix_approximation_rank=rank)
+    decay = {16: 0.85, 32: 0.92}.get(rank)
+    a = PowerSGDState(**hp)
+    b = PowerSGDState(**hp)
+    for t in range(4):
+        x = _bucket(VIEWS, t, 40 + rank, rank, decay=decay).cuda()
+        xa, xb = x.clone(), x.clone()
+        a.compress_bucket_wrapped(xa, VIEWS, dt, bucket_index=2)
+        b.compress_bucket_wrapped(xb, VIEWS, dt, bucket_index=2)
+        torch.cuda.synchronize()
+        assert torch.equal(xa.view(torch.int32), xb.view(torch.int32)), t
+        blob = bytes(b.export_state())
+        b = PowerSGDState(**hp)
+        b.import_state(blob)
+        # a materializes its error from M'; b widens the 16-bit error it imported
+        for vi in range(len(VIEWS)):
+            try:
+                ea = a.error(2, vi)
+            except PowerSGDError:
+                continue  # not compressed
+            assert torch.equal(ea.view(torch.int32), b.error(2, vi).view(torch.int32)), (t, vi)
+        assert bytes(a.export_state()) == blob, t
+    log("  4 calls: outputs, errors and snapshots bitwise identical")
+
+
 # ------------------------------------------ the wrappers around batched_powerSGD_hook
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
