@@ -310,10 +310,10 @@ def algorithmic_bytes(cfg, comp_elems: int, per_elt_f32: float = 28.0):
 def moved_bytes(cfg, comp_elems: int):
     """Bytes the library actually moves per step: with error feedback the error memory's
     place keeps M' and the error is rebuilt from it, so pass 3 only writes M_hat. fp32
-    buckets: 12 + 4 + 4 per compressed element; fp16 buckets: the inf check of the whole
-    bucket first (2 per element), then 10 + 4 + 2, and the unscale of the uncompressed
-    views (2 + 2); the wrapped hook (16-bit M'): 8 + 2 + 4 and the cast of the
-    uncompressed views (4 + 4). Without error feedback: the algorithmic bytes."""
+    buckets: 12 + 4 + 4 per compressed element; fp16 buckets (M' in two alternating
+    places, the inf check inside pass 1): 10 + 4 + 2, and the check and unscale of the
+    uncompressed views (2 + 2 + 2); the wrapped hook (16-bit M'): 8 + 2 + 4 and the cast
+    of the uncompressed views (4 + 4). Without error feedback: the algorithmic bytes."""
     ef = bool(cfg.hparams.get("use_error_feedback", True))
     if cfg.wrap and ef:
         return comp_elems * 14 + (cfg.numel - comp_elems) * 8
@@ -321,7 +321,7 @@ def moved_bytes(cfg, comp_elems: int):
         if cfg.dtype == "f32":
             return comp_elems * 20
         unc = 0 if cfg.batched else cfg.numel - comp_elems
-        return cfg.numel * 2 + comp_elems * 16 + unc * 4
+        return comp_elems * 16 + unc * 6
     return algorithmic_bytes(cfg, comp_elems)
 
 

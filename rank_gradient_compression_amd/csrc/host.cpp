@@ -164,6 +164,12 @@ struct BucketPlan {
   // error in place: the device flag wflag says which, for the kernels)
   bool w_holds_e = true;
   int32_t* wflag = nullptr;  // device: non-zero while E's place holds the error itself
+  // fp32 state created by an fp16 call: E's place is two buffers wstride floats apart,
+  // the device index widx naming the current one; a step's pass 1 writes M' into the
+  // other and pass 3 of a step that ran switches them, so a step skipped for inf leaves
+  // M'_prev untouched without checking the bucket first (wstride 0: one buffer)
+  int32_t* widx = nullptr;
+  int64_t wstride = 0;
   float* Emat = nullptr;  // the materialized error for introspection and export
   bool allocated = false;
   bool q_ready = false;
@@ -179,7 +185,7 @@ struct BucketPlan {
   void release() {
     void* ptrs[] = {E, Eh, Mh, P, Praw, Ppart, Q, QT, partial, gram, tmat, d_pgram_tiles, d_qgram_tiles, d_td, d_td_scalar,
                     d_tiles1, d_tiles2, d_tiles3, d_tiles2r, d_flat_unc, d_flat_all, d_pjobs, d_qjobs,
-                    d_qinit, intro_E, intro_PQ, Emat, wflag};
+                    d_qinit, intro_E, intro_PQ, Emat, wflag, widx};
     for (void* p : ptrs)
       if (p) (void)hipFree(p);
     E = P = Praw = Ppart = Q = QT = partial = nullptr;
@@ -194,6 +200,8 @@ struct BucketPlan {
     d_qinit = nullptr;
     intro_E = intro_PQ = Emat = nullptr;
     wflag = nullptr;
+    widx = nullptr;
+    wstride = 0;
     intro_off.clear();
     allocated = false;
   }
@@ -513,7 +521,7 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
   return POWERSGD_OK;
 }
 
-powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
+powersgd_status allocate_plan(BucketPlan& pl, bool need_e, bool double_w, hipStream_t s) {
   auto alloc = [&](void** p, size_t bytes) -> bool {
     if (bytes == 0) {
       *p = nullptr;
@@ -523,8 +531,9 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   };
   bool ok = true;
   const bool h16 = pl.st != kStF32;
+  double_w = double_w && need_e && !h16 && pl.e_floats > 0;
   ok = ok && alloc(reinterpret_cast<void**>(&pl.E),
-                   (need_e && !h16) ? pl.e_floats * sizeof(float) : 0);
+                   (need_e && !h16) ? (double_w ? 2 : 1) * pl.e_floats * sizeof(float) : 0);
   ok = ok && alloc(reinterpret_cast<void**>(&pl.Eh),
                    (need_e && h16) ? pl.e_floats * sizeof(uint16_t) : 0);
   ok = ok && alloc(reinterpret_cast<void**>(&pl.Mh),
@@ -540,13 +549,16 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   ok = ok && alloc(reinterpret_cast<void**>(&pl.tmat),
                    pl.tensors.size() * static_cast<size_t>(pl.R) * pl.R * sizeof(double));
   ok = ok && alloc(reinterpret_cast<void**>(&pl.wflag), (pl.E || pl.Eh) ? sizeof(int32_t) : 0);
+  ok = ok && alloc(reinterpret_cast<void**>(&pl.widx), double_w ? sizeof(int32_t) : 0);
+  pl.wstride = double_w ? pl.e_floats : 0;
 
   if (!ok) {
     pl.release();
     return fail(POWERSGD_ERR_OOM, "device allocation of the bucket state failed");
   }
   hipError_t e = hipSuccess;
-  if (pl.E && e == hipSuccess) e = hipMemsetAsync(pl.E, 0, pl.e_floats * sizeof(float), s);
+  if (pl.E && e == hipSuccess)
+    e = hipMemsetAsync(pl.E, 0, (pl.wstride ? 2 : 1) * pl.e_floats * sizeof(float), s);
   if (pl.Eh && e == hipSuccess) e = hipMemsetAsync(pl.Eh, 0, pl.e_floats * sizeof(uint16_t), s);
   if (pl.Mh && e == hipSuccess) e = hipMemsetAsync(pl.Mh, 0, pl.e_floats * sizeof(uint16_t), s);
   if (pl.P && e == hipSuccess) e = hipMemsetAsync(pl.P, 0, pl.p_floats * sizeof(float), s);
@@ -555,6 +567,7 @@ powersgd_status allocate_plan(BucketPlan& pl, bool need_e, hipStream_t s) {
   if (pl.Q && e == hipSuccess) e = hipMemsetAsync(pl.Q, 0, pl.q_floats * sizeof(float), s);
   if (pl.QT && e == hipSuccess) e = hipMemsetAsync(pl.QT, 0, pl.qt_floats * sizeof(float), s);
   if (pl.wflag && e == hipSuccess) e = launch_set_flag(pl.wflag, 1, s);  // E = 0 in place
+  if (pl.widx && e == hipSuccess) e = launch_set_flag(pl.widx, 0, s);
 
   if (e != hipSuccess) {
     pl.release();
@@ -638,8 +651,8 @@ namespace {
 
 // The error of every tensor of a plan keeping M' in E's place, on stream s: E = M'_prev -
 // P Q^T with pass 3's rounding, or E's place as it is while the device flag says it holds
-// the error. Written as binary32 to dst (E's layout; an fp32 plan may pass pl.E itself),
-// or, for a 16-bit plan with dst NULL, back into E's place in 16 bits.
+// the error. Written as binary32 to dst (E's layout), or, with dst NULL, back into E's
+// current place (in 16 bits for a 16-bit plan).
 powersgd_status materialize_error(BucketPlan& pl, float* dst, hipStream_t s) {
   Pass3Args a{};
   a.tiles = pl.d_tiles3;
@@ -653,16 +666,19 @@ powersgd_status materialize_error(BucketPlan& pl, float* dst, hipStream_t s) {
   a.inv_scale = 1.0f;
   a.Eout = dst;
   a.wflag = pl.wflag;  // E's place may still hold the error itself (a skipped fp16 step)
+  a.widx = pl.widx;
+  a.wstride = pl.wstride;
   const hipError_t e = launch_error_materialize(pl.R, pl.st, a, s);
   if (e != hipSuccess) return hip_fail(e, "error materialization");
   return POWERSGD_OK;
 }
 
-// Device memory holding the error of a plan as binary32, E's layout: an fp32 plan's E's
-// place itself while it holds the error, else a copy materialized on stream s (a 16-bit
-// plan whose E's place holds the error is widened by the callers instead).
+// Device memory holding the error of a plan as binary32, E's layout: an fp32 plan's
+// single E's place itself while it holds the error, else a copy materialized on stream s
+// (which of two places is current is known on the device only; a 16-bit plan whose E's
+// place holds the error is widened by the callers instead).
 powersgd_status error_source(BucketPlan& pl, hipStream_t s, const float** out) {
-  if (pl.w_holds_e && pl.E) {
+  if (pl.w_holds_e && pl.E && pl.wstride == 0) {
     *out = pl.E;
     return POWERSGD_OK;
   }
@@ -876,7 +892,8 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     auto pl = std::make_unique<BucketPlan>();
     powersgd_status b = build_plan(hp, numel, batched, prec, std::move(keys), *pl);
     if (b != POWERSGD_OK) return b;
-    b = allocate_plan(*pl, ef, s);
+    // an fp16 bucket's fp32 state keeps M' in two alternating places
+    b = allocate_plan(*pl, ef, f16 && prec == kStF32, s);
     if (b != POWERSGD_OK) return b;
     it = st->buckets.emplace(bucket_index, std::move(pl)).first;
   }
@@ -900,7 +917,7 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
   if (ef && pl.keeps_mprime() && !pl.w_holds_e && nt > 0 && !hp.warm_start) {
     // this call cannot rebuild (a fresh Q draw replaces the Q it would need): the error
     // itself goes into E's place first
-    r = materialize_error(pl, pl.E, s);
+    r = materialize_error(pl, nullptr, s);
     if (r != POWERSGD_OK) return r;
     const hipError_t e = launch_set_flag(pl.wflag, 1, s);
     if (e != hipSuccess) return hip_fail(e, "error flag");
@@ -937,9 +954,10 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
       if (e != hipSuccess) return hip_fail(e, "padding fill");
     }
   }
-  // fp16 with M' kept in E's place: the inf check of every view comes first, so that a
-  // step to be skipped writes nothing (pass 1 would overwrite M'_prev).
-  const bool precheck = f16 && sm;
+  // fp16 with M' kept in a single E's place: the inf check of every view comes first, so
+  // that a step to be skipped writes nothing (pass 1 would overwrite M'_prev); with two
+  // places pass 1 checks the bucket as it reads it.
+  const bool precheck = f16 && sm && pl.wstride == 0;
   if (precheck) {
     const double all = static_cast<double>(pl.all_elems);
     r = timed_launch(st, s, K_UNSCALE, all * 2.0, "fp16 check", [&] {
@@ -964,6 +982,8 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.Ppart = pl.Ppart;
     a.Pe = sm ? pl.P : nullptr;  // the kernels skip the rebuild while wflag is set
     a.wflag = sm ? pl.wflag : nullptr;
+    a.widx = pl.widx;
+    a.wstride = pl.wstride;
     a.gram = pl.gram;
     a.Eh = pl.Eh;
     a.Mh = pl.mprime16();
@@ -1008,6 +1028,8 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.Mh = pl.mprime16();
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
+    a.widx = pl.widx;
+    a.wstride = pl.wstride;
     r = timed_launch(st, s, K_PASS2, ce * pass_bytes(K_PASS2, f16, ef, prec), "pass 2",
                      [&] {
                        return launch_pass2(R, f16, ef, prec, aligned && pl.all_wide, a, s);
@@ -1045,6 +1067,8 @@ powersgd_status run_call(powersgd_state* st, int64_t bucket_index, int32_t is_la
     a.inv_scale = inv_loss_scale;
     a.found_inf = found_inf_dev;
     a.wflag = sm ? pl.wflag : nullptr;  // cleared by the pass once the step runs
+    a.widx = pl.widx;                   // switched by the pass once the step runs
+    a.wstride = pl.wstride;
     const double bytes = ce * pass_bytes(K_PASS3, f16, ef, prec) +
                          (f16 ? ue * 4.0 : (prec != kStF32 ? ue * 8.0 : 0.0));
     r = timed_launch(st, s, K_PASS3, bytes, "pass 3",
@@ -1654,7 +1678,8 @@ void write_snapshot(const powersgd_state* st, SnapWriter& w, ExportCopies* copie
                 ExportCopies::EPiece{ebuf, d.eoff, static_cast<int64_t>(d.n) * d.m, pl.st, dst});
           else
             copies->segs.push_back(
-                CopySeg{(pl.w_holds_e ? pl.E : pl.Emat) + d.eoff, dst, bytes});
+                CopySeg{(pl.w_holds_e && pl.wstride == 0 ? pl.E : pl.Emat) + d.eoff, dst,
+                        bytes});
         }
       }
       if (has_q) {
@@ -1750,7 +1775,8 @@ powersgd_status upload_bucket(const powersgd_hparams& hp, SnapBucket& sb, hipStr
                               std::list<std::vector<float>>& keep,
                               std::list<std::vector<uint16_t>>& keep16) {
   BucketPlan& pl = *sb.plan;
-  powersgd_status r = allocate_plan(pl, hp.use_error_feedback != 0, s);
+  // one E's place (a later fp16 call then checks the bucket before pass 1)
+  powersgd_status r = allocate_plan(pl, hp.use_error_feedback != 0, false, s);
   if (r != POWERSGD_OK) return r;
   const int prec = pl.st;
   std::vector<uint16_t>* eh = nullptr;  // a 16-bit E, rounded from the snapshot's binary32
@@ -1821,7 +1847,7 @@ powersgd_status powersgd_state_export(powersgd_state* st, void* host_buf, int64_
   // buckets whose E's place holds M': their error, materialized for the copies
   for (auto& kv : st->buckets) {
     BucketPlan& pl = *kv.second;
-    if (pl.keeps_mprime() && !pl.w_holds_e) {
+    if (pl.keeps_mprime() && (!pl.w_holds_e || pl.wstride != 0)) {
       const float* src = nullptr;
       powersgd_status r = error_source(pl, s, &src);
       if (r != POWERSGD_OK) return r;

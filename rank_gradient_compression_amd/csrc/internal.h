@@ -117,6 +117,11 @@ struct Pass1Args {
   // With Pe: device flag, non-zero while E's place still holds the error itself (then
   // nothing is rebuilt); pass 3 of a step that ran clears it.
   const int32_t* wflag;
+  // E's place double-buffered (an fp16 bucket's M'): two places wstride floats apart,
+  // *widx (0 or 1) naming the current one (M'_prev or the error); pass 1 writes M' into
+  // the other. wstride 0: one place, read and overwritten in place (widx unused).
+  const int32_t* widx;
+  int64_t wstride;
   const float* QT;         // matrix-core ranks: Q^T (B fragments as 16-byte loads)
   double* gram;            // P Gram partials (ranks <= 8: computed here)
   uint16_t* Eh;            // 16-bit state: E's place (E's offsets)
@@ -142,6 +147,8 @@ struct Pass2Args {
   const uint16_t* Mh;      // 16-bit state: M' (E's offsets; E's place with error feedback)
   float inv_scale;
   const int32_t* found_inf;
+  const int32_t* widx;     // E's places as in Pass1Args; M' is read from the one pass 1
+  int64_t wstride;         // wrote
 };
 
 // Sum of pass-2 partial slots: one work item per (tensor, column block).
@@ -170,13 +177,18 @@ struct Pass3Args {
   const uint16_t* Mh;      // 16-bit state: M' (E's offsets; Eh itself with error feedback)
   float inv_scale;
   const int32_t* found_inf;
-  // error materialization: E = M' - P Q^T written here as binary32 (E's offsets); a
-  // 16-bit state with Eout null writes it back into Eh in 16 bits
+  // error materialization: E = M' - P Q^T written here as binary32 (E's offsets); with
+  // Eout null it goes back into E's current place (in 16 bits into Eh for a 16-bit
+  // state)
   float* Eout;
   // Buckets keeping M' in E's place: the device flag that says E's place still holds the
   // error itself. Pass 3 of a step that ran clears it; the materialization reads it (set:
   // the error is copied as it is). Null: E's place holds M'.
   int32_t* wflag;
+  // E's places as in Pass1Args: pass 3 of a step that ran makes the place pass 1 wrote
+  // the current one; the materialization reads the current one.
+  int32_t* widx;
+  int64_t wstride;
 };
 
 // Precision of the state a bucket keeps: kStF32 for the hook on fp32 or fp16 buckets;
@@ -198,10 +210,10 @@ hipError_t launch_pass2(int R, bool f16, bool ef, int st, bool wide_only, const 
 hipError_t launch_pass2_reduce(int R, int st, const Pass2ReduceArgs& a, hipStream_t s);
 hipError_t launch_pass3(int R, bool f16, bool ef, int st, const Pass3Args& a, hipStream_t s);
 // A state with error feedback (precision st): the error E = M' - P Q^T of every tensor,
-// from the M' kept in E's place (a.E, or a.Mh = a.Eh for a 16-bit state) and the step's
-// P and Q, into a.Eout (binary32, E's layout; may be a.E) or, for a 16-bit state with
-// a.Eout null, back into a.Eh, with pass 3's tiling and arithmetic, so the values are
-// the ones pass 3's M_hat implies.
+// from the M' kept in E's current place (in a.E, or a.Mh = a.Eh for a 16-bit state) and
+// the step's P and Q, into a.Eout (binary32, E's layout) or, with a.Eout null, back into
+// E's current place, with pass 3's tiling and arithmetic, so the values are the ones
+// pass 3's M_hat implies.
 hipError_t launch_error_materialize(int R, int st, const Pass3Args& a, hipStream_t s);
 // *flag = value (one thread; no memset node, so it can sit in a captured graph).
 hipError_t launch_set_flag(int32_t* flag, int32_t value, hipStream_t s);

@@ -616,25 +616,38 @@ __device__ __forceinline__ bool holds_error(const Pass3Args& a) {
   return a.wflag != nullptr && *a.wflag != 0;
 }
 
+// Offset (floats) of E's current place, holding M'_prev (or the error): 0 for one
+// buffer; with two (wstride apart, an fp16 bucket's double-buffered M') the one *widx
+// names. A step's pass 1 writes M' into the other place, wstride - w_cur.
+__device__ __forceinline__ int64_t w_cur(const int32_t* widx, int64_t wstride) {
+  return (wstride != 0 && *widx != 0) ? wstride : 0;
+}
+
 // Pass 3 of a step that ran (after its inf check) marks E's place as holding M': one
 // lane of workgroup 0 (a vector store).
 template <bool F16, bool EF, int ST, bool MAT>
 __device__ __forceinline__ void mark_mprime(const Pass3Args& a) {
   if constexpr (stored_mprime<F16, EF, ST>() && !MAT) {
-    if (a.wflag != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *a.wflag = 0;
+    if (a.wflag != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
+      *a.wflag = 0;
+      // double-buffered M': the place pass 1 wrote becomes the current one
+      if (a.wstride != 0) *a.widx = 1 - *a.widx;
+    }
   }
 }
 
 // A materialized error (4 values from element off of E's layout): binary32 into Eout,
-// or, for a 16-bit state called without Eout, back into E's place in its 16 bits.
+// or, called without Eout, back into E's current place (wc: its offset), in 16 bits for
+// a 16-bit state.
 template <int ST, int LD>
-__device__ __forceinline__ void store_materialized(const Pass3Args& a, int64_t off, int valid,
-                                                   const float (&e)[4]) {
-  if constexpr (ST != kStF32) {
-    if (a.Eout == nullptr) {
+__device__ __forceinline__ void store_materialized(const Pass3Args& a, int64_t wc, int64_t off,
+                                                   int valid, const float (&e)[4]) {
+  if (a.Eout == nullptr) {
+    if constexpr (ST != kStF32)
       st_h4<ST, LD>(a.Eh + off, valid, e);
-      return;
-    }
+    else
+      st_f32x4<LD>(a.E + wc + off, valid, e);
+    return;
   }
   st_f32x4<LD>(a.Eout + off, valid, e);
 }
@@ -736,7 +749,11 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
   const int r0 = t.a * d.rpb1;
   const int r1 = min(d.n, r0 + d.rpb1);
   const float* __restrict__ Qt = args.Q + d.qoff;
-  float* __restrict__ Et = args.E + d.eoff;
+  // E's current place holds M'_prev (or the error); M' goes to the other place (the
+  // same one with a single buffer)
+  const int64_t wc = w_cur(args.widx, args.wstride);
+  const float* __restrict__ Ein = args.E + d.eoff + wc;
+  float* __restrict__ Eout = args.E + d.eoff + (args.wstride - wc);
   constexpr bool SM = stored_mprime<F16, EF, ST>();
   // E's place holds M'_prev: rebuild E = M'_prev - Pe Q^T (Q is the warm-start Q)
   const bool rebuild = SM && rebuild_error(args);
@@ -802,7 +819,7 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
       } else if constexpr (EF) {
         float e[U][4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) ld_f32x4<LD>(Et + rbase[u] + c, valid, e[u]);
+        for (int u = 0; u < U; ++u) ld_f32x4<LD>(Ein + rbase[u] + c, valid, e[u]);
         if (rebuild) {
 #pragma unroll
           for (int u = 0; u < U; ++u) {
@@ -816,7 +833,7 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
         for (int u = 0; u < U; ++u) {
 #pragma unroll
           for (int a = 0; a < 4; ++a) x[u][a] += e[u][a];
-          if (rok[u]) st_f32x4<LD>(Et + rbase[u] + c, valid, x[u]);  // M' in E's place
+          if (rok[u]) st_f32x4<LD>(Eout + rbase[u] + c, valid, x[u]);  // M' in E's place
         }
       }
 #pragma unroll
@@ -921,7 +938,8 @@ __global__ void __launch_bounds__(kThreads) k_pass1(Pass1Args args) {
   __shared__ float red[kPass1SlotSums * R];
   __shared__ double gred[kThreads / 64][pass1_ng<R>()];
   if constexpr (F16 && stored_mprime<F16, EF, ST>()) {
-    // the bucket's inf check ran before this pass: a skipped step writes nothing
+    // a step already known to be skipped (the bucket's check ran before this pass, or,
+    // with two E places, another workgroup of it found inf) needs none of its results
     if (*args.found_inf) return;
   }
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
@@ -1486,7 +1504,10 @@ __device__ __forceinline__ void pass2_body(const Pass2Args& args, const TensorDe
   const int r1 = min(d.n, r0 + d.rpb);
   const int stride = 4 * L.rpw;
   const int rw0 = r0 + wave * L.rpw;
-  const float* __restrict__ Et = args.E + d.eoff;
+  // the step's M' (pass 1 wrote it to the place other than E's current one, which is
+  // the same place with a single buffer)
+  const float* __restrict__ Et =
+      args.E + d.eoff + (args.wstride - w_cur(args.widx, args.wstride));
   // lanes past the last column load (and then ignore) an in-range group, so the first
   // loads need no branch and the wait counts stay exact: the row's last 4 elements
   // (m >= 4; valid = 4 keeps the unaligned access from shifting further back) or its
@@ -1777,7 +1798,8 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
   const int r1 = min(d.n, r0 + d.rpb3);
   const int stride = 4 * L.rpw;
   const float* __restrict__ Pt = args.P + d.poff;
-  float* __restrict__ Et = args.E + d.eoff;
+  const int64_t wc = MAT ? w_cur(args.widx, args.wstride) : 0;
+  const float* __restrict__ Et = args.E + d.eoff + wc;  // M' (materialization)
   for (int rw = r0 + wave * L.rpw; rw < r1; rw += stride * U) {
     float x[U][4];
     float p[U][R];
@@ -1807,7 +1829,7 @@ __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDe
         float e[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) e[a] = we ? x[u][a] : rebuilt_error<ST>(x[u][a], mh[a]);
-        store_materialized<ST, LD>(args, d.eoff + off, L.valid, e);
+        store_materialized<ST, LD>(args, wc, d.eoff + off, L.valid, e);
         continue;
       }
       if constexpr (F16)
@@ -1895,7 +1917,10 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
   const int row = r0 + cl;
   const bool row_ok = row < r1;
   const int rowc = min(row, r1 - 1);
-  float* __restrict__ Et = args.E + d.eoff;
+  // M'_prev (or the error) from E's current place, M' to the other one
+  const int64_t wc = w_cur(args.widx, args.wstride);
+  const float* __restrict__ Ein = args.E + d.eoff + wc;
+  float* __restrict__ Eout = args.E + d.eoff + (args.wstride - wc);
   const float* __restrict__ QTt = args.QT + d.qtoff;
   constexpr bool SM = stored_mprime<F16, EF, ST>();
   constexpr int KQ = R / 4;
@@ -1937,7 +1962,7 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
         if constexpr (EF && ST != kStF32)
           ld_h4<ST, kLdAligned>(args.Eh + d.eoff + off, 4, e[u]);
         else if constexpr (EF)
-          load_f4(Et + off, e[u]);
+          load_f4(Ein + off, e[u]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           load_f4(QTt + static_cast<int64_t>(16 * nt + cl) * d.mstride + colc, b[u][nt]);
@@ -1953,7 +1978,7 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
           if constexpr (EF && ST != kStF32)
             ld_h4<ST, kLdScalar>(args.Eh + d.eoff + off, m - col, e[u]);
           else if constexpr (EF)
-            load_f32x4(Et + off, false, m - col, e[u]);
+            load_f32x4(Ein + off, false, m - col, e[u]);
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -2012,7 +2037,7 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
                                  x[u]);
         }
       } else if constexpr (SM) {
-        if (ok[u]) store_f32x4(Et + static_cast<int64_t>(row) * m + col, VEC, m - col, x[u]);
+        if (ok[u]) store_f32x4(Eout + static_cast<int64_t>(row) * m + col, VEC, m - col, x[u]);
       }
     }
 #pragma unroll
@@ -2075,7 +2100,10 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
   // the work item's column group: columns c0 .. c1 - 1 (its P is a partial sum)
   const int c0 = t.b * kPass1Cols;
   const int c1 = min(m, c0 + kPass1Cols);
-  float* __restrict__ Et = args.E + d.eoff;
+  // M'_prev (or the error) from E's current place, M' to the other one
+  const int64_t wc = w_cur(args.widx, args.wstride);
+  const float* __restrict__ Ein = args.E + d.eoff + wc;
+  float* __restrict__ Eout = args.E + d.eoff + (args.wstride - wc);
   const float* __restrict__ QTt = args.QT + d.qtoff;
   constexpr bool SM = stored_mprime<F16, EF, ST>();
   constexpr int KQ = R / 4;
@@ -2182,7 +2210,7 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
       if constexpr (EF && ST != kStF32)
         ld_h4<ST, kLdAligned>(args.Eh + d.eoff + rbase[i] + colc, 4, xe[i]);
       else if constexpr (EF)
-        load_f4(Et + rbase[i] + colc, xe[i]);
+        load_f4(Ein + rbase[i] + colc, xe[i]);
     }
   };
   load_rows(c0);
@@ -2222,7 +2250,7 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
       if constexpr (ST != kStF32) {
         if (rok[i] && cok) st_h4<ST, kLdAligned>(args.Mh + d.eoff + rbase[i] + col, 4, v);
       } else if constexpr (SM) {
-        if (rok[i] && cok) store_f32x4(Et + rbase[i] + col, true, 4, v);  // M' in E's place
+        if (rok[i] && cok) store_f32x4(Eout + rbase[i] + col, true, 4, v);  // M' in E's place
       }
       *reinterpret_cast<float4*>(tile + (RW * wave + i) * LS + 4 * lane) =
           make_float4(v[0], v[1], v[2], v[3]);
@@ -2307,7 +2335,8 @@ __global__ void __launch_bounds__(kThreads) k_pass1_mfma(Pass1Args args) {
   float* red = tile;
   const int lane = threadIdx.x & 63;
   if constexpr (F16 && stored_mprime<F16, EF, ST>()) {
-    // the bucket's inf check ran before this pass: a skipped step writes nothing
+    // a step already known to be skipped (the bucket's check ran before this pass, or,
+    // with two E places, another workgroup of it found inf) needs none of its results
     if (*args.found_inf) return;
   }
   if (static_cast<int>(blockIdx.x) >= args.ntiles) {
@@ -2348,7 +2377,9 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
   const bool col_ok = col < m;
   const int colc = VEC ? min(col, m - 4) : col;
   const float* __restrict__ Pt = args.P + d.poff;
-  const float* __restrict__ Et = args.E + d.eoff;
+  // the step's M' (the place pass 1 wrote)
+  const float* __restrict__ Et =
+      args.E + d.eoff + (args.wstride - w_cur(args.widx, args.wstride));
   mfma_f4 acc[4][NT];
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4)
@@ -2370,12 +2401,6 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
         } else {
           bool rb;
           load_grad4_vec<F16>(args.bucket, d.boff + off, args.inv_scale, x[u], rb);
-          if constexpr (F16 && EF) {
-            float e[4];
-            load_f4(Et + off, e);
-#pragma unroll
-            for (int a = 0; a < 4; ++a) x[u][a] += e[a];
-          }
         }
       } else {
         if (row < r1 && col_ok) {
@@ -2614,7 +2639,8 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
   if (c0 >= m) return;
   const float* __restrict__ Pt = args.P + d.poff;
   const float* __restrict__ Qt = args.Q + d.qoff;
-  float* __restrict__ Et = args.E + d.eoff;
+  const int64_t wc = MAT ? w_cur(args.widx, args.wstride) : 0;
+  const float* __restrict__ Et = args.E + d.eoff + wc;  // M' (materialization)
   float qa[4][KQ];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -2678,7 +2704,8 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
 #pragma unroll
             for (int a = 0; a < 4; ++a)
               e[a] = we ? x[ur][g][a] : rebuilt_error<ST>(x[ur][g][a], mh[a]);
-            store_materialized<ST, VEC ? kLdAligned : kLdScalar>(args, d.eoff + off, m - col, e);
+            store_materialized<ST, VEC ? kLdAligned : kLdScalar>(args, wc, d.eoff + off, m - col,
+                                                                 e);
             continue;
           }
           if constexpr (F16)
@@ -2723,7 +2750,8 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
   const int crc = min(cr, m - 4);
   const float* __restrict__ Pt = args.P + d.poff;
   const float* __restrict__ Qt = args.Q + d.qoff;
-  float* __restrict__ Et = args.E + d.eoff;
+  const int64_t wc = MAT ? w_cur(args.widx, args.wstride) : 0;
+  const float* __restrict__ Et = args.E + d.eoff + wc;  // M' (materialization)
   float qa[4][KQ];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -2794,7 +2822,7 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
           float e[4];
 #pragma unroll
           for (int a = 0; a < 4; ++a) e[a] = we ? x[i][a] : rebuilt_error<ST>(x[i][a], mh[a]);
-          store_materialized<ST, kLdAligned>(args, d.eoff + off, 4, e);
+          store_materialized<ST, kLdAligned>(args, wc, d.eoff + off, 4, e);
           continue;
         }
         if constexpr (F16)

@@ -223,6 +223,52 @@ def test_fp16_skip_right_after_an_import():
         assert rep.found_inf == (step == 2)
 
 
+@pytest.mark.parametrize("rank", [2, 32])
+def test_fp16_two_mprime_places_match_one_checked_place(rank):
+    """A state whose bucket plan was created by an fp16 call keeps M' in two
+    alternating places and checks the bucket inside pass 1; a state restored from a
+    snapshot keeps one place and checks the bucket before pass 1. Both must give the
+    same bits through steps skipped for inf (two of them in a row) and the steps after
+    them: outputs, found_inf, errors and snapshots. Rows of 160, 64, 77 and 2100 values
+    take the aligned, unaligned and (rank 32) several-column-group paths."""
+    log(f"case: fp16, r={rank}, two M' places against one, inf at steps 2, 3 and 5")
+    shapes = [(96, 160), (40,), (300, 64), (130, 77), (40, 2100)]
+    views = packed_views(shapes)
+    hp = _hp(matrix_approximation_rank=rank, min_compression_rate=1.0)
+    scale = 2.0 ** -10
+    bad = {2, 3, 5}
+    a = PowerSGDState(**hp)
+    b = None
+    for step in range(7):
+        x = _rand_bucket(shapes, 500 + step, scale=50.0)
+        if step in bad:
+            x[11 + 3 * step] = float("inf")
+        xh = x.to(torch.float16).cuda()
+        if step == 1:
+            b = PowerSGDState(**hp)
+            b.import_state(a.export_state())
+        outs = []
+        for st in (a, b) if b is not None else (a,):
+            xs = xh.clone()
+            fi = torch.zeros(1, dtype=torch.int32, device="cuda")
+            st.compress_bucket(xs, views, inv_loss_scale=scale, found_inf=fi)
+            outs.append((xs, fi))
+        torch.cuda.synchronize()
+        assert outs[0][1].item() == (1 if step in bad else 0), step
+        if b is None:
+            continue
+        (xa, fa), (xb, fb) = outs
+        assert fa.item() == fb.item(), step
+        assert torch.equal(xa.view(torch.int16), xb.view(torch.int16)), step
+        for vi, (_, shp) in enumerate(views):
+            if len(shp) < 2:
+                continue
+            assert torch.equal(a.error(0, vi).view(torch.int32),
+                               b.error(0, vi).view(torch.int32)), (step, vi)
+        assert a.export_state() == b.export_state(), step
+    log("  7 steps: outputs, found_inf, errors and snapshots bitwise identical")
+
+
 def test_misaligned_bucket_base_pointer():
     log("case: bucket starts 1 element into an allocation (scalar path)")
     shapes = [(64, 64), (48, 100), (7,)]
