@@ -135,7 +135,11 @@ POWERSGD_API void powersgd_state_destroy(powersgd_state* st);
  *                 into it when any view element is inf or NaN, and skips everything
  *                 (bucket, error memory and Q left bit-identical) when the flag is
  *                 non-zero after the check; the caller zeroes it before the first
- *                 bucket of an iteration. Never read back on the host here.
+ *                 bucket of an iteration. Never read back on the host here. With
+ *                 error feedback a bucket first called with F16 keeps its error
+ *                 memory in two alternating fp32 places (8 bytes per compressed
+ *                 element) so that the check runs inside the first pass; a bucket
+ *                 restored by powersgd_state_import keeps one and checks first.
  *   stream        hipStream_t (NULL = the legacy default stream).
  *
  * While iteration < start_powerSGD_iter the call is the vanilla allreduce: F32 is a

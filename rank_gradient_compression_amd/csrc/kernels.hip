@@ -15,9 +15,11 @@
 //           wrappers' 16-bit states): with the step's P and Q (which the state keeps
 //           anyway) the error is rebuilt exactly, as E = M'_prev - P Q^T with the very
 //           arithmetic and rounding pass 3 uses for M_hat. Pass 3 then only writes
-//           M_hat. A device flag says when E's place still holds the error itself;
-//           fp16 buckets check the whole bucket for inf first, so a skipped step
-//           writes nothing.
+//           M_hat. A device flag says when E's place still holds the error itself.
+//           An fp16 step skipped for inf must leave M'_prev intact: its plan keeps
+//           M' in two alternating places (a device index names the current one; pass
+//           1 writes the other, pass 3 of a step that ran switches them), or, with
+//           one place, the whole bucket is checked before pass 1.
 //   pass 1  M' = G (+ E), the error rebuilt from M'_prev and M' written over it;
 //           P = M' Q. Vector ranks: a workgroup owns whole rows, so each dot product is
 //           finished inside it (shuffles, then LDS across wavefronts); matrix-core
