@@ -754,8 +754,9 @@ __device__ __forceinline__ void pass1_body(const Pass1Args& args, const TensorDe
   // E's current place holds M'_prev (or the error); M' goes to the other place (the
   // same one with a single buffer)
   const int64_t wc = w_cur(args.widx, args.wstride);
-  const float* __restrict__ Ein = args.E + d.eoff + wc;
-  float* __restrict__ Eout = args.E + d.eoff + (args.wstride - wc);
+  float* __restrict__ Ebase = args.E + d.eoff;  // both places derive from it (they may be one)
+  const float* Ein = Ebase + wc;
+  float* Eout = Ebase + (args.wstride - wc);
   constexpr bool SM = stored_mprime<F16, EF, ST>();
   // E's place holds M'_prev: rebuild E = M'_prev - Pe Q^T (Q is the warm-start Q)
   const bool rebuild = SM && rebuild_error(args);
@@ -1921,8 +1922,9 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
   const int rowc = min(row, r1 - 1);
   // M'_prev (or the error) from E's current place, M' to the other one
   const int64_t wc = w_cur(args.widx, args.wstride);
-  const float* __restrict__ Ein = args.E + d.eoff + wc;
-  float* __restrict__ Eout = args.E + d.eoff + (args.wstride - wc);
+  float* __restrict__ Ebase = args.E + d.eoff;  // both places derive from it (they may be one)
+  const float* Ein = Ebase + wc;
+  float* Eout = Ebase + (args.wstride - wc);
   const float* __restrict__ QTt = args.QT + d.qtoff;
   constexpr bool SM = stored_mprime<F16, EF, ST>();
   constexpr int KQ = R / 4;
@@ -2104,8 +2106,9 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
   const int c1 = min(m, c0 + kPass1Cols);
   // M'_prev (or the error) from E's current place, M' to the other one
   const int64_t wc = w_cur(args.widx, args.wstride);
-  const float* __restrict__ Ein = args.E + d.eoff + wc;
-  float* __restrict__ Eout = args.E + d.eoff + (args.wstride - wc);
+  float* __restrict__ Ebase = args.E + d.eoff;  // both places derive from it (they may be one)
+  const float* Ein = Ebase + wc;
+  float* Eout = Ebase + (args.wstride - wc);
   const float* __restrict__ QTt = args.QT + d.qtoff;
   constexpr bool SM = stored_mprime<F16, EF, ST>();
   constexpr int KQ = R / 4;
