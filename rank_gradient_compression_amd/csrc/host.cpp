@@ -482,7 +482,10 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
     if (fused_gram) rpb = std::min<int64_t>(rpb, kPass2StageFloats / R);
     d.rpb = static_cast<int32_t>(rpb);
     d.nrb = static_cast<int32_t>((d.n + rpb - 1) / rpb);
-    d.rpb3 = static_cast<int32_t>(row_block(target));
+    // vector ranks: every pass-3 work item first sums the pass-2 partial slots of its
+    // column block, so taller items pay that less often
+    d.rpb3 = static_cast<int32_t>(
+        row_block(R <= kMaxFusedGramRank ? target * PSGD_PASS3_TILE_SCALE : target));
     const int32_t nrb3 = (d.n + d.rpb3 - 1) / d.rpb3;
     d.ncb = static_cast<int32_t>((d.m + kColBlock - 1) / kColBlock);
     if (d.nrb > 1) {

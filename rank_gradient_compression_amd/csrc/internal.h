@@ -274,6 +274,9 @@ hipError_t launch_unscale_only(const FlatTile* ftiles, int nftiles, void* bucket
 #ifndef PSGD_PASS2_TILE_SCALE
 #define PSGD_PASS2_TILE_SCALE 4  // pass-2 work items this many times larger (vector ranks)
 #endif
+#ifndef PSGD_PASS3_TILE_SCALE
+#define PSGD_PASS3_TILE_SCALE 4  // pass-3 work items this many times taller (vector ranks)
+#endif
 
 // Rows loaded per thread before use in pass 1 (P = M' Q), by padded rank.
 constexpr int pass1_unroll(int R) { return R <= 4 ? PSGD_PASS1_ROWS : 1; }
