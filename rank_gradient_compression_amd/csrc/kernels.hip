@@ -20,7 +20,8 @@
 //           M' in two alternating places (a device index names the current one; pass
 //           1 writes the other, pass 3 of a step that ran switches them), or, with
 //           one place, the whole bucket is checked before pass 1.
-//   pass 1  M' = G (+ E), the error rebuilt from M'_prev and M' written over it;
+//   pass 1  M' = G (+ E), the error rebuilt from M'_prev and M' written over it (or
+//           into the other place);
 //           P = M' Q. Vector ranks: a workgroup owns whole rows, so each dot product is
 //           finished inside it (shuffles, then LDS across wavefronts); matrix-core
 //           ranks: 32 rows x 2048 columns per workgroup, a partial P per column group,
@@ -576,8 +577,7 @@ __device__ __forceinline__ void store_p_row(float* __restrict__ Pt, int row,
 
 // M_hat = P Q^T for 4 consecutive columns of one row (vector ranks): one fused
 // multiply-add chain in rank order per value. Pass 3 writes these values and the error
-// memory of an fp32 state is rebuilt from them (E = M' - M_hat), so every user computes
-// them here.
+// memory is rebuilt from them (E = M' - M_hat), so every user computes them here.
 template <int R>
 __device__ __forceinline__ void mhat4(const float (&p)[R], const float (&q)[4][R],
                                       float (&mh)[4]) {
@@ -1776,11 +1776,11 @@ __device__ __forceinline__ void pass3_q_from_partials(const Pass3Args& args, con
   }
 }
 
-// M_hat = P Q^T into the bucket and E = M' - M_hat over one tile. All loads of an
-// iteration come from rows clamped into the tile; stores are kept to real rows. An fp32
-// state with error feedback writes M_hat only (its error is rebuilt from M' and the
-// factors); MAT (the error materialization) writes E = M' - M_hat to Eout instead of
-// M_hat to the bucket, with the same M_hat.
+// M_hat = P Q^T into the bucket over one tile. All loads of an iteration come from rows
+// clamped into the tile; stores are kept to real rows. With error feedback the error is
+// not written (the next pass 1 rebuilds it from M' and the factors); MAT (the error
+// materialization) writes E = M' - M_hat to Eout (or E's place) instead of M_hat to the
+// bucket, with the same M_hat.
 template <int R, int U, bool F16, bool EF, int LD, bool WIDE, int ST, bool MAT = false>
 __device__ __forceinline__ void pass3_body(const Pass3Args& args, const TensorDesc& d,
                                            const Tile& t, float* qred) {
@@ -2623,8 +2623,9 @@ __global__ void __launch_bounds__(kThreads) k_pass2_mfma(Pass2Args args) {
   pass2_mfma_body<R, F16, EF, false, ST>(args, d, t, lane, wave);
 }
 
-// Pass 3, M_hat = P Q^T and E = M' - M_hat, computed as (Q P^T)^T so that lane l
-// holds 4 consecutive columns (4h..4h+3) of row cl of each 16 x 16 output block.
+// Pass 3, M_hat = P Q^T (or, materializing, E = M' - M_hat), computed as (Q P^T)^T so
+// that lane l holds 4 consecutive columns (4h..4h+3) of row cl of each 16 x 16 output
+// block.
 // MFMA K-step kq of lane group h uses rank index h * KQ + kq, so A and B fragments are
 // KQ consecutive floats of a Q row and of a P row.
 template <int R, bool F16, bool EF, bool VEC, int ST, bool MAT = false>
@@ -2727,9 +2728,9 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
 // each 32-row step the wavefronts compute their 16 x 16 blocks of M_hat = (Q P^T)^T as
 // above (wavefront w: columns 64w..64w+63 of the 256-column block) into an LDS tile of
 // 32 rows x 256 columns; after a barrier wavefront w takes rows 8w..8w+7 of the tile,
-// lane l columns 4l..4l+3, so M' loads and the M_hat and E stores cover 1 KB of one
-// row per instruction instead of 64 bytes of 16 rows. The step's M' rows are
-// requested before its MFMAs.
+// lane l columns 4l..4l+3, so the M_hat stores (and, materializing the error, the M'
+// loads and E stores) cover 1 KB of one row per instruction instead of 64 bytes of 16
+// rows. The step's M' rows are requested before its MFMAs.
 constexpr int kPass3TileStride = kColBlock + 4;  // LDS row stride (floats), padded
 
 template <int R, bool F16, bool EF, int ST, bool MAT = false>
