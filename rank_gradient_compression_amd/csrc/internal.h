@@ -296,7 +296,7 @@ constexpr int kMfmaPass1Rows = 32;
 // Matrix-core pass 1 splits rows into groups of this many columns (the work items of a
 // row block run side by side, so the running workgroups read neighbouring rows); each
 // writes a partial P, summed in the Gram kernel.
-constexpr int kPass1Cols = 2048;
+constexpr int kPass1Cols = 4096;
 constexpr int kMfmaRowBlock = 1024;
 // Matrix-core pass 2 row blocks: twice the pass-3 ones, half the Q partial slots to
 // write and to sum.

@@ -24,7 +24,7 @@
 //           into the other place);
 //           P = M' Q. Vector ranks: a workgroup owns whole rows, so each dot product is
 //           finished inside it (shuffles, then LDS across wavefronts); matrix-core
-//           ranks: 32 rows x 2048 columns per workgroup, a partial P per column group,
+//           ranks: 32 rows x 4096 columns per workgroup, a partial P per column group,
 //           summed by the Gram kernel. fp16: x * inv_scale (and an OR of "not finite"
 //           into found_inf when no check ran before).
 //   orth    Gram-Schmidt with epsilon on P (and on the initial Q draw), run on the

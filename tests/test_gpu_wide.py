@@ -81,11 +81,12 @@ def test_wide_wrapped_stepwise(dt, rank, shapes):
             + f" (tol {tol:.1e})")
 
 
-# Matrix-core ranks split each 32-row block into groups of 2048 columns whose partial P
-# are summed in the Gram kernel: two and three groups with a short last one (2052,
-# 4608, 2060 columns), rows that are not 16-byte multiples (4099 and 6150 columns: the
-# scalar-access body, also split into groups), several row blocks with a ragged tail.
-MC_WIDE = [(77, 4608), (64,), (40, 2052), (96, 4099), (9,), (300, 6150), (2100, 2060)]
+# Matrix-core ranks split each 32-row block into groups of 4096 columns whose partial P
+# are summed in the Gram kernel: two and three groups with a short last one (4608 and
+# 8452 columns), rows that are not 16-byte multiples (4099 and 6150 columns: the
+# scalar-access body, also split into groups), one group over several row blocks with
+# a ragged tail (2100 x 2060).
+MC_WIDE = [(77, 4608), (64,), (40, 8452), (96, 4099), (9,), (300, 6150), (2100, 2060)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
