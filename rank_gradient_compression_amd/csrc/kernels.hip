@@ -1894,6 +1894,25 @@ __device__ __forceinline__ mfma_f4 mfma16(float a, float b, mfma_f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// The 16-bit matrix cores (v_mfma_f32_16x16x16 f16, or bf16_1k) for values that are
+// exact in the state's 16 bits: lane l supplies A[l%16][4(l/16)..4(l/16)+3] and
+// B[4(l/16)..4(l/16)+3][l%16], four 16-bit values in two registers (the first in the
+// low half); D as above. The products are exact, so the result differs from four
+// v_mfma_f32_16x16x4f32 steps over the same values only in the fp32 accumulation.
+typedef short mfma_s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 mfma_h16x4 __attribute__((ext_vector_type(4)));
+
+template <int ST>
+__device__ __forceinline__ mfma_f4 mfma16x16x16(uint2 a, uint2 b, mfma_f4 c) {
+  if constexpr (ST == kStBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mfma_s16x4, a),
+                                                     __builtin_bit_cast(mfma_s16x4, b), c, 0, 0,
+                                                     0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(mfma_h16x4, a),
+                                                 __builtin_bit_cast(mfma_h16x4, b), c, 0, 0, 0);
+}
+
 // Pass 1, P = M' Q, for rows that are not 16-byte aligned (or a bucket that is not): the
 // 16-row group grp of the work item's rows, over its column group. Wavefront w takes
 // the 64-column chunks w, w + 4, w + 8, ... of the group (U = 4 K-steps of 16 columns
@@ -2045,11 +2064,23 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      if constexpr (ST != kStF32) {
+        // a 16-bit state's M' and Q are exact in 16 bits: one K = 16 step
+        const uint2 a = make_uint2(pack_h16x2<ST>(x[u][0], x[u][1]), pack_h16x2<ST>(x[u][2], x[u][3]));
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint2 bb = make_uint2(pack_h16x2<ST>(b[u][nt][0], b[u][nt][1]),
+                                      pack_h16x2<ST>(b[u][nt][2], b[u][nt][3]));
+          acc[nt] = mfma16x16x16<ST>(a, bb, acc[nt]);
+        }
+      } else {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(x[u][s4], b[u][nt][s4], acc[nt]);
+        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(x[u][s4], b[u][nt][s4], acc[nt]);
+      }
+    }
   }
   if constexpr (F16) {
     if (__any(bad) && lane == 0) atomicOr(args.found_inf, 1);
@@ -2080,11 +2111,13 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
 // Pass 1 on matrix cores with row-contiguous memory traffic (rows 16-byte aligned): the
 // workgroup's MT groups of 16 rows are processed in 256-column chunks. Row phase:
 // wavefront w loads rows 4MT w .. 4MT w + 4MT - 1 of the chunk (lane l: columns
-// 4l..4l+3, 1 KB of a row per load), forms M' (fp32 with error feedback: stored back the
+// 4l..4l+3, 1 KB of a row per load), forms M' (with error feedback: stored back the
 // same way) and writes it to an LDS tile. MFMA phase: wavefront w takes the chunk's
 // columns 64w..64w+63 (four K-steps of 16) of every row group, with the matching 16
-// bytes of Q^T rows 16nt + cl per K-step, loaded once for all MT groups. The next
-// chunk's rows are requested before the MFMA phase of this one.
+// bytes of Q^T rows 16nt + cl per K-step, loaded once for all MT groups; a 16-bit
+// state's K-step of 16 is one 16-bit MFMA (its M' and Q are exact in 16 bits) instead
+// of four fp32 ones. The next chunk's rows are requested before the MFMA phase of this
+// one.
 constexpr int kPass1TileStride = kColBlock + 4;  // LDS row stride (floats), padded
 constexpr int kPass1Groups = kMfmaPass1Rows / 16;
 
@@ -2274,15 +2307,31 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
 #pragma unroll
           for (int a = 0; a < 4; ++a) b[u][nt][a] = 0.f;
       }
+      if constexpr (ST != kStF32) {
+        // a 16-bit state's M' and Q are exact in 16 bits: one K = 16 step per block
+        uint2 bb[NT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const float4 av = *reinterpret_cast<const float4*>(tile + (16 * mt + cl) * LS + kc);
-        const float a4[4] = {av.x, av.y, av.z, av.w};
+        for (int nt = 0; nt < NT; ++nt)
+          bb[nt] = make_uint2(pack_h16x2<ST>(b[u][nt][0], b[u][nt][1]),
+                              pack_h16x2<ST>(b[u][nt][2], b[u][nt][3]));
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
+        for (int mt = 0; mt < MT; ++mt) {
+          const float4 av = *reinterpret_cast<const float4*>(tile + (16 * mt + cl) * LS + kc);
+          const uint2 a = make_uint2(pack_h16x2<ST>(av.x, av.y), pack_h16x2<ST>(av.z, av.w));
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            acc[mt][nt] = mfma16(a4[s4], b[u][nt][s4], acc[mt][nt]);
+          for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x16<ST>(a, bb[nt], acc[mt][nt]);
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const float4 av = *reinterpret_cast<const float4*>(tile + (16 * mt + cl) * LS + kc);
+          const float a4[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              acc[mt][nt] = mfma16(a4[s4], b[u][nt][s4], acc[mt][nt]);
+        }
       }
     }
     if constexpr (SM) {
@@ -2490,28 +2539,13 @@ __device__ __forceinline__ void pass2_mfma_body(const Pass2Args& args, const Ten
   }
 }
 
-// Pass 2 for a 16-bit state on the 16-bit matrix cores (v_mfma_f32_16x16x16 f16, or
-// bf16_1k): M' and P hold 16-bit values, so their products are exact and the result
-// differs from the fp32 matrix cores only in the fp32 accumulation order, at a quarter
-// of the instructions. Lane l supplies A[l%16][4(l/16)..4(l/16)+3] and
-// B[4(l/16)..4(l/16)+3][l%16] (four 16-bit values in two registers); D as above. Lane
-// (h, cl) loads rows 4h..4h+3 of each 16-row step at columns c0 + 4cl..4cl+3 (four
+// Pass 2 for a 16-bit state on the 16-bit matrix cores (mfma16x16x16): M' and P hold
+// 16-bit values, so their products are exact and the result differs from the fp32
+// matrix cores only in the fp32 accumulation order, at a quarter of the instructions.
+// Lane (h, cl) loads rows 4h..4h+3 of each 16-row step at columns c0 + 4cl..4cl+3 (four
 // 8-byte loads): column s of that 4 x 4 block is the A operand of MFMA s (output
 // columns c0 + 4i + s, as in pass2_mfma_body), and B holds the same four rows of P's
 // column 16nt + cl.
-typedef short mfma_s16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 mfma_h16x4 __attribute__((ext_vector_type(4)));
-
-template <int ST>
-__device__ __forceinline__ mfma_f4 mfma16x16x16(uint2 a, uint2 b, mfma_f4 c) {
-  if constexpr (ST == kStBF16)
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mfma_s16x4, a),
-                                                     __builtin_bit_cast(mfma_s16x4, b), c, 0, 0,
-                                                     0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(mfma_h16x4, a),
-                                                 __builtin_bit_cast(mfma_h16x4, b), c, 0, 0, 0);
-}
 
 template <int R, int ST>
 __device__ __forceinline__ void pass2_mfma16_rows(const Pass2Args& args, const TensorDesc& d,
