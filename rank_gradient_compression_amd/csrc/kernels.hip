@@ -1913,6 +1913,27 @@ __device__ __forceinline__ mfma_f4 mfma16x16x16(uint2 a, uint2 b, mfma_f4 c) {
                                                  __builtin_bit_cast(mfma_h16x4, b), c, 0, 0, 0);
 }
 
+// A 16 x 16 block of M_hat^T = Q P^T from the KQ ranks each lane holds of a Q row (qa)
+// and a P row (pb), lane group h holding ranks h KQ .. h KQ + KQ - 1. An fp32 state
+// takes KQ fp32 MFMA steps (written out where it is used); a 16-bit state (P and Q
+// exact in 16 bits) the KQ / 4 16-bit steps over the groups of four of those ranks
+// here. Pass 3 and the error rebuild of pass 1 take the same steps, so their values
+// agree bit for bit.
+template <int ST, int KQ>
+__device__ __forceinline__ mfma_f4 mhat_block16(const float (&qa)[KQ], const float (&pb)[KQ]) {
+  static_assert(ST != kStF32 && KQ % 4 == 0, "a 16-bit state, whole groups of four ranks");
+  mfma_f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < KQ / 4; ++j) {
+    const uint2 a = make_uint2(pack_h16x2<ST>(qa[4 * j], qa[4 * j + 1]),
+                               pack_h16x2<ST>(qa[4 * j + 2], qa[4 * j + 3]));
+    const uint2 b = make_uint2(pack_h16x2<ST>(pb[4 * j], pb[4 * j + 1]),
+                               pack_h16x2<ST>(pb[4 * j + 2], pb[4 * j + 3]));
+    acc = mfma16x16x16<ST>(a, b, acc);
+  }
+  return acc;
+}
+
 // Pass 1, P = M' Q, for rows that are not 16-byte aligned (or a bucket that is not): the
 // 16-row group grp of the work item's rows, over its column group. Wavefront w takes
 // the 64-column chunks w, w + 4, w + 8, ... of the group (U = 4 K-steps of 16 columns
@@ -2034,8 +2055,12 @@ __device__ __forceinline__ void pass1_mfma_body(const Pass1Args& args, const Ten
             for (int a = 0; a < 4; ++a) qa[4 * k4 + a] = w[a];
           }
           mfma_f4 mh = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (ST != kStF32) {
+            mh = mhat_block16<ST, KQ>(qa, pe);
+          } else {
 #pragma unroll
-          for (int kq = 0; kq < KQ; ++kq) mh = mfma16(qa[kq], pe[kq], mh);
+            for (int kq = 0; kq < KQ; ++kq) mh = mfma16(qa[kq], pe[kq], mh);
+          }
 #pragma unroll
           for (int a = 0; a < 4; ++a) e[u][a] = rebuilt_error<ST>(e[u][a], mh[a]);
         }
@@ -2195,8 +2220,12 @@ __device__ __forceinline__ void pass1_mfma_rows(const Pass1Args& args, const Ten
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         mfma_f4 mh = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (ST != kStF32) {
+          mh = mhat_block16<ST, KQ>(qa, pe[mt]);
+        } else {
 #pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) mh = mfma16(qa[kq], pe[mt][kq], mh);
+          for (int kq = 0; kq < KQ; ++kq) mh = mfma16(qa[kq], pe[mt][kq], mh);
+        }
         *reinterpret_cast<float4*>(mh_tile + (16 * mt + cl) * LS + 64 * wave + 16 * g + 4 * h) =
             make_float4(mh[0], mh[1], mh[2], mh[3]);
       }
@@ -2732,8 +2761,12 @@ __device__ __forceinline__ void pass3_mfma_body(const Pass3Args& args, const Ten
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         mfma_f4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (ST != kStF32) {
+          acc = mhat_block16<ST, KQ>(qa[g], pb[ur]);
+        } else {
 #pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) acc = mfma16(qa[g][kq], pb[ur][kq], acc);
+          for (int kq = 0; kq < KQ; ++kq) acc = mfma16(qa[g][kq], pb[ur][kq], acc);
+        }
         const int col = c0 + 16 * g + 4 * h;
         if (row < r1 && col < m) {
           const int64_t off = static_cast<int64_t>(row) * m + col;
@@ -2839,8 +2872,12 @@ __device__ __forceinline__ void pass3_mfma_rows(const Pass3Args& args, const Ten
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         mfma_f4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (ST != kStF32) {
+          acc = mhat_block16<ST, KQ>(qa[g], pb[ur]);
+        } else {
 #pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) acc = mfma16(qa[g][kq], pb[ur][kq], acc);
+          for (int kq = 0; kq < KQ; ++kq) acc = mfma16(qa[g][kq], pb[ur][kq], acc);
+        }
         *reinterpret_cast<float4*>(tile + (16 * ur + cl) * LS + 64 * wave + 16 * g + 4 * h) =
             make_float4(acc[0], acc[1], acc[2], acc[3]);
       }
