@@ -394,6 +394,10 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
   const int64_t target1 = prec != kStF32 ? std::max<int64_t>(1 << 13, target / 2) : target;
   const int64_t ng = static_cast<int64_t>(R) * (R + 1) / 2;
   const bool fused_gram = R <= kMaxFusedGramRank;
+  // a 16-bit state's pass-2 work item carries half the bytes of an fp32 one for the same
+  // orthogonalization prologue: twice the rows, where the bucket is large enough to be
+  // sized above the element floor (a smaller one would run too few work items)
+  const int64_t h16_scale = (prec != kStF32 && target > (1 << 13)) ? 2 : 1;
   int64_t goff = 0;
   int64_t eoff = 0, poff = 0, qoff = 0, qtoff = 0, p1off = 0;
   int32_t pslot = 0;
@@ -476,7 +480,8 @@ powersgd_status build_plan(const powersgd_hparams& hp, int64_t numel, bool batch
     };
     // vector ranks: every pass-2 workgroup orthogonalizes its P rows first, so its
     // work items are larger (fewer of them pay that prologue) and its rows fit in LDS
-    int64_t rpb = row_block(fused_gram ? std::min<int64_t>(1 << 16, target * PSGD_PASS2_TILE_SCALE)
+    int64_t rpb = row_block(fused_gram ? std::min<int64_t>(h16_scale << 16,
+                                                           target * PSGD_PASS2_TILE_SCALE * h16_scale)
                                        : target);
     if (R >= kMfmaMinRank) rpb = std::min<int64_t>(kMfmaPass2Rows, round_up(d.n, 16));
     if (fused_gram) rpb = std::min<int64_t>(rpb, kPass2StageFloats / R);
