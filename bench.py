@@ -249,11 +249,12 @@ class Workload:
             st.compress_bucket(bucket, self.views, inv_loss_scale=self.inv, found_inf=fi,
                                stream=stream)
 
-    def timed_steps(self, first: int, k: int, flush=None):
+    def timed_steps(self, first: int, k: int, flush=None, flush_read: bool = False):
         """Per-step milliseconds of steps first..first+k-1 from events on the launch
-        stream, each step timed alone; `flush` (a device tensor) is overwritten before
-        every step, outside its events, so each step starts with a cold last-level
-        cache. The K steps are bracketed by synchronizations."""
+        stream, each step timed alone; `flush` (a device tensor) is overwritten, or with
+        `flush_read` read, before every step, outside its events, so each step starts
+        with a cold last-level cache (holding the flush buffer's dirty lines, or clean
+        ones). The K steps are bracketed by synchronizations."""
         torch = self.torch
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(k)]
@@ -261,7 +262,10 @@ class Workload:
         t0 = time.perf_counter()
         for j in range(k):
             if flush is not None:
-                flush.fill_(float(j))
+                if flush_read:
+                    flush.sum()
+                else:
+                    flush.fill_(float(j))
             ev[j][0].record()
             self.run(first + j)
             ev[j][1].record()
@@ -277,7 +281,8 @@ class Workload:
         self.torch.cuda.empty_cache()
 
 
-def measure(torch, cfg, steps: int, warmup: int, repeats: int, flush=None):
+def measure(torch, cfg, steps: int, warmup: int, repeats: int, flush=None,
+            flush_read: bool = False):
     """`repeats` fresh states, each: `warmup` untimed steps (the first allocates), then
     `steps` timed steps. Returns the per-step times of every repeat, the walls of the
     timed regions, and the workload (its last state still open)."""
@@ -288,7 +293,7 @@ def measure(torch, cfg, steps: int, warmup: int, repeats: int, flush=None):
         for i in range(warmup):
             wl.run(i)
         torch.cuda.synchronize()
-        t, wall = wl.timed_steps(warmup, steps, flush)
+        t, wall = wl.timed_steps(warmup, steps, flush, flush_read)
         per_rep.append(t)
         walls.append(wall)
     return per_rep, walls, wl
@@ -440,14 +445,17 @@ def main() -> int:
 
     # Other workloads, for context (stderr and a summary object): the ResNet-50-shaped
     # bucket warm (its 74 MB bucket and E stay in the 256 MB last-level cache between
-    # steps) and cold (a 1 GiB buffer written before every step), and BERT-large.
+    # steps) and cold (a 1 GiB buffer written before every step, which leaves the cache
+    # full of dirty lines the step then writes back; or read, which leaves clean ones),
+    # and BERT-large.
     secondary = {}
     if not args.no_secondary:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        for key, c, fl in (("resnet50-bucket-r2 warm", CONFIGS[1], None),
-                           ("resnet50-bucket-r2 cold", CONFIGS[1], flush),
-                           ("bert-large-bucket-r4-batched", CONFIGS[2], None)):
-            pr, _, w2 = measure(torch, c, args.steps, args.warmup, 1, fl)
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(0.0)
+        for key, c, fl, rd in (("resnet50-bucket-r2 warm", CONFIGS[1], None, False),
+                               ("resnet50-bucket-r2 cold", CONFIGS[1], flush, False),
+                               ("resnet50-bucket-r2 cold, clean cache", CONFIGS[1], flush, True),
+                               ("bert-large-bucket-r4-batched", CONFIGS[2], None, False)):
+            pr, _, w2 = measure(torch, c, args.steps, args.warmup, 1, fl, rd)
             med = float(np.median(pr[0]))
             ce = compressed_elements(c, w2.side)
             w2.close()
